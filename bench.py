@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Throughput of the product-key memory layer, forward + backward, on one MI355X.
+
+One step = zero the value gradient, then the whole layer forward (selection,
+gather) and backward (value scatter + softmax backward, query/sub-key
+gradients) over one batch of synthetic tokens resident in HBM.  Every stage is
+a call into libpkm.so's C ABI on the current stream; HIP events recorded on
+that stream between the stages give each kernel's duration inside the timed
+region.  Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+METRIC = "PKM layer tokens/sec fwd+bwd (n=512,H=4,k=32,d=1024); gather HBM GB/s % peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+MFMA_FP32_PEAK_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="base-bf16-zipf-bwd")
+    ap.add_argument("--cpu-tokens", type=int, default=256,
+                    help="tokens of the same workload the CPU oracle is timed on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def stage_bytes(w, elt: int) -> dict:
+    """Algorithmic work of one launch of each stage: every one of the T*H*k
+    picks counted once, cache hits not subtracted."""
+    T, H, k, n, d_k, d_v, half = w.T, w.H, w.k, w.n, w.d_k, w.d_v, w.d_k // 2
+    picks = T * H * k
+    return {
+        "zero_dvalues": {"bytes": n * n * d_v * 4},
+        "select": {"flops": 2 * T * H * 2 * n * half,
+                   "bytes": T * H * d_k * elt + H * 2 * n * half * elt + picks * 12},
+        "gather": {"bytes": picks * d_v * elt + T * d_v * elt + picks * 8},
+        "bwd_values": {"bytes": picks * d_v * elt + picks * d_v * 4 + T * d_v * elt + picks * 12},
+        "bwd_queries": {"bytes": T * H * d_k * elt + T * H * d_k * 4 + picks * 8
+                        + H * 2 * n * half * (elt + 4)},
+    }
+
+
+def cpu_baseline(inp, k: int, count: int) -> dict:
+    import oracle
+    import pkm_inputs
+    orc = oracle.default()
+    w = inp["w"]
+    sub = pkm_inputs.token_subset(w.T, count, seed=4242)
+    q = inp["q"][sub]
+    dy = inp["dy"][sub]
+    t0 = time.perf_counter()
+    ref = orc.forward(q, inp["keys"], inp["values"], k)
+    orc.backward(q, inp["keys"], inp["values"], ref["idx"], ref["weights"], dy)
+    dt = time.perf_counter() - t0
+    return {"value": len(sub) / dt, "unit": "tokens/s", "cores": orc.max_threads(),
+            "kind": "oracle",
+            "sample": f"{len(sub)} seeded tokens of {w.name}, forward+backward in float64: flat "
+                      f"scoring and full sort of all {w.n * w.n} slots per head, dense gradients; "
+                      f"{dt:.2f} s wall on {orc.max_threads()} threads ({platform.processor() or platform.machine()})"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the sharding design is described in the design notes); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import pkm_inputs
+    from product_key_memory_amd import _lib
+    from product_key_memory_amd.pkm import problem
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    _lib.lib()                                   # fail loudly if libpkm.so is missing
+
+    inp = pkm_inputs.make(args.workload, with_dy=True)
+    w = inp["w"]
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    elt = 2 if w.dtype == "bf16" else 4
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    q, keys, values, dy = (to_dev(inp[x]) for x in ("q", "keys", "values", "dy"))
+    T, H, n, k, d_k, d_v = w.T, w.H, w.n, w.k, w.d_k, w.d_v
+    y = torch.empty((T, d_v), dtype=tdt, device=dev)
+    idx = torch.empty((T, H, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, H, k), dtype=torch.float32, device=dev)
+    scores = torch.empty((T, H, k), dtype=torch.float32, device=dev)
+    ds = torch.empty((T, H, k), dtype=torch.float32, device=dev)
+    dq = torch.empty((T, H, d_k), dtype=torch.float32, device=dev)
+    dkeys = torch.empty((H, 2, n, d_k // 2), dtype=torch.float32, device=dev)
+    dvalues = torch.empty((n * n, d_v), dtype=torch.float32, device=dev)
+    p = problem(T, H, n, k, d_k, d_v, tdt)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    P = lambda t: t.data_ptr()  # noqa: E731
+
+    stages = ["zero_dvalues", "select", "gather", "bwd_values", "bwd_queries"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        dvalues.zero_()
+        mark(1)
+        rc = _lib.forward_select(p, P(q), P(keys), P(idx), P(wts), P(scores), sp)
+        mark(2)
+        rc |= _lib.forward_gather(p, P(values), P(idx), P(wts), P(y), sp)
+        mark(3)
+        rc |= _lib.backward_values(p, P(values), P(idx), P(wts), P(dy), P(dvalues), P(ds), sp)
+        mark(4)
+        rc |= _lib.backward_queries(p, P(q), P(keys), P(idx), P(ds), P(dq), P(dkeys), sp)
+        mark(5)
+        if rc:
+            raise RuntimeError(f"libpkm returned {rc}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    per_stage = {name: 0.0 for name in stages}
+    for ev in events:
+        for i, name in enumerate(stages):
+            per_stage[name] += ev[i].elapsed_time(ev[i + 1])
+    per_stage = {name: v / args.steps for name, v in per_stage.items()}   # ms per launch
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    tokens_per_s = T / (wall_ms * 1e-3)
+
+    work = stage_bytes(w, elt)
+    kernels = {}
+    for name in stages:
+        ms = per_stage[name]
+        entry = {"ms": round(ms, 5), "bytes": work[name]["bytes"],
+                 "GB/s": round(work[name]["bytes"] / (ms * 1e-3) / 1e9, 1)}
+        entry["hbm_frac"] = round(entry["GB/s"] / HBM_PEAK_GBS, 4)
+        if "flops" in work[name]:
+            tf = work[name]["flops"] / (ms * 1e-3) / 1e12
+            peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+            entry.update({"flops": work[name]["flops"], "TFLOP/s": round(tf, 2),
+                          "mfma_frac": round(tf / peak, 4)})
+        kernels[name] = entry
+
+    dominant = max(("select", "gather", "bwd_values", "bwd_queries"), key=lambda s: per_stage[s])
+    dk = kernels[dominant]
+    roofline = {"kernel": dominant, "bound": "hbm", "achieved": dk["GB/s"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(dk["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "heads": H, "n": n, "slots": n * n, "k": k,
+                   "d_k": d_k, "d_v": d_v, "storage": w.dtype, "accumulate": "fp32",
+                   "zipf": w.zipf, "step": "zero dvalues + forward + backward"},
+        "gather": {"GB/s": kernels["gather"]["GB/s"], "hbm_frac": kernels["gather"]["hbm_frac"]},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, k, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

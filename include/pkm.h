@@ -1,0 +1,167 @@
+/*
+ * pkm.h -- C ABI of the product-key memory (PKM) layer for AMD Instinct MI355X
+ * (gfx950).  Forward and backward of one memory layer, as described in
+ * "Large Memory Layers with Product Keys" (Lample et al., 2019); the pages
+ * cited below are the summary on gptget.net (section "Methodology" and the
+ * methodology list of its "Deep Analysis") and the companion page "Product
+ * Keys Give Transformers Million-Slot Memory Layers" (sections "Implied keys
+ * vs stored sub-keys", "Why top-k of each half is enough", "Search cost: flat
+ * vs product keys").
+ *
+ * Notation: T tokens, H heads, n sub-keys per codebook (n*n memory slots),
+ * k selected slots per head, d_k query width per head (half = d_k / 2),
+ * d_v value width.  Slot f = i*n + j is the implied key made of left sub-key i
+ * followed by right sub-key j.
+ *
+ * Conventions for every entry point:
+ *  - All array arguments are DEVICE pointers owned by the caller, row-major
+ *    and contiguous, 16-byte aligned, and must not alias one another.  The
+ *    problem descriptor `p` is a HOST pointer, read during the call only.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  All work
+ *    is enqueued on it; no call synchronises with the host.
+ *  - The library allocates no memory and keeps no state between calls; it is
+ *    re-entrant.  Scratch memory comes from the caller's `workspace`, sized by
+ *    pkm_workspace_bytes().
+ *  - Arguments are validated completely before anything is enqueued.  On any
+ *    error a non-zero status is returned and NOTHING has been enqueued.  A
+ *    launch failure reported by the HIP runtime returns PKM_ERR_HIP (work
+ *    enqueued before it may still run).
+ *  - T == 0 is a successful no-op.
+ *  - Supported shapes (else PKM_ERR_SHAPE): H in [1, 64]; n in [1, 1024];
+ *    k in [1, min(n, 64)]; d_k in [16, 1024] and a multiple of 16; d_v >= 8
+ *    and a multiple of 8; for pkm_backward additionally d_v <= 4096.
+ *  - Inputs must be finite; the result for NaN or Inf inputs is unspecified.
+ */
+#ifndef PKM_H
+#define PKM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of q, keys, values, y and dy.  Arithmetic is always float32
+ * (products of bfloat16 operands are exact in float32). */
+typedef enum { PKM_FP32 = 0, PKM_BF16 = 1 } pkm_dtype_t;
+
+typedef enum {
+    PKM_OK = 0,
+    PKM_ERR_NULL = 1,      /* a required pointer is NULL                         */
+    PKM_ERR_SHAPE = 2,     /* a size outside the supported range                 */
+    PKM_ERR_DTYPE = 3,     /* unknown dtype                                      */
+    PKM_ERR_WORKSPACE = 4, /* workspace smaller than pkm_workspace_bytes()       */
+    PKM_ERR_HIP = 5,       /* the HIP runtime rejected a launch                  */
+    PKM_ERR_ALIGN = 6      /* an array pointer is not 16-byte aligned            */
+} pkm_status_t;
+
+/* Problem sizes.  32 bytes, no padding: T, then six int32 fields. */
+typedef struct {
+    int64_t T;      /* tokens (>= 0)                                          */
+    int32_t H;      /* heads                                                  */
+    int32_t n;      /* sub-keys per codebook; the memory has n*n slots        */
+    int32_t k;      /* slots selected per head (also the per-half top-k)      */
+    int32_t d_k;    /* query width per head; halves of d_k/2                  */
+    int32_t d_v;    /* value row width                                        */
+    int32_t dtype;  /* pkm_dtype_t                                            */
+} pkm_problem_t;
+
+/* Bytes of device workspace pkm_forward (backward = 0) or pkm_backward
+ * (backward = 1) needs for this problem; 0 if none.  Returns (size_t)-1 for
+ * an invalid descriptor. */
+size_t pkm_workspace_bytes(const pkm_problem_t *p, int backward);
+
+/*
+ * Forward pass (gptget.net summary, "Methodology"; companion page, "Why top-k
+ * of each half is enough").  For every token t and head h:
+ *   1. split q[t][h] into q1 = first half, q2 = second half;
+ *   2. score q1 against the n left sub-keys and q2 against the n right
+ *      sub-keys (inner products, float32 accumulation);
+ *   3. keep the exact top-k of each half, ordered (score desc, index asc);
+ *   4. combine: the score of slot (i, j) is left_i + right_j; keep the k best
+ *      slots by (score desc, slot asc) -- the same set as a flat search over
+ *      all n*n implied keys;
+ *   5. weights = softmax of the k selected scores;
+ * and y[t] = sum over heads and picks of weight * values[slot].
+ *
+ *   q        [T][H][d_k]        dtype   (q1 = first d_k/2 of each head)
+ *   keys     [H][2][n][d_k/2]   dtype   ([h][0] left codebook, [h][1] right)
+ *   values   [n*n][d_v]         dtype   (row f = i*n + j)
+ *   y        [T][d_v]           dtype   OUT, overwritten (float32 sums,
+ *                                       rounded to nearest-even for bf16)
+ *   idx      [T][H][k]          int32   OUT, slots in (score desc, slot asc)
+ *   weights  [T][H][k]          float32 OUT, softmax weights
+ *   scores   [T][H][k]          float32 OUT, selected scores; may be NULL
+ */
+pkm_status_t pkm_forward(const pkm_problem_t *p, const void *q, const void *keys,
+                         const void *values, void *y, int32_t *idx, float *weights,
+                         float *scores, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/*
+ * Backward pass for an upstream gradient dy = dL/dy (gptget.net summary,
+ * "Methodology": the whole layer is trained by backprop and only the selected
+ * memory slots receive a value update).  The selection is held fixed; with
+ * w = weights and picks (t, h, r) of slot f = idx[t][h][r] = i*n + j:
+ *   dw     = <dy[t], values[f]>
+ *   ds     = w_r * (dw_r - sum_r' w_r' dw_r')            (softmax backward)
+ *   dvalues[f]         += w_r * dy[t]
+ *   dq[t][h][left]      = sum_r ds_r * keys[h][0][i_r]
+ *   dq[t][h][right]     = sum_r ds_r * keys[h][1][j_r]
+ *   dkeys[h][0][i]      = sum over picks with left index i of ds * q1[t][h]
+ *   dkeys[h][1][j]      = sum over picks with right index j of ds * q2[t][h]
+ *
+ *   q, keys, values   as for pkm_forward (same p)
+ *   idx, weights      [T][H][k] as produced by pkm_forward for these inputs
+ *   dy       [T][d_v]           dtype
+ *   dq       [T][H][d_k]        float32 OUT, overwritten
+ *   dkeys    [H][2][n][d_k/2]   float32 OUT, overwritten
+ *   dvalues  [n*n][d_v]         float32 IN/OUT, ACCUMULATED (+=): the caller
+ *                               zeroes it before the first call.  Rows no pick
+ *                               selects are left untouched.
+ * Floating-point atomics make the summation order (not the result beyond
+ * rounding) vary from run to run.
+ */
+pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *keys,
+                          const void *values, const int32_t *idx, const float *weights,
+                          const void *dy, float *dq, float *dkeys, float *dvalues,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The two passes above, stage by stage, for callers that keep the
+ * intermediate results or time the stages: pkm_forward is
+ * pkm_forward_select followed by pkm_forward_gather; pkm_backward is
+ * pkm_backward_values followed by pkm_backward_queries (with `ds` in its
+ * workspace).  Same conventions, same array layouts as above.
+ */
+
+/* Steps 1-5 of pkm_forward: the selection and its softmax weights
+ * (companion page, "Why top-k of each half is enough"). */
+pkm_status_t pkm_forward_select(const pkm_problem_t *p, const void *q, const void *keys,
+                                int32_t *idx, float *weights, float *scores, void *stream);
+
+/* y[t] = sum over heads h and picks r of weights[t][h][r] * values[idx[t][h][r]]
+ * (gptget.net summary, "Methodology": weighted sum of the selected values). */
+pkm_status_t pkm_forward_gather(const pkm_problem_t *p, const void *values, const int32_t *idx,
+                                const float *weights, void *y, void *stream);
+
+/* dw, the sparse value update dvalues[f] += w * dy[t] (accumulated), and the
+ * softmax backward ds [T][H][k] float32 (OUT, overwritten). */
+pkm_status_t pkm_backward_values(const pkm_problem_t *p, const void *values, const int32_t *idx,
+                                 const float *weights, const void *dy, float *dvalues,
+                                 float *ds, void *stream);
+
+/* dq (overwritten) and dkeys (overwritten) from ds: each pick's ds reaches its
+ * left sub-key i = f / n and right sub-key j = f % n. */
+pkm_status_t pkm_backward_queries(const pkm_problem_t *p, const void *q, const void *keys,
+                                  const int32_t *idx, const float *ds, float *dq, float *dkeys,
+                                  void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *pkm_status_string(pkm_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKM_H */

@@ -199,3 +199,39 @@ def token_subset(T: int, count: int, seed: int) -> np.ndarray:
     rng = np.random.default_rng(seed)
     count = min(count, T)
     return np.sort(rng.choice(T, size=count, replace=False)).astype(np.int64)
+
+
+def custom(T: int, H: int, n: int, k: int, d_k: int, d_v: int, dtype: str = "fp32",
+           seed: int = 0, kind: str = "normal", with_dy: bool = True) -> dict:
+    """Small seeded problems for edge cases, same dict layout as make().
+
+    kind: "normal"     all N(0, 1)
+          "integer"    q in {-3..3}, sub-keys in {-2..2} (exact float arithmetic,
+                       many exactly tied scores), values N(0, 1)
+          "dup"        normal, with duplicated sub-key rows in both codebooks
+          "right_zero" normal, with the right half of every query set to 0
+    """
+    w = Workload(f"custom-{kind}", T=T, H=H, d_k=d_k, n=n, k=k, d_v=d_v, dtype=dtype,
+                 seed=seed, query=kind, backward=with_dy)
+    rng = np.random.default_rng(seed)
+    half = d_k // 2
+    if kind == "integer":
+        q = rng.integers(-3, 4, size=(T, H, d_k)).astype(np.float32)
+        keys = rng.integers(-2, 3, size=(H, 2, n, half)).astype(np.float32)
+    else:
+        q = rng.standard_normal((T, H, d_k), dtype=np.float32)
+        keys = rng.standard_normal((H, 2, n, half), dtype=np.float32)
+    if kind == "dup" and n >= 3:
+        keys[:, 0, n - 1] = keys[:, 0, 0]
+        keys[:, 1, 1] = keys[:, 1, n - 2]
+    if kind == "right_zero":
+        q[:, :, half:] = 0.0
+    values = rng.standard_normal((n * n, d_v), dtype=np.float32)
+    dy = rng.standard_normal((T, d_v), dtype=np.float32) if with_dy else None
+    out = dict(w=w, target=None)
+    if dtype == "bf16":
+        out["q"], out["keys"], out["values"] = bf16_bits(q), bf16_bits(keys), bf16_bits(values)
+        out["dy"] = bf16_bits(dy) if dy is not None else None
+    else:
+        out["q"], out["keys"], out["values"], out["dy"] = q, keys, values, dy
+    return out

@@ -1,0 +1,110 @@
+"""ctypes view of libpkm.so (the C ABI declared in include/pkm.h).
+
+Loading fails loudly: there is no fallback path.  If the library has not been
+built (``python -m product_key_memory_amd.build``) every entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkm.so")
+
+PKM_FP32 = 0
+PKM_BF16 = 1
+
+STATUS = {
+    0: "PKM_OK",
+    1: "PKM_ERR_NULL",
+    2: "PKM_ERR_SHAPE",
+    3: "PKM_ERR_DTYPE",
+    4: "PKM_ERR_WORKSPACE",
+    5: "PKM_ERR_HIP",
+    6: "PKM_ERR_ALIGN",
+}
+
+# every symbol include/pkm.h declares
+EXPORTS = ("pkm_workspace_bytes", "pkm_forward", "pkm_backward", "pkm_forward_select",
+           "pkm_forward_gather", "pkm_backward_values", "pkm_backward_queries",
+           "pkm_status_string")
+
+
+class Problem(ctypes.Structure):
+    """pkm_problem_t: int64 T, then int32 H, n, k, d_k, d_v, dtype (32 bytes)."""
+    _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int32), ("n", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class PKMError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {status_string(code)} ({code})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"libpkm.so is not built at {LIB_PATH}; run `python -m product_key_memory_amd.build` "
+                "(the HIP library is required: there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, c_size = ctypes.c_void_p, ctypes.c_size_t
+        L.pkm_workspace_bytes.argtypes = [ctypes.POINTER(Problem), ctypes.c_int]
+        L.pkm_workspace_bytes.restype = c_size
+        L.pkm_forward.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, c_size, P]
+        L.pkm_forward.restype = ctypes.c_int
+        L.pkm_backward.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P, P,
+                                   c_size, P]
+        L.pkm_backward.restype = ctypes.c_int
+        PP = ctypes.POINTER(Problem)
+        L.pkm_forward_select.argtypes = [PP, P, P, P, P, P, P]
+        L.pkm_forward_gather.argtypes = [PP, P, P, P, P, P]
+        L.pkm_backward_values.argtypes = [PP, P, P, P, P, P, P, P]
+        L.pkm_backward_queries.argtypes = [PP, P, P, P, P, P, P, P]
+        for name in ("pkm_forward_select", "pkm_forward_gather", "pkm_backward_values",
+                     "pkm_backward_queries"):
+            getattr(L, name).restype = ctypes.c_int
+        L.pkm_status_string.argtypes = [ctypes.c_int]
+        L.pkm_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().pkm_status_string(code).decode()
+
+
+def workspace_bytes(p: Problem, backward: bool) -> int:
+    return int(lib().pkm_workspace_bytes(ctypes.byref(p), int(backward)))
+
+
+def forward(p: Problem, q, keys, values, y, idx, weights, scores, ws, ws_bytes, stream) -> int:
+    return lib().pkm_forward(ctypes.byref(p), q, keys, values, y, idx, weights, scores, ws,
+                             ws_bytes, stream)
+
+
+def backward(p: Problem, q, keys, values, idx, weights, dy, dq, dkeys, dvalues, ws, ws_bytes,
+             stream) -> int:
+    return lib().pkm_backward(ctypes.byref(p), q, keys, values, idx, weights, dy, dq, dkeys,
+                              dvalues, ws, ws_bytes, stream)
+
+
+def forward_select(p: Problem, q, keys, idx, weights, scores, stream) -> int:
+    return lib().pkm_forward_select(ctypes.byref(p), q, keys, idx, weights, scores, stream)
+
+
+def forward_gather(p: Problem, values, idx, weights, y, stream) -> int:
+    return lib().pkm_forward_gather(ctypes.byref(p), values, idx, weights, y, stream)
+
+
+def backward_values(p: Problem, values, idx, weights, dy, dvalues, ds, stream) -> int:
+    return lib().pkm_backward_values(ctypes.byref(p), values, idx, weights, dy, dvalues, ds, stream)
+
+
+def backward_queries(p: Problem, q, keys, idx, ds, dq, dkeys, stream) -> int:
+    return lib().pkm_backward_queries(ctypes.byref(p), q, keys, idx, ds, dq, dkeys, stream)

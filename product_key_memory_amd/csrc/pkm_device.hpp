@@ -1,0 +1,167 @@
+// pkm_device.hpp -- device-side building blocks shared by the PKM kernels:
+// storage-type conversions, order-preserving selection keys, and wave64
+// primitives (reductions, scans, bitonic sorts across the 64 lanes).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkm {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// bfloat16 storage is carried as raw 16-bit patterns.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// float32 -> bfloat16, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Unpack 16 bytes of storage into float32 lanes.
+__device__ __forceinline__ void unpack16(const uint4 v, float (&out)[8])
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        out[2 * i] = __uint_as_float(w[i] << 16);
+        out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+__device__ __forceinline__ void unpack16(const uint4 v, float (&out)[4])
+{
+    out[0] = __uint_as_float(v.x);
+    out[1] = __uint_as_float(v.y);
+    out[2] = __uint_as_float(v.z);
+    out[3] = __uint_as_float(v.w);
+}
+
+// Elements of a storage type per 16-byte chunk.
+template <typename DT> struct Elt;
+template <> struct Elt<float> { static constexpr int per16 = 4; };
+template <> struct Elt<bf16_t> { static constexpr int per16 = 8; };
+
+// ---------------------------------------------------------------------------
+// Selection keys.  A 64-bit key orders (score descending, index ascending) as
+// plain unsigned integer descending: high word = order-preserving image of the
+// float score (-0 folded onto +0), low word = bitwise NOT of the index.  Every
+// key of a finite score is > 0, so 0 pads a sort and sinks to the end.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t ord_f32(float s)
+{
+    uint32_t u = __float_as_uint(s);
+    if (u == 0x80000000u)
+        u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unord_f32(uint32_t o)
+{
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ uint64_t make_key(float s, uint32_t index)
+{
+    return ((uint64_t)ord_f32(s) << 32) | (uint64_t)(~index);
+}
+__device__ __forceinline__ float key_score(uint64_t key) { return unord_f32((uint32_t)(key >> 32)); }
+__device__ __forceinline__ uint32_t key_index(uint64_t key) { return ~(uint32_t)key; }
+
+// ---------------------------------------------------------------------------
+// wave64 primitives
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask)
+{
+    const uint32_t lo = __shfl_xor((int)(uint32_t)v, mask);
+    const uint32_t hi = __shfl_xor((int)(uint32_t)(v >> 32), mask);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v += __shfl_xor(v, m);
+    return v;
+}
+
+// Exclusive prefix sum over the 64 lanes; *total receives the wave total.
+__device__ __forceinline__ int wave_exclusive_scan(int v, int *total)
+{
+    const int lane = lane_id();
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(inc, d);
+        if (lane >= d)
+            inc += o;
+    }
+    *total = __shfl(inc, kWave - 1);
+    return inc - v;
+}
+
+// Bitonic sort, descending, of 64 floats (one per lane).  Lane i ends with
+// the i-th largest.
+__device__ __forceinline__ float wave_sort64_desc(float v)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const float o = __shfl_xor(v, stride);
+            const bool desc = (lane & size) == 0 || size == kWave;
+            const bool lower = (lane & stride) == 0;
+            v = (lower == desc) ? fmaxf(v, o) : fminf(v, o);
+        }
+    }
+    return v;
+}
+
+// Bitonic sort, descending, of R*64 keys held R per lane; element i = r*64 + lane.
+template <int R>
+__device__ __forceinline__ void wave_sort_desc(uint64_t (&v)[R])
+{
+    const int lane = lane_id();
+    constexpr int P = R * kWave;
+#pragma unroll
+    for (int size = 2; size <= P; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride >= kWave) {
+                const int rs = stride / kWave;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if ((r & rs) == 0) {
+                        const bool desc = ((r * kWave) & size) == 0;
+                        const uint64_t a = v[r], b = v[r | rs];
+                        const bool swap = desc ? (a < b) : (a > b);
+                        v[r] = swap ? b : a;
+                        v[r | rs] = swap ? a : b;
+                    }
+                }
+            } else {
+                const bool lower = (lane & stride) == 0;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const uint64_t o = shfl_xor_u64(v[r], stride);
+                    const bool desc = ((r * kWave + lane) & size) == 0;
+                    const bool keep_max = (lower == desc);
+                    v[r] = keep_max ? (v[r] > o ? v[r] : o) : (v[r] < o ? v[r] : o);
+                }
+            }
+        }
+    }
+}
+
+}  // namespace pkm

@@ -1,0 +1,144 @@
+"""PyTorch marshalling for the C ABI of libpkm.so.
+
+Each function checks tensor placement and shapes, allocates the outputs and the
+workspace with PyTorch's allocator, and passes raw device pointers plus the
+current HIP stream to the library.  No arithmetic of the layer happens here.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import PKMError, Problem
+
+_DTYPES = {torch.float32: _lib.PKM_FP32, torch.bfloat16: _lib.PKM_BF16}
+
+
+def pkm_status_string(code: int) -> str:
+    return _lib.status_string(code)
+
+
+def problem(T, H, n, k, d_k, d_v, dtype) -> Problem:
+    code = _DTYPES.get(dtype, dtype) if isinstance(dtype, torch.dtype) else dtype
+    if isinstance(code, torch.dtype):
+        raise TypeError(f"unsupported dtype {dtype}")
+    return Problem(int(T), int(H), int(n), int(k), int(d_k), int(d_v), int(code))
+
+
+def pkm_workspace_bytes(p: Problem, backward: bool = False) -> int:
+    return _lib.workspace_bytes(p, backward)
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _shapes(q, keys, values):
+    if q.dim() != 3 or keys.dim() != 4 or values.dim() != 2:
+        raise ValueError("expected q [T,H,d_k], keys [H,2,n,d_k/2], values [n*n,d_v]")
+    T, H, d_k = q.shape
+    n = keys.shape[2]
+    d_v = values.shape[1]
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    if q.device.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    return T, H, n, d_k, d_v
+
+
+def pkm_forward(q: torch.Tensor, keys: torch.Tensor, values: torch.Tensor, k: int,
+                want_scores: bool = True, out=None):
+    """Forward pass.  Returns (y [T,d_v] in q.dtype, idx [T,H,k] int32,
+    weights [T,H,k] float32, scores [T,H,k] float32 or None)."""
+    T, H, n, d_k, d_v = _shapes(q, keys, values)
+    dev, dt = q.device, q.dtype
+    _check(q, "q", (T, H, d_k), dt, dev)
+    _check(keys, "keys", (H, 2, n, d_k // 2), dt, dev)
+    _check(values, "values", (n * n, d_v), dt, dev)
+    p = problem(T, H, n, k, d_k, d_v, dt)
+    ws_bytes = pkm_workspace_bytes(p, False)
+    if ws_bytes == (1 << 64) - 1:
+        raise PKMError(2, "pkm_forward")
+    if out is None:
+        y = torch.empty((T, d_v), dtype=dt, device=dev)
+        idx = torch.empty((T, H, k), dtype=torch.int32, device=dev)
+        weights = torch.empty((T, H, k), dtype=torch.float32, device=dev)
+        scores = torch.empty((T, H, k), dtype=torch.float32, device=dev) if want_scores else None
+    else:
+        y, idx, weights, scores = out
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
+    rc = _lib.forward(p, _ptr(q), _ptr(keys), _ptr(values), _ptr(y), _ptr(idx), _ptr(weights),
+                      _ptr(scores), _ptr(ws), ws_bytes, _stream(dev))
+    if rc != 0:
+        raise PKMError(rc, "pkm_forward")
+    return y, idx, weights, scores
+
+
+def pkm_backward(q: torch.Tensor, keys: torch.Tensor, values: torch.Tensor, idx: torch.Tensor,
+                 weights: torch.Tensor, dy: torch.Tensor, dvalues: torch.Tensor | None = None,
+                 out=None):
+    """Backward pass.  Returns (dq [T,H,d_k], dkeys [H,2,n,d_k/2], dvalues [n*n,d_v]),
+    all float32.  dvalues is ACCUMULATED into when given (zeros are allocated
+    otherwise)."""
+    T, H, n, d_k, d_v = _shapes(q, keys, values)
+    dev, dt = q.device, q.dtype
+    k = idx.shape[2]
+    _check(q, "q", (T, H, d_k), dt, dev)
+    _check(keys, "keys", (H, 2, n, d_k // 2), dt, dev)
+    _check(values, "values", (n * n, d_v), dt, dev)
+    _check(idx, "idx", (T, H, k), torch.int32, dev)
+    _check(weights, "weights", (T, H, k), torch.float32, dev)
+    _check(dy, "dy", (T, d_v), dt, dev)
+    p = problem(T, H, n, k, d_k, d_v, dt)
+    ws_bytes = pkm_workspace_bytes(p, True)
+    if ws_bytes == (1 << 64) - 1:
+        raise PKMError(2, "pkm_backward")
+    if dvalues is None:
+        dvalues = torch.zeros((n * n, d_v), dtype=torch.float32, device=dev)
+    else:
+        _check(dvalues, "dvalues", (n * n, d_v), torch.float32, dev)
+    if out is None:
+        dq = torch.empty((T, H, d_k), dtype=torch.float32, device=dev)
+        dkeys = torch.empty((H, 2, n, d_k // 2), dtype=torch.float32, device=dev)
+    else:
+        dq, dkeys = out
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
+    rc = _lib.backward(p, _ptr(q), _ptr(keys), _ptr(values), _ptr(idx), _ptr(weights), _ptr(dy),
+                       _ptr(dq), _ptr(dkeys), _ptr(dvalues), _ptr(ws), ws_bytes, _stream(dev))
+    if rc != 0:
+        raise PKMError(rc, "pkm_backward")
+    return dq, dkeys, dvalues
+
+
+class ProductKeyMemoryFunction(torch.autograd.Function):
+    """y = PKM(q, keys, values) with the library's backward."""
+
+    @staticmethod
+    def forward(ctx, q, keys, values, k: int):
+        y, idx, weights, _ = pkm_forward(q, keys, values, k, want_scores=False)
+        ctx.save_for_backward(q, keys, values, idx, weights)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        q, keys, values, idx, weights = ctx.saved_tensors
+        dq, dkeys, dvalues = pkm_backward(q, keys, values, idx, weights,
+                                          dy.contiguous().to(q.dtype))
+        return dq.to(q.dtype), dkeys.to(keys.dtype), dvalues.to(values.dtype), None

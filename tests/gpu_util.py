@@ -1,0 +1,89 @@
+"""Helpers for the GPU tests: numpy <-> torch and one parity run."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import parity
+
+
+def device():
+    assert torch.cuda.is_available(), "GPU tests need a GPU (run them with -m gpu on an MI355X)"
+    return torch.device("cuda", 0)
+
+
+def to_dev(a: np.ndarray, dev) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def bits_to_f64(a: np.ndarray) -> np.ndarray:
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def run_parity(orc, inp: dict, k: int, subset=None, backward: bool = False, tol=None,
+               tight=None, nthreads: int = 0) -> dict:
+    """Run the GPU path on all of inp's tokens; check `subset` (all if None)
+    against the oracle.  Returns a report dict."""
+    import product_key_memory_amd as pk
+
+    dev = device()
+    w = inp["w"]
+    n = w.n
+    tol = parity.TOL[w.dtype] if tol is None else tol
+    q, keys, values = (to_dev(inp[x], dev) for x in ("q", "keys", "values"))
+    print(f"[parity] {w.name} T={w.T} H={w.H} n={n} k={k} d_k={w.d_k} d_v={w.d_v} {w.dtype}",
+          flush=True)
+    y, idx, wts, sc = pk.pkm_forward(q, keys, values, k)
+    torch.cuda.synchronize()
+    sub = np.arange(w.T) if subset is None else np.asarray(subset)
+    g_idx = to_host(idx)[sub]
+    g_w = to_host(wts)[sub]
+    g_sc = to_host(sc)[sub]
+    g_y = bits_to_f64(to_host(y))[sub]
+    q_sub = inp["q"][sub]
+    ref = orc.forward(q_sub, inp["keys"], inp["values"], k, nthreads=nthreads)
+    given = orc.forward_given_idx(q_sub, inp["keys"], inp["values"], g_idx, nthreads=nthreads)
+    rep = parity.check_selection(g_idx, ref, given, n)
+    werr = float(np.abs(g_w - given["weights"]).max())
+    assert werr <= 1e-4, f"weights differ by {werr:.3e}"
+    serr = float((np.abs(g_sc - given["scores"]) / np.maximum(1.0, np.abs(given["scores"]))).max())
+    assert serr <= 1e-4, f"scores differ by {serr:.3e}"
+    rep["w_err"], rep["score_err"] = werr, serr
+    rep["y_err"] = parity.assert_rows_close("y", g_y, given["y"], tol)
+    if tight is not None:
+        assert rep["y_err"] <= tight["y"], f"y error {rep['y_err']:.3e} above the expected {tight['y']}"
+    if backward:
+        dy_np = inp["dy"]
+        mask = np.zeros(w.T, bool)
+        mask[sub] = True
+        dy_masked = dy_np.copy()
+        dy_masked[~mask] = 0
+        dq, dkeys, dvalues = pk.pkm_backward(q, keys, values, idx, wts, to_dev(dy_masked, dev))
+        torch.cuda.synchronize()
+        ob = orc.backward(q_sub, inp["keys"], inp["values"], g_idx, given["weights"], dy_np[sub],
+                          nthreads=nthreads)
+        g_dq = to_host(dq)[sub]
+        rep["dq_err"] = parity.assert_rows_close("dq", g_dq, ob["dq"], tol)
+        g_dk = to_host(dkeys).reshape(-1, w.d_k // 2)
+        rep["dkeys_err"] = parity.assert_rows_close("dkeys", g_dk, ob["dkeys"].reshape(-1, w.d_k // 2), tol)
+        g_dv = to_host(dvalues)
+        touched = np.zeros(n * n, bool)
+        touched[g_idx.ravel()] = True
+        assert np.all(g_dv[~touched] == 0.0), "unselected value rows must stay exactly 0"
+        rows = np.nonzero(touched)[0]
+        rep["dvalues_err"] = parity.assert_rows_close("dvalues", g_dv[rows], ob["dvalues"][rows], tol)
+        if tight is not None:
+            for key in ("dq_err", "dkeys_err", "dvalues_err"):
+                assert rep[key] <= tight["grad"], f"{key} {rep[key]:.3e} above the expected {tight['grad']}"
+    print(f"[parity] ok {rep}", flush=True)
+    return rep

@@ -1,0 +1,75 @@
+"""The C ABI library loads, exports what include/pkm.h declares, and rejects
+bad arguments on the host before anything reaches a GPU (no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from product_key_memory_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "pkm.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(pkm_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib.lib()
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_problem_struct_layout():
+    assert ctypes.sizeof(_lib.Problem) == 32
+
+
+def P(**kw):
+    base = dict(T=16, H=2, n=64, k=8, d_k=64, d_v=32, dtype=0)
+    base.update(kw)
+    return _lib.Problem(base["T"], base["H"], base["n"], base["k"], base["d_k"], base["d_v"], base["dtype"])
+
+
+FAKE = 1 << 20          # an aligned, never-dereferenced address
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=0), 2), (dict(k=65, n=128), 2), (dict(k=9, n=8), 2), (dict(n=0), 2), (dict(n=1025), 2),
+    (dict(d_k=24), 2), (dict(d_k=8), 2), (dict(d_k=1040), 2), (dict(d_v=12), 2), (dict(d_v=0), 2),
+    (dict(H=0), 2), (dict(H=65), 2), (dict(T=-1), 2), (dict(dtype=7), 3),
+])
+def test_forward_rejects_bad_shapes(kw, code):
+    rc = _lib.forward(P(**kw), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None)
+    assert rc == code, _lib.STATUS.get(rc)
+
+
+def test_null_and_alignment():
+    assert _lib.forward(P(), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 1
+    assert _lib.forward(P(), FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 6
+    assert _lib.forward_select(P(), FAKE, FAKE, None, FAKE, None, None) == 1
+    assert _lib.backward_values(P(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, None) == 6
+
+
+def test_backward_workspace_checks():
+    p = P()
+    need = _lib.workspace_bytes(p, True)
+    assert need == ((16 * 2 * 8 * 4 + 255) // 256) * 256
+    assert _lib.workspace_bytes(p, False) == 0
+    args = [FAKE] * 9
+    assert _lib.backward(p, *args, FAKE, need - 1, None) == 4
+    assert _lib.backward(p, *args, None, 0, None) == 1
+    assert _lib.backward(P(d_v=4104), *args, FAKE, 1 << 30, None) == 2   # backward row limit
+
+
+def test_workspace_of_invalid_problem():
+    assert _lib.workspace_bytes(P(k=0), True) == (1 << 64) - 1
+
+
+def test_status_strings():
+    for code, name in _lib.STATUS.items():
+        assert _lib.status_string(code).startswith(name)

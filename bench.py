@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="base-bf16-zipf-bwd")
-    ap.add_argument("--cpu-tokens", type=int, default=256,
+    ap.add_argument("--cpu-tokens", type=int, default=1024,
                     help="tokens of the same workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -50,7 +50,7 @@ def stage_bytes(w, elt: int) -> dict:
                    "bytes": T * H * d_k * elt + H * 2 * n * half * elt + picks * 12},
         "gather": {"bytes": picks * d_v * elt + T * d_v * elt + picks * 8},
         "bwd_values": {"bytes": picks * d_v * elt + picks * d_v * 4 + T * d_v * elt + picks * 12},
-        "bwd_queries": {"bytes": T * H * d_k * elt + T * H * d_k * 4 + picks * 8
+        "bwd_queries": {"bytes": T * H * d_k * elt + T * H * d_k * 4 + picks * 12
                         + H * 2 * n * half * (elt + 4)},
     }
 
@@ -108,7 +108,7 @@ def main():
     idx = torch.empty((T, H, k), dtype=torch.int32, device=dev)
     wts = torch.empty((T, H, k), dtype=torch.float32, device=dev)
     scores = torch.empty((T, H, k), dtype=torch.float32, device=dev)
-    ds = torch.empty((T, H, k), dtype=torch.float32, device=dev)
+    dw = torch.empty((T, H, k), dtype=torch.float32, device=dev)
     dq = torch.empty((T, H, d_k), dtype=torch.float32, device=dev)
     dkeys = torch.empty((H, 2, n, d_k // 2), dtype=torch.float32, device=dev)
     dvalues = torch.empty((n * n, d_v), dtype=torch.float32, device=dev)
@@ -130,9 +130,9 @@ def main():
         mark(2)
         rc |= _lib.forward_gather(p, P(values), P(idx), P(wts), P(y), sp)
         mark(3)
-        rc |= _lib.backward_values(p, P(values), P(idx), P(wts), P(dy), P(dvalues), P(ds), sp)
+        rc |= _lib.backward_values(p, P(values), P(idx), P(wts), P(dy), P(dvalues), P(dw), sp)
         mark(4)
-        rc |= _lib.backward_queries(p, P(q), P(keys), P(idx), P(ds), P(dq), P(dkeys), sp)
+        rc |= _lib.backward_queries(p, P(q), P(keys), P(idx), P(wts), P(dw), P(dq), P(dkeys), sp)
         mark(5)
         if rc:
             raise RuntimeError(f"libpkm returned {rc}")

@@ -26,7 +26,9 @@
  *    error a non-zero status is returned and NOTHING has been enqueued.  A
  *    launch failure reported by the HIP runtime returns PKM_ERR_HIP (work
  *    enqueued before it may still run).
- *  - T == 0 is a successful no-op.
+ *  - T == 0 is a successful no-op (pkm_backward and pkm_backward_queries still
+ *    overwrite dkeys with zeros).  A pointer to an array with no elements may
+ *    be NULL.
  *  - Supported shapes (else PKM_ERR_SHAPE): H in [1, 64]; n in [1, 1024];
  *    k in [1, min(n, 64)]; d_k in [16, 1024] and a multiple of 16; d_v >= 8
  *    and a multiple of 8; for pkm_backward additionally d_v <= 4096.
@@ -132,7 +134,7 @@ pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *key
  * The two passes above, stage by stage, for callers that keep the
  * intermediate results or time the stages: pkm_forward is
  * pkm_forward_select followed by pkm_forward_gather; pkm_backward is
- * pkm_backward_values followed by pkm_backward_queries (with `ds` in its
+ * pkm_backward_values followed by pkm_backward_queries (with `dw` in its
  * workspace).  Same conventions, same array layouts as above.
  */
 
@@ -146,17 +148,19 @@ pkm_status_t pkm_forward_select(const pkm_problem_t *p, const void *q, const voi
 pkm_status_t pkm_forward_gather(const pkm_problem_t *p, const void *values, const int32_t *idx,
                                 const float *weights, void *y, void *stream);
 
-/* dw, the sparse value update dvalues[f] += w * dy[t] (accumulated), and the
- * softmax backward ds [T][H][k] float32 (OUT, overwritten). */
+/* The value side of pkm_backward: dw [T][H][k] float32 (OUT, overwritten),
+ * dw = <dy[t], values[f]>, and the sparse update dvalues[f] += w * dy[t]
+ * (ACCUMULATED, as in pkm_backward). */
 pkm_status_t pkm_backward_values(const pkm_problem_t *p, const void *values, const int32_t *idx,
                                  const float *weights, const void *dy, float *dvalues,
-                                 float *ds, void *stream);
+                                 float *dw, void *stream);
 
-/* dq (overwritten) and dkeys (overwritten) from ds: each pick's ds reaches its
- * left sub-key i = f / n and right sub-key j = f % n. */
+/* The query side of pkm_backward, from weights and dw: the softmax backward,
+ * then dq and dkeys (both OUT, overwritten).  Each pick's ds reaches its left
+ * sub-key i = f / n and its right sub-key j = f % n. */
 pkm_status_t pkm_backward_queries(const pkm_problem_t *p, const void *q, const void *keys,
-                                  const int32_t *idx, const float *ds, float *dq, float *dkeys,
-                                  void *stream);
+                                  const int32_t *idx, const float *weights, const float *dw,
+                                  float *dq, float *dkeys, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *pkm_status_string(pkm_status_t s);

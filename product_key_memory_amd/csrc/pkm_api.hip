@@ -16,6 +16,9 @@ constexpr int kMaxDvBackward = 4096;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A pointer to an array with no elements (T == 0) may be NULL.
+bool missing(const void *p, int64_t count) { return count > 0 && p == nullptr; }
+
 pkm_status_t check_problem(const pkm_problem_t *p, bool backward)
 {
     if (!p)
@@ -58,7 +61,8 @@ pkm_status_t pkm_forward(const pkm_problem_t *p, const void *q, const void *keys
         return st;
     (void)workspace;
     (void)workspace_bytes;      // the forward pass needs no workspace
-    if (!q || !keys || !values || !y || !idx || !weights)
+    const int64_t T = p->T;
+    if (missing(q, T) || !keys || !values || missing(y, T) || missing(idx, T) || missing(weights, T))
         return PKM_ERR_NULL;
     if (!aligned16(q) || !aligned16(keys) || !aligned16(values) || !aligned16(y) ||
         !aligned16(idx) || !aligned16(weights) || (scores && !aligned16(scores)))
@@ -83,7 +87,9 @@ pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *key
     pkm_status_t st = check_problem(p, true);
     if (st != PKM_OK)
         return st;
-    if (!q || !keys || !values || !idx || !weights || !dy || !dq || !dkeys || !dvalues)
+    const int64_t T = p->T;
+    if (missing(q, T) || !keys || !values || missing(idx, T) || missing(weights, T) ||
+        missing(dy, T) || missing(dq, T) || !dkeys || !dvalues)
         return PKM_ERR_NULL;
     if (!aligned16(q) || !aligned16(keys) || !aligned16(values) || !aligned16(idx) ||
         !aligned16(weights) || !aligned16(dy) || !aligned16(dq) || !aligned16(dkeys) ||
@@ -98,12 +104,12 @@ pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *key
         return PKM_ERR_HIP;
     if (p->T == 0)
         return PKM_OK;
-    float *ds = static_cast<float *>(workspace);
-    if (pkm::launch_bwd_value(p->dtype, values, idx, weights, dy, dvalues, ds, p->T, p->H, p->k,
+    float *dw = static_cast<float *>(workspace);
+    if (pkm::launch_bwd_value(p->dtype, values, idx, weights, dy, dvalues, dw, p->T, p->H, p->k,
                               p->d_v, s) != hipSuccess)
         return PKM_ERR_HIP;
-    if (pkm::launch_bwd_query(p->dtype, q, keys, idx, ds, dq, dkeys, p->T, p->H, p->n, p->k,
-                              p->d_k, s) != hipSuccess)
+    if (pkm::launch_bwd_query(p->dtype, q, keys, idx, weights, dw, dq, dkeys, p->T, p->H, p->n,
+                              p->k, p->d_k, s) != hipSuccess)
         return PKM_ERR_HIP;
     return PKM_OK;
 }
@@ -114,7 +120,8 @@ pkm_status_t pkm_forward_select(const pkm_problem_t *p, const void *q, const voi
     pkm_status_t st = check_problem(p, false);
     if (st != PKM_OK)
         return st;
-    if (!q || !keys || !idx || !weights)
+    const int64_t T = p->T;
+    if (missing(q, T) || !keys || missing(idx, T) || missing(weights, T))
         return PKM_ERR_NULL;
     if (!aligned16(q) || !aligned16(keys) || !aligned16(idx) || !aligned16(weights) ||
         (scores && !aligned16(scores)))
@@ -133,7 +140,8 @@ pkm_status_t pkm_forward_gather(const pkm_problem_t *p, const void *values, cons
     pkm_status_t st = check_problem(p, false);
     if (st != PKM_OK)
         return st;
-    if (!values || !idx || !weights || !y)
+    const int64_t T = p->T;
+    if (!values || missing(idx, T) || missing(weights, T) || missing(y, T))
         return PKM_ERR_NULL;
     if (!aligned16(values) || !aligned16(idx) || !aligned16(weights) || !aligned16(y))
         return PKM_ERR_ALIGN;
@@ -147,43 +155,47 @@ pkm_status_t pkm_forward_gather(const pkm_problem_t *p, const void *values, cons
 
 pkm_status_t pkm_backward_values(const pkm_problem_t *p, const void *values, const int32_t *idx,
                                  const float *weights, const void *dy, float *dvalues,
-                                 float *ds, void *stream)
+                                 float *dw, void *stream)
 {
     pkm_status_t st = check_problem(p, true);
     if (st != PKM_OK)
         return st;
-    if (!values || !idx || !weights || !dy || !dvalues || !ds)
+    const int64_t T = p->T;
+    if (!values || missing(idx, T) || missing(weights, T) || missing(dy, T) || !dvalues ||
+        missing(dw, T))
         return PKM_ERR_NULL;
     if (!aligned16(values) || !aligned16(idx) || !aligned16(weights) || !aligned16(dy) ||
-        !aligned16(dvalues) || !aligned16(ds))
+        !aligned16(dvalues) || !aligned16(dw))
         return PKM_ERR_ALIGN;
     if (p->T == 0)
         return PKM_OK;
-    return pkm::launch_bwd_value(p->dtype, values, idx, weights, dy, dvalues, ds, p->T, p->H,
+    return pkm::launch_bwd_value(p->dtype, values, idx, weights, dy, dvalues, dw, p->T, p->H,
                                  p->k, p->d_v, static_cast<hipStream_t>(stream)) == hipSuccess
                ? PKM_OK
                : PKM_ERR_HIP;
 }
 
 pkm_status_t pkm_backward_queries(const pkm_problem_t *p, const void *q, const void *keys,
-                                  const int32_t *idx, const float *ds, float *dq, float *dkeys,
-                                  void *stream)
+                                  const int32_t *idx, const float *weights, const float *dw,
+                                  float *dq, float *dkeys, void *stream)
 {
     pkm_status_t st = check_problem(p, true);
     if (st != PKM_OK)
         return st;
-    if (!q || !keys || !idx || !ds || !dq || !dkeys)
+    const int64_t T = p->T;
+    if (missing(q, T) || !keys || missing(idx, T) || missing(weights, T) || missing(dw, T) ||
+        missing(dq, T) || !dkeys)
         return PKM_ERR_NULL;
-    if (!aligned16(q) || !aligned16(keys) || !aligned16(idx) || !aligned16(ds) ||
-        !aligned16(dq) || !aligned16(dkeys))
+    if (!aligned16(q) || !aligned16(keys) || !aligned16(idx) || !aligned16(weights) ||
+        !aligned16(dw) || !aligned16(dq) || !aligned16(dkeys))
         return PKM_ERR_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (pkm::launch_zero_f32(dkeys, (int64_t)p->H * 2 * p->n * (p->d_k / 2), s) != hipSuccess)
         return PKM_ERR_HIP;
     if (p->T == 0)
         return PKM_OK;
-    return pkm::launch_bwd_query(p->dtype, q, keys, idx, ds, dq, dkeys, p->T, p->H, p->n, p->k,
-                                 p->d_k, s) == hipSuccess
+    return pkm::launch_bwd_query(p->dtype, q, keys, idx, weights, dw, dq, dkeys, p->T, p->H, p->n,
+                                 p->k, p->d_k, s) == hipSuccess
                ? PKM_OK
                : PKM_ERR_HIP;
 }

@@ -8,11 +8,15 @@
 // bwd_value: one wave per token.  For each pick (h, r) the value row is
 //   re-read once and serves both  dw = <dy[t], values[f]>  and the sparse
 //   update  dvalues[f] += w * dy[t]  (float32 hardware atomics, lane-
-//   contiguous 256-byte bursts).  The softmax backward
-//   ds_r = w_r (dw_r - sum_r' w_r' dw_r') closes each head.
-// bwd_query: one wave per (token, head).  Picks sharing a sub-key are merged
-//   first, then  dq = sum ds * sub-key row  and  dkeys[sub] += ds * q_half
-//   (atomics) for each distinct sub-key of each half.
+//   contiguous 256-byte bursts).  dw goes to [T][H][k].
+// bwd_query: one wave per (token, head), one lane per pick.  The softmax
+//   backward ds_r = w_r (dw_r - sum_r' w_r' dw_r') only matters summed over the
+//   picks S that share a sub-key i of one half; that sum is taken as
+//       g_i = A * (1 - W) - B * W,  A = sum_S w dw, W = sum_S w,
+//                                   B = sum_notS w dw, 1 - W = sum_notS w,
+//   with both complements summed directly, so a sub-key shared by most picks
+//   (its g is a near-cancelling sum) keeps full relative accuracy.  Then
+//   dq = sum_i g_i * sub-key row i  and  dkeys[i] += g_i * q_half  (atomics).
 #include "pkm_device.hpp"
 #include "pkm_kernels.hpp"
 
@@ -35,7 +39,7 @@ template <typename DT, int MCH, int U>
 __global__ __launch_bounds__(kBwdWaves *kWave) void bwd_value_kernel(
     const DT *__restrict__ values, const int32_t *__restrict__ idx,
     const float *__restrict__ weights, const DT *__restrict__ dy, float *__restrict__ dvalues,
-    float *__restrict__ ds, int64_t T, int H, int k, int d_v)
+    float *__restrict__ dw, int64_t T, int H, int k, int d_v)
 {
     constexpr int EPC = Elt<DT>::per16;
     constexpr int NI = MCH * EPC;          // interleaved dy elements per lane (>= d_v / 64)
@@ -109,49 +113,47 @@ __global__ __launch_bounds__(kBwdWaves *kWave) void bwd_value_kernel(
                 }
             }
         }
-        const float w_mine = lane < k ? weights[base + lane] : 0.f;
-        const float wdw = wave_sum(w_mine * dw_mine);
         if (lane < k)
-            ds[base + lane] = w_mine * (dw_mine - wdw);
+            dw[base + lane] = dw_mine;
     }
 }
 
 template <typename DT, int MCH, int U>
 static hipError_t launch_bwd_value_t(const void *values, const int32_t *idx, const float *weights,
-                                     const void *dy, float *dvalues, float *ds, int64_t T, int H,
+                                     const void *dy, float *dvalues, float *dw, int64_t T, int H,
                                      int k, int d_v, hipStream_t stream)
 {
     const dim3 grid((unsigned)((T + kBwdWaves - 1) / kBwdWaves));
     hipLaunchKernelGGL((bwd_value_kernel<DT, MCH, U>), grid, dim3(kBwdWaves * kWave), 0, stream,
                        static_cast<const DT *>(values), idx, weights,
-                       static_cast<const DT *>(dy), dvalues, ds, T, H, k, d_v);
+                       static_cast<const DT *>(dy), dvalues, dw, T, H, k, d_v);
     return hipGetLastError();
 }
 
 template <typename DT>
 static hipError_t launch_bwd_value_dt(const void *values, const int32_t *idx, const float *weights,
-                                      const void *dy, float *dvalues, float *ds, int64_t T, int H,
+                                      const void *dy, float *dvalues, float *dw, int64_t T, int H,
                                       int k, int d_v, hipStream_t stream)
 {
     const int per_lane = (d_v / Elt<DT>::per16 + kWave - 1) / kWave;
     if (per_lane <= 1)
-        return launch_bwd_value_t<DT, 1, 8>(values, idx, weights, dy, dvalues, ds, T, H, k, d_v, stream);
+        return launch_bwd_value_t<DT, 1, 8>(values, idx, weights, dy, dvalues, dw, T, H, k, d_v, stream);
     if (per_lane <= 2)
-        return launch_bwd_value_t<DT, 2, 4>(values, idx, weights, dy, dvalues, ds, T, H, k, d_v, stream);
+        return launch_bwd_value_t<DT, 2, 4>(values, idx, weights, dy, dvalues, dw, T, H, k, d_v, stream);
     if (per_lane <= 4)
-        return launch_bwd_value_t<DT, 4, 2>(values, idx, weights, dy, dvalues, ds, T, H, k, d_v, stream);
+        return launch_bwd_value_t<DT, 4, 2>(values, idx, weights, dy, dvalues, dw, T, H, k, d_v, stream);
     if (per_lane <= 8)
-        return launch_bwd_value_t<DT, 8, 1>(values, idx, weights, dy, dvalues, ds, T, H, k, d_v, stream);
-    return launch_bwd_value_t<DT, 16, 1>(values, idx, weights, dy, dvalues, ds, T, H, k, d_v, stream);
+        return launch_bwd_value_t<DT, 8, 1>(values, idx, weights, dy, dvalues, dw, T, H, k, d_v, stream);
+    return launch_bwd_value_t<DT, 16, 1>(values, idx, weights, dy, dvalues, dw, T, H, k, d_v, stream);
 }
 
 hipError_t launch_bwd_value(int dtype, const void *values, const int32_t *idx,
-                            const float *weights, const void *dy, float *dvalues, float *ds,
+                            const float *weights, const void *dy, float *dvalues, float *dw,
                             int64_t T, int H, int k, int d_v, hipStream_t stream)
 {
     if (dtype == 1)
-        return launch_bwd_value_dt<bf16_t>(values, idx, weights, dy, dvalues, ds, T, H, k, d_v, stream);
-    return launch_bwd_value_dt<float>(values, idx, weights, dy, dvalues, ds, T, H, k, d_v, stream);
+        return launch_bwd_value_dt<bf16_t>(values, idx, weights, dy, dvalues, dw, T, H, k, d_v, stream);
+    return launch_bwd_value_dt<float>(values, idx, weights, dy, dvalues, dw, T, H, k, d_v, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -160,8 +162,8 @@ constexpr int kMaxHalfPerLane = 8;   // half <= 512
 template <typename DT>
 __global__ __launch_bounds__(kBwdWaves *kWave) void bwd_query_kernel(
     const DT *__restrict__ q, const DT *__restrict__ keys, const int32_t *__restrict__ idx,
-    const float *__restrict__ ds, float *__restrict__ dq, float *__restrict__ dkeys, int64_t T,
-    int H, int n, int k, int d_k)
+    const float *__restrict__ weights, const float *__restrict__ dw, float *__restrict__ dq,
+    float *__restrict__ dkeys, int64_t T, int H, int n, int k, int d_k)
 {
     const int lane = lane_id();
     const int64_t row = (int64_t)blockIdx.x * kBwdWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -172,22 +174,30 @@ __global__ __launch_bounds__(kBwdWaves *kWave) void bwd_query_kernel(
     const int half = d_k / 2;
     const int64_t base = row * (int64_t)k;
     const int f = lane < k ? idx[base + lane] : 0;
-    const float g0 = lane < k ? ds[base + lane] : 0.f;
+    const float w_mine = lane < k ? weights[base + lane] : 0.f;
+    const float wdw_mine = lane < k ? w_mine * dw[base + lane] : 0.f;
 
     for (int s = 0; s < 2; ++s) {
         const int sub = s == 0 ? f / n : f % n;
-        // merge picks that share this half's sub-key; the first one carries the sum
-        float g = 0.f;
+        // sums over the picks sharing this lane's sub-key (A, W) and over the
+        // rest (B, Wc); the first pick of each sub-key carries its g
+        float A = 0.f, W = 0.f, B = 0.f, Wc = 0.f;
         bool first = lane < k;
         for (int r = 0; r < k; ++r) {
             const int sub_r = __shfl(sub, r);
-            const float g_r = __shfl(g0, r);
+            const float w_r = __shfl(w_mine, r);
+            const float wdw_r = __shfl(wdw_mine, r);
             if (sub_r == sub) {
-                g += g_r;
+                A += wdw_r;
+                W += w_r;
                 if (r < lane)
                     first = false;
+            } else {
+                B += wdw_r;
+                Wc += w_r;
             }
         }
+        const float g = A * Wc - B * W;
         const DT *qh = q + row * (int64_t)d_k + (int64_t)s * half;
         const DT *kb = keys + ((int64_t)h * 2 + s) * (int64_t)n * half;
         float *dkb = dkeys + ((int64_t)h * 2 + s) * (int64_t)n * half;
@@ -228,24 +238,25 @@ __global__ __launch_bounds__(kBwdWaves *kWave) void bwd_query_kernel(
 
 template <typename DT>
 static hipError_t launch_bwd_query_t(const void *q, const void *keys, const int32_t *idx,
-                                     const float *ds, float *dq, float *dkeys, int64_t T, int H,
-                                     int n, int k, int d_k, hipStream_t stream)
+                                     const float *weights, const float *dw, float *dq,
+                                     float *dkeys, int64_t T, int H, int n, int k, int d_k,
+                                     hipStream_t stream)
 {
     const int64_t rows = T * H;
     const dim3 grid((unsigned)((rows + kBwdWaves - 1) / kBwdWaves));
     hipLaunchKernelGGL(bwd_query_kernel<DT>, grid, dim3(kBwdWaves * kWave), 0, stream,
-                       static_cast<const DT *>(q), static_cast<const DT *>(keys), idx, ds, dq,
-                       dkeys, T, H, n, k, d_k);
+                       static_cast<const DT *>(q), static_cast<const DT *>(keys), idx, weights,
+                       dw, dq, dkeys, T, H, n, k, d_k);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_query(int dtype, const void *q, const void *keys, const int32_t *idx,
-                            const float *ds, float *dq, float *dkeys, int64_t T, int H, int n,
-                            int k, int d_k, hipStream_t stream)
+                            const float *weights, const float *dw, float *dq, float *dkeys,
+                            int64_t T, int H, int n, int k, int d_k, hipStream_t stream)
 {
     if (dtype == 1)
-        return launch_bwd_query_t<bf16_t>(q, keys, idx, ds, dq, dkeys, T, H, n, k, d_k, stream);
-    return launch_bwd_query_t<float>(q, keys, idx, ds, dq, dkeys, T, H, n, k, d_k, stream);
+        return launch_bwd_query_t<bf16_t>(q, keys, idx, weights, dw, dq, dkeys, T, H, n, k, d_k, stream);
+    return launch_bwd_query_t<float>(q, keys, idx, weights, dw, dq, dkeys, T, H, n, k, d_k, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -12,6 +12,7 @@ constexpr int kWave = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef double doublex4 __attribute__((ext_vector_type(4)));
 
 // bfloat16 storage is carried as raw 16-bit patterns.
 struct bf16_t {

@@ -20,16 +20,17 @@ hipError_t launch_fwd_gather(int dtype, const void *values, const int32_t *idx,
                              const float *weights, void *y, int64_t T, int HK, int d_v,
                              hipStream_t stream);
 
-// dw = <dy, values[slot]>, dvalues[slot] += w * dy (atomics), ds = softmax
-// backward; ds is written to `ds` [T][H][k].
+// dw = <dy, values[slot]> written to `dw` [T][H][k]; dvalues[slot] += w * dy
+// (atomics).
 hipError_t launch_bwd_value(int dtype, const void *values, const int32_t *idx,
-                            const float *weights, const void *dy, float *dvalues, float *ds,
+                            const float *weights, const void *dy, float *dvalues, float *dw,
                             int64_t T, int H, int k, int d_v, hipStream_t stream);
 
-// dq (overwritten) and dkeys (accumulated; zero it first) from ds.
+// Softmax backward, then dq (overwritten) and dkeys (accumulated; zero it
+// first) from weights and dw.
 hipError_t launch_bwd_query(int dtype, const void *q, const void *keys, const int32_t *idx,
-                            const float *ds, float *dq, float *dkeys, int64_t T, int H, int n,
-                            int k, int d_k, hipStream_t stream);
+                            const float *weights, const float *dw, float *dq, float *dkeys,
+                            int64_t T, int H, int n, int k, int d_k, hipStream_t stream);
 
 // Fill `count` floats with zero (a kernel, so it can sit inside a captured graph).
 hipError_t launch_zero_f32(float *p, int64_t count, hipStream_t stream);

@@ -5,9 +5,11 @@
 // "Methodology": split q into q1, q2 and search each against its own sub-key
 // set):
 //   1. the 16 query halves are staged in LDS, and the 16 x n score tile
-//      <q_s[t], C_s[i]> is computed with MFMA (bf16: v_mfma_f32_16x16x32_bf16,
-//      fp32: v_mfma_f32_16x16x4_f32), sub-keys as the M dimension, tokens as N,
-//      float32 accumulation, straight into LDS -- scores never reach HBM;
+//      <q_s[t], C_s[i]> is computed with MFMA (bf16 storage:
+//      v_mfma_f32_16x16x32_bf16, exact products, float32 accumulation; float32
+//      storage: v_mfma_f64_16x16x4_f64, exact products and float64
+//      accumulation, rounded once), sub-keys as the M dimension, tokens as N,
+//      straight into LDS -- scores never reach HBM;
 //   2. every row's exact top-k, ordered (score desc, index asc), is found by a
 //      threshold filter: tau = k-th largest of the 64 per-lane maxima is a
 //      lower bound of the k-th largest score (the k lanes above it each hold
@@ -103,6 +105,10 @@ __device__ __forceinline__ floatx4 score_tile(const bf16_t *krow_base, int n, in
     return acc;
 }
 
+// float32 storage: the operands widen exactly to float64 and v_mfma_f64_16x16x4_f64
+// accumulates in float64, so each score is the exact dot product rounded once
+// to float32 (scores of any magnitude keep full float32 accuracy, which the
+// softmax weights inherit).
 __device__ __forceinline__ floatx4 score_tile(const float *krow_base, int n, int half,
                                               const float *qt, int q_stride, int tile)
 {
@@ -112,7 +118,7 @@ __device__ __forceinline__ floatx4 score_tile(const float *krow_base, int n, int
     const bool valid = sub < n;
     const float *arow = krow_base + (int64_t)(valid ? sub : 0) * half;
     const float *brow = qt + r16 * q_stride;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    doublex4 acc = {0.0, 0.0, 0.0, 0.0};
     for (int kk = 0; kk < half; kk += 16) {
         const int c = kk + kg * 4;
         float4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
@@ -121,12 +127,13 @@ __device__ __forceinline__ floatx4 score_tile(const float *krow_base, int n, int
                 a = *reinterpret_cast<const float4 *>(arow + c);
             b = *reinterpret_cast<const float4 *>(brow + c);
         }
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a.x, (double)b.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a.y, (double)b.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a.z, (double)b.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a.w, (double)b.w, acc, 0, 0, 0);
     }
-    return acc;
+    floatx4 out = {(float)acc[0], (float)acc[1], (float)acc[2], (float)acc[3]};
+    return out;
 }
 
 // ---- step 2: exact top-k of one score row --------------------------------
@@ -266,9 +273,17 @@ __global__ __launch_bounds__(kSelThreads) void fwd_select_kernel(
         const int ntiles = (n + 15) / 16;
         for (int tile = wave; tile < ntiles; tile += kSelWaves) {
             const floatx4 acc = score_tile(kbase, n, half, qt, L.q_stride, tile);
-            // lane l holds sub-keys tile*16 + 4*(l/16) + i of token l%16
-            float4 out = {acc[0], acc[1], acc[2], acc[3]};
-            *reinterpret_cast<float4 *>(sc + (lane & 15) * L.n_pad + tile * 16 + 4 * (lane >> 4)) = out;
+            float *dst = sc + (lane & 15) * L.n_pad + tile * 16;
+            if constexpr (sizeof(DT) == 2) {
+                // f32 MFMA: lane l holds sub-keys 4*(l/16) + i of token l%16
+                float4 out = {acc[0], acc[1], acc[2], acc[3]};
+                *reinterpret_cast<float4 *>(dst + 4 * (lane >> 4)) = out;
+            } else {
+                // f64 MFMA: lane l holds sub-keys 4*i + l/16 of token l%16
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    dst[4 * i + (lane >> 4)] = acc[i];
+            }
         }
         __syncthreads();
 

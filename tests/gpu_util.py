@@ -72,18 +72,36 @@ def run_parity(orc, inp: dict, k: int, subset=None, backward: bool = False, tol=
         torch.cuda.synchronize()
         ob = orc.backward(q_sub, inp["keys"], inp["values"], g_idx, given["weights"], dy_np[sub],
                           nthreads=nthreads)
+        # size of one term of each gradient's sums (see parity.row_rel_err)
+        half = w.d_k // 2
+        wdw = np.sqrt(np.mean((given["weights"] * ob["dw"]) ** 2))
+        rms_row = lambda a: float(np.sqrt(np.mean(np.sum(a * a, axis=1))))  # noqa: E731
+        term = {"dq": wdw * rms_row(bits_to_f64(inp["keys"]).reshape(-1, half)),
+                "dkeys": wdw * rms_row(bits_to_f64(q_sub).reshape(-1, half)),
+                "dvalues": float(np.sqrt(np.mean(given["weights"] ** 2)))
+                * rms_row(bits_to_f64(dy_np[sub]))}
         g_dq = to_host(dq)[sub]
-        rep["dq_err"] = parity.assert_rows_close("dq", g_dq, ob["dq"], tol)
-        g_dk = to_host(dkeys).reshape(-1, w.d_k // 2)
-        rep["dkeys_err"] = parity.assert_rows_close("dkeys", g_dk, ob["dkeys"].reshape(-1, w.d_k // 2), tol)
+        rep["dq_err"] = parity.assert_rows_close("dq", g_dq, ob["dq"], tol,
+                                                 abs_floor=1e-3 * term["dq"])
+        g_dk = to_host(dkeys).reshape(-1, half)
+        rep["dkeys_err"] = parity.assert_rows_close("dkeys", g_dk, ob["dkeys"].reshape(-1, half), tol,
+                                                    abs_floor=1e-3 * term["dkeys"])
         g_dv = to_host(dvalues)
         touched = np.zeros(n * n, bool)
         touched[g_idx.ravel()] = True
         assert np.all(g_dv[~touched] == 0.0), "unselected value rows must stay exactly 0"
         rows = np.nonzero(touched)[0]
-        rep["dvalues_err"] = parity.assert_rows_close("dvalues", g_dv[rows], ob["dvalues"][rows], tol)
+        rep["dvalues_err"] = parity.assert_rows_close("dvalues", g_dv[rows], ob["dvalues"][rows], tol,
+                                                      abs_floor=1e-3 * term["dvalues"])
         if tight is not None:
-            for key in ("dq_err", "dkeys_err", "dvalues_err"):
-                assert rep[key] <= tight["grad"], f"{key} {rep[key]:.3e} above the expected {tight['grad']}"
+            # against the typical row size: rows whose own sum nearly cancels
+            # (a hot sub-key shared by most picks of a head) amplify float32
+            # rounding in the relative measure above, not in this one
+            for key, got, want in (("dq", g_dq, ob["dq"]),
+                                   ("dkeys", g_dk, ob["dkeys"].reshape(-1, half)),
+                                   ("dvalues", g_dv[rows], ob["dvalues"][rows])):
+                e = float(parity.row_rel_err(got, want, floor=1.0, abs_floor=term[key]).max())
+                rep[key + "_err_vs_rms"] = e
+                assert e <= tight["grad"], f"{key}: error {e:.3e} of the rms row above {tight['grad']}"
     print(f"[parity] ok {rep}", flush=True)
     return rep

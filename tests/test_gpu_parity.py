@@ -13,8 +13,9 @@ import pkm_inputs
 pytestmark = pytest.mark.gpu
 
 # Besides the gate tolerances, the errors expected from the arithmetic itself:
-# float32 accumulation everywhere, and for bf16 one rounding of y on store.
-TIGHT = {"fp32": {"y": 1e-5, "grad": 1e-4}, "bf16": {"y": 6e-3, "grad": 2e-4}}
+# float32 accumulation everywhere, and for bf16 one rounding of y on store
+# (y: per-row relative error; gradients: error relative to the rms row norm).
+TIGHT = {"fp32": {"y": 5e-5, "grad": 2e-5}, "bf16": {"y": 6e-3, "grad": 5e-5}}
 
 
 def test_tiny_fp32_full(orc):

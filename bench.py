@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=1024,
                     help="tokens of the same workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run 3 plain 256 MiB device copies, whose FETCH_SIZE/WRITE_SIZE "
+                         "counters calibrate the HBM-traffic counters of the kernels")
     return ap.parse_args()
 
 
@@ -136,6 +139,14 @@ def main():
         mark(5)
         if rc:
             raise RuntimeError(f"libpkm returned {rc}")
+
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

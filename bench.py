@@ -116,6 +116,8 @@ def main():
     dkeys = torch.empty((H, 2, n, d_k // 2), dtype=torch.float32, device=dev)
     dvalues = torch.empty((n * n, d_v), dtype=torch.float32, device=dev)
     p = problem(T, H, n, k, d_k, d_v, tdt)
+    ws_bytes = _lib.workspace_bytes(p, True)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     P = lambda t: t.data_ptr()  # noqa: E731
@@ -133,9 +135,11 @@ def main():
         mark(2)
         rc |= _lib.forward_gather(p, P(values), P(idx), P(wts), P(y), sp)
         mark(3)
-        rc |= _lib.backward_values(p, P(values), P(idx), P(wts), P(dy), P(dvalues), P(dw), sp)
+        rc |= _lib.backward_values(p, P(values), P(idx), P(wts), P(dy), P(dvalues), P(dw),
+                                  P(ws), ws_bytes, sp)
         mark(4)
-        rc |= _lib.backward_queries(p, P(q), P(keys), P(idx), P(wts), P(dw), P(dq), P(dkeys), sp)
+        rc |= _lib.backward_queries(p, P(q), P(keys), P(idx), P(wts), P(dw), P(dq), P(dkeys),
+                                   P(ws), ws_bytes, sp)
         mark(5)
         if rc:
             raise RuntimeError(f"libpkm returned {rc}")

@@ -122,8 +122,9 @@ pkm_status_t pkm_forward(const pkm_problem_t *p, const void *q, const void *keys
  *   dvalues  [n*n][d_v]         float32 IN/OUT, ACCUMULATED (+=): the caller
  *                               zeroes it before the first call.  Rows no pick
  *                               selects are left untouched.
- * Floating-point atomics make the summation order (not the result beyond
- * rounding) vary from run to run.
+ * The order in which float32 partial sums meet (slot sort, atomics on rows
+ * shared by several waves) varies from run to run, so results vary at the
+ * rounding level.
  */
 pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *keys,
                           const void *values, const int32_t *idx, const float *weights,
@@ -134,8 +135,9 @@ pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *key
  * The two passes above, stage by stage, for callers that keep the
  * intermediate results or time the stages: pkm_forward is
  * pkm_forward_select followed by pkm_forward_gather; pkm_backward is
- * pkm_backward_values followed by pkm_backward_queries (with `dw` in its
- * workspace).  Same conventions, same array layouts as above.
+ * pkm_backward_values followed by pkm_backward_queries.  Same conventions,
+ * same array layouts as above.  A workspace of pkm_workspace_bytes(p, 1)
+ * bytes serves either backward stage.
  */
 
 /* Steps 1-5 of pkm_forward: the selection and its softmax weights
@@ -150,17 +152,20 @@ pkm_status_t pkm_forward_gather(const pkm_problem_t *p, const void *values, cons
 
 /* The value side of pkm_backward: dw [T][H][k] float32 (OUT, overwritten),
  * dw = <dy[t], values[f]>, and the sparse update dvalues[f] += w * dy[t]
- * (ACCUMULATED, as in pkm_backward). */
+ * (ACCUMULATED, as in pkm_backward).  The picks are sorted by slot in the
+ * workspace, so each value row is read once per run of picks and most rows
+ * of dvalues are updated without atomics. */
 pkm_status_t pkm_backward_values(const pkm_problem_t *p, const void *values, const int32_t *idx,
-                                 const float *weights, const void *dy, float *dvalues,
-                                 float *dw, void *stream);
+                                 const float *weights, const void *dy, float *dvalues, float *dw,
+                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /* The query side of pkm_backward, from weights and dw: the softmax backward,
  * then dq and dkeys (both OUT, overwritten).  Each pick's ds reaches its left
  * sub-key i = f / n and its right sub-key j = f % n. */
 pkm_status_t pkm_backward_queries(const pkm_problem_t *p, const void *q, const void *keys,
                                   const int32_t *idx, const float *weights, const float *dw,
-                                  float *dq, float *dkeys, void *stream);
+                                  float *dq, float *dkeys, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *pkm_status_string(pkm_status_t s);

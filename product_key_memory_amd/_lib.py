@@ -64,8 +64,8 @@ def lib() -> ctypes.CDLL:
         PP = ctypes.POINTER(Problem)
         L.pkm_forward_select.argtypes = [PP, P, P, P, P, P, P]
         L.pkm_forward_gather.argtypes = [PP, P, P, P, P, P]
-        L.pkm_backward_values.argtypes = [PP, P, P, P, P, P, P, P]
-        L.pkm_backward_queries.argtypes = [PP, P, P, P, P, P, P, P, P]
+        L.pkm_backward_values.argtypes = [PP, P, P, P, P, P, P, P, c_size, P]
+        L.pkm_backward_queries.argtypes = [PP, P, P, P, P, P, P, P, P, c_size, P]
         for name in ("pkm_forward_select", "pkm_forward_gather", "pkm_backward_values",
                      "pkm_backward_queries"):
             getattr(L, name).restype = ctypes.c_int
@@ -102,9 +102,13 @@ def forward_gather(p: Problem, values, idx, weights, y, stream) -> int:
     return lib().pkm_forward_gather(ctypes.byref(p), values, idx, weights, y, stream)
 
 
-def backward_values(p: Problem, values, idx, weights, dy, dvalues, dw, stream) -> int:
-    return lib().pkm_backward_values(ctypes.byref(p), values, idx, weights, dy, dvalues, dw, stream)
+def backward_values(p: Problem, values, idx, weights, dy, dvalues, dw, ws, ws_bytes,
+                    stream) -> int:
+    return lib().pkm_backward_values(ctypes.byref(p), values, idx, weights, dy, dvalues, dw, ws,
+                                     ws_bytes, stream)
 
 
-def backward_queries(p: Problem, q, keys, idx, weights, dw, dq, dkeys, stream) -> int:
-    return lib().pkm_backward_queries(ctypes.byref(p), q, keys, idx, weights, dw, dq, dkeys, stream)
+def backward_queries(p: Problem, q, keys, idx, weights, dw, dq, dkeys, ws, ws_bytes,
+                     stream) -> int:
+    return lib().pkm_backward_queries(ctypes.byref(p), q, keys, idx, weights, dw, dq, dkeys, ws,
+                                      ws_bytes, stream)

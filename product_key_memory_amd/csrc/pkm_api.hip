@@ -31,15 +31,35 @@ pkm_status_t check_problem(const pkm_problem_t *p, bool backward)
         return PKM_ERR_SHAPE;
     if (backward && p->d_v > kMaxDvBackward)
         return PKM_ERR_SHAPE;
-    // grid limits: every launch keeps its x dimension below 2^31 blocks
-    if (p->T > ((int64_t)1 << 32) || p->T * p->H > ((int64_t)1 << 32))
+    // grid limits, and pick ids T*H*k held in int32 by the slot sort
+    if (p->T > ((int64_t)1 << 32) || p->T * p->H > ((int64_t)1 << 32) ||
+        p->T * p->H * p->k > (int64_t)INT32_MAX)
         return PKM_ERR_SHAPE;
     return PKM_OK;
 }
 
-size_t backward_ws(const pkm_problem_t *p) { return (size_t)(p->T * p->H * p->k) * sizeof(float); }
+size_t dw_bytes(const pkm_problem_t *p) { return pkm::align256((size_t)(p->T * p->H * p->k) * 4); }
 
-size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t stage_scratch_bytes(const pkm_problem_t *p)
+{
+    const size_t v = pkm::bwd_value_scratch(p->T, p->H, p->n, p->k).total;
+    const size_t q = pkm::bwd_query_scratch(p->T, p->H, p->n, p->k, p->d_k).total;
+    return v > q ? v : q;
+}
+
+// pkm_backward: dw first, the stages' scratch after it.
+size_t backward_bytes(const pkm_problem_t *p) { return dw_bytes(p) + stage_scratch_bytes(p); }
+
+pkm_status_t check_workspace(const pkm_problem_t *p, const void *ws, size_t have, size_t need)
+{
+    if (p->T == 0)
+        return PKM_OK;
+    if (!ws)
+        return PKM_ERR_NULL;
+    if (!aligned16(ws))
+        return PKM_ERR_ALIGN;
+    return have < need ? PKM_ERR_WORKSPACE : PKM_OK;
+}
 
 }  // namespace
 
@@ -49,69 +69,7 @@ size_t pkm_workspace_bytes(const pkm_problem_t *p, int backward)
 {
     if (check_problem(p, backward != 0) != PKM_OK)
         return (size_t)-1;
-    return backward ? round256(backward_ws(p)) : 0;
-}
-
-pkm_status_t pkm_forward(const pkm_problem_t *p, const void *q, const void *keys,
-                         const void *values, void *y, int32_t *idx, float *weights,
-                         float *scores, void *workspace, size_t workspace_bytes, void *stream)
-{
-    pkm_status_t st = check_problem(p, false);
-    if (st != PKM_OK)
-        return st;
-    (void)workspace;
-    (void)workspace_bytes;      // the forward pass needs no workspace
-    const int64_t T = p->T;
-    if (missing(q, T) || !keys || !values || missing(y, T) || missing(idx, T) || missing(weights, T))
-        return PKM_ERR_NULL;
-    if (!aligned16(q) || !aligned16(keys) || !aligned16(values) || !aligned16(y) ||
-        !aligned16(idx) || !aligned16(weights) || (scores && !aligned16(scores)))
-        return PKM_ERR_ALIGN;
-    if (p->T == 0)
-        return PKM_OK;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (pkm::launch_fwd_select(p->dtype, q, keys, p->T, p->H, p->n, p->k, p->d_k, idx, weights,
-                               scores, s) != hipSuccess)
-        return PKM_ERR_HIP;
-    if (pkm::launch_fwd_gather(p->dtype, values, idx, weights, y, p->T, p->H * p->k, p->d_v, s) !=
-        hipSuccess)
-        return PKM_ERR_HIP;
-    return PKM_OK;
-}
-
-pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *keys,
-                          const void *values, const int32_t *idx, const float *weights,
-                          const void *dy, float *dq, float *dkeys, float *dvalues,
-                          void *workspace, size_t workspace_bytes, void *stream)
-{
-    pkm_status_t st = check_problem(p, true);
-    if (st != PKM_OK)
-        return st;
-    const int64_t T = p->T;
-    if (missing(q, T) || !keys || !values || missing(idx, T) || missing(weights, T) ||
-        missing(dy, T) || missing(dq, T) || !dkeys || !dvalues)
-        return PKM_ERR_NULL;
-    if (!aligned16(q) || !aligned16(keys) || !aligned16(values) || !aligned16(idx) ||
-        !aligned16(weights) || !aligned16(dy) || !aligned16(dq) || !aligned16(dkeys) ||
-        !aligned16(dvalues) || (workspace && !aligned16(workspace)))
-        return PKM_ERR_ALIGN;
-    const size_t need = round256(backward_ws(p));
-    if (p->T > 0 && (!workspace || workspace_bytes < need))
-        return workspace ? PKM_ERR_WORKSPACE : PKM_ERR_NULL;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int64_t dkeys_count = (int64_t)p->H * 2 * p->n * (p->d_k / 2);
-    if (pkm::launch_zero_f32(dkeys, dkeys_count, s) != hipSuccess)
-        return PKM_ERR_HIP;
-    if (p->T == 0)
-        return PKM_OK;
-    float *dw = static_cast<float *>(workspace);
-    if (pkm::launch_bwd_value(p->dtype, values, idx, weights, dy, dvalues, dw, p->T, p->H, p->k,
-                              p->d_v, s) != hipSuccess)
-        return PKM_ERR_HIP;
-    if (pkm::launch_bwd_query(p->dtype, q, keys, idx, weights, dw, dq, dkeys, p->T, p->H, p->n,
-                              p->k, p->d_k, s) != hipSuccess)
-        return PKM_ERR_HIP;
-    return PKM_OK;
+    return backward ? backward_bytes(p) : 0;
 }
 
 pkm_status_t pkm_forward_select(const pkm_problem_t *p, const void *q, const void *keys,
@@ -126,7 +84,7 @@ pkm_status_t pkm_forward_select(const pkm_problem_t *p, const void *q, const voi
     if (!aligned16(q) || !aligned16(keys) || !aligned16(idx) || !aligned16(weights) ||
         (scores && !aligned16(scores)))
         return PKM_ERR_ALIGN;
-    if (p->T == 0)
+    if (T == 0)
         return PKM_OK;
     return pkm::launch_fwd_select(p->dtype, q, keys, p->T, p->H, p->n, p->k, p->d_k, idx, weights,
                                   scores, static_cast<hipStream_t>(stream)) == hipSuccess
@@ -145,7 +103,7 @@ pkm_status_t pkm_forward_gather(const pkm_problem_t *p, const void *values, cons
         return PKM_ERR_NULL;
     if (!aligned16(values) || !aligned16(idx) || !aligned16(weights) || !aligned16(y))
         return PKM_ERR_ALIGN;
-    if (p->T == 0)
+    if (T == 0)
         return PKM_OK;
     return pkm::launch_fwd_gather(p->dtype, values, idx, weights, y, p->T, p->H * p->k, p->d_v,
                                   static_cast<hipStream_t>(stream)) == hipSuccess
@@ -153,9 +111,31 @@ pkm_status_t pkm_forward_gather(const pkm_problem_t *p, const void *values, cons
                : PKM_ERR_HIP;
 }
 
+pkm_status_t pkm_forward(const pkm_problem_t *p, const void *q, const void *keys,
+                         const void *values, void *y, int32_t *idx, float *weights,
+                         float *scores, void *workspace, size_t workspace_bytes, void *stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;      // the forward pass needs no workspace
+    pkm_status_t st = check_problem(p, false);
+    if (st != PKM_OK)
+        return st;
+    const int64_t T = p->T;
+    if (missing(q, T) || !keys || !values || missing(y, T) || missing(idx, T) ||
+        missing(weights, T))
+        return PKM_ERR_NULL;
+    if (!aligned16(q) || !aligned16(keys) || !aligned16(values) || !aligned16(y) ||
+        !aligned16(idx) || !aligned16(weights) || (scores && !aligned16(scores)))
+        return PKM_ERR_ALIGN;
+    st = pkm_forward_select(p, q, keys, idx, weights, scores, stream);
+    if (st != PKM_OK)
+        return st;
+    return pkm_forward_gather(p, values, idx, weights, y, stream);
+}
+
 pkm_status_t pkm_backward_values(const pkm_problem_t *p, const void *values, const int32_t *idx,
-                                 const float *weights, const void *dy, float *dvalues,
-                                 float *dw, void *stream)
+                                 const float *weights, const void *dy, float *dvalues, float *dw,
+                                 void *workspace, size_t workspace_bytes, void *stream)
 {
     pkm_status_t st = check_problem(p, true);
     if (st != PKM_OK)
@@ -167,17 +147,21 @@ pkm_status_t pkm_backward_values(const pkm_problem_t *p, const void *values, con
     if (!aligned16(values) || !aligned16(idx) || !aligned16(weights) || !aligned16(dy) ||
         !aligned16(dvalues) || !aligned16(dw))
         return PKM_ERR_ALIGN;
-    if (p->T == 0)
-        return PKM_OK;
+    st = check_workspace(p, workspace, workspace_bytes,
+                         pkm::bwd_value_scratch(p->T, p->H, p->n, p->k).total);
+    if (st != PKM_OK || T == 0)
+        return st;
     return pkm::launch_bwd_value(p->dtype, values, idx, weights, dy, dvalues, dw, p->T, p->H,
-                                 p->k, p->d_v, static_cast<hipStream_t>(stream)) == hipSuccess
+                                 p->n, p->k, p->d_v, workspace,
+                                 static_cast<hipStream_t>(stream)) == hipSuccess
                ? PKM_OK
                : PKM_ERR_HIP;
 }
 
 pkm_status_t pkm_backward_queries(const pkm_problem_t *p, const void *q, const void *keys,
                                   const int32_t *idx, const float *weights, const float *dw,
-                                  float *dq, float *dkeys, void *stream)
+                                  float *dq, float *dkeys, void *workspace,
+                                  size_t workspace_bytes, void *stream)
 {
     pkm_status_t st = check_problem(p, true);
     if (st != PKM_OK)
@@ -189,15 +173,49 @@ pkm_status_t pkm_backward_queries(const pkm_problem_t *p, const void *q, const v
     if (!aligned16(q) || !aligned16(keys) || !aligned16(idx) || !aligned16(weights) ||
         !aligned16(dw) || !aligned16(dq) || !aligned16(dkeys))
         return PKM_ERR_ALIGN;
+    st = check_workspace(p, workspace, workspace_bytes,
+                         pkm::bwd_query_scratch(p->T, p->H, p->n, p->k, p->d_k).total);
+    if (st != PKM_OK)
+        return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (pkm::launch_zero_f32(dkeys, (int64_t)p->H * 2 * p->n * (p->d_k / 2), s) != hipSuccess)
-        return PKM_ERR_HIP;
-    if (p->T == 0)
-        return PKM_OK;
+    if (T == 0)
+        return pkm::launch_zero_f32(dkeys, (int64_t)p->H * 2 * p->n * (p->d_k / 2), s) == hipSuccess
+                   ? PKM_OK
+                   : PKM_ERR_HIP;
     return pkm::launch_bwd_query(p->dtype, q, keys, idx, weights, dw, dq, dkeys, p->T, p->H, p->n,
-                                 p->k, p->d_k, s) == hipSuccess
+                                 p->k, p->d_k, workspace, s) == hipSuccess
                ? PKM_OK
                : PKM_ERR_HIP;
+}
+
+pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *keys,
+                          const void *values, const int32_t *idx, const float *weights,
+                          const void *dy, float *dq, float *dkeys, float *dvalues,
+                          void *workspace, size_t workspace_bytes, void *stream)
+{
+    pkm_status_t st = check_problem(p, true);
+    if (st != PKM_OK)
+        return st;
+    const int64_t T = p->T;
+    if (missing(q, T) || !keys || !values || missing(idx, T) || missing(weights, T) ||
+        missing(dy, T) || missing(dq, T) || !dkeys || !dvalues)
+        return PKM_ERR_NULL;
+    if (!aligned16(q) || !aligned16(keys) || !aligned16(values) || !aligned16(idx) ||
+        !aligned16(weights) || !aligned16(dy) || !aligned16(dq) || !aligned16(dkeys) ||
+        !aligned16(dvalues))
+        return PKM_ERR_ALIGN;
+    st = check_workspace(p, workspace, workspace_bytes, backward_bytes(p));
+    if (st != PKM_OK)
+        return st;
+    float *dw = T > 0 ? static_cast<float *>(workspace) : nullptr;
+    void *scratch = T > 0 ? static_cast<char *>(workspace) + dw_bytes(p) : nullptr;
+    const size_t scratch_bytes = T > 0 ? workspace_bytes - dw_bytes(p) : 0;
+    st = pkm_backward_values(p, values, idx, weights, dy, dvalues, dw, scratch, scratch_bytes,
+                             stream);
+    if (st != PKM_OK)
+        return st;
+    return pkm_backward_queries(p, q, keys, idx, weights, dw, dq, dkeys, scratch, scratch_bytes,
+                                stream);
 }
 
 const char *pkm_status_string(pkm_status_t s)

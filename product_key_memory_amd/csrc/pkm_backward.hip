@@ -5,24 +5,32 @@
 // backward pass; gradient reaches the k selected scores of each head, and from
 // each score its left and right sub-key scores.
 //
-// bwd_value: one wave per token.  For each pick (h, r) the value row is
-//   re-read once and serves both  dw = <dy[t], values[f]>  and the sparse
-//   update  dvalues[f] += w * dy[t]  (float32 hardware atomics, lane-
-//   contiguous 256-byte bursts).  dw goes to [T][H][k].
-// bwd_query: one wave per (token, head), one lane per pick.  The softmax
-//   backward ds_r = w_r (dw_r - sum_r' w_r' dw_r') only matters summed over the
-//   picks S that share a sub-key i of one half; that sum is taken as
-//       g_i = A * (1 - W) - B * W,  A = sum_S w dw, W = sum_S w,
-//                                   B = sum_notS w dw, 1 - W = sum_notS w,
-//   with both complements summed directly, so a sub-key shared by most picks
-//   (its g is a near-cancelling sum) keeps full relative accuracy.  Then
-//   dq = sum_i g_i * sub-key row i  and  dkeys[i] += g_i * q_half  (atomics).
+// Value side (no float atomics on the value gradient in the common case):
+//   1. the T*H*k picks are counting-sorted by slot (histogram, scan, scatter);
+//   2. one wave per fixed chunk of the sorted picks walks its slot segments:
+//      the value row of a segment is read once, every pick p of it gives
+//      dw_p = <dy[t_p], values[f]>, and sum_p w_p dy[t_p] is added to
+//      dvalues[f] with a plain read-modify-write when the whole segment lies
+//      in the chunk (no other wave touches that row), with float atomics only
+//      for segments cut by a chunk boundary (this also spreads a hot slot
+//      over many waves).
+// Query side:
+//   3. one wave per (token, head), one lane per pick: the softmax backward
+//      ds_r = w_r (dw_r - sum_r' w_r' dw_r') matters only summed over the
+//      picks S sharing a sub-key i of one half, and that sum is taken as
+//          g_i = A * (1 - W) - B * W,  A = sum_S w dw, W = sum_S w,
+//                                      B = sum_notS w dw, 1 - W = sum_notS w,
+//      both complements summed directly, so a sub-key shared by most picks
+//      (a near-cancelling sum) keeps full relative accuracy;
+//      dq = sum_i g_i * sub-key row i, and (i, g_i) goes to a compact list;
+//   4. dkeys[h][s][i] = sum_t g * q_half[t]: each workgroup owns one token
+//      block and 64 columns of one codebook and accumulates the product of
+//      the sparse g matrix (densified per 32-token step in LDS) with q in
+//      MFMA registers; a last kernel sums the token blocks' partials.
 #include "pkm_device.hpp"
 #include "pkm_kernels.hpp"
 
 namespace pkm {
-
-constexpr int kBwdWaves = 4;
 
 template <typename DT>
 __device__ __forceinline__ float load_elem(const DT *p, int64_t i);
@@ -34,54 +42,185 @@ __device__ __forceinline__ float load_elem<bf16_t>(const bf16_t *p, int64_t i)
     return bf16_to_f32(reinterpret_cast<const uint16_t *>(p)[i]);
 }
 
-// MCH: 16-byte chunks per lane covering the whole row; U: picks in flight.
+// ---------------------------------------------------------------------------
+// 1. counting sort of the picks by slot
+// ---------------------------------------------------------------------------
+__global__ void slot_count_kernel(const int32_t *__restrict__ idx, int64_t picks,
+                                  int32_t *__restrict__ count)
+{
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p < picks)
+        atomicAdd(&count[idx[p]], 1);
+}
+
+constexpr int kScanBlock = 1024;     // counts per scan block (256 threads x 4)
+
+__global__ __launch_bounds__(256) void scan_block_sums_kernel(const int32_t *__restrict__ count,
+                                                              int64_t slots,
+                                                              int32_t *__restrict__ block_sums)
+{
+    __shared__ int32_t part[4];
+    const int64_t base = (int64_t)blockIdx.x * kScanBlock;
+    int v = 0;
+    for (int i = threadIdx.x; i < kScanBlock; i += 256)
+        if (base + i < slots)
+            v += count[base + i];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v += __shfl_xor(v, m);
+    if (lane_id() == 0)
+        part[threadIdx.x / kWave] = v;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        block_sums[blockIdx.x] = part[0] + part[1] + part[2] + part[3];
+}
+
+// start[f] = number of picks with slot < f (f = 0..slots), cursor = copy.
+__global__ __launch_bounds__(256) void scan_apply_kernel(const int32_t *__restrict__ count,
+                                                         const int32_t *__restrict__ block_sums,
+                                                         int64_t slots, int32_t *__restrict__ start,
+                                                         int32_t *__restrict__ cursor)
+{
+    __shared__ int32_t wsum[4];
+    __shared__ int32_t offset_sh;
+    const int64_t base = (int64_t)blockIdx.x * kScanBlock;
+    // offset of this block = sum of the earlier block sums
+    int pre = 0;
+    for (int b = threadIdx.x; b < (int)blockIdx.x; b += 256)
+        pre += block_sums[b];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        pre += __shfl_xor(pre, m);
+    if (lane_id() == 0)
+        wsum[threadIdx.x / kWave] = pre;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        offset_sh = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    const int offset = offset_sh;
+    __syncthreads();
+
+    // thread i owns counts [base + 4i, base + 4i + 4)
+    int c[4];
+    int local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t f = base + 4 * threadIdx.x + j;
+        c[j] = f < slots ? count[f] : 0;
+        local += c[j];
+    }
+    int total_w;
+    const int excl_w = wave_exclusive_scan(local, &total_w);
+    if (lane_id() == 0)
+        wsum[threadIdx.x / kWave] = total_w;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < (int)(threadIdx.x / kWave); ++w)
+        before += wsum[w];
+    int run = offset + before + excl_w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t f = base + 4 * threadIdx.x + j;
+        if (f < slots) {
+            start[f] = run;
+            cursor[f] = run;
+        }
+        run += c[j];
+    }
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 255)
+        start[slots] = run;
+}
+
+__global__ void slot_fill_kernel(const int32_t *__restrict__ idx, int64_t picks,
+                                 int32_t *__restrict__ cursor, int32_t *__restrict__ order)
+{
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p < picks)
+        order[atomicAdd(&cursor[idx[p]], 1)] = (int32_t)p;
+}
+
+// ---------------------------------------------------------------------------
+// 2. segmented reduction over the slot-sorted picks
+// ---------------------------------------------------------------------------
+constexpr int kSegWaves = 4;
+
+// MCH: 16-byte chunks of a row per lane; U: picks in flight per wave.  Each
+// wave first stages the (pick, slot, weight) of its chunk in LDS, so inside
+// the loop a dy row address is one LDS read away; a segment's value row and
+// (when the wave owns the whole segment) its dvalues row are fetched together
+// before the first dy rows.
 template <typename DT, int MCH, int U>
-__global__ __launch_bounds__(kBwdWaves *kWave) void bwd_value_kernel(
-    const DT *__restrict__ values, const int32_t *__restrict__ idx,
-    const float *__restrict__ weights, const DT *__restrict__ dy, float *__restrict__ dvalues,
-    float *__restrict__ dw, int64_t T, int H, int k, int d_v)
+__global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
+    const DT *__restrict__ values, const DT *__restrict__ dy, const int32_t *__restrict__ idx,
+    const float *__restrict__ weights, const int32_t *__restrict__ order,
+    const int32_t *__restrict__ start, float *__restrict__ dvalues, float *__restrict__ dw,
+    int64_t picks, int HK, int d_v)
 {
     constexpr int EPC = Elt<DT>::per16;
-    constexpr int NI = MCH * EPC;          // interleaved dy elements per lane (>= d_v / 64)
+    __shared__ int32_t s_pk[kSegWaves][kSegChunk];
+    __shared__ int32_t s_slot[kSegWaves][kSegChunk];
+    __shared__ float s_w[kSegWaves][kSegChunk];
     const int lane = lane_id();
-    const int64_t t = (int64_t)blockIdx.x * kBwdWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    if (t >= T)
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t p_begin = ((int64_t)blockIdx.x * kSegWaves + wv) * kSegChunk;
+    if (p_begin >= picks)
         return;
+    const int len = (int)(picks - p_begin < kSegChunk ? picks - p_begin : kSegChunk);
     const int nchunks = d_v / EPC;
 
-    // dy[t] twice: 16-byte chunk layout for the dot products, and lane-interleaved
-    // (element lane + 64*j) for contiguous atomics.
-    float dyc[MCH][EPC];
-    const uint4 *dyrow = reinterpret_cast<const uint4 *>(dy + t * d_v);
-#pragma unroll
-    for (int m = 0; m < MCH; ++m) {
-        const int c = lane + m * kWave;
-        unpack16(c < nchunks ? dyrow[c] : make_uint4(0u, 0u, 0u, 0u), dyc[m]);
+    for (int j = lane; j < len; j += kWave) {
+        const int32_t pk = order[p_begin + j];
+        s_pk[wv][j] = pk;
+        s_slot[wv][j] = idx[pk];
+        s_w[wv][j] = weights[pk];
     }
-    float dyi[NI];
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-        const int x = lane + j * kWave;
-        dyi[j] = x < d_v ? load_elem(dy, t * d_v + x) : 0.f;
-    }
+    wave_lds_sync();
 
-    for (int h = 0; h < H; ++h) {
-        const int64_t base = (t * H + h) * (int64_t)k;
-        float dw_mine = 0.f;                 // lane r keeps dw of pick r
-        for (int r0 = 0; r0 < k; r0 += U) {
+    int pos = 0;
+    while (pos < len) {
+        const int f = __builtin_amdgcn_readfirstlane(s_slot[wv][pos]);
+        const int64_t seg_begin = start[f], seg_end = start[f + 1];
+        const int stop = (int)(seg_end - p_begin < len ? seg_end - p_begin : len);
+        const bool exclusive = seg_begin >= p_begin && seg_end <= p_begin + len;
+
+        uint4 vraw[MCH];
+        float4 dold[MCH][EPC / 4];
+        const uint4 *vsrc = reinterpret_cast<const uint4 *>(values + (int64_t)f * d_v);
+        float *drow = dvalues + (int64_t)f * d_v;
+#pragma unroll
+        for (int m = 0; m < MCH; ++m) {
+            const int c = lane + m * kWave;
+            vraw[m] = c < nchunks ? vsrc[c] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int e = 0; e < EPC / 4; ++e)
+                dold[m][e] = (exclusive && c < nchunks)
+                                 ? *reinterpret_cast<const float4 *>(drow + (int64_t)c * EPC + 4 * e)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        float vrow[MCH][EPC], acc[MCH][EPC];
+#pragma unroll
+        for (int m = 0; m < MCH; ++m) {
+            unpack16(vraw[m], vrow[m]);
+#pragma unroll
+            for (int e = 0; e < EPC; ++e)
+                acc[m][e] = 0.f;
+        }
+
+        for (int j = pos; j < stop; j += U) {
             uint4 buf[U][MCH];
-            int64_t f[U];
-            float w[U];
+            float wv_u[U];
+            int32_t pk[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const bool live = r0 + u < k;
-                f[u] = live ? idx[base + r0 + u] : 0;
-                w[u] = live ? weights[base + r0 + u] : 0.f;
-                const uint4 *row = reinterpret_cast<const uint4 *>(values + f[u] * d_v);
+                const bool live = j + u < stop;
+                pk[u] = live ? __builtin_amdgcn_readfirstlane(s_pk[wv][j + u]) : 0;
+                wv_u[u] = live ? s_w[wv][j + u] : 0.f;
+                const int64_t t = pk[u] / HK;
+                const uint4 *drow_in = reinterpret_cast<const uint4 *>(dy + t * d_v);
 #pragma unroll
                 for (int m = 0; m < MCH; ++m) {
                     const int c = lane + m * kWave;
-                    buf[u][m] = (live && c < nchunks) ? row[c] : make_uint4(0u, 0u, 0u, 0u);
+                    buf[u][m] = (live && c < nchunks) ? drow_in[c] : make_uint4(0u, 0u, 0u, 0u);
                 }
             }
 #pragma unroll
@@ -89,87 +228,63 @@ __global__ __launch_bounds__(kBwdWaves *kWave) void bwd_value_kernel(
                 float part = 0.f;
 #pragma unroll
                 for (int m = 0; m < MCH; ++m) {
-                    float v[EPC];
-                    unpack16(buf[u][m], v);
+                    float g[EPC];
+                    unpack16(buf[u][m], g);
 #pragma unroll
-                    for (int e = 0; e < EPC; ++e)
-                        part = fmaf(v[e], dyc[m][e], part);
+                    for (int e = 0; e < EPC; ++e) {
+                        part = fmaf(vrow[m][e], g[e], part);
+                        acc[m][e] = fmaf(wv_u[u], g[e], acc[m][e]);
+                    }
                 }
                 const float dot = wave_sum(part);
-                if (lane == r0 + u)
-                    dw_mine = dot;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (r0 + u >= k)
-                    break;
-                float *drow = dvalues + f[u] * d_v;
-#pragma unroll
-                for (int j = 0; j < NI; ++j) {
-                    const int x = lane + j * kWave;
-                    if (x < d_v)
-                        __hip_atomic_fetch_add(drow + x, w[u] * dyi[j], __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-                }
+                if (j + u < stop && lane == 0)
+                    dw[pk[u]] = dot;
             }
         }
-        if (lane < k)
-            dw[base + lane] = dw_mine;
+
+#pragma unroll
+        for (int m = 0; m < MCH; ++m) {
+            const int c = lane + m * kWave;
+            if (c >= nchunks)
+                continue;
+            float *dst = drow + (int64_t)c * EPC;
+            if (exclusive) {
+#pragma unroll
+                for (int e = 0; e < EPC / 4; ++e) {
+                    float4 o = dold[m][e];
+                    o.x += acc[m][4 * e];
+                    o.y += acc[m][4 * e + 1];
+                    o.z += acc[m][4 * e + 2];
+                    o.w += acc[m][4 * e + 3];
+                    *reinterpret_cast<float4 *>(dst + 4 * e) = o;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < EPC; ++e)
+                    __hip_atomic_fetch_add(dst + e, acc[m][e], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        pos = stop;
     }
 }
 
-template <typename DT, int MCH, int U>
-static hipError_t launch_bwd_value_t(const void *values, const int32_t *idx, const float *weights,
-                                     const void *dy, float *dvalues, float *dw, int64_t T, int H,
-                                     int k, int d_v, hipStream_t stream)
-{
-    const dim3 grid((unsigned)((T + kBwdWaves - 1) / kBwdWaves));
-    hipLaunchKernelGGL((bwd_value_kernel<DT, MCH, U>), grid, dim3(kBwdWaves * kWave), 0, stream,
-                       static_cast<const DT *>(values), idx, weights,
-                       static_cast<const DT *>(dy), dvalues, dw, T, H, k, d_v);
-    return hipGetLastError();
-}
-
-template <typename DT>
-static hipError_t launch_bwd_value_dt(const void *values, const int32_t *idx, const float *weights,
-                                      const void *dy, float *dvalues, float *dw, int64_t T, int H,
-                                      int k, int d_v, hipStream_t stream)
-{
-    const int per_lane = (d_v / Elt<DT>::per16 + kWave - 1) / kWave;
-    if (per_lane <= 1)
-        return launch_bwd_value_t<DT, 1, 8>(values, idx, weights, dy, dvalues, dw, T, H, k, d_v, stream);
-    if (per_lane <= 2)
-        return launch_bwd_value_t<DT, 2, 4>(values, idx, weights, dy, dvalues, dw, T, H, k, d_v, stream);
-    if (per_lane <= 4)
-        return launch_bwd_value_t<DT, 4, 2>(values, idx, weights, dy, dvalues, dw, T, H, k, d_v, stream);
-    if (per_lane <= 8)
-        return launch_bwd_value_t<DT, 8, 1>(values, idx, weights, dy, dvalues, dw, T, H, k, d_v, stream);
-    return launch_bwd_value_t<DT, 16, 1>(values, idx, weights, dy, dvalues, dw, T, H, k, d_v, stream);
-}
-
-hipError_t launch_bwd_value(int dtype, const void *values, const int32_t *idx,
-                            const float *weights, const void *dy, float *dvalues, float *dw,
-                            int64_t T, int H, int k, int d_v, hipStream_t stream)
-{
-    if (dtype == 1)
-        return launch_bwd_value_dt<bf16_t>(values, idx, weights, dy, dvalues, dw, T, H, k, d_v, stream);
-    return launch_bwd_value_dt<float>(values, idx, weights, dy, dvalues, dw, T, H, k, d_v, stream);
-}
-
 // ---------------------------------------------------------------------------
+// 3. softmax backward per distinct sub-key, dq, compact (i, g) lists
+// ---------------------------------------------------------------------------
+constexpr int kQryWaves = 4;
 constexpr int kMaxHalfPerLane = 8;   // half <= 512
 
 template <typename DT>
-__global__ __launch_bounds__(kBwdWaves *kWave) void bwd_query_kernel(
-    const DT *__restrict__ q, const DT *__restrict__ keys, const int32_t *__restrict__ idx,
+__global__ __launch_bounds__(kQryWaves *kWave) void bwd_query_kernel(
+    const DT *__restrict__ keys, const int32_t *__restrict__ idx,
     const float *__restrict__ weights, const float *__restrict__ dw, float *__restrict__ dq,
-    float *__restrict__ dkeys, int64_t T, int H, int n, int k, int d_k)
+    int32_t *__restrict__ gl_i, float *__restrict__ gl_g, int64_t T, int H, int n, int k, int d_k)
 {
     const int lane = lane_id();
-    const int64_t row = (int64_t)blockIdx.x * kBwdWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t row = (int64_t)blockIdx.x * kQryWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (row >= T * H)
         return;
-    const int64_t t = row / H;
     const int h = (int)(row % H);
     const int half = d_k / 2;
     const int64_t base = row * (int64_t)k;
@@ -198,16 +313,17 @@ __global__ __launch_bounds__(kBwdWaves *kWave) void bwd_query_kernel(
             }
         }
         const float g = A * Wc - B * W;
-        const DT *qh = q + row * (int64_t)d_k + (int64_t)s * half;
-        const DT *kb = keys + ((int64_t)h * 2 + s) * (int64_t)n * half;
-        float *dkb = dkeys + ((int64_t)h * 2 + s) * (int64_t)n * half;
-        float qv[kMaxHalfPerLane], acc[kMaxHalfPerLane];
-#pragma unroll
-        for (int j = 0; j < kMaxHalfPerLane; ++j) {
-            const int c = lane + j * kWave;
-            qv[j] = c < half ? load_elem(qh, c) : 0.f;
-            acc[j] = 0.f;
+        const int64_t lbase = (row * 2 + s) * (int64_t)k;
+        if (lane < k) {
+            gl_i[lbase + lane] = sub;
+            gl_g[lbase + lane] = first ? g : 0.f;
         }
+
+        const DT *kb = keys + ((int64_t)h * 2 + s) * (int64_t)n * half;
+        float acc[kMaxHalfPerLane];
+#pragma unroll
+        for (int j = 0; j < kMaxHalfPerLane; ++j)
+            acc[j] = 0.f;
         uint64_t todo = __ballot(first);
         while (todo) {
             const int r = __builtin_ctzll(todo);
@@ -215,15 +331,11 @@ __global__ __launch_bounds__(kBwdWaves *kWave) void bwd_query_kernel(
             const int sub_r = __shfl(sub, r);
             const float g_r = __shfl(g, r);
             const DT *krow = kb + (int64_t)sub_r * half;
-            float *dkrow = dkb + (int64_t)sub_r * half;
 #pragma unroll
             for (int j = 0; j < kMaxHalfPerLane; ++j) {
                 const int c = lane + j * kWave;
-                if (c < half) {
+                if (c < half)
                     acc[j] = fmaf(g_r, load_elem(krow, c), acc[j]);
-                    __hip_atomic_fetch_add(dkrow + c, g_r * qv[j], __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-                }
             }
         }
         float *dqh = dq + row * (int64_t)d_k + (int64_t)s * half;
@@ -236,27 +348,321 @@ __global__ __launch_bounds__(kBwdWaves *kWave) void bwd_query_kernel(
     }
 }
 
-template <typename DT>
-static hipError_t launch_bwd_query_t(const void *q, const void *keys, const int32_t *idx,
-                                     const float *weights, const float *dw, float *dq,
-                                     float *dkeys, int64_t T, int H, int n, int k, int d_k,
-                                     hipStream_t stream)
+// ---------------------------------------------------------------------------
+// 4. sub-key gradient as a dense MFMA product over token steps
+// ---------------------------------------------------------------------------
+// dkeys[h][s] = dS^T q_s, where dS [T][n] holds, per token, the g of each
+// distinct sub-key of its k picks and zeros elsewhere.  A workgroup owns one
+// token block and 64 columns of one codebook; per step of 32 tokens it
+// scatters the (sub-key, g) entries into a zeroed LDS tile dS^T [n][32] (no
+// two entries share a cell, so plain stores), stages q's 64 columns
+// transposed [64][32], and accumulates [n][64] in MFMA registers: wave w owns
+// the 16-row tiles w, w+16, ...  No atomics, so hot sub-keys cost nothing
+// extra and the result does not depend on timing.
+//   bf16 storage: g = hi + lo (two bfloat16, ~16 significant bits), q exact in
+//     bfloat16, v_mfma_f32_16x16x32_bf16 twice per tile: exact products,
+//     float32 sums;
+//   float32 storage: v_mfma_f32_16x16x4_f32 on the float32 values.
+constexpr int kDkWaves = 16;
+constexpr int kDkTok = 32;          // tokens per step (the MFMA K extent)
+constexpr int kDkCols = 64;         // columns per workgroup (4 MFMA N blocks)
+constexpr int kDkMaxTiles = 4;      // 16-row tiles per wave: n <= 16 * 16 * 4
+
+template <typename DT> struct DkTile;
+template <> struct DkTile<bf16_t> { typedef uint16_t elt; static constexpr int parts = 2; };
+template <> struct DkTile<float> { typedef float elt; static constexpr int parts = 1; };
+
+__device__ __forceinline__ floatx4 dk_mfma(const uint16_t *a_row, const uint16_t *b_row, int kg,
+                                           floatx4 acc)
 {
+    const uint4 a = *reinterpret_cast<const uint4 *>(a_row + 8 * kg);
+    const uint4 b = *reinterpret_cast<const uint4 *>(b_row + 8 * kg);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 dk_mfma(const float *a_row, const float *b_row, int kg,
+                                           floatx4 acc)
+{
+    // K = 32 tokens as 2 x 4 consecutive per lane group; A and B share the order
+#pragma unroll
+    for (int half_k = 0; half_k < 2; ++half_k) {
+        const float4 a = *reinterpret_cast<const float4 *>(a_row + 16 * half_k + 4 * kg);
+        const float4 b = *reinterpret_cast<const float4 *>(b_row + 16 * half_k + 4 * kg);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ void dk_store(uint16_t *hi, uint16_t *lo, size_t at, float g)
+{
+    const uint32_t h = f32_to_bf16_bits(g);
+    hi[at] = (uint16_t)h;
+    lo[at] = (uint16_t)f32_to_bf16_bits(g - bf16_to_f32(h));
+}
+__device__ __forceinline__ void dk_store(float *a, float *, size_t at, float g) { a[at] = g; }
+__device__ __forceinline__ void dk_clear(uint16_t *hi, uint16_t *lo, size_t at)
+{
+    hi[at] = 0;
+    lo[at] = 0;
+}
+__device__ __forceinline__ void dk_clear(float *a, float *, size_t at) { a[at] = 0.f; }
+__device__ __forceinline__ uint16_t dk_q(const bf16_t *q, int64_t i)
+{
+    return reinterpret_cast<const uint16_t *>(q)[i];
+}
+__device__ __forceinline__ float dk_q(const float *q, int64_t i) { return q[i]; }
+
+template <typename DT>
+__global__ __launch_bounds__(kDkWaves *kWave) void dkeys_mfma_kernel(
+    const DT *__restrict__ q, const int32_t *__restrict__ gl_i, const float *__restrict__ gl_g,
+    float *__restrict__ partial, int64_t T, int H, int n, int k, int d_k, int tokens_per_block)
+{
+    typedef typename DkTile<DT>::elt E;
+    constexpr int PARTS = DkTile<DT>::parts;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int n_pad = (n + 15) & ~15;
+    E *a_hi = reinterpret_cast<E *>(smem);                      // [n_pad][32]
+    E *a_lo = a_hi + (PARTS == 2 ? (size_t)n_pad * kDkTok : 0);  // [n_pad][32] (bf16 only)
+    E *bt = a_hi + (size_t)PARTS * n_pad * kDkTok;                // [64][32]
+
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int tid = threadIdx.x;
+    const int half = d_k / 2;
+    const int ncb = (half + kDkCols - 1) / kDkCols;
+    const int hs = blockIdx.y / ncb;
+    const int c0 = (blockIdx.y % ncb) * kDkCols;
+    const int width = half - c0 < kDkCols ? half - c0 : kDkCols;
+    const int h = hs / 2, s = hs % 2;
+    const int ntiles = n_pad / 16;
+
+    for (size_t e = tid; e < (size_t)(PARTS * n_pad + kDkCols) * kDkTok; e += kDkWaves * kWave)
+        a_hi[e] = (E)0;
+
+    floatx4 acc[kDkMaxTiles][4];
+#pragma unroll
+    for (int ti = 0; ti < kDkMaxTiles; ++ti)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+            acc[ti][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t t_begin = (int64_t)blockIdx.x * tokens_per_block;
+    const int64_t t_end = t_begin + tokens_per_block < T ? t_begin + tokens_per_block : T;
+    const int pairs = kDkTok * k;                 // (token, pick) pairs per step, <= 2048
+    int mine_at[2] = {-1, -1};                    // cells this thread wrote
+    __syncthreads();
+
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += kDkTok) {
+        // scatter the step's entries into dS^T, stage q^T
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int pr = tid + j * kDkWaves * kWave;
+            mine_at[j] = -1;
+            if (pr < pairs) {
+                const int tl = pr / k, r = pr % k;
+                const int64_t t = t0 + tl;
+                if (t < t_end) {
+                    const int64_t at = ((t * H + h) * 2 + s) * (int64_t)k + r;
+                    const float g = gl_g[at];
+                    if (g != 0.f) {
+                        const int cell = gl_i[at] * kDkTok + tl;
+                        dk_store(a_hi, a_lo, cell, g);
+                        mine_at[j] = cell;
+                    }
+                }
+            }
+            const int qe = tid + j * kDkWaves * kWave;      // 2048 = 64 columns x 32 tokens
+            const int d = qe % kDkCols, tl = qe / kDkCols;
+            const int64_t t = t0 + tl;
+            E v = (E)0;
+            if (d < width && t < t_end)
+                v = dk_q(q, (t * H + h) * (int64_t)d_k + (int64_t)s * half + c0 + d);
+            bt[d * kDkTok + tl] = v;
+        }
+        __syncthreads();
+
+        const int r16 = lane & 15, kg = lane >> 4;
+#pragma unroll
+        for (int ti = 0; ti < kDkMaxTiles; ++ti) {
+            const int tile = wave + ti * kDkWaves;
+            if (tile < ntiles) {
+                const E *arow_hi = a_hi + (size_t)(tile * 16 + r16) * kDkTok;
+                const E *arow_lo = a_lo + (size_t)(tile * 16 + r16) * kDkTok;
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    const E *brow = bt + (size_t)(nb * 16 + r16) * kDkTok;
+                    acc[ti][nb] = dk_mfma(arow_hi, brow, kg, acc[ti][nb]);
+                    if constexpr (PARTS == 2)
+                        acc[ti][nb] = dk_mfma(arow_lo, brow, kg, acc[ti][nb]);
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if (mine_at[j] >= 0)
+                dk_clear(a_hi, a_lo, mine_at[j]);
+        __syncthreads();
+    }
+
+    // partial[block][h][s][row][c0 + col]; lane holds rows 4*(l/16)+i, column l%16
+    float *dst = partial + ((int64_t)blockIdx.x * H * 2 + hs) * (int64_t)n * half + c0;
+#pragma unroll
+    for (int ti = 0; ti < kDkMaxTiles; ++ti) {
+        const int tile = wave + ti * kDkWaves;
+        if (tile >= ntiles)
+            continue;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int col = nb * 16 + (lane & 15);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = tile * 16 + 4 * (lane >> 4) + i;
+                if (row < n && col < width)
+                    dst[(int64_t)row * half + col] = acc[ti][nb][i];
+            }
+        }
+    }
+}
+
+__global__ void dkeys_reduce_kernel(const float *__restrict__ partial, int blocks, int64_t count,
+                                    float *__restrict__ dkeys)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < count; e += stride) {
+        float acc = 0.f;
+        for (int b = 0; b < blocks; ++b)
+            acc += partial[(int64_t)b * count + e];
+        dkeys[e] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+static unsigned grid1d(int64_t n, int per)
+{
+    return (unsigned)((n + per - 1) / per);
+}
+
+template <typename DT, int MCH, int U>
+static hipError_t launch_seg_t(const void *values, const void *dy, const int32_t *idx,
+                               const float *weights, const int32_t *order, const int32_t *start,
+                               float *dvalues, float *dw, int64_t picks, int HK, int d_v,
+                               hipStream_t stream)
+{
+    const int64_t waves = (picks + kSegChunk - 1) / kSegChunk;
+    hipLaunchKernelGGL((seg_value_kernel<DT, MCH, U>), dim3(grid1d(waves, kSegWaves)),
+                       dim3(kSegWaves * kWave), 0, stream, static_cast<const DT *>(values),
+                       static_cast<const DT *>(dy), idx, weights, order, start, dvalues, dw, picks,
+                       HK, d_v);
+    return hipGetLastError();
+}
+
+template <typename DT>
+static hipError_t launch_seg_dt(const void *values, const void *dy, const int32_t *idx,
+                                const float *weights, const int32_t *order, const int32_t *start,
+                                float *dvalues, float *dw, int64_t picks, int HK, int d_v,
+                                hipStream_t stream)
+{
+    const int per_lane = (d_v / Elt<DT>::per16 + kWave - 1) / kWave;
+    if (per_lane <= 1)
+        return launch_seg_t<DT, 1, 8>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, stream);
+    if (per_lane <= 2)
+        return launch_seg_t<DT, 2, 8>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, stream);
+    if (per_lane <= 4)
+        return launch_seg_t<DT, 4, 2>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, stream);
+    if (per_lane <= 8 || sizeof(DT) == 2)       // bf16 rows of <= 4096 fit 8 chunks per lane
+        return launch_seg_t<DT, 8, 1>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, stream);
+    if constexpr (sizeof(DT) == 4)
+        return launch_seg_t<DT, 16, 1>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_value(int dtype, const void *values, const int32_t *idx,
+                            const float *weights, const void *dy, float *dvalues, float *dw,
+                            int64_t T, int H, int n, int k, int d_v, void *scratch,
+                            hipStream_t stream)
+{
+    const BwdValueScratch S = bwd_value_scratch(T, H, n, k);
+    char *base = static_cast<char *>(scratch);
+    int32_t *count = reinterpret_cast<int32_t *>(base + S.off_count);
+    int32_t *start = reinterpret_cast<int32_t *>(base + S.off_start);
+    int32_t *cursor = reinterpret_cast<int32_t *>(base + S.off_cursor);
+    int32_t *bsums = reinterpret_cast<int32_t *>(base + S.off_bsums);
+    int32_t *order = reinterpret_cast<int32_t *>(base + S.off_order);
+    const int64_t slots = (int64_t)n * n;
+    const int64_t picks = T * H * (int64_t)k;
+    hipError_t err = launch_zero_f32(reinterpret_cast<float *>(count), slots, stream);
+    if (err != hipSuccess)
+        return err;
+    hipLaunchKernelGGL(slot_count_kernel, dim3(grid1d(picks, 256)), dim3(256), 0, stream, idx,
+                       picks, count);
+    const unsigned sblocks = grid1d(slots, kScanBlock);
+    hipLaunchKernelGGL(scan_block_sums_kernel, dim3(sblocks), dim3(256), 0, stream, count, slots,
+                       bsums);
+    hipLaunchKernelGGL(scan_apply_kernel, dim3(sblocks), dim3(256), 0, stream, count, bsums,
+                       slots, start, cursor);
+    hipLaunchKernelGGL(slot_fill_kernel, dim3(grid1d(picks, 256)), dim3(256), 0, stream, idx,
+                       picks, cursor, order);
+    if ((err = hipGetLastError()) != hipSuccess)
+        return err;
+    if (dtype == 1)
+        return launch_seg_dt<bf16_t>(values, dy, idx, weights, order, start, dvalues, dw, picks,
+                                     H * k, d_v, stream);
+    return launch_seg_dt<float>(values, dy, idx, weights, order, start, dvalues, dw, picks, H * k,
+                                d_v, stream);
+}
+
+template <typename DT>
+static hipError_t launch_query_t(const void *q, const void *keys, const int32_t *idx,
+                                 const float *weights, const float *dw, float *dq, float *dkeys,
+                                 int64_t T, int H, int n, int k, int d_k, void *scratch,
+                                 hipStream_t stream)
+{
+    const BwdQueryScratch S = bwd_query_scratch(T, H, n, k, d_k);
+    char *base = static_cast<char *>(scratch);
+    int32_t *gl_i = reinterpret_cast<int32_t *>(base + S.off_gl_i);
+    float *gl_g = reinterpret_cast<float *>(base + S.off_gl_g);
+    float *partial = reinterpret_cast<float *>(base + S.off_partial);
     const int64_t rows = T * H;
-    const dim3 grid((unsigned)((rows + kBwdWaves - 1) / kBwdWaves));
-    hipLaunchKernelGGL(bwd_query_kernel<DT>, grid, dim3(kBwdWaves * kWave), 0, stream,
-                       static_cast<const DT *>(q), static_cast<const DT *>(keys), idx, weights,
-                       dw, dq, dkeys, T, H, n, k, d_k);
+    hipLaunchKernelGGL(bwd_query_kernel<DT>, dim3(grid1d(rows, kQryWaves)),
+                       dim3(kQryWaves * kWave), 0, stream, static_cast<const DT *>(keys), idx,
+                       weights, dw, dq, gl_i, gl_g, T, H, n, k, d_k);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    const int n_pad = (n + 15) & ~15;
+    const size_t lds = ((size_t)DkTile<DT>::parts * n_pad + kDkCols) * kDkTok * sizeof(typename DkTile<DT>::elt);
+    err = hipFuncSetAttribute(reinterpret_cast<const void *>(&dkeys_mfma_kernel<DT>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess)
+        return err;
+    const int half = d_k / 2;
+    const int ncb = (half + kDkCols - 1) / kDkCols;
+    hipLaunchKernelGGL(dkeys_mfma_kernel<DT>, dim3((unsigned)S.blocks, (unsigned)(H * 2 * ncb)),
+                       dim3(kDkWaves * kWave), lds, stream, static_cast<const DT *>(q), gl_i, gl_g,
+                       partial, T, H, n, k, d_k, S.tokens_per_block);
+    const int64_t count = (int64_t)H * 2 * n * half;
+    const int64_t rblocks = grid1d(count, 256);
+    hipLaunchKernelGGL(dkeys_reduce_kernel, dim3((unsigned)(rblocks < 8192 ? rblocks : 8192)),
+                       dim3(256), 0, stream, partial, S.blocks, count, dkeys);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_query(int dtype, const void *q, const void *keys, const int32_t *idx,
                             const float *weights, const float *dw, float *dq, float *dkeys,
-                            int64_t T, int H, int n, int k, int d_k, hipStream_t stream)
+                            int64_t T, int H, int n, int k, int d_k, void *scratch,
+                            hipStream_t stream)
 {
     if (dtype == 1)
-        return launch_bwd_query_t<bf16_t>(q, keys, idx, weights, dw, dq, dkeys, T, H, n, k, d_k, stream);
-    return launch_bwd_query_t<float>(q, keys, idx, weights, dw, dq, dkeys, T, H, n, k, d_k, stream);
+        return launch_query_t<bf16_t>(q, keys, idx, weights, dw, dq, dkeys, T, H, n, k, d_k,
+                                      scratch, stream);
+    return launch_query_t<float>(q, keys, idx, weights, dw, dq, dkeys, T, H, n, k, d_k, scratch,
+                                 stream);
 }
 
 // ---------------------------------------------------------------------------

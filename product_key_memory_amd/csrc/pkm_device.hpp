@@ -111,6 +111,14 @@ __device__ __forceinline__ int wave_exclusive_scan(int v, int *total)
     return inc - v;
 }
 
+// Make this wave's LDS stores visible to its own later LDS loads.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Bitonic sort, descending, of 64 floats (one per lane).  Lane i ends with
 // the i-th largest.
 __device__ __forceinline__ float wave_sort64_desc(float v)

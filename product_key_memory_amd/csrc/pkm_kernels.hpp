@@ -20,17 +20,74 @@ hipError_t launch_fwd_gather(int dtype, const void *values, const int32_t *idx,
                              const float *weights, void *y, int64_t T, int HK, int d_v,
                              hipStream_t stream);
 
-// dw = <dy, values[slot]> written to `dw` [T][H][k]; dvalues[slot] += w * dy
-// (atomics).
+// ---- backward scratch layouts (byte offsets inside the caller's workspace) ----
+constexpr int kSegChunk = 256;      // sorted picks per wave in the value segmented reduction
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BwdValueScratch {
+    size_t off_count, off_start, off_cursor, off_bsums, off_order, total;
+};
+
+inline BwdValueScratch bwd_value_scratch(int64_t T, int H, int n, int k)
+{
+    const size_t slots = (size_t)n * n, picks = (size_t)T * H * k;
+    const size_t sblocks = (slots + 1023) / 1024;
+    BwdValueScratch S;
+    S.off_count = 0;
+    S.off_start = align256(S.off_count + slots * 4);
+    S.off_cursor = align256(S.off_start + (slots + 1) * 4);
+    S.off_bsums = align256(S.off_cursor + slots * 4);
+    S.off_order = align256(S.off_bsums + sblocks * 4);
+    S.total = align256(S.off_order + picks * 4);
+    return S;
+}
+
+struct BwdQueryScratch {
+    size_t off_gl_i, off_gl_g, off_partial, total;
+    int blocks;             // token blocks (one partial sum each)
+    int tokens_per_block;   // a multiple of 32
+};
+
+inline BwdQueryScratch bwd_query_scratch(int64_t T, int H, int n, int k, int d_k)
+{
+    BwdQueryScratch S;
+    const int half = d_k / 2;
+    // about one workgroup (16 waves, n x 32 LDS tile) per compute unit
+    const int64_t groups = (int64_t)H * 2 * ((half + 63) / 64);
+    int64_t blocks = (256 + groups - 1) / groups;
+    const int64_t max_blocks = T > 128 ? (T + 127) / 128 : 1;
+    if (blocks > max_blocks)
+        blocks = max_blocks;
+    if (blocks < 1)
+        blocks = 1;
+    int64_t tpb = T > 0 ? (T + blocks - 1) / blocks : 32;
+    tpb = (tpb + 31) & ~(int64_t)31;
+    S.tokens_per_block = (int)tpb;
+    S.blocks = (int)(T > 0 ? (T + tpb - 1) / tpb : 1);
+    const size_t lists = (size_t)T * H * 2 * k * 4;
+    S.off_gl_i = 0;
+    S.off_gl_g = align256(lists);
+    S.off_partial = align256(S.off_gl_g + lists);
+    S.total = align256(S.off_partial + (size_t)S.blocks * H * 2 * n * half * 4);
+    return S;
+}
+
+// Value side of the backward: slot sort of the picks, then per slot segment
+// dw = <dy, values[slot]> for each pick and dvalues[slot] += sum w * dy.
+// `scratch` holds bwd_value_scratch(T, H, n, k).total bytes.
 hipError_t launch_bwd_value(int dtype, const void *values, const int32_t *idx,
                             const float *weights, const void *dy, float *dvalues, float *dw,
-                            int64_t T, int H, int k, int d_v, hipStream_t stream);
+                            int64_t T, int H, int n, int k, int d_v, void *scratch,
+                            hipStream_t stream);
 
-// Softmax backward, then dq (overwritten) and dkeys (accumulated; zero it
-// first) from weights and dw.
+// Query side: softmax backward per distinct sub-key, dq (overwritten) and
+// dkeys (overwritten) from weights and dw.  `scratch` holds
+// bwd_query_scratch(T, H, n, k, d_k).total bytes.
 hipError_t launch_bwd_query(int dtype, const void *q, const void *keys, const int32_t *idx,
                             const float *weights, const float *dw, float *dq, float *dkeys,
-                            int64_t T, int H, int n, int k, int d_k, hipStream_t stream);
+                            int64_t T, int H, int n, int k, int d_k, void *scratch,
+                            hipStream_t stream);
 
 // Fill `count` floats with zero (a kernel, so it can sit inside a captured graph).
 hipError_t launch_zero_f32(float *p, int64_t count, hipStream_t stream);

@@ -69,14 +69,6 @@ static SelLayout sel_layout(int n, int k, int half, int elt_bytes)
     return L;
 }
 
-// Make this wave's LDS stores visible to its own later LDS loads.
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // ---- step 1: score tile --------------------------------------------------
 // Scores of sub-keys [tile*16, tile*16+16) against the 16 staged queries.
 // Lane l supplies A row (sub-key) l%16 and B column (token) l%16; the K slice

@@ -52,14 +52,18 @@ def test_null_and_alignment():
     assert _lib.forward(P(), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 1
     assert _lib.forward(P(), FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 6
     assert _lib.forward_select(P(), FAKE, FAKE, None, FAKE, None, None) == 1
-    assert _lib.backward_values(P(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, None) == 6
+    assert _lib.backward_values(P(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, FAKE, 1 << 30, None) == 6
 
 
 def test_backward_workspace_checks():
     p = P()
     need = _lib.workspace_bytes(p, True)
-    assert need == ((16 * 2 * 8 * 4 + 255) // 256) * 256
+    picks = 16 * 2 * 8
+    assert need >= picks * 4 + 64 * 64 * 4 * 3 + picks * 4     # dw + slot sort at least
     assert _lib.workspace_bytes(p, False) == 0
+    # either stage alone accepts the full workspace and rejects a 16-byte one
+    assert _lib.backward_values(p, *[FAKE] * 6, FAKE, 16, None) == 4
+    assert _lib.backward_queries(p, *[FAKE] * 7, FAKE, 16, None) == 4
     args = [FAKE] * 9
     assert _lib.backward(p, *args, FAKE, need - 1, None) == 4
     assert _lib.backward(p, *args, None, 0, None) == 1

@@ -8,7 +8,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkm.so")
+# PKM_LIB may name another build of the same library (e.g. a variant under test)
+LIB_PATH = os.environ.get("PKM_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                     "libpkm.so")
 
 PKM_FP32 = 0
 PKM_BF16 = 1

@@ -25,14 +25,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm toolchain required to build libpkm.so)")
 
 
-def build_library(out: str = LIB_PATH, verbose: bool = False) -> str:
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+def build_library(out: str = LIB_PATH, verbose: bool = False, defines: tuple = (),
+                  csrc: str = CSRC) -> str:
+    sources = sorted(glob.glob(os.path.join(csrc, "*.hip")))
     cmd = [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-munsafe-fp-atomics",
         # packed float32 VALU forms are kept out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-I", INCLUDE, "-I", CSRC, *sources, "-o", out + ".tmp",
+        "-I", INCLUDE, "-I", csrc, *[f"-D{d}" for d in defines], *sources, "-o", out + ".tmp",
     ]
     if verbose:
         print(" ".join(cmd), flush=True)

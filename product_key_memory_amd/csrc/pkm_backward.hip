@@ -158,6 +158,7 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
 {
     constexpr int EPC = Elt<DT>::per16;
     __shared__ int32_t s_pk[kSegWaves][kSegChunk];
+    __shared__ int32_t s_tok[kSegWaves][kSegChunk];
     __shared__ int32_t s_slot[kSegWaves][kSegChunk];
     __shared__ float s_w[kSegWaves][kSegChunk];
     const int lane = lane_id();
@@ -171,6 +172,7 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
     for (int j = lane; j < len; j += kWave) {
         const int32_t pk = order[p_begin + j];
         s_pk[wv][j] = pk;
+        s_tok[wv][j] = pk / HK;
         s_slot[wv][j] = idx[pk];
         s_w[wv][j] = weights[pk];
     }
@@ -209,13 +211,11 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
         for (int j = pos; j < stop; j += U) {
             uint4 buf[U][MCH];
             float wv_u[U];
-            int32_t pk[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const bool live = j + u < stop;
-                pk[u] = live ? __builtin_amdgcn_readfirstlane(s_pk[wv][j + u]) : 0;
+                const int64_t t = live ? __builtin_amdgcn_readfirstlane(s_tok[wv][j + u]) : 0;
                 wv_u[u] = live ? s_w[wv][j + u] : 0.f;
-                const int64_t t = pk[u] / HK;
                 const uint4 *drow_in = reinterpret_cast<const uint4 *>(dy + t * d_v);
 #pragma unroll
                 for (int m = 0; m < MCH; ++m) {
@@ -223,23 +223,26 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
                     buf[u][m] = (live && c < nchunks) ? drow_in[c] : make_uint4(0u, 0u, 0u, 0u);
                 }
             }
+            float part[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                float part = 0.f;
+                part[u] = 0.f;
 #pragma unroll
                 for (int m = 0; m < MCH; ++m) {
                     float g[EPC];
                     unpack16(buf[u][m], g);
 #pragma unroll
                     for (int e = 0; e < EPC; ++e) {
-                        part = fmaf(vrow[m][e], g[e], part);
+                        part[u] = fmaf(vrow[m][e], g[e], part[u]);
                         acc[m][e] = fmaf(wv_u[u], g[e], acc[m][e]);
                     }
                 }
-                const float dot = wave_sum(part);
-                if (j + u < stop && lane == 0)
-                    dw[pk[u]] = dot;
             }
+            // lane l ends with the dot of pick j + l / (64 / U)
+            wave_multi_sum<U>(part);
+            const int u_mine = lane / (kWave / U);
+            if (lane % (kWave / U) == 0 && j + u_mine < stop)
+                dw[s_pk[wv][j + u_mine]] = part[0];
         }
 
 #pragma unroll

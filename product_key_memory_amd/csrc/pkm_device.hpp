@@ -96,6 +96,36 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+// Sums of U values over the 64 lanes at once (U a power of two <= 64).  On
+// return v[0] of lane l holds the total of value (l / (64 / U)).  Each halving
+// step exchanges half of the remaining values, so U sums cost about
+// U + log2(64 / U) cross-lane moves instead of 6 U.
+template <int U>
+__device__ __forceinline__ void wave_multi_sum(float (&v)[U])
+{
+    const int lane = lane_id();
+    int width = U;
+#pragma unroll
+    for (int stride = 32; stride >= 1; stride >>= 1) {
+        if (width > 1) {
+            // lanes with the stride bit set keep the upper half of the values
+            const bool upper = (lane & stride) != 0;
+            const int h = width / 2;
+#pragma unroll
+            for (int j = 0; j < U / 2; ++j) {
+                if (j < h) {
+                    const float send = upper ? v[j] : v[j + h];
+                    const float keep = upper ? v[j + h] : v[j];
+                    v[j] = keep + __shfl_xor(send, stride);
+                }
+            }
+            width = h;
+        } else {
+            v[0] += __shfl_xor(v[0], stride);
+        }
+    }
+}
+
 // Exclusive prefix sum over the 64 lanes; *total receives the wave total.
 __device__ __forceinline__ int wave_exclusive_scan(int v, int *total)
 {
@@ -167,6 +197,59 @@ __device__ __forceinline__ void wave_sort_desc(uint64_t (&v)[R])
                     const bool desc = ((r * kWave + lane) & size) == 0;
                     const bool keep_max = (lower == desc);
                     v[r] = keep_max ? (v[r] > o ? v[r] : o) : (v[r] < o ? v[r] : o);
+                }
+            }
+        }
+    }
+}
+
+// Bitonic sort, descending, inside each group of 4 lanes {l, l^16, l^32, l^48}
+// (the lanes that share l % 16), of the 4R values the group holds: element
+// e = (lane / 16) * R + r lives in register r of lane group lane / 16.
+template <int R, typename T>
+__device__ __forceinline__ T g4_max(T a, T b) { return a > b ? a : b; }
+template <int R, typename T>
+__device__ __forceinline__ T g4_min(T a, T b) { return a < b ? a : b; }
+__device__ __forceinline__ float g4_shfl(float v, int m) { return __shfl_xor(v, m); }
+__device__ __forceinline__ uint32_t g4_shfl(uint32_t v, int m) { return (uint32_t)__shfl_xor((int)v, m); }
+__device__ __forceinline__ uint64_t g4_shfl(uint64_t v, int m) { return shfl_xor_u64(v, m); }
+
+// Sum over the 4 lanes that share lane % 16.
+__device__ __forceinline__ int group4_sum(int v)
+{
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+template <int R, typename T>
+__device__ __forceinline__ void group4_sort_desc(T (&v)[R])
+{
+    const int g = lane_id() >> 4;
+    constexpr int P = 4 * R;
+#pragma unroll
+    for (int size = 2; size <= P; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride >= R) {
+                const int lm = 16 * (stride / R);
+                const bool lower = ((g * R) & stride) == 0;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const bool desc = ((g * R + r) & size) == 0;
+                    const T o = g4_shfl(v[r], lm);
+                    v[r] = (lower == desc) ? g4_max<R>(v[r], o) : g4_min<R>(v[r], o);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if ((r & stride) == 0) {
+                        const bool desc = ((g * R + r) & size) == 0;
+                        const T a = v[r], b = v[r | stride];
+                        const bool swap = desc ? (a < b) : (a > b);
+                        v[r] = swap ? b : a;
+                        v[r | stride] = swap ? a : b;
+                    }
                 }
             }
         }

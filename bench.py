@@ -37,25 +37,62 @@ def parse():
                     help="tokens of the same workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="first run 3 plain 256 MiB device copies, whose FETCH_SIZE/WRITE_SIZE "
-                         "counters calibrate the HBM-traffic counters of the kernels")
+                    help="first run 3 plain elementwise copies of 256 MiB (x * 2), whose "
+                         "FETCH_SIZE/WRITE_SIZE counters calibrate those of the kernels")
     return ap.parse_args()
 
 
-def stage_bytes(w, elt: int) -> dict:
-    """Algorithmic work of one launch of each stage: every one of the T*H*k
-    picks counted once, cache hits not subtracted."""
+STAGES = ["zero_dvalues", "select", "gather", "slot_sort", "bwd_values", "bwd_queries"]
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "hbm_traffic_base-bf16-zipf-bwd.json")
+
+
+def stage_bytes(w, elt: int, touched: int) -> dict:
+    """Algorithmic work of one launch of each stage (what its formulation must
+    move, cache hits not subtracted; `touched` = memory slots picked at least
+    once in the batch)."""
     T, H, k, n, d_k, d_v, half = w.T, w.H, w.k, w.n, w.d_k, w.d_v, w.d_k // 2
-    picks = T * H * k
+    picks, slots = T * H * k, n * n
     return {
-        "zero_dvalues": {"bytes": n * n * d_v * 4},
+        "zero_dvalues": {"bytes": slots * d_v * 4},
         "select": {"flops": 2 * T * H * 2 * n * half,
                    "bytes": T * H * d_k * elt + H * 2 * n * half * elt + picks * 12},
+        # one value row per pick, y written once, idx + weights read
         "gather": {"bytes": picks * d_v * elt + T * d_v * elt + picks * 8},
-        "bwd_values": {"bytes": picks * d_v * elt + picks * d_v * 4 + T * d_v * elt + picks * 12},
-        "bwd_queries": {"bytes": T * H * d_k * elt + T * H * d_k * 4 + picks * 12
-                        + H * 2 * n * half * (elt + 4)},
+        # idx read twice, order written, counts/cursors/starts per slot
+        "slot_sort": {"bytes": picks * 12 + slots * 16},
+        # each touched value row once, a read-modify-write of each touched
+        # dvalues row, one dy row per pick, per-pick metadata
+        "bwd_values": {"bytes": touched * d_v * (elt + 8) + picks * d_v * elt + picks * 16 + slots * 4},
+        # q once, sub-keys once, per-pick metadata, dq written, (i, g) lists
+        # written and read, partial sub-key sums written and read
+        "bwd_queries": {"bytes": T * H * d_k * elt + H * 2 * n * half * elt + picks * 12
+                        + T * H * d_k * 4 + T * H * 2 * k * 8 * 2 + H * 2 * n * half * 4 * 3},
     }
+
+
+def source_hash() -> str:
+    import glob
+    import hashlib
+    hsh = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "product_key_memory_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*"))):
+        with open(f, "rb") as fh:
+            hsh.update(os.path.basename(f).encode() + fh.read())
+    return hsh.hexdigest()
+
+
+def measured_traffic(workload: str) -> dict:
+    """HBM bytes per stage from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs, only if they were taken on the kernels as they are now."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    if rec.get("source_sha256") != source_hash() or rec.get("workload") != workload:
+        return {}
+    return rec.get("stages", {})
 
 
 def cpu_baseline(inp, k: int, count: int) -> dict:
@@ -112,6 +149,8 @@ def main():
     wts = torch.empty((T, H, k), dtype=torch.float32, device=dev)
     scores = torch.empty((T, H, k), dtype=torch.float32, device=dev)
     dw = torch.empty((T, H, k), dtype=torch.float32, device=dev)
+    slot_start = torch.empty(n * n + 1, dtype=torch.int32, device=dev)
+    order = torch.empty((T * H * k,), dtype=torch.int32, device=dev)
     dq = torch.empty((T, H, d_k), dtype=torch.float32, device=dev)
     dkeys = torch.empty((H, 2, n, d_k // 2), dtype=torch.float32, device=dev)
     dvalues = torch.empty((n * n, d_v), dtype=torch.float32, device=dev)
@@ -121,8 +160,6 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     P = lambda t: t.data_ptr()  # noqa: E731
-
-    stages = ["zero_dvalues", "select", "gather", "bwd_values", "bwd_queries"]
 
     def step(ev=None):
         def mark(i):
@@ -135,20 +172,24 @@ def main():
         mark(2)
         rc |= _lib.forward_gather(p, P(values), P(idx), P(wts), P(y), sp)
         mark(3)
-        rc |= _lib.backward_values(p, P(values), P(idx), P(wts), P(dy), P(dvalues), P(dw),
-                                  P(ws), ws_bytes, sp)
+        rc |= _lib.slot_sort(p, P(idx), P(slot_start), P(order), P(ws), ws_bytes, sp)
         mark(4)
-        rc |= _lib.backward_queries(p, P(q), P(keys), P(idx), P(wts), P(dw), P(dq), P(dkeys),
-                                   P(ws), ws_bytes, sp)
+        rc |= _lib.backward_values(p, P(values), P(idx), P(wts), P(dy), P(slot_start), P(order),
+                                   P(dvalues), P(dw), sp)
         mark(5)
+        rc |= _lib.backward_queries(p, P(q), P(keys), P(idx), P(wts), P(dw), P(dq), P(dkeys),
+                                    P(ws), ws_bytes, sp)
+        mark(6)
         if rc:
             raise RuntimeError(f"libpkm returned {rc}")
 
     if args.calibrate_copy:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        # a plain elementwise kernel of known size (reads 256 MiB, writes 256 MiB,
+        # 16-byte accesses like the layer's own kernels)
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.mul(src, 2.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -156,7 +197,8 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    nev = len(STAGES) + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -164,17 +206,19 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
-    per_stage = {name: 0.0 for name in stages}
+    per_stage = {name: 0.0 for name in STAGES}
     for ev in events:
-        for i, name in enumerate(stages):
+        for i, name in enumerate(STAGES):
             per_stage[name] += ev[i].elapsed_time(ev[i + 1])
     per_stage = {name: v / args.steps for name, v in per_stage.items()}   # ms per launch
     wall_ms = (t1 - t0) * 1e3 / args.steps
     tokens_per_s = T / (wall_ms * 1e-3)
 
-    work = stage_bytes(w, elt)
+    touched = int(((slot_start[1:] - slot_start[:-1]) > 0).sum().item())
+    work = stage_bytes(w, elt, touched)
+    traffic = measured_traffic(w.name)
     kernels = {}
-    for name in stages:
+    for name in STAGES:
         ms = per_stage[name]
         entry = {"ms": round(ms, 5), "bytes": work[name]["bytes"],
                  "GB/s": round(work[name]["bytes"] / (ms * 1e-3) / 1e9, 1)}
@@ -184,12 +228,15 @@ def main():
             peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
             entry.update({"flops": work[name]["flops"], "TFLOP/s": round(tf, 2),
                           "mfma_frac": round(tf / peak, 4)})
+        if name in traffic:
+            entry["traffic"] = traffic[name]["read_bytes"] + traffic[name]["write_bytes"]
         kernels[name] = entry
 
-    dominant = max(("select", "gather", "bwd_values", "bwd_queries"), key=lambda s: per_stage[s])
+    dominant = max(STAGES[1:], key=lambda s: per_stage[s])
     dk = kernels[dominant]
     roofline = {"kernel": dominant, "bound": "hbm", "achieved": dk["GB/s"], "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(dk["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(dk["GB/s"] / HBM_PEAK_GBS, 4),
+                "traffic": dk.get("traffic")}
 
     out = {
         "metric": METRIC,
@@ -206,7 +253,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": T, "heads": H, "n": n, "slots": n * n, "k": k,
                    "d_k": d_k, "d_v": d_v, "storage": w.dtype, "accumulate": "fp32",
-                   "zipf": w.zipf, "step": "zero dvalues + forward + backward"},
+                   "zipf": w.zipf, "touched_slots": touched,
+                   "step": "zero dvalues + forward + backward"},
         "gather": {"GB/s": kernels["gather"]["GB/s"], "hbm_frac": kernels["gather"]["hbm_frac"]},
         "roofline": roofline,
         "kernels": kernels,

@@ -135,9 +135,10 @@ pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *key
  * The two passes above, stage by stage, for callers that keep the
  * intermediate results or time the stages: pkm_forward is
  * pkm_forward_select followed by pkm_forward_gather; pkm_backward is
- * pkm_backward_values followed by pkm_backward_queries.  Same conventions,
- * same array layouts as above.  A workspace of pkm_workspace_bytes(p, 1)
- * bytes serves either backward stage.
+ * pkm_slot_sort, pkm_backward_values and pkm_backward_queries.  Same
+ * conventions, same array layouts as above.  A workspace of
+ * pkm_workspace_bytes(p, 1) bytes serves pkm_slot_sort and
+ * pkm_backward_queries.
  */
 
 /* Steps 1-5 of pkm_forward: the selection and its softmax weights
@@ -150,14 +151,24 @@ pkm_status_t pkm_forward_select(const pkm_problem_t *p, const void *q, const voi
 pkm_status_t pkm_forward_gather(const pkm_problem_t *p, const void *values, const int32_t *idx,
                                 const float *weights, void *y, void *stream);
 
-/* The value side of pkm_backward: dw [T][H][k] float32 (OUT, overwritten),
- * dw = <dy[t], values[f]>, and the sparse update dvalues[f] += w * dy[t]
- * (ACCUMULATED, as in pkm_backward).  The picks are sorted by slot in the
- * workspace, so each value row is read once per run of picks and most rows
- * of dvalues are updated without atomics. */
+/* Groups the T*H*k picks of idx by memory slot (a counting sort): the picks
+ * that selected slot f are order[slot_start[f] .. slot_start[f+1]), as pick
+ * ids t*H*k + h*k + r.  These are exactly the slots that receive a value
+ * update (gptget.net summary, "Methodology": only a few memory slots are
+ * updated).
+ *   slot_start  [n*n + 1]  int32 OUT;  order  [T*H*k]  int32 OUT
+ * The order of picks inside one slot is unspecified. */
+pkm_status_t pkm_slot_sort(const pkm_problem_t *p, const int32_t *idx, int32_t *slot_start,
+                           int32_t *order, void *workspace, size_t workspace_bytes, void *stream);
+
+/* The value side of pkm_backward over the slot-sorted picks: dw [T][H][k]
+ * float32 (OUT, overwritten), dw = <dy[t], values[f]>, and the sparse update
+ * dvalues[f] += w * dy[t] (ACCUMULATED, as in pkm_backward).  Each value row
+ * is read once per run of picks and most rows of dvalues are updated without
+ * atomics.  slot_start and order come from pkm_slot_sort on the same idx. */
 pkm_status_t pkm_backward_values(const pkm_problem_t *p, const void *values, const int32_t *idx,
-                                 const float *weights, const void *dy, float *dvalues, float *dw,
-                                 void *workspace, size_t workspace_bytes, void *stream);
+                                 const float *weights, const void *dy, const int32_t *slot_start,
+                                 const int32_t *order, float *dvalues, float *dw, void *stream);
 
 /* The query side of pkm_backward, from weights and dw: the softmax backward,
  * then dq and dkeys (both OUT, overwritten).  Each pick's ds reaches its left

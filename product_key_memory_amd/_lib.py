@@ -27,7 +27,7 @@ STATUS = {
 
 # every symbol include/pkm.h declares
 EXPORTS = ("pkm_workspace_bytes", "pkm_forward", "pkm_backward", "pkm_forward_select",
-           "pkm_forward_gather", "pkm_backward_values", "pkm_backward_queries",
+           "pkm_forward_gather", "pkm_slot_sort", "pkm_backward_values", "pkm_backward_queries",
            "pkm_status_string")
 
 
@@ -66,10 +66,11 @@ def lib() -> ctypes.CDLL:
         PP = ctypes.POINTER(Problem)
         L.pkm_forward_select.argtypes = [PP, P, P, P, P, P, P]
         L.pkm_forward_gather.argtypes = [PP, P, P, P, P, P]
-        L.pkm_backward_values.argtypes = [PP, P, P, P, P, P, P, P, c_size, P]
+        L.pkm_slot_sort.argtypes = [PP, P, P, P, P, c_size, P]
+        L.pkm_backward_values.argtypes = [PP, P, P, P, P, P, P, P, P, P]
         L.pkm_backward_queries.argtypes = [PP, P, P, P, P, P, P, P, P, c_size, P]
-        for name in ("pkm_forward_select", "pkm_forward_gather", "pkm_backward_values",
-                     "pkm_backward_queries"):
+        for name in ("pkm_forward_select", "pkm_forward_gather", "pkm_slot_sort",
+                     "pkm_backward_values", "pkm_backward_queries"):
             getattr(L, name).restype = ctypes.c_int
         L.pkm_status_string.argtypes = [ctypes.c_int]
         L.pkm_status_string.restype = ctypes.c_char_p
@@ -104,10 +105,14 @@ def forward_gather(p: Problem, values, idx, weights, y, stream) -> int:
     return lib().pkm_forward_gather(ctypes.byref(p), values, idx, weights, y, stream)
 
 
-def backward_values(p: Problem, values, idx, weights, dy, dvalues, dw, ws, ws_bytes,
+def slot_sort(p: Problem, idx, slot_start, order, ws, ws_bytes, stream) -> int:
+    return lib().pkm_slot_sort(ctypes.byref(p), idx, slot_start, order, ws, ws_bytes, stream)
+
+
+def backward_values(p: Problem, values, idx, weights, dy, slot_start, order, dvalues, dw,
                     stream) -> int:
-    return lib().pkm_backward_values(ctypes.byref(p), values, idx, weights, dy, dvalues, dw, ws,
-                                     ws_bytes, stream)
+    return lib().pkm_backward_values(ctypes.byref(p), values, idx, weights, dy, slot_start, order,
+                                     dvalues, dw, stream)
 
 
 def backward_queries(p: Problem, q, keys, idx, weights, dw, dq, dkeys, ws, ws_bytes,

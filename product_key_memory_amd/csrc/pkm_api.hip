@@ -38,17 +38,21 @@ pkm_status_t check_problem(const pkm_problem_t *p, bool backward)
     return PKM_OK;
 }
 
-size_t dw_bytes(const pkm_problem_t *p) { return pkm::align256((size_t)(p->T * p->H * p->k) * 4); }
+size_t picks_bytes(const pkm_problem_t *p) { return pkm::align256((size_t)(p->T * p->H * p->k) * 4); }
+size_t starts_bytes(const pkm_problem_t *p) { return pkm::align256(((size_t)p->n * p->n + 1) * 4); }
 
 size_t stage_scratch_bytes(const pkm_problem_t *p)
 {
-    const size_t v = pkm::bwd_value_scratch(p->T, p->H, p->n, p->k).total;
+    const size_t v = pkm::slot_sort_scratch(p->n).total;
     const size_t q = pkm::bwd_query_scratch(p->T, p->H, p->n, p->k, p->d_k).total;
     return v > q ? v : q;
 }
 
-// pkm_backward: dw first, the stages' scratch after it.
-size_t backward_bytes(const pkm_problem_t *p) { return dw_bytes(p) + stage_scratch_bytes(p); }
+// pkm_backward: dw, slot_start, order, then the stages' scratch.
+size_t backward_bytes(const pkm_problem_t *p)
+{
+    return picks_bytes(p) + starts_bytes(p) + picks_bytes(p) + stage_scratch_bytes(p);
+}
 
 pkm_status_t check_workspace(const pkm_problem_t *p, const void *ws, size_t have, size_t need)
 {
@@ -133,26 +137,53 @@ pkm_status_t pkm_forward(const pkm_problem_t *p, const void *q, const void *keys
     return pkm_forward_gather(p, values, idx, weights, y, stream);
 }
 
-pkm_status_t pkm_backward_values(const pkm_problem_t *p, const void *values, const int32_t *idx,
-                                 const float *weights, const void *dy, float *dvalues, float *dw,
-                                 void *workspace, size_t workspace_bytes, void *stream)
+pkm_status_t pkm_slot_sort(const pkm_problem_t *p, const int32_t *idx, int32_t *slot_start,
+                           int32_t *order, void *workspace, size_t workspace_bytes, void *stream)
 {
     pkm_status_t st = check_problem(p, true);
     if (st != PKM_OK)
         return st;
     const int64_t T = p->T;
-    if (!values || missing(idx, T) || missing(weights, T) || missing(dy, T) || !dvalues ||
-        missing(dw, T))
+    if (missing(idx, T) || !slot_start || missing(order, T))
+        return PKM_ERR_NULL;
+    if (!aligned16(idx) || !aligned16(slot_start) || !aligned16(order))
+        return PKM_ERR_ALIGN;
+    if (T == 0)      // no picks: every slot starts (and ends) at 0
+        return pkm::launch_zero_f32(reinterpret_cast<float *>(slot_start),
+                                    (int64_t)p->n * p->n + 1,
+                                    static_cast<hipStream_t>(stream)) == hipSuccess
+                   ? PKM_OK
+                   : PKM_ERR_HIP;
+    if (!workspace)
+        return PKM_ERR_NULL;
+    if (!aligned16(workspace))
+        return PKM_ERR_ALIGN;
+    if (workspace_bytes < pkm::slot_sort_scratch(p->n).total)
+        return PKM_ERR_WORKSPACE;
+    return pkm::launch_slot_sort(idx, T * p->H * p->k, p->n, slot_start, order, workspace,
+                                 static_cast<hipStream_t>(stream)) == hipSuccess
+               ? PKM_OK
+               : PKM_ERR_HIP;
+}
+
+pkm_status_t pkm_backward_values(const pkm_problem_t *p, const void *values, const int32_t *idx,
+                                 const float *weights, const void *dy, const int32_t *slot_start,
+                                 const int32_t *order, float *dvalues, float *dw, void *stream)
+{
+    pkm_status_t st = check_problem(p, true);
+    if (st != PKM_OK)
+        return st;
+    const int64_t T = p->T;
+    if (!values || missing(idx, T) || missing(weights, T) || missing(dy, T) || !slot_start ||
+        missing(order, T) || !dvalues || missing(dw, T))
         return PKM_ERR_NULL;
     if (!aligned16(values) || !aligned16(idx) || !aligned16(weights) || !aligned16(dy) ||
-        !aligned16(dvalues) || !aligned16(dw))
+        !aligned16(slot_start) || !aligned16(order) || !aligned16(dvalues) || !aligned16(dw))
         return PKM_ERR_ALIGN;
-    st = check_workspace(p, workspace, workspace_bytes,
-                         pkm::bwd_value_scratch(p->T, p->H, p->n, p->k).total);
-    if (st != PKM_OK || T == 0)
-        return st;
-    return pkm::launch_bwd_value(p->dtype, values, idx, weights, dy, dvalues, dw, p->T, p->H,
-                                 p->n, p->k, p->d_v, workspace,
+    if (T == 0)
+        return PKM_OK;
+    return pkm::launch_bwd_value(p->dtype, values, idx, weights, dy, slot_start, order, dvalues,
+                                 dw, p->T, p->H, p->k, p->d_v,
                                  static_cast<hipStream_t>(stream)) == hipSuccess
                ? PKM_OK
                : PKM_ERR_HIP;
@@ -207,13 +238,22 @@ pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *key
     st = check_workspace(p, workspace, workspace_bytes, backward_bytes(p));
     if (st != PKM_OK)
         return st;
-    float *dw = T > 0 ? static_cast<float *>(workspace) : nullptr;
-    void *scratch = T > 0 ? static_cast<char *>(workspace) + dw_bytes(p) : nullptr;
-    const size_t scratch_bytes = T > 0 ? workspace_bytes - dw_bytes(p) : 0;
-    st = pkm_backward_values(p, values, idx, weights, dy, dvalues, dw, scratch, scratch_bytes,
-                             stream);
-    if (st != PKM_OK)
-        return st;
+    char *base = static_cast<char *>(workspace);
+    float *dw = reinterpret_cast<float *>(base);
+    int32_t *slot_start = reinterpret_cast<int32_t *>(base + picks_bytes(p));
+    int32_t *order = reinterpret_cast<int32_t *>(base + picks_bytes(p) + starts_bytes(p));
+    const size_t head = 2 * picks_bytes(p) + starts_bytes(p);
+    void *scratch = T > 0 ? base + head : nullptr;
+    const size_t scratch_bytes = T > 0 ? workspace_bytes - head : 0;
+    if (T > 0) {
+        st = pkm_slot_sort(p, idx, slot_start, order, scratch, scratch_bytes, stream);
+        if (st != PKM_OK)
+            return st;
+        st = pkm_backward_values(p, values, idx, weights, dy, slot_start, order, dvalues, dw,
+                                 stream);
+        if (st != PKM_OK)
+            return st;
+    }
     return pkm_backward_queries(p, q, keys, idx, weights, dw, dq, dkeys, scratch, scratch_bytes,
                                 stream);
 }

@@ -6,7 +6,8 @@
 // each score its left and right sub-key scores.
 //
 // Value side (no float atomics on the value gradient in the common case):
-//   1. the T*H*k picks are counting-sorted by slot (histogram, scan, scatter);
+//   1. the T*H*k picks are counting-sorted by slot (histogram, scan, scatter)
+//      into slot_start [n*n + 1] and order [T*H*k];
 //   2. one wave per fixed chunk of the sorted picks walks its slot segments:
 //      the value row of a segment is read once, every pick p of it gives
 //      dw_p = <dy[t_p], values[f]>, and sum_p w_p dy[t_p] is added to
@@ -585,20 +586,15 @@ static hipError_t launch_seg_dt(const void *values, const void *dy, const int32_
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_value(int dtype, const void *values, const int32_t *idx,
-                            const float *weights, const void *dy, float *dvalues, float *dw,
-                            int64_t T, int H, int n, int k, int d_v, void *scratch,
-                            hipStream_t stream)
+hipError_t launch_slot_sort(const int32_t *idx, int64_t picks, int n, int32_t *slot_start,
+                            int32_t *order, void *scratch, hipStream_t stream)
 {
-    const BwdValueScratch S = bwd_value_scratch(T, H, n, k);
+    const SlotSortScratch S = slot_sort_scratch(n);
     char *base = static_cast<char *>(scratch);
     int32_t *count = reinterpret_cast<int32_t *>(base + S.off_count);
-    int32_t *start = reinterpret_cast<int32_t *>(base + S.off_start);
     int32_t *cursor = reinterpret_cast<int32_t *>(base + S.off_cursor);
     int32_t *bsums = reinterpret_cast<int32_t *>(base + S.off_bsums);
-    int32_t *order = reinterpret_cast<int32_t *>(base + S.off_order);
     const int64_t slots = (int64_t)n * n;
-    const int64_t picks = T * H * (int64_t)k;
     hipError_t err = launch_zero_f32(reinterpret_cast<float *>(count), slots, stream);
     if (err != hipSuccess)
         return err;
@@ -608,16 +604,23 @@ hipError_t launch_bwd_value(int dtype, const void *values, const int32_t *idx,
     hipLaunchKernelGGL(scan_block_sums_kernel, dim3(sblocks), dim3(256), 0, stream, count, slots,
                        bsums);
     hipLaunchKernelGGL(scan_apply_kernel, dim3(sblocks), dim3(256), 0, stream, count, bsums,
-                       slots, start, cursor);
+                       slots, slot_start, cursor);
     hipLaunchKernelGGL(slot_fill_kernel, dim3(grid1d(picks, 256)), dim3(256), 0, stream, idx,
                        picks, cursor, order);
-    if ((err = hipGetLastError()) != hipSuccess)
-        return err;
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_value(int dtype, const void *values, const int32_t *idx,
+                            const float *weights, const void *dy, const int32_t *slot_start,
+                            const int32_t *order, float *dvalues, float *dw, int64_t T, int H,
+                            int k, int d_v, hipStream_t stream)
+{
+    const int64_t picks = T * H * (int64_t)k;
     if (dtype == 1)
-        return launch_seg_dt<bf16_t>(values, dy, idx, weights, order, start, dvalues, dw, picks,
-                                     H * k, d_v, stream);
-    return launch_seg_dt<float>(values, dy, idx, weights, order, start, dvalues, dw, picks, H * k,
-                                d_v, stream);
+        return launch_seg_dt<bf16_t>(values, dy, idx, weights, order, slot_start, dvalues, dw,
+                                     picks, H * k, d_v, stream);
+    return launch_seg_dt<float>(values, dy, idx, weights, order, slot_start, dvalues, dw, picks,
+                                H * k, d_v, stream);
 }
 
 template <typename DT>

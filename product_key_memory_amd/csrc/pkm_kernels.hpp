@@ -25,21 +25,20 @@ constexpr int kSegChunk = 256;      // sorted picks per wave in the value segmen
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-struct BwdValueScratch {
-    size_t off_count, off_start, off_cursor, off_bsums, off_order, total;
+// Scratch of the slot sort: per-slot counts and cursors, scan block sums.
+struct SlotSortScratch {
+    size_t off_count, off_cursor, off_bsums, total;
 };
 
-inline BwdValueScratch bwd_value_scratch(int64_t T, int H, int n, int k)
+inline SlotSortScratch slot_sort_scratch(int n)
 {
-    const size_t slots = (size_t)n * n, picks = (size_t)T * H * k;
+    const size_t slots = (size_t)n * n;
     const size_t sblocks = (slots + 1023) / 1024;
-    BwdValueScratch S;
+    SlotSortScratch S;
     S.off_count = 0;
-    S.off_start = align256(S.off_count + slots * 4);
-    S.off_cursor = align256(S.off_start + (slots + 1) * 4);
+    S.off_cursor = align256(slots * 4);
     S.off_bsums = align256(S.off_cursor + slots * 4);
-    S.off_order = align256(S.off_bsums + sblocks * 4);
-    S.total = align256(S.off_order + picks * 4);
+    S.total = align256(S.off_bsums + sblocks * 4);
     return S;
 }
 
@@ -73,13 +72,18 @@ inline BwdQueryScratch bwd_query_scratch(int64_t T, int H, int n, int k, int d_k
     return S;
 }
 
-// Value side of the backward: slot sort of the picks, then per slot segment
-// dw = <dy, values[slot]> for each pick and dvalues[slot] += sum w * dy.
-// `scratch` holds bwd_value_scratch(T, H, n, k).total bytes.
+// Counting sort of the T*H*k picks by slot: slot_start [n*n + 1] (the picks
+// of slot f are order[slot_start[f] .. slot_start[f+1])), order [picks] (pick
+// ids t*H*k + h*k + r).  `scratch` holds slot_sort_scratch(n).total bytes.
+hipError_t launch_slot_sort(const int32_t *idx, int64_t picks, int n, int32_t *slot_start,
+                            int32_t *order, void *scratch, hipStream_t stream);
+
+// Value side of the backward over the slot-sorted picks: dw = <dy, values[slot]>
+// per pick and dvalues[slot] += sum w * dy.
 hipError_t launch_bwd_value(int dtype, const void *values, const int32_t *idx,
-                            const float *weights, const void *dy, float *dvalues, float *dw,
-                            int64_t T, int H, int n, int k, int d_v, void *scratch,
-                            hipStream_t stream);
+                            const float *weights, const void *dy, const int32_t *slot_start,
+                            const int32_t *order, float *dvalues, float *dw, int64_t T, int H,
+                            int k, int d_v, hipStream_t stream);
 
 // Query side: softmax backward per distinct sub-key, dq (overwritten) and
 // dkeys (overwritten) from weights and dw.  `scratch` holds

@@ -52,7 +52,8 @@ def test_null_and_alignment():
     assert _lib.forward(P(), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 1
     assert _lib.forward(P(), FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 6
     assert _lib.forward_select(P(), FAKE, FAKE, None, FAKE, None, None) == 1
-    assert _lib.backward_values(P(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, FAKE, 1 << 30, None) == 6
+    assert _lib.backward_values(P(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, None) == 6
+    assert _lib.slot_sort(P(), FAKE, None, FAKE, FAKE, 1 << 30, None) == 1
 
 
 def test_backward_workspace_checks():
@@ -61,8 +62,8 @@ def test_backward_workspace_checks():
     picks = 16 * 2 * 8
     assert need >= picks * 4 + 64 * 64 * 4 * 3 + picks * 4     # dw + slot sort at least
     assert _lib.workspace_bytes(p, False) == 0
-    # either stage alone accepts the full workspace and rejects a 16-byte one
-    assert _lib.backward_values(p, *[FAKE] * 6, FAKE, 16, None) == 4
+    # the stages that take a workspace reject a 16-byte one
+    assert _lib.slot_sort(p, FAKE, FAKE, FAKE, FAKE, 16, None) == 4
     assert _lib.backward_queries(p, *[FAKE] * 7, FAKE, 16, None) == 4
     args = [FAKE] * 9
     assert _lib.backward(p, *args, FAKE, need - 1, None) == 4

@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """Throughput of the product-key memory layer, forward + backward, on one MI355X.
 
-One step = zero the value gradient, then the whole layer forward (selection,
-gather) and backward (value scatter + softmax backward, query/sub-key
-gradients) over one batch of synthetic tokens resident in HBM.  Every stage is
+One step = the whole layer forward (selection, gather) and backward (slot sort,
+value gradient written in full, softmax backward, query and sub-key gradients)
+over one batch of synthetic tokens resident in HBM.  Every stage is
 a call into libpkm.so's C ABI on the current stream; HIP events recorded on
 that stream between the stages give each kernel's duration inside the timed
 region.  Prints ONE JSON line.
@@ -42,7 +42,7 @@ def parse():
     return ap.parse_args()
 
 
-STAGES = ["zero_dvalues", "select", "gather", "slot_sort", "bwd_values", "bwd_queries"]
+STAGES = ["select", "gather", "slot_sort", "bwd_values", "bwd_queries"]
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "hbm_traffic_base-bf16-zipf-bwd.json")
 
@@ -54,16 +54,16 @@ def stage_bytes(w, elt: int, touched: int) -> dict:
     T, H, k, n, d_k, d_v, half = w.T, w.H, w.k, w.n, w.d_k, w.d_v, w.d_k // 2
     picks, slots = T * H * k, n * n
     return {
-        "zero_dvalues": {"bytes": slots * d_v * 4},
         "select": {"flops": 2 * T * H * 2 * n * half,
                    "bytes": T * H * d_k * elt + H * 2 * n * half * elt + picks * 12},
         # one value row per pick, y written once, idx + weights read
         "gather": {"bytes": picks * d_v * elt + T * d_v * elt + picks * 8},
         # idx read twice, order written, counts/cursors/starts per slot
         "slot_sort": {"bytes": picks * 12 + slots * 16},
-        # each touched value row once, a read-modify-write of each touched
-        # dvalues row, one dy row per pick, per-pick metadata
-        "bwd_values": {"bytes": touched * d_v * (elt + 8) + picks * d_v * elt + picks * 16 + slots * 4},
+        # each touched value row read once, every dvalues row written once
+        # (overwrite mode), one dy row per pick, per-pick metadata
+        "bwd_values": {"bytes": touched * d_v * elt + slots * d_v * 4 + picks * d_v * elt
+                       + picks * 16 + slots * 4},
         # q once, sub-keys once, per-pick metadata, dq written, (i, g) lists
         # written and read, partial sub-key sums written and read
         "bwd_queries": {"bytes": T * H * d_k * elt + H * 2 * n * half * elt + picks * 12
@@ -166,20 +166,18 @@ def main():
             if ev is not None:
                 ev[i].record(stream)
         mark(0)
-        dvalues.zero_()
-        mark(1)
         rc = _lib.forward_select(p, P(q), P(keys), P(idx), P(wts), P(scores), sp)
-        mark(2)
+        mark(1)
         rc |= _lib.forward_gather(p, P(values), P(idx), P(wts), P(y), sp)
-        mark(3)
+        mark(2)
         rc |= _lib.slot_sort(p, P(idx), P(slot_start), P(order), P(ws), ws_bytes, sp)
-        mark(4)
+        mark(3)
         rc |= _lib.backward_values(p, P(values), P(idx), P(wts), P(dy), P(slot_start), P(order),
-                                   P(dvalues), P(dw), sp)
-        mark(5)
+                                   P(dvalues), 0, P(dw), sp)      # dvalues overwritten
+        mark(4)
         rc |= _lib.backward_queries(p, P(q), P(keys), P(idx), P(wts), P(dw), P(dq), P(dkeys),
                                     P(ws), ws_bytes, sp)
-        mark(6)
+        mark(5)
         if rc:
             raise RuntimeError(f"libpkm returned {rc}")
 
@@ -232,7 +230,7 @@ def main():
             entry["traffic"] = traffic[name]["read_bytes"] + traffic[name]["write_bytes"]
         kernels[name] = entry
 
-    dominant = max(STAGES[1:], key=lambda s: per_stage[s])
+    dominant = max(STAGES, key=lambda s: per_stage[s])
     dk = kernels[dominant]
     roofline = {"kernel": dominant, "bound": "hbm", "achieved": dk["GB/s"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(dk["GB/s"] / HBM_PEAK_GBS, 4),
@@ -254,7 +252,7 @@ def main():
         "config": {"workload": w.name, "tokens": T, "heads": H, "n": n, "slots": n * n, "k": k,
                    "d_k": d_k, "d_v": d_v, "storage": w.dtype, "accumulate": "fp32",
                    "zipf": w.zipf, "touched_slots": touched,
-                   "step": "zero dvalues + forward + backward"},
+                   "step": "forward + backward (dvalues overwritten)"},
         "gather": {"GB/s": kernels["gather"]["GB/s"], "hbm_frac": kernels["gather"]["hbm_frac"]},
         "roofline": roofline,
         "kernels": kernels,

@@ -119,9 +119,11 @@ pkm_status_t pkm_forward(const pkm_problem_t *p, const void *q, const void *keys
  *   dy       [T][d_v]           dtype
  *   dq       [T][H][d_k]        float32 OUT, overwritten
  *   dkeys    [H][2][n][d_k/2]   float32 OUT, overwritten
- *   dvalues  [n*n][d_v]         float32 IN/OUT, ACCUMULATED (+=): the caller
- *                               zeroes it before the first call.  Rows no pick
- *                               selects are left untouched.
+ *   dvalues  [n*n][d_v]         float32; dvalues_accumulate != 0: IN/OUT,
+ *                               ACCUMULATED (+=), rows no pick selects are left
+ *                               untouched; dvalues_accumulate == 0: OUT,
+ *                               overwritten (rows no pick selects become 0),
+ *                               which also spares reading the old rows.
  * The order in which float32 partial sums meet (slot sort, atomics on rows
  * shared by several waves) varies from run to run, so results vary at the
  * rounding level.
@@ -129,7 +131,8 @@ pkm_status_t pkm_forward(const pkm_problem_t *p, const void *q, const void *keys
 pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *keys,
                           const void *values, const int32_t *idx, const float *weights,
                           const void *dy, float *dq, float *dkeys, float *dvalues,
-                          void *workspace, size_t workspace_bytes, void *stream);
+                          int dvalues_accumulate, void *workspace, size_t workspace_bytes,
+                          void *stream);
 
 /*
  * The two passes above, stage by stage, for callers that keep the
@@ -163,12 +166,14 @@ pkm_status_t pkm_slot_sort(const pkm_problem_t *p, const int32_t *idx, int32_t *
 
 /* The value side of pkm_backward over the slot-sorted picks: dw [T][H][k]
  * float32 (OUT, overwritten), dw = <dy[t], values[f]>, and the sparse update
- * dvalues[f] += w * dy[t] (ACCUMULATED, as in pkm_backward).  Each value row
- * is read once per run of picks and most rows of dvalues are updated without
- * atomics.  slot_start and order come from pkm_slot_sort on the same idx. */
+ * dvalues[f] += w * dy[t] (accumulated or overwritten, as in pkm_backward).
+ * Each value row is read once per run of picks and most rows of dvalues are
+ * written without atomics.  slot_start and order come from pkm_slot_sort on
+ * the same idx. */
 pkm_status_t pkm_backward_values(const pkm_problem_t *p, const void *values, const int32_t *idx,
                                  const float *weights, const void *dy, const int32_t *slot_start,
-                                 const int32_t *order, float *dvalues, float *dw, void *stream);
+                                 const int32_t *order, float *dvalues, int dvalues_accumulate,
+                                 float *dw, void *stream);
 
 /* The query side of pkm_backward, from weights and dw: the softmax backward,
  * then dq and dkeys (both OUT, overwritten).  Each pick's ds reaches its left

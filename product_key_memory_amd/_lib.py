@@ -60,14 +60,14 @@ def lib() -> ctypes.CDLL:
         L.pkm_workspace_bytes.restype = c_size
         L.pkm_forward.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, c_size, P]
         L.pkm_forward.restype = ctypes.c_int
-        L.pkm_backward.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P, P,
-                                   c_size, P]
+        L.pkm_backward.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P,
+                                   ctypes.c_int, P, c_size, P]
         L.pkm_backward.restype = ctypes.c_int
         PP = ctypes.POINTER(Problem)
         L.pkm_forward_select.argtypes = [PP, P, P, P, P, P, P]
         L.pkm_forward_gather.argtypes = [PP, P, P, P, P, P]
         L.pkm_slot_sort.argtypes = [PP, P, P, P, P, c_size, P]
-        L.pkm_backward_values.argtypes = [PP, P, P, P, P, P, P, P, P, P]
+        L.pkm_backward_values.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_int, P, P]
         L.pkm_backward_queries.argtypes = [PP, P, P, P, P, P, P, P, P, c_size, P]
         for name in ("pkm_forward_select", "pkm_forward_gather", "pkm_slot_sort",
                      "pkm_backward_values", "pkm_backward_queries"):
@@ -91,10 +91,10 @@ def forward(p: Problem, q, keys, values, y, idx, weights, scores, ws, ws_bytes, 
                              ws_bytes, stream)
 
 
-def backward(p: Problem, q, keys, values, idx, weights, dy, dq, dkeys, dvalues, ws, ws_bytes,
-             stream) -> int:
+def backward(p: Problem, q, keys, values, idx, weights, dy, dq, dkeys, dvalues, accumulate,
+             ws, ws_bytes, stream) -> int:
     return lib().pkm_backward(ctypes.byref(p), q, keys, values, idx, weights, dy, dq, dkeys,
-                              dvalues, ws, ws_bytes, stream)
+                              dvalues, int(accumulate), ws, ws_bytes, stream)
 
 
 def forward_select(p: Problem, q, keys, idx, weights, scores, stream) -> int:
@@ -109,10 +109,10 @@ def slot_sort(p: Problem, idx, slot_start, order, ws, ws_bytes, stream) -> int:
     return lib().pkm_slot_sort(ctypes.byref(p), idx, slot_start, order, ws, ws_bytes, stream)
 
 
-def backward_values(p: Problem, values, idx, weights, dy, slot_start, order, dvalues, dw,
-                    stream) -> int:
+def backward_values(p: Problem, values, idx, weights, dy, slot_start, order, dvalues,
+                    accumulate, dw, stream) -> int:
     return lib().pkm_backward_values(ctypes.byref(p), values, idx, weights, dy, slot_start, order,
-                                     dvalues, dw, stream)
+                                     dvalues, int(accumulate), dw, stream)
 
 
 def backward_queries(p: Problem, q, keys, idx, weights, dw, dq, dkeys, ws, ws_bytes,

@@ -168,7 +168,8 @@ pkm_status_t pkm_slot_sort(const pkm_problem_t *p, const int32_t *idx, int32_t *
 
 pkm_status_t pkm_backward_values(const pkm_problem_t *p, const void *values, const int32_t *idx,
                                  const float *weights, const void *dy, const int32_t *slot_start,
-                                 const int32_t *order, float *dvalues, float *dw, void *stream)
+                                 const int32_t *order, float *dvalues, int dvalues_accumulate,
+                                 float *dw, void *stream)
 {
     pkm_status_t st = check_problem(p, true);
     if (st != PKM_OK)
@@ -180,11 +181,15 @@ pkm_status_t pkm_backward_values(const pkm_problem_t *p, const void *values, con
     if (!aligned16(values) || !aligned16(idx) || !aligned16(weights) || !aligned16(dy) ||
         !aligned16(slot_start) || !aligned16(order) || !aligned16(dvalues) || !aligned16(dw))
         return PKM_ERR_ALIGN;
-    if (T == 0)
-        return PKM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0)      // no picks: overwrite leaves an all-zero gradient
+        return dvalues_accumulate || pkm::launch_zero_f32(dvalues, (int64_t)p->n * p->n * p->d_v,
+                                                          s) == hipSuccess
+                   ? PKM_OK
+                   : PKM_ERR_HIP;
     return pkm::launch_bwd_value(p->dtype, values, idx, weights, dy, slot_start, order, dvalues,
-                                 dw, p->T, p->H, p->k, p->d_v,
-                                 static_cast<hipStream_t>(stream)) == hipSuccess
+                                 dvalues_accumulate, dw, p->T, p->H, p->n, p->k, p->d_v,
+                                 s) == hipSuccess
                ? PKM_OK
                : PKM_ERR_HIP;
 }
@@ -222,7 +227,8 @@ pkm_status_t pkm_backward_queries(const pkm_problem_t *p, const void *q, const v
 pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *keys,
                           const void *values, const int32_t *idx, const float *weights,
                           const void *dy, float *dq, float *dkeys, float *dvalues,
-                          void *workspace, size_t workspace_bytes, void *stream)
+                          int dvalues_accumulate, void *workspace, size_t workspace_bytes,
+                          void *stream)
 {
     pkm_status_t st = check_problem(p, true);
     if (st != PKM_OK)
@@ -249,11 +255,11 @@ pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *key
         st = pkm_slot_sort(p, idx, slot_start, order, scratch, scratch_bytes, stream);
         if (st != PKM_OK)
             return st;
-        st = pkm_backward_values(p, values, idx, weights, dy, slot_start, order, dvalues, dw,
-                                 stream);
-        if (st != PKM_OK)
-            return st;
     }
+    st = pkm_backward_values(p, values, idx, weights, dy, slot_start, order, dvalues,
+                             dvalues_accumulate, dw, stream);
+    if (st != PKM_OK)
+        return st;
     return pkm_backward_queries(p, q, keys, idx, weights, dw, dq, dkeys, scratch, scratch_bytes,
                                 stream);
 }

@@ -140,6 +140,26 @@ __global__ void slot_fill_kernel(const int32_t *__restrict__ idx, int64_t picks,
         order[atomicAdd(&cursor[idx[p]], 1)] = (int32_t)p;
 }
 
+// Overwrite mode: zero the dvalues rows no wave will write whole -- rows no
+// pick selected, and rows whose run of sorted picks is cut by a chunk boundary
+// (several waves add into those with atomics).
+__global__ void dv_prepare_kernel(const int32_t *__restrict__ start, int64_t slots, int d_v,
+                                  float *__restrict__ dvalues)
+{
+    const int lane = lane_id();
+    const int64_t f = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (f >= slots)
+        return;
+    const int64_t b = start[f], e = start[f + 1];
+    const bool untouched = b == e;
+    const bool split = !untouched && (b / kSegChunk) != ((e - 1) / kSegChunk);
+    if (!untouched && !split)
+        return;
+    float4 *row = reinterpret_cast<float4 *>(dvalues + f * d_v);
+    for (int c = lane; c < d_v / 4; c += kWave)
+        row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 // ---------------------------------------------------------------------------
 // 2. segmented reduction over the slot-sorted picks
 // ---------------------------------------------------------------------------
@@ -155,7 +175,7 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
     const DT *__restrict__ values, const DT *__restrict__ dy, const int32_t *__restrict__ idx,
     const float *__restrict__ weights, const int32_t *__restrict__ order,
     const int32_t *__restrict__ start, float *__restrict__ dvalues, float *__restrict__ dw,
-    int64_t picks, int HK, int d_v)
+    int64_t picks, int HK, int d_v, int accumulate)
 {
     constexpr int EPC = Elt<DT>::per16;
     __shared__ int32_t s_pk[kSegWaves][kSegChunk];
@@ -185,6 +205,7 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
         const int64_t seg_begin = start[f], seg_end = start[f + 1];
         const int stop = (int)(seg_end - p_begin < len ? seg_end - p_begin : len);
         const bool exclusive = seg_begin >= p_begin && seg_end <= p_begin + len;
+        const bool read_old = exclusive && accumulate;     // overwrite: the wave owns the row
 
         uint4 vraw[MCH];
         float4 dold[MCH][EPC / 4];
@@ -196,7 +217,7 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
             vraw[m] = c < nchunks ? vsrc[c] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
             for (int e = 0; e < EPC / 4; ++e)
-                dold[m][e] = (exclusive && c < nchunks)
+                dold[m][e] = (read_old && c < nchunks)
                                  ? *reinterpret_cast<const float4 *>(drow + (int64_t)c * EPC + 4 * e)
                                  : make_float4(0.f, 0.f, 0.f, 0.f);
         }
@@ -556,13 +577,13 @@ template <typename DT, int MCH, int U>
 static hipError_t launch_seg_t(const void *values, const void *dy, const int32_t *idx,
                                const float *weights, const int32_t *order, const int32_t *start,
                                float *dvalues, float *dw, int64_t picks, int HK, int d_v,
-                               hipStream_t stream)
+                               int accumulate, hipStream_t stream)
 {
     const int64_t waves = (picks + kSegChunk - 1) / kSegChunk;
     hipLaunchKernelGGL((seg_value_kernel<DT, MCH, U>), dim3(grid1d(waves, kSegWaves)),
                        dim3(kSegWaves * kWave), 0, stream, static_cast<const DT *>(values),
                        static_cast<const DT *>(dy), idx, weights, order, start, dvalues, dw, picks,
-                       HK, d_v);
+                       HK, d_v, accumulate);
     return hipGetLastError();
 }
 
@@ -570,19 +591,19 @@ template <typename DT>
 static hipError_t launch_seg_dt(const void *values, const void *dy, const int32_t *idx,
                                 const float *weights, const int32_t *order, const int32_t *start,
                                 float *dvalues, float *dw, int64_t picks, int HK, int d_v,
-                                hipStream_t stream)
+                                int accumulate, hipStream_t stream)
 {
     const int per_lane = (d_v / Elt<DT>::per16 + kWave - 1) / kWave;
     if (per_lane <= 1)
-        return launch_seg_t<DT, 1, 8>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, stream);
+        return launch_seg_t<DT, 1, 8>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, accumulate, stream);
     if (per_lane <= 2)
-        return launch_seg_t<DT, 2, 8>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, stream);
+        return launch_seg_t<DT, 2, 8>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, accumulate, stream);
     if (per_lane <= 4)
-        return launch_seg_t<DT, 4, 2>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, stream);
+        return launch_seg_t<DT, 4, 2>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, accumulate, stream);
     if (per_lane <= 8 || sizeof(DT) == 2)       // bf16 rows of <= 4096 fit 8 chunks per lane
-        return launch_seg_t<DT, 8, 1>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, stream);
+        return launch_seg_t<DT, 8, 1>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, accumulate, stream);
     if constexpr (sizeof(DT) == 4)
-        return launch_seg_t<DT, 16, 1>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, stream);
+        return launch_seg_t<DT, 16, 1>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, accumulate, stream);
     return hipErrorInvalidValue;
 }
 
@@ -612,15 +633,23 @@ hipError_t launch_slot_sort(const int32_t *idx, int64_t picks, int n, int32_t *s
 
 hipError_t launch_bwd_value(int dtype, const void *values, const int32_t *idx,
                             const float *weights, const void *dy, const int32_t *slot_start,
-                            const int32_t *order, float *dvalues, float *dw, int64_t T, int H,
-                            int k, int d_v, hipStream_t stream)
+                            const int32_t *order, float *dvalues, int accumulate, float *dw,
+                            int64_t T, int H, int n, int k, int d_v, hipStream_t stream)
 {
     const int64_t picks = T * H * (int64_t)k;
+    if (!accumulate) {
+        const int64_t slots = (int64_t)n * n;
+        hipLaunchKernelGGL(dv_prepare_kernel, dim3(grid1d(slots, 4)), dim3(4 * kWave), 0, stream,
+                           slot_start, slots, d_v, dvalues);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+    }
     if (dtype == 1)
         return launch_seg_dt<bf16_t>(values, dy, idx, weights, order, slot_start, dvalues, dw,
-                                     picks, H * k, d_v, stream);
+                                     picks, H * k, d_v, accumulate, stream);
     return launch_seg_dt<float>(values, dy, idx, weights, order, slot_start, dvalues, dw, picks,
-                                H * k, d_v, stream);
+                                H * k, d_v, accumulate, stream);
 }
 
 template <typename DT>

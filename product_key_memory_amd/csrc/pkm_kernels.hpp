@@ -79,11 +79,12 @@ hipError_t launch_slot_sort(const int32_t *idx, int64_t picks, int n, int32_t *s
                             int32_t *order, void *scratch, hipStream_t stream);
 
 // Value side of the backward over the slot-sorted picks: dw = <dy, values[slot]>
-// per pick and dvalues[slot] += sum w * dy.
+// per pick and dvalues[slot] (+)= sum w * dy -- accumulated into dvalues when
+// `accumulate`, else dvalues is overwritten (untouched rows become 0).
 hipError_t launch_bwd_value(int dtype, const void *values, const int32_t *idx,
                             const float *weights, const void *dy, const int32_t *slot_start,
-                            const int32_t *order, float *dvalues, float *dw, int64_t T, int H,
-                            int k, int d_v, hipStream_t stream);
+                            const int32_t *order, float *dvalues, int accumulate, float *dw,
+                            int64_t T, int H, int n, int k, int d_v, hipStream_t stream);
 
 // Query side: softmax backward per distinct sub-key, dq (overwritten) and
 // dkeys (overwritten) from weights and dw.  `scratch` holds

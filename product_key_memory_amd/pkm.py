@@ -95,8 +95,8 @@ def pkm_backward(q: torch.Tensor, keys: torch.Tensor, values: torch.Tensor, idx:
                  weights: torch.Tensor, dy: torch.Tensor, dvalues: torch.Tensor | None = None,
                  out=None):
     """Backward pass.  Returns (dq [T,H,d_k], dkeys [H,2,n,d_k/2], dvalues [n*n,d_v]),
-    all float32.  dvalues is ACCUMULATED into when given (zeros are allocated
-    otherwise)."""
+    all float32.  A given dvalues is ACCUMULATED into; otherwise a new one is
+    returned (overwritten by the library: rows no pick selected are 0)."""
     T, H, n, d_k, d_v = _shapes(q, keys, values)
     dev, dt = q.device, q.dtype
     k = idx.shape[2]
@@ -110,8 +110,9 @@ def pkm_backward(q: torch.Tensor, keys: torch.Tensor, values: torch.Tensor, idx:
     ws_bytes = pkm_workspace_bytes(p, True)
     if ws_bytes == (1 << 64) - 1:
         raise PKMError(2, "pkm_backward")
+    accumulate = dvalues is not None
     if dvalues is None:
-        dvalues = torch.zeros((n * n, d_v), dtype=torch.float32, device=dev)
+        dvalues = torch.empty((n * n, d_v), dtype=torch.float32, device=dev)
     else:
         _check(dvalues, "dvalues", (n * n, d_v), torch.float32, dev)
     if out is None:
@@ -121,7 +122,8 @@ def pkm_backward(q: torch.Tensor, keys: torch.Tensor, values: torch.Tensor, idx:
         dq, dkeys = out
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
     rc = _lib.backward(p, _ptr(q), _ptr(keys), _ptr(values), _ptr(idx), _ptr(weights), _ptr(dy),
-                       _ptr(dq), _ptr(dkeys), _ptr(dvalues), _ptr(ws), ws_bytes, _stream(dev))
+                       _ptr(dq), _ptr(dkeys), _ptr(dvalues), accumulate, _ptr(ws), ws_bytes,
+                       _stream(dev))
     if rc != 0:
         raise PKMError(rc, "pkm_backward")
     return dq, dkeys, dvalues

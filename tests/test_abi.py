@@ -52,7 +52,7 @@ def test_null_and_alignment():
     assert _lib.forward(P(), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 1
     assert _lib.forward(P(), FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 6
     assert _lib.forward_select(P(), FAKE, FAKE, None, FAKE, None, None) == 1
-    assert _lib.backward_values(P(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 8, None) == 6
+    assert _lib.backward_values(P(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE + 8, None) == 6
     assert _lib.slot_sort(P(), FAKE, None, FAKE, FAKE, 1 << 30, None) == 1
 
 
@@ -66,9 +66,9 @@ def test_backward_workspace_checks():
     assert _lib.slot_sort(p, FAKE, FAKE, FAKE, FAKE, 16, None) == 4
     assert _lib.backward_queries(p, *[FAKE] * 7, FAKE, 16, None) == 4
     args = [FAKE] * 9
-    assert _lib.backward(p, *args, FAKE, need - 1, None) == 4
-    assert _lib.backward(p, *args, None, 0, None) == 1
-    assert _lib.backward(P(d_v=4104), *args, FAKE, 1 << 30, None) == 2   # backward row limit
+    assert _lib.backward(p, *args, 0, FAKE, need - 1, None) == 4
+    assert _lib.backward(p, *args, 1, None, 0, None) == 1
+    assert _lib.backward(P(d_v=4104), *args, 0, FAKE, 1 << 30, None) == 2   # backward row limit
 
 
 def test_workspace_of_invalid_problem():

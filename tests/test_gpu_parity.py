@@ -151,3 +151,28 @@ def test_autograd_function(orc):
     assert np.allclose(q.grad.cpu().numpy(), ob["dq"], rtol=1e-4, atol=1e-5)
     assert np.allclose(keys.grad.cpu().numpy(), ob["dkeys"], rtol=1e-4, atol=1e-5)
     assert np.allclose(values.grad.cpu().numpy(), ob["dvalues"], rtol=1e-4, atol=1e-5)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_dvalues_accumulate_mode(orc, dtype):
+    """A given dvalues is accumulated into: result - prefill equals the
+    overwrite-mode gradient (same kernels, same sums), rows nobody picked keep
+    the prefill bit for bit."""
+    import product_key_memory_amd as pk
+    dev = gpu_util.device()
+    inp = pkm_inputs.custom(300, 2, 40, 8, 32, 64, dtype=dtype, seed=77)
+    print(f"[accumulate] {dtype}", flush=True)
+    q, keys, values, dy = (gpu_util.to_dev(inp[x], dev) for x in ("q", "keys", "values", "dy"))
+    _, idx, wts, _ = pk.pkm_forward(q, keys, values, 8)
+    _, _, fresh = pk.pkm_backward(q, keys, values, idx, wts, dy)
+    prefill = torch.randn((40 * 40, 64), device=dev)
+    acc = prefill.clone()
+    pk.pkm_backward(q, keys, values, idx, wts, dy, dvalues=acc)
+    torch.cuda.synchronize()
+    touched = torch.zeros(1600, dtype=torch.bool, device=dev)
+    touched[idx.reshape(-1).long()] = True
+    assert torch.equal(acc[~touched], prefill[~touched])
+    assert torch.all(fresh[~touched] == 0)
+    diff = (acc - prefill)[touched].double()
+    ref = fresh[touched].double()
+    assert torch.allclose(diff, ref, rtol=1e-5, atol=1e-6 * ref.abs().max().item())

@@ -3,6 +3,7 @@
 // caller's stream.  Nothing here allocates memory or keeps state.
 #include "pkm.h"
 #include "pkm_kernels.hpp"
+#include "pkm_scratch.hpp"
 
 #include <hip/hip_runtime.h>
 
@@ -43,7 +44,7 @@ size_t starts_bytes(const pkm_problem_t *p) { return pkm::align256(((size_t)p->n
 
 size_t stage_scratch_bytes(const pkm_problem_t *p)
 {
-    const size_t v = pkm::slot_sort_scratch(p->n).total;
+    const size_t v = pkm::slot_sort_scratch(p->T * p->H * p->k, p->n).total;
     const size_t q = pkm::bwd_query_scratch(p->T, p->H, p->n, p->k, p->d_k).total;
     return v > q ? v : q;
 }
@@ -158,7 +159,7 @@ pkm_status_t pkm_slot_sort(const pkm_problem_t *p, const int32_t *idx, int32_t *
         return PKM_ERR_NULL;
     if (!aligned16(workspace))
         return PKM_ERR_ALIGN;
-    if (workspace_bytes < pkm::slot_sort_scratch(p->n).total)
+    if (workspace_bytes < pkm::slot_sort_scratch(p->T * p->H * p->k, p->n).total)
         return PKM_ERR_WORKSPACE;
     return pkm::launch_slot_sort(idx, T * p->H * p->k, p->n, slot_start, order, workspace,
                                  static_cast<hipStream_t>(stream)) == hipSuccess

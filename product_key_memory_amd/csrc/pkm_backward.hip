@@ -6,8 +6,8 @@
 // each score its left and right sub-key scores.
 //
 // Value side (no float atomics on the value gradient in the common case):
-//   1. the T*H*k picks are counting-sorted by slot (histogram, scan, scatter)
-//      into slot_start [n*n + 1] and order [T*H*k];
+//   1. the T*H*k picks are counting-sorted by slot into slot_start [n*n + 1]
+//      and order [T*H*k], in two levels whose counters all sit in LDS;
 //   2. one wave per fixed chunk of the sorted picks walks its slot segments:
 //      the value row of a segment is read once, every pick p of it gives
 //      dw_p = <dy[t_p], values[f]>, and sum_p w_p dy[t_p] is added to
@@ -30,6 +30,7 @@
 //      MFMA registers; a last kernel sums the token blocks' partials.
 #include "pkm_device.hpp"
 #include "pkm_kernels.hpp"
+#include "pkm_scratch.hpp"
 
 namespace pkm {
 
@@ -44,100 +45,171 @@ __device__ __forceinline__ float load_elem<bf16_t>(const bf16_t *p, int64_t i)
 }
 
 // ---------------------------------------------------------------------------
-// 1. counting sort of the picks by slot
+// 1. counting sort of the picks by slot, in two levels so that every counter
+//    lives in LDS: level 1 groups the picks by bucket = slot >> shift (at most
+//    2048 buckets) with per-block histograms; level 2 sorts each bucket by the
+//    low bits of the slot inside one workgroup.
 // ---------------------------------------------------------------------------
-__global__ void slot_count_kernel(const int32_t *__restrict__ idx, int64_t picks,
-                                  int32_t *__restrict__ count)
+constexpr int kL1Threads = 512;
+constexpr int kColWaves = 16;
+constexpr int kColRows = 16;          // block rows per wave in the column scan (blocks <= 256)
+constexpr int kL2Threads = 1024;
+
+__device__ __forceinline__ int64_t l1_begin(int64_t chunk, int64_t picks)
 {
-    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (p < picks)
-        atomicAdd(&count[idx[p]], 1);
+    const int64_t b = (int64_t)blockIdx.x * chunk;
+    return b < picks ? b : picks;
 }
 
-constexpr int kScanBlock = 1024;     // counts per scan block (256 threads x 4)
-
-__global__ __launch_bounds__(256) void scan_block_sums_kernel(const int32_t *__restrict__ count,
-                                                              int64_t slots,
-                                                              int32_t *__restrict__ block_sums)
+// bhist[block][bucket] = number of picks of this block's chunk in the bucket.
+__global__ __launch_bounds__(kL1Threads) void bucket_hist_kernel(
+    const int32_t *__restrict__ idx, int64_t picks, int64_t chunk, int shift, int nb,
+    int32_t *__restrict__ bhist)
 {
-    __shared__ int32_t part[4];
-    const int64_t base = (int64_t)blockIdx.x * kScanBlock;
-    int v = 0;
-    for (int i = threadIdx.x; i < kScanBlock; i += 256)
-        if (base + i < slots)
-            v += count[base + i];
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        v += __shfl_xor(v, m);
-    if (lane_id() == 0)
-        part[threadIdx.x / kWave] = v;
+    __shared__ int32_t h[kMaxBuckets];
+    for (int b = threadIdx.x; b < nb; b += kL1Threads)
+        h[b] = 0;
     __syncthreads();
-    if (threadIdx.x == 0)
-        block_sums[blockIdx.x] = part[0] + part[1] + part[2] + part[3];
+    const int64_t p0 = l1_begin(chunk, picks);
+    const int64_t p1 = p0 + chunk < picks ? p0 + chunk : picks;
+    for (int64_t p = p0 + threadIdx.x; p < p1; p += kL1Threads)
+        atomicAdd(&h[idx[p] >> shift], 1);
+    __syncthreads();
+    int32_t *row = bhist + (int64_t)blockIdx.x * nb;
+    for (int b = threadIdx.x; b < nb; b += kL1Threads)
+        row[b] = h[b];
 }
 
-// start[f] = number of picks with slot < f (f = 0..slots), cursor = copy.
-__global__ __launch_bounds__(256) void scan_apply_kernel(const int32_t *__restrict__ count,
-                                                         const int32_t *__restrict__ block_sums,
-                                                         int64_t slots, int32_t *__restrict__ start,
-                                                         int32_t *__restrict__ cursor)
+// Per bucket (a column of bhist), in place: bhist[block][i] becomes the number
+// of picks of bucket i in the chunks before `block`; total[i] = all of them.
+// One lane per bucket; the 16 waves of a workgroup split the block rows.
+__global__ __launch_bounds__(kColWaves *kWave) void bucket_colscan_kernel(
+    int32_t *__restrict__ bhist, int blocks, int nb, int32_t *__restrict__ total)
 {
-    __shared__ int32_t wsum[4];
-    __shared__ int32_t offset_sh;
-    const int64_t base = (int64_t)blockIdx.x * kScanBlock;
-    // offset of this block = sum of the earlier block sums
+    __shared__ int32_t part[kColWaves][kWave];
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    const int i = blockIdx.x * kWave + lane;
+    const int rows = (blocks + kColWaves - 1) / kColWaves;
+    const int r0 = w * rows;
+    int v[kColRows];
+    int s = 0;
+#pragma unroll
+    for (int r = 0; r < kColRows; ++r) {
+        const bool ok = r < rows && r0 + r < blocks && i < nb;
+        v[r] = ok ? bhist[(int64_t)(r0 + r) * nb + i] : 0;
+        s += v[r];
+    }
+    part[w][lane] = s;
+    __syncthreads();
     int pre = 0;
-    for (int b = threadIdx.x; b < (int)blockIdx.x; b += 256)
-        pre += block_sums[b];
+    for (int u = 0; u < w; ++u)
+        pre += part[u][lane];
+    if (w == kColWaves - 1 && i < nb)
+        total[i] = pre + s;
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        pre += __shfl_xor(pre, m);
-    if (lane_id() == 0)
-        wsum[threadIdx.x / kWave] = pre;
-    __syncthreads();
-    if (threadIdx.x == 0)
-        offset_sh = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
-    const int offset = offset_sh;
-    __syncthreads();
+    for (int r = 0; r < kColRows; ++r) {
+        if (r < rows && r0 + r < blocks && i < nb)
+            bhist[(int64_t)(r0 + r) * nb + i] = pre;
+        pre += v[r];
+    }
+}
 
-    // thread i owns counts [base + 4i, base + 4i + 4)
-    int c[4];
+// Level-1 scatter: bucket_base = exclusive scan of total (block 0 stores it,
+// nb + 1 entries), then every pick of the chunk goes to
+// pairs[base[bucket] + bhist[block][bucket] + rank in block] as
+// (pick id, slot & (2^shift - 1)).
+__global__ __launch_bounds__(kL1Threads) void bucket_scatter_kernel(
+    const int32_t *__restrict__ idx, int64_t picks, int64_t chunk, int shift, int nb,
+    const int32_t *__restrict__ bhist, const int32_t *__restrict__ total,
+    int32_t *__restrict__ bucket_base, int2 *__restrict__ pairs)
+{
+    constexpr int PER = kMaxBuckets / kL1Threads;
+    constexpr int W = kL1Threads / kWave;
+    __shared__ int32_t cur[kMaxBuckets];
+    __shared__ int32_t wsum[W];
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    // thread t owns buckets [PER t, PER t + PER)
+    int c[PER];
     int local = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t f = base + 4 * threadIdx.x + j;
-        c[j] = f < slots ? count[f] : 0;
+    for (int j = 0; j < PER; ++j) {
+        const int b = PER * threadIdx.x + j;
+        c[j] = b < nb ? total[b] : 0;
         local += c[j];
     }
-    int total_w;
-    const int excl_w = wave_exclusive_scan(local, &total_w);
-    if (lane_id() == 0)
-        wsum[threadIdx.x / kWave] = total_w;
+    int tw;
+    const int excl = wave_exclusive_scan(local, &tw);
+    if (lane == 0)
+        wsum[w] = tw;
     __syncthreads();
-    int before = 0;
-    for (int w = 0; w < (int)(threadIdx.x / kWave); ++w)
-        before += wsum[w];
-    int run = offset + before + excl_w;
+    int run = excl;
+    for (int u = 0; u < w; ++u)
+        run += wsum[u];
+    const int32_t *row = bhist + (int64_t)blockIdx.x * nb;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t f = base + 4 * threadIdx.x + j;
-        if (f < slots) {
-            start[f] = run;
-            cursor[f] = run;
+    for (int j = 0; j < PER; ++j) {
+        const int b = PER * threadIdx.x + j;
+        if (b < nb) {
+            cur[b] = run + row[b];
+            if (blockIdx.x == 0)
+                bucket_base[b] = run;
         }
         run += c[j];
     }
-    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 255)
-        start[slots] = run;
+    if (blockIdx.x == 0 && threadIdx.x == kL1Threads - 1)
+        bucket_base[nb] = run;
+    __syncthreads();
+    const int32_t lowmask = (1 << shift) - 1;
+    const int64_t p0 = l1_begin(chunk, picks);
+    const int64_t p1 = p0 + chunk < picks ? p0 + chunk : picks;
+    for (int64_t p = p0 + threadIdx.x; p < p1; p += kL1Threads) {
+        const int32_t f = idx[p];
+        const int pos = atomicAdd(&cur[f >> shift], 1);
+        pairs[pos] = make_int2((int32_t)p, f & lowmask);
+    }
 }
 
-__global__ void slot_fill_kernel(const int32_t *__restrict__ idx, int64_t picks,
-                                 int32_t *__restrict__ cursor, int32_t *__restrict__ order)
+// Level 2, one workgroup per bucket: histogram of the low slot bits in LDS,
+// scan, slot_start of the bucket's 2^shift slots, then every pick's place.
+__global__ __launch_bounds__(kL2Threads) void bucket_sort_kernel(
+    const int2 *__restrict__ pairs, const int32_t *__restrict__ bucket_base, int shift,
+    int64_t slots, int32_t *__restrict__ slot_start, int32_t *__restrict__ order)
 {
-    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (p < picks)
-        order[atomicAdd(&cursor[idx[p]], 1)] = (int32_t)p;
+    constexpr int W = kL2Threads / kWave;
+    __shared__ int32_t h[kMaxBucketSlots];
+    __shared__ int32_t wsum[W];
+    const int B = 1 << shift;
+    const int64_t f0 = (int64_t)blockIdx.x << shift;
+    const int nbins = (int)(slots - f0 < B ? slots - f0 : B);
+    const int beg = bucket_base[blockIdx.x], end = bucket_base[blockIdx.x + 1];
+    for (int j = threadIdx.x; j < B; j += kL2Threads)
+        h[j] = 0;
+    __syncthreads();
+    for (int64_t p = beg + (int)threadIdx.x; p < end; p += kL2Threads)
+        atomicAdd(&h[pairs[p].y], 1);
+    __syncthreads();
+    // exclusive scan of h[0 .. B), B <= kL2Threads: one bin per thread
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    const int v = (int)threadIdx.x < B ? h[threadIdx.x] : 0;
+    int tw;
+    const int excl = wave_exclusive_scan(v, &tw);
+    if (lane == 0)
+        wsum[w] = tw;
+    __syncthreads();
+    int run = beg + excl;
+    for (int u = 0; u < w; ++u)
+        run += wsum[u];
+    if ((int)threadIdx.x < nbins) {
+        h[threadIdx.x] = run;
+        slot_start[f0 + threadIdx.x] = run;
+    }
+    if (f0 + B >= slots && threadIdx.x == 0)
+        slot_start[slots] = end;
+    __syncthreads();
+    for (int64_t p = beg + (int)threadIdx.x; p < end; p += kL2Threads) {
+        const int2 pr = pairs[p];
+        order[atomicAdd(&h[pr.y], 1)] = pr.x;
+    }
 }
 
 // Overwrite mode: zero the dvalues rows no wave will write whole -- rows no
@@ -610,24 +682,21 @@ static hipError_t launch_seg_dt(const void *values, const void *dy, const int32_
 hipError_t launch_slot_sort(const int32_t *idx, int64_t picks, int n, int32_t *slot_start,
                             int32_t *order, void *scratch, hipStream_t stream)
 {
-    const SlotSortScratch S = slot_sort_scratch(n);
+    const SlotSortScratch S = slot_sort_scratch(picks, n);
     char *base = static_cast<char *>(scratch);
-    int32_t *count = reinterpret_cast<int32_t *>(base + S.off_count);
-    int32_t *cursor = reinterpret_cast<int32_t *>(base + S.off_cursor);
-    int32_t *bsums = reinterpret_cast<int32_t *>(base + S.off_bsums);
+    int32_t *bhist = reinterpret_cast<int32_t *>(base + S.off_bhist);
+    int32_t *total = reinterpret_cast<int32_t *>(base + S.off_total);
+    int32_t *bucket_base = reinterpret_cast<int32_t *>(base + S.off_base);
+    int2 *pairs = reinterpret_cast<int2 *>(base + S.off_pairs);
     const int64_t slots = (int64_t)n * n;
-    hipError_t err = launch_zero_f32(reinterpret_cast<float *>(count), slots, stream);
-    if (err != hipSuccess)
-        return err;
-    hipLaunchKernelGGL(slot_count_kernel, dim3(grid1d(picks, 256)), dim3(256), 0, stream, idx,
-                       picks, count);
-    const unsigned sblocks = grid1d(slots, kScanBlock);
-    hipLaunchKernelGGL(scan_block_sums_kernel, dim3(sblocks), dim3(256), 0, stream, count, slots,
-                       bsums);
-    hipLaunchKernelGGL(scan_apply_kernel, dim3(sblocks), dim3(256), 0, stream, count, bsums,
-                       slots, slot_start, cursor);
-    hipLaunchKernelGGL(slot_fill_kernel, dim3(grid1d(picks, 256)), dim3(256), 0, stream, idx,
-                       picks, cursor, order);
+    hipLaunchKernelGGL(bucket_hist_kernel, dim3(S.blocks), dim3(kL1Threads), 0, stream, idx,
+                       picks, S.chunk, S.shift, S.buckets, bhist);
+    hipLaunchKernelGGL(bucket_colscan_kernel, dim3(grid1d(S.buckets, kWave)),
+                       dim3(kColWaves * kWave), 0, stream, bhist, S.blocks, S.buckets, total);
+    hipLaunchKernelGGL(bucket_scatter_kernel, dim3(S.blocks), dim3(kL1Threads), 0, stream, idx,
+                       picks, S.chunk, S.shift, S.buckets, bhist, total, bucket_base, pairs);
+    hipLaunchKernelGGL(bucket_sort_kernel, dim3(S.buckets), dim3(kL2Threads), 0, stream, pairs,
+                       bucket_base, S.shift, slots, slot_start, order);
     return hipGetLastError();
 }
 

@@ -129,6 +129,33 @@ def pkm_backward(q: torch.Tensor, keys: torch.Tensor, values: torch.Tensor, idx:
     return dq, dkeys, dvalues
 
 
+def pkm_slot_sort(idx: torch.Tensor, n: int, out=None):
+    """Groups the picks of idx [T,H,k] int32 by memory slot.  Returns
+    (slot_start [n*n+1] int32, order [T*H*k] int32): the picks (ids
+    t*H*k + h*k + r) of slot f are order[slot_start[f]:slot_start[f+1]]."""
+    if idx.dim() != 3 or idx.dtype != torch.int32 or idx.device.type != "cuda":
+        raise ValueError("idx must be a [T,H,k] int32 GPU tensor")
+    T, H, k = idx.shape
+    dev = idx.device
+    _check(idx, "idx", (T, H, k), torch.int32, dev)
+    # d_k / d_v / dtype do not enter the sort; any admissible values serve
+    p = problem(T, H, n, k, 16, 8, torch.float32)
+    ws_bytes = pkm_workspace_bytes(p, True)
+    if ws_bytes == (1 << 64) - 1:
+        raise PKMError(2, "pkm_slot_sort")
+    if out is None:
+        slot_start = torch.empty(n * n + 1, dtype=torch.int32, device=dev)
+        order = torch.empty(T * H * k, dtype=torch.int32, device=dev)
+    else:
+        slot_start, order = out
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
+    rc = _lib.slot_sort(p, _ptr(idx), _ptr(slot_start), _ptr(order), _ptr(ws), ws_bytes,
+                        _stream(dev))
+    if rc != 0:
+        raise PKMError(rc, "pkm_slot_sort")
+    return slot_start, order
+
+
 class ProductKeyMemoryFunction(torch.autograd.Function):
     """y = PKM(q, keys, values) with the library's backward."""
 

@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kL2Threads) void bucket_sort_kernel(
 }
 
 // Overwrite mode: zero the dvalues rows no wave will write whole -- rows no
-// pick selected, and rows whose run of sorted picks is cut by a chunk boundary
+// pick selected, and rows with a run of more than kSegChunk sorted picks
 // (several waves add into those with atomics).
 __global__ void dv_prepare_kernel(const int32_t *__restrict__ start, int64_t slots, int d_v,
                                   float *__restrict__ dvalues)
@@ -224,7 +224,7 @@ __global__ void dv_prepare_kernel(const int32_t *__restrict__ start, int64_t slo
         return;
     const int64_t b = start[f], e = start[f + 1];
     const bool untouched = b == e;
-    const bool split = !untouched && (b / kSegChunk) != ((e - 1) / kSegChunk);
+    const bool split = e - b > kSegChunk;
     if (!untouched && !split)
         return;
     float4 *row = reinterpret_cast<float4 *>(dvalues + f * d_v);
@@ -237,122 +237,75 @@ __global__ void dv_prepare_kernel(const int32_t *__restrict__ start, int64_t slo
 // ---------------------------------------------------------------------------
 constexpr int kSegWaves = 4;
 
-// MCH: 16-byte chunks of a row per lane; U: picks in flight per wave.  Each
-// wave first stages the (pick, slot, weight) of its chunk in LDS, so inside
-// the loop a dy row address is one LDS read away; a segment's value row and
-// (when the wave owns the whole segment) its dvalues row are fetched together
-// before the first dy rows.
+// MCH: 16-byte chunks of a row per lane; U: picks per group.  Wave w takes
+// the sorted picks of its nominal range [256 w, 256 w + 256), moved so that a
+// slot's run of at most kSegChunk picks is never cut: such a run belongs to
+// the wave whose range holds its first pick (a range grows to < 2 kSegChunk).
+// Longer runs are cut at the nominal bounds.  The wave stages the (pick,
+// token, slot, weight) of its picks in LDS and lists where each run starts,
+// then streams the picks in groups of U with two groups of dy rows in flight;
+// the value row of the next run is fetched while the current one is worked
+// on.  A run's sum is stored (the row is this wave's alone) unless the run is
+// longer than kSegChunk: those rows, zeroed beforehand in overwrite mode, take
+// float atomics from each wave that holds a piece.
+template <int MCH, int U>
+struct DyGroup {
+    uint4 r[U][MCH];
+};
+
+// dy rows of picks j .. j+U-1 of the chunk; picks past its end read as zeros.
+// Exactly U * MCH loads whatever the data, so that the loop's waits stay
+// partial (the other group remains in flight).
 template <typename DT, int MCH, int U>
-__global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
-    const DT *__restrict__ values, const DT *__restrict__ dy, const int32_t *__restrict__ idx,
-    const float *__restrict__ weights, const int32_t *__restrict__ order,
-    const int32_t *__restrict__ start, float *__restrict__ dvalues, float *__restrict__ dw,
-    int64_t picks, int HK, int d_v, int accumulate)
+__device__ __forceinline__ void seg_load_group(DyGroup<MCH, U> &g, const DT *__restrict__ dy,
+                                               const int32_t *s_tok, int j, int len, int d_v,
+                                               int lane)
 {
-    constexpr int EPC = Elt<DT>::per16;
-    __shared__ int32_t s_pk[kSegWaves][kSegChunk];
-    __shared__ int32_t s_tok[kSegWaves][kSegChunk];
-    __shared__ int32_t s_slot[kSegWaves][kSegChunk];
-    __shared__ float s_w[kSegWaves][kSegChunk];
-    const int lane = lane_id();
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t p_begin = ((int64_t)blockIdx.x * kSegWaves + wv) * kSegChunk;
-    if (p_begin >= picks)
-        return;
-    const int len = (int)(picks - p_begin < kSegChunk ? picks - p_begin : kSegChunk);
-    const int nchunks = d_v / EPC;
-
-    for (int j = lane; j < len; j += kWave) {
-        const int32_t pk = order[p_begin + j];
-        s_pk[wv][j] = pk;
-        s_tok[wv][j] = pk / HK;
-        s_slot[wv][j] = idx[pk];
-        s_w[wv][j] = weights[pk];
+    const int row_bytes = d_v * (int)sizeof(DT);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const bool live = j + u < len;
+        const int64_t t = __builtin_amdgcn_readfirstlane(s_tok[live ? j + u : len - 1]);
+        const __amdgpu_buffer_rsrc_t r = buffer_over(dy + t * d_v, live ? row_bytes : 0);
+#pragma unroll
+        for (int m = 0; m < MCH; ++m)
+            g.r[u][m] = buffer_load16(r, (lane + m * kWave) * 16, 0);
     }
-    wave_lds_sync();
+}
 
-    int pos = 0;
-    while (pos < len) {
-        const int f = __builtin_amdgcn_readfirstlane(s_slot[wv][pos]);
-        const int64_t seg_begin = start[f], seg_end = start[f + 1];
-        const int stop = (int)(seg_end - p_begin < len ? seg_end - p_begin : len);
-        const bool exclusive = seg_begin >= p_begin && seg_end <= p_begin + len;
-        const bool read_old = exclusive && accumulate;     // overwrite: the wave owns the row
+template <typename DT, int MCH>
+__device__ __forceinline__ void seg_load_row(uint4 (&v)[MCH], const DT *__restrict__ values,
+                                             int64_t f, int d_v, int lane)
+{
+    const __amdgpu_buffer_rsrc_t r = buffer_over(values + f * d_v, d_v * (int)sizeof(DT));
+#pragma unroll
+    for (int m = 0; m < MCH; ++m)
+        v[m] = buffer_load16(r, (lane + m * kWave) * 16, 0);
+}
 
-        uint4 vraw[MCH];
-        float4 dold[MCH][EPC / 4];
-        const uint4 *vsrc = reinterpret_cast<const uint4 *>(values + (int64_t)f * d_v);
-        float *drow = dvalues + (int64_t)f * d_v;
+template <int MCH, int EPC>
+__device__ __forceinline__ void seg_flush(float (&acc)[MCH][EPC], float *__restrict__ dvalues,
+                                          int64_t f, int d_v, int nchunks, int lane,
+                                          bool exclusive, int accumulate)
+{
+    float *drow = dvalues + f * d_v;
 #pragma unroll
-        for (int m = 0; m < MCH; ++m) {
-            const int c = lane + m * kWave;
-            vraw[m] = c < nchunks ? vsrc[c] : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-            for (int e = 0; e < EPC / 4; ++e)
-                dold[m][e] = (read_old && c < nchunks)
-                                 ? *reinterpret_cast<const float4 *>(drow + (int64_t)c * EPC + 4 * e)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        float vrow[MCH][EPC], acc[MCH][EPC];
-#pragma unroll
-        for (int m = 0; m < MCH; ++m) {
-            unpack16(vraw[m], vrow[m]);
-#pragma unroll
-            for (int e = 0; e < EPC; ++e)
-                acc[m][e] = 0.f;
-        }
-
-        for (int j = pos; j < stop; j += U) {
-            uint4 buf[U][MCH];
-            float wv_u[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const bool live = j + u < stop;
-                const int64_t t = live ? __builtin_amdgcn_readfirstlane(s_tok[wv][j + u]) : 0;
-                wv_u[u] = live ? s_w[wv][j + u] : 0.f;
-                const uint4 *drow_in = reinterpret_cast<const uint4 *>(dy + t * d_v);
-#pragma unroll
-                for (int m = 0; m < MCH; ++m) {
-                    const int c = lane + m * kWave;
-                    buf[u][m] = (live && c < nchunks) ? drow_in[c] : make_uint4(0u, 0u, 0u, 0u);
-                }
-            }
-            float part[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                part[u] = 0.f;
-#pragma unroll
-                for (int m = 0; m < MCH; ++m) {
-                    float g[EPC];
-                    unpack16(buf[u][m], g);
-#pragma unroll
-                    for (int e = 0; e < EPC; ++e) {
-                        part[u] = fmaf(vrow[m][e], g[e], part[u]);
-                        acc[m][e] = fmaf(wv_u[u], g[e], acc[m][e]);
-                    }
-                }
-            }
-            // lane l ends with the dot of pick j + l / (64 / U)
-            wave_multi_sum<U>(part);
-            const int u_mine = lane / (kWave / U);
-            if (lane % (kWave / U) == 0 && j + u_mine < stop)
-                dw[s_pk[wv][j + u_mine]] = part[0];
-        }
-
-#pragma unroll
-        for (int m = 0; m < MCH; ++m) {
-            const int c = lane + m * kWave;
-            if (c >= nchunks)
-                continue;
+    for (int m = 0; m < MCH; ++m) {
+        const int c = lane + m * kWave;
+        if (c < nchunks) {
             float *dst = drow + (int64_t)c * EPC;
             if (exclusive) {
 #pragma unroll
                 for (int e = 0; e < EPC / 4; ++e) {
-                    float4 o = dold[m][e];
-                    o.x += acc[m][4 * e];
-                    o.y += acc[m][4 * e + 1];
-                    o.z += acc[m][4 * e + 2];
-                    o.w += acc[m][4 * e + 3];
+                    float4 o = make_float4(acc[m][4 * e], acc[m][4 * e + 1], acc[m][4 * e + 2],
+                                           acc[m][4 * e + 3]);
+                    if (accumulate) {
+                        const float4 old = *reinterpret_cast<const float4 *>(dst + 4 * e);
+                        o.x += old.x;
+                        o.y += old.y;
+                        o.z += old.z;
+                        o.w += old.w;
+                    }
                     *reinterpret_cast<float4 *>(dst + 4 * e) = o;
                 }
             } else {
@@ -362,8 +315,151 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
                                            __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-        pos = stop;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+            acc[m][e] = 0.f;
     }
+}
+
+template <typename DT, int MCH, int U>
+__global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
+    const DT *__restrict__ values, const DT *__restrict__ dy, const int32_t *__restrict__ idx,
+    const float *__restrict__ weights, const int32_t *__restrict__ order,
+    const int32_t *__restrict__ start, float *__restrict__ dvalues, float *__restrict__ dw,
+    int64_t picks, int HK, int d_v, int accumulate)
+{
+    constexpr int EPC = Elt<DT>::per16;
+    constexpr int kMaxLen = 2 * kSegChunk;
+    __shared__ int32_t s_pk[kSegWaves][kMaxLen];
+    __shared__ int32_t s_tok[kSegWaves][kMaxLen];
+    __shared__ int32_t s_slot[kSegWaves][kMaxLen];
+    __shared__ float s_w[kSegWaves][kMaxLen];
+    __shared__ float s_dw[kSegWaves][kMaxLen];
+    __shared__ int32_t s_seg[kSegWaves][kMaxLen + 1];
+    const int lane = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t nom = ((int64_t)blockIdx.x * kSegWaves + wv) * kSegChunk;
+    if (nom >= picks)
+        return;
+    // a bound inside a run of at most kSegChunk picks moves to the run's end
+    auto run_len = [&](int f) { return start[f + 1] - start[f]; };
+    auto adjust = [&](int64_t p) -> int64_t {
+        if (p == 0 || p >= picks)
+            return p;
+        const int f = idx[order[p]];
+        const int64_t b = start[f], e = start[f + 1];
+        return (p == b || e - b > kSegChunk) ? p : e;
+    };
+    const int64_t p_begin = adjust(nom);
+    const int64_t p_end = adjust(nom + kSegChunk < picks ? nom + kSegChunk : picks);
+    if (p_end <= p_begin)
+        return;
+    const int len = (int)(p_end - p_begin);
+    const int nchunks = d_v / EPC;
+    const int32_t *tok = s_tok[wv];
+    const int32_t *slot = s_slot[wv];
+    int32_t *segs = s_seg[wv];
+
+    for (int j = lane; j < len; j += kWave) {
+        const int32_t pk = order[p_begin + j];
+        s_pk[wv][j] = pk;
+        s_tok[wv][j] = pk / HK;
+        s_slot[wv][j] = idx[pk];
+        s_w[wv][j] = weights[pk];
+    }
+    wave_lds_sync();
+    // segment starts: positions whose slot differs from the previous one
+    int nseg = 0;
+    for (int b = 0; b < len; b += kWave) {
+        const int j = b + lane;
+        const bool head = j < len && (j == 0 || slot[j] != slot[j - 1]);
+        const uint64_t mask = __ballot(head);
+        if (head)
+            segs[nseg + __builtin_popcountll(mask & ((1ull << lane) - 1))] = j;
+        nseg += __builtin_popcountll(mask);
+    }
+    if (lane == 0)
+        segs[nseg] = len;
+    wave_lds_sync();
+
+    // the value rows of segments 0 and 1, two groups of dy rows
+    uint4 vcur[MCH], vnext[MCH];
+    const int f_first = __builtin_amdgcn_readfirstlane(slot[0]);
+    seg_load_row<DT, MCH>(vcur, values, f_first, d_v, lane);
+    seg_load_row<DT, MCH>(vnext, values,
+                          __builtin_amdgcn_readfirstlane(slot[segs[nseg > 1 ? 1 : 0]]), d_v, lane);
+    DyGroup<MCH, U> ga, gb;
+    seg_load_group<DT, MCH, U>(ga, dy, tok, 0, len, d_v, lane);
+    seg_load_group<DT, MCH, U>(gb, dy, tok, U, len, d_v, lane);
+    // only the first and the last run can be long ones, shared with other waves
+    const int f_last = __builtin_amdgcn_readfirstlane(slot[len - 1]);
+    const bool first_split = run_len(f_first) > kSegChunk;
+    const bool last_split = run_len(f_last) > kSegChunk;
+
+    float vrow[MCH][EPC], acc[MCH][EPC];
+#pragma unroll
+    for (int m = 0; m < MCH; ++m) {
+        unpack16(vcur[m], vrow[m]);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+            acc[m][e] = 0.f;
+    }
+    int seg = 0;
+    int seg_end = __builtin_amdgcn_readfirstlane(segs[1]);
+    int f_cur = f_first;
+
+    auto work = [&](DyGroup<MCH, U> &g, int j) {
+        float part[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            part[u] = 0.f;
+            if (j + u < len) {
+                if (j + u == seg_end) {          // next run of slots
+                    seg_flush<MCH, EPC>(acc, dvalues, f_cur, d_v, nchunks, lane,
+                                        !((seg == 0 && first_split) || (seg == nseg - 1 && last_split)),
+                                        accumulate);
+                    ++seg;
+                    seg_end = __builtin_amdgcn_readfirstlane(segs[seg + 1]);
+                    f_cur = __builtin_amdgcn_readfirstlane(slot[j + u]);
+#pragma unroll
+                    for (int m = 0; m < MCH; ++m)
+                        unpack16(vnext[m], vrow[m]);
+                    const int nxt = seg + 1 < nseg ? seg + 1 : seg;
+                    seg_load_row<DT, MCH>(vnext, values,
+                                          __builtin_amdgcn_readfirstlane(slot[segs[nxt]]), d_v,
+                                          lane);
+                }
+                const float w = s_w[wv][j + u];
+#pragma unroll
+                for (int m = 0; m < MCH; ++m) {
+                    float x[EPC];
+                    unpack16(g.r[u][m], x);
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) {
+                        part[u] = fmaf(vrow[m][e], x[e], part[u]);
+                        acc[m][e] = fmaf(w, x[e], acc[m][e]);
+                    }
+                }
+            }
+        }
+        // lane l ends with the dot of pick j + l / (64 / U)
+        wave_multi_sum<U>(part);
+        const int u_mine = lane / (kWave / U);
+        if (lane % (kWave / U) == 0 && j + u_mine < len)
+            s_dw[wv][j + u_mine] = part[0];
+    };
+
+    for (int j = 0; j < len; j += 2 * U) {
+        work(ga, j);
+        seg_load_group<DT, MCH, U>(ga, dy, tok, j + 2 * U, len, d_v, lane);
+        work(gb, j + U);
+        seg_load_group<DT, MCH, U>(gb, dy, tok, j + 3 * U, len, d_v, lane);
+    }
+    seg_flush<MCH, EPC>(acc, dvalues, f_cur, d_v, nchunks, lane,
+                        !((seg == 0 && first_split) || (seg == nseg - 1 && last_split)), accumulate);
+    wave_lds_sync();
+    for (int j = lane; j < len; j += kWave)
+        dw[s_pk[wv][j]] = s_dw[wv][j];
 }
 
 // ---------------------------------------------------------------------------
@@ -669,7 +765,7 @@ static hipError_t launch_seg_dt(const void *values, const void *dy, const int32_
     if (per_lane <= 1)
         return launch_seg_t<DT, 1, 8>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, accumulate, stream);
     if (per_lane <= 2)
-        return launch_seg_t<DT, 2, 8>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, accumulate, stream);
+        return launch_seg_t<DT, 2, 4>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, accumulate, stream);
     if (per_lane <= 4)
         return launch_seg_t<DT, 4, 2>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, accumulate, stream);
     if (per_lane <= 8 || sizeof(DT) == 2)       // bf16 rows of <= 4096 fit 8 chunks per lane

@@ -109,13 +109,16 @@ __device__ __forceinline__ void wave_multi_sum(float (&v)[U])
     for (int stride = 32; stride >= 1; stride >>= 1) {
         if (width > 1) {
             // lanes with the stride bit set keep the upper half of the values
-            const bool upper = (lane & stride) != 0;
+            // bit masks instead of a select between two array elements, which
+            // the compiler may turn into a private-memory indexed load
+            const uint32_t up = (lane & stride) != 0 ? 0xffffffffu : 0u;
             const int h = width / 2;
 #pragma unroll
             for (int j = 0; j < U / 2; ++j) {
                 if (j < h) {
-                    const float send = upper ? v[j] : v[j + h];
-                    const float keep = upper ? v[j + h] : v[j];
+                    const uint32_t a = __float_as_uint(v[j]), b = __float_as_uint(v[j + h]);
+                    const float send = __uint_as_float((a & up) | (b & ~up));
+                    const float keep = __uint_as_float((b & up) | (a & ~up));
                     v[j] = keep + __shfl_xor(send, stride);
                 }
             }
@@ -124,6 +127,20 @@ __device__ __forceinline__ void wave_multi_sum(float (&v)[U])
             v[0] += __shfl_xor(v[0], stride);
         }
     }
+}
+
+// Buffer descriptor over `bytes` bytes at p: loads that reach past the end
+// return zeros, so loads can be issued unconditionally (a fixed count of
+// memory operations per loop trip keeps the compiler's waits partial).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void *p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voffset, int soffset)
+{
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 // Exclusive prefix sum over the 64 lanes; *total receives the wave total.

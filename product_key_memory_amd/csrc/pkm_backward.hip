@@ -23,7 +23,8 @@
 //                                      B = sum_notS w dw, 1 - W = sum_notS w,
 //      both complements summed directly, so a sub-key shared by most picks
 //      (a near-cancelling sum) keeps full relative accuracy;
-//      dq = sum_i g_i * sub-key row i, and (i, g_i) goes to a compact list;
+//      dq = sum_i g_i * sub-key row i (the rows of the distinct sub-keys are
+//      fetched in batches), and (i, g_i) goes to a compact list;
 //   4. dkeys[h][s][i] = sum_t g * q_half[t]: each workgroup owns one token
 //      block and 64 columns of one codebook and accumulates the product of
 //      the sparse g matrix (densified per 32-token step in LDS) with q in
@@ -466,79 +467,176 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
 // 3. softmax backward per distinct sub-key, dq, compact (i, g) lists
 // ---------------------------------------------------------------------------
 constexpr int kQryWaves = 4;
-constexpr int kMaxHalfPerLane = 8;   // half <= 512
+constexpr int kQryMaxK = 64;
 
+// Four consecutive elements of a sub-key row through a buffer descriptor
+// (offsets past the codebook read as zeros): raw load, then widening.
 template <typename DT>
+struct Row4;
+template <>
+struct Row4<float> {
+    uint4 raw;
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int voff)
+    {
+        raw = buffer_load16(r, voff, 0);
+    }
+    __device__ __forceinline__ float operator[](int e) const
+    {
+        return __uint_as_float(e == 0 ? raw.x : e == 1 ? raw.y : e == 2 ? raw.z : raw.w);
+    }
+};
+template <>
+struct Row4<bf16_t> {
+    uint32_t lo, hi;
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int voff)
+    {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+        lo = v[0];
+        hi = v[1];
+    }
+    __device__ __forceinline__ float operator[](int e) const
+    {
+        const uint32_t w = e < 2 ? lo : hi;
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+
+// One wave per (token, head).  For k <= 32 one pass gives each lane one
+// (half, pick): lanes 0-31 the left sub-keys, lanes 32-63 the right ones;
+// for larger k two passes, one half each.  A lane's sums A, W, B, Wc run over
+// the picks staged in LDS (one broadcast read per pick).  The distinct
+// sub-keys of both halves then form one list, and their rows are fetched in
+// batches of kBatch before they are used: in the dq product each lane owns JPL
+// groups of 4 consecutive elements of a half (half <= 256 JPL).
+template <typename DT, int JPL>
 __global__ __launch_bounds__(kQryWaves *kWave) void bwd_query_kernel(
     const DT *__restrict__ keys, const int32_t *__restrict__ idx,
     const float *__restrict__ weights, const float *__restrict__ dw, float *__restrict__ dq,
     int32_t *__restrict__ gl_i, float *__restrict__ gl_g, int64_t T, int H, int n, int k, int d_k)
 {
+    constexpr int kBatch = (sizeof(DT) == 2 ? 32 : 16) / JPL;     // sub-key rows in flight
+    __shared__ int4 s_pick[kQryWaves][kQryMaxK];                   // left, right, w, w dw
+    __shared__ int32_t s_sub[kQryWaves][kWave];      // distinct (half * n + sub), <= 64 a pass
+    __shared__ float s_g[kQryWaves][kWave];
     const int lane = lane_id();
-    const int64_t row = (int64_t)blockIdx.x * kQryWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t row = (int64_t)blockIdx.x * kQryWaves + wv;
     if (row >= T * H)
         return;
     const int h = (int)(row % H);
     const int half = d_k / 2;
+    const int groups = half / 4;
     const int64_t base = row * (int64_t)k;
-    const int f = lane < k ? idx[base + lane] : 0;
-    const float w_mine = lane < k ? weights[base + lane] : 0.f;
-    const float wdw_mine = lane < k ? w_mine * dw[base + lane] : 0.f;
+    if (lane < k) {
+        const int f = idx[base + lane];
+        const float w = weights[base + lane];
+        s_pick[wv][lane] = make_int4(f / n, f % n, __float_as_int(w),
+                                     __float_as_int(w * dw[base + lane]));
+    }
+    wave_lds_sync();
 
-    for (int s = 0; s < 2; ++s) {
-        const int sub = s == 0 ? f / n : f % n;
+    const int passes = k <= kWave / 2 ? 1 : 2;
+    const DT *kh = keys + (int64_t)h * 2 * n * half;
+    const __amdgpu_buffer_rsrc_t rsrc = buffer_over(kh, 2 * n * half * (int)sizeof(DT));
+    constexpr int kOut = 0x40000000;      // an offset past any codebook: reads zeros
+    float acc[2][JPL][4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int j = 0; j < JPL; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc[s][j][e] = 0.f;
+
+    for (int pass = 0; pass < passes; ++pass) {
+        const int s = passes == 1 ? lane / (kWave / 2) : pass;
+        const int r = passes == 1 ? lane % (kWave / 2) : lane;
+        const bool valid = r < k;
+        const int4 mine = s_pick[wv][valid ? r : 0];
+        const int sub = s == 0 ? mine.x : mine.y;
         // sums over the picks sharing this lane's sub-key (A, W) and over the
         // rest (B, Wc); the first pick of each sub-key carries its g
+        // (selects, not branches: the loop stays free of exec-mask updates)
         float A = 0.f, W = 0.f, B = 0.f, Wc = 0.f;
-        bool first = lane < k;
-        for (int r = 0; r < k; ++r) {
-            const int sub_r = __shfl(sub, r);
-            const float w_r = __shfl(w_mine, r);
-            const float wdw_r = __shfl(wdw_mine, r);
-            if (sub_r == sub) {
-                A += wdw_r;
-                W += w_r;
-                if (r < lane)
-                    first = false;
-            } else {
-                B += wdw_r;
-                Wc += w_r;
-            }
+        uint32_t earlier = 0;      // an earlier pick has this sub-key
+        for (int q = 0; q < k; ++q) {
+            const int4 e = s_pick[wv][q];
+            const int sub_q = s == 0 ? e.x : e.y;
+            const float w_q = __int_as_float(e.z), wdw_q = __int_as_float(e.w);
+            const bool same = sub_q == sub;
+            A += same ? wdw_q : 0.f;
+            W += same ? w_q : 0.f;
+            B += same ? 0.f : wdw_q;
+            Wc += same ? 0.f : w_q;
+            earlier |= (uint32_t)(same & (q < r));
         }
+        const bool first = valid && earlier == 0;
         const float g = A * Wc - B * W;
-        const int64_t lbase = (row * 2 + s) * (int64_t)k;
-        if (lane < k) {
-            gl_i[lbase + lane] = sub;
-            gl_g[lbase + lane] = first ? g : 0.f;
+        if (valid) {
+            const int64_t at = (row * 2 + s) * (int64_t)k + r;
+            gl_i[at] = sub;
+            gl_g[at] = first ? g : 0.f;
         }
+        // the distinct sub-keys of this pass (left ones first), compacted:
+        // lane u then holds entry u (as codebook row s * n + sub and its g
+        // split by half); lanes past the list hold a row past the codebooks
+        // (reads zeros) with g = 0
+        const uint64_t mask = __ballot(first);
+        const int cnt = __builtin_popcountll(mask);
+        if (first) {
+            const int rank = __builtin_popcountll(mask & ((1ull << lane) - 1));
+            s_sub[wv][rank] = s * n + sub;
+            s_g[wv][rank] = g;
+        }
+        wave_lds_sync();
+        const bool in_list = lane < cnt;
+        const int l_row = in_list ? s_sub[wv][lane] : 2 * n;
+        const float l_g = in_list ? s_g[wv][lane] : 0.f;
+        const float l_g0 = l_row < n ? l_g : 0.f, l_g1 = l_row < n ? 0.f : l_g;
 
-        const DT *kb = keys + ((int64_t)h * 2 + s) * (int64_t)n * half;
-        float acc[kMaxHalfPerLane];
+        // dq halves += g * sub-key row, kBatch rows in flight
 #pragma unroll
-        for (int j = 0; j < kMaxHalfPerLane; ++j)
-            acc[j] = 0.f;
-        uint64_t todo = __ballot(first);
-        while (todo) {
-            const int r = __builtin_ctzll(todo);
-            todo &= todo - 1;
-            const int sub_r = __shfl(sub, r);
-            const float g_r = __shfl(g, r);
-            const DT *krow = kb + (int64_t)sub_r * half;
+        for (int b = 0; b < kWave / kBatch; ++b) {
+            if (b * kBatch >= cnt)
+                break;
+            Row4<DT> x[kBatch][JPL];
 #pragma unroll
-            for (int j = 0; j < kMaxHalfPerLane; ++j) {
-                const int c = lane + j * kWave;
-                if (c < half)
-                    acc[j] = fmaf(g_r, load_elem(krow, c), acc[j]);
+            for (int u = 0; u < kBatch; ++u) {
+                const int sr = __builtin_amdgcn_readlane(l_row, b * kBatch + u);
+#pragma unroll
+                for (int j = 0; j < JPL; ++j) {
+                    const int c = lane + j * kWave;
+                    const int voff = c < groups ? (sr * half + 4 * c) * (int)sizeof(DT) : kOut;
+                    x[u][j].load(rsrc, voff);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const float g0 = __int_as_float(
+                    __builtin_amdgcn_readlane(__float_as_int(l_g0), b * kBatch + u));
+                const float g1 = __int_as_float(
+                    __builtin_amdgcn_readlane(__float_as_int(l_g1), b * kBatch + u));
+#pragma unroll
+                for (int j = 0; j < JPL; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[0][j][e] = fmaf(g0, x[u][j][e], acc[0][j][e]);
+                        acc[1][j][e] = fmaf(g1, x[u][j][e], acc[1][j][e]);
+                    }
             }
         }
-        float *dqh = dq + row * (int64_t)d_k + (int64_t)s * half;
-#pragma unroll
-        for (int j = 0; j < kMaxHalfPerLane; ++j) {
-            const int c = lane + j * kWave;
-            if (c < half)
-                dqh[c] = acc[j];
-        }
+        wave_lds_sync();     // s_sub / s_g are rewritten by the next pass
     }
+    float *dqr = dq + row * (int64_t)d_k;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int j = 0; j < JPL; ++j) {
+            const int c = lane + j * kWave;
+            if (c < groups)
+                *reinterpret_cast<float4 *>(dqr + s * half + 4 * c) =
+                    make_float4(acc[s][j][0], acc[s][j][1], acc[s][j][2], acc[s][j][3]);
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -829,9 +927,14 @@ static hipError_t launch_query_t(const void *q, const void *keys, const int32_t 
     float *gl_g = reinterpret_cast<float *>(base + S.off_gl_g);
     float *partial = reinterpret_cast<float *>(base + S.off_partial);
     const int64_t rows = T * H;
-    hipLaunchKernelGGL(bwd_query_kernel<DT>, dim3(grid1d(rows, kQryWaves)),
-                       dim3(kQryWaves * kWave), 0, stream, static_cast<const DT *>(keys), idx,
-                       weights, dw, dq, gl_i, gl_g, T, H, n, k, d_k);
+    if (d_k / 2 <= 4 * kWave)
+        hipLaunchKernelGGL((bwd_query_kernel<DT, 1>), dim3(grid1d(rows, kQryWaves)),
+                           dim3(kQryWaves * kWave), 0, stream, static_cast<const DT *>(keys), idx,
+                           weights, dw, dq, gl_i, gl_g, T, H, n, k, d_k);
+    else
+        hipLaunchKernelGGL((bwd_query_kernel<DT, 2>), dim3(grid1d(rows, kQryWaves)),
+                           dim3(kQryWaves * kWave), 0, stream, static_cast<const DT *>(keys), idx,
+                           weights, dw, dq, gl_i, gl_g, T, H, n, k, d_k);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;

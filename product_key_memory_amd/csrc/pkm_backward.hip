@@ -644,150 +644,262 @@ __global__ __launch_bounds__(kQryWaves *kWave) void bwd_query_kernel(
 // ---------------------------------------------------------------------------
 // dkeys[h][s] = dS^T q_s, where dS [T][n] holds, per token, the g of each
 // distinct sub-key of its k picks and zeros elsewhere.  A workgroup owns one
-// token block and 64 columns of one codebook; per step of 32 tokens it
+// token block and 16 CT columns of one codebook; per step of 32 tokens it
 // scatters the (sub-key, g) entries into a zeroed LDS tile dS^T [n][32] (no
-// two entries share a cell, so plain stores), stages q's 64 columns
-// transposed [64][32], and accumulates [n][64] in MFMA registers: wave w owns
-// the 16-row tiles w, w+16, ...  No atomics, so hot sub-keys cost nothing
-// extra and the result does not depend on timing.
+// two entries share a cell, so plain stores), stages q's columns transposed
+// [16 CT][32], and accumulates [n][16 CT] in MFMA registers: wave w owns
+// the 16-row tiles w, w + 16, ... and loads each of their A fragments once per
+// step for all column tiles.  The global reads of step i + 1 are issued
+// before the MFMAs of step i.  Tiles keep 16-byte chunks XOR-swizzled by row,
+// so the 16 rows an MFMA operand read touches fall in distinct banks.  No
+// atomics, so hot sub-keys cost nothing extra and the result does not depend
+// on timing.
 //   bf16 storage: g = hi + lo (two bfloat16, ~16 significant bits), q exact in
 //     bfloat16, v_mfma_f32_16x16x32_bf16 twice per tile: exact products,
 //     float32 sums;
 //   float32 storage: v_mfma_f32_16x16x4_f32 on the float32 values.
 constexpr int kDkWaves = 16;
 constexpr int kDkTok = 32;          // tokens per step (the MFMA K extent)
-constexpr int kDkCols = 64;         // columns per workgroup (4 MFMA N blocks)
-constexpr int kDkMaxTiles = 4;      // 16-row tiles per wave: n <= 16 * 16 * 4
 
 template <typename DT> struct DkTile;
-template <> struct DkTile<bf16_t> { typedef uint16_t elt; static constexpr int parts = 2; };
-template <> struct DkTile<float> { typedef float elt; static constexpr int parts = 1; };
+template <> struct DkTile<bf16_t> {
+    typedef uint16_t elt;
+    static constexpr int parts = 2;
+    static constexpr int chunks = 4;        // 16-byte chunks in a row of 32 tokens
+};
+template <> struct DkTile<float> {
+    typedef float elt;
+    static constexpr int parts = 1;
+    static constexpr int chunks = 8;
+};
 
-__device__ __forceinline__ floatx4 dk_mfma(const uint16_t *a_row, const uint16_t *b_row, int kg,
-                                           floatx4 acc)
+// Element offset of (row, token) in a [rows][32] tile whose 16-byte chunks
+// are XOR-swizzled by row: the 16 rows of an operand read cover all banks.
+template <int C>
+__device__ __forceinline__ int dk_cell(int row, int tl)
 {
-    const uint4 a = *reinterpret_cast<const uint4 *>(a_row + 8 * kg);
-    const uint4 b = *reinterpret_cast<const uint4 *>(b_row + 8 * kg);
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
-}
-__device__ __forceinline__ floatx4 dk_mfma(const float *a_row, const float *b_row, int kg,
-                                           floatx4 acc)
-{
-    // K = 32 tokens as 2 x 4 consecutive per lane group; A and B share the order
-#pragma unroll
-    for (int half_k = 0; half_k < 2; ++half_k) {
-        const float4 a = *reinterpret_cast<const float4 *>(a_row + 16 * half_k + 4 * kg);
-        const float4 b = *reinterpret_cast<const float4 *>(b_row + 16 * half_k + 4 * kg);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc, 0, 0, 0);
-    }
-    return acc;
+    constexpr int EPC = kDkTok / C;                 // elements per chunk
+    const int c = (tl / EPC) ^ ((row / (16 / C)) % C);
+    return row * kDkTok + c * EPC + tl % EPC;
 }
 
-__device__ __forceinline__ void dk_store(uint16_t *hi, uint16_t *lo, size_t at, float g)
+__device__ __forceinline__ uint4 dk_chunk(const uint16_t *tile, int row, int c)
+{
+    return *reinterpret_cast<const uint4 *>(tile + dk_cell<4>(row, 8 * c));
+}
+__device__ __forceinline__ float4 dk_chunk(const float *tile, int row, int c)
+{
+    return *reinterpret_cast<const float4 *>(tile + dk_cell<8>(row, 4 * c));
+}
+
+__device__ __forceinline__ void dk_store(uint16_t *hi, uint16_t *lo, int at, float g)
 {
     const uint32_t h = f32_to_bf16_bits(g);
     hi[at] = (uint16_t)h;
     lo[at] = (uint16_t)f32_to_bf16_bits(g - bf16_to_f32(h));
 }
-__device__ __forceinline__ void dk_store(float *a, float *, size_t at, float g) { a[at] = g; }
-__device__ __forceinline__ void dk_clear(uint16_t *hi, uint16_t *lo, size_t at)
+__device__ __forceinline__ void dk_store(float *a, float *, int at, float g) { a[at] = g; }
+__device__ __forceinline__ void dk_clear(uint16_t *hi, uint16_t *lo, int at)
 {
     hi[at] = 0;
     lo[at] = 0;
 }
-__device__ __forceinline__ void dk_clear(float *a, float *, size_t at) { a[at] = 0.f; }
-__device__ __forceinline__ uint16_t dk_q(const bf16_t *q, int64_t i)
-{
-    return reinterpret_cast<const uint16_t *>(q)[i];
-}
-__device__ __forceinline__ float dk_q(const float *q, int64_t i) { return q[i]; }
+__device__ __forceinline__ void dk_clear(float *a, float *, int at) { a[at] = 0.f; }
 
-template <typename DT>
+// q staging of one step.  bf16: thread u < 256 takes the token pair
+// (2 (u % 16), + 1) and 8 columns 8 (u / 16) ..: two 16-byte loads, eight
+// packed 4-byte LDS stores.  float32: thread u takes token u % 32 and 4
+// columns 4 (u / 32) ..: one 16-byte load, four LDS stores.
+struct DkQBf16 {
+    uint4 a, b;
+};
+struct DkQF32 {
+    float4 a;
+};
+template <typename DT> struct DkQ;
+template <> struct DkQ<bf16_t> { typedef DkQBf16 type; };
+template <> struct DkQ<float> { typedef DkQF32 type; };
+
+template <int CT>
+__device__ __forceinline__ void dk_q_load(DkQBf16 &v, const bf16_t *q, int64_t t0, int64_t t_end,
+                                          int H, int h, int d_k, int col0, int half, int tid)
+{
+    v.a = v.b = make_uint4(0u, 0u, 0u, 0u);
+    if (tid >= 16 * (16 * CT / 8))
+        return;
+    const int tp = tid % 16, cg = tid / 16;
+    const int col = col0 + 8 * cg;
+    if (col >= half)
+        return;
+    const int64_t ta = t0 + 2 * tp, tb = ta + 1;
+    const uint16_t *qb = reinterpret_cast<const uint16_t *>(q);
+    if (ta < t_end)
+        v.a = *reinterpret_cast<const uint4 *>(qb + (ta * H + h) * (int64_t)d_k + col);
+    if (tb < t_end)
+        v.b = *reinterpret_cast<const uint4 *>(qb + (tb * H + h) * (int64_t)d_k + col);
+}
+template <int CT>
+__device__ __forceinline__ void dk_q_store(const DkQBf16 &v, uint16_t *bt, int tid)
+{
+    if (tid >= 16 * (16 * CT / 8))
+        return;
+    const int tp = tid % 16, cg = tid / 16;
+    const uint32_t a[4] = {v.a.x, v.a.y, v.a.z, v.a.w}, b[4] = {v.b.x, v.b.y, v.b.z, v.b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = (i & 1) ? a[i / 2] >> 16 : a[i / 2] & 0xffffu;
+        const uint32_t hi = (i & 1) ? b[i / 2] >> 16 : b[i / 2] & 0xffffu;
+        *reinterpret_cast<uint32_t *>(bt + dk_cell<4>(8 * cg + i, 2 * tp)) = lo | (hi << 16);
+    }
+}
+template <int CT>
+__device__ __forceinline__ void dk_q_load(DkQF32 &v, const float *q, int64_t t0, int64_t t_end,
+                                          int H, int h, int d_k, int col0, int half, int tid)
+{
+    v.a = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int tl = tid % kDkTok, cg = tid / kDkTok;
+    const int col = col0 + 4 * cg;
+    const int64_t t = t0 + tl;
+    if (cg < 16 * CT / 4 && col < half && t < t_end)
+        v.a = *reinterpret_cast<const float4 *>(q + (t * H + h) * (int64_t)d_k + col);
+}
+template <int CT>
+__device__ __forceinline__ void dk_q_store(const DkQF32 &v, float *bt, int tid)
+{
+    const int tl = tid % kDkTok, cg = tid / kDkTok;
+    if (cg >= 16 * CT / 4)
+        return;
+    const float a[4] = {v.a.x, v.a.y, v.a.z, v.a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        bt[dk_cell<8>(4 * cg + i, tl)] = a[i];
+}
+
+// One 16 x 16 x 32-token product on fragments read from the swizzled tiles.
+__device__ __forceinline__ floatx4 dk_mfma(const uint4 &a, const uint4 &b, floatx4 acc)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
+template <typename DT, int RT, int CT>
 __global__ __launch_bounds__(kDkWaves *kWave) void dkeys_mfma_kernel(
     const DT *__restrict__ q, const int32_t *__restrict__ gl_i, const float *__restrict__ gl_g,
     float *__restrict__ partial, int64_t T, int H, int n, int k, int d_k, int tokens_per_block)
 {
     typedef typename DkTile<DT>::elt E;
     constexpr int PARTS = DkTile<DT>::parts;
+    constexpr int C = DkTile<DT>::chunks;
     extern __shared__ __align__(16) unsigned char smem[];
     const int n_pad = (n + 15) & ~15;
     E *a_hi = reinterpret_cast<E *>(smem);                      // [n_pad][32]
     E *a_lo = a_hi + (PARTS == 2 ? (size_t)n_pad * kDkTok : 0);  // [n_pad][32] (bf16 only)
-    E *bt = a_hi + (size_t)PARTS * n_pad * kDkTok;                // [64][32]
+    E *bt = a_hi + (size_t)PARTS * n_pad * kDkTok;                // [16 CT][32]
 
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
     const int tid = threadIdx.x;
     const int half = d_k / 2;
-    const int ncb = (half + kDkCols - 1) / kDkCols;
+    constexpr int CW = 16 * CT;
+    const int ncb = (half + CW - 1) / CW;
     const int hs = blockIdx.y / ncb;
-    const int c0 = (blockIdx.y % ncb) * kDkCols;
-    const int width = half - c0 < kDkCols ? half - c0 : kDkCols;
+    const int c0 = (blockIdx.y % ncb) * CW;
+    const int width = half - c0 < CW ? half - c0 : CW;
     const int h = hs / 2, s = hs % 2;
     const int ntiles = n_pad / 16;
+    const DT *qs = q + (int64_t)s * half;
 
-    for (size_t e = tid; e < (size_t)(PARTS * n_pad + kDkCols) * kDkTok; e += kDkWaves * kWave)
+    for (int e = tid; e < (PARTS * n_pad + CW) * kDkTok; e += kDkWaves * kWave)
         a_hi[e] = (E)0;
 
-    floatx4 acc[kDkMaxTiles][4];
+    floatx4 acc[RT][CT];
 #pragma unroll
-    for (int ti = 0; ti < kDkMaxTiles; ++ti)
+    for (int ti = 0; ti < RT; ++ti)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < CT; ++nb)
             acc[ti][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     const int64_t t_begin = (int64_t)blockIdx.x * tokens_per_block;
     const int64_t t_end = t_begin + tokens_per_block < T ? t_begin + tokens_per_block : T;
     const int pairs = kDkTok * k;                 // (token, pick) pairs per step, <= 2048
-    int mine_at[2] = {-1, -1};                    // cells this thread wrote
-    __syncthreads();
 
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += kDkTok) {
-        // scatter the step's entries into dS^T, stage q^T
+    // this thread's entries of a step: g and the tile cell (or -1)
+    auto load_entries = [&](int64_t t0, float (&g)[2], int (&cell)[2]) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int pr = tid + j * kDkWaves * kWave;
-            mine_at[j] = -1;
+            g[j] = 0.f;
+            cell[j] = -1;
             if (pr < pairs) {
                 const int tl = pr / k, r = pr % k;
                 const int64_t t = t0 + tl;
                 if (t < t_end) {
                     const int64_t at = ((t * H + h) * 2 + s) * (int64_t)k + r;
-                    const float g = gl_g[at];
-                    if (g != 0.f) {
-                        const int cell = gl_i[at] * kDkTok + tl;
-                        dk_store(a_hi, a_lo, cell, g);
-                        mine_at[j] = cell;
-                    }
+                    g[j] = gl_g[at];
+                    cell[j] = gl_i[at] * 64 + tl;      // row * 64 + token, decoded below
                 }
             }
-            const int qe = tid + j * kDkWaves * kWave;      // 2048 = 64 columns x 32 tokens
-            const int d = qe % kDkCols, tl = qe / kDkCols;
-            const int64_t t = t0 + tl;
-            E v = (E)0;
-            if (d < width && t < t_end)
-                v = dk_q(q, (t * H + h) * (int64_t)d_k + (int64_t)s * half + c0 + d);
-            bt[d * kDkTok + tl] = v;
+        }
+    };
+    float g_next[2];
+    int cell_next[2];
+    typename DkQ<DT>::type q_next;
+    load_entries(t_begin, g_next, cell_next);
+    dk_q_load<CT>(q_next, qs, t_begin, t_end, H, h, d_k, c0, half, tid);
+    int mine_at[2] = {-1, -1};                    // cells this thread wrote
+    __syncthreads();
+
+    const int r16 = lane & 15, kg = lane >> 4;
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += kDkTok) {
+        // scatter this step's entries into dS^T, stage q^T
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            mine_at[j] = -1;
+            if (cell_next[j] >= 0 && g_next[j] != 0.f) {
+                const int at = dk_cell<C>(cell_next[j] / 64, cell_next[j] % 64);
+                dk_store(a_hi, a_lo, at, g_next[j]);
+                mine_at[j] = at;
+            }
+        }
+        dk_q_store<CT>(q_next, bt, tid);
+        // the next step's global reads fly during this step's products
+        if (t0 + kDkTok < t_end) {
+            load_entries(t0 + kDkTok, g_next, cell_next);
+            dk_q_load<CT>(q_next, qs, t0 + kDkTok, t_end, H, h, d_k, c0, half, tid);
         }
         __syncthreads();
 
-        const int r16 = lane & 15, kg = lane >> 4;
 #pragma unroll
-        for (int ti = 0; ti < kDkMaxTiles; ++ti) {
+        for (int ti = 0; ti < RT; ++ti) {
             const int tile = wave + ti * kDkWaves;
             if (tile < ntiles) {
-                const E *arow_hi = a_hi + (size_t)(tile * 16 + r16) * kDkTok;
-                const E *arow_lo = a_lo + (size_t)(tile * 16 + r16) * kDkTok;
+                const int row = tile * 16 + r16;
+                if constexpr (PARTS == 2) {
+                    const uint4 ah = dk_chunk(a_hi, row, kg), al = dk_chunk(a_lo, row, kg);
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
-                    const E *brow = bt + (size_t)(nb * 16 + r16) * kDkTok;
-                    acc[ti][nb] = dk_mfma(arow_hi, brow, kg, acc[ti][nb]);
-                    if constexpr (PARTS == 2)
-                        acc[ti][nb] = dk_mfma(arow_lo, brow, kg, acc[ti][nb]);
+                    for (int nb = 0; nb < CT; ++nb) {
+                        const uint4 b = dk_chunk(bt, nb * 16 + r16, kg);
+                        acc[ti][nb] = dk_mfma(ah, b, acc[ti][nb]);
+                        acc[ti][nb] = dk_mfma(al, b, acc[ti][nb]);
+                    }
+                } else {
+                    // K = 32 tokens as chunks kg and kg + 4 of the row (4 tokens each)
+                    const float4 a0 = dk_chunk(a_hi, row, kg), a1 = dk_chunk(a_hi, row, kg + 4);
+#pragma unroll
+                    for (int nb = 0; nb < CT; ++nb) {
+                        const float4 b0 = dk_chunk(bt, nb * 16 + r16, kg);
+                        const float4 b1 = dk_chunk(bt, nb * 16 + r16, kg + 4);
+                        floatx4 c = acc[ti][nb];
+                        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a0.x, b0.x, c, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a0.y, b0.y, c, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a0.z, b0.z, c, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a0.w, b0.w, c, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a1.x, b1.x, c, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a1.y, b1.y, c, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a1.z, b1.z, c, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a1.w, b1.w, c, 0, 0, 0);
+                        acc[ti][nb] = c;
+                    }
                 }
             }
         }
@@ -802,12 +914,12 @@ __global__ __launch_bounds__(kDkWaves *kWave) void dkeys_mfma_kernel(
     // partial[block][h][s][row][c0 + col]; lane holds rows 4*(l/16)+i, column l%16
     float *dst = partial + ((int64_t)blockIdx.x * H * 2 + hs) * (int64_t)n * half + c0;
 #pragma unroll
-    for (int ti = 0; ti < kDkMaxTiles; ++ti) {
+    for (int ti = 0; ti < RT; ++ti) {
         const int tile = wave + ti * kDkWaves;
         if (tile >= ntiles)
             continue;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
+        for (int nb = 0; nb < CT; ++nb) {
             const int col = nb * 16 + (lane & 15);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -939,16 +1051,28 @@ static hipError_t launch_query_t(const void *q, const void *keys, const int32_t 
     if (err != hipSuccess)
         return err;
     const int n_pad = (n + 15) & ~15;
-    const size_t lds = ((size_t)DkTile<DT>::parts * n_pad + kDkCols) * kDkTok * sizeof(typename DkTile<DT>::elt);
-    err = hipFuncSetAttribute(reinterpret_cast<const void *>(&dkeys_mfma_kernel<DT>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const int cols = dk_cols(n);
+    const size_t lds = ((size_t)DkTile<DT>::parts * n_pad + cols) * kDkTok * sizeof(typename DkTile<DT>::elt);
+    const int half = d_k / 2;
+    const int ncb = (half + cols - 1) / cols;
+    const dim3 grid((unsigned)S.blocks, (unsigned)(H * 2 * ncb));
+    const int rt = (n_pad / 16 + kDkWaves - 1) / kDkWaves;
+    auto go = [&](auto kern) -> hipError_t {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(kern, grid, dim3(kDkWaves * kWave), lds, stream,
+                           static_cast<const DT *>(q), gl_i, gl_g, partial, T, H, n, k, d_k,
+                           S.tokens_per_block);
+        return hipGetLastError();
+    };
+    // accumulators: rt row tiles x cols / 16 column tiles of 4 registers
+    err = rt <= 1 ? go(dkeys_mfma_kernel<DT, 1, 8>)
+        : rt <= 2 ? go(dkeys_mfma_kernel<DT, 2, 8>)
+                  : go(dkeys_mfma_kernel<DT, 4, 4>);
     if (err != hipSuccess)
         return err;
-    const int half = d_k / 2;
-    const int ncb = (half + kDkCols - 1) / kDkCols;
-    hipLaunchKernelGGL(dkeys_mfma_kernel<DT>, dim3((unsigned)S.blocks, (unsigned)(H * 2 * ncb)),
-                       dim3(kDkWaves * kWave), lds, stream, static_cast<const DT *>(q), gl_i, gl_g,
-                       partial, T, H, n, k, d_k, S.tokens_per_block);
     const int64_t count = (int64_t)H * 2 * n * half;
     const int64_t rblocks = grid1d(count, 256);
     hipLaunchKernelGGL(dkeys_reduce_kernel, dim3((unsigned)(rblocks < 8192 ? rblocks : 8192)),

@@ -53,6 +53,10 @@ inline SlotSortScratch slot_sort_scratch(int64_t picks, int n)
     return S;
 }
 
+// Sub-key gradient: codebook columns per workgroup (its MFMA accumulators
+// are n/16 row tiles x cols/16 column tiles over 16 waves of <= 128 registers).
+inline int dk_cols(int n) { return n > 512 ? 64 : 128; }
+
 struct BwdQueryScratch {
     size_t off_gl_i, off_gl_g, off_partial, total;
     int blocks;             // token blocks (one partial sum each)
@@ -64,7 +68,8 @@ inline BwdQueryScratch bwd_query_scratch(int64_t T, int H, int n, int k, int d_k
     BwdQueryScratch S;
     const int half = d_k / 2;
     // about one workgroup (16 waves, n x 32 LDS tile) per compute unit
-    const int64_t groups = (int64_t)H * 2 * ((half + 63) / 64);
+    const int cols = dk_cols(n);
+    const int64_t groups = (int64_t)H * 2 * ((half + cols - 1) / cols);
     int64_t blocks = (256 + groups - 1) / groups;
     const int64_t max_blocks = T > 128 ? (T + 127) / 128 : 1;
     if (blocks > max_blocks)

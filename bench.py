@@ -157,6 +157,8 @@ def main():
     p = problem(T, H, n, k, d_k, d_v, tdt)
     ws_bytes = _lib.workspace_bytes(p, True)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    fws_bytes = _lib.workspace_bytes(p, False)
+    fws = torch.empty(max(fws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     P = lambda t: t.data_ptr()  # noqa: E731
@@ -166,7 +168,8 @@ def main():
             if ev is not None:
                 ev[i].record(stream)
         mark(0)
-        rc = _lib.forward_select(p, P(q), P(keys), P(idx), P(wts), P(scores), sp)
+        rc = _lib.forward_select(p, P(q), P(keys), P(idx), P(wts), P(scores), P(fws), fws_bytes,
+                                 sp)
         mark(1)
         rc |= _lib.forward_gather(p, P(values), P(idx), P(wts), P(y), sp)
         mark(2)

@@ -69,9 +69,12 @@ typedef struct {
     int32_t dtype;  /* pkm_dtype_t                                            */
 } pkm_problem_t;
 
-/* Bytes of device workspace pkm_forward (backward = 0) or pkm_backward
- * (backward = 1) needs for this problem; 0 if none.  Returns (size_t)-1 for
- * an invalid descriptor. */
+/* Bytes of device workspace pkm_forward and pkm_forward_select (backward = 0)
+ * or pkm_backward and its stages (backward = 1) need for this problem; 0 if
+ * none (the workspace may then be NULL).  Returns (size_t)-1 for an invalid
+ * descriptor.  The forward needs workspace only on its two-kernel selection
+ * path (bf16, d_k = 512, 256 < n <= 512, k <= 32): T*H*2*k*8 bytes rounded up
+ * to 256, for the per-half top-k lists. */
 size_t pkm_workspace_bytes(const pkm_problem_t *p, int backward);
 
 /*
@@ -145,9 +148,11 @@ pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *key
  */
 
 /* Steps 1-5 of pkm_forward: the selection and its softmax weights
- * (companion page, "Why top-k of each half is enough"). */
+ * (companion page, "Why top-k of each half is enough").  The workspace
+ * (pkm_workspace_bytes(p, 0) bytes) is the same as pkm_forward's. */
 pkm_status_t pkm_forward_select(const pkm_problem_t *p, const void *q, const void *keys,
-                                int32_t *idx, float *weights, float *scores, void *stream);
+                                int32_t *idx, float *weights, float *scores, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /* y[t] = sum over heads h and picks r of weights[t][h][r] * values[idx[t][h][r]]
  * (gptget.net summary, "Methodology": weighted sum of the selected values). */

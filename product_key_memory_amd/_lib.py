@@ -64,7 +64,7 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_int, P, c_size, P]
         L.pkm_backward.restype = ctypes.c_int
         PP = ctypes.POINTER(Problem)
-        L.pkm_forward_select.argtypes = [PP, P, P, P, P, P, P]
+        L.pkm_forward_select.argtypes = [PP, P, P, P, P, P, P, c_size, P]
         L.pkm_forward_gather.argtypes = [PP, P, P, P, P, P]
         L.pkm_slot_sort.argtypes = [PP, P, P, P, P, c_size, P]
         L.pkm_backward_values.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_int, P, P]
@@ -97,8 +97,9 @@ def backward(p: Problem, q, keys, values, idx, weights, dy, dq, dkeys, dvalues, 
                               dvalues, int(accumulate), ws, ws_bytes, stream)
 
 
-def forward_select(p: Problem, q, keys, idx, weights, scores, stream) -> int:
-    return lib().pkm_forward_select(ctypes.byref(p), q, keys, idx, weights, scores, stream)
+def forward_select(p: Problem, q, keys, idx, weights, scores, ws, ws_bytes, stream) -> int:
+    return lib().pkm_forward_select(ctypes.byref(p), q, keys, idx, weights, scores, ws, ws_bytes,
+                                    stream)
 
 
 def forward_gather(p: Problem, values, idx, weights, y, stream) -> int:

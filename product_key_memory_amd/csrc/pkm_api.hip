@@ -55,9 +55,14 @@ size_t backward_bytes(const pkm_problem_t *p)
     return picks_bytes(p) + starts_bytes(p) + picks_bytes(p) + stage_scratch_bytes(p);
 }
 
+size_t forward_bytes(const pkm_problem_t *p)
+{
+    return pkm::select_workspace_bytes(p->T, p->H, p->n, p->k, p->dtype, p->d_k);
+}
+
 pkm_status_t check_workspace(const pkm_problem_t *p, const void *ws, size_t have, size_t need)
 {
-    if (p->T == 0)
+    if (p->T == 0 || need == 0)
         return PKM_OK;
     if (!ws)
         return PKM_ERR_NULL;
@@ -74,11 +79,12 @@ size_t pkm_workspace_bytes(const pkm_problem_t *p, int backward)
 {
     if (check_problem(p, backward != 0) != PKM_OK)
         return (size_t)-1;
-    return backward ? backward_bytes(p) : 0;
+    return backward ? backward_bytes(p) : forward_bytes(p);
 }
 
 pkm_status_t pkm_forward_select(const pkm_problem_t *p, const void *q, const void *keys,
-                                int32_t *idx, float *weights, float *scores, void *stream)
+                                int32_t *idx, float *weights, float *scores, void *workspace,
+                                size_t workspace_bytes, void *stream)
 {
     pkm_status_t st = check_problem(p, false);
     if (st != PKM_OK)
@@ -89,10 +95,13 @@ pkm_status_t pkm_forward_select(const pkm_problem_t *p, const void *q, const voi
     if (!aligned16(q) || !aligned16(keys) || !aligned16(idx) || !aligned16(weights) ||
         (scores && !aligned16(scores)))
         return PKM_ERR_ALIGN;
+    st = check_workspace(p, workspace, workspace_bytes, forward_bytes(p));
+    if (st != PKM_OK)
+        return st;
     if (T == 0)
         return PKM_OK;
     return pkm::launch_fwd_select(p->dtype, q, keys, p->T, p->H, p->n, p->k, p->d_k, idx, weights,
-                                  scores, static_cast<hipStream_t>(stream)) == hipSuccess
+                                  scores, workspace, static_cast<hipStream_t>(stream)) == hipSuccess
                ? PKM_OK
                : PKM_ERR_HIP;
 }
@@ -120,8 +129,6 @@ pkm_status_t pkm_forward(const pkm_problem_t *p, const void *q, const void *keys
                          const void *values, void *y, int32_t *idx, float *weights,
                          float *scores, void *workspace, size_t workspace_bytes, void *stream)
 {
-    (void)workspace;
-    (void)workspace_bytes;      // the forward pass needs no workspace
     pkm_status_t st = check_problem(p, false);
     if (st != PKM_OK)
         return st;
@@ -132,7 +139,7 @@ pkm_status_t pkm_forward(const pkm_problem_t *p, const void *q, const void *keys
     if (!aligned16(q) || !aligned16(keys) || !aligned16(values) || !aligned16(y) ||
         !aligned16(idx) || !aligned16(weights) || (scores && !aligned16(scores)))
         return PKM_ERR_ALIGN;
-    st = pkm_forward_select(p, q, keys, idx, weights, scores, stream);
+    st = pkm_forward_select(p, q, keys, idx, weights, scores, workspace, workspace_bytes, stream);
     if (st != PKM_OK)
         return st;
     return pkm_forward_gather(p, values, idx, weights, y, stream);

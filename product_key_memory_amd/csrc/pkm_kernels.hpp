@@ -11,11 +11,38 @@ namespace pkm {
 
 constexpr int kSegChunk = 256;      // sorted picks per wave in the value segmented reduction
 
-// Fused forward selection: sub-key scoring (MFMA), exact per-half top-k,
-// pruned k x k combine, softmax.  Writes idx / weights / scores [T][H][k].
+// Rank pairs (a, b) with (a + 1)(b + 1) <= k: the combine candidates.
+inline int merge_candidates(int k)
+{
+    int c = 0;
+    for (int a = 1; a <= k; ++a)
+        c += k / a;
+    return c;
+}
+
+// The two-kernel selection path: bf16 storage, query halves of exactly 256,
+// 256 < n <= 512, k <= 32.  Its per-half top-k lists pass through the
+// workspace: [T][H][2][k] entries of (score bits, sub-key), 8 bytes each.
+inline bool select_fast_ok(int dtype, int n, int k, int d_k)
+{
+    return dtype == 1 && n > 256 && n <= 512 && k <= 32 && d_k == 512;
+}
+inline size_t select_workspace_bytes(int64_t T, int H, int n, int k, int dtype, int d_k)
+{
+    if (!select_fast_ok(dtype, n, k, d_k))
+        return 0;
+    return (((size_t)T * H * 2 * k * 8) + 255) & ~(size_t)255;
+}
+
+// Forward selection: sub-key scoring (MFMA), exact per-half top-k, pruned
+// k x k combine, softmax.  Writes idx / weights / scores [T][H][k].
+// `workspace` holds select_workspace_bytes(...) bytes.
 hipError_t launch_fwd_select(int dtype, const void *q, const void *keys, int64_t T, int H,
                              int n, int k, int d_k, int32_t *idx, float *weights,
-                             float *scores, hipStream_t stream);
+                             float *scores, void *workspace, hipStream_t stream);
+hipError_t launch_select_fast(const void *q, const void *keys, int64_t T, int H, int n, int k,
+                              int d_k, int32_t *idx, float *weights, float *scores,
+                              void *workspace, hipStream_t stream);
 
 // y[t] = sum over the H*k picks of token t of weight * values[slot].
 hipError_t launch_fwd_gather(int dtype, const void *values, const int32_t *idx,

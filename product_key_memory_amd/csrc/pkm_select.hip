@@ -40,14 +40,6 @@ struct SelLayout {
 
 static inline unsigned align16(unsigned x) { return (x + 15u) & ~15u; }
 
-static int merge_candidates(int k)
-{
-    int c = 0;
-    for (int a = 1; a <= k; ++a)
-        c += k / a;
-    return c;
-}
-
 static SelLayout sel_layout(int n, int k, int half, int elt_bytes)
 {
     SelLayout L;
@@ -307,347 +299,6 @@ __global__ __launch_bounds__(kSelThreads) void fwd_select_kernel(
     }
 }
 
-// ===========================================================================
-// Register-resident variant for bf16 storage, 256 < n <= 512, k <= 32, d_k = 512.
-//
-// Each wave owns 16 tokens (the MFMA N dimension) and computes their n
-// scores per half straight into registers: lane l holds, for token l % 16,
-// the scores of sub-keys 16 j + 4 (l / 16) + i (tile j < 32, i < 4).  All
-// selection work then runs on the 4 lanes that share a token, so every
-// instruction serves the wave's 16 tokens at once:
-//   - tau = k-th largest of the token's 64 group maxima (groups of 8 scores),
-//     by a bitonic sort inside the 4-lane group;
-//   - survivors (score >= tau, at least k of them) are compacted into LDS and
-//     sorted as 64-bit keys inside the 4-lane group; when a token has more
-//     than 64 survivors (heavy ties) its exact k-th largest key is found by
-//     bisection on the score bits, then on the index among exact ties, and
-//     exactly k survive;
-//   - the k x k combine sorts the token's <= 128 pruned candidates inside the
-//     4-lane group, and the lane holding the winners computes the softmax.
-// ===========================================================================
-constexpr int kFastWaves = 4;
-constexpr int kFastTok = 16;                         // tokens per wave
-constexpr int kFastTokWG = kFastWaves * kFastTok;    // tokens per workgroup
-constexpr int kFastTiles = 32;                       // 16-sub-key tiles: n <= 512
-constexpr int kFastKSteps = 8;                       // 32-wide K steps: half <= 256
-constexpr int kFastSurv = 64;                        // survivor slots per token
-
-struct FastLayout {
-    int n_pairs;
-    unsigned off_li, off_surv, off_pairs, total;     // ls at offset 0
-};
-
-static FastLayout fast_layout(int n, int k)
-{
-    FastLayout L;
-    L.n_pairs = merge_candidates(k);
-    const unsigned lists = (unsigned)(kFastTokWG * 2 * k * 4);
-    L.off_li = align16(lists);
-    L.off_surv = align16(L.off_li + lists);
-    const unsigned per_wave = (unsigned)(kFastTok * kFastSurv * 8);    // 16 tokens x 64 keys
-    L.off_pairs = align16(L.off_surv + kFastWaves * per_wave);
-    L.total = align16(L.off_pairs + (unsigned)(L.n_pairs * 2));
-    return L;
-}
-
-// bf16 storage, query halves of exactly 256, 256 < n <= 512, k <= 32 (the
-// other shapes take the general kernel)
-static bool fast_path_ok(int dtype, int n, int k, int d_k)
-{
-    return dtype == 1 && n > kFastTiles * 8 && n <= kFastTiles * 16 && k <= 32 &&
-           d_k / 2 == kFastKSteps * 32;
-}
-
-// Scores of the wave's 16 tokens against sub-keys 0..n-1 of one codebook, as
-// order-preserving integers: so[j][i] = ord(score of sub-key 16 j + 4 g + i)
-// for token `tok` (ord(-inf) past n).
-__device__ __forceinline__ void fast_scores(uint32_t (&so)[kFastTiles][4], const uint16_t *kb,
-                                            const uint4 (&qf)[kFastKSteps], int n, int tok, int g)
-{
-    constexpr int half = kFastKSteps * 32;
-    constexpr int kDepth = 4;                     // A fragments in flight
-    constexpr int kSteps = kFastTiles * kFastKSteps;
-    // one buffer descriptor over the codebook: rows past n read as zeros, and
-    // every fragment is the lane offset plus a constant
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(kb), (short)0, n * half * 2, 0x00020000);
-    const int lane_off = tok * half * 2 + 16 * g;
-    auto load_step = [&](int step) {
-        const int soff = (step / kFastKSteps) * 16 * half * 2 + (step % kFastKSteps) * 64;
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off, soff, 0);
-        return make_uint4(v[0], v[1], v[2], v[3]);
-    };
-    uint4 ring[kDepth];
-#pragma unroll
-    for (int p = 0; p < kDepth; ++p)
-        ring[p] = load_step(p);
-#pragma unroll
-    for (int j = 0; j < kFastTiles; ++j) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < kFastKSteps; ++kk) {
-            const int step = j * kFastKSteps + kk;
-            const uint4 cur = ring[step % kDepth];
-            if (step + kDepth < kSteps)
-                ring[step % kDepth] = load_step(step + kDepth);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur),
-                                                         __builtin_bit_cast(bf16x8, qf[kk]), acc,
-                                                         0, 0, 0);
-        }
-        // n > 256 on this path: only the upper 16 tiles can hold sub-keys >= n
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            so[j][i] = ord_f32((j < kFastTiles / 2 || 16 * j + 4 * g + i < n) ? acc[i] : -INFINITY);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-__device__ __forceinline__ float pick_reg16(const float (&v)[16], int r)
-{
-    float o = v[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i)
-        if (i == r)
-            o = v[i];
-    return o;
-}
-
-__global__ __launch_bounds__(kFastWaves *kWave) void fwd_select_fast_kernel(
-    const bf16_t *__restrict__ q, const bf16_t *__restrict__ keys, int64_t T, int H, int n,
-    int k, int d_k, FastLayout L, int32_t *__restrict__ idx, float *__restrict__ weights,
-    float *__restrict__ scores)
-{
-    extern __shared__ __align__(16) unsigned char smem[];
-    float *ls = reinterpret_cast<float *>(smem);                    // [64 tokens][2][k]
-    int *li = reinterpret_cast<int *>(smem + L.off_li);             // [64 tokens][2][k]
-    uint16_t *pairs = reinterpret_cast<uint16_t *>(smem + L.off_pairs);
-
-    const int lane = lane_id();
-    const int wave = threadIdx.x / kWave;
-    const int tok = lane & 15, g_lane = lane >> 4;
-    const int half = d_k / 2;
-    const int h = blockIdx.y;
-    const int wt = wave * kFastTok + tok;                           // token within the workgroup
-    const int64_t t = (int64_t)blockIdx.x * kFastTokWG + wt;
-    const bool live = t < T;
-    const unsigned per_wave = (L.off_pairs - L.off_surv) / kFastWaves;
-    unsigned char *wave_lds = smem + L.off_surv + wave * per_wave;
-    uint64_t *surv = reinterpret_cast<uint64_t *>(wave_lds) + tok * kFastSurv;
-
-    if (wave == 0) {
-        const int cnt = lane < k ? k / (lane + 1) : 0;
-        int total;
-        const int start = wave_exclusive_scan(cnt, &total);
-        for (int b = 0; b < cnt; ++b)
-            pairs[start + b] = (uint16_t)(lane | (b << 8));
-    }
-
-    for (int s = 0; s < 2; ++s) {
-        // an opaque copy of the lane group per half, so values derived from it
-        // (the 128 sub-key indices) are formed where used instead of being
-        // hoisted out of this loop and held in registers
-        int g = g_lane;
-        asm volatile("" : "+v"(g));
-        // B fragments: token `tok`, K slice 32 kk + 8 g .. + 7
-        uint4 qf[kFastKSteps];
-        const uint16_t *qrow = reinterpret_cast<const uint16_t *>(q) + ((live ? t : 0) * H + h) * (int64_t)d_k + (int64_t)s * half;
-#pragma unroll
-        for (int kk = 0; kk < kFastKSteps; ++kk)
-            qf[kk] = *reinterpret_cast<const uint4 *>(qrow + 32 * kk + 8 * g);
-        const uint16_t *kb = reinterpret_cast<const uint16_t *>(keys) + ((int64_t)h * 2 + s) * (int64_t)n * half;
-        uint32_t so[kFastTiles][4];
-        fast_scores(so, kb, qf, n, tok, g);
-
-        // tau: k-th largest of the token's 64 group maxima (groups of 8 scores)
-        uint32_t gm[16];
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            uint32_t v = so[2 * m][0];
-#pragma unroll
-            for (int i = 1; i < 4; ++i)
-                v = max(v, so[2 * m][i]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                v = max(v, so[2 * m + 1][i]);
-            gm[m] = v;
-        }
-        group4_sort_desc<16>(gm);
-        uint32_t tau_src = gm[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r)
-            if (r == ((k - 1) & 15))
-                tau_src = gm[r];
-        const uint32_t tau = (uint32_t)__shfl((int)tau_src, tok + 16 * ((k - 1) >> 4));
-
-        // survivors: ord >= tau (tau is a real score: n > 256 gives >= 33 groups
-        // of valid scores, so the sub-keys past n never survive)
-        int cnt = 0;
-#pragma unroll
-        for (int j = 0; j < kFastTiles; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                cnt += so[j][i] >= tau ? 1 : 0;
-        int total = group4_sum(cnt);
-        bool fits = total <= kFastSurv;
-
-        // heavy ties: the exact k-th largest key instead of tau, by bisection on
-        // the score bits and then on the index among exactly tied scores
-        uint32_t kth = tau, tie_idx = 0xFFFFFFFFu;
-        if (__ballot(!fits && live) != 0) {
-            uint32_t K = 0;
-            for (int bit = 31; bit >= 0; --bit) {
-                const uint32_t cand = K | (1u << bit);
-                int c = 0;
-#pragma unroll
-                for (int j = 0; j < kFastTiles; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        c += so[j][i] >= cand ? 1 : 0;
-                if (group4_sum(c) >= k)
-                    K = cand;
-            }
-            int above = 0;
-#pragma unroll
-            for (int j = 0; j < kFastTiles; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    above += so[j][i] > K ? 1 : 0;
-            const int need = k - group4_sum(above);     // tied picks to take, lowest index first
-            uint32_t I = 0;                              // largest bound with < need tied indices below it
-            for (int bit = 9; bit >= 0; --bit) {
-                const uint32_t cand = I | (1u << bit);
-                int gb = g;                   // opaque: keep the indices out of registers
-                asm volatile("" : "+v"(gb));
-                int c = 0;
-#pragma unroll
-                for (int j = 0; j < kFastTiles; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        c += (so[j][i] == K && (uint32_t)(16 * j + 4 * gb + i) < cand) ? 1 : 0;
-                if (group4_sum(c) < need)
-                    I = cand;
-            }
-            if (!fits) {
-                kth = K;
-                tie_idx = I;             // exactly k keys are >= (K, I)
-                total = k;
-                fits = true;
-            }
-        }
-
-        // compact the survivors (keys) per token, then sort them in the 4-lane group
-        int off;
-        {
-            const int c0 = __shfl(cnt, tok), c1 = __shfl(cnt, tok + 16), c2 = __shfl(cnt, tok + 32);
-            off = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
-        }
-        if (tie_idx != 0xFFFFFFFFu) {
-            // recount this lane's share under the exact bound
-            int c = 0;
-#pragma unroll
-            for (int j = 0; j < kFastTiles; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t o = so[j][i];
-                    c += (o > kth || (o == kth && (uint32_t)(16 * j + 4 * g + i) <= tie_idx)) ? 1 : 0;
-                }
-            const int c0 = __shfl(c, tok), c1 = __shfl(c, tok + 16), c2 = __shfl(c, tok + 32);
-            off = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
-        }
-#pragma unroll
-        for (int j = 0; j < kFastTiles; ++j) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t o = so[j][i];
-                const uint32_t sub = (uint32_t)(16 * j + 4 * g + i);
-                const bool keep = tie_idx == 0xFFFFFFFFu ? o >= kth : (o > kth || (o == kth && sub <= tie_idx));
-                if (keep)
-                    surv[off++] = ((uint64_t)o << 32) | (uint64_t)(~sub);
-            }
-            __builtin_amdgcn_sched_barrier(0);     // one tile's keys at a time
-        }
-        wave_lds_sync();
-        {
-            uint64_t v[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int e = 16 * g + r;
-                v[r] = e < total ? surv[e] : 0ull;
-            }
-            group4_sort_desc<16>(v);
-            float *os = ls + (wt * 2 + s) * k;
-            int *oi = li + (wt * 2 + s) * k;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int e = 16 * g + r;
-                if (live && e < k) {
-                    os[e] = key_score(v[r]);
-                    oi[e] = (int)key_index(v[r]);
-                }
-            }
-        }
-        wave_lds_sync();
-    }
-    __syncthreads();
-
-    // combine the halves: candidates (a, b) with (a + 1)(b + 1) <= k, inside the 4-lane group
-    {
-        const int g = g_lane;
-        uint64_t v[32];
-        const float *l_s = ls + (wt * 2 + 0) * k;
-        const int *l_i = li + (wt * 2 + 0) * k;
-        const float *r_s = ls + (wt * 2 + 1) * k;
-        const int *r_i = li + (wt * 2 + 1) * k;
-#pragma unroll
-        for (int r = 0; r < 32; ++r) {
-            const int c = 32 * g + r;
-            if (live && c < L.n_pairs) {
-                const int a = pairs[c] & 0xFF, b = pairs[c] >> 8;
-                v[r] = make_key(l_s[a] + r_s[b], (uint32_t)l_i[a] * (uint32_t)n + (uint32_t)r_i[b]);
-            } else {
-                v[r] = 0ull;
-            }
-        }
-        group4_sort_desc<32>(v);
-        // the k <= 32 winners are registers 0..k-1 of the group's first lane
-        if (live && g == 0) {
-            const float top = key_score(v[0]);
-            float e[32], z = 0.f;
-#pragma unroll
-            for (int r = 0; r < 32; ++r) {
-                e[r] = r < k ? expf(key_score(v[r]) - top) : 0.f;
-                z += e[r];
-            }
-            const int64_t out = (t * H + h) * (int64_t)k;
-#pragma unroll
-            for (int r = 0; r < 32; ++r) {
-                if (r < k) {
-                    idx[out + r] = (int32_t)key_index(v[r]);
-                    weights[out + r] = e[r] / z;
-                    if (scores)
-                        scores[out + r] = key_score(v[r]);
-                }
-            }
-        }
-    }
-}
-
-static hipError_t launch_select_fast(const void *q, const void *keys, int64_t T, int H, int n,
-                                     int k, int d_k, int32_t *idx, float *weights, float *scores,
-                                     hipStream_t stream)
-{
-    const FastLayout L = fast_layout(n, k);
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_select_fast_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
-    if (err != hipSuccess)
-        return err;
-    const dim3 grid((unsigned)((T + kFastTokWG - 1) / kFastTokWG), (unsigned)H);
-    hipLaunchKernelGGL(fwd_select_fast_kernel, grid, dim3(kFastWaves * kWave), L.total, stream,
-                       static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(keys), T, H, n,
-                       k, d_k, L, idx, weights, scores);
-    return hipGetLastError();
-}
-
 template <typename DT>
 static hipError_t launch_select_t(const void *q, const void *keys, int64_t T, int H, int n,
                                   int k, int d_k, int32_t *idx, float *weights, float *scores,
@@ -667,10 +318,11 @@ static hipError_t launch_select_t(const void *q, const void *keys, int64_t T, in
 
 hipError_t launch_fwd_select(int dtype, const void *q, const void *keys, int64_t T, int H,
                              int n, int k, int d_k, int32_t *idx, float *weights,
-                             float *scores, hipStream_t stream)
+                             float *scores, void *workspace, hipStream_t stream)
 {
-    if (fast_path_ok(dtype, n, k, d_k))
-        return launch_select_fast(q, keys, T, H, n, k, d_k, idx, weights, scores, stream);
+    if (select_fast_ok(dtype, n, k, d_k))
+        return launch_select_fast(q, keys, T, H, n, k, d_k, idx, weights, scores, workspace,
+                                  stream);
     if (dtype == 1)
         return launch_select_t<bf16_t>(q, keys, T, H, n, k, d_k, idx, weights, scores, stream);
     return launch_select_t<float>(q, keys, T, H, n, k, d_k, idx, weights, scores, stream);

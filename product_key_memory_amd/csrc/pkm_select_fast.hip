@@ -1,0 +1,350 @@
+// pkm_select_fast.hip -- forward selection for bf16 storage, query halves of
+// 256, 256 < n <= 512, k <= 32, as two kernels (gptget.net summary of "Large
+// Memory Layers with Product Keys", "Methodology": split q into q1, q2, search
+// each against its own sub-key set, combine the best sub-keys; companion page
+// "Why top-k of each half is enough").
+//
+// 1. fwd_topk_half_kernel: one wave per (16 tokens, head, half).  The wave
+//    computes its tokens' n scores straight into registers with
+//    v_mfma_f32_16x16x32_bf16 (sub-keys as M, tokens as N): lane l holds, for
+//    token l % 16, the scores of sub-keys 16 j + 4 (l / 16) + i (tile j < 32,
+//    i < 4).  All selection work then runs on the 4 lanes that share a token,
+//    so every instruction serves the wave's 16 tokens at once:
+//      - tau = k-th largest of the token's 64 group maxima (groups of 8
+//        scores), by a bitonic sort inside the 4-lane group: the k groups
+//        above it each hold a score >= tau, so at least k scores survive;
+//      - survivors (score >= tau) are compacted into LDS and sorted as 64-bit
+//        keys (score, then lower index first) inside the 4-lane group; when a
+//        token has more than 64 survivors (heavy ties) its exact k-th largest
+//        key is found by bisection on the score bits, then on the index among
+//        exact ties, and exactly k survive;
+//      - the top k (score, sub-key) of the half go to the workspace.
+// 2. fwd_merge_kernel: one wave per 16 (token, head) rows, 4 lanes per row.
+//    A pair of ranks (a, b) can only make the final top-k if
+//    (a + 1)(b + 1) <= k: every pair (a', b') <= (a, b) componentwise scores at
+//    least as high and, on a tie, has the lower slot f = i n + j.  The
+//    sum_a floor(k / a) candidates (119 for k = 32) are sorted inside the
+//    4-lane group by (score desc, slot asc), the first k kept, and a softmax
+//    over them gives the weights.
+// Splitting the two phases keeps each kernel's registers low enough for two
+// or more waves per SIMD, which hides the latency a single wave exposes.
+#include "pkm_device.hpp"
+#include "pkm_kernels.hpp"
+
+namespace pkm {
+
+constexpr int kFastWaves = 4;
+constexpr int kFastTok = 16;                         // tokens per wave
+constexpr int kFastTokWG = kFastWaves * kFastTok;    // tokens per workgroup
+constexpr int kFastTiles = 32;                       // 16-sub-key tiles: n <= 512
+constexpr int kFastKSteps = 8;                       // 32-wide K steps: half = 256
+constexpr int kFastSurv = 64;                        // survivor slots per token
+constexpr int kMergeWaves = 4;
+constexpr int kMergeRows = 16;                       // (token, head) rows per wave
+constexpr int kMaxPairs = 128;                       // merge_candidates(32) = 119
+
+// Scores of the wave's 16 tokens against sub-keys 0..n-1 of one codebook, as
+// order-preserving integers: so[j][i] = ord(score of sub-key 16 j + 4 g + i)
+// for token `tok` (ord(-inf) past n).  Tiles are computed in pairs whose two
+// accumulation chains alternate, so consecutive MFMAs do not wait on each
+// other.
+__device__ __forceinline__ void fast_scores(uint32_t (&so)[kFastTiles][4], const uint16_t *kb,
+                                            const uint4 (&qf)[kFastKSteps], int n, int tok, int g)
+{
+    constexpr int half = kFastKSteps * 32;
+    constexpr int kDepth = 8;                     // A fragments in flight
+    constexpr int kSteps = kFastTiles * kFastKSteps;
+    // one buffer descriptor over the codebook: rows past n read as zeros, and
+    // every fragment is the lane offset plus a constant
+    const __amdgpu_buffer_rsrc_t rsrc = buffer_over(kb, n * half * 2);
+    const int lane_off = tok * half * 2 + 16 * g;
+    // step -> (tile, K step): tiles 2p and 2p + 1 alternate within pair p
+    auto load_step = [&](int step) {
+        const int p = step / (2 * kFastKSteps), rem = step % (2 * kFastKSteps);
+        const int tile = 2 * p + (rem & 1), kk = rem >> 1;
+        return buffer_load16(rsrc, lane_off, tile * 16 * half * 2 + kk * 64);
+    };
+    uint4 ring[kDepth];
+#pragma unroll
+    for (int p = 0; p < kDepth; ++p)
+        ring[p] = load_step(p);
+#pragma unroll
+    for (int pr = 0; pr < kFastTiles / 2; ++pr) {
+        floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int kk = 0; kk < kFastKSteps; ++kk) {
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+                const int step = pr * 2 * kFastKSteps + 2 * kk + w;
+                const uint4 cur = ring[step % kDepth];
+                if (step + kDepth < kSteps)
+                    ring[step % kDepth] = load_step(step + kDepth);
+                acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, cur), __builtin_bit_cast(bf16x8, qf[kk]), acc[w],
+                    0, 0, 0);
+            }
+        }
+        // n > 256 on this path: only the upper 16 tiles can hold sub-keys >= n
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const int j = 2 * pr + w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                so[j][i] = ord_f32((j < kFastTiles / 2 || 16 * j + 4 * g + i < n) ? acc[w][i]
+                                                                                  : -INFINITY);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// lists[((t H + h) 2 + s) k + e] = (ord score, sub-key) of the e-th best
+// sub-key of half s, e < k.
+__global__ __launch_bounds__(kFastWaves *kWave) void fwd_topk_half_kernel(
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ keys, int64_t T, int H, int n,
+    int k, uint2 *__restrict__ lists)
+{
+    __shared__ uint64_t surv_all[kFastWaves][kFastTok * kFastSurv];
+
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int tok = lane & 15, g_lane = lane >> 4;
+    constexpr int half = kFastKSteps * 32;
+    constexpr int d_k = 2 * half;
+    const int h = blockIdx.y, s = blockIdx.z;
+    const int64_t t = (int64_t)blockIdx.x * kFastTokWG + wave * kFastTok + tok;
+    const bool live = t < T;
+    uint64_t *surv = surv_all[wave] + tok * kFastSurv;
+
+    // an opaque copy of the lane group, so values derived from it (the 128
+    // sub-key indices) are formed where used instead of being held in registers
+    int g = g_lane;
+    asm volatile("" : "+v"(g));
+    // B fragments: token `tok`, K slice 32 kk + 8 g .. + 7
+    uint4 qf[kFastKSteps];
+    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(q) +
+                           ((live ? t : 0) * H + h) * (int64_t)d_k + (int64_t)s * half;
+#pragma unroll
+    for (int kk = 0; kk < kFastKSteps; ++kk)
+        qf[kk] = *reinterpret_cast<const uint4 *>(qrow + 32 * kk + 8 * g);
+    const uint16_t *kb = reinterpret_cast<const uint16_t *>(keys) + ((int64_t)h * 2 + s) * (int64_t)n * half;
+    uint32_t so[kFastTiles][4];
+    fast_scores(so, kb, qf, n, tok, g);
+
+    // tau: k-th largest of the token's 64 group maxima (groups of 8 scores)
+    uint32_t gm[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        uint32_t v = so[2 * m][0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i)
+            v = max(v, so[2 * m][i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v = max(v, so[2 * m + 1][i]);
+        gm[m] = v;
+    }
+    group4_sort_desc<16>(gm);
+    uint32_t tau_src = gm[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r)
+        if (r == ((k - 1) & 15))
+            tau_src = gm[r];
+    const uint32_t tau = (uint32_t)__shfl((int)tau_src, tok + 16 * ((k - 1) >> 4));
+
+    // survivors: ord >= tau (tau is a real score: n > 256 gives >= 33 groups
+    // of valid scores, so the sub-keys past n never survive)
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kFastTiles; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            cnt += so[j][i] >= tau ? 1 : 0;
+    int total = group4_sum(cnt);
+    bool fits = total <= kFastSurv;
+
+    // heavy ties: the exact k-th largest key instead of tau, by bisection on
+    // the score bits and then on the index among exactly tied scores
+    uint32_t kth = tau, tie_idx = 0xFFFFFFFFu;
+    if (__ballot(!fits && live) != 0) {
+        uint32_t K = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = K | (1u << bit);
+            int c = 0;
+#pragma unroll
+            for (int j = 0; j < kFastTiles; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    c += so[j][i] >= cand ? 1 : 0;
+            if (group4_sum(c) >= k)
+                K = cand;
+        }
+        int above = 0;
+#pragma unroll
+        for (int j = 0; j < kFastTiles; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                above += so[j][i] > K ? 1 : 0;
+        const int need = k - group4_sum(above);     // tied picks to take, lowest index first
+        uint32_t I = 0;                              // largest bound with < need tied indices below it
+        for (int bit = 9; bit >= 0; --bit) {
+            const uint32_t cand = I | (1u << bit);
+            int gb = g;                   // opaque: keep the indices out of registers
+            asm volatile("" : "+v"(gb));
+            int c = 0;
+#pragma unroll
+            for (int j = 0; j < kFastTiles; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    c += (so[j][i] == K && (uint32_t)(16 * j + 4 * gb + i) < cand) ? 1 : 0;
+            if (group4_sum(c) < need)
+                I = cand;
+        }
+        if (!fits) {
+            kth = K;
+            tie_idx = I;             // exactly k keys are >= (K, I)
+            total = k;
+            fits = true;
+        }
+    }
+
+    // compact the survivors (keys) per token, then sort them in the 4-lane group
+    int off;
+    {
+        const int c0 = __shfl(cnt, tok), c1 = __shfl(cnt, tok + 16), c2 = __shfl(cnt, tok + 32);
+        off = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
+    }
+    if (tie_idx != 0xFFFFFFFFu) {
+        // recount this lane's share under the exact bound
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < kFastTiles; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t o = so[j][i];
+                c += (o > kth || (o == kth && (uint32_t)(16 * j + 4 * g + i) <= tie_idx)) ? 1 : 0;
+            }
+        const int c0 = __shfl(c, tok), c1 = __shfl(c, tok + 16), c2 = __shfl(c, tok + 32);
+        off = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kFastTiles; ++j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t o = so[j][i];
+            const uint32_t sub = (uint32_t)(16 * j + 4 * g + i);
+            const bool keep = tie_idx == 0xFFFFFFFFu ? o >= kth : (o > kth || (o == kth && sub <= tie_idx));
+            if (keep)
+                surv[off++] = ((uint64_t)o << 32) | (uint64_t)(~sub);
+        }
+        __builtin_amdgcn_sched_barrier(0);     // one tile's keys at a time
+    }
+    wave_lds_sync();
+    uint64_t v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int e = 16 * g + r;
+        v[r] = e < total ? surv[e] : 0ull;
+    }
+    group4_sort_desc<16>(v);
+    // lane group g holds ranks 16 g .. 16 g + 15
+    if (live) {
+        uint2 *out = lists + ((t * H + h) * 2 + s) * (int64_t)k;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int e = 16 * g + r;
+            if (e < k)
+                out[e] = make_uint2((uint32_t)(v[r] >> 32), ~(uint32_t)v[r]);
+        }
+    }
+}
+
+// The combine and the softmax per (token, head) row from the two lists.
+__global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
+    const uint2 *__restrict__ lists, int64_t rows, int n, int k, int n_pairs,
+    int32_t *__restrict__ idx, float *__restrict__ weights, float *__restrict__ scores)
+{
+    __shared__ uint2 s_list[kMergeWaves][kMergeRows * 2 * 32];
+    __shared__ uint16_t s_pairs[kMaxPairs];
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int tok = lane & 15, g = lane >> 4;
+    if (wave == 0) {
+        const int cnt = lane < k ? k / (lane + 1) : 0;
+        int total;
+        const int start = wave_exclusive_scan(cnt, &total);
+        for (int b = 0; b < cnt; ++b)
+            s_pairs[start + b] = (uint16_t)(lane | (b << 8));
+    }
+    // the wave's rows are contiguous in the lists: stage them in LDS
+    const int64_t row0 = ((int64_t)blockIdx.x * kMergeWaves + wave) * kMergeRows;
+    const int64_t nrows = rows - row0 < kMergeRows ? rows - row0 : kMergeRows;
+    uint2 *sl = s_list[wave];
+    if (nrows > 0) {
+        const int entries = (int)nrows * 2 * k;
+        const uint2 *src = lists + row0 * 2 * k;
+        for (int e = lane; e < entries; e += kWave)
+            sl[e] = src[e];
+    }
+    __syncthreads();
+    if (nrows <= 0)
+        return;
+    const bool live = tok < nrows;
+    const uint2 *l = sl + tok * 2 * k;
+    const uint2 *r = l + k;
+    uint64_t v[32];
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+        const int pc = 32 * g + c;
+        if (live && pc < n_pairs) {
+            const int a = s_pairs[pc] & 0xFF, b = s_pairs[pc] >> 8;
+            const uint2 la = l[a], rb = r[b];
+            v[c] = make_key(unord_f32(la.x) + unord_f32(rb.x), la.y * (uint32_t)n + rb.y);
+        } else {
+            v[c] = 0ull;
+        }
+    }
+    group4_sort_desc<32>(v);
+    // the k <= 32 winners are registers 0..k-1 of the group's first lane
+    if (live && g == 0) {
+        const float top = key_score(v[0]);
+        float e[32], z = 0.f;
+#pragma unroll
+        for (int c = 0; c < 32; ++c) {
+            e[c] = c < k ? expf(key_score(v[c]) - top) : 0.f;
+            z += e[c];
+        }
+        const int64_t out = (row0 + tok) * (int64_t)k;
+#pragma unroll
+        for (int c = 0; c < 32; ++c) {
+            if (c < k) {
+                idx[out + c] = (int32_t)key_index(v[c]);
+                weights[out + c] = e[c] / z;
+                if (scores)
+                    scores[out + c] = key_score(v[c]);
+            }
+        }
+    }
+}
+
+hipError_t launch_select_fast(const void *q, const void *keys, int64_t T, int H, int n, int k,
+                              int d_k, int32_t *idx, float *weights, float *scores,
+                              void *workspace, hipStream_t stream)
+{
+    (void)d_k;      // 512 on this path
+    uint2 *lists = static_cast<uint2 *>(workspace);
+    const dim3 grid((unsigned)((T + kFastTokWG - 1) / kFastTokWG), (unsigned)H, 2);
+    hipLaunchKernelGGL(fwd_topk_half_kernel, grid, dim3(kFastWaves * kWave), 0, stream,
+                       static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(keys), T, H, n,
+                       k, lists);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    const int64_t rows = T * H;
+    const int64_t per_block = (int64_t)kMergeWaves * kMergeRows;
+    hipLaunchKernelGGL(fwd_merge_kernel, dim3((unsigned)((rows + per_block - 1) / per_block)),
+                       dim3(kMergeWaves * kWave), 0, stream, lists, rows, n, k,
+                       merge_candidates(k), idx, weights, scores);
+    return hipGetLastError();
+}
+
+}  // namespace pkm

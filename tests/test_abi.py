@@ -51,7 +51,7 @@ def test_forward_rejects_bad_shapes(kw, code):
 def test_null_and_alignment():
     assert _lib.forward(P(), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 1
     assert _lib.forward(P(), FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 6
-    assert _lib.forward_select(P(), FAKE, FAKE, None, FAKE, None, None) == 1
+    assert _lib.forward_select(P(), FAKE, FAKE, None, FAKE, None, None, 0, None) == 1
     assert _lib.backward_values(P(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE + 8, None) == 6
     assert _lib.slot_sort(P(), FAKE, None, FAKE, FAKE, 1 << 30, None) == 1
 
@@ -61,7 +61,7 @@ def test_backward_workspace_checks():
     need = _lib.workspace_bytes(p, True)
     picks = 16 * 2 * 8
     assert need >= picks * 4 + 64 * 64 * 4 * 3 + picks * 4     # dw + slot sort at least
-    assert _lib.workspace_bytes(p, False) == 0
+    assert _lib.workspace_bytes(p, False) == 0       # this shape takes the one-kernel selection
     # the stages that take a workspace reject a 16-byte one
     assert _lib.slot_sort(p, FAKE, FAKE, FAKE, FAKE, 16, None) == 4
     assert _lib.backward_queries(p, *[FAKE] * 7, FAKE, 16, None) == 4
@@ -78,3 +78,19 @@ def test_workspace_of_invalid_problem():
 def test_status_strings():
     for code, name in _lib.STATUS.items():
         assert _lib.status_string(code).startswith(name)
+
+
+def test_forward_workspace_checks():
+    """The two-kernel selection (bf16, d_k = 512, 256 < n <= 512, k <= 32)
+    keeps its per-half top-k lists in the caller's workspace."""
+    p = P(T=100, H=3, n=300, k=20, d_k=512, d_v=64, dtype=_lib.PKM_BF16)
+    need = _lib.workspace_bytes(p, False)
+    assert need == (100 * 3 * 2 * 20 * 8 + 255) // 256 * 256
+    args = [FAKE] * 5
+    assert _lib.forward_select(p, *args, None, 0, None) == 1
+    assert _lib.forward_select(p, *args, FAKE, need - 1, None) == 4
+    assert _lib.forward_select(p, *args, FAKE + 8, need, None) == 6
+    assert _lib.forward(p, *[FAKE] * 7, FAKE, need - 1, None) == 4
+    # other shapes need none, and accept a NULL workspace
+    q = P(T=100, H=3, n=300, k=20, d_k=256, d_v=64, dtype=_lib.PKM_BF16)
+    assert _lib.workspace_bytes(q, False) == 0

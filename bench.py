@@ -39,12 +39,28 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run 3 plain elementwise copies of 256 MiB (x * 2), whose "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate those of the kernels")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="no GPU work: read the rocprofv3 databases of a FETCH_SIZE run and a "
+                         "WRITE_SIZE run of `bench.py --calibrate-copy`, and write the "
+                         "calibrated HBM bytes per stage to " + "profiles/hbm_traffic_<workload>.json")
     return ap.parse_args()
 
 
 STAGES = ["select", "gather", "slot_sort", "bwd_values", "bwd_queries"]
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                            "hbm_traffic_base-bf16-zipf-bwd.json")
+# kernels of each stage (name prefixes inside namespace pkm)
+STAGE_KERNELS = {
+    "select": ("fwd_topk_half_kernel", "fwd_merge_kernel", "fwd_select_kernel"),
+    "gather": ("fwd_gather_kernel",),
+    "slot_sort": ("bucket_hist_kernel", "bucket_colscan_kernel", "bucket_scatter_kernel",
+                  "bucket_sort_kernel"),
+    "bwd_values": ("dv_prepare_kernel", "seg_value_kernel"),
+    "bwd_queries": ("bwd_query_kernel", "dkeys_mfma_kernel", "dkeys_reduce_kernel"),
+}
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"hbm_traffic_{workload}.json")
 
 
 def stage_bytes(w, elt: int, touched: int) -> dict:
@@ -86,13 +102,61 @@ def measured_traffic(workload: str) -> dict:
     """HBM bytes per stage from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     runs, only if they were taken on the kernels as they are now."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return {}
     if rec.get("source_sha256") != source_hash() or rec.get("workload") != workload:
         return {}
     return rec.get("stages", {})
+
+
+def _counter_means(db: str, counter: str) -> dict:
+    """Mean value per dispatch of `counter`, by kernel name, from a rocprofv3
+    database (its counters_collection view)."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute("select kernel_name, avg(value), count(*) from counters_collection "
+                       "where counter_name = ? group by kernel_name", (counter,)).fetchall()
+    con.close()
+    return {name: (float(avg), int(cnt)) for name, avg, cnt in rows}
+
+
+def record_traffic(fetch_db: str, write_db: str, workload: str) -> str:
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of every stage's kernels,
+    each scaled by the ratio of the known size of the calibration copy
+    (x * 2 over 64 Mi floats: 256 MiB read, 256 MiB written) to what the same
+    counter read for it; summed per stage: bytes per launch of the stage."""
+    fetch, write = _counter_means(fetch_db, "FETCH_SIZE"), _counter_means(write_db, "WRITE_SIZE")
+    copy_kib = 256 * 1024
+
+    def calib(table):
+        cands = [v for name, (v, _) in table.items() if "MulFunctor" in name and v > copy_kib / 4]
+        if not cands:
+            raise SystemExit("no calibration copy in the database (run bench.py --calibrate-copy)")
+        return copy_kib / max(cands)
+
+    f_fac, w_fac = calib(fetch), calib(write)
+    stages = {}
+    for stage, prefixes in STAGE_KERNELS.items():
+        rec = {"read_bytes": 0, "write_bytes": 0, "kernels": {}}
+        for table, fac, key in ((fetch, f_fac, "read_bytes"), (write, w_fac, "write_bytes")):
+            for name, (kib, cnt) in table.items():
+                short = name.split("(")[0].replace("void ", "").replace("pkm::", "")
+                if short.split("<")[0] in prefixes:
+                    b = int(round(kib * fac * 1024))
+                    rec[key] += b
+                    rec["kernels"].setdefault(short, {})[key] = b
+        stages[stage] = rec
+    out = {"source_sha256": source_hash(), "workload": workload,
+           "calibration": {"copy_bytes_read": copy_kib * 1024, "copy_bytes_written": copy_kib * 1024,
+                           "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
+           "units": "bytes per launch of the stage (the sum of its kernels' dispatches)",
+           "stages": stages}
+    path = traffic_file(workload)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    return path
 
 
 def cpu_baseline(inp, k: int, count: int) -> dict:
@@ -116,6 +180,9 @@ def cpu_baseline(inp, k: int, count: int) -> dict:
 
 def main():
     args = parse()
+    if args.record_traffic:
+        print(record_traffic(*args.record_traffic, args.workload))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

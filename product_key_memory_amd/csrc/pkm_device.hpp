@@ -223,10 +223,6 @@ __device__ __forceinline__ void wave_sort_desc(uint64_t (&v)[R])
 // Bitonic sort, descending, inside each group of 4 lanes {l, l^16, l^32, l^48}
 // (the lanes that share l % 16), of the 4R values the group holds: element
 // e = (lane / 16) * R + r lives in register r of lane group lane / 16.
-template <int R, typename T>
-__device__ __forceinline__ T g4_max(T a, T b) { return a > b ? a : b; }
-template <int R, typename T>
-__device__ __forceinline__ T g4_min(T a, T b) { return a < b ? a : b; }
 __device__ __forceinline__ float g4_shfl(float v, int m) { return __shfl_xor(v, m); }
 __device__ __forceinline__ uint32_t g4_shfl(uint32_t v, int m) { return (uint32_t)__shfl_xor((int)v, m); }
 __device__ __forceinline__ uint64_t g4_shfl(uint64_t v, int m) { return shfl_xor_u64(v, m); }
@@ -244,26 +240,32 @@ __device__ __forceinline__ void group4_sort_desc(T (&v)[R])
 {
     const int g = lane_id() >> 4;
     constexpr int P = 4 * R;
+    // Every compare-exchange is one compare, at most one lane-mask XOR (a
+    // scalar op) and plain selects: the direction of a stage, where it depends
+    // on the lane group, is a lane mask computed once per stage.
 #pragma unroll
     for (int size = 2; size <= P; size <<= 1) {
 #pragma unroll
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
             if (stride >= R) {
+                // partner in lane group g ^ (stride / R); the lane keeps the
+                // larger value iff (lower half) == (descending block)
                 const int lm = 16 * (stride / R);
-                const bool lower = ((g * R) & stride) == 0;
+                const bool keep_min = (((g * R) & stride) == 0) != (((g * R) & size) == 0);
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const bool desc = ((g * R + r) & size) == 0;
                     const T o = g4_shfl(v[r], lm);
-                    v[r] = (lower == desc) ? g4_max<R>(v[r], o) : g4_min<R>(v[r], o);
+                    const bool take = (v[r] < o) != keep_min;   // o is the one to keep
+                    v[r] = take ? o : v[r];
                 }
             } else {
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     if ((r & stride) == 0) {
-                        const bool desc = ((g * R + r) & size) == 0;
+                        // ascending block: swap when a >= b (equal keys are identical)
+                        const bool asc = ((g * R + r) & size) != 0;
                         const T a = v[r], b = v[r | stride];
-                        const bool swap = desc ? (a < b) : (a > b);
+                        const bool swap = (a < b) != asc;
                         v[r] = swap ? b : a;
                         v[r | stride] = swap ? a : b;
                     }

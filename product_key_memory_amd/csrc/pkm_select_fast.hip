@@ -58,6 +58,7 @@ __device__ __forceinline__ void fast_scores(uint32_t (&so)[kFastTiles][4], const
     // every fragment is the lane offset plus a constant
     const __amdgpu_buffer_rsrc_t rsrc = buffer_over(kb, n * half * 2);
     const int lane_off = tok * half * 2 + 16 * g;
+    const int lim = n - 4 * g;        // sub-key 16 j + 4 g + i exists iff 16 j + i < lim
     // step -> (tile, K step): tiles 2p and 2p + 1 alternate within pair p
     auto load_step = [&](int step) {
         const int p = step / (2 * kFastKSteps), rem = step % (2 * kFastKSteps);
@@ -90,8 +91,7 @@ __device__ __forceinline__ void fast_scores(uint32_t (&so)[kFastTiles][4], const
             const int j = 2 * pr + w;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                so[j][i] = ord_f32((j < kFastTiles / 2 || 16 * j + 4 * g + i < n) ? acc[w][i]
-                                                                                  : -INFINITY);
+                so[j][i] = ord_f32((j < kFastTiles / 2 || 16 * j + i < lim) ? acc[w][i] : -INFINITY);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -103,7 +103,8 @@ __global__ __launch_bounds__(kFastWaves *kWave) void fwd_topk_half_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ keys, int64_t T, int H, int n,
     int k, uint2 *__restrict__ lists)
 {
-    __shared__ uint64_t surv_all[kFastWaves][kFastTok * kFastSurv];
+    __shared__ uint32_t surv_s_all[kFastWaves][kFastTok * kFastSurv];
+    __shared__ uint32_t surv_i_all[kFastWaves][kFastTok * kFastSurv];
 
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
@@ -113,7 +114,8 @@ __global__ __launch_bounds__(kFastWaves *kWave) void fwd_topk_half_kernel(
     const int h = blockIdx.y, s = blockIdx.z;
     const int64_t t = (int64_t)blockIdx.x * kFastTokWG + wave * kFastTok + tok;
     const bool live = t < T;
-    uint64_t *surv = surv_all[wave] + tok * kFastSurv;
+    uint32_t *surv_s = surv_s_all[wave] + tok * kFastSurv;
+    uint32_t *surv_i = surv_i_all[wave] + tok * kFastSurv;
 
     // an opaque copy of the lane group, so values derived from it (the 128
     // sub-key indices) are formed where used instead of being held in registers
@@ -188,14 +190,14 @@ __global__ __launch_bounds__(kFastWaves *kWave) void fwd_topk_half_kernel(
         uint32_t I = 0;                              // largest bound with < need tied indices below it
         for (int bit = 9; bit >= 0; --bit) {
             const uint32_t cand = I | (1u << bit);
-            int gb = g;                   // opaque: keep the indices out of registers
-            asm volatile("" : "+v"(gb));
+            // sub-key 16 j + 4 g + i < cand  <=>  16 j + i < cand - 4 g
+            const int lim_c = (int)cand - 4 * g;
             int c = 0;
 #pragma unroll
             for (int j = 0; j < kFastTiles; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    c += (so[j][i] == K && (uint32_t)(16 * j + 4 * gb + i) < cand) ? 1 : 0;
+                    c += (so[j][i] == K && 16 * j + i < lim_c) ? 1 : 0;
             if (group4_sum(c) < need)
                 I = cand;
         }
@@ -207,13 +209,15 @@ __global__ __launch_bounds__(kFastWaves *kWave) void fwd_topk_half_kernel(
         }
     }
 
-    // compact the survivors (keys) per token, then sort them in the 4-lane group
-    int off;
-    {
-        const int c0 = __shfl(cnt, tok), c1 = __shfl(cnt, tok + 16), c2 = __shfl(cnt, tok + 32);
-        off = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
-    }
-    if (tie_idx != 0xFFFFFFFFu) {
+    // compact the survivors per token as two 32-bit arrays (scores, and the
+    // part 16 j + i of the sub-key known at compile time: 64-bit keys built
+    // here would pin register pairs for all 128 candidates), then sort them as
+    // keys in the 4-lane group.  The reader adds 4 x (the writing lane group),
+    // which it knows from the survivor's position.
+    const bool exact = tie_idx != 0xFFFFFFFFu;
+    const int lim_t = exact ? (int)tie_idx - 4 * g : 0;   // 16 j + i <= lim_t among ties
+    int mine = cnt;
+    if (exact) {
         // recount this lane's share under the exact bound
         int c = 0;
 #pragma unroll
@@ -221,29 +225,34 @@ __global__ __launch_bounds__(kFastWaves *kWave) void fwd_topk_half_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t o = so[j][i];
-                c += (o > kth || (o == kth && (uint32_t)(16 * j + 4 * g + i) <= tie_idx)) ? 1 : 0;
+                c += (o > kth || (o == kth && 16 * j + i <= lim_t)) ? 1 : 0;
             }
-        const int c0 = __shfl(c, tok), c1 = __shfl(c, tok + 16), c2 = __shfl(c, tok + 32);
-        off = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
+        mine = c;
     }
+    const int c0 = __shfl(mine, tok), c1 = __shfl(mine, tok + 16), c2 = __shfl(mine, tok + 32);
+    int off = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
 #pragma unroll
     for (int j = 0; j < kFastTiles; ++j) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t o = so[j][i];
-            const uint32_t sub = (uint32_t)(16 * j + 4 * g + i);
-            const bool keep = tie_idx == 0xFFFFFFFFu ? o >= kth : (o > kth || (o == kth && sub <= tie_idx));
-            if (keep)
-                surv[off++] = ((uint64_t)o << 32) | (uint64_t)(~sub);
+            const bool keep = exact ? (o > kth || (o == kth && 16 * j + i <= lim_t)) : o >= kth;
+            if (keep) {
+                surv_s[off] = o;
+                surv_i[off] = (uint32_t)(16 * j + i);
+                ++off;
+            }
         }
         __builtin_amdgcn_sched_barrier(0);     // one tile's keys at a time
     }
     wave_lds_sync();
     uint64_t v[16];
+    const int b1 = c0, b2 = c0 + c1, b3 = c0 + c1 + c2;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int e = 16 * g + r;
-        v[r] = e < total ? surv[e] : 0ull;
+        const uint32_t src_g = (e >= b1 ? 1u : 0u) + (e >= b2 ? 1u : 0u) + (e >= b3 ? 1u : 0u);
+        v[r] = e < total ? ((uint64_t)surv_s[e] << 32) | (uint64_t)~(surv_i[e] + 4u * src_g) : 0ull;
     }
     group4_sort_desc<16>(v);
     // lane group g holds ranks 16 g .. 16 g + 15
@@ -275,15 +284,27 @@ __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
         for (int b = 0; b < cnt; ++b)
             s_pairs[start + b] = (uint16_t)(lane | (b << 8));
     }
-    // the wave's rows are contiguous in the lists: stage them in LDS
+    // the wave's rows are contiguous in the lists: stage them in LDS, all
+    // 16-byte loads in flight before the first store
     const int64_t row0 = ((int64_t)blockIdx.x * kMergeWaves + wave) * kMergeRows;
     const int64_t nrows = rows - row0 < kMergeRows ? rows - row0 : kMergeRows;
     uint2 *sl = s_list[wave];
     if (nrows > 0) {
-        const int entries = (int)nrows * 2 * k;
-        const uint2 *src = lists + row0 * 2 * k;
-        for (int e = lane; e < entries; e += kWave)
-            sl[e] = src[e];
+        constexpr int kPerLane = kMergeRows * 2 * 32 / 2 / kWave;     // uint4 per lane
+        const int units = (int)nrows * k;                               // 2 entries each
+        const uint4 *src = reinterpret_cast<const uint4 *>(lists + row0 * 2 * k);
+        uint4 buf[kPerLane];
+#pragma unroll
+        for (int u = 0; u < kPerLane; ++u) {
+            const int e = lane + u * kWave;
+            buf[u] = e < units ? src[e] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < kPerLane; ++u) {
+            const int e = lane + u * kWave;
+            if (e < units)
+                reinterpret_cast<uint4 *>(sl)[e] = buf[u];
+        }
     }
     __syncthreads();
     if (nrows <= 0)

@@ -252,11 +252,17 @@ __device__ __forceinline__ void group4_sort_desc(T (&v)[R])
                 // larger value iff (lower half) == (descending block)
                 const int lm = 16 * (stride / R);
                 const bool keep_min = (((g * R) & stride) == 0) != (((g * R) & size) == 0);
+                // all R exchanges are issued before the first is used, so their
+                // LDS round trips overlap
+                T o[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    o[r] = g4_shfl(v[r], lm);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const T o = g4_shfl(v[r], lm);
-                    const bool take = (v[r] < o) != keep_min;   // o is the one to keep
-                    v[r] = take ? o : v[r];
+                    const bool take = (v[r] < o[r]) != keep_min;   // o is the one to keep
+                    v[r] = take ? o[r] : v[r];
                 }
             } else {
 #pragma unroll

@@ -45,55 +45,74 @@ constexpr int kMaxPairs = 128;                       // merge_candidates(32) = 1
 
 // Scores of the wave's 16 tokens against sub-keys 0..n-1 of one codebook, as
 // order-preserving integers: so[j][i] = ord(score of sub-key 16 j + 4 g + i)
-// for token `tok` (ord(-inf) past n).  Tiles are computed in pairs whose two
-// accumulation chains alternate, so consecutive MFMAs do not wait on each
-// other.
+// for token `tok` (ord(-inf) past n).  The workgroup's 4 waves (64 tokens)
+// share the codebook through LDS: per step p it holds rows 32 p .. 32 p + 31
+// (16 KB, double-buffered), each thread loading 4 of its 16-byte chunks, so
+// the L2 serves each codebook once per 64 tokens instead of once per 16.
+// Chunk c of local row r sits at position c ^ (r % 16) of the row: the 16
+// rows an MFMA operand read touches (same chunk, rows r16 = 0..15) then fall
+// in distinct banks.  Within a step the two tiles' accumulation chains
+// alternate, so consecutive MFMAs do not wait on each other.
 __device__ __forceinline__ void fast_scores(uint32_t (&so)[kFastTiles][4], const uint16_t *kb,
-                                            const uint4 (&qf)[kFastKSteps], int n, int tok, int g)
+                                            const uint4 (&qf)[kFastKSteps], int n, int r16, int g,
+                                            uint4 *kbuf, int tid)
 {
     constexpr int half = kFastKSteps * 32;
-    constexpr int kDepth = 8;                     // A fragments in flight
-    constexpr int kSteps = kFastTiles * kFastKSteps;
-    // one buffer descriptor over the codebook: rows past n read as zeros, and
-    // every fragment is the lane offset plus a constant
+    constexpr int chunks = half * 2 / 16;            // 32 chunks of 16 bytes per row
+    constexpr int step_units = 32 * chunks;          // 1024 chunks per 32-row step
+    constexpr int per_thread = step_units / (kFastWaves * kWave);
+    constexpr int steps = kFastTiles / 2;
+    // rows past n read as zeros
     const __amdgpu_buffer_rsrc_t rsrc = buffer_over(kb, n * half * 2);
-    const int lane_off = tok * half * 2 + 16 * g;
     const int lim = n - 4 * g;        // sub-key 16 j + 4 g + i exists iff 16 j + i < lim
-    // step -> (tile, K step): tiles 2p and 2p + 1 alternate within pair p
-    auto load_step = [&](int step) {
-        const int p = step / (2 * kFastKSteps), rem = step % (2 * kFastKSteps);
-        const int tile = 2 * p + (rem & 1), kk = rem >> 1;
-        return buffer_load16(rsrc, lane_off, tile * 16 * half * 2 + kk * 64);
+    uint4 pre[per_thread];
+    auto gload = [&](int p) {
+#pragma unroll
+        for (int m = 0; m < per_thread; ++m) {
+            const int u = tid + m * kFastWaves * kWave;
+            const int rl = u / chunks, c = (u % chunks) ^ (rl & 15);
+            pre[m] = buffer_load16(rsrc, ((32 * p + rl) * chunks + c) * 16, 0);
+        }
     };
-    uint4 ring[kDepth];
+    auto lstore = [&](int buf) {
 #pragma unroll
-    for (int p = 0; p < kDepth; ++p)
-        ring[p] = load_step(p);
+        for (int m = 0; m < per_thread; ++m)
+            kbuf[buf * step_units + tid + m * kFastWaves * kWave] = pre[m];
+    };
+    gload(0);
+    lstore(0);
+    gload(1);
+    __syncthreads();
 #pragma unroll
-    for (int pr = 0; pr < kFastTiles / 2; ++pr) {
+    for (int p = 0; p < steps; ++p) {
+        const uint4 *cur = kbuf + (p & 1) * step_units;
         floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int kk = 0; kk < kFastKSteps; ++kk) {
 #pragma unroll
             for (int w = 0; w < 2; ++w) {
-                const int step = pr * 2 * kFastKSteps + 2 * kk + w;
-                const uint4 cur = ring[step % kDepth];
-                if (step + kDepth < kSteps)
-                    ring[step % kDepth] = load_step(step + kDepth);
+                const int rl = 16 * w + r16;
+                const uint4 a = cur[rl * chunks + ((4 * kk + g) ^ r16)];
                 acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, cur), __builtin_bit_cast(bf16x8, qf[kk]), acc[w],
+                    __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[kk]), acc[w],
                     0, 0, 0);
             }
         }
         // n > 256 on this path: only the upper 16 tiles can hold sub-keys >= n
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
-            const int j = 2 * pr + w;
+            const int j = 2 * p + w;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 so[j][i] = ord_f32((j < kFastTiles / 2 || 16 * j + i < lim) ? acc[w][i] : -INFINITY);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        // step p + 1 goes to the other buffer (its readers finished at the
+        // last barrier); step p + 2 is fetched while step p + 1 is worked on
+        if (p + 1 < steps)
+            lstore((p + 1) & 1);
+        if (p + 2 < steps)
+            gload(p + 2);
+        __syncthreads();
     }
 }
 
@@ -103,8 +122,12 @@ __global__ __launch_bounds__(kFastWaves *kWave) void fwd_topk_half_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ keys, int64_t T, int H, int n,
     int k, uint2 *__restrict__ lists)
 {
-    __shared__ uint32_t surv_s_all[kFastWaves][kFastTok * kFastSurv];
-    __shared__ uint32_t surv_i_all[kFastWaves][kFastTok * kFastSurv];
+    // the codebook steps during the scoring, the survivors afterwards
+    __shared__ uint4 lds[2 * 32 * 32];
+    static_assert(sizeof(lds) >= 2 * kFastWaves * kFastTok * kFastSurv * 4, "survivor space");
+    uint32_t(*surv_s_all)[kFastTok * kFastSurv] =
+        reinterpret_cast<uint32_t(*)[kFastTok * kFastSurv]>(lds);
+    uint32_t(*surv_i_all)[kFastTok * kFastSurv] = surv_s_all + kFastWaves;
 
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
@@ -130,7 +153,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) void fwd_topk_half_kernel(
         qf[kk] = *reinterpret_cast<const uint4 *>(qrow + 32 * kk + 8 * g);
     const uint16_t *kb = reinterpret_cast<const uint16_t *>(keys) + ((int64_t)h * 2 + s) * (int64_t)n * half;
     uint32_t so[kFastTiles][4];
-    fast_scores(so, kb, qf, n, tok, g);
+    fast_scores(so, kb, qf, n, tok, g, lds, threadIdx.x);
 
     // tau: k-th largest of the token's 64 group maxima (groups of 8 scores)
     uint32_t gm[16];

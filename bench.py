@@ -159,6 +159,45 @@ def record_traffic(fetch_db: str, write_db: str, workload: str) -> str:
     return path
 
 
+def measure_extras(torch, _lib, p, values, dvalues, slot_start, w, elt, touched, stream) -> dict:
+    """The value-table update and the usage counter that follow the backward
+    (not part of the step): event time per call over 5 calls after 2 warm-up
+    calls, on the step's own gradient and slot sort."""
+    slots, d_v = w.n * w.n, w.d_v
+    dev = values.device
+    m = torch.zeros((slots, d_v), dtype=torch.float32, device=dev)
+    v = torch.zeros_like(m)
+    counts = torch.zeros(slots, dtype=torch.int64, device=dev)
+    used = torch.zeros(1, dtype=torch.int64, device=dev)
+    sp = stream.cuda_stream
+    P = lambda t: t.data_ptr()  # noqa: E731
+    calls = {
+        "sparse_sgd": (lambda i: _lib.sparse_sgd(p, P(values), P(dvalues), P(slot_start), 1e-3, sp),
+                       touched * d_v * (2 * elt + 4) + (slots + 1) * 4),
+        "sparse_adam": (lambda i: _lib.sparse_adam(p, P(values), P(dvalues), P(slot_start), P(m),
+                                                   P(v), i + 1, 1e-3, 0.9, 0.999, 1e-8, sp),
+                        touched * d_v * (2 * elt + 4 + 16) + (slots + 1) * 4),
+        "slot_usage": (lambda i: _lib.slot_usage(p, P(slot_start), P(counts), P(used), sp),
+                       (slots + 1) * 4 + slots * 16),
+    }
+    out = {}
+    for name, (fn, nbytes) in calls.items():
+        for i in range(2):
+            assert fn(i) == 0, name
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(5):
+            fn(2 + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 5), "bytes": nbytes, "GB/s": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    out["slot_usage"]["used_fraction"] = round(int(used.item()) / slots, 4)
+    return out
+
+
 def cpu_baseline(inp, k: int, count: int) -> dict:
     import oracle
     import pkm_inputs
@@ -300,6 +339,8 @@ def main():
             entry["traffic"] = traffic[name]["read_bytes"] + traffic[name]["write_bytes"]
         kernels[name] = entry
 
+    extras = measure_extras(torch, _lib, p, values, dvalues, slot_start, w, elt, touched, stream)
+
     dominant = max(STAGES, key=lambda s: per_stage[s])
     dk = kernels[dominant]
     roofline = {"kernel": dominant, "bound": "hbm", "achieved": dk["GB/s"], "peak": HBM_PEAK_GBS,
@@ -326,6 +367,7 @@ def main():
         "gather": {"GB/s": kernels["gather"]["GB/s"], "hbm_frac": kernels["gather"]["hbm_frac"]},
         "roofline": roofline,
         "kernels": kernels,
+        "after_backward": extras,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, k, args.cpu_tokens)

@@ -55,7 +55,9 @@ typedef enum {
     PKM_ERR_DTYPE = 3,     /* unknown dtype                                      */
     PKM_ERR_WORKSPACE = 4, /* workspace smaller than pkm_workspace_bytes()       */
     PKM_ERR_HIP = 5,       /* the HIP runtime rejected a launch                  */
-    PKM_ERR_ALIGN = 6      /* an array pointer is not 16-byte aligned            */
+    PKM_ERR_ALIGN = 6,     /* an array pointer is not 16-byte aligned            */
+    PKM_ERR_ARG = 7        /* a scalar argument outside its domain (learning
+                              rate, Adam constants, step)                        */
 } pkm_status_t;
 
 /* Problem sizes.  32 bytes, no padding: T, then six int32 fields. */
@@ -187,6 +189,53 @@ pkm_status_t pkm_backward_queries(const pkm_problem_t *p, const void *q, const v
                                   const int32_t *idx, const float *weights, const float *dw,
                                   float *dq, float *dkeys, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/*
+ * After the backward: the value table's sparse update and the slot-usage
+ * counter.  Both read the slot sort of the batch (slot_start from
+ * pkm_slot_sort, or the workspace of pkm_backward: its slot_start follows the
+ * T*H*k floats of dw, rounded up to 256 bytes): slot f is TOUCHED iff
+ * slot_start[f+1] > slot_start[f], i.e. some pick selected it.  Only T, H and
+ * k of `p` may differ from the backward's problem; n, d_v and dtype must be
+ * the same.
+ */
+
+/* Sparse update of the memory values (gptget.net summary, "Methodology": the
+ * layer is trained with sparse updates, only the selected slots change),
+ * plain SGD: for every touched slot f and every column c,
+ *   values[f][c] = values[f][c] - lr * dvalues[f][c]
+ * computed as one float32 fused multiply-add, rounded once to the storage
+ * type (bf16: nearest, ties to even).  Rows of untouched slots are not read
+ * or written.
+ *   values   [n*n][d_v] dtype    IN/OUT
+ *   dvalues  [n*n][d_v] float32  IN (pkm_backward's value gradient)
+ *   lr       finite, else PKM_ERR_ARG */
+pkm_status_t pkm_sparse_sgd(const pkm_problem_t *p, void *values, const float *dvalues,
+                            const int32_t *slot_start, float lr, void *stream);
+
+/* The same with Adam, moments kept and advanced only for touched rows (a
+ * "lazy" Adam: a row's moments stand still while it is not selected):
+ *   m = beta1 m + (1 - beta1) g;  v = beta2 v + (1 - beta2) g^2;
+ *   values -= lr * (m / c1) / (sqrt(v / c2) + eps),
+ *   c1 = 1 - beta1^step, c2 = 1 - beta2^step (computed in double on the host,
+ *   rounded to float32); float32 arithmetic, one rounding to the storage type.
+ *   adam_m, adam_v  [n*n][d_v] float32 IN/OUT, caller-owned (zero at step 1)
+ *   step >= 1, beta1, beta2 in [0, 1), eps > 0 and finite, lr finite, else
+ *   PKM_ERR_ARG. */
+pkm_status_t pkm_sparse_adam(const pkm_problem_t *p, void *values, const float *dvalues,
+                             const int32_t *slot_start, float *adam_m, float *adam_v,
+                             int64_t step, float lr, float beta1, float beta2, float eps,
+                             void *stream);
+
+/* Memory usage (gptget.net summary, "Key Results": the share of memory slots
+ * in use, which batch-norm in the query network raises above 80%):
+ *   counts[f] += slot_start[f+1] - slot_start[f]   (picks of slot f)
+ *   *used      = number of slots f with counts[f] != 0 after the update
+ *   counts  [n*n]  int64  IN/OUT, accumulates over calls (zero it to start)
+ *   used    [1]    int64  OUT, device memory, 8-byte aligned; may be NULL
+ * usage = *used / (n*n). */
+pkm_status_t pkm_slot_usage(const pkm_problem_t *p, const int32_t *slot_start, int64_t *counts,
+                            int64_t *used, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *pkm_status_string(pkm_status_t s);

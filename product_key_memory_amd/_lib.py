@@ -23,12 +23,13 @@ STATUS = {
     4: "PKM_ERR_WORKSPACE",
     5: "PKM_ERR_HIP",
     6: "PKM_ERR_ALIGN",
+    7: "PKM_ERR_ARG",
 }
 
 # every symbol include/pkm.h declares
 EXPORTS = ("pkm_workspace_bytes", "pkm_forward", "pkm_backward", "pkm_forward_select",
            "pkm_forward_gather", "pkm_slot_sort", "pkm_backward_values", "pkm_backward_queries",
-           "pkm_status_string")
+           "pkm_sparse_sgd", "pkm_sparse_adam", "pkm_slot_usage", "pkm_status_string")
 
 
 class Problem(ctypes.Structure):
@@ -69,8 +70,13 @@ def lib() -> ctypes.CDLL:
         L.pkm_slot_sort.argtypes = [PP, P, P, P, P, c_size, P]
         L.pkm_backward_values.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_int, P, P]
         L.pkm_backward_queries.argtypes = [PP, P, P, P, P, P, P, P, P, c_size, P]
+        F, I64 = ctypes.c_float, ctypes.c_int64
+        L.pkm_sparse_sgd.argtypes = [PP, P, P, P, F, P]
+        L.pkm_sparse_adam.argtypes = [PP, P, P, P, P, P, I64, F, F, F, F, P]
+        L.pkm_slot_usage.argtypes = [PP, P, P, P, P]
         for name in ("pkm_forward_select", "pkm_forward_gather", "pkm_slot_sort",
-                     "pkm_backward_values", "pkm_backward_queries"):
+                     "pkm_backward_values", "pkm_backward_queries", "pkm_sparse_sgd",
+                     "pkm_sparse_adam", "pkm_slot_usage"):
             getattr(L, name).restype = ctypes.c_int
         L.pkm_status_string.argtypes = [ctypes.c_int]
         L.pkm_status_string.restype = ctypes.c_char_p
@@ -120,3 +126,17 @@ def backward_queries(p: Problem, q, keys, idx, weights, dw, dq, dkeys, ws, ws_by
                      stream) -> int:
     return lib().pkm_backward_queries(ctypes.byref(p), q, keys, idx, weights, dw, dq, dkeys, ws,
                                       ws_bytes, stream)
+
+
+def sparse_sgd(p: Problem, values, dvalues, slot_start, lr, stream) -> int:
+    return lib().pkm_sparse_sgd(ctypes.byref(p), values, dvalues, slot_start, float(lr), stream)
+
+
+def sparse_adam(p: Problem, values, dvalues, slot_start, m, v, step, lr, beta1, beta2, eps,
+                stream) -> int:
+    return lib().pkm_sparse_adam(ctypes.byref(p), values, dvalues, slot_start, m, v, int(step),
+                                 float(lr), float(beta1), float(beta2), float(eps), stream)
+
+
+def slot_usage(p: Problem, slot_start, counts, used, stream) -> int:
+    return lib().pkm_slot_usage(ctypes.byref(p), slot_start, counts, used, stream)

@@ -4,8 +4,11 @@
 #include "pkm.h"
 #include "pkm_kernels.hpp"
 #include "pkm_scratch.hpp"
+#include "pkm_update.hpp"
 
 #include <hip/hip_runtime.h>
+
+#include <cmath>
 
 namespace {
 
@@ -272,6 +275,71 @@ pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *key
                                 stream);
 }
 
+pkm_status_t pkm_sparse_sgd(const pkm_problem_t *p, void *values, const float *dvalues,
+                            const int32_t *slot_start, float lr, void *stream)
+{
+    pkm_status_t st = check_problem(p, false);
+    if (st != PKM_OK)
+        return st;
+    if (!values || !dvalues || !slot_start)
+        return PKM_ERR_NULL;
+    if (!aligned16(values) || !aligned16(dvalues) || !aligned16(slot_start))
+        return PKM_ERR_ALIGN;
+    if (!std::isfinite(lr))
+        return PKM_ERR_ARG;
+    pkm::UpdateParams prm{lr, 0.f, 0.f, 0.f, 1.f, 1.f};
+    return pkm::launch_sparse_update(p->dtype, values, dvalues, slot_start, nullptr, nullptr,
+                                     (int64_t)p->n * p->n, p->d_v, false, prm,
+                                     static_cast<hipStream_t>(stream)) == hipSuccess
+               ? PKM_OK
+               : PKM_ERR_HIP;
+}
+
+pkm_status_t pkm_sparse_adam(const pkm_problem_t *p, void *values, const float *dvalues,
+                             const int32_t *slot_start, float *adam_m, float *adam_v,
+                             int64_t step, float lr, float beta1, float beta2, float eps,
+                             void *stream)
+{
+    pkm_status_t st = check_problem(p, false);
+    if (st != PKM_OK)
+        return st;
+    if (!values || !dvalues || !slot_start || !adam_m || !adam_v)
+        return PKM_ERR_NULL;
+    if (!aligned16(values) || !aligned16(dvalues) || !aligned16(slot_start) ||
+        !aligned16(adam_m) || !aligned16(adam_v))
+        return PKM_ERR_ALIGN;
+    if (step < 1 || !std::isfinite(lr) || !(beta1 >= 0.f && beta1 < 1.f) ||
+        !(beta2 >= 0.f && beta2 < 1.f) || !(eps > 0.f) || !std::isfinite(eps))
+        return PKM_ERR_ARG;
+    const double c1 = 1.0 - std::pow((double)beta1, (double)step);
+    const double c2 = 1.0 - std::pow((double)beta2, (double)step);
+    if (!(c1 > 0.0) || !(c2 > 0.0))
+        return PKM_ERR_ARG;
+    pkm::UpdateParams prm{lr, beta1, beta2, eps, (float)c1, (float)c2};
+    return pkm::launch_sparse_update(p->dtype, values, dvalues, slot_start, adam_m, adam_v,
+                                     (int64_t)p->n * p->n, p->d_v, true, prm,
+                                     static_cast<hipStream_t>(stream)) == hipSuccess
+               ? PKM_OK
+               : PKM_ERR_HIP;
+}
+
+pkm_status_t pkm_slot_usage(const pkm_problem_t *p, const int32_t *slot_start, int64_t *counts,
+                            int64_t *used, void *stream)
+{
+    pkm_status_t st = check_problem(p, false);
+    if (st != PKM_OK)
+        return st;
+    if (!slot_start || !counts)
+        return PKM_ERR_NULL;
+    if (!aligned16(slot_start) || !aligned16(counts) ||
+        (used && (reinterpret_cast<uintptr_t>(used) & 7u)))
+        return PKM_ERR_ALIGN;
+    return pkm::launch_slot_usage(slot_start, counts, (int64_t)p->n * p->n, used,
+                                  static_cast<hipStream_t>(stream)) == hipSuccess
+               ? PKM_OK
+               : PKM_ERR_HIP;
+}
+
 const char *pkm_status_string(pkm_status_t s)
 {
     switch (s) {
@@ -282,6 +350,7 @@ const char *pkm_status_string(pkm_status_t s)
     case PKM_ERR_WORKSPACE: return "PKM_ERR_WORKSPACE: workspace smaller than pkm_workspace_bytes()";
     case PKM_ERR_HIP: return "PKM_ERR_HIP: the HIP runtime rejected a launch";
     case PKM_ERR_ALIGN: return "PKM_ERR_ALIGN: an array pointer is not 16-byte aligned";
+    case PKM_ERR_ARG: return "PKM_ERR_ARG: a scalar argument is outside its domain";
     }
     return "PKM: unknown status";
 }

@@ -156,6 +156,66 @@ def pkm_slot_sort(idx: torch.Tensor, n: int, out=None):
     return slot_start, order
 
 
+def _update_problem(values: torch.Tensor, n: int):
+    if values.dim() != 2 or values.shape[0] != n * n or values.dtype not in _DTYPES:
+        raise ValueError("values must be [n*n, d_v] float32 or bfloat16")
+    # T, H, k, d_k do not enter the update; any admissible values serve
+    return problem(0, 1, n, 1, 16, values.shape[1], values.dtype)
+
+
+def pkm_sparse_sgd(values: torch.Tensor, dvalues: torch.Tensor, slot_start: torch.Tensor,
+                   lr: float) -> torch.Tensor:
+    """In place: values[f] -= lr * dvalues[f] for the slots f the batch selected
+    (slot_start from pkm_slot_sort).  Returns values."""
+    n = int(round((slot_start.numel() - 1) ** 0.5))
+    p = _update_problem(values, n)
+    dev = values.device
+    _check(values, "values", values.shape, values.dtype, dev)
+    _check(dvalues, "dvalues", values.shape, torch.float32, dev)
+    _check(slot_start, "slot_start", (n * n + 1,), torch.int32, dev)
+    rc = _lib.sparse_sgd(p, _ptr(values), _ptr(dvalues), _ptr(slot_start), lr, _stream(dev))
+    if rc != 0:
+        raise PKMError(rc, "pkm_sparse_sgd")
+    return values
+
+
+def pkm_sparse_adam(values: torch.Tensor, dvalues: torch.Tensor, slot_start: torch.Tensor,
+                    m: torch.Tensor, v: torch.Tensor, step: int, lr: float,
+                    beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8) -> torch.Tensor:
+    """In place Adam on the selected slots only (moments of other rows stand
+    still).  m, v: float32 [n*n, d_v], zero before step 1.  Returns values."""
+    n = int(round((slot_start.numel() - 1) ** 0.5))
+    p = _update_problem(values, n)
+    dev = values.device
+    _check(values, "values", values.shape, values.dtype, dev)
+    for t, name in ((dvalues, "dvalues"), (m, "m"), (v, "v")):
+        _check(t, name, values.shape, torch.float32, dev)
+    _check(slot_start, "slot_start", (n * n + 1,), torch.int32, dev)
+    rc = _lib.sparse_adam(p, _ptr(values), _ptr(dvalues), _ptr(slot_start), _ptr(m), _ptr(v),
+                          step, lr, beta1, beta2, eps, _stream(dev))
+    if rc != 0:
+        raise PKMError(rc, "pkm_sparse_adam")
+    return values
+
+
+def pkm_slot_usage(slot_start: torch.Tensor, counts: torch.Tensor | None = None):
+    """counts [n*n] int64 += picks per slot of this batch (a new zeroed array
+    if None).  Returns (counts, used) with used a 1-element int64 tensor: the
+    slots with a non-zero count."""
+    n = int(round((slot_start.numel() - 1) ** 0.5))
+    dev = slot_start.device
+    _check(slot_start, "slot_start", (n * n + 1,), torch.int32, dev)
+    if counts is None:
+        counts = torch.zeros(n * n, dtype=torch.int64, device=dev)
+    _check(counts, "counts", (n * n,), torch.int64, dev)
+    used = torch.empty(1, dtype=torch.int64, device=dev)
+    p = problem(0, 1, n, 1, 16, 8, torch.float32)
+    rc = _lib.slot_usage(p, _ptr(slot_start), _ptr(counts), _ptr(used), _stream(dev))
+    if rc != 0:
+        raise PKMError(rc, "pkm_slot_usage")
+    return counts, used
+
+
 class ProductKeyMemoryFunction(torch.autograd.Function):
     """y = PKM(q, keys, values) with the library's backward."""
 

@@ -41,53 +41,67 @@ __global__ __launch_bounds__(kUpdWaves *kWave) void sparse_update_kernel(
     const int64_t f = (int64_t)blockIdx.x * kUpdWaves + threadIdx.x / kWave;
     if (f >= slots || start[f + 1] == start[f])
         return;
-    // 8 elements per step: one 16-byte chunk of a bf16 row, two of a float32 row
+    // 8 elements per step: one 16-byte chunk of a bf16 row, two of a float32
+    // row; a lane's steps are all loaded before the first is updated
     const int64_t row = f * d_v;
-    for (int e0 = 8 * lane; e0 < d_v; e0 += 8 * kWave) {
-        float w[8], g[8];
-        const float4 *gs = reinterpret_cast<const float4 *>(dvalues + row + e0);
-        const float4 g0 = gs[0], g1 = gs[1];
-        g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
-        g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
-        if constexpr (sizeof(DT) == 2) {
-            upd_unpack(*reinterpret_cast<const uint4 *>(values + row + e0), w);
-        } else {
-            const float4 *ws = reinterpret_cast<const float4 *>(values + row + e0);
-            const float4 w0 = ws[0], w1 = ws[1];
-            w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
-            w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
-        }
-        if constexpr (ADAM) {
-            float4 *ma = reinterpret_cast<float4 *>(m1 + row + e0);
-            float4 *va = reinterpret_cast<float4 *>(m2 + row + e0);
-            float m[8], v[8];
-            const float4 ma0 = ma[0], ma1 = ma[1], va0 = va[0], va1 = va[1];
-            m[0] = ma0.x; m[1] = ma0.y; m[2] = ma0.z; m[3] = ma0.w;
-            m[4] = ma1.x; m[5] = ma1.y; m[6] = ma1.z; m[7] = ma1.w;
-            v[0] = va0.x; v[1] = va0.y; v[2] = va0.z; v[3] = va0.w;
-            v[4] = va1.x; v[5] = va1.y; v[6] = va1.z; v[7] = va1.w;
+    constexpr int kMaxSteps = 4;            // d_v <= 4 * 8 * 64 = 2048 in one pass
+    for (int base = 0; base < d_v; base += kMaxSteps * 8 * kWave) {
+        float w[kMaxSteps][8], g[kMaxSteps][8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                m[i] = prm.b1 * m[i] + (1.f - prm.b1) * g[i];
-                v[i] = prm.b2 * v[i] + (1.f - prm.b2) * (g[i] * g[i]);
-                const float step = (m[i] / prm.c1) / (sqrtf(v[i] / prm.c2) + prm.eps);
-                w[i] = fmaf(-prm.lr, step, w[i]);
+        for (int st = 0; st < kMaxSteps; ++st) {
+            const int e0 = base + 8 * (lane + st * kWave);
+            if (e0 >= d_v)
+                continue;
+            const float4 *gs = reinterpret_cast<const float4 *>(dvalues + row + e0);
+            const float4 g0 = gs[0], g1 = gs[1];
+            g[st][0] = g0.x; g[st][1] = g0.y; g[st][2] = g0.z; g[st][3] = g0.w;
+            g[st][4] = g1.x; g[st][5] = g1.y; g[st][6] = g1.z; g[st][7] = g1.w;
+            if constexpr (sizeof(DT) == 2) {
+                upd_unpack(*reinterpret_cast<const uint4 *>(values + row + e0), w[st]);
+            } else {
+                const float4 *ws = reinterpret_cast<const float4 *>(values + row + e0);
+                const float4 w0 = ws[0], w1 = ws[1];
+                w[st][0] = w0.x; w[st][1] = w0.y; w[st][2] = w0.z; w[st][3] = w0.w;
+                w[st][4] = w1.x; w[st][5] = w1.y; w[st][6] = w1.z; w[st][7] = w1.w;
             }
-            ma[0] = make_float4(m[0], m[1], m[2], m[3]);
-            ma[1] = make_float4(m[4], m[5], m[6], m[7]);
-            va[0] = make_float4(v[0], v[1], v[2], v[3]);
-            va[1] = make_float4(v[4], v[5], v[6], v[7]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                w[i] = fmaf(-prm.lr, g[i], w[i]);
         }
-        if constexpr (sizeof(DT) == 2) {
-            *reinterpret_cast<uint4 *>(values + row + e0) = upd_pack(w);
-        } else {
-            float4 *ws = reinterpret_cast<float4 *>(values + row + e0);
-            ws[0] = make_float4(w[0], w[1], w[2], w[3]);
-            ws[1] = make_float4(w[4], w[5], w[6], w[7]);
+#pragma unroll
+        for (int st = 0; st < kMaxSteps; ++st) {
+            const int e0 = base + 8 * (lane + st * kWave);
+            if (e0 >= d_v)
+                continue;
+            if constexpr (ADAM) {
+                float4 *ma = reinterpret_cast<float4 *>(m1 + row + e0);
+                float4 *va = reinterpret_cast<float4 *>(m2 + row + e0);
+                float m[8], v[8];
+                const float4 ma0 = ma[0], ma1 = ma[1], va0 = va[0], va1 = va[1];
+                m[0] = ma0.x; m[1] = ma0.y; m[2] = ma0.z; m[3] = ma0.w;
+                m[4] = ma1.x; m[5] = ma1.y; m[6] = ma1.z; m[7] = ma1.w;
+                v[0] = va0.x; v[1] = va0.y; v[2] = va0.z; v[3] = va0.w;
+                v[4] = va1.x; v[5] = va1.y; v[6] = va1.z; v[7] = va1.w;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    m[i] = prm.b1 * m[i] + (1.f - prm.b1) * g[st][i];
+                    v[i] = prm.b2 * v[i] + (1.f - prm.b2) * (g[st][i] * g[st][i]);
+                    const float step = (m[i] / prm.c1) / (sqrtf(v[i] / prm.c2) + prm.eps);
+                    w[st][i] = fmaf(-prm.lr, step, w[st][i]);
+                }
+                ma[0] = make_float4(m[0], m[1], m[2], m[3]);
+                ma[1] = make_float4(m[4], m[5], m[6], m[7]);
+                va[0] = make_float4(v[0], v[1], v[2], v[3]);
+                va[1] = make_float4(v[4], v[5], v[6], v[7]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    w[st][i] = fmaf(-prm.lr, g[st][i], w[st][i]);
+            }
+            if constexpr (sizeof(DT) == 2) {
+                *reinterpret_cast<uint4 *>(values + row + e0) = upd_pack(w[st]);
+            } else {
+                float4 *ws = reinterpret_cast<float4 *>(values + row + e0);
+                ws[0] = make_float4(w[st][0], w[st][1], w[st][2], w[st][3]);
+                ws[1] = make_float4(w[st][4], w[st][5], w[st][6], w[st][7]);
+            }
         }
     }
 }

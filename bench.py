@@ -198,6 +198,53 @@ def measure_extras(torch, _lib, p, values, dvalues, slot_start, w, elt, touched,
     return out
 
 
+def measure_query_net(torch, _lib, w, dq, stream, d_model: int = 1600) -> dict:
+    """The query network q = BN(x W^T) in front of the layer (not part of the
+    step, whose q is given): x [T][1600] (the pages' model width) and
+    W [H d_k][1600] in the workload's dtype, seeded normal; forward and
+    backward (dq of the step) timed with events over 5 calls after 2."""
+    dev = dq.device
+    D = w.H * w.d_k
+    gen = torch.Generator(device=dev).manual_seed(1600)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    x = torch.randn((w.T, d_model), device=dev, generator=gen).to(tdt)
+    W = (torch.randn((D, d_model), device=dev, generator=gen) * d_model ** -0.5).to(tdt)
+    qp = _lib.QueryProblem(w.T, d_model, D, 1 if w.dtype == "bf16" else 0, 0)
+    nf, nb = _lib.query_workspace_bytes(qp, False), _lib.query_workspace_bytes(qp, True)
+    ws = torch.empty(max(nf, nb), dtype=torch.uint8, device=dev)
+    q = torch.empty((w.T, D), dtype=tdt, device=dev)
+    z = torch.empty((w.T, D), dtype=torch.float32, device=dev)
+    mean = torch.empty(D, dtype=torch.float32, device=dev)
+    rstd = torch.empty_like(mean)
+    dx = torch.empty((w.T, d_model), dtype=torch.float32, device=dev)
+    dW = torch.empty((D, d_model), dtype=torch.float32, device=dev)
+    dg, db = torch.empty_like(mean), torch.empty_like(mean)
+    dq2 = dq.reshape(w.T, D)
+    sp = stream.cuda_stream
+    P = lambda t: t.data_ptr()  # noqa: E731
+    fwd = lambda: _lib.query_forward(qp, P(x), P(W), None, None, 1e-5, P(q), P(z), P(mean),  # noqa: E731
+                                     P(rstd), P(ws), nf, sp)
+    bwd = lambda: _lib.query_backward(qp, P(x), P(W), None, P(z), P(mean), P(rstd), P(dq2),  # noqa: E731
+                                      P(dx), P(dW), P(dg), P(db), P(ws), nb, sp)
+    flops = 2 * w.T * d_model * D
+    peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    out = {"d_model": d_model, "d_out": D}
+    for name, fn, fl in (("forward", fwd, flops), ("backward", bwd, 2 * flops)):
+        for _ in range(2):
+            assert fn() == 0, name
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        tf = fl / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 5), "flops": fl, "TFLOP/s": round(tf, 1),
+                     "mfma_frac": round(tf / peak, 4)}
+    return out
+
+
 def cpu_baseline(inp, k: int, count: int) -> dict:
     import oracle
     import pkm_inputs
@@ -340,6 +387,7 @@ def main():
         kernels[name] = entry
 
     extras = measure_extras(torch, _lib, p, values, dvalues, slot_start, w, elt, touched, stream)
+    query_net = measure_query_net(torch, _lib, w, dq, stream)
 
     dominant = max(STAGES, key=lambda s: per_stage[s])
     dk = kernels[dominant]
@@ -368,6 +416,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "after_backward": extras,
+        "query_network": query_net,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, k, args.cpu_tokens)

@@ -237,6 +237,59 @@ pkm_status_t pkm_sparse_adam(const pkm_problem_t *p, void *values, const float *
 pkm_status_t pkm_slot_usage(const pkm_problem_t *p, const int32_t *slot_start, int64_t *counts,
                             int64_t *used, void *stream);
 
+/*
+ * The query network in front of the layer (gptget.net summary, methodology
+ * list of "Deep Analysis": the input x passes through the query network,
+ * which gives q; "Key Results": batch normalization in the query network
+ * raises memory utilization): one bias-free projection and batch
+ * normalization of every output feature over the batch's T tokens,
+ *   z = x W^T,   q = gamma (z - mean_t z) / sqrt(var_t z + eps) + beta,
+ * with the batch's mean and biased variance (float32 sums, the variance from
+ * a one-pass Welford merge; float64 for the final merge).  q has d_out =
+ * H * d_k features and is the q of pkm_forward ([T][H][d_k] is [T][d_out]).
+ */
+typedef struct {
+    int64_t T;        /* tokens (>= 0)                                        */
+    int32_t d_model;  /* input width: a multiple of 8, in [8, 16384]          */
+    int32_t d_out;    /* output width H * d_k: a multiple of 8, in [8, 65536] */
+    int32_t dtype;    /* pkm_dtype_t of x, W and q                            */
+    int32_t reserved; /* 0                                                    */
+} pkm_query_problem_t;
+
+/* Workspace bytes of pkm_query_forward (backward = 0) or pkm_query_backward
+ * (backward = 1); (size_t)-1 for an invalid descriptor. */
+size_t pkm_query_workspace_bytes(const pkm_query_problem_t *qp, int backward);
+
+/*   x      [T][d_model]      dtype
+ *   W      [d_out][d_model]  dtype
+ *   gamma, beta [d_out]      float32, or NULL for gamma = 1, beta = 0
+ *   eps    > 0 and finite, else PKM_ERR_ARG (PyTorch's default is 1e-5)
+ *   q      [T][d_out]        dtype   OUT (nearest-even for bf16)
+ *   z      [T][d_out]        float32 OUT, x W^T (kept for the backward)
+ *   mean, rstd  [d_out]      float32 OUT, batch mean and 1/sqrt(var + eps)
+ * T must be >= 2 for the statistics to mean anything; T == 0 is a no-op. */
+pkm_status_t pkm_query_forward(const pkm_query_problem_t *qp, const void *x, const void *W,
+                               const float *gamma, const float *beta, float eps, void *q,
+                               float *z, float *mean, float *rstd, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* Backward of pkm_query_forward for dq = dL/dq (float32, e.g. pkm_backward's
+ * dq), with zhat = (z - mean) * rstd:
+ *   dbeta = sum_t dq;  dgamma = sum_t dq * zhat;
+ *   dz = gamma rstd (dq - mean_t dq - zhat mean_t(dq zhat));
+ *   dx = dz W;  dW = dz^T x.
+ *   x, W, gamma, z, mean, rstd   as given to / returned by the forward
+ *   dq      [T][d_out]      float32
+ *   dx      [T][d_model]    float32 OUT;  dW [d_out][d_model] float32 OUT
+ *   dgamma, dbeta [d_out]   float32 OUT, each may be NULL
+ * bf16 storage: dz enters the MFMA products split into two bfloat16 parts
+ * (about 16 significant bits), float32 sums. */
+pkm_status_t pkm_query_backward(const pkm_query_problem_t *qp, const void *x, const void *W,
+                                const float *gamma, const float *z, const float *mean,
+                                const float *rstd, const float *dq, float *dx, float *dW,
+                                float *dgamma, float *dbeta, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *pkm_status_string(pkm_status_t s);
 

@@ -29,7 +29,14 @@ STATUS = {
 # every symbol include/pkm.h declares
 EXPORTS = ("pkm_workspace_bytes", "pkm_forward", "pkm_backward", "pkm_forward_select",
            "pkm_forward_gather", "pkm_slot_sort", "pkm_backward_values", "pkm_backward_queries",
-           "pkm_sparse_sgd", "pkm_sparse_adam", "pkm_slot_usage", "pkm_status_string")
+           "pkm_sparse_sgd", "pkm_sparse_adam", "pkm_slot_usage", "pkm_query_workspace_bytes",
+           "pkm_query_forward", "pkm_query_backward", "pkm_status_string")
+
+
+class QueryProblem(ctypes.Structure):
+    """pkm_query_problem_t: int64 T, then int32 d_model, d_out, dtype, reserved (24 bytes)."""
+    _fields_ = [("T", ctypes.c_int64), ("d_model", ctypes.c_int32), ("d_out", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class Problem(ctypes.Structure):
@@ -74,9 +81,15 @@ def lib() -> ctypes.CDLL:
         L.pkm_sparse_sgd.argtypes = [PP, P, P, P, F, P]
         L.pkm_sparse_adam.argtypes = [PP, P, P, P, P, P, I64, F, F, F, F, P]
         L.pkm_slot_usage.argtypes = [PP, P, P, P, P]
+        QP = ctypes.POINTER(QueryProblem)
+        L.pkm_query_workspace_bytes.argtypes = [QP, ctypes.c_int]
+        L.pkm_query_workspace_bytes.restype = c_size
+        L.pkm_query_forward.argtypes = [QP, P, P, P, P, F, P, P, P, P, P, c_size, P]
+        L.pkm_query_backward.argtypes = [QP, P, P, P, P, P, P, P, P, P, P, P, P, c_size, P]
         for name in ("pkm_forward_select", "pkm_forward_gather", "pkm_slot_sort",
                      "pkm_backward_values", "pkm_backward_queries", "pkm_sparse_sgd",
-                     "pkm_sparse_adam", "pkm_slot_usage"):
+                     "pkm_sparse_adam", "pkm_slot_usage", "pkm_query_forward",
+                     "pkm_query_backward"):
             getattr(L, name).restype = ctypes.c_int
         L.pkm_status_string.argtypes = [ctypes.c_int]
         L.pkm_status_string.restype = ctypes.c_char_p
@@ -140,3 +153,19 @@ def sparse_adam(p: Problem, values, dvalues, slot_start, m, v, step, lr, beta1, 
 
 def slot_usage(p: Problem, slot_start, counts, used, stream) -> int:
     return lib().pkm_slot_usage(ctypes.byref(p), slot_start, counts, used, stream)
+
+
+def query_workspace_bytes(qp: QueryProblem, backward: bool) -> int:
+    return int(lib().pkm_query_workspace_bytes(ctypes.byref(qp), int(backward)))
+
+
+def query_forward(qp: QueryProblem, x, W, gamma, beta, eps, q, z, mean, rstd, ws, ws_bytes,
+                  stream) -> int:
+    return lib().pkm_query_forward(ctypes.byref(qp), x, W, gamma, beta, float(eps), q, z, mean,
+                                   rstd, ws, ws_bytes, stream)
+
+
+def query_backward(qp: QueryProblem, x, W, gamma, z, mean, rstd, dq, dx, dW, dgamma, dbeta, ws,
+                   ws_bytes, stream) -> int:
+    return lib().pkm_query_backward(ctypes.byref(qp), x, W, gamma, z, mean, rstd, dq, dx, dW,
+                                    dgamma, dbeta, ws, ws_bytes, stream)

@@ -3,6 +3,7 @@
 // caller's stream.  Nothing here allocates memory or keeps state.
 #include "pkm.h"
 #include "pkm_kernels.hpp"
+#include "pkm_query.hpp"
 #include "pkm_scratch.hpp"
 #include "pkm_update.hpp"
 
@@ -336,6 +337,109 @@ pkm_status_t pkm_slot_usage(const pkm_problem_t *p, const int32_t *slot_start, i
         return PKM_ERR_ALIGN;
     return pkm::launch_slot_usage(slot_start, counts, (int64_t)p->n * p->n, used,
                                   static_cast<hipStream_t>(stream)) == hipSuccess
+               ? PKM_OK
+               : PKM_ERR_HIP;
+}
+
+}  // extern "C"
+
+namespace {
+
+pkm_status_t check_query(const pkm_query_problem_t *qp)
+{
+    if (!qp)
+        return PKM_ERR_NULL;
+    if (qp->dtype != PKM_FP32 && qp->dtype != PKM_BF16)
+        return PKM_ERR_DTYPE;
+    if (qp->T < 0 || qp->d_model < 8 || qp->d_model > 16384 || qp->d_model % 8 != 0 ||
+        qp->d_out < 8 || qp->d_out > 65536 || qp->d_out % 8 != 0 || qp->reserved != 0)
+        return PKM_ERR_SHAPE;
+    // GEMM grids and int32 row counts
+    if (qp->T > INT32_MAX / 2)
+        return PKM_ERR_SHAPE;
+    return PKM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pkm_query_workspace_bytes(const pkm_query_problem_t *qp, int backward)
+{
+    if (check_query(qp) != PKM_OK)
+        return (size_t)-1;
+    return pkm::query_scratch(qp->T, qp->d_model, qp->d_out, backward != 0).total;
+}
+
+pkm_status_t pkm_query_forward(const pkm_query_problem_t *qp, const void *x, const void *W,
+                               const float *gamma, const float *beta, float eps, void *q,
+                               float *z, float *mean, float *rstd, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    pkm_status_t st = check_query(qp);
+    if (st != PKM_OK)
+        return st;
+    const int64_t T = qp->T;
+    if (missing(x, T) || !W || missing(q, T) || missing(z, T) || !mean || !rstd)
+        return PKM_ERR_NULL;
+    if (!aligned16(x) || !aligned16(W) || !aligned16(q) || !aligned16(z) || !aligned16(mean) ||
+        !aligned16(rstd) || (gamma && !aligned16(gamma)) || (beta && !aligned16(beta)))
+        return PKM_ERR_ALIGN;
+    if (!(eps > 0.f) || !std::isfinite(eps))
+        return PKM_ERR_ARG;
+    if (T == 0)
+        return PKM_OK;
+    const size_t need = pkm::query_scratch(T, qp->d_model, qp->d_out, 0).total;
+    if (!workspace)
+        return PKM_ERR_NULL;
+    if (!aligned16(workspace))
+        return PKM_ERR_ALIGN;
+    if (workspace_bytes < need)
+        return PKM_ERR_WORKSPACE;
+    return pkm::launch_query_forward(qp->dtype, x, W, gamma, beta, eps, q, z, mean, rstd, T,
+                                     qp->d_model, qp->d_out, workspace,
+                                     static_cast<hipStream_t>(stream)) == hipSuccess
+               ? PKM_OK
+               : PKM_ERR_HIP;
+}
+
+pkm_status_t pkm_query_backward(const pkm_query_problem_t *qp, const void *x, const void *W,
+                                const float *gamma, const float *z, const float *mean,
+                                const float *rstd, const float *dq, float *dx, float *dW,
+                                float *dgamma, float *dbeta, void *workspace,
+                                size_t workspace_bytes, void *stream)
+{
+    pkm_status_t st = check_query(qp);
+    if (st != PKM_OK)
+        return st;
+    const int64_t T = qp->T;
+    if (missing(x, T) || !W || missing(z, T) || !mean || !rstd || missing(dq, T) ||
+        missing(dx, T) || !dW)
+        return PKM_ERR_NULL;
+    if (!aligned16(x) || !aligned16(W) || !aligned16(z) || !aligned16(mean) || !aligned16(rstd) ||
+        !aligned16(dq) || !aligned16(dx) || !aligned16(dW) || (gamma && !aligned16(gamma)) ||
+        (dgamma && !aligned16(dgamma)) || (dbeta && !aligned16(dbeta)))
+        return PKM_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t D = qp->d_out;
+    if (T == 0) {       // no tokens: every gradient is zero
+        hipError_t e = pkm::launch_zero_f32(dW, D * qp->d_model, s);
+        if (e == hipSuccess && dgamma)
+            e = pkm::launch_zero_f32(dgamma, D, s);
+        if (e == hipSuccess && dbeta)
+            e = pkm::launch_zero_f32(dbeta, D, s);
+        return e == hipSuccess ? PKM_OK : PKM_ERR_HIP;
+    }
+    const size_t need = pkm::query_scratch(T, qp->d_model, qp->d_out, 1).total;
+    if (!workspace)
+        return PKM_ERR_NULL;
+    if (!aligned16(workspace))
+        return PKM_ERR_ALIGN;
+    if (workspace_bytes < need)
+        return PKM_ERR_WORKSPACE;
+    return pkm::launch_query_backward(qp->dtype, x, W, gamma, z, mean, rstd, dq, dx, dW, dgamma,
+                                      dbeta, T, qp->d_model, qp->d_out, workspace,
+                                      s) == hipSuccess
                ? PKM_OK
                : PKM_ERR_HIP;
 }

@@ -216,6 +216,60 @@ def pkm_slot_usage(slot_start: torch.Tensor, counts: torch.Tensor | None = None)
     return counts, used
 
 
+def _query_problem(x: torch.Tensor, W: torch.Tensor) -> "_lib.QueryProblem":
+    if x.dim() != 2 or W.dim() != 2 or x.shape[1] != W.shape[1]:
+        raise ValueError("expected x [T, d_model] and W [d_out, d_model]")
+    if x.dtype not in _DTYPES or W.dtype != x.dtype:
+        raise TypeError("x and W must share a dtype, float32 or bfloat16")
+    return _lib.QueryProblem(int(x.shape[0]), int(x.shape[1]), int(W.shape[0]), _DTYPES[x.dtype], 0)
+
+
+def pkm_query_forward(x: torch.Tensor, W: torch.Tensor, gamma=None, beta=None, eps: float = 1e-5):
+    """q = BN(x W^T) with batch statistics.  Returns (q [T, d_out] in x.dtype,
+    z [T, d_out] float32, mean, rstd [d_out] float32)."""
+    qp = _query_problem(x, W)
+    dev = x.device
+    T, D = x.shape[0], W.shape[0]
+    _check(x, "x", x.shape, x.dtype, dev)
+    _check(W, "W", W.shape, x.dtype, dev)
+    for t, name in ((gamma, "gamma"), (beta, "beta")):
+        if t is not None:
+            _check(t, name, (D,), torch.float32, dev)
+    q = torch.empty((T, D), dtype=x.dtype, device=dev)
+    z = torch.empty((T, D), dtype=torch.float32, device=dev)
+    mean = torch.empty(D, dtype=torch.float32, device=dev)
+    rstd = torch.empty(D, dtype=torch.float32, device=dev)
+    nb = _lib.query_workspace_bytes(qp, False)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    rc = _lib.query_forward(qp, _ptr(x), _ptr(W), _ptr(gamma), _ptr(beta), eps, _ptr(q), _ptr(z),
+                            _ptr(mean), _ptr(rstd), _ptr(ws), nb, _stream(dev))
+    if rc != 0:
+        raise PKMError(rc, "pkm_query_forward")
+    return q, z, mean, rstd
+
+
+def pkm_query_backward(x, W, gamma, z, mean, rstd, dq, want_affine: bool = True):
+    """Returns (dx [T, d_model], dW [d_out, d_model], dgamma, dbeta), float32
+    (dgamma, dbeta are None unless want_affine)."""
+    qp = _query_problem(x, W)
+    dev = x.device
+    T, dm, D = x.shape[0], x.shape[1], W.shape[0]
+    _check(z, "z", (T, D), torch.float32, dev)
+    _check(dq, "dq", (T, D), torch.float32, dev)
+    dx = torch.empty((T, dm), dtype=torch.float32, device=dev)
+    dW = torch.empty((D, dm), dtype=torch.float32, device=dev)
+    dgamma = torch.empty(D, dtype=torch.float32, device=dev) if want_affine else None
+    dbeta = torch.empty(D, dtype=torch.float32, device=dev) if want_affine else None
+    nb = _lib.query_workspace_bytes(qp, True)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    rc = _lib.query_backward(qp, _ptr(x), _ptr(W), _ptr(gamma), _ptr(z), _ptr(mean), _ptr(rstd),
+                             _ptr(dq), _ptr(dx), _ptr(dW), _ptr(dgamma), _ptr(dbeta), _ptr(ws), nb,
+                             _stream(dev))
+    if rc != 0:
+        raise PKMError(rc, "pkm_query_backward")
+    return dx, dW, dgamma, dbeta
+
+
 class ProductKeyMemoryFunction(torch.autograd.Function):
     """y = PKM(q, keys, values) with the library's backward."""
 

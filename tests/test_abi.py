@@ -94,3 +94,43 @@ def test_forward_workspace_checks():
     # other shapes need none, and accept a NULL workspace
     q = P(T=100, H=3, n=300, k=20, d_k=256, d_v=64, dtype=_lib.PKM_BF16)
     assert _lib.workspace_bytes(q, False) == 0
+
+
+def QP(**kw):
+    base = dict(T=64, d_model=48, d_out=32, dtype=_lib.PKM_BF16, reserved=0)
+    base.update(kw)
+    return _lib.QueryProblem(base["T"], base["d_model"], base["d_out"], base["dtype"], base["reserved"])
+
+
+def test_query_struct_layout():
+    assert ctypes.sizeof(_lib.QueryProblem) == 24
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_model=12), 2), (dict(d_out=4), 2), (dict(d_model=0), 2), (dict(T=-1), 2),
+    (dict(reserved=1), 2), (dict(dtype=7), 3),
+])
+def test_query_rejects_bad_shapes(kw, code):
+    assert _lib.query_workspace_bytes(QP(**kw), False) == (1 << 64) - 1
+    args = [FAKE] * 2 + [None, None]
+    rc = _lib.query_forward(QP(**kw), *args, 1e-5, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert rc == code, _lib.STATUS.get(rc)
+
+
+def test_query_argument_checks():
+    qp = QP()
+    need_f, need_b = _lib.query_workspace_bytes(qp, False), _lib.query_workspace_bytes(qp, True)
+    assert 0 < need_f < need_b            # the backward also keeps dz [T][d_out]
+    assert need_b >= 64 * 32 * 4
+    fwd = lambda **o: _lib.query_forward(qp, FAKE, FAKE, o.get("g"), None, o.get("eps", 1e-5),  # noqa: E731
+                                         FAKE, FAKE, FAKE, FAKE, o.get("ws", FAKE),
+                                         o.get("nb", need_f), None)
+    assert fwd(eps=0.0) == 7 and fwd(eps=float("nan")) == 7
+    assert fwd(ws=None) == 1 and fwd(nb=need_f - 1) == 4 and fwd(ws=FAKE + 4) == 6
+    assert fwd(g=FAKE + 8) == 6
+    rc = _lib.query_backward(qp, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                             FAKE, need_b - 1, None)
+    assert rc == 4
+    rc = _lib.query_backward(qp, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None,
+                             FAKE, need_b, None)
+    assert rc == 1

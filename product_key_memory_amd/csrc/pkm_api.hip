@@ -368,7 +368,8 @@ size_t pkm_query_workspace_bytes(const pkm_query_problem_t *qp, int backward)
 {
     if (check_query(qp) != PKM_OK)
         return (size_t)-1;
-    return pkm::query_scratch(qp->T, qp->d_model, qp->d_out, backward != 0).total;
+    return pkm::query_scratch(qp->T, qp->d_model, qp->d_out, backward != 0,
+                              qp->dtype == PKM_BF16 ? 2 : 4).total;
 }
 
 pkm_status_t pkm_query_forward(const pkm_query_problem_t *qp, const void *x, const void *W,
@@ -389,7 +390,8 @@ pkm_status_t pkm_query_forward(const pkm_query_problem_t *qp, const void *x, con
         return PKM_ERR_ARG;
     if (T == 0)
         return PKM_OK;
-    const size_t need = pkm::query_scratch(T, qp->d_model, qp->d_out, 0).total;
+    const size_t need = pkm::query_scratch(T, qp->d_model, qp->d_out, 0,
+                                           qp->dtype == PKM_BF16 ? 2 : 4).total;
     if (!workspace)
         return PKM_ERR_NULL;
     if (!aligned16(workspace))
@@ -430,7 +432,8 @@ pkm_status_t pkm_query_backward(const pkm_query_problem_t *qp, const void *x, co
             e = pkm::launch_zero_f32(dbeta, D, s);
         return e == hipSuccess ? PKM_OK : PKM_ERR_HIP;
     }
-    const size_t need = pkm::query_scratch(T, qp->d_model, qp->d_out, 1).total;
+    const size_t need = pkm::query_scratch(T, qp->d_model, qp->d_out, 1,
+                                           qp->dtype == PKM_BF16 ? 2 : 4).total;
     if (!workspace)
         return PKM_ERR_NULL;
     if (!aligned16(workspace))

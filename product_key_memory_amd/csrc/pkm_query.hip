@@ -24,6 +24,8 @@
 #include "pkm_device.hpp"
 #include "pkm_query.hpp"
 
+#include <type_traits>
+
 namespace pkm {
 
 // ---------------------------------------------------------------------------
@@ -48,52 +50,41 @@ __device__ __forceinline__ int g_cell(int row, int k)
     return row * kGBK + (((k / EPC) ^ ((row / (16 / C)) % C)) * EPC) + k % EPC;
 }
 
-// Eight (bf16) or four (float32) consecutive elements as floats.
-template <typename T> struct GVec;
-template <> struct GVec<bf16_t> {
-    static constexpr int n = 8;
-    __device__ static void load(float (&x)[8], const bf16_t *p)
-    {
-        unpack16(*reinterpret_cast<const uint4 *>(p), x);
-    }
-};
-template <> struct GVec<float> {
-    static constexpr int n = 4;
-    __device__ static void load(float (&x)[4], const float *p)
-    {
-        const float4 v = *reinterpret_cast<const float4 *>(p);
-        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-    }
-};
-
 // One operand's staging: T elements, stored K-contiguous (KMAJ = false: [R][K])
-// or R-contiguous (KMAJ = true: [K][R]); R = the operand's M or N.
+// or R-contiguous (KMAJ = true: [K][R]); R = the operand's M or N.  Each
+// thread moves 16-byte pieces (8 bf16 or 4 float32); K-contiguous pieces go
+// to LDS whole (one 16- or 8-byte store), R-contiguous ones are transposed
+// element by element.
+template <typename T> struct GRaw;
+template <> struct GRaw<bf16_t> { static constexpr int V = 8; };
+template <> struct GRaw<float> { static constexpr int V = 4; };
+
 template <typename T, bool KMAJ, int MODE, bool SPLIT>
 struct GStage {
-    static constexpr int V = GVec<T>::n;                    // elements per 16-byte load
+    static constexpr int V = GRaw<T>::V;                    // elements per 16-byte load
     static constexpr int loads = kGBM * kGBK / V / kGThreads;
-    float x[loads][V];
+    uint4 raw[loads];
+    __device__ static void coords(int u, int &r, int &k)
+    {
+        if (!KMAJ) {        // V consecutive k of one row
+            r = u / (kGBK / V);
+            k = (u % (kGBK / V)) * V;
+        } else {            // V consecutive rows of one k
+            k = u / (kGBM / V);
+            r = (u % (kGBM / V)) * V;
+        }
+    }
     __device__ void load(const T *__restrict__ src, int64_t ld, int r0, int R, int k0, int K, int tid)
     {
 #pragma unroll
         for (int l = 0; l < loads; ++l) {
-            const int u = tid + l * kGThreads;
             int r, k;
-            if (!KMAJ) {        // V consecutive k of one row
-                r = u / (kGBK / V);
-                k = (u % (kGBK / V)) * V;
-            } else {            // V consecutive rows of one k
-                k = u / (kGBM / V);
-                r = (u % (kGBM / V)) * V;
-            }
+            coords(tid + l * kGThreads, r, k);
             const int gr = r0 + r, gk = k0 + k;
-            const bool ok = gr < R && gk < K;
-            if (ok)
-                GVec<T>::load(x[l], !KMAJ ? src + (int64_t)gr * ld + gk : src + (int64_t)gk * ld + gr);
-            else
-#pragma unroll
-                for (int e = 0; e < V; ++e)
-                    x[l][e] = 0.f;
+            raw[l] = (gr < R && gk < K)
+                         ? *reinterpret_cast<const uint4 *>(!KMAJ ? src + (int64_t)gr * ld + gk
+                                                                  : src + (int64_t)gk * ld + gr)
+                         : make_uint4(0u, 0u, 0u, 0u);
         }
     }
     __device__ void store(typename GTile<MODE>::E *hi, typename GTile<MODE>::E *lo, int tid) const
@@ -101,36 +92,56 @@ struct GStage {
         constexpr int C = GTile<MODE>::C;
 #pragma unroll
         for (int l = 0; l < loads; ++l) {
-            const int u = tid + l * kGThreads;
+            int r, k;
+            coords(tid + l * kGThreads, r, k);
+            if constexpr (!KMAJ && (MODE == kF32 || (sizeof(T) == 2 && !SPLIT))) {
+                // a whole chunk (8 bf16 / 4 float32) in place
+                *reinterpret_cast<uint4 *>(hi + g_cell<C>(r, k)) = raw[l];
+            } else if constexpr (!KMAJ && SPLIT) {
+                // 4 float32 -> 4 bf16 hi + 4 bf16 lo, half a chunk each
+                const uint32_t w[4] = {raw[l].x, raw[l].y, raw[l].z, raw[l].w};
+                uint32_t h[4], o[4];
 #pragma unroll
-            for (int e = 0; e < V; ++e) {
-                int r, k;
-                if (!KMAJ) {
-                    r = u / (kGBK / V);
-                    k = (u % (kGBK / V)) * V + e;
-                } else {
-                    k = u / (kGBM / V);
-                    r = (u % (kGBM / V)) * V + e;
+                for (int e = 0; e < 4; ++e) {
+                    const float f = __uint_as_float(w[e]);
+                    h[e] = f32_to_bf16_bits(f);
+                    o[e] = f32_to_bf16_bits(f - bf16_to_f32(h[e]));
                 }
-                const int at = g_cell<C>(r, k);
-                if constexpr (MODE == kF32) {
-                    hi[at] = x[l][e];
-                } else {
-                    const uint32_t h = f32_to_bf16_bits(x[l][e]);
-                    hi[at] = (uint16_t)h;
-                    if constexpr (SPLIT)
-                        lo[at] = (uint16_t)f32_to_bf16_bits(x[l][e] - bf16_to_f32(h));
+                *reinterpret_cast<uint2 *>(hi + g_cell<C>(r, k)) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                *reinterpret_cast<uint2 *>(lo + g_cell<C>(r, k)) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+            } else {
+                float x[V];
+                if constexpr (V == 8)
+                    unpack16(raw[l], x);
+                else {
+                    x[0] = __uint_as_float(raw[l].x); x[1] = __uint_as_float(raw[l].y);
+                    x[2] = __uint_as_float(raw[l].z); x[3] = __uint_as_float(raw[l].w);
+                }
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const int at = g_cell<C>(KMAJ ? r + e : r, KMAJ ? k : k + e);
+                    if constexpr (MODE == kF32) {
+                        hi[at] = x[e];
+                    } else {
+                        const uint32_t hb = f32_to_bf16_bits(x[e]);
+                        hi[at] = (uint16_t)hb;
+                        if constexpr (SPLIT)
+                            lo[at] = (uint16_t)f32_to_bf16_bits(x[e] - bf16_to_f32(hb));
+                    }
                 }
             }
         }
     }
 };
 
+// blockIdx.z = a slice of K (split-K): slice z covers [z k_slice, (z+1) k_slice)
+// and writes its own C at Cm + z M N.
 template <typename TA, typename TB, bool A_KM, bool B_KN, int MODE>
 __global__ __launch_bounds__(kGThreads) void gemm_kernel(const TA *__restrict__ A,
                                                          const TB *__restrict__ B,
                                                          float *__restrict__ Cm, int M, int N,
-                                                         int K, int64_t lda, int64_t ldb)
+                                                         int K, int64_t lda, int64_t ldb,
+                                                         int k_slice)
 {
     typedef typename GTile<MODE>::E E;
     constexpr int C = GTile<MODE>::C;
@@ -151,16 +162,19 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(const TA *__restrict__ 
         for (int j = 0; j < 4; ++j)
             acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = (K + kGBK - 1) / kGBK;
-    sa.load(A, lda, m0, M, 0, K, tid);
-    sb.load(B, ldb, n0, N, 0, K, tid);
+    const int kb = blockIdx.z * k_slice;
+    const int ke = kb + k_slice < K ? kb + k_slice : K;
+    Cm += (int64_t)blockIdx.z * M * N;
+    const int nk = (ke - kb + kGBK - 1) / kGBK;
+    sa.load(A, lda, m0, M, kb, ke, tid);
+    sb.load(B, ldb, n0, N, kb, ke, tid);
     sa.store(lds[0], lds[0] + TILE, tid);
     sb.store(lds[0] + PA * TILE, nullptr, tid);
     __syncthreads();
     for (int c = 0; c < nk; ++c) {
         if (c + 1 < nk) {
-            sa.load(A, lda, m0, M, (c + 1) * kGBK, K, tid);
-            sb.load(B, ldb, n0, N, (c + 1) * kGBK, K, tid);
+            sa.load(A, lda, m0, M, kb + (c + 1) * kGBK, ke, tid);
+            sb.load(B, ldb, n0, N, kb + (c + 1) * kGBK, ke, tid);
         }
         const E *ah = lds[c & 1], *al = lds[c & 1] + TILE, *bt = lds[c & 1] + PA * TILE;
         if constexpr (MODE == kF32) {
@@ -232,13 +246,72 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(const TA *__restrict__ 
         }
 }
 
+// C = A B^T with both operands K-contiguous unless A_KM / B_KN.  With
+// splits > 1 the K range is cut into `splits` slices whose partial products
+// go to `parts` ([splits][M][N]) and are then summed into C.
+__global__ void sum_slices_kernel(const float *__restrict__ parts, int splits, int64_t count,
+                                  float *__restrict__ C)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+        float a = 0.f;
+        for (int z = 0; z < splits; ++z)
+            a += parts[(int64_t)z * count + i];
+        C[i] = a;
+    }
+}
+
 template <typename TA, typename TB, bool A_KM, bool B_KN, int MODE>
 static hipError_t gemm(const TA *A, const TB *B, float *Cm, int M, int N, int K, int64_t lda,
-                       int64_t ldb, hipStream_t stream)
+                       int64_t ldb, hipStream_t stream, int splits = 1, float *parts = nullptr)
 {
-    const dim3 grid((unsigned)((N + kGBN - 1) / kGBN), (unsigned)((M + kGBM - 1) / kGBM));
+    int k_slice = K;
+    if (splits > 1) {
+        k_slice = (K + splits - 1) / splits;
+        k_slice = (k_slice + kGBK - 1) / kGBK * kGBK;
+        splits = (K + k_slice - 1) / k_slice;
+    }
+    const dim3 grid((unsigned)((N + kGBN - 1) / kGBN), (unsigned)((M + kGBM - 1) / kGBM),
+                    (unsigned)splits);
     hipLaunchKernelGGL((gemm_kernel<TA, TB, A_KM, B_KN, MODE>), grid, dim3(kGThreads), 0, stream,
-                       A, B, Cm, M, N, K, lda, ldb);
+                       A, B, splits > 1 ? parts : Cm, M, N, K, lda, ldb, k_slice);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || splits <= 1)
+        return err;
+    const int64_t count = (int64_t)M * N;
+    const int64_t blocks = (count + 255) / 256;
+    hipLaunchKernelGGL(sum_slices_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256),
+                       0, stream, parts, splits, count, Cm);
+    return hipGetLastError();
+}
+
+// out[c][r] = in[r][c] for an R x C matrix of 2- or 4-byte elements, through
+// 64 x 64 LDS tiles (both sides coalesced).
+template <typename E>
+__global__ __launch_bounds__(256) void transpose_kernel(const E *__restrict__ in, E *__restrict__ out,
+                                                        int64_t R, int64_t C)
+{
+    __shared__ E tile[64][65];
+    const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+    const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
+    for (int i = ty; i < 64; i += 4) {
+        const int64_t r = r0 + i, c = c0 + tx;
+        if (r < R && c < C)
+            tile[i][tx] = in[r * C + c];
+    }
+    __syncthreads();
+    for (int i = ty; i < 64; i += 4) {
+        const int64_t c = c0 + i, r = r0 + tx;
+        if (r < R && c < C)
+            out[c * R + r] = tile[tx][i];
+    }
+}
+
+template <typename E>
+static hipError_t transpose(const E *in, E *out, int64_t R, int64_t C, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
+    hipLaunchKernelGGL((transpose_kernel<E>), grid, dim3(256), 0, stream, in, out, R, C);
     return hipGetLastError();
 }
 
@@ -418,9 +491,8 @@ __global__ void bn_bwd_apply_kernel(const float *__restrict__ z, const float *__
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-QueryScratch query_scratch(int64_t T, int d_model, int D, int backward)
+QueryScratch query_scratch(int64_t T, int d_model, int D, int backward, int elt)
 {
-    (void)d_model;
     QueryScratch S;
     int64_t chunks = (T + 255) / 256;           // rows per chunk >= 256
     if (chunks > 256)
@@ -433,8 +505,25 @@ QueryScratch query_scratch(int64_t T, int d_model, int D, int backward)
     S.off_part = 0;
     S.off_coef = a256((size_t)chunks * D * 3 * 4);
     S.off_dz = a256(S.off_coef + (size_t)D * 2 * 4);
-    S.total = backward ? a256(S.off_dz + (size_t)T * D * 4) : S.off_coef;
+    S.off_dzt = a256(S.off_dz + (size_t)T * D * 4);
+    S.off_wt = a256(S.off_dzt + (size_t)T * D * 4);
+    S.off_xt = a256(S.off_wt + (size_t)D * d_model * elt);
+    S.off_dwp = a256(S.off_xt + (size_t)T * d_model * elt);
+    S.dw_splits = dw_splits(T, d_model, D);
+    S.total = backward ? a256(S.off_dwp + (size_t)S.dw_splits * D * d_model * 4) : S.off_coef;
     return S;
+}
+
+// dW = dz^T x has only (D / 128) (d_model / 128) output tiles and a long K
+// (the tokens): cut K so that about 1024 workgroups run.
+int dw_splits(int64_t T, int d_model, int D)
+{
+    const int64_t tiles = (int64_t)((D + kGBM - 1) / kGBM) * ((d_model + kGBN - 1) / kGBN);
+    int64_t s = (1024 + tiles - 1) / tiles;
+    const int64_t max_s = (T + 8 * kGBK - 1) / (8 * kGBK);     // >= 8 K steps a slice
+    if (s > max_s)
+        s = max_s;
+    return (int)(s < 1 ? 1 : s);
 }
 
 static unsigned elem_grid(int64_t n)
@@ -448,7 +537,7 @@ static hipError_t query_forward_t(const DT *x, const DT *W, const float *gamma, 
                                   float eps, DT *q, float *z, float *mean, float *rstd, int64_t T,
                                   int d_model, int D, void *ws, hipStream_t stream)
 {
-    const QueryScratch S = query_scratch(T, d_model, D, 0);
+    const QueryScratch S = query_scratch(T, d_model, D, 0, (int)sizeof(DT));
     float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + S.off_part);
     constexpr int MODE = sizeof(DT) == 2 ? kBf16 : kF32;
     hipError_t err = gemm<DT, DT, false, false, MODE>(x, W, z, (int)T, D, d_model, d_model,
@@ -470,11 +559,16 @@ static hipError_t query_backward_t(const DT *x, const DT *W, const float *gamma,
                                    float *dx, float *dW, float *dgamma, float *dbeta, int64_t T,
                                    int d_model, int D, void *ws, hipStream_t stream)
 {
-    const QueryScratch S = query_scratch(T, d_model, D, 1);
+    const QueryScratch S = query_scratch(T, d_model, D, 1, (int)sizeof(DT));
     char *base = static_cast<char *>(ws);
     float *part = reinterpret_cast<float *>(base + S.off_part);
     float *coef = reinterpret_cast<float *>(base + S.off_coef);
     float *dz = reinterpret_cast<float *>(base + S.off_dz);
+    float *dzt = reinterpret_cast<float *>(base + S.off_dzt);
+    DT *Wt = reinterpret_cast<DT *>(base + S.off_wt);
+    DT *xt = reinterpret_cast<DT *>(base + S.off_xt);
+    float *dwp = reinterpret_cast<float *>(base + S.off_dwp);
+    typedef typename std::conditional<sizeof(DT) == 2, uint16_t, float>::type E;
     hipLaunchKernelGGL(bn_bwd_partial_kernel, dim3((unsigned)((D + kBnCols - 1) / kBnCols), (unsigned)S.chunks),
                        dim3(kBnWaves * kWave), 0, stream, z, dq, T, D, mean, rstd,
                        S.rows_per_chunk, part);
@@ -483,15 +577,23 @@ static hipError_t query_backward_t(const DT *x, const DT *W, const float *gamma,
     hipLaunchKernelGGL(bn_bwd_apply_kernel, dim3(elem_grid(T * D)), dim3(256), 0, stream, z, dq, T,
                        D, mean, rstd, gamma, coef, dz);
     hipError_t err = hipGetLastError();
+    // every GEMM operand K-contiguous: W^T [d_model][D], x^T [d_model][T], dz^T [D][T]
+    if (err == hipSuccess)
+        err = transpose<E>(reinterpret_cast<const E *>(W), reinterpret_cast<E *>(Wt), D, d_model, stream);
+    if (err == hipSuccess)
+        err = transpose<E>(reinterpret_cast<const E *>(x), reinterpret_cast<E *>(xt), T, d_model, stream);
+    if (err == hipSuccess)
+        err = transpose<float>(dz, dzt, T, D, stream);
     if (err != hipSuccess)
         return err;
     constexpr int MODE = sizeof(DT) == 2 ? kBf16SplitA : kF32;
-    // dx [T][d_model] = dz [T][D] . W [D][d_model]   (B stored K-major)
-    err = gemm<float, DT, false, true, MODE>(dz, W, dx, (int)T, d_model, D, D, d_model, stream);
+    // dx [T][d_model] = dz [T][D] . (W^T)^T
+    err = gemm<float, DT, false, false, MODE>(dz, Wt, dx, (int)T, d_model, D, D, D, stream);
     if (err != hipSuccess)
         return err;
-    // dW [D][d_model] = dz^T . x                     (A and B stored K-major)
-    return gemm<float, DT, true, true, MODE>(dz, x, dW, D, d_model, (int)T, D, d_model, stream);
+    // dW [D][d_model] = dz^T [D][T] . (x^T)^T, K = T cut into slices
+    return gemm<float, DT, false, false, MODE>(dzt, xt, dW, D, d_model, (int)T, T, T, stream,
+                                               S.dw_splits, dwp);
 }
 
 hipError_t launch_query_forward(int dtype, const void *x, const void *W, const float *gamma,

@@ -10,13 +10,17 @@
 namespace pkm {
 
 // Workspace: per-(row chunk, column) batch-norm partials, then (backward)
-// two per-column coefficients and dz [T][D] float32.
+// two per-column coefficients, dz [T][D] and dz^T [D][T] float32, W^T
+// [d_model][D] and x^T [d_model][T] (storage type), and the split-K partial
+// sums of dW [dw_splits][D][d_model].
 struct QueryScratch {
     int chunks;
     int64_t rows_per_chunk;
-    size_t off_part, off_coef, off_dz, total;
+    int dw_splits;
+    size_t off_part, off_coef, off_dz, off_dzt, off_wt, off_xt, off_dwp, total;
 };
-QueryScratch query_scratch(int64_t T, int d_model, int D, int backward);
+QueryScratch query_scratch(int64_t T, int d_model, int D, int backward, int elt);
+int dw_splits(int64_t T, int d_model, int D);
 
 // z = x W^T [T][D] (float32), mean/rstd per column, q = gamma (z - mean) rstd + beta.
 hipError_t launch_query_forward(int dtype, const void *x, const void *W, const float *gamma,

@@ -75,7 +75,7 @@ typedef struct {
  * or pkm_backward and its stages (backward = 1) need for this problem; 0 if
  * none (the workspace may then be NULL).  Returns (size_t)-1 for an invalid
  * descriptor.  The forward needs workspace only on its two-kernel selection
- * path (bf16, d_k = 512, 256 < n <= 512, k <= 32): T*H*2*k*8 bytes rounded up
+ * path (bf16, d_k = 512, 256 < n <= 1024, k <= 32): T*H*2*k*8 bytes rounded up
  * to 256, for the per-half top-k lists. */
 size_t pkm_workspace_bytes(const pkm_problem_t *p, int backward);
 

@@ -1,15 +1,17 @@
 // pkm_select_fast.hip -- forward selection for bf16 storage, query halves of
-// 256, 256 < n <= 512, k <= 32, as two kernels (gptget.net summary of "Large
+// 256, 256 < n <= 1024, k <= 32, as two kernels (gptget.net summary of "Large
 // Memory Layers with Product Keys", "Methodology": split q into q1, q2, search
 // each against its own sub-key set, combine the best sub-keys; companion page
 // "Why top-k of each half is enough").
 //
-// 1. fwd_topk_half_kernel: one wave per (16 tokens, head, half).  The wave
-//    computes its tokens' n scores straight into registers with
-//    v_mfma_f32_16x16x32_bf16 (sub-keys as M, tokens as N): lane l holds, for
-//    token l % 16, the scores of sub-keys 16 j + 4 (l / 16) + i (tile j < 32,
-//    i < 4).  All selection work then runs on the 4 lanes that share a token,
-//    so every instruction serves the wave's 16 tokens at once:
+// 1. fwd_topk_half_kernel: one wave per (16 tokens, head, half).  The
+//    codebook is scored in blocks of 512 sub-keys (one block for n <= 512,
+//    two for n <= 1024).  The wave computes its tokens' scores of a block
+//    straight into registers with v_mfma_f32_16x16x32_bf16 (sub-keys as M,
+//    tokens as N): lane l holds, for token l % 16, the scores of sub-keys
+//    16 j + 4 (l / 16) + i of the block (tile j < 32, i < 4).  All selection
+//    work then runs on the 4 lanes that share a token, so every instruction
+//    serves the wave's 16 tokens at once:
 //      - tau = k-th largest of the token's 64 group maxima (groups of 8
 //        scores), by a bitonic sort inside the 4-lane group: the k groups
 //        above it each hold a score >= tau, so at least k scores survive;
@@ -18,6 +20,10 @@
 //        token has more than 64 survivors (heavy ties) its exact k-th largest
 //        key is found by bisection on the score bits, then on the index among
 //        exact ties, and exactly k survive;
+//      - a second block's survivors must also reach the first block's k-th
+//        key; its sorted list and the first block's (kept in LDS) are merged
+//        (the top k of two sorted lists A, B are the larger of A[e] and
+//        B[k - 1 - e], a bitonic sequence, which a bitonic merge orders);
 //      - the top k (score, sub-key) of the half go to the workspace.
 // 2. fwd_merge_kernel: one wave per 16 (token, head) rows, 4 lanes per row.
 //    A pair of ranks (a, b) can only make the final top-k if
@@ -28,6 +34,8 @@
 //    over them gives the weights.
 // Splitting the two phases keeps each kernel's registers low enough for two
 // or more waves per SIMD, which hides the latency a single wave exposes.
+#include <type_traits>
+
 #include "pkm_device.hpp"
 #include "pkm_kernels.hpp"
 
@@ -36,16 +44,18 @@ namespace pkm {
 constexpr int kFastWaves = 4;
 constexpr int kFastTok = 16;                         // tokens per wave
 constexpr int kFastTokWG = kFastWaves * kFastTok;    // tokens per workgroup
-constexpr int kFastTiles = 32;                       // 16-sub-key tiles: n <= 512
+constexpr int kFastTiles = 32;                       // 16-sub-key tiles per block
+constexpr int kFastBlock = 16 * kFastTiles;          // 512 sub-keys per block
 constexpr int kFastKSteps = 8;                       // 32-wide K steps: half = 256
 constexpr int kFastSurv = 64;                        // survivor slots per token
 constexpr int kMergeWaves = 4;
 constexpr int kMergeRows = 16;                       // (token, head) rows per wave
 constexpr int kMaxPairs = 128;                       // merge_candidates(32) = 119
 
-// Scores of the wave's 16 tokens against sub-keys 0..n-1 of one codebook, as
-// order-preserving integers: so[j][i] = ord(score of sub-key 16 j + 4 g + i)
-// for token `tok` (ord(-inf) past n).  The workgroup's 4 waves (64 tokens)
+// Scores of the wave's 16 tokens against the sub-keys 0..n_loc-1 of one block
+// (kb = its first row), as order-preserving integers: so[j][i] = ord(score of
+// sub-key 16 j + 4 g + i) for token `tok` (rows past n_loc score 0; the caller
+// masks them).  The workgroup's 4 waves (64 tokens)
 // share the codebook through LDS: per step p it holds rows 32 p .. 32 p + 31
 // (16 KB, double-buffered), each thread loading 4 of its 16-byte chunks, so
 // the L2 serves each codebook once per 64 tokens instead of once per 16.
@@ -54,17 +64,16 @@ constexpr int kMaxPairs = 128;                       // merge_candidates(32) = 1
 // in distinct banks.  Within a step the two tiles' accumulation chains
 // alternate, so consecutive MFMAs do not wait on each other.
 __device__ __forceinline__ void fast_scores(uint32_t (&so)[kFastTiles][4], const uint16_t *kb,
-                                            const uint4 (&qf)[kFastKSteps], int n, int r16, int g,
-                                            uint4 *kbuf, int tid)
+                                            const uint4 (&qf)[kFastKSteps], int n_loc, int r16,
+                                            int g, uint4 *kbuf, int tid)
 {
     constexpr int half = kFastKSteps * 32;
     constexpr int chunks = half * 2 / 16;            // 32 chunks of 16 bytes per row
     constexpr int step_units = 32 * chunks;          // 1024 chunks per 32-row step
     constexpr int per_thread = step_units / (kFastWaves * kWave);
     constexpr int steps = kFastTiles / 2;
-    // rows past n read as zeros
-    const __amdgpu_buffer_rsrc_t rsrc = buffer_over(kb, n * half * 2);
-    const int lim = n - 4 * g;        // sub-key 16 j + 4 g + i exists iff 16 j + i < lim
+    // rows past n_loc read as zeros
+    const __amdgpu_buffer_rsrc_t rsrc = buffer_over(kb, n_loc * half * 2);
     uint4 pre[per_thread];
     auto gload = [&](int p) {
 #pragma unroll
@@ -98,14 +107,11 @@ __device__ __forceinline__ void fast_scores(uint32_t (&so)[kFastTiles][4], const
                     0, 0, 0);
             }
         }
-        // n > 256 on this path: only the upper 16 tiles can hold sub-keys >= n
 #pragma unroll
-        for (int w = 0; w < 2; ++w) {
-            const int j = 2 * p + w;
+        for (int w = 0; w < 2; ++w)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                so[j][i] = ord_f32((j < kFastTiles / 2 || 16 * j + i < lim) ? acc[w][i] : -INFINITY);
-        }
+                so[2 * p + w][i] = ord_f32(acc[w][i]);
         // step p + 1 goes to the other buffer (its readers finished at the
         // last barrier); step p + 2 is fetched while step p + 1 is worked on
         if (p + 1 < steps)
@@ -117,7 +123,10 @@ __device__ __forceinline__ void fast_scores(uint32_t (&so)[kFastTiles][4], const
 }
 
 // lists[((t H + h) 2 + s) k + e] = (ord score, sub-key) of the e-th best
-// sub-key of half s, e < k.
+// sub-key of half s, e < k.  BLOCKS = number of 512-sub-key blocks (1: n <= 512,
+// 2: n <= 1024), a template argument so that each case gets its own register
+// allocation.
+template <int BLOCKS>
 __global__ __launch_bounds__(kFastWaves *kWave) void fwd_topk_half_kernel(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ keys, int64_t T, int H, int n,
     int k, uint2 *__restrict__ lists)
@@ -125,6 +134,9 @@ __global__ __launch_bounds__(kFastWaves *kWave) void fwd_topk_half_kernel(
     // the codebook steps during the scoring, the survivors afterwards
     __shared__ uint4 lds[2 * 32 * 32];
     static_assert(sizeof(lds) >= 2 * kFastWaves * kFastTok * kFastSurv * 4, "survivor space");
+    // the first block's top k per token while the second block is scored
+    // (row stride 33 keys: the 16 tokens' rows start in distinct banks)
+    __shared__ uint64_t s_prev[kFastWaves][kFastTok][33];
     uint32_t(*surv_s_all)[kFastTok * kFastSurv] =
         reinterpret_cast<uint32_t(*)[kFastTok * kFastSurv]>(lds);
     uint32_t(*surv_i_all)[kFastTok * kFastSurv] = surv_s_all + kFastWaves;
@@ -139,154 +151,243 @@ __global__ __launch_bounds__(kFastWaves *kWave) void fwd_topk_half_kernel(
     const bool live = t < T;
     uint32_t *surv_s = surv_s_all[wave] + tok * kFastSurv;
     uint32_t *surv_i = surv_i_all[wave] + tok * kFastSurv;
+    uint64_t *prev = s_prev[wave][tok];
 
-    // an opaque copy of the lane group, so values derived from it (the 128
-    // sub-key indices) are formed where used instead of being held in registers
-    int g = g_lane;
-    asm volatile("" : "+v"(g));
-    // B fragments: token `tok`, K slice 32 kk + 8 g .. + 7
-    uint4 qf[kFastKSteps];
     const uint16_t *qrow = reinterpret_cast<const uint16_t *>(q) +
                            ((live ? t : 0) * H + h) * (int64_t)d_k + (int64_t)s * half;
-#pragma unroll
-    for (int kk = 0; kk < kFastKSteps; ++kk)
-        qf[kk] = *reinterpret_cast<const uint4 *>(qrow + 32 * kk + 8 * g);
+    const int tid0 = threadIdx.x;
     const uint16_t *kb = reinterpret_cast<const uint16_t *>(keys) + ((int64_t)h * 2 + s) * (int64_t)n * half;
-    uint32_t so[kFastTiles][4];
-    fast_scores(so, kb, qf, n, tok, g, lds, threadIdx.x);
 
-    // tau: k-th largest of the token's 64 group maxima (groups of 8 scores)
-    uint32_t gm[16];
+    // one block of sub-keys; straight-line code for each block (a loop over
+    // the blocks kept values alive across its back edge and cost a wave per
+    // SIMD)
+    auto block = [&](auto first_c, auto last_c) {
+        constexpr bool kFirst = decltype(first_c)::value, kLast = decltype(last_c)::value;
+        // opaque copies of the lane group and the thread id, so values derived
+        // from them (the 128 sub-key indices, the LDS and codebook offsets) are
+        // formed where used instead of being held in registers, also from one
+        // block to the next
+        int g = g_lane, tid = tid0;
+        asm volatile("" : "+v"(g), "+v"(tid));
+        const int base = kFirst ? 0 : kFastBlock;
+        const int n_loc = n - base < kFastBlock ? n - base : kFastBlock;
+        // B fragments: token `tok`, K slice 32 kk + 8 g .. + 7 (loaded per
+        // block, so they are not held through the selection)
+        uint4 qf[kFastKSteps];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        uint32_t v = so[2 * m][0];
-#pragma unroll
-        for (int i = 1; i < 4; ++i)
-            v = max(v, so[2 * m][i]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            v = max(v, so[2 * m + 1][i]);
-        gm[m] = v;
-    }
-    group4_sort_desc<16>(gm);
-    uint32_t tau_src = gm[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r)
-        if (r == ((k - 1) & 15))
-            tau_src = gm[r];
-    const uint32_t tau = (uint32_t)__shfl((int)tau_src, tok + 16 * ((k - 1) >> 4));
-
-    // survivors: ord >= tau (tau is a real score: n > 256 gives >= 33 groups
-    // of valid scores, so the sub-keys past n never survive)
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < kFastTiles; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            cnt += so[j][i] >= tau ? 1 : 0;
-    int total = group4_sum(cnt);
-    bool fits = total <= kFastSurv;
-
-    // heavy ties: the exact k-th largest key instead of tau, by bisection on
-    // the score bits and then on the index among exactly tied scores
-    uint32_t kth = tau, tie_idx = 0xFFFFFFFFu;
-    if (__ballot(!fits && live) != 0) {
-        uint32_t K = 0;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cand = K | (1u << bit);
-            int c = 0;
+        for (int kk = 0; kk < kFastKSteps; ++kk)
+            qf[kk] = *reinterpret_cast<const uint4 *>(qrow + 32 * kk + 8 * g);
+        uint32_t so[kFastTiles][4];
+        fast_scores(so, kb + (int64_t)base * half, qf, n_loc, tok, g, lds, tid);
+        if (n_loc < kFastBlock) {
+            // sub-key 16 j + 4 g + i of the block exists iff 16 j + i < lim
+            const int lim = n_loc - 4 * g;
+            const uint32_t neg = ord_f32(-INFINITY);
 #pragma unroll
             for (int j = 0; j < kFastTiles; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    c += so[j][i] >= cand ? 1 : 0;
-            if (group4_sum(c) >= k)
-                K = cand;
+                    so[j][i] = 16 * j + i < lim ? so[j][i] : neg;
         }
-        int above = 0;
+
+        // tau: k-th largest of the token's 64 group maxima (groups of 8 scores)
+        uint32_t gm[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            uint32_t x = so[2 * m][0];
+#pragma unroll
+            for (int i = 1; i < 4; ++i)
+                x = max(x, so[2 * m][i]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                x = max(x, so[2 * m + 1][i]);
+            gm[m] = x;
+        }
+        group4_sort_desc<16>(gm);
+        uint32_t tau_src = gm[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r)
+            if (r == ((k - 1) & 15))
+                tau_src = gm[r];
+        uint32_t tau = (uint32_t)__shfl((int)tau_src, tok + 16 * ((k - 1) >> 4));
+        // A single block has n > 256 valid sub-keys, >= 33 groups of real
+        // scores, so tau is a real score and the sub-keys past n never
+        // survive.  A second block may hold fewer than k sub-keys: there the
+        // first block's k-th key (a real score) raises the bar, and keys
+        // below it cannot reach the top k anyway.
+        if constexpr (!kFirst)
+            tau = max(tau, (uint32_t)(prev[k - 1] >> 32));
+
+        // survivors: ord >= tau
+        int cnt = 0;
 #pragma unroll
         for (int j = 0; j < kFastTiles; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                above += so[j][i] > K ? 1 : 0;
-        const int need = k - group4_sum(above);     // tied picks to take, lowest index first
-        uint32_t I = 0;                              // largest bound with < need tied indices below it
-        for (int bit = 9; bit >= 0; --bit) {
-            const uint32_t cand = I | (1u << bit);
-            // sub-key 16 j + 4 g + i < cand  <=>  16 j + i < cand - 4 g
-            const int lim_c = (int)cand - 4 * g;
-            int c = 0;
+                cnt += so[j][i] >= tau ? 1 : 0;
+        int total = group4_sum(cnt);
+        bool fits = total <= kFastSurv;
+
+        // heavy ties: the exact k-th largest key of the block instead of tau,
+        // by bisection on the score bits and then on the index among exactly
+        // tied scores (more than 64 survivors are real scores, so is the
+        // k-th largest)
+        uint32_t kth = tau, tie_idx = 0xFFFFFFFFu;
+        if (__ballot(!fits && live) != 0) {
+            uint32_t K = 0;
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t cand = K | (1u << bit);
+                int c = 0;
+#pragma unroll
+                for (int j = 0; j < kFastTiles; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        c += so[j][i] >= cand ? 1 : 0;
+                if (group4_sum(c) >= k)
+                    K = cand;
+            }
+            int above = 0;
 #pragma unroll
             for (int j = 0; j < kFastTiles; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    c += (so[j][i] == K && 16 * j + i < lim_c) ? 1 : 0;
-            if (group4_sum(c) < need)
-                I = cand;
-        }
-        if (!fits) {
-            kth = K;
-            tie_idx = I;             // exactly k keys are >= (K, I)
-            total = k;
-            fits = true;
-        }
-    }
-
-    // compact the survivors per token as two 32-bit arrays (scores, and the
-    // part 16 j + i of the sub-key known at compile time: 64-bit keys built
-    // here would pin register pairs for all 128 candidates), then sort them as
-    // keys in the 4-lane group.  The reader adds 4 x (the writing lane group),
-    // which it knows from the survivor's position.
-    const bool exact = tie_idx != 0xFFFFFFFFu;
-    const int lim_t = exact ? (int)tie_idx - 4 * g : 0;   // 16 j + i <= lim_t among ties
-    int mine = cnt;
-    if (exact) {
-        // recount this lane's share under the exact bound
-        int c = 0;
+                    above += so[j][i] > K ? 1 : 0;
+            const int need = k - group4_sum(above);     // tied picks to take, lowest index first
+            uint32_t I = 0;                              // largest bound with < need tied indices below it
+            for (int bit = 9; bit >= 0; --bit) {
+                const uint32_t cand = I | (1u << bit);
+                // sub-key 16 j + 4 g + i < cand  <=>  16 j + i < cand - 4 g
+                const int lim_c = (int)cand - 4 * g;
+                int c = 0;
 #pragma unroll
-        for (int j = 0; j < kFastTiles; ++j)
+                for (int j = 0; j < kFastTiles; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        c += (so[j][i] == K && 16 * j + i < lim_c) ? 1 : 0;
+                if (group4_sum(c) < need)
+                    I = cand;
+            }
+            if (!fits) {
+                kth = K;
+                tie_idx = I;             // exactly k keys of the block are >= (K, I)
+                total = k;
+                fits = true;
+            }
+        }
+
+        // compact the survivors per token as two 32-bit arrays (scores, and
+        // the part 16 j + i of the sub-key known at compile time: 64-bit keys
+        // built here would pin register pairs for all 128 candidates), then
+        // sort them as keys in the 4-lane group.  The reader adds 4 x (the
+        // writing lane group), which it knows from the survivor's position,
+        // and the block's first sub-key.
+        const bool exact = tie_idx != 0xFFFFFFFFu;
+        const int lim_t = exact ? (int)tie_idx - 4 * g : 0;   // 16 j + i <= lim_t among ties
+        int mine = cnt;
+        if (exact) {
+            // recount this lane's share under the exact bound
+            int c = 0;
+#pragma unroll
+            for (int j = 0; j < kFastTiles; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t o = so[j][i];
+                    c += (o > kth || (o == kth && 16 * j + i <= lim_t)) ? 1 : 0;
+                }
+            mine = c;
+        }
+        const int c0 = __shfl(mine, tok), c1 = __shfl(mine, tok + 16), c2 = __shfl(mine, tok + 32);
+        int off = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
+#pragma unroll
+        for (int j = 0; j < kFastTiles; ++j) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t o = so[j][i];
-                c += (o > kth || (o == kth && 16 * j + i <= lim_t)) ? 1 : 0;
+                const bool keep = exact ? (o > kth || (o == kth && 16 * j + i <= lim_t)) : o >= kth;
+                if (keep) {
+                    surv_s[off] = o;
+                    surv_i[off] = (uint32_t)(16 * j + i);
+                    ++off;
+                }
             }
-        mine = c;
-    }
-    const int c0 = __shfl(mine, tok), c1 = __shfl(mine, tok + 16), c2 = __shfl(mine, tok + 32);
-    int off = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
-#pragma unroll
-    for (int j = 0; j < kFastTiles; ++j) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t o = so[j][i];
-            const bool keep = exact ? (o > kth || (o == kth && 16 * j + i <= lim_t)) : o >= kth;
-            if (keep) {
-                surv_s[off] = o;
-                surv_i[off] = (uint32_t)(16 * j + i);
-                ++off;
-            }
+            __builtin_amdgcn_sched_barrier(0);     // one tile's keys at a time
         }
-        __builtin_amdgcn_sched_barrier(0);     // one tile's keys at a time
-    }
-    wave_lds_sync();
-    uint64_t v[16];
-    const int b1 = c0, b2 = c0 + c1, b3 = c0 + c1 + c2;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int e = 16 * g + r;
-        const uint32_t src_g = (e >= b1 ? 1u : 0u) + (e >= b2 ? 1u : 0u) + (e >= b3 ? 1u : 0u);
-        v[r] = e < total ? ((uint64_t)surv_s[e] << 32) | (uint64_t)~(surv_i[e] + 4u * src_g) : 0ull;
-    }
-    group4_sort_desc<16>(v);
-    // lane group g holds ranks 16 g .. 16 g + 15
-    if (live) {
-        uint2 *out = lists + ((t * H + h) * 2 + s) * (int64_t)k;
+        wave_lds_sync();
+        const int b1 = c0, b2 = c0 + c1, b3 = c0 + c1 + c2;
+        uint64_t v[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int e = 16 * g + r;
-            if (e < k)
-                out[e] = make_uint2((uint32_t)(v[r] >> 32), ~(uint32_t)v[r]);
+            const uint32_t src_g = (e >= b1 ? 1u : 0u) + (e >= b2 ? 1u : 0u) + (e >= b3 ? 1u : 0u);
+            v[r] = e < total
+                       ? ((uint64_t)surv_s[e] << 32) | (uint64_t)~(surv_i[e] + 4u * src_g + (uint32_t)base)
+                       : 0ull;
         }
+        group4_sort_desc<16>(v);
+        // lane group g holds ranks 16 g .. 16 g + 15 of the block
+        if constexpr (!kFirst) {
+            // top k of the two sorted lists A (first block) and B (this one):
+            // C[e] = max(A[e], B[31 - e]) for e < 32 (both padded with zero
+            // keys past their ends), then a bitonic merge.  Lane groups 0 and
+            // 1 hold C; B[31 - e] is register 15 - r of the other group.
+            const int ga = g & 1;
+            uint64_t c[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int e = 16 * ga + r;
+                const uint64_t a = e < k ? prev[e] : 0ull;
+                const uint64_t b = shfl_xor_u64(v[15 - r], 16);
+                c[r] = a > b ? a : b;
+            }
+            // stride 16: across the two lane groups, group 0 keeps the larger
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const uint64_t o = shfl_xor_u64(c[r], 16);
+                c[r] = ((c[r] > o) == (ga == 0)) ? c[r] : o;
+            }
+#pragma unroll
+            for (int stride = 8; stride > 0; stride >>= 1)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if ((r & stride) == 0) {
+                        const uint64_t x = c[r], y = c[r | stride];
+                        c[r] = x > y ? x : y;
+                        c[r | stride] = x > y ? y : x;
+                    }
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                v[r] = c[r];
+        } else if constexpr (!kLast) {
+            if (g < 2) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (16 * g + r < k)
+                        prev[16 * g + r] = v[r];
+            }
+            wave_lds_sync();
+            // the next block's codebook steps overwrite every wave's survivors
+            __syncthreads();
+            return;
+        }
+
+        // last block: lane groups 0 and 1 hold ranks 0 .. 31
+        if (live && g < 2) {
+            uint2 *out = lists + ((t * H + h) * 2 + s) * (int64_t)k;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int e = 16 * g + r;
+                if (e < k)
+                    out[e] = make_uint2((uint32_t)(v[r] >> 32), ~(uint32_t)v[r]);
+            }
+        }
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    if constexpr (BLOCKS == 1) {
+        block(yes{}, yes{});
+    } else {
+        block(yes{}, no{});
+        block(no{}, yes{});
     }
 }
 
@@ -377,9 +478,14 @@ hipError_t launch_select_fast(const void *q, const void *keys, int64_t T, int H,
     (void)d_k;      // 512 on this path
     uint2 *lists = static_cast<uint2 *>(workspace);
     const dim3 grid((unsigned)((T + kFastTokWG - 1) / kFastTokWG), (unsigned)H, 2);
-    hipLaunchKernelGGL(fwd_topk_half_kernel, grid, dim3(kFastWaves * kWave), 0, stream,
-                       static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(keys), T, H, n,
-                       k, lists);
+    if (n <= kFastBlock)
+        hipLaunchKernelGGL(fwd_topk_half_kernel<1>, grid, dim3(kFastWaves * kWave), 0, stream,
+                           static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(keys), T, H,
+                           n, k, lists);
+    else
+        hipLaunchKernelGGL(fwd_topk_half_kernel<2>, grid, dim3(kFastWaves * kWave), 0, stream,
+                           static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(keys), T, H,
+                           n, k, lists);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;

@@ -81,7 +81,7 @@ def test_status_strings():
 
 
 def test_forward_workspace_checks():
-    """The two-kernel selection (bf16, d_k = 512, 256 < n <= 512, k <= 32)
+    """The two-kernel selection (bf16, d_k = 512, 256 < n <= 1024, k <= 32)
     keeps its per-half top-k lists in the caller's workspace."""
     p = P(T=100, H=3, n=300, k=20, d_k=512, d_v=64, dtype=_lib.PKM_BF16)
     need = _lib.workspace_bytes(p, False)
@@ -92,8 +92,13 @@ def test_forward_workspace_checks():
     assert _lib.forward_select(p, *args, FAKE + 8, need, None) == 6
     assert _lib.forward(p, *[FAKE] * 7, FAKE, need - 1, None) == 4
     # other shapes need none, and accept a NULL workspace
+    big = P(T=100, H=3, n=1024, k=32, d_k=512, d_v=64, dtype=_lib.PKM_BF16)
+    assert _lib.workspace_bytes(big, False) == (100 * 3 * 2 * 32 * 8 + 255) // 256 * 256
     q = P(T=100, H=3, n=300, k=20, d_k=256, d_v=64, dtype=_lib.PKM_BF16)
     assert _lib.workspace_bytes(q, False) == 0
+    for n, k in ((256, 20), (1024, 33)):
+        assert _lib.workspace_bytes(P(T=100, H=3, n=n, k=k, d_k=512, d_v=64,
+                                      dtype=_lib.PKM_BF16), False) == 0
 
 
 def QP(**kw):

@@ -110,6 +110,44 @@ def test_edge(orc, case, dtype):
     assert rep["rows"] == T * H
 
 
+# the two-kernel selection (bf16, d_k = 512, 256 < n <= 1024, k <= 32): per-half
+# top-k over blocks of 512 sub-keys, then the pruned combine
+FAST_EDGE = [
+    # T,  H, n,    k,  d_k, d_v, kind
+    (100, 3, 300, 20, 512, 24, "normal"),      # ragged T and n, k < 32
+    (70, 2, 257, 32, 512, 16, "normal"),       # smallest n on the path: one sub-key in the last tile
+    (64, 2, 512, 1, 512, 16, "normal"),        # k = 1
+    (48, 2, 400, 32, 512, 16, "dup"),          # duplicated sub-keys
+    (30, 1, 512, 32, 512, 16, "right_zero"),   # every right score ties: the exact bisection branch
+    (40, 2, 300, 9, 512, 16, "integer"),       # exact arithmetic, ties everywhere
+    (24, 2, 1024, 32, 512, 16, "normal"),      # two full blocks
+    (40, 2, 600, 32, 512, 16, "normal"),       # a second block of 88 sub-keys
+    (40, 1, 520, 32, 512, 16, "normal"),       # a second block with fewer sub-keys than k
+    (24, 2, 1024, 32, 512, 16, "dup"),         # ties across the blocks (sub-key 0 = sub-key n-1)
+    (12, 1, 1024, 32, 512, 16, "right_zero"),  # the exact branch in both blocks
+    (30, 2, 700, 5, 512, 16, "integer"),       # exact arithmetic across the blocks
+]
+
+
+@pytest.mark.parametrize("case", FAST_EDGE, ids=[f"T{c[0]}H{c[1]}n{c[2]}k{c[3]}-{c[6]}" for c in FAST_EDGE])
+def test_edge_two_kernel_selection(orc, case):
+    import product_key_memory_amd as pk
+    from product_key_memory_amd import _lib
+    T, H, n, k, d_k, d_v, kind = case
+    # this shape takes the two-kernel path: it is the one that needs a forward workspace
+    assert _lib.workspace_bytes(_lib.Problem(T, H, n, k, d_k, d_v, _lib.PKM_BF16), False) > 0
+    inp = pkm_inputs.custom(T, H, n, k, d_k, d_v, dtype="bf16", seed=T * 131 + n + 7, kind=kind)
+    rep = gpu_util.run_parity(orc, inp, k, backward=True, tight=TIGHT["bf16"])
+    assert rep["rows"] == T * H
+    if kind == "integer":
+        # exact arithmetic: the order itself, ties included, is the oracle's
+        dev = gpu_util.device()
+        q, keys, values = (gpu_util.to_dev(inp[x], dev) for x in ("q", "keys", "values"))
+        _, idx, _, _ = pk.pkm_forward(q, keys, values, k)
+        ref = orc.forward(inp["q"], inp["keys"], inp["values"], k)
+        assert np.array_equal(gpu_util.to_host(idx), ref["idx"]), "exact-arithmetic order differs"
+
+
 def test_k1_is_the_row_itself(orc):
     """k = 1, one head: the weight is exactly 1 and y is the selected value row, bit for bit."""
     import product_key_memory_amd as pk

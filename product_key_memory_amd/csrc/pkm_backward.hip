@@ -539,14 +539,36 @@ __global__ __launch_bounds__(kQryWaves *kWave) void bwd_query_kernel(
     const DT *kh = keys + (int64_t)h * 2 * n * half;
     const __amdgpu_buffer_rsrc_t rsrc = buffer_over(kh, 2 * n * half * (int)sizeof(DT));
     constexpr int kOut = 0x40000000;      // an offset past any codebook: reads zeros
-    float acc[2][JPL][4];
+    // byte offset of this lane's 4 elements in a sub-key row (kOut past the
+    // half: kOut plus any row offset still reads zeros)
+    int lane_off[JPL];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int j = 0; j < JPL; ++j) {
+        const int c = lane + j * kWave;
+        lane_off[j] = c < groups ? 4 * c * (int)sizeof(DT) : kOut;
+    }
+    // one set of accumulators, for the half whose entries are being summed;
+    // `flush` writes it to half `acc_half` of dq and clears it
+    float acc[JPL][4];
 #pragma unroll
-        for (int j = 0; j < JPL; ++j)
+    for (int j = 0; j < JPL; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            acc[j][e] = 0.f;
+    int acc_half = 0;
+    float *dqr = dq + row * (int64_t)d_k;
+    auto flush = [&]() {
+#pragma unroll
+        for (int j = 0; j < JPL; ++j) {
+            const int c = lane + j * kWave;
+            if (c < groups)
+                *reinterpret_cast<float4 *>(dqr + acc_half * half + 4 * c) =
+                    make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                acc[s][j][e] = 0.f;
+                acc[j][e] = 0.f;
+        }
+    };
 
     for (int pass = 0; pass < passes; ++pass) {
         const int s = passes == 1 ? lane / (kWave / 2) : pass;
@@ -577,66 +599,78 @@ __global__ __launch_bounds__(kQryWaves *kWave) void bwd_query_kernel(
             gl_i[at] = sub;
             gl_g[at] = first ? g : 0.f;
         }
-        // the distinct sub-keys of this pass (left ones first), compacted:
-        // lane u then holds entry u (as codebook row s * n + sub and its g
-        // split by half); lanes past the list hold a row past the codebooks
-        // (reads zeros) with g = 0
+        // the distinct sub-keys of this pass, compacted into two segments of
+        // 32 list positions: one pass (k <= 32) puts the left half's entries
+        // in segment 0 and the right half's in segment 1; with two passes
+        // (one half each) the pass's entries fill segment 0, then segment 1.
+        // Position p is held by lane p (as codebook row s * n + sub, and g);
+        // positions past a segment's count hold a row past the codebooks
+        // (reads zeros) with g = 0.
         const uint64_t mask = __ballot(first);
-        const int cnt = __builtin_popcountll(mask);
+        int seg_cnt[2];
+        if (passes == 1) {
+            seg_cnt[0] = __builtin_popcountll(mask & 0xFFFFFFFFull);
+            seg_cnt[1] = __builtin_popcountll(mask >> 32);
+        } else {
+            const int cnt = __builtin_popcountll(mask);
+            seg_cnt[0] = cnt < 32 ? cnt : 32;
+            seg_cnt[1] = cnt - seg_cnt[0];
+        }
         if (first) {
-            const int rank = __builtin_popcountll(mask & ((1ull << lane) - 1));
-            s_sub[wv][rank] = s * n + sub;
-            s_g[wv][rank] = g;
+            const uint64_t below = mask & ((1ull << lane) - 1);
+            const int pos = passes == 1
+                                ? (lane & 32) + __builtin_popcountll(below & (lane < 32 ? 0xFFFFFFFFull : ~0xFFFFFFFFull))
+                                : __builtin_popcountll(below);
+            s_sub[wv][pos] = s * n + sub;
+            s_g[wv][pos] = g;
         }
         wave_lds_sync();
-        const bool in_list = lane < cnt;
+        const bool in_list = (lane & 31) < seg_cnt[lane >> 5];
         const int l_row = in_list ? s_sub[wv][lane] : 2 * n;
         const float l_g = in_list ? s_g[wv][lane] : 0.f;
-        const float l_g0 = l_row < n ? l_g : 0.f, l_g1 = l_row < n ? 0.f : l_g;
 
-        // dq halves += g * sub-key row, kBatch rows in flight
+        // dq half += g * sub-key row, kBatch rows in flight, each entry 4 JPL
+        // FMAs; a segment's unused tail is skipped 8 entries at a time
 #pragma unroll
-        for (int b = 0; b < kWave / kBatch; ++b) {
-            if (b * kBatch >= cnt)
-                break;
-            Row4<DT> x[kBatch][JPL];
+        for (int sg = 0; sg < 2; ++sg) {
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int sr = __builtin_amdgcn_readlane(l_row, b * kBatch + u);
+            for (int b = 0; b < 32 / kBatch; ++b) {
+                const int first_e = b * kBatch;             // in the segment
+                if (first_e >= seg_cnt[sg])
+                    break;
+                Row4<DT> x[kBatch][JPL];
 #pragma unroll
-                for (int j = 0; j < JPL; ++j) {
-                    const int c = lane + j * kWave;
-                    const int voff = c < groups ? (sr * half + 4 * c) * (int)sizeof(DT) : kOut;
-                    x[u][j].load(rsrc, voff);
+                for (int u = 0; u < kBatch; ++u) {
+                    const int row_off = __builtin_amdgcn_readlane(l_row, 32 * sg + first_e + u) *
+                                        half * (int)sizeof(DT);
+#pragma unroll
+                    for (int j = 0; j < JPL; ++j)
+                        x[u][j].load(rsrc, lane_off[j] + row_off);
+                }
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    if (u % 8 == 0 && first_e + u >= seg_cnt[sg])
+                        break;
+                    const float gv = __int_as_float(
+                        __builtin_amdgcn_readlane(__float_as_int(l_g), 32 * sg + first_e + u));
+#pragma unroll
+                    for (int j = 0; j < JPL; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[j][e] = fmaf(gv, x[u][j][e], acc[j][e]);
                 }
             }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const float g0 = __int_as_float(
-                    __builtin_amdgcn_readlane(__float_as_int(l_g0), b * kBatch + u));
-                const float g1 = __int_as_float(
-                    __builtin_amdgcn_readlane(__float_as_int(l_g1), b * kBatch + u));
-#pragma unroll
-                for (int j = 0; j < JPL; ++j)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        acc[0][j][e] = fmaf(g0, x[u][j][e], acc[0][j][e]);
-                        acc[1][j][e] = fmaf(g1, x[u][j][e], acc[1][j][e]);
-                    }
+            if (passes == 1) {
+                acc_half = sg;
+                flush();
             }
+        }
+        if (passes == 2) {
+            acc_half = pass;
+            flush();
         }
         wave_lds_sync();     // s_sub / s_g are rewritten by the next pass
     }
-    float *dqr = dq + row * (int64_t)d_k;
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int j = 0; j < JPL; ++j) {
-            const int c = lane + j * kWave;
-            if (c < groups)
-                *reinterpret_cast<float4 *>(dqr + s * half + 4 * c) =
-                    make_float4(acc[s][j][0], acc[s][j][1], acc[s][j][2], acc[s][j][3]);
-        }
 }
 
 // ---------------------------------------------------------------------------

@@ -515,7 +515,7 @@ __global__ __launch_bounds__(kQryWaves *kWave) void bwd_query_kernel(
     int32_t *__restrict__ gl_i, float *__restrict__ gl_g, int64_t T, int H, int n, int k, int d_k)
 {
     constexpr int kBatch = (sizeof(DT) == 2 ? 32 : 16) / JPL;     // sub-key rows in flight
-    __shared__ int4 s_pick[kQryWaves][kQryMaxK];                   // left, right, w, w dw
+    __shared__ int4 s_pick[kQryWaves][2][kQryMaxK];    // per half: sub-key, w, w dw, 0
     __shared__ int32_t s_sub[kQryWaves][kWave];      // distinct (half * n + sub), <= 64 a pass
     __shared__ float s_g[kQryWaves][kWave];
     const int lane = lane_id();
@@ -530,8 +530,12 @@ __global__ __launch_bounds__(kQryWaves *kWave) void bwd_query_kernel(
     if (lane < k) {
         const int f = idx[base + lane];
         const float w = weights[base + lane];
-        s_pick[wv][lane] = make_int4(f / n, f % n, __float_as_int(w),
-                                     __float_as_int(w * dw[base + lane]));
+        const int wi = __float_as_int(w), wdwi = __float_as_int(w * dw[base + lane]);
+        s_pick[wv][0][lane] = make_int4(f / n, wi, wdwi, 0);
+        s_pick[wv][1][lane] = make_int4(f % n, wi, wdwi, 0);
+    } else if (lane < ((k + 3) & ~3)) {
+        // padding up to a multiple of 4 picks: no sub-key, zero weights
+        s_pick[wv][0][lane] = s_pick[wv][1][lane] = make_int4(-1, 0, 0, 0);
     }
     wave_lds_sync();
 
@@ -574,25 +578,38 @@ __global__ __launch_bounds__(kQryWaves *kWave) void bwd_query_kernel(
         const int s = passes == 1 ? lane / (kWave / 2) : pass;
         const int r = passes == 1 ? lane % (kWave / 2) : lane;
         const bool valid = r < k;
-        const int4 mine = s_pick[wv][valid ? r : 0];
-        const int sub = s == 0 ? mine.x : mine.y;
+        const int4 *picks = s_pick[wv][s];
+        const int sub = picks[valid ? r : 0].x;
         // sums over the picks sharing this lane's sub-key (A, W) and over the
-        // rest (B, Wc); the first pick of each sub-key carries its g
-        // (selects, not branches: the loop stays free of exec-mask updates)
+        // rest (B, Wc), as fmas with a 1 or 0 factor (the same roundings as
+        // plain sums, and no exec-mask updates); the first pick of each
+        // sub-key carries its g.  `earlier` collects, as a lane mask, the
+        // lanes that an earlier pick with the same sub-key has already seen
+        // (lane r is "later" than pick q iff r > q).
         float A = 0.f, W = 0.f, B = 0.f, Wc = 0.f;
-        uint32_t earlier = 0;      // an earlier pick has this sub-key
-        for (int q = 0; q < k; ++q) {
-            const int4 e = s_pick[wv][q];
-            const int sub_q = s == 0 ? e.x : e.y;
-            const float w_q = __int_as_float(e.z), wdw_q = __int_as_float(e.w);
-            const bool same = sub_q == sub;
-            A += same ? wdw_q : 0.f;
-            W += same ? w_q : 0.f;
-            B += same ? 0.f : wdw_q;
-            Wc += same ? 0.f : w_q;
-            earlier |= (uint32_t)(same & (q < r));
+        uint64_t earlier = 0;
+        // lanes later than pick q: r > q, per 32-lane half with one pass
+        const uint64_t keep = passes == 1 ? 0xFFFFFFFEFFFFFFFFull : ~0ull;
+        uint64_t later = passes == 1 ? 0xFFFFFFFEFFFFFFFEull : ~1ull;
+        for (int q0 = 0; q0 < k; q0 += 4) {
+            int4 e[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                e[u] = picks[q0 + u];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float w_q = __int_as_float(e[u].y), wdw_q = __int_as_float(e[u].z);
+                const bool same = e[u].x == sub;
+                const float in = same ? 1.f : 0.f, out = same ? 0.f : 1.f;
+                A = fmaf(wdw_q, in, A);
+                W = fmaf(w_q, in, W);
+                B = fmaf(wdw_q, out, B);
+                Wc = fmaf(w_q, out, Wc);
+                earlier |= __ballot(same) & later;
+                later = (later << 1) & keep;
+            }
         }
-        const bool first = valid && earlier == 0;
+        const bool first = valid && ((earlier >> lane) & 1ull) == 0;
         const float g = A * Wc - B * W;
         if (valid) {
             const int64_t at = (row * 2 + s) * (int64_t)k + r;

@@ -710,37 +710,43 @@ __global__ __launch_bounds__(kQryWaves *kWave) void bwd_query_kernel(
 //     float32 sums;
 //   float32 storage: v_mfma_f32_16x16x4_f32 on the float32 values.
 constexpr int kDkWaves = 16;
-constexpr int kDkTok = 32;          // tokens per step (the MFMA K extent)
+constexpr int kDkTok = 32;          // tokens per step (the MFMA K extent), or 64 (see below)
 
 template <typename DT> struct DkTile;
 template <> struct DkTile<bf16_t> {
     typedef uint16_t elt;
     static constexpr int parts = 2;
-    static constexpr int chunks = 4;        // 16-byte chunks in a row of 32 tokens
 };
 template <> struct DkTile<float> {
     typedef float elt;
     static constexpr int parts = 1;
-    static constexpr int chunks = 8;
 };
 
-// Element offset of (row, token) in a [rows][32] tile whose 16-byte chunks
-// are XOR-swizzled by row: the 16 rows of an operand read cover all banks.
-template <int C>
+// Element offset of (row, token) in a [rows][TOK] tile of C 16-byte chunks
+// per row, the chunks XOR-swizzled by row: the 16 rows of an operand read
+// cover all banks.
+template <int C, int TOK>
 __device__ __forceinline__ int dk_cell(int row, int tl)
 {
-    constexpr int EPC = kDkTok / C;                 // elements per chunk
+    constexpr int EPC = TOK / C;                    // elements per chunk
     const int c = (tl / EPC) ^ ((row / (16 / C)) % C);
-    return row * kDkTok + c * EPC + tl % EPC;
+    return row * TOK + c * EPC + tl % EPC;
+}
+template <typename E, int TOK>
+__device__ __forceinline__ int dk_cell_of(int row, int tl)
+{
+    return dk_cell<TOK * (int)sizeof(E) / 16, TOK>(row, tl);
 }
 
+template <int TOK>
 __device__ __forceinline__ uint4 dk_chunk(const uint16_t *tile, int row, int c)
 {
-    return *reinterpret_cast<const uint4 *>(tile + dk_cell<4>(row, 8 * c));
+    return *reinterpret_cast<const uint4 *>(tile + dk_cell<TOK / 8, TOK>(row, 8 * c));
 }
+template <int TOK>
 __device__ __forceinline__ float4 dk_chunk(const float *tile, int row, int c)
 {
-    return *reinterpret_cast<const float4 *>(tile + dk_cell<8>(row, 4 * c));
+    return *reinterpret_cast<const float4 *>(tile + dk_cell<TOK / 4, TOK>(row, 4 * c));
 }
 
 __device__ __forceinline__ void dk_store(uint16_t *hi, uint16_t *lo, int at, float g)
@@ -757,28 +763,60 @@ __device__ __forceinline__ void dk_clear(uint16_t *hi, uint16_t *lo, int at)
 }
 __device__ __forceinline__ void dk_clear(float *a, float *, int at) { a[at] = 0.f; }
 
-// q staging of one step.  bf16: thread u < 256 takes the token pair
+// q staging of one step.  bf16, 32-token steps: thread u < 256 takes the token pair
 // (2 (u % 16), + 1) and 8 columns 8 (u / 16) ..: two 16-byte loads, eight
 // packed 4-byte LDS stores.  float32: thread u takes token u % 32 and 4
 // columns 4 (u / 32) ..: one 16-byte load, four LDS stores.
 struct DkQBf16 {
     uint4 a, b;
 };
+struct DkQBf16One {
+    uint4 a;
+};
 struct DkQF32 {
     float4 a;
 };
-template <typename DT> struct DkQ;
-template <> struct DkQ<bf16_t> { typedef DkQBf16 type; };
-template <> struct DkQ<float> { typedef DkQF32 type; };
+template <typename DT, int TOK> struct DkQ;
+template <> struct DkQ<bf16_t, 32> { typedef DkQBf16 type; };
+template <> struct DkQ<bf16_t, 64> { typedef DkQBf16One type; };
+template <> struct DkQ<float, 32> { typedef DkQF32 type; };
 
-template <int CT>
+// bf16, 64-token steps: thread u takes token u % 64 and 8 columns 8 (u / 64)
+// ..: one 16-byte load, eight 2-byte LDS stores.
+template <int CT, int TOK>
+__device__ __forceinline__ void dk_q_load(DkQBf16One &v, const bf16_t *q, int64_t t0, int64_t t_end,
+                                          int H, int h, int d_k, int col0, int half, int tid)
+{
+    static_assert(TOK == 64, "one token per thread");
+    v.a = make_uint4(0u, 0u, 0u, 0u);
+    const int tl = tid % TOK, cg = tid / TOK;
+    const int col = col0 + 8 * cg;
+    const int64_t t = t0 + tl;
+    if (cg < 16 * CT / 8 && col < half && t < t_end)
+        v.a = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(q) +
+                                               (t * H + h) * (int64_t)d_k + col);
+}
+template <int CT, int TOK>
+__device__ __forceinline__ void dk_q_store(const DkQBf16One &v, uint16_t *bt, int tid)
+{
+    const int tl = tid % TOK, cg = tid / TOK;
+    if (cg >= 16 * CT / 8)
+        return;
+    const uint32_t a[4] = {v.a.x, v.a.y, v.a.z, v.a.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        bt[dk_cell<TOK / 8, TOK>(8 * cg + i, tl)] = (uint16_t)((i & 1) ? a[i / 2] >> 16 : a[i / 2]);
+}
+
+template <int CT, int TOK>
 __device__ __forceinline__ void dk_q_load(DkQBf16 &v, const bf16_t *q, int64_t t0, int64_t t_end,
                                           int H, int h, int d_k, int col0, int half, int tid)
 {
+    constexpr int PAIRS = TOK / 2;
     v.a = v.b = make_uint4(0u, 0u, 0u, 0u);
-    if (tid >= 16 * (16 * CT / 8))
+    if (tid >= PAIRS * (16 * CT / 8))
         return;
-    const int tp = tid % 16, cg = tid / 16;
+    const int tp = tid % PAIRS, cg = tid / PAIRS;
     const int col = col0 + 8 * cg;
     if (col >= half)
         return;
@@ -789,41 +827,43 @@ __device__ __forceinline__ void dk_q_load(DkQBf16 &v, const bf16_t *q, int64_t t
     if (tb < t_end)
         v.b = *reinterpret_cast<const uint4 *>(qb + (tb * H + h) * (int64_t)d_k + col);
 }
-template <int CT>
+template <int CT, int TOK>
 __device__ __forceinline__ void dk_q_store(const DkQBf16 &v, uint16_t *bt, int tid)
 {
-    if (tid >= 16 * (16 * CT / 8))
+    constexpr int PAIRS = TOK / 2;
+    if (tid >= PAIRS * (16 * CT / 8))
         return;
-    const int tp = tid % 16, cg = tid / 16;
+    const int tp = tid % PAIRS, cg = tid / PAIRS;
     const uint32_t a[4] = {v.a.x, v.a.y, v.a.z, v.a.w}, b[4] = {v.b.x, v.b.y, v.b.z, v.b.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const uint32_t lo = (i & 1) ? a[i / 2] >> 16 : a[i / 2] & 0xffffu;
         const uint32_t hi = (i & 1) ? b[i / 2] >> 16 : b[i / 2] & 0xffffu;
-        *reinterpret_cast<uint32_t *>(bt + dk_cell<4>(8 * cg + i, 2 * tp)) = lo | (hi << 16);
+        *reinterpret_cast<uint32_t *>(bt + dk_cell<TOK / 8, TOK>(8 * cg + i, 2 * tp)) = lo | (hi << 16);
     }
 }
-template <int CT>
+template <int CT, int TOK>
 __device__ __forceinline__ void dk_q_load(DkQF32 &v, const float *q, int64_t t0, int64_t t_end,
                                           int H, int h, int d_k, int col0, int half, int tid)
 {
+    static_assert(TOK == kDkTok, "float32 storage steps over 32 tokens");
     v.a = make_float4(0.f, 0.f, 0.f, 0.f);
-    const int tl = tid % kDkTok, cg = tid / kDkTok;
+    const int tl = tid % TOK, cg = tid / TOK;
     const int col = col0 + 4 * cg;
     const int64_t t = t0 + tl;
     if (cg < 16 * CT / 4 && col < half && t < t_end)
         v.a = *reinterpret_cast<const float4 *>(q + (t * H + h) * (int64_t)d_k + col);
 }
-template <int CT>
+template <int CT, int TOK>
 __device__ __forceinline__ void dk_q_store(const DkQF32 &v, float *bt, int tid)
 {
-    const int tl = tid % kDkTok, cg = tid / kDkTok;
+    const int tl = tid % TOK, cg = tid / TOK;
     if (cg >= 16 * CT / 4)
         return;
     const float a[4] = {v.a.x, v.a.y, v.a.z, v.a.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        bt[dk_cell<8>(4 * cg + i, tl)] = a[i];
+        bt[dk_cell<TOK / 4, TOK>(4 * cg + i, tl)] = a[i];
 }
 
 // One 16 x 16 x 32-token product on fragments read from the swizzled tiles.
@@ -833,19 +873,19 @@ __device__ __forceinline__ floatx4 dk_mfma(const uint4 &a, const uint4 &b, float
                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }
 
-template <typename DT, int RT, int CT>
+template <typename DT, int RT, int CT, int TOK>
 __global__ __launch_bounds__(kDkWaves *kWave) void dkeys_mfma_kernel(
     const DT *__restrict__ q, const int32_t *__restrict__ gl_i, const float *__restrict__ gl_g,
     float *__restrict__ partial, int64_t T, int H, int n, int k, int d_k, int tokens_per_block)
 {
     typedef typename DkTile<DT>::elt E;
     constexpr int PARTS = DkTile<DT>::parts;
-    constexpr int C = DkTile<DT>::chunks;
+    static_assert(TOK == 32 || (TOK == 64 && PARTS == 2), "steps of 32 tokens, or 64 for bf16");
     extern __shared__ __align__(16) unsigned char smem[];
     const int n_pad = (n + 15) & ~15;
     E *a_hi = reinterpret_cast<E *>(smem);                      // [n_pad][32]
-    E *a_lo = a_hi + (PARTS == 2 ? (size_t)n_pad * kDkTok : 0);  // [n_pad][32] (bf16 only)
-    E *bt = a_hi + (size_t)PARTS * n_pad * kDkTok;                // [16 CT][32]
+    E *a_lo = a_hi + (PARTS == 2 ? (size_t)n_pad * TOK : 0);  // [n_pad][TOK] (bf16 only)
+    E *bt = a_hi + (size_t)PARTS * n_pad * TOK;                // [16 CT][TOK]
 
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
@@ -860,7 +900,7 @@ __global__ __launch_bounds__(kDkWaves *kWave) void dkeys_mfma_kernel(
     const int ntiles = n_pad / 16;
     const DT *qs = q + (int64_t)s * half;
 
-    for (int e = tid; e < (PARTS * n_pad + CW) * kDkTok; e += kDkWaves * kWave)
+    for (int e = tid; e < (PARTS * n_pad + CW) * TOK; e += kDkWaves * kWave)
         a_hi[e] = (E)0;
 
     floatx4 acc[RT][CT];
@@ -872,7 +912,8 @@ __global__ __launch_bounds__(kDkWaves *kWave) void dkeys_mfma_kernel(
 
     const int64_t t_begin = (int64_t)blockIdx.x * tokens_per_block;
     const int64_t t_end = t_begin + tokens_per_block < T ? t_begin + tokens_per_block : T;
-    const int pairs = kDkTok * k;                 // (token, pick) pairs per step, <= 2048
+    // (token, pick) pairs per step, <= 2048 (64-token steps only with k <= 32)
+    const int pairs = TOK * k;
 
     // this thread's entries of a step: g and the tile cell (or -1)
     auto load_entries = [&](int64_t t0, float (&g)[2], int (&cell)[2]) {
@@ -894,29 +935,29 @@ __global__ __launch_bounds__(kDkWaves *kWave) void dkeys_mfma_kernel(
     };
     float g_next[2];
     int cell_next[2];
-    typename DkQ<DT>::type q_next;
+    typename DkQ<DT, TOK>::type q_next;
     load_entries(t_begin, g_next, cell_next);
-    dk_q_load<CT>(q_next, qs, t_begin, t_end, H, h, d_k, c0, half, tid);
+    dk_q_load<CT, TOK>(q_next, qs, t_begin, t_end, H, h, d_k, c0, half, tid);
     int mine_at[2] = {-1, -1};                    // cells this thread wrote
     __syncthreads();
 
     const int r16 = lane & 15, kg = lane >> 4;
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += kDkTok) {
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += TOK) {
         // scatter this step's entries into dS^T, stage q^T
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             mine_at[j] = -1;
             if (cell_next[j] >= 0 && g_next[j] != 0.f) {
-                const int at = dk_cell<C>(cell_next[j] / 64, cell_next[j] % 64);
+                const int at = dk_cell_of<E, TOK>(cell_next[j] / 64, cell_next[j] % 64);
                 dk_store(a_hi, a_lo, at, g_next[j]);
                 mine_at[j] = at;
             }
         }
-        dk_q_store<CT>(q_next, bt, tid);
+        dk_q_store<CT, TOK>(q_next, bt, tid);
         // the next step's global reads fly during this step's products
-        if (t0 + kDkTok < t_end) {
-            load_entries(t0 + kDkTok, g_next, cell_next);
-            dk_q_load<CT>(q_next, qs, t0 + kDkTok, t_end, H, h, d_k, c0, half, tid);
+        if (t0 + TOK < t_end) {
+            load_entries(t0 + TOK, g_next, cell_next);
+            dk_q_load<CT, TOK>(q_next, qs, t0 + TOK, t_end, H, h, d_k, c0, half, tid);
         }
         __syncthreads();
 
@@ -926,20 +967,25 @@ __global__ __launch_bounds__(kDkWaves *kWave) void dkeys_mfma_kernel(
             if (tile < ntiles) {
                 const int row = tile * 16 + r16;
                 if constexpr (PARTS == 2) {
-                    const uint4 ah = dk_chunk(a_hi, row, kg), al = dk_chunk(a_lo, row, kg);
+                    // K = TOK tokens in steps of 32: chunks 4 ks + kg of the rows
 #pragma unroll
-                    for (int nb = 0; nb < CT; ++nb) {
-                        const uint4 b = dk_chunk(bt, nb * 16 + r16, kg);
-                        acc[ti][nb] = dk_mfma(ah, b, acc[ti][nb]);
-                        acc[ti][nb] = dk_mfma(al, b, acc[ti][nb]);
+                    for (int ks = 0; ks < TOK / 32; ++ks) {
+                        const uint4 ah = dk_chunk<TOK>(a_hi, row, 4 * ks + kg);
+                        const uint4 al = dk_chunk<TOK>(a_lo, row, 4 * ks + kg);
+#pragma unroll
+                        for (int nb = 0; nb < CT; ++nb) {
+                            const uint4 b = dk_chunk<TOK>(bt, nb * 16 + r16, 4 * ks + kg);
+                            acc[ti][nb] = dk_mfma(ah, b, acc[ti][nb]);
+                            acc[ti][nb] = dk_mfma(al, b, acc[ti][nb]);
+                        }
                     }
                 } else {
                     // K = 32 tokens as chunks kg and kg + 4 of the row (4 tokens each)
-                    const float4 a0 = dk_chunk(a_hi, row, kg), a1 = dk_chunk(a_hi, row, kg + 4);
+                    const float4 a0 = dk_chunk<TOK>(a_hi, row, kg), a1 = dk_chunk<TOK>(a_hi, row, kg + 4);
 #pragma unroll
                     for (int nb = 0; nb < CT; ++nb) {
-                        const float4 b0 = dk_chunk(bt, nb * 16 + r16, kg);
-                        const float4 b1 = dk_chunk(bt, nb * 16 + r16, kg + 4);
+                        const float4 b0 = dk_chunk<TOK>(bt, nb * 16 + r16, kg);
+                        const float4 b1 = dk_chunk<TOK>(bt, nb * 16 + r16, kg + 4);
                         floatx4 c = acc[ti][nb];
                         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a0.x, b0.x, c, 0, 0, 0);
                         c = __builtin_amdgcn_mfma_f32_16x16x4f32(a0.y, b0.y, c, 0, 0, 0);
@@ -1103,7 +1149,10 @@ static hipError_t launch_query_t(const void *q, const void *keys, const int32_t 
         return err;
     const int n_pad = (n + 15) & ~15;
     const int cols = dk_cols(n);
-    const size_t lds = ((size_t)DkTile<DT>::parts * n_pad + cols) * kDkTok * sizeof(typename DkTile<DT>::elt);
+    // bf16 with n <= 512 and k <= 32 steps over 64 tokens (twice the products
+    // per barrier; the tiles fit in 147 KB of LDS), every other case over 32
+    const int tok = (sizeof(DT) == 2 && n_pad <= 512 && k <= 32) ? 64 : kDkTok;
+    const size_t lds = ((size_t)DkTile<DT>::parts * n_pad + cols) * tok * sizeof(typename DkTile<DT>::elt);
     const int half = d_k / 2;
     const int ncb = (half + cols - 1) / cols;
     const dim3 grid((unsigned)S.blocks, (unsigned)(H * 2 * ncb));
@@ -1119,9 +1168,13 @@ static hipError_t launch_query_t(const void *q, const void *keys, const int32_t 
         return hipGetLastError();
     };
     // accumulators: rt row tiles x cols / 16 column tiles of 4 registers
-    err = rt <= 1 ? go(dkeys_mfma_kernel<DT, 1, 8>)
-        : rt <= 2 ? go(dkeys_mfma_kernel<DT, 2, 8>)
-                  : go(dkeys_mfma_kernel<DT, 4, 4>);
+    if constexpr (sizeof(DT) == 2)
+        if (tok == 64)
+            err = rt <= 1 ? go(dkeys_mfma_kernel<DT, 1, 8, 64>) : go(dkeys_mfma_kernel<DT, 2, 8, 64>);
+    if (tok == kDkTok)
+        err = rt <= 1 ? go(dkeys_mfma_kernel<DT, 1, 8, kDkTok>)
+            : rt <= 2 ? go(dkeys_mfma_kernel<DT, 2, 8, kDkTok>)
+                      : go(dkeys_mfma_kernel<DT, 4, 4, kDkTok>);
     if (err != hipSuccess)
         return err;
     const int64_t count = (int64_t)H * 2 * n * half;

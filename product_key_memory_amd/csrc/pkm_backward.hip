@@ -215,22 +215,29 @@ __global__ __launch_bounds__(kL2Threads) void bucket_sort_kernel(
 
 // Overwrite mode: zero the dvalues rows no wave will write whole -- rows no
 // pick selected, and rows with a run of more than kSegChunk sorted picks
-// (several waves add into those with atomics).
+// (several waves add into those with atomics).  Each wave checks 64 slots,
+// one per lane, then zeroes the rows found, all lanes on one row at a time.
 __global__ void dv_prepare_kernel(const int32_t *__restrict__ start, int64_t slots, int d_v,
                                   float *__restrict__ dvalues)
 {
     const int lane = lane_id();
-    const int64_t f = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    if (f >= slots)
+    const int64_t f0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * kWave;
+    if (f0 >= slots)
         return;
-    const int64_t b = start[f], e = start[f + 1];
-    const bool untouched = b == e;
-    const bool split = e - b > kSegChunk;
-    if (!untouched && !split)
-        return;
-    float4 *row = reinterpret_cast<float4 *>(dvalues + f * d_v);
-    for (int c = lane; c < d_v / 4; c += kWave)
-        row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int64_t f = f0 + lane;
+    bool zero = false;
+    if (f < slots) {
+        const int64_t b = start[f], e = start[f + 1];
+        zero = b == e || e - b > kSegChunk;
+    }
+    uint64_t todo = __ballot(zero);
+    while (todo) {
+        const int i = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        float4 *row = reinterpret_cast<float4 *>(dvalues + (f0 + i) * d_v);
+        for (int c = lane; c < d_v / 4; c += kWave)
+            row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1111,8 +1118,8 @@ hipError_t launch_bwd_value(int dtype, const void *values, const int32_t *idx,
     const int64_t picks = T * H * (int64_t)k;
     if (!accumulate) {
         const int64_t slots = (int64_t)n * n;
-        hipLaunchKernelGGL(dv_prepare_kernel, dim3(grid1d(slots, 4)), dim3(4 * kWave), 0, stream,
-                           slot_start, slots, d_v, dvalues);
+        hipLaunchKernelGGL(dv_prepare_kernel, dim3(grid1d(slots, 4 * kWave)), dim3(4 * kWave), 0,
+                           stream, slot_start, slots, d_v, dvalues);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess)
             return err;

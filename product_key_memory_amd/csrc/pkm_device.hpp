@@ -60,10 +60,11 @@ template <> struct Elt<bf16_t> { static constexpr int per16 = 8; };
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t ord_f32(float s)
 {
-    uint32_t u = __float_as_uint(s);
-    if (u == 0x80000000u)
-        u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    // s + 0 turns -0 into +0 (round to nearest) and leaves every other value
+    // as it is; then flip the sign bit of a positive pattern and every bit of
+    // a negative one -- integer ops only, no compare-and-select
+    const uint32_t u = __float_as_uint(s + 0.0f);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float unord_f32(uint32_t o)
 {

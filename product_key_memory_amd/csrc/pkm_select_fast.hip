@@ -47,7 +47,8 @@ constexpr int kFastTokWG = kFastWaves * kFastTok;    // tokens per workgroup
 constexpr int kFastTiles = 32;                       // 16-sub-key tiles per block
 constexpr int kFastBlock = 16 * kFastTiles;          // 512 sub-keys per block
 constexpr int kFastKSteps = 8;                       // 32-wide K steps: half = 256
-constexpr int kFastSurv = 64;                        // survivor slots per token
+constexpr int kFastSurv = 64;                        // survivors per token at most
+constexpr int kSurvStride = kFastSurv + 4;           // + one spare slot per lane group
 constexpr int kMergeWaves = 4;
 constexpr int kMergeRows = 16;                       // (token, head) rows per wave
 constexpr int kMaxPairs = 128;                       // merge_candidates(32) = 119
@@ -132,14 +133,14 @@ __global__ __launch_bounds__(kFastWaves *kWave) void fwd_topk_half_kernel(
     int k, uint2 *__restrict__ lists)
 {
     // the codebook steps during the scoring, the survivors afterwards
-    __shared__ uint4 lds[2 * 32 * 32];
-    static_assert(sizeof(lds) >= 2 * kFastWaves * kFastTok * kFastSurv * 4, "survivor space");
+    constexpr int kSurvUnits = 2 * kFastWaves * kFastTok * kSurvStride * 4 / 16;
+    __shared__ uint4 lds[kSurvUnits > 2 * 32 * 32 ? kSurvUnits : 2 * 32 * 32];
     // the first block's top k per token while the second block is scored
     // (row stride 33 keys: the 16 tokens' rows start in distinct banks)
     __shared__ uint64_t s_prev[kFastWaves][kFastTok][33];
-    uint32_t(*surv_s_all)[kFastTok * kFastSurv] =
-        reinterpret_cast<uint32_t(*)[kFastTok * kFastSurv]>(lds);
-    uint32_t(*surv_i_all)[kFastTok * kFastSurv] = surv_s_all + kFastWaves;
+    uint32_t(*surv_s_all)[kFastTok * kSurvStride] =
+        reinterpret_cast<uint32_t(*)[kFastTok * kSurvStride]>(lds);
+    uint32_t(*surv_i_all)[kFastTok * kSurvStride] = surv_s_all + kFastWaves;
 
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
@@ -149,8 +150,8 @@ __global__ __launch_bounds__(kFastWaves *kWave) void fwd_topk_half_kernel(
     const int h = blockIdx.y, s = blockIdx.z;
     const int64_t t = (int64_t)blockIdx.x * kFastTokWG + wave * kFastTok + tok;
     const bool live = t < T;
-    uint32_t *surv_s = surv_s_all[wave] + tok * kFastSurv;
-    uint32_t *surv_i = surv_i_all[wave] + tok * kFastSurv;
+    uint32_t *surv_s = surv_s_all[wave] + tok * kSurvStride;
+    uint32_t *surv_i = surv_i_all[wave] + tok * kSurvStride;
     uint64_t *prev = s_prev[wave][tok];
 
     const uint16_t *qrow = reinterpret_cast<const uint16_t *>(q) +
@@ -296,19 +297,22 @@ __global__ __launch_bounds__(kFastWaves *kWave) void fwd_topk_half_kernel(
                 }
             mine = c;
         }
+        // Lane group g writes its survivors from position g + (the counts of
+        // the groups before it): every candidate is stored at the next free
+        // position, which only a kept one claims, so the writes need no
+        // branches; the last unclaimed store lands in the spare slot that
+        // ends the group's range.
         const int c0 = __shfl(mine, tok), c1 = __shfl(mine, tok + 16), c2 = __shfl(mine, tok + 32);
-        int off = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
+        int off = g + (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
 #pragma unroll
         for (int j = 0; j < kFastTiles; ++j) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t o = so[j][i];
                 const bool keep = exact ? (o > kth || (o == kth && 16 * j + i <= lim_t)) : o >= kth;
-                if (keep) {
-                    surv_s[off] = o;
-                    surv_i[off] = (uint32_t)(16 * j + i);
-                    ++off;
-                }
+                surv_s[off] = o;
+                surv_i[off] = (uint32_t)(16 * j + i);
+                off += keep ? 1 : 0;
             }
             __builtin_amdgcn_sched_barrier(0);     // one tile's keys at a time
         }
@@ -317,11 +321,12 @@ __global__ __launch_bounds__(kFastWaves *kWave) void fwd_topk_half_kernel(
         uint64_t v[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
+            // survivor e was written by lane group src_g, at position e + src_g
             const int e = 16 * g + r;
-            const uint32_t src_g = (e >= b1 ? 1u : 0u) + (e >= b2 ? 1u : 0u) + (e >= b3 ? 1u : 0u);
-            v[r] = e < total
-                       ? ((uint64_t)surv_s[e] << 32) | (uint64_t)~(surv_i[e] + 4u * src_g + (uint32_t)base)
-                       : 0ull;
+            const int src_g = (e >= b1 ? 1 : 0) + (e >= b2 ? 1 : 0) + (e >= b3 ? 1 : 0);
+            v[r] = e < total ? ((uint64_t)surv_s[e + src_g] << 32) |
+                                   (uint64_t)~(surv_i[e + src_g] + 4u * (uint32_t)src_g + (uint32_t)base)
+                             : 0ull;
         }
         group4_sort_desc<16>(v);
         // lane group g holds ranks 16 g .. 16 g + 15 of the block

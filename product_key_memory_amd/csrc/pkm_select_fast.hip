@@ -397,12 +397,28 @@ __global__ __launch_bounds__(kFastWaves *kWave) void fwd_topk_half_kernel(
 }
 
 // The combine and the softmax per (token, head) row from the two lists.
+// First a lower bound on the k-th best combined score prunes the candidates:
+// the set S = {(a, b) : (a + 1)(b + 1) <= m}, m the least value with |S| >= k,
+// holds at least k candidates, so the k-th best score is at least the least
+// score in S -- the least of its corner scores s(a, m / (a + 1) - 1), as the
+// lists are sorted and rounding is monotone.  When no row of the wave keeps
+// more than kMergeSurv candidates, the survivors are compacted into LDS and
+// sorted 64 per row; otherwise every candidate is sorted, 128 per row.
+constexpr int kMaxCorners = 16;
+constexpr int kMergeSurv = 60;      // + a spare slot per lane group: < 64 per row
+
+__device__ __forceinline__ float merge_score(uint2 l, uint2 r)
+{
+    return unord_f32(l.x) + unord_f32(r.x);
+}
+
 __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
-    const uint2 *__restrict__ lists, int64_t rows, int n, int k, int n_pairs,
+    const uint2 *__restrict__ lists, int64_t rows, int n, int k, int n_pairs, int m,
     int32_t *__restrict__ idx, float *__restrict__ weights, float *__restrict__ scores)
 {
     __shared__ uint2 s_list[kMergeWaves][kMergeRows * 2 * 32];
     __shared__ uint16_t s_pairs[kMaxPairs];
+    __shared__ uint16_t s_corner[kMaxCorners];
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
     const int tok = lane & 15, g = lane >> 4;
@@ -412,6 +428,8 @@ __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
         const int start = wave_exclusive_scan(cnt, &total);
         for (int b = 0; b < cnt; ++b)
             s_pairs[start + b] = (uint16_t)(lane | (b << 8));
+        if (lane < m)
+            s_corner[lane] = (uint16_t)(lane | ((m / (lane + 1) - 1) << 8));
     }
     // the wave's rows are contiguous in the lists: stage them in LDS, all
     // 16-byte loads in flight before the first store
@@ -441,39 +459,149 @@ __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
     const bool live = tok < nrows;
     const uint2 *l = sl + tok * 2 * k;
     const uint2 *r = l + k;
+
+    // the bound: least corner score of the row (lane group g takes corners
+    // g, g + 4, ...), as an order-preserving key
+    float tau = INFINITY;
+#pragma unroll
+    for (int c0 = 0; c0 < kMaxCorners; c0 += 4) {
+        const int c = c0 + g;
+        if (c < m) {
+            const int a = s_corner[c] & 0xFF, b = s_corner[c] >> 8;
+            tau = fminf(tau, merge_score(l[a], r[b]));
+        }
+    }
+    tau = fminf(tau, __shfl_xor(tau, 16));
+    tau = fminf(tau, __shfl_xor(tau, 32));
+    uint32_t otau = ord_f32(tau);
+
     uint64_t v[32];
+    int cnt = 0;
 #pragma unroll
     for (int c = 0; c < 32; ++c) {
         const int pc = 32 * g + c;
         if (live && pc < n_pairs) {
             const int a = s_pairs[pc] & 0xFF, b = s_pairs[pc] >> 8;
             const uint2 la = l[a], rb = r[b];
-            v[c] = make_key(unord_f32(la.x) + unord_f32(rb.x), la.y * (uint32_t)n + rb.y);
+            v[c] = make_key(merge_score(la, rb), la.y * (uint32_t)n + rb.y);
         } else {
             v[c] = 0ull;
         }
+        cnt += (uint32_t)(v[c] >> 32) >= otau ? 1 : 0;
     }
-    group4_sort_desc<32>(v);
-    // the k <= 32 winners are registers 0..k-1 of the group's first lane
-    if (live && g == 0) {
-        const float top = key_score(v[0]);
-        float e[32], z = 0.f;
+    if (!live)
+        cnt = 0;        // rows past the end keep nothing
+    int total = group4_sum(cnt);
+    auto count_ge = [&](uint32_t o) {
+        int c = 0;
 #pragma unroll
-        for (int c = 0; c < 32; ++c) {
-            e[c] = c < k ? expf(key_score(v[c]) - top) : 0.f;
-            z += e[c];
-        }
-        const int64_t out = (row0 + tok) * (int64_t)k;
-#pragma unroll
-        for (int c = 0; c < 32; ++c) {
-            if (c < k) {
-                idx[out + c] = (int32_t)key_index(v[c]);
-                weights[out + c] = e[c] / z;
-                if (scores)
-                    scores[out + c] = key_score(v[c]);
+        for (int e = 0; e < 32; ++e)
+            c += (uint32_t)(v[e] >> 32) >= o ? 1 : 0;
+        return c;
+    };
+    // Raise the bound while more than kMergeSurv survive: bisection on the
+    // score between the bound (>= k survive) and the best pair (0, 0).
+    {
+        float lo = tau, hi = merge_score(l[0], r[0]);
+        for (int it = 0; it < 8; ++it) {
+            const bool more = live && total > kMergeSurv;
+            if (__ballot(more) == 0)
+                break;
+            const float mid = lo + 0.5f * (hi - lo);
+            const uint32_t om = ord_f32(mid);
+            const int c_mid = count_ge(om);
+            const int t_mid = group4_sum(c_mid);
+            if (more && t_mid >= k) {
+                lo = mid;
+                otau = om;
+                cnt = c_mid;
+                total = t_mid;
+            } else if (more) {
+                hi = mid;
             }
         }
     }
+    // Rows still above (heavy ties): the exact k-th largest key by bisection
+    // on the 64-bit keys, which are distinct (the slot is part of the key);
+    // exactly k keys are >= it.
+    uint64_t kth = live ? (uint64_t)otau << 32 : ~0ull;
+    if (__ballot(live && total > kMergeSurv) != 0) {
+        const bool more = live && total > kMergeSurv;
+        uint64_t K = 0;
+        for (int bit = 63; bit >= 0; --bit) {
+            const uint64_t cand = K | (1ull << bit);
+            int c = 0;
+#pragma unroll
+            for (int e = 0; e < 32; ++e)
+                c += v[e] >= cand ? 1 : 0;
+            if (group4_sum(c) >= k)
+                K = cand;
+        }
+        if (more) {
+            kth = K;
+            int c = 0;
+#pragma unroll
+            for (int e = 0; e < 32; ++e)
+                c += v[e] >= K ? 1 : 0;
+            cnt = c;
+            total = k;
+        }
+    }
+
+    // The survivors (key >= kth) go to this wave's list area, free once every
+    // lane has its candidates: 64 slots per row.  Lane group g writes from
+    // position g + (the counts of the groups before it), every candidate at
+    // the next free slot, which only a kept one claims.
+    wave_lds_sync();
+    uint64_t *surv = reinterpret_cast<uint64_t *>(sl) + tok * 64;
+    const int c0 = __shfl(cnt, tok), c1 = __shfl(cnt, tok + 16), c2 = __shfl(cnt, tok + 32);
+    int off = g + (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+        surv[off] = v[c];
+        off += live && v[c] >= kth ? 1 : 0;
+    }
+    wave_lds_sync();
+    const int b1 = c0, b2 = c0 + c1, b3 = c0 + c1 + c2;
+    uint64_t w[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int e = 16 * g + q;
+        const int src_g = (e >= b1 ? 1 : 0) + (e >= b2 ? 1 : 0) + (e >= b3 ? 1 : 0);
+        w[q] = live && e < total ? surv[e + src_g] : 0ull;
+    }
+    group4_sort_desc<16>(w);
+
+    // ranks 16 g + q sit in lane groups 0 and 1; the softmax sums both
+    const int64_t out = (row0 + tok) * (int64_t)k;
+    const float top = __shfl(key_score(w[0]), tok);
+    float ex[16], z = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        ex[q] = 16 * g + q < k ? expf(key_score(w[q]) - top) : 0.f;
+        z += ex[q];
+    }
+    z += __shfl_xor(z, 16);
+    if (live && g < 2) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int e = 16 * g + q;
+            if (e < k) {
+                idx[out + e] = (int32_t)key_index(w[q]);
+                weights[out + e] = ex[q] / z;
+                if (scores)
+                    scores[out + e] = key_score(w[q]);
+            }
+        }
+    }
+}
+
+// The least m with |{(a, b) : (a + 1)(b + 1) <= m}| = sum_a floor(m / a) >= k.
+static int merge_bound_size(int k)
+{
+    for (int m = 1;; ++m)
+        if (merge_candidates(m) >= k)
+            return m;
 }
 
 hipError_t launch_select_fast(const void *q, const void *keys, int64_t T, int H, int n, int k,
@@ -498,7 +626,7 @@ hipError_t launch_select_fast(const void *q, const void *keys, int64_t T, int H,
     const int64_t per_block = (int64_t)kMergeWaves * kMergeRows;
     hipLaunchKernelGGL(fwd_merge_kernel, dim3((unsigned)((rows + per_block - 1) / per_block)),
                        dim3(kMergeWaves * kWave), 0, stream, lists, rows, n, k,
-                       merge_candidates(k), idx, weights, scores);
+                       merge_candidates(k), merge_bound_size(k), idx, weights, scores);
     return hipGetLastError();
 }
 

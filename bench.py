@@ -37,7 +37,7 @@ def parse():
                     help="tokens of the same workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="first run 3 plain elementwise copies of 256 MiB (x * 2), whose "
+                    help="first run 3 plain elementwise copies of 256 MiB (bitwise not), whose "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate those of the kernels")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="no GPU work: read the rocprofv3 databases of a FETCH_SIZE run and a "
@@ -122,21 +122,33 @@ def _counter_means(db: str, counter: str) -> dict:
     return {name: (float(avg), int(cnt)) for name, avg, cnt in rows}
 
 
+def _calibration_values(db: str, counter: str) -> list:
+    """Per-dispatch values of `counter` for the calibration copy (the only
+    bitwise-not kernel the bench runs)."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute("select value from counters_collection where counter_name = ? and "
+                       "kernel_name like '%bitwise_not%'", (counter,)).fetchall()
+    con.close()
+    return sorted(float(v) for (v,) in rows)
+
+
 def record_traffic(fetch_db: str, write_db: str, workload: str) -> str:
     """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of every stage's kernels,
     each scaled by the ratio of the known size of the calibration copy
-    (x * 2 over 64 Mi floats: 256 MiB read, 256 MiB written) to what the same
-    counter read for it; summed per stage: bytes per launch of the stage."""
+    (bitwise not over 64 Mi int32: 256 MiB read, 256 MiB written) to the
+    median of what the same counter read for its dispatches; summed per stage:
+    bytes per launch of the stage."""
     fetch, write = _counter_means(fetch_db, "FETCH_SIZE"), _counter_means(write_db, "WRITE_SIZE")
     copy_kib = 256 * 1024
 
-    def calib(table):
-        cands = [v for name, (v, _) in table.items() if "MulFunctor" in name and v > copy_kib / 4]
-        if not cands:
+    def calib(db, counter):
+        vals = _calibration_values(db, counter)
+        if not vals:
             raise SystemExit("no calibration copy in the database (run bench.py --calibrate-copy)")
-        return copy_kib / max(cands)
+        return copy_kib / vals[len(vals) // 2]
 
-    f_fac, w_fac = calib(fetch), calib(write)
+    f_fac, w_fac = calib(fetch_db, "FETCH_SIZE"), calib(write_db, "WRITE_SIZE")
     stages = {}
     for stage, prefixes in STAGE_KERNELS.items():
         rec = {"read_bytes": 0, "write_bytes": 0, "kernels": {}}
@@ -339,11 +351,12 @@ def main():
 
     if args.calibrate_copy:
         # a plain elementwise kernel of known size (reads 256 MiB, writes 256 MiB,
-        # 16-byte accesses like the layer's own kernels)
-        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        # 16-byte accesses like the layer's own kernels), of a kind the bench
+        # runs nowhere else, so its dispatches are easy to find
+        src = torch.ones(64 << 20, dtype=torch.int32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            torch.mul(src, 2.0, out=dst)
+            torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 

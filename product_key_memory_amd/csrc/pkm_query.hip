@@ -363,54 +363,85 @@ __global__ __launch_bounds__(kBnWaves *kWave) void bn_partial_kernel(const float
     }
 }
 
+// Chan's merge of (count, mean, M2) b into a, in double.
+__device__ __forceinline__ void chan_merge(double &N, double &M, double &S, double nb, double mb,
+                                           double sb)
+{
+    if (nb == 0.0)
+        return;
+    const double nt = N + nb, d = mb - M;
+    M += d * (nb / nt);
+    S += sb + d * d * (N * nb / nt);
+    N = nt;
+}
+
+// One wave per column: lane l merges chunks l, l + 64, ..., then a butterfly
+// merges the lanes.
 __global__ void bn_finalize_kernel(const float *__restrict__ part, int chunks, int D, float eps,
                                    float *__restrict__ mean_out, float *__restrict__ rstd_out)
 {
-    const int col = blockIdx.x * blockDim.x + threadIdx.x;
+    const int lane = lane_id();
+    const int col = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     if (col >= D)
         return;
     double N = 0.0, M = 0.0, S = 0.0;
-    for (int c = 0; c < chunks; ++c) {
+    for (int c = lane; c < chunks; c += kWave) {
         const float *p = part + ((int64_t)c * D + col) * 3;
-        const double nb = p[0];
-        if (nb == 0.0)
-            continue;
-        const double nt = N + nb, d = (double)p[1] - M;
-        M += d * (nb / nt);
-        S += (double)p[2] + d * d * (N * nb / nt);
-        N = nt;
+        chan_merge(N, M, S, p[0], p[1], p[2]);
     }
-    const double var = N > 0.0 ? S / N : 0.0;
-    mean_out[col] = (float)M;
-    rstd_out[col] = (float)(1.0 / sqrt(var + (double)eps));
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+        const double nb = __shfl_xor(N, m), mb = __shfl_xor(M, m), sb = __shfl_xor(S, m);
+        chan_merge(N, M, S, nb, mb, sb);
+    }
+    if (lane == 0) {
+        const double var = N > 0.0 ? S / N : 0.0;
+        mean_out[col] = (float)M;
+        rstd_out[col] = (float)(1.0 / sqrt(var + (double)eps));
+    }
 }
 
-// q = gamma (z - mean) rstd + beta, 4 columns per thread, rounded once.
+// q = gamma (z - mean) rstd + beta, rounded once.  A thread owns 4 columns
+// (blockIdx.x picks 1024 of them) and walks the rows blockIdx.y, + gridDim.y,
+// ...: its columns' constants are loaded once.
+constexpr int kBnApplyRows = 2048;      // gridDim.y at most
+
 template <typename DT>
 __global__ void bn_apply_kernel(const float *__restrict__ z, int64_t T, int D,
                                 const float *__restrict__ mean, const float *__restrict__ rstd,
                                 const float *__restrict__ gamma, const float *__restrict__ beta,
                                 DT *__restrict__ q)
 {
-    const int64_t n4 = T * (int64_t)D / 4;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-        const int c = (int)((i * 4) % D);
-        const float4 v = reinterpret_cast<const float4 *>(z)[i];
+    const int c = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
+    if (c >= D)
+        return;
+    float a[4], o[4];        // y = a x + o with a = gamma rstd, o = beta - a mean
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float g = gamma ? gamma[c + e] : 1.f, b = beta ? beta[c + e] : 0.f;
+        a[e] = g;
+        o[e] = b;
+    }
+    float mu[4], rs[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        mu[e] = mean[c + e];
+        rs[e] = rstd[c + e];
+    }
+    for (int64_t r = blockIdx.y; r < T; r += gridDim.y) {
+        const float4 v = *reinterpret_cast<const float4 *>(z + r * D + c);
         const float x[4] = {v.x, v.y, v.z, v.w};
         float y[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float g = gamma ? gamma[c + e] : 1.f, b = beta ? beta[c + e] : 0.f;
-            y[e] = fmaf(g, (x[e] - mean[c + e]) * rstd[c + e], b);
-        }
+        for (int e = 0; e < 4; ++e)
+            y[e] = fmaf(a[e], (x[e] - mu[e]) * rs[e], o[e]);
         if constexpr (sizeof(DT) == 2) {
-            uint2 o;
-            o.x = f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
-            o.y = f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16);
-            reinterpret_cast<uint2 *>(q)[i] = o;
+            uint2 w;
+            w.x = f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
+            w.y = f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16);
+            *reinterpret_cast<uint2 *>(q + r * D + c) = w;
         } else {
-            reinterpret_cast<float4 *>(q)[i] = make_float4(y[0], y[1], y[2], y[3]);
+            *reinterpret_cast<float4 *>(q + r * D + c) = make_float4(y[0], y[1], y[2], y[3]);
         }
     }
 }
@@ -451,40 +482,66 @@ __global__ __launch_bounds__(kBnWaves *kWave) void bn_bwd_partial_kernel(
 }
 
 // dbeta = sum dq, dgamma = sum dq * zhat; coef = (sum dq / T, sum dq zhat / T).
+// One wave per column: lanes sum the chunks in double, then a butterfly.
 __global__ void bn_bwd_finalize_kernel(const float *__restrict__ part, int chunks, int D,
                                        int64_t T, float *__restrict__ coef,
                                        float *__restrict__ dgamma, float *__restrict__ dbeta)
 {
-    const int col = blockIdx.x * blockDim.x + threadIdx.x;
+    const int lane = lane_id();
+    const int col = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     if (col >= D)
         return;
     double a = 0.0, b = 0.0;
-    for (int c = 0; c < chunks; ++c) {
+    for (int c = lane; c < chunks; c += kWave) {
         a += part[((int64_t)c * D + col) * 2];
         b += part[((int64_t)c * D + col) * 2 + 1];
     }
-    coef[2 * col] = (float)(a / (double)T);
-    coef[2 * col + 1] = (float)(b / (double)T);
-    if (dbeta)
-        dbeta[col] = (float)a;
-    if (dgamma)
-        dgamma[col] = (float)b;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+        a += __shfl_xor(a, m);
+        b += __shfl_xor(b, m);
+    }
+    if (lane == 0) {
+        coef[2 * col] = (float)(a / (double)T);
+        coef[2 * col + 1] = (float)(b / (double)T);
+        if (dbeta)
+            dbeta[col] = (float)a;
+        if (dgamma)
+            dgamma[col] = (float)b;
+    }
 }
 
-// dz = gamma rstd (dq - mean(dq) - zhat mean(dq zhat)).
+// dz = gamma rstd (dq - mean(dq) - zhat mean(dq zhat)); laid out like
+// bn_apply_kernel: 4 columns per thread, rows strided by gridDim.y.
 __global__ void bn_bwd_apply_kernel(const float *__restrict__ z, const float *__restrict__ dq,
                                     int64_t T, int D, const float *__restrict__ mean,
                                     const float *__restrict__ rstd,
                                     const float *__restrict__ gamma,
                                     const float *__restrict__ coef, float *__restrict__ dz)
 {
-    const int64_t n = T * (int64_t)D;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-        const int c = (int)(i % D);
-        const float zh = (z[i] - mean[c]) * rstd[c];
-        const float g = gamma ? gamma[c] : 1.f;
-        dz[i] = g * rstd[c] * (dq[i] - coef[2 * c] - zh * coef[2 * c + 1]);
+    const int c = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
+    if (c >= D)
+        return;
+    float mu[4], rs[4], gr[4], c0[4], c1[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        mu[e] = mean[c + e];
+        rs[e] = rstd[c + e];
+        gr[e] = (gamma ? gamma[c + e] : 1.f) * rs[e];
+        c0[e] = coef[2 * (c + e)];
+        c1[e] = coef[2 * (c + e) + 1];
+    }
+    for (int64_t r = blockIdx.y; r < T; r += gridDim.y) {
+        const float4 zv = *reinterpret_cast<const float4 *>(z + r * D + c);
+        const float4 gv = *reinterpret_cast<const float4 *>(dq + r * D + c);
+        const float zz[4] = {zv.x, zv.y, zv.z, zv.w}, gg[4] = {gv.x, gv.y, gv.z, gv.w};
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float zh = (zz[e] - mu[e]) * rs[e];
+            o[e] = gr[e] * (gg[e] - c0[e] - zh * c1[e]);
+        }
+        *reinterpret_cast<float4 *>(dz + r * D + c) = make_float4(o[0], o[1], o[2], o[3]);
     }
 }
 
@@ -526,10 +583,12 @@ int dw_splits(int64_t T, int d_model, int D)
     return (int)(s < 1 ? 1 : s);
 }
 
-static unsigned elem_grid(int64_t n)
+// bn_apply / bn_bwd_apply: 1024 columns per workgroup along x, row groups
+// along y (T > 0)
+static dim3 bn_rows_grid(int64_t T, int D)
 {
-    const int64_t b = (n + 255) / 256;
-    return (unsigned)(b < 8192 ? b : 8192);
+    const int64_t rows = T < kBnApplyRows ? T : kBnApplyRows;
+    return dim3((unsigned)((D + 1023) / 1024), (unsigned)rows);
 }
 
 template <typename DT>
@@ -546,10 +605,10 @@ static hipError_t query_forward_t(const DT *x, const DT *W, const float *gamma, 
         return err;
     hipLaunchKernelGGL(bn_partial_kernel, dim3((unsigned)((D + kBnCols - 1) / kBnCols), (unsigned)S.chunks),
                        dim3(kBnWaves * kWave), 0, stream, z, T, D, S.rows_per_chunk, part);
-    hipLaunchKernelGGL(bn_finalize_kernel, dim3((unsigned)((D + 255) / 256)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(bn_finalize_kernel, dim3((unsigned)((D + 3) / 4)), dim3(4 * kWave), 0, stream,
                        part, S.chunks, D, eps, mean, rstd);
-    hipLaunchKernelGGL((bn_apply_kernel<DT>), dim3(elem_grid(T * D / 4)), dim3(256), 0, stream, z,
-                       T, D, mean, rstd, gamma, beta, q);
+    hipLaunchKernelGGL((bn_apply_kernel<DT>), bn_rows_grid(T, D), dim3(256), 0, stream, z, T, D,
+                       mean, rstd, gamma, beta, q);
     return hipGetLastError();
 }
 
@@ -572,10 +631,10 @@ static hipError_t query_backward_t(const DT *x, const DT *W, const float *gamma,
     hipLaunchKernelGGL(bn_bwd_partial_kernel, dim3((unsigned)((D + kBnCols - 1) / kBnCols), (unsigned)S.chunks),
                        dim3(kBnWaves * kWave), 0, stream, z, dq, T, D, mean, rstd,
                        S.rows_per_chunk, part);
-    hipLaunchKernelGGL(bn_bwd_finalize_kernel, dim3((unsigned)((D + 255) / 256)), dim3(256), 0,
+    hipLaunchKernelGGL(bn_bwd_finalize_kernel, dim3((unsigned)((D + 3) / 4)), dim3(4 * kWave), 0,
                        stream, part, S.chunks, D, T, coef, dgamma, dbeta);
-    hipLaunchKernelGGL(bn_bwd_apply_kernel, dim3(elem_grid(T * D)), dim3(256), 0, stream, z, dq, T,
-                       D, mean, rstd, gamma, coef, dz);
+    hipLaunchKernelGGL(bn_bwd_apply_kernel, bn_rows_grid(T, D), dim3(256), 0, stream, z, dq, T, D,
+                       mean, rstd, gamma, coef, dz);
     hipError_t err = hipGetLastError();
     // every GEMM operand K-contiguous: W^T [d_model][D], x^T [d_model][T], dz^T [D][T]
     if (err == hipSuccess)

@@ -286,32 +286,44 @@ static hipError_t gemm(const TA *A, const TB *B, float *Cm, int M, int N, int K,
 }
 
 // out[c][r] = in[r][c] for an R x C matrix of 2- or 4-byte elements, through
-// 64 x 64 LDS tiles (both sides coalesced).
+// 64 x 64 LDS tiles (both sides coalesced); out rows have pitch ldo >= R and
+// their tail r in [R, ldo) is written with zeros.
 template <typename E>
 __global__ __launch_bounds__(256) void transpose_kernel(const E *__restrict__ in, E *__restrict__ out,
-                                                        int64_t R, int64_t C)
+                                                        int64_t R, int64_t C, int64_t ldo)
 {
     __shared__ E tile[64][65];
     const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
     const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
     for (int i = ty; i < 64; i += 4) {
         const int64_t r = r0 + i, c = c0 + tx;
-        if (r < R && c < C)
-            tile[i][tx] = in[r * C + c];
+        tile[i][tx] = (r < R && c < C) ? in[r * C + c] : (E)0;
     }
     __syncthreads();
     for (int i = ty; i < 64; i += 4) {
         const int64_t c = c0 + i, r = r0 + tx;
-        if (r < R && c < C)
-            out[c * R + r] = tile[tx][i];
+        if (r < ldo && c < C)
+            out[c * ldo + r] = tile[tx][i];
     }
 }
 
-template <typename E>
-static hipError_t transpose(const E *in, E *out, int64_t R, int64_t C, hipStream_t stream)
+// K of the GEMM that runs over the tokens (dW = dz^T x): the token count
+// rounded up to 8, so that every 16-byte piece of a transposed row (8 bf16 or
+// 4 float32 elements) lies inside the row and is 16-byte aligned; the padding
+// holds zeros.
+static int64_t token_pitch(int64_t T)
 {
-    const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
-    hipLaunchKernelGGL((transpose_kernel<E>), grid, dim3(256), 0, stream, in, out, R, C);
+    return (T + 7) & ~(int64_t)7;
+}
+
+template <typename E>
+static hipError_t transpose(const E *in, E *out, int64_t R, int64_t C, hipStream_t stream,
+                            int64_t ldo = -1)
+{
+    if (ldo < 0)
+        ldo = R;
+    const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((ldo + 63) / 64));
+    hipLaunchKernelGGL((transpose_kernel<E>), grid, dim3(256), 0, stream, in, out, R, C, ldo);
     return hipGetLastError();
 }
 
@@ -561,11 +573,12 @@ QueryScratch query_scratch(int64_t T, int d_model, int D, int backward, int elt)
     auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
     S.off_part = 0;
     S.off_coef = a256((size_t)chunks * D * 3 * 4);
+    const int64_t Tp = token_pitch(T);
     S.off_dz = a256(S.off_coef + (size_t)D * 2 * 4);
     S.off_dzt = a256(S.off_dz + (size_t)T * D * 4);
-    S.off_wt = a256(S.off_dzt + (size_t)T * D * 4);
+    S.off_wt = a256(S.off_dzt + (size_t)Tp * D * 4);
     S.off_xt = a256(S.off_wt + (size_t)D * d_model * elt);
-    S.off_dwp = a256(S.off_xt + (size_t)T * d_model * elt);
+    S.off_dwp = a256(S.off_xt + (size_t)Tp * d_model * elt);
     S.dw_splits = dw_splits(T, d_model, D);
     S.total = backward ? a256(S.off_dwp + (size_t)S.dw_splits * D * d_model * 4) : S.off_coef;
     return S;
@@ -627,6 +640,7 @@ static hipError_t query_backward_t(const DT *x, const DT *W, const float *gamma,
     DT *Wt = reinterpret_cast<DT *>(base + S.off_wt);
     DT *xt = reinterpret_cast<DT *>(base + S.off_xt);
     float *dwp = reinterpret_cast<float *>(base + S.off_dwp);
+    const int64_t Tp = token_pitch(T);
     typedef typename std::conditional<sizeof(DT) == 2, uint16_t, float>::type E;
     hipLaunchKernelGGL(bn_bwd_partial_kernel, dim3((unsigned)((D + kBnCols - 1) / kBnCols), (unsigned)S.chunks),
                        dim3(kBnWaves * kWave), 0, stream, z, dq, T, D, mean, rstd,
@@ -640,9 +654,10 @@ static hipError_t query_backward_t(const DT *x, const DT *W, const float *gamma,
     if (err == hipSuccess)
         err = transpose<E>(reinterpret_cast<const E *>(W), reinterpret_cast<E *>(Wt), D, d_model, stream);
     if (err == hipSuccess)
-        err = transpose<E>(reinterpret_cast<const E *>(x), reinterpret_cast<E *>(xt), T, d_model, stream);
+        err = transpose<E>(reinterpret_cast<const E *>(x), reinterpret_cast<E *>(xt), T, d_model, stream,
+                           Tp);
     if (err == hipSuccess)
-        err = transpose<float>(dz, dzt, T, D, stream);
+        err = transpose<float>(dz, dzt, T, D, stream, Tp);
     if (err != hipSuccess)
         return err;
     constexpr int MODE = sizeof(DT) == 2 ? kBf16SplitA : kF32;
@@ -650,8 +665,9 @@ static hipError_t query_backward_t(const DT *x, const DT *W, const float *gamma,
     err = gemm<float, DT, false, false, MODE>(dz, Wt, dx, (int)T, d_model, D, D, D, stream);
     if (err != hipSuccess)
         return err;
-    // dW [D][d_model] = dz^T [D][T] . (x^T)^T, K = T cut into slices
-    return gemm<float, DT, false, false, MODE>(dzt, xt, dW, D, d_model, (int)T, T, T, stream,
+    // dW [D][d_model] = dz^T [D][Tp] . (x^T)^T, K = Tp (zero-padded tokens) cut
+    // into slices
+    return gemm<float, DT, false, false, MODE>(dzt, xt, dW, D, d_model, (int)Tp, Tp, Tp, stream,
                                                S.dw_splits, dwp);
 }
 

@@ -210,6 +210,45 @@ def measure_extras(torch, _lib, p, values, dvalues, slot_start, w, elt, touched,
     return out
 
 
+def measure_fused_sgd(torch, _lib, p, bufs, ws, ws_bytes, stream) -> dict:
+    """The training backward with its value update: pkm_backward (dvalues
+    overwritten) then pkm_sparse_sgd, against pkm_backward_sgd (the update
+    fused into the value side, no dvalues array); event time per call over 5
+    calls after 2 warm-up calls, on the step's inputs (the values drift by
+    lr = 1e-3 per call, the selection is the step's)."""
+    q, keys, values, idx, wts, dy, dq, dkeys, dvalues = bufs
+    sp = stream.cuda_stream
+    P = lambda t: t.data_ptr()  # noqa: E731
+    fws_bytes = _lib.workspace_bytes(p, 2)
+    fws = torch.empty(max(fws_bytes, 1), dtype=torch.uint8, device=values.device)
+
+    # the update reads the backward's own slot sort: slot_start follows the
+    # T*H*k floats of dw in its workspace, rounded up to 256 bytes
+    starts = P(ws) + ((p.T * p.H * p.k * 4 + 255) // 256) * 256
+
+    def chain():
+        rc = _lib.backward(p, P(q), P(keys), P(values), P(idx), P(wts), P(dy), P(dq), P(dkeys),
+                           P(dvalues), 0, P(ws), ws_bytes, sp)
+        return rc | _lib.sparse_sgd(p, P(values), P(dvalues), starts, 1e-3, sp)
+
+    def fused():
+        return _lib.backward_sgd(p, P(q), P(keys), P(values), P(idx), P(wts), P(dy), P(dq),
+                                 P(dkeys), 1e-3, P(fws), fws_bytes, sp)
+
+    out = {}
+    for name, fn in (("backward_then_sgd", chain), ("backward_sgd_fused", fused)):
+        for _ in range(2):
+            assert fn() == 0, name
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = {"ms": round(e0.elapsed_time(e1) / 5, 5)}
+    return out
+
+
 def measure_query_net(torch, _lib, w, dq, stream, d_model: int = 1600) -> dict:
     """The query network q = BN(x W^T) in front of the layer (not part of the
     step, whose q is given): x [T][1600] (the pages' model width) and
@@ -400,6 +439,8 @@ def main():
         kernels[name] = entry
 
     extras = measure_extras(torch, _lib, p, values, dvalues, slot_start, w, elt, touched, stream)
+    extras.update(measure_fused_sgd(torch, _lib, p, (q, keys, values, idx, wts, dy, dq, dkeys,
+                                                     dvalues), ws, ws_bytes, stream))
     query_net = measure_query_net(torch, _lib, w, dq, stream)
 
     dominant = max(STAGES, key=lambda s: per_stage[s])

@@ -71,10 +71,11 @@ typedef struct {
     int32_t dtype;  /* pkm_dtype_t                                            */
 } pkm_problem_t;
 
-/* Bytes of device workspace pkm_forward and pkm_forward_select (backward = 0)
- * or pkm_backward and its stages (backward = 1) need for this problem; 0 if
- * none (the workspace may then be NULL).  Returns (size_t)-1 for an invalid
- * descriptor.  The forward needs workspace only on its two-kernel selection
+/* Bytes of device workspace pkm_forward and pkm_forward_select (backward = 0),
+ * pkm_backward and its stages (backward = 1) or pkm_backward_sgd
+ * (backward = 2) need for this problem; 0 if none (the workspace may then be
+ * NULL).  Returns (size_t)-1 for an invalid descriptor or another value of
+ * `backward`.  The forward needs workspace only on its two-kernel selection
  * path (bf16, d_k = 512, 256 < n <= 1024, k <= 32): T*H*2*k*8 bytes rounded up
  * to 256, for the per-half top-k lists. */
 size_t pkm_workspace_bytes(const pkm_problem_t *p, int backward);
@@ -138,6 +139,28 @@ pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *key
                           const void *dy, float *dq, float *dkeys, float *dvalues,
                           int dvalues_accumulate, void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/*
+ * The backward with the sparse SGD step fused in (gptget.net summary,
+ * "Methodology": trained with sparse updates, only the selected memory slots
+ * change): dq and dkeys exactly as pkm_backward, and instead of dvalues the
+ * value rows themselves are updated in place -- every row f some pick
+ * selected becomes values[f] = fmaf(-lr, g[f], values[f]) rounded once to the
+ * storage type, g[f] being the float32 row pkm_backward would write to
+ * dvalues; rows no pick selected are left as they are.  The same result as
+ * pkm_backward (dvalues overwritten) followed by pkm_sparse_sgd, without the
+ * n*n x d_v float32 gradient array: each row's sum is applied where it is
+ * formed (rows with more than 256 picks go through a workspace buffer).
+ *   values    [n*n][d_v]  dtype, IN/OUT
+ *   lr        the learning rate; finite, else PKM_ERR_ARG
+ *   workspace pkm_workspace_bytes(p, 2) bytes
+ * Other arguments as pkm_backward.  dw is computed from the values as they
+ * were on entry.
+ */
+pkm_status_t pkm_backward_sgd(const pkm_problem_t *p, const void *q, const void *keys,
+                              void *values, const int32_t *idx, const float *weights,
+                              const void *dy, float *dq, float *dkeys, float lr, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
 /*
  * The two passes above, stage by stage, for callers that keep the

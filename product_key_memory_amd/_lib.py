@@ -27,7 +27,8 @@ STATUS = {
 }
 
 # every symbol include/pkm.h declares
-EXPORTS = ("pkm_workspace_bytes", "pkm_forward", "pkm_backward", "pkm_forward_select",
+EXPORTS = ("pkm_workspace_bytes", "pkm_forward", "pkm_backward", "pkm_backward_sgd",
+           "pkm_forward_select",
            "pkm_forward_gather", "pkm_slot_sort", "pkm_backward_values", "pkm_backward_queries",
            "pkm_sparse_sgd", "pkm_sparse_adam", "pkm_slot_usage", "pkm_query_workspace_bytes",
            "pkm_query_forward", "pkm_query_backward", "pkm_status_string")
@@ -71,6 +72,9 @@ def lib() -> ctypes.CDLL:
         L.pkm_backward.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P,
                                    ctypes.c_int, P, c_size, P]
         L.pkm_backward.restype = ctypes.c_int
+        L.pkm_backward_sgd.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P,
+                                       ctypes.c_float, P, c_size, P]
+        L.pkm_backward_sgd.restype = ctypes.c_int
         PP = ctypes.POINTER(Problem)
         L.pkm_forward_select.argtypes = [PP, P, P, P, P, P, P, c_size, P]
         L.pkm_forward_gather.argtypes = [PP, P, P, P, P, P]
@@ -101,7 +105,8 @@ def status_string(code: int) -> str:
     return lib().pkm_status_string(code).decode()
 
 
-def workspace_bytes(p: Problem, backward: bool) -> int:
+def workspace_bytes(p: Problem, backward) -> int:
+    """backward: 0 (forward), 1 (backward and its stages), 2 (backward_sgd)."""
     return int(lib().pkm_workspace_bytes(ctypes.byref(p), int(backward)))
 
 
@@ -114,6 +119,12 @@ def backward(p: Problem, q, keys, values, idx, weights, dy, dq, dkeys, dvalues, 
              ws, ws_bytes, stream) -> int:
     return lib().pkm_backward(ctypes.byref(p), q, keys, values, idx, weights, dy, dq, dkeys,
                               dvalues, int(accumulate), ws, ws_bytes, stream)
+
+
+def backward_sgd(p: Problem, q, keys, values, idx, weights, dy, dq, dkeys, lr, ws, ws_bytes,
+                 stream) -> int:
+    return lib().pkm_backward_sgd(ctypes.byref(p), q, keys, values, idx, weights, dy, dq, dkeys,
+                                  float(lr), ws, ws_bytes, stream)
 
 
 def forward_select(p: Problem, q, keys, idx, weights, scores, ws, ws_bytes, stream) -> int:

@@ -59,6 +59,16 @@ size_t backward_bytes(const pkm_problem_t *p)
     return picks_bytes(p) + starts_bytes(p) + picks_bytes(p) + stage_scratch_bytes(p);
 }
 
+// pkm_backward_sgd: the same head; the stages' scratch also holds the sums
+// of the long runs while the value side runs (slot sort before, query side
+// after: the three never overlap).
+size_t backward_sgd_bytes(const pkm_problem_t *p)
+{
+    const size_t split = pkm::split_rows_bytes(p->T * p->H * p->k, p->d_v);
+    const size_t stage = stage_scratch_bytes(p);
+    return picks_bytes(p) + starts_bytes(p) + picks_bytes(p) + (stage > split ? stage : split);
+}
+
 size_t forward_bytes(const pkm_problem_t *p)
 {
     return pkm::select_workspace_bytes(p->T, p->H, p->n, p->k, p->dtype, p->d_k);
@@ -81,9 +91,9 @@ extern "C" {
 
 size_t pkm_workspace_bytes(const pkm_problem_t *p, int backward)
 {
-    if (check_problem(p, backward != 0) != PKM_OK)
+    if (backward < 0 || backward > 2 || check_problem(p, backward != 0) != PKM_OK)
         return (size_t)-1;
-    return backward ? backward_bytes(p) : forward_bytes(p);
+    return backward == 2 ? backward_sgd_bytes(p) : backward ? backward_bytes(p) : forward_bytes(p);
 }
 
 pkm_status_t pkm_forward_select(const pkm_problem_t *p, const void *q, const void *keys,
@@ -272,6 +282,46 @@ pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *key
                              dvalues_accumulate, dw, stream);
     if (st != PKM_OK)
         return st;
+    return pkm_backward_queries(p, q, keys, idx, weights, dw, dq, dkeys, scratch, scratch_bytes,
+                                stream);
+}
+
+pkm_status_t pkm_backward_sgd(const pkm_problem_t *p, const void *q, const void *keys,
+                              void *values, const int32_t *idx, const float *weights,
+                              const void *dy, float *dq, float *dkeys, float lr, void *workspace,
+                              size_t workspace_bytes, void *stream)
+{
+    pkm_status_t st = check_problem(p, true);
+    if (st != PKM_OK)
+        return st;
+    const int64_t T = p->T;
+    if (missing(q, T) || !keys || !values || missing(idx, T) || missing(weights, T) ||
+        missing(dy, T) || missing(dq, T) || !dkeys)
+        return PKM_ERR_NULL;
+    if (!aligned16(q) || !aligned16(keys) || !aligned16(values) || !aligned16(idx) ||
+        !aligned16(weights) || !aligned16(dy) || !aligned16(dq) || !aligned16(dkeys))
+        return PKM_ERR_ALIGN;
+    if (!std::isfinite(lr))
+        return PKM_ERR_ARG;
+    st = check_workspace(p, workspace, workspace_bytes, backward_sgd_bytes(p));
+    if (st != PKM_OK)
+        return st;
+    char *base = static_cast<char *>(workspace);
+    float *dw = reinterpret_cast<float *>(base);
+    int32_t *slot_start = reinterpret_cast<int32_t *>(base + picks_bytes(p));
+    int32_t *order = reinterpret_cast<int32_t *>(base + picks_bytes(p) + starts_bytes(p));
+    const size_t head = 2 * picks_bytes(p) + starts_bytes(p);
+    void *scratch = T > 0 ? base + head : nullptr;
+    const size_t scratch_bytes = T > 0 ? workspace_bytes - head : 0;
+    if (T > 0) {
+        st = pkm_slot_sort(p, idx, slot_start, order, scratch, scratch_bytes, stream);
+        if (st != PKM_OK)
+            return st;
+        if (pkm::launch_bwd_value_sgd(p->dtype, values, idx, weights, dy, slot_start, order, lr,
+                                      static_cast<float *>(scratch), dw, T, p->H, p->n, p->k,
+                                      p->d_v, static_cast<hipStream_t>(stream)) != hipSuccess)
+            return PKM_ERR_HIP;
+    }
     return pkm_backward_queries(p, q, keys, idx, weights, dw, dq, dkeys, scratch, scratch_bytes,
                                 stream);
 }

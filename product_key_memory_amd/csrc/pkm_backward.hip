@@ -240,6 +240,66 @@ __global__ void dv_prepare_kernel(const int32_t *__restrict__ start, int64_t slo
     }
 }
 
+// The fused SGD: zero the split_acc rows of the runs longer than kSegChunk
+// (row start[f] / kSegChunk), before the segmented reduction adds into them.
+__global__ void split_prepare_kernel(const int32_t *__restrict__ start, int64_t slots, int d_v,
+                                     float *__restrict__ split_acc)
+{
+    const int lane = lane_id();
+    const int64_t f0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * kWave;
+    if (f0 >= slots)
+        return;
+    const int64_t f = f0 + lane;
+    const bool split = f < slots && start[f + 1] - start[f] > kSegChunk;
+    uint64_t todo = __ballot(split);
+    while (todo) {
+        const int i = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        float4 *row = reinterpret_cast<float4 *>(split_acc + (int64_t)(start[f0 + i] >> kSegShift) * d_v);
+        for (int c = lane; c < d_v / 4; c += kWave)
+            row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+// ... and afterwards apply those sums: w = fmaf(-lr, g, w), rounded once.
+template <typename DT>
+__global__ void split_apply_kernel(const int32_t *__restrict__ start, int64_t slots, int d_v,
+                                   const float *__restrict__ split_acc, DT *__restrict__ values,
+                                   float lr)
+{
+    constexpr int EPC = Elt<DT>::per16;
+    const int lane = lane_id();
+    const int64_t f0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * kWave;
+    if (f0 >= slots)
+        return;
+    const int64_t f = f0 + lane;
+    const bool split = f < slots && start[f + 1] - start[f] > kSegChunk;
+    uint64_t todo = __ballot(split);
+    while (todo) {
+        const int i = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        const float *g = split_acc + (int64_t)(start[f0 + i] >> kSegShift) * d_v;
+        DT *row = values + (f0 + i) * d_v;
+        for (int c = lane; c < d_v / EPC; c += kWave) {
+            float w[EPC];
+            unpack16(*reinterpret_cast<const uint4 *>(row + (int64_t)c * EPC), w);
+#pragma unroll
+            for (int e = 0; e < EPC; ++e)
+                w[e] = fmaf(-lr, g[c * EPC + e], w[e]);
+            if constexpr (sizeof(DT) == 2) {
+                uint4 r;
+                r.x = f32_to_bf16_bits(w[0]) | (f32_to_bf16_bits(w[1]) << 16);
+                r.y = f32_to_bf16_bits(w[2]) | (f32_to_bf16_bits(w[3]) << 16);
+                r.z = f32_to_bf16_bits(w[4]) | (f32_to_bf16_bits(w[5]) << 16);
+                r.w = f32_to_bf16_bits(w[6]) | (f32_to_bf16_bits(w[7]) << 16);
+                *reinterpret_cast<uint4 *>(row + (int64_t)c * EPC) = r;
+            } else {
+                *reinterpret_cast<float4 *>(row + (int64_t)c * EPC) = make_float4(w[0], w[1], w[2], w[3]);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // 2. segmented reduction over the slot-sorted picks
 // ---------------------------------------------------------------------------
@@ -329,12 +389,62 @@ __device__ __forceinline__ void seg_flush(float (&acc)[MCH][EPC], float *__restr
     }
 }
 
-template <typename DT, int MCH, int U>
+// The fused update: the run's sum g updates its value row in place,
+// w = fmaf(-lr, g, w) rounded once to the storage type (vrow holds the row's
+// old values), when the row is this wave's alone; a long run's pieces add
+// into its row of split_acc (row start[f] / kSegChunk: long runs hold more
+// than kSegChunk sorted picks, so their first positions differ in that
+// quotient), applied after the kernel.
+template <typename DT, int MCH, int EPC>
+__device__ __forceinline__ void seg_flush_sgd(float (&acc)[MCH][EPC], const float (&vrow)[MCH][EPC],
+                                              DT *values, float *__restrict__ split_acc,
+                                              const int32_t *__restrict__ start, int64_t f,
+                                              int d_v, int nchunks, int lane, bool exclusive,
+                                              float lr)
+{
+    const int64_t srow = exclusive ? 0 : (int64_t)(start[f] >> kSegShift);
+#pragma unroll
+    for (int m = 0; m < MCH; ++m) {
+        const int c = lane + m * kWave;
+        if (c < nchunks) {
+            if (exclusive) {
+                float w[EPC];
+#pragma unroll
+                for (int e = 0; e < EPC; ++e)
+                    w[e] = fmaf(-lr, acc[m][e], vrow[m][e]);
+                DT *dst = values + f * d_v + (int64_t)c * EPC;
+                if constexpr (sizeof(DT) == 2) {
+                    uint4 r;
+                    r.x = f32_to_bf16_bits(w[0]) | (f32_to_bf16_bits(w[1]) << 16);
+                    r.y = f32_to_bf16_bits(w[2]) | (f32_to_bf16_bits(w[3]) << 16);
+                    r.z = f32_to_bf16_bits(w[4]) | (f32_to_bf16_bits(w[5]) << 16);
+                    r.w = f32_to_bf16_bits(w[6]) | (f32_to_bf16_bits(w[7]) << 16);
+                    *reinterpret_cast<uint4 *>(dst) = r;
+                } else {
+                    *reinterpret_cast<float4 *>(dst) = make_float4(w[0], w[1], w[2], w[3]);
+                }
+            } else {
+                float *dst = split_acc + srow * d_v + (int64_t)c * EPC;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e)
+                    __hip_atomic_fetch_add(dst + e, acc[m][e], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+            acc[m][e] = 0.f;
+    }
+}
+
+// SGD: the value rows are updated in place (values is then written, and
+// dvalues is split_acc, see seg_flush_sgd); dw is the same in every mode.
+template <typename DT, int MCH, int U, bool SGD>
 __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
-    const DT *__restrict__ values, const DT *__restrict__ dy, const int32_t *__restrict__ idx,
+    const DT *values, const DT *__restrict__ dy, const int32_t *__restrict__ idx,
     const float *__restrict__ weights, const int32_t *__restrict__ order,
     const int32_t *__restrict__ start, float *__restrict__ dvalues, float *__restrict__ dw,
-    int64_t picks, int HK, int d_v, int accumulate)
+    int64_t picks, int HK, int d_v, int accumulate, float lr)
 {
     constexpr int EPC = Elt<DT>::per16;
     constexpr int kMaxLen = 2 * kSegChunk;
@@ -415,6 +525,14 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
     int seg = 0;
     int seg_end = __builtin_amdgcn_readfirstlane(segs[1]);
     int f_cur = f_first;
+    // the current run's sum leaves: stored, added, or (SGD) applied to its row
+    auto flush = [&](bool exclusive) {
+        if constexpr (SGD)
+            seg_flush_sgd<DT, MCH, EPC>(acc, vrow, const_cast<DT *>(values), dvalues, start, f_cur,
+                                        d_v, nchunks, lane, exclusive, lr);
+        else
+            seg_flush<MCH, EPC>(acc, dvalues, f_cur, d_v, nchunks, lane, exclusive, accumulate);
+    };
 
     auto work = [&](DyGroup<MCH, U> &g, int j) {
         float part[U];
@@ -423,9 +541,7 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
             part[u] = 0.f;
             if (j + u < len) {
                 if (j + u == seg_end) {          // next run of slots
-                    seg_flush<MCH, EPC>(acc, dvalues, f_cur, d_v, nchunks, lane,
-                                        !((seg == 0 && first_split) || (seg == nseg - 1 && last_split)),
-                                        accumulate);
+                    flush(!((seg == 0 && first_split) || (seg == nseg - 1 && last_split)));
                     ++seg;
                     seg_end = __builtin_amdgcn_readfirstlane(segs[seg + 1]);
                     f_cur = __builtin_amdgcn_readfirstlane(slot[j + u]);
@@ -463,8 +579,7 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
         work(gb, j + U);
         seg_load_group<DT, MCH, U>(gb, dy, tok, j + 3 * U, len, d_v, lane);
     }
-    seg_flush<MCH, EPC>(acc, dvalues, f_cur, d_v, nchunks, lane,
-                        !((seg == 0 && first_split) || (seg == nseg - 1 && last_split)), accumulate);
+    flush(!((seg == 0 && first_split) || (seg == nseg - 1 && last_split)));
     wave_lds_sync();
     for (int j = lane; j < len; j += kWave)
         dw[s_pk[wv][j]] = s_dw[wv][j];
@@ -1055,37 +1170,41 @@ static unsigned grid1d(int64_t n, int per)
     return (unsigned)((n + per - 1) / per);
 }
 
-template <typename DT, int MCH, int U>
+template <typename DT, int MCH, int U, bool SGD>
 static hipError_t launch_seg_t(const void *values, const void *dy, const int32_t *idx,
                                const float *weights, const int32_t *order, const int32_t *start,
                                float *dvalues, float *dw, int64_t picks, int HK, int d_v,
-                               int accumulate, hipStream_t stream)
+                               int accumulate, float lr, hipStream_t stream)
 {
     const int64_t waves = (picks + kSegChunk - 1) / kSegChunk;
-    hipLaunchKernelGGL((seg_value_kernel<DT, MCH, U>), dim3(grid1d(waves, kSegWaves)),
+    hipLaunchKernelGGL((seg_value_kernel<DT, MCH, U, SGD>), dim3(grid1d(waves, kSegWaves)),
                        dim3(kSegWaves * kWave), 0, stream, static_cast<const DT *>(values),
                        static_cast<const DT *>(dy), idx, weights, order, start, dvalues, dw, picks,
-                       HK, d_v, accumulate);
+                       HK, d_v, accumulate, lr);
     return hipGetLastError();
 }
 
-template <typename DT>
+template <typename DT, bool SGD>
 static hipError_t launch_seg_dt(const void *values, const void *dy, const int32_t *idx,
                                 const float *weights, const int32_t *order, const int32_t *start,
                                 float *dvalues, float *dw, int64_t picks, int HK, int d_v,
-                                int accumulate, hipStream_t stream)
+                                int accumulate, float lr, hipStream_t stream)
 {
     const int per_lane = (d_v / Elt<DT>::per16 + kWave - 1) / kWave;
+#define PKM_SEG(MCH, U)                                                                        \
+    launch_seg_t<DT, MCH, U, SGD>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, \
+                                  d_v, accumulate, lr, stream)
     if (per_lane <= 1)
-        return launch_seg_t<DT, 1, 8>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, accumulate, stream);
+        return PKM_SEG(1, 8);
     if (per_lane <= 2)
-        return launch_seg_t<DT, 2, 4>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, accumulate, stream);
+        return PKM_SEG(2, 4);
     if (per_lane <= 4)
-        return launch_seg_t<DT, 4, 2>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, accumulate, stream);
+        return PKM_SEG(4, 2);
     if (per_lane <= 8 || sizeof(DT) == 2)       // bf16 rows of <= 4096 fit 8 chunks per lane
-        return launch_seg_t<DT, 8, 1>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, accumulate, stream);
+        return PKM_SEG(8, 1);
     if constexpr (sizeof(DT) == 4)
-        return launch_seg_t<DT, 16, 1>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, d_v, accumulate, stream);
+        return PKM_SEG(16, 1);
+#undef PKM_SEG
     return hipErrorInvalidValue;
 }
 
@@ -1125,10 +1244,38 @@ hipError_t launch_bwd_value(int dtype, const void *values, const int32_t *idx,
             return err;
     }
     if (dtype == 1)
-        return launch_seg_dt<bf16_t>(values, dy, idx, weights, order, slot_start, dvalues, dw,
-                                     picks, H * k, d_v, accumulate, stream);
-    return launch_seg_dt<float>(values, dy, idx, weights, order, slot_start, dvalues, dw, picks,
-                                H * k, d_v, accumulate, stream);
+        return launch_seg_dt<bf16_t, false>(values, dy, idx, weights, order, slot_start, dvalues,
+                                            dw, picks, H * k, d_v, accumulate, 0.f, stream);
+    return launch_seg_dt<float, false>(values, dy, idx, weights, order, slot_start, dvalues, dw,
+                                       picks, H * k, d_v, accumulate, 0.f, stream);
+}
+
+hipError_t launch_bwd_value_sgd(int dtype, void *values, const int32_t *idx, const float *weights,
+                                const void *dy, const int32_t *slot_start, const int32_t *order,
+                                float lr, float *split_acc, float *dw, int64_t T, int H, int n,
+                                int k, int d_v, hipStream_t stream)
+{
+    const int64_t picks = T * H * (int64_t)k;
+    const int64_t slots = (int64_t)n * n;
+    const dim3 grid(grid1d(slots, 4 * kWave)), block(4 * kWave);
+    hipLaunchKernelGGL(split_prepare_kernel, grid, block, 0, stream, slot_start, slots, d_v,
+                       split_acc);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    err = dtype == 1 ? launch_seg_dt<bf16_t, true>(values, dy, idx, weights, order, slot_start,
+                                                   split_acc, dw, picks, H * k, d_v, 0, lr, stream)
+                     : launch_seg_dt<float, true>(values, dy, idx, weights, order, slot_start,
+                                                  split_acc, dw, picks, H * k, d_v, 0, lr, stream);
+    if (err != hipSuccess)
+        return err;
+    if (dtype == 1)
+        hipLaunchKernelGGL(split_apply_kernel<bf16_t>, grid, block, 0, stream, slot_start, slots,
+                           d_v, split_acc, static_cast<bf16_t *>(values), lr);
+    else
+        hipLaunchKernelGGL(split_apply_kernel<float>, grid, block, 0, stream, slot_start, slots,
+                           d_v, split_acc, static_cast<float *>(values), lr);
+    return hipGetLastError();
 }
 
 template <typename DT>

@@ -10,6 +10,8 @@
 namespace pkm {
 
 constexpr int kSegChunk = 256;      // sorted picks per wave in the value segmented reduction
+constexpr int kSegShift = 8;        // log2(kSegChunk)
+static_assert((1 << kSegShift) == kSegChunk, "kSegShift = log2(kSegChunk)");
 
 // Rank pairs (a, b) with (a + 1)(b + 1) <= k: the combine candidates.
 inline int merge_candidates(int k)
@@ -63,6 +65,19 @@ hipError_t launch_bwd_value(int dtype, const void *values, const int32_t *idx,
                             const float *weights, const void *dy, const int32_t *slot_start,
                             const int32_t *order, float *dvalues, int accumulate, float *dw,
                             int64_t T, int H, int n, int k, int d_v, hipStream_t stream);
+
+// The value side with the SGD step fused in: dw as launch_bwd_value, and every
+// selected value row updated in place, w = fmaf(-lr, g, w) rounded once, with
+// g the row's gradient; no dvalues.  split_acc holds split_rows_bytes(...)
+// bytes (the sums of the runs longer than the reduction's chunk).
+hipError_t launch_bwd_value_sgd(int dtype, void *values, const int32_t *idx, const float *weights,
+                                const void *dy, const int32_t *slot_start, const int32_t *order,
+                                float lr, float *split_acc, float *dw, int64_t T, int H, int n,
+                                int k, int d_v, hipStream_t stream);
+inline size_t split_rows_bytes(int64_t picks, int d_v)
+{
+    return (size_t)((picks >> kSegShift) + 1) * (size_t)d_v * 4;
+}
 
 // Query side: softmax backward per distinct sub-key, dq (overwritten) and
 // dkeys (overwritten) from weights and dw.  `scratch` holds

@@ -129,6 +129,40 @@ def pkm_backward(q: torch.Tensor, keys: torch.Tensor, values: torch.Tensor, idx:
     return dq, dkeys, dvalues
 
 
+def pkm_backward_sgd(q: torch.Tensor, keys: torch.Tensor, values: torch.Tensor,
+                     idx: torch.Tensor, weights: torch.Tensor, dy: torch.Tensor, lr: float,
+                     out=None):
+    """Backward pass with the sparse SGD step fused in: returns (dq, dkeys) as
+    pkm_backward does, and updates `values` IN PLACE -- every row some pick
+    selected becomes fmaf(-lr, g, w) rounded once to the storage type, g being
+    the row's float32 gradient (pkm_backward's dvalues row).  No dvalues array
+    is formed."""
+    T, H, n, d_k, d_v = _shapes(q, keys, values)
+    dev, dt = q.device, q.dtype
+    k = idx.shape[2]
+    _check(q, "q", (T, H, d_k), dt, dev)
+    _check(keys, "keys", (H, 2, n, d_k // 2), dt, dev)
+    _check(values, "values", (n * n, d_v), dt, dev)
+    _check(idx, "idx", (T, H, k), torch.int32, dev)
+    _check(weights, "weights", (T, H, k), torch.float32, dev)
+    _check(dy, "dy", (T, d_v), dt, dev)
+    p = problem(T, H, n, k, d_k, d_v, dt)
+    ws_bytes = pkm_workspace_bytes(p, 2)
+    if ws_bytes == (1 << 64) - 1:
+        raise PKMError(2, "pkm_backward_sgd")
+    if out is None:
+        dq = torch.empty((T, H, d_k), dtype=torch.float32, device=dev)
+        dkeys = torch.empty((H, 2, n, d_k // 2), dtype=torch.float32, device=dev)
+    else:
+        dq, dkeys = out
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
+    rc = _lib.backward_sgd(p, _ptr(q), _ptr(keys), _ptr(values), _ptr(idx), _ptr(weights),
+                           _ptr(dy), _ptr(dq), _ptr(dkeys), lr, _ptr(ws), ws_bytes, _stream(dev))
+    if rc != 0:
+        raise PKMError(rc, "pkm_backward_sgd")
+    return dq, dkeys
+
+
 def pkm_slot_sort(idx: torch.Tensor, n: int, out=None):
     """Groups the picks of idx [T,H,k] int32 by memory slot.  Returns
     (slot_start [n*n+1] int32, order [T*H*k] int32): the picks (ids

@@ -71,6 +71,21 @@ def test_backward_workspace_checks():
     assert _lib.backward(P(d_v=4104), *args, 0, FAKE, 1 << 30, None) == 2   # backward row limit
 
 
+def test_backward_sgd_checks():
+    """The fused backward + SGD: its own workspace size (backward = 2), host-side
+    argument checks before any launch."""
+    p = P()
+    need = _lib.workspace_bytes(p, 2)
+    assert need >= _lib.workspace_bytes(p, 1)
+    assert _lib.workspace_bytes(p, 3) == (1 << 64) - 1
+    args = [FAKE] * 8                 # q, keys, values, idx, weights, dy, dq, dkeys
+    assert _lib.backward_sgd(p, *args, 0.1, FAKE, need - 1, None) == 4
+    assert _lib.backward_sgd(p, *args, float("inf"), FAKE, need, None) == 7
+    assert _lib.backward_sgd(p, None, *args[1:], 0.1, FAKE, need, None) == 1
+    assert _lib.backward_sgd(p, FAKE, FAKE, FAKE + 8, *args[3:], 0.1, FAKE, need, None) == 6
+    assert _lib.backward_sgd(P(d_v=4104), *args, 0.1, FAKE, 1 << 30, None) == 2
+
+
 def test_workspace_of_invalid_problem():
     assert _lib.workspace_bytes(P(k=0), True) == (1 << 64) - 1
 

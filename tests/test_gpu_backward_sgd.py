@@ -83,6 +83,14 @@ def test_fused_sgd_hot_slots(dtype):
     assert (counts > 256).sum() == 4
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_fused_sgd_widest_rows(dtype):
+    """d_v = 4096, the backward's widest value row (the most chunks per lane)."""
+    inp = pkm_inputs.custom(64, 1, 8, 3, 16, 4096, dtype=dtype, seed=604)
+    print(f"[backward_sgd] d_v 4096 {dtype}", flush=True)
+    _fused_vs_chain(inp, 3, 0.02)
+
+
 def test_fused_sgd_bench_workload():
     """The full bench workload (Zipf-hot slots: some runs are long)."""
     inp = pkm_inputs.make("base-bf16-zipf-bwd")

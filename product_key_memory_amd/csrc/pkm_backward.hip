@@ -1197,7 +1197,7 @@ static hipError_t launch_seg_dt(const void *values, const void *dy, const int32_
     if (per_lane <= 1)
         return PKM_SEG(1, 8);
     if (per_lane <= 2)
-        return PKM_SEG(2, 4);
+        return PKM_SEG(2, 8);
     if (per_lane <= 4)
         return PKM_SEG(4, 2);
     if (per_lane <= 8 || sizeof(DT) == 2)       // bf16 rows of <= 4096 fit 8 chunks per lane

@@ -296,6 +296,17 @@ def measure_query_net(torch, _lib, w, dq, stream, d_model: int = 1600) -> dict:
     return out
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(inp, k: int, count: int) -> dict:
     import oracle
     import pkm_inputs
@@ -312,7 +323,7 @@ def cpu_baseline(inp, k: int, count: int) -> dict:
             "kind": "oracle",
             "sample": f"{len(sub)} seeded tokens of {w.name}, forward+backward in float64: flat "
                       f"scoring and full sort of all {w.n * w.n} slots per head, dense gradients; "
-                      f"{dt:.2f} s wall on {orc.max_threads()} threads ({platform.processor() or platform.machine()})"}
+                      f"{dt:.2f} s wall on {orc.max_threads()} threads ({_cpu_model()})"}
 
 
 def main():
@@ -467,6 +478,8 @@ def main():
                    "zipf": w.zipf, "touched_slots": touched,
                    "step": "forward + backward (dvalues overwritten)"},
         "gather": {"GB/s": kernels["gather"]["GB/s"], "hbm_frac": kernels["gather"]["hbm_frac"]},
+        # the forward alone (selection + gather, from the same stage events)
+        "forward_tokens_per_s": round(T / ((kernels["select"]["ms"] + kernels["gather"]["ms"]) * 1e-3), 1),
         "roofline": roofline,
         "kernels": kernels,
         "after_backward": extras,

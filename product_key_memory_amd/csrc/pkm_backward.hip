@@ -626,10 +626,11 @@ struct Row4<bf16_t> {
 // One wave per (token, head).  For k <= 32 one pass gives each lane one
 // (half, pick): lanes 0-31 the left sub-keys, lanes 32-63 the right ones;
 // for larger k two passes, one half each.  A lane's sums A, W, B, Wc run over
-// the picks staged in LDS (one broadcast read per pick).  The distinct
-// sub-keys of both halves then form one list, and their rows are fetched in
-// batches of kBatch before they are used: in the dq product each lane owns JPL
-// groups of 4 consecutive elements of a half (half <= 256 JPL).
+// its half's picks staged in LDS (one broadcast read per pick).  The distinct
+// sub-keys then form a list in two segments of 32 positions (see below), and
+// their rows are fetched in batches of kBatch before they are used: in the dq
+// product each lane owns JPL groups of 4 consecutive elements of a half
+// (half <= 256 JPL).
 template <typename DT, int JPL>
 __global__ __launch_bounds__(kQryWaves *kWave) void bwd_query_kernel(
     const DT *__restrict__ keys, const int32_t *__restrict__ idx,

@@ -150,7 +150,8 @@ pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *key
  * dvalues; rows no pick selected are left as they are.  The same result as
  * pkm_backward (dvalues overwritten) followed by pkm_sparse_sgd, without the
  * n*n x d_v float32 gradient array: each row's sum is applied where it is
- * formed (rows with more than 256 picks go through a workspace buffer).
+ * formed (rows picked more often than one wave's share -- 256 picks, fewer
+ * on small batches -- go through a workspace buffer).
  *   values    [n*n][d_v]  dtype, IN/OUT
  *   lr        the learning rate; finite, else PKM_ERR_ARG
  *   workspace pkm_workspace_bytes(p, 2) bytes

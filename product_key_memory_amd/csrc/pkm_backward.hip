@@ -214,11 +214,11 @@ __global__ __launch_bounds__(kL2Threads) void bucket_sort_kernel(
 }
 
 // Overwrite mode: zero the dvalues rows no wave will write whole -- rows no
-// pick selected, and rows with a run of more than kSegChunk sorted picks
+// pick selected, and rows with a run of more than `chunk` sorted picks
 // (several waves add into those with atomics).  Each wave checks 64 slots,
 // one per lane, then zeroes the rows found, all lanes on one row at a time.
 __global__ void dv_prepare_kernel(const int32_t *__restrict__ start, int64_t slots, int d_v,
-                                  float *__restrict__ dvalues)
+                                  int chunk, float *__restrict__ dvalues)
 {
     const int lane = lane_id();
     const int64_t f0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * kWave;
@@ -228,7 +228,7 @@ __global__ void dv_prepare_kernel(const int32_t *__restrict__ start, int64_t slo
     bool zero = false;
     if (f < slots) {
         const int64_t b = start[f], e = start[f + 1];
-        zero = b == e || e - b > kSegChunk;
+        zero = b == e || e - b > chunk;
     }
     uint64_t todo = __ballot(zero);
     while (todo) {
@@ -240,22 +240,23 @@ __global__ void dv_prepare_kernel(const int32_t *__restrict__ start, int64_t slo
     }
 }
 
-// The fused SGD: zero the split_acc rows of the runs longer than kSegChunk
-// (row start[f] / kSegChunk), before the segmented reduction adds into them.
+// The fused SGD: zero the split_acc rows of the runs longer than the chunk
+// of 2^shift picks (row start[f] >> shift), before the segmented reduction
+// adds into them.
 __global__ void split_prepare_kernel(const int32_t *__restrict__ start, int64_t slots, int d_v,
-                                     float *__restrict__ split_acc)
+                                     int shift, float *__restrict__ split_acc)
 {
     const int lane = lane_id();
     const int64_t f0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * kWave;
     if (f0 >= slots)
         return;
     const int64_t f = f0 + lane;
-    const bool split = f < slots && start[f + 1] - start[f] > kSegChunk;
+    const bool split = f < slots && start[f + 1] - start[f] > (1 << shift);
     uint64_t todo = __ballot(split);
     while (todo) {
         const int i = __builtin_ctzll(todo);
         todo &= todo - 1;
-        float4 *row = reinterpret_cast<float4 *>(split_acc + (int64_t)(start[f0 + i] >> kSegShift) * d_v);
+        float4 *row = reinterpret_cast<float4 *>(split_acc + (int64_t)(start[f0 + i] >> shift) * d_v);
         for (int c = lane; c < d_v / 4; c += kWave)
             row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -264,8 +265,8 @@ __global__ void split_prepare_kernel(const int32_t *__restrict__ start, int64_t 
 // ... and afterwards apply those sums: w = fmaf(-lr, g, w), rounded once.
 template <typename DT>
 __global__ void split_apply_kernel(const int32_t *__restrict__ start, int64_t slots, int d_v,
-                                   const float *__restrict__ split_acc, DT *__restrict__ values,
-                                   float lr)
+                                   int shift, const float *__restrict__ split_acc,
+                                   DT *__restrict__ values, float lr)
 {
     constexpr int EPC = Elt<DT>::per16;
     const int lane = lane_id();
@@ -273,12 +274,12 @@ __global__ void split_apply_kernel(const int32_t *__restrict__ start, int64_t sl
     if (f0 >= slots)
         return;
     const int64_t f = f0 + lane;
-    const bool split = f < slots && start[f + 1] - start[f] > kSegChunk;
+    const bool split = f < slots && start[f + 1] - start[f] > (1 << shift);
     uint64_t todo = __ballot(split);
     while (todo) {
         const int i = __builtin_ctzll(todo);
         todo &= todo - 1;
-        const float *g = split_acc + (int64_t)(start[f0 + i] >> kSegShift) * d_v;
+        const float *g = split_acc + (int64_t)(start[f0 + i] >> shift) * d_v;
         DT *row = values + (f0 + i) * d_v;
         for (int c = lane; c < d_v / EPC; c += kWave) {
             float w[EPC];
@@ -307,14 +308,15 @@ constexpr int kSegWaves = 4;
 
 // MCH: 16-byte chunks of a row per lane; U: picks per group.  Wave w takes
 // the sorted picks of its nominal range [256 w, 256 w + 256), moved so that a
-// slot's run of at most kSegChunk picks is never cut: such a run belongs to
-// the wave whose range holds its first pick (a range grows to < 2 kSegChunk).
+// slot's run of at most `chunk` picks is never cut: such a run belongs to
+// the wave whose range holds its first pick (a range grows to < 2 chunk).
+// chunk = 2^shift <= kSegChunk: 256, or less on small batches.
 // Longer runs are cut at the nominal bounds.  The wave stages the (pick,
 // token, slot, weight) of its picks in LDS and lists where each run starts,
 // then streams the picks in groups of U with two groups of dy rows in flight;
 // the value row of the next run is fetched while the current one is worked
 // on.  A run's sum is stored (the row is this wave's alone) unless the run is
-// longer than kSegChunk: those rows, zeroed beforehand in overwrite mode, take
+// longer than chunk: those rows, zeroed beforehand in overwrite mode, take
 // float atomics from each wave that holds a piece.
 template <int MCH, int U>
 struct DyGroup {
@@ -392,17 +394,17 @@ __device__ __forceinline__ void seg_flush(float (&acc)[MCH][EPC], float *__restr
 // The fused update: the run's sum g updates its value row in place,
 // w = fmaf(-lr, g, w) rounded once to the storage type (vrow holds the row's
 // old values), when the row is this wave's alone; a long run's pieces add
-// into its row of split_acc (row start[f] / kSegChunk: long runs hold more
-// than kSegChunk sorted picks, so their first positions differ in that
-// quotient), applied after the kernel.
+// into its row of split_acc (row start[f] >> shift: long runs hold more than
+// 2^shift sorted picks, so their first positions differ in that quotient),
+// applied after the kernel.
 template <typename DT, int MCH, int EPC>
 __device__ __forceinline__ void seg_flush_sgd(float (&acc)[MCH][EPC], const float (&vrow)[MCH][EPC],
                                               DT *values, float *__restrict__ split_acc,
                                               const int32_t *__restrict__ start, int64_t f,
                                               int d_v, int nchunks, int lane, bool exclusive,
-                                              float lr)
+                                              float lr, int shift)
 {
-    const int64_t srow = exclusive ? 0 : (int64_t)(start[f] >> kSegShift);
+    const int64_t srow = exclusive ? 0 : (int64_t)(start[f] >> shift);
 #pragma unroll
     for (int m = 0; m < MCH; ++m) {
         const int c = lane + m * kWave;
@@ -444,8 +446,9 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
     const DT *values, const DT *__restrict__ dy, const int32_t *__restrict__ idx,
     const float *__restrict__ weights, const int32_t *__restrict__ order,
     const int32_t *__restrict__ start, float *__restrict__ dvalues, float *__restrict__ dw,
-    int64_t picks, int HK, int d_v, int accumulate, float lr)
+    int64_t picks, int HK, int d_v, int accumulate, float lr, int shift)
 {
+    const int chunk = 1 << shift;
     constexpr int EPC = Elt<DT>::per16;
     constexpr int kMaxLen = 2 * kSegChunk;
     __shared__ int32_t s_pk[kSegWaves][kMaxLen];
@@ -456,20 +459,20 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
     __shared__ int32_t s_seg[kSegWaves][kMaxLen + 1];
     const int lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t nom = ((int64_t)blockIdx.x * kSegWaves + wv) * kSegChunk;
+    const int64_t nom = ((int64_t)blockIdx.x * kSegWaves + wv) * chunk;
     if (nom >= picks)
         return;
-    // a bound inside a run of at most kSegChunk picks moves to the run's end
+    // a bound inside a run of at most chunk picks moves to the run's end
     auto run_len = [&](int f) { return start[f + 1] - start[f]; };
     auto adjust = [&](int64_t p) -> int64_t {
         if (p == 0 || p >= picks)
             return p;
         const int f = idx[order[p]];
         const int64_t b = start[f], e = start[f + 1];
-        return (p == b || e - b > kSegChunk) ? p : e;
+        return (p == b || e - b > chunk) ? p : e;
     };
     const int64_t p_begin = adjust(nom);
-    const int64_t p_end = adjust(nom + kSegChunk < picks ? nom + kSegChunk : picks);
+    const int64_t p_end = adjust(nom + chunk < picks ? nom + chunk : picks);
     if (p_end <= p_begin)
         return;
     const int len = (int)(p_end - p_begin);
@@ -511,8 +514,8 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
     seg_load_group<DT, MCH, U>(gb, dy, tok, U, len, d_v, lane);
     // only the first and the last run can be long ones, shared with other waves
     const int f_last = __builtin_amdgcn_readfirstlane(slot[len - 1]);
-    const bool first_split = run_len(f_first) > kSegChunk;
-    const bool last_split = run_len(f_last) > kSegChunk;
+    const bool first_split = run_len(f_first) > chunk;
+    const bool last_split = run_len(f_last) > chunk;
 
     float vrow[MCH][EPC], acc[MCH][EPC];
 #pragma unroll
@@ -529,7 +532,7 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
     auto flush = [&](bool exclusive) {
         if constexpr (SGD)
             seg_flush_sgd<DT, MCH, EPC>(acc, vrow, const_cast<DT *>(values), dvalues, start, f_cur,
-                                        d_v, nchunks, lane, exclusive, lr);
+                                        d_v, nchunks, lane, exclusive, lr, shift);
         else
             seg_flush<MCH, EPC>(acc, dvalues, f_cur, d_v, nchunks, lane, exclusive, accumulate);
     };
@@ -1177,11 +1180,12 @@ static hipError_t launch_seg_t(const void *values, const void *dy, const int32_t
                                float *dvalues, float *dw, int64_t picks, int HK, int d_v,
                                int accumulate, float lr, hipStream_t stream)
 {
-    const int64_t waves = (picks + kSegChunk - 1) / kSegChunk;
+    const int shift = seg_shift(picks);
+    const int64_t waves = (picks + (1 << shift) - 1) >> shift;
     hipLaunchKernelGGL((seg_value_kernel<DT, MCH, U, SGD>), dim3(grid1d(waves, kSegWaves)),
                        dim3(kSegWaves * kWave), 0, stream, static_cast<const DT *>(values),
                        static_cast<const DT *>(dy), idx, weights, order, start, dvalues, dw, picks,
-                       HK, d_v, accumulate, lr);
+                       HK, d_v, accumulate, lr, shift);
     return hipGetLastError();
 }
 
@@ -1239,7 +1243,7 @@ hipError_t launch_bwd_value(int dtype, const void *values, const int32_t *idx,
     if (!accumulate) {
         const int64_t slots = (int64_t)n * n;
         hipLaunchKernelGGL(dv_prepare_kernel, dim3(grid1d(slots, 4 * kWave)), dim3(4 * kWave), 0,
-                           stream, slot_start, slots, d_v, dvalues);
+                           stream, slot_start, slots, d_v, 1 << seg_shift(picks), dvalues);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess)
             return err;
@@ -1259,7 +1263,8 @@ hipError_t launch_bwd_value_sgd(int dtype, void *values, const int32_t *idx, con
     const int64_t picks = T * H * (int64_t)k;
     const int64_t slots = (int64_t)n * n;
     const dim3 grid(grid1d(slots, 4 * kWave)), block(4 * kWave);
-    hipLaunchKernelGGL(split_prepare_kernel, grid, block, 0, stream, slot_start, slots, d_v,
+    const int shift = seg_shift(picks);
+    hipLaunchKernelGGL(split_prepare_kernel, grid, block, 0, stream, slot_start, slots, d_v, shift,
                        split_acc);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
@@ -1272,10 +1277,10 @@ hipError_t launch_bwd_value_sgd(int dtype, void *values, const int32_t *idx, con
         return err;
     if (dtype == 1)
         hipLaunchKernelGGL(split_apply_kernel<bf16_t>, grid, block, 0, stream, slot_start, slots,
-                           d_v, split_acc, static_cast<bf16_t *>(values), lr);
+                           d_v, shift, split_acc, static_cast<bf16_t *>(values), lr);
     else
         hipLaunchKernelGGL(split_apply_kernel<float>, grid, block, 0, stream, slot_start, slots,
-                           d_v, split_acc, static_cast<float *>(values), lr);
+                           d_v, shift, split_acc, static_cast<float *>(values), lr);
     return hipGetLastError();
 }
 

@@ -9,9 +9,20 @@
 
 namespace pkm {
 
-constexpr int kSegChunk = 256;      // sorted picks per wave in the value segmented reduction
+constexpr int kSegChunk = 256;      // sorted picks per wave in the value segmented reduction, at most
 constexpr int kSegShift = 8;        // log2(kSegChunk)
 static_assert((1 << kSegShift) == kSegChunk, "kSegShift = log2(kSegChunk)");
+
+// log2 of the picks per wave of the value side: 256, or fewer (down to 32) on
+// small batches, so that about 2048 waves share the work.  Runs of more than
+// that many sorted picks are "long" (cut between waves).
+inline int seg_shift(int64_t picks)
+{
+    int s = kSegShift;
+    while (s > 5 && (picks >> s) < 2048)
+        --s;
+    return s;
+}
 
 // Rank pairs (a, b) with (a + 1)(b + 1) <= k: the combine candidates.
 inline int merge_candidates(int k)
@@ -76,7 +87,7 @@ hipError_t launch_bwd_value_sgd(int dtype, void *values, const int32_t *idx, con
                                 int k, int d_v, hipStream_t stream);
 inline size_t split_rows_bytes(int64_t picks, int d_v)
 {
-    return (size_t)((picks >> kSegShift) + 1) * (size_t)d_v * 4;
+    return (size_t)((picks >> seg_shift(picks)) + 1) * (size_t)d_v * 4;
 }
 
 // Query side: softmax backward per distinct sub-key, dq (overwritten) and

@@ -75,7 +75,8 @@ def test_fused_sgd_small_against_chain_and_oracle(orc, dtype):
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_fused_sgd_hot_slots(dtype):
     """Every token asks the same query: each selected slot gets T*H picks, runs
-    longer than one wave's share, so the long-run path carries the update."""
+    longer than one wave's share (32 picks at this batch size), so the
+    long-run path carries the update."""
     inp = pkm_inputs.custom(700, 1, 24, 4, 32, 48, dtype=dtype, seed=602)
     inp["q"][:] = inp["q"][0]
     print(f"[backward_sgd] hot slots {dtype}", flush=True)

@@ -39,6 +39,10 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run 3 plain elementwise copies of 256 MiB (bitwise not), whose "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate those of the kernels")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the bench line: the step (forward + backward) over heads "
+                         "H in 1, 2, 4, 8 and picks k in 8, 16, 32 on the workload's other shapes, "
+                         "one JSON line each with tokens/s and the fraction of slots in use")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="no GPU work: read the rocprofv3 databases of a FETCH_SIZE run and a "
                          "WRITE_SIZE run of `bench.py --calibrate-copy`, and write the "
@@ -326,10 +330,82 @@ def cpu_baseline(inp, k: int, count: int) -> dict:
                       f"{dt:.2f} s wall on {orc.max_threads()} threads ({_cpu_model()})"}
 
 
+def run_sweep(args) -> None:
+    """The speed / memory-use knobs: heads H and picks k on the workload's
+    remaining shapes (synthetic inputs of the same recipe, one draw per H).
+    Per point: W warm-up and K timed steps of pkm_forward + pkm_backward
+    (dvalues overwritten) bracketed by events, and the share of the n*n slots
+    some pick selected in the batch."""
+    import dataclasses
+
+    import torch
+    import pkm_inputs
+    from product_key_memory_amd import _lib
+    from product_key_memory_amd.pkm import problem
+
+    dev = torch.device("cuda", 0)
+    base = pkm_inputs.WORKLOADS[args.workload]
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    P = lambda t: t.data_ptr()  # noqa: E731
+    for H in (1, 2, 4, 8):
+        w0 = dataclasses.replace(base, H=H, name=f"{base.name}-H{H}")
+        inp = pkm_inputs.make(w0, with_dy=True)
+        tdt = torch.bfloat16 if w0.dtype == "bf16" else torch.float32
+
+        def to_dev(a):
+            t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+            return t.view(torch.bfloat16) if a.dtype == np.uint16 else t
+
+        q, keys, values, dy = (to_dev(inp[x]) for x in ("q", "keys", "values", "dy"))
+        del inp
+        T, n, d_k, d_v = w0.T, w0.n, w0.d_k, w0.d_v
+        y = torch.empty((T, d_v), dtype=tdt, device=dev)
+        dvalues = torch.empty((n * n, d_v), dtype=torch.float32, device=dev)
+        dq = torch.empty((T, H, d_k), dtype=torch.float32, device=dev)
+        dkeys = torch.empty((H, 2, n, d_k // 2), dtype=torch.float32, device=dev)
+        for k in (8, 16, 32):
+            p = problem(T, H, n, k, d_k, d_v, tdt)
+            fb, bb = _lib.workspace_bytes(p, False), _lib.workspace_bytes(p, True)
+            fws = torch.empty(max(fb, 1), dtype=torch.uint8, device=dev)
+            bws = torch.empty(max(bb, 1), dtype=torch.uint8, device=dev)
+            idx = torch.empty((T, H, k), dtype=torch.int32, device=dev)
+            wts = torch.empty((T, H, k), dtype=torch.float32, device=dev)
+
+            def step():
+                rc = _lib.forward(p, P(q), P(keys), P(values), P(y), P(idx), P(wts), None,
+                                  P(fws), fb, sp)
+                rc |= _lib.backward(p, P(q), P(keys), P(values), P(idx), P(wts), P(dy), P(dq),
+                                    P(dkeys), P(dvalues), 0, P(bws), bb, sp)
+                if rc:
+                    raise RuntimeError(f"libpkm returned {rc}")
+
+            for _ in range(args.warmup):
+                step()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            used = torch.unique(idx).numel() / (n * n)
+            print(json.dumps({"sweep": {"workload": base.name, "H": H, "k": k},
+                              "tokens_per_s": round(T / (ms * 1e-3), 1),
+                              "ms_per_step": round(ms, 4), "used_fraction": round(used, 4)}),
+                  flush=True)
+        del q, keys, values, dy, y, dvalues, dq, dkeys
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.record_traffic:
         print(record_traffic(*args.record_traffic, args.workload))
+        return
+    if args.sweep:
+        run_sweep(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

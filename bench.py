@@ -60,6 +60,20 @@ STAGE_KERNELS = {
     "bwd_values": ("dv_prepare_kernel", "seg_value_kernel"),
     "bwd_queries": ("bwd_query_kernel", "dkeys_mfma_kernel", "dkeys_reduce_kernel"),
 }
+# the value side of pkm_backward_sgd (timed after the step; in the traffic
+# record only): its seg_value instance is the one whose SGD flag is true
+SGD_VALUE_KERNELS = ("split_prepare_kernel", "seg_value_kernel", "split_apply_kernel")
+
+
+def stage_of(short: str):
+    """The stage a kernel (name without namespace and arguments) belongs to."""
+    base = short.split("<")[0]
+    if base in SGD_VALUE_KERNELS and (base != "seg_value_kernel" or short.endswith("true>")):
+        return "bwd_values_sgd"
+    for stage, prefixes in STAGE_KERNELS.items():
+        if base in prefixes:
+            return stage
+    return None
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 
 
@@ -153,17 +167,17 @@ def record_traffic(fetch_db: str, write_db: str, workload: str) -> str:
         return copy_kib / vals[len(vals) // 2]
 
     f_fac, w_fac = calib(fetch_db, "FETCH_SIZE"), calib(write_db, "WRITE_SIZE")
-    stages = {}
-    for stage, prefixes in STAGE_KERNELS.items():
-        rec = {"read_bytes": 0, "write_bytes": 0, "kernels": {}}
-        for table, fac, key in ((fetch, f_fac, "read_bytes"), (write, w_fac, "write_bytes")):
-            for name, (kib, cnt) in table.items():
-                short = name.split("(")[0].replace("void ", "").replace("pkm::", "")
-                if short.split("<")[0] in prefixes:
-                    b = int(round(kib * fac * 1024))
-                    rec[key] += b
-                    rec["kernels"].setdefault(short, {})[key] = b
-        stages[stage] = rec
+    stages = {stage: {"read_bytes": 0, "write_bytes": 0, "kernels": {}}
+              for stage in list(STAGE_KERNELS) + ["bwd_values_sgd"]}
+    for table, fac, key in ((fetch, f_fac, "read_bytes"), (write, w_fac, "write_bytes")):
+        for name, (kib, cnt) in table.items():
+            short = name.split("(")[0].replace("void ", "").replace("pkm::", "")
+            stage = stage_of(short)
+            if stage is None:
+                continue
+            b = int(round(kib * fac * 1024))
+            stages[stage][key] += b
+            stages[stage]["kernels"].setdefault(short, {})[key] = b
     out = {"source_sha256": source_hash(), "workload": workload,
            "calibration": {"copy_bytes_read": copy_kib * 1024, "copy_bytes_written": copy_kib * 1024,
                            "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},

@@ -29,6 +29,8 @@
 //      block and 64 columns of one codebook and accumulates the product of
 //      the sparse g matrix (densified per 32-token step in LDS) with q in
 //      MFMA registers; a last kernel sums the token blocks' partials.
+#include <type_traits>
+
 #include "pkm_device.hpp"
 #include "pkm_kernels.hpp"
 #include "pkm_scratch.hpp"
@@ -441,9 +443,12 @@ __device__ __forceinline__ void seg_flush_sgd(float (&acc)[MCH][EPC], const floa
 
 // SGD: the value rows are updated in place (values is then written, and
 // dvalues is split_acc, see seg_flush_sgd); dw is the same in every mode.
+template <typename DT, bool SGD>
+using ValuesPtr = typename std::conditional<SGD, DT *, const DT *>::type;
+
 template <typename DT, int MCH, int U, bool SGD>
 __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
-    const DT *values, const DT *__restrict__ dy, const int32_t *__restrict__ idx,
+    ValuesPtr<DT, SGD> values, const DT *__restrict__ dy, const int32_t *__restrict__ idx,
     const float *__restrict__ weights, const int32_t *__restrict__ order,
     const int32_t *__restrict__ start, float *__restrict__ dvalues, float *__restrict__ dw,
     int64_t picks, int HK, int d_v, int accumulate, float lr, int shift)
@@ -531,7 +536,7 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
     // the current run's sum leaves: stored, added, or (SGD) applied to its row
     auto flush = [&](bool exclusive) {
         if constexpr (SGD)
-            seg_flush_sgd<DT, MCH, EPC>(acc, vrow, const_cast<DT *>(values), dvalues, start, f_cur,
+            seg_flush_sgd<DT, MCH, EPC>(acc, vrow, values, dvalues, start, f_cur,
                                         d_v, nchunks, lane, exclusive, lr, shift);
         else
             seg_flush<MCH, EPC>(acc, dvalues, f_cur, d_v, nchunks, lane, exclusive, accumulate);
@@ -1182,8 +1187,11 @@ static hipError_t launch_seg_t(const void *values, const void *dy, const int32_t
 {
     const int shift = seg_shift(picks);
     const int64_t waves = (picks + (1 << shift) - 1) >> shift;
+    // SGD: the rows are written; launch_bwd_value_sgd's caller handed them over
+    // as writable memory (void *), only the shared signature carries const
+    const auto vptr = static_cast<ValuesPtr<DT, SGD>>(const_cast<void *>(values));
     hipLaunchKernelGGL((seg_value_kernel<DT, MCH, U, SGD>), dim3(grid1d(waves, kSegWaves)),
-                       dim3(kSegWaves * kWave), 0, stream, static_cast<const DT *>(values),
+                       dim3(kSegWaves * kWave), 0, stream, vptr,
                        static_cast<const DT *>(dy), idx, weights, order, start, dvalues, dw, picks,
                        HK, d_v, accumulate, lr, shift);
     return hipGetLastError();

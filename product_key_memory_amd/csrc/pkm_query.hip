@@ -31,113 +31,129 @@ namespace pkm {
 // ---------------------------------------------------------------------------
 // GEMM
 // ---------------------------------------------------------------------------
-constexpr int kGBM = 128, kGBN = 128, kGBK = 32;
+constexpr int kGBN = 128, kGBK = 32;
 constexpr int kGThreads = 256;
+constexpr int kXcds = 8;          // workgroups are dealt to the XCDs in turn
+constexpr int kGroupM = 8;        // tile rows walked together on one XCD
 
+// kBf16: bf16 A and B.  kBf16SplitA: A given as two bf16 planes, hi + lo (a
+// float32 operand split once by its producer), two MFMAs per product.
+// kF32: float32 A and B on the float32 MFMA.
 enum GemmMode { kBf16 = 0, kBf16SplitA = 1, kF32 = 2 };
 
+// Per mode: LDS element type, 16-byte chunks per 32-wide K row (C), A planes,
+// and the rows of C a wave owns (WM; a workgroup is 2 x 2 waves: 2 WM rows by
+// 128 columns).
 template <int MODE> struct GTile;
-template <> struct GTile<kBf16> { typedef uint16_t E; static constexpr int C = 4; static constexpr int parts = 1; };
-template <> struct GTile<kBf16SplitA> { typedef uint16_t E; static constexpr int C = 4; static constexpr int parts = 2; };
-template <> struct GTile<kF32> { typedef float E; static constexpr int C = 8; static constexpr int parts = 1; };
+template <> struct GTile<kBf16> { typedef uint16_t E; static constexpr int C = 4, parts = 1, WM = 128; };
+template <> struct GTile<kBf16SplitA> { typedef uint16_t E; static constexpr int C = 4, parts = 2, WM = 128; };
+template <> struct GTile<kF32> { typedef float E; static constexpr int C = 8, parts = 1, WM = 64; };
 
-// element offset of (row, k) in a [rows][32] tile whose 16-byte chunks are
-// XOR-swizzled by row (the 16 rows an MFMA operand read touches hit distinct banks)
+// The 16-byte chunks of a [rows][32] tile are XOR-swizzled by row so that an
+// MFMA operand read (rows r16 = 0..15 of the fragment, chunk kg = 0..3 by lane
+// group) is free of bank conflicts.  bf16 (4 chunks, 64-byte rows): chunk kg
+// of row r sits at position kg ^ swz4(r mod 16), which gives distinct banks to
+// any 8 consecutive rows (32 banks, 8 lanes per cycle) and to any 4 rows of
+// one residue mod 4 in 16 (64 banks, 16 lanes per cycle).  float32 (8 chunks,
+// 128-byte rows): position kg ^ ((r / 2) mod 8).
+__device__ __forceinline__ int swz4(int r)
+{
+    return ((r >> 1) ^ (r >> 3)) & 3;
+}
+
+// element offset of (row, k) in such a tile
 template <int C>
 __device__ __forceinline__ int g_cell(int row, int k)
 {
     constexpr int EPC = kGBK / C;
-    return row * kGBK + (((k / EPC) ^ ((row / (16 / C)) % C)) * EPC) + k % EPC;
+    const int s = C == 4 ? swz4(row & 15) : (row / 2) % 8;
+    return row * kGBK + (((k / EPC) ^ s) * EPC) + k % EPC;
 }
 
-// One operand's staging: T elements, stored K-contiguous (KMAJ = false: [R][K])
-// or R-contiguous (KMAJ = true: [K][R]); R = the operand's M or N.  Each
-// thread moves 16-byte pieces (8 bf16 or 4 float32); K-contiguous pieces go
-// to LDS whole (one 16- or 8-byte store), R-contiguous ones are transposed
-// element by element.
+// The output tile (tx, ty) and K slice tz of this workgroup.  Workgroup ids
+// are renumbered so that each XCD gets one contiguous range of tiles, walked
+// kGroupM tile rows at a time: tiles that share A and B panels run on the
+// same XCD at about the same time and meet in its L2.  A bijection for any
+// grid, so correctness does not depend on how workgroups are dealt.
+__device__ __forceinline__ void gemm_tile(int &tx, int &ty, int &tz)
+{
+    const int gx = gridDim.x, gy = gridDim.y;
+    const int total = gx * gy * (int)gridDim.z;
+    const int g = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    const int q = total / kXcds, r = total % kXcds;
+    const int xcd = g % kXcds, pos = g / kXcds;
+    const int id = xcd < r ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
+    const int per_z = gx * gy;
+    tz = id / per_z;
+    const int l = id % per_z;
+    const int span = kGroupM * gx;
+    const int first = l / span * kGroupM;
+    const int rows = gy - first < kGroupM ? gy - first : kGroupM;
+    ty = first + l % span % rows;
+    tx = l % span / rows;
+}
+
+// lane holds D rows 4 (l / 16) + e, column l % 16 of each 16 x 16 tile
+template <int FI>
+__device__ __forceinline__ void gemm_store(const floatx4 (&acc)[FI][4], float *__restrict__ Cm, int M,
+                                           int N, int m0, int n0, int lane)
+{
+    const int r16 = lane & 15, kg = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = n0 + 16 * j + r16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = m0 + 16 * i + 4 * kg + e;
+                if (row < M && col < N)
+                    Cm[(int64_t)row * N + col] = acc[i][j][e];
+            }
+        }
+}
+
+// ---- register-staged kernel (any K, any alignment; float32 operands) -------
+// One operand's staging, ROWS x 32 elements of a K-contiguous [R][K] array:
+// each thread loads 16-byte pieces (8 bf16 or 4 float32) into registers, then
+// stores them to LDS whole.  Pieces past R or K read as zeros.
 template <typename T> struct GRaw;
 template <> struct GRaw<bf16_t> { static constexpr int V = 8; };
 template <> struct GRaw<float> { static constexpr int V = 4; };
 
-template <typename T, bool KMAJ, int MODE, bool SPLIT>
+template <int ROWS, typename T, typename E>
 struct GStage {
     static constexpr int V = GRaw<T>::V;                    // elements per 16-byte load
-    static constexpr int loads = kGBM * kGBK / V / kGThreads;
+    static constexpr int CPR = kGBK / V;                    // pieces per row
+    static constexpr int C = 16 / sizeof(E) == 8 ? 4 : 8;   // chunks per LDS row
+    static constexpr int loads = ROWS * CPR / kGThreads;
     uint4 raw[loads];
-    __device__ static void coords(int u, int &r, int &k)
-    {
-        if (!KMAJ) {        // V consecutive k of one row
-            r = u / (kGBK / V);
-            k = (u % (kGBK / V)) * V;
-        } else {            // V consecutive rows of one k
-            k = u / (kGBM / V);
-            r = (u % (kGBM / V)) * V;
-        }
-    }
     __device__ void load(const T *__restrict__ src, int64_t ld, int r0, int R, int k0, int K, int tid)
     {
 #pragma unroll
         for (int l = 0; l < loads; ++l) {
-            int r, k;
-            coords(tid + l * kGThreads, r, k);
-            const int gr = r0 + r, gk = k0 + k;
-            raw[l] = (gr < R && gk < K)
-                         ? *reinterpret_cast<const uint4 *>(!KMAJ ? src + (int64_t)gr * ld + gk
-                                                                  : src + (int64_t)gk * ld + gr)
-                         : make_uint4(0u, 0u, 0u, 0u);
+            const int u = tid + l * kGThreads;
+            const int gr = r0 + u / CPR, gk = k0 + (u % CPR) * V;
+            raw[l] = (gr < R && gk < K) ? *reinterpret_cast<const uint4 *>(src + (int64_t)gr * ld + gk)
+                                        : make_uint4(0u, 0u, 0u, 0u);
         }
     }
-    __device__ void store(typename GTile<MODE>::E *hi, typename GTile<MODE>::E *lo, int tid) const
+    __device__ void store(E *dst, int tid) const
     {
-        constexpr int C = GTile<MODE>::C;
 #pragma unroll
         for (int l = 0; l < loads; ++l) {
-            int r, k;
-            coords(tid + l * kGThreads, r, k);
-            if constexpr (!KMAJ && (MODE == kF32 || (sizeof(T) == 2 && !SPLIT))) {
-                // a whole chunk (8 bf16 / 4 float32) in place
-                *reinterpret_cast<uint4 *>(hi + g_cell<C>(r, k)) = raw[l];
-            } else if constexpr (!KMAJ && SPLIT) {
-                // 4 float32 -> 4 bf16 hi + 4 bf16 lo, half a chunk each
-                const uint32_t w[4] = {raw[l].x, raw[l].y, raw[l].z, raw[l].w};
-                uint32_t h[4], o[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float f = __uint_as_float(w[e]);
-                    h[e] = f32_to_bf16_bits(f);
-                    o[e] = f32_to_bf16_bits(f - bf16_to_f32(h[e]));
-                }
-                *reinterpret_cast<uint2 *>(hi + g_cell<C>(r, k)) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-                *reinterpret_cast<uint2 *>(lo + g_cell<C>(r, k)) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
-            } else {
-                float x[V];
-                if constexpr (V == 8)
-                    unpack16(raw[l], x);
-                else {
-                    x[0] = __uint_as_float(raw[l].x); x[1] = __uint_as_float(raw[l].y);
-                    x[2] = __uint_as_float(raw[l].z); x[3] = __uint_as_float(raw[l].w);
-                }
-#pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    const int at = g_cell<C>(KMAJ ? r + e : r, KMAJ ? k : k + e);
-                    if constexpr (MODE == kF32) {
-                        hi[at] = x[e];
-                    } else {
-                        const uint32_t hb = f32_to_bf16_bits(x[e]);
-                        hi[at] = (uint16_t)hb;
-                        if constexpr (SPLIT)
-                            lo[at] = (uint16_t)f32_to_bf16_bits(x[e] - bf16_to_f32(hb));
-                    }
-                }
-            }
+            const int u = tid + l * kGThreads;
+            *reinterpret_cast<uint4 *>(dst + g_cell<C>(u / CPR, (u % CPR) * V)) = raw[l];
         }
     }
 };
 
-// blockIdx.z = a slice of K (split-K): slice z covers [z k_slice, (z+1) k_slice)
-// and writes its own C at Cm + z M N.
-template <typename TA, typename TB, bool A_KM, bool B_KN, int MODE>
+// C[M][N] (+ slice z of K) = sum_k A[m][k] B[n][k] (A = A + A2 for the split
+// mode); slice z covers [z k_slice, (z+1) k_slice) and writes its own C at
+// Cm + z M N.
+template <typename TA, typename TB, int MODE>
 __global__ __launch_bounds__(kGThreads) void gemm_kernel(const TA *__restrict__ A,
+                                                         const TA *__restrict__ A2,
                                                          const TB *__restrict__ B,
                                                          float *__restrict__ Cm, int M, int N,
                                                          int K, int64_t lda, int64_t ldb,
@@ -146,44 +162,55 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(const TA *__restrict__ 
     typedef typename GTile<MODE>::E E;
     constexpr int C = GTile<MODE>::C;
     constexpr int PA = GTile<MODE>::parts;
-    constexpr int TILE = kGBM * kGBK;
-    __shared__ __align__(16) E lds[2][(PA + 1) * TILE];
+    constexpr int WM = GTile<MODE>::WM, BM = 2 * WM, FI = WM / 16;
+    constexpr int TILE_A = BM * kGBK, TILE_B = kGBN * kGBK;
+    __shared__ __align__(16) E lds[2][PA * TILE_A + TILE_B];
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-    const int m0 = blockIdx.y * kGBM, n0 = blockIdx.x * kGBN;
-    const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+    int tx, ty, tz;
+    gemm_tile(tx, ty, tz);
+    const int m0 = ty * BM, n0 = tx * kGBN;
+    const int wm = (wave & 1) * WM, wn = (wave >> 1) * 64;
     const int r16 = lane & 15, kg = lane >> 4;
 
-    GStage<TA, A_KM, MODE, MODE == kBf16SplitA> sa;
-    GStage<TB, B_KN, MODE, false> sb;
-    floatx4 acc[4][4];
+    GStage<BM, TA, E> sa[PA];
+    GStage<kGBN, TB, E> sb;
+    floatx4 acc[FI][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    const int kb = blockIdx.z * k_slice;
+    const int kb = tz * k_slice;
     const int ke = kb + k_slice < K ? kb + k_slice : K;
-    Cm += (int64_t)blockIdx.z * M * N;
+    Cm += (int64_t)tz * M * N;
     const int nk = (ke - kb + kGBK - 1) / kGBK;
-    sa.load(A, lda, m0, M, kb, ke, tid);
-    sb.load(B, ldb, n0, N, kb, ke, tid);
-    sa.store(lds[0], lds[0] + TILE, tid);
-    sb.store(lds[0] + PA * TILE, nullptr, tid);
+    auto load = [&](int k0) {
+        sa[0].load(A, lda, m0, M, k0, ke, tid);
+        if constexpr (PA == 2)
+            sa[1].load(A2, lda, m0, M, k0, ke, tid);
+        sb.load(B, ldb, n0, N, k0, ke, tid);
+    };
+    auto store = [&](E *dst) {
+#pragma unroll
+        for (int pa = 0; pa < PA; ++pa)
+            sa[pa].store(dst + pa * TILE_A, tid);
+        sb.store(dst + PA * TILE_A, tid);
+    };
+    load(kb);
+    store(lds[0]);
     __syncthreads();
     for (int c = 0; c < nk; ++c) {
-        if (c + 1 < nk) {
-            sa.load(A, lda, m0, M, kb + (c + 1) * kGBK, ke, tid);
-            sb.load(B, ldb, n0, N, kb + (c + 1) * kGBK, ke, tid);
-        }
-        const E *ah = lds[c & 1], *al = lds[c & 1] + TILE, *bt = lds[c & 1] + PA * TILE;
+        if (c + 1 < nk)
+            load(kb + (c + 1) * kGBK);
+        const E *at = lds[c & 1], *bt = lds[c & 1] + PA * TILE_A;
         if constexpr (MODE == kF32) {
-            float4 a[4][2], b[4][2];
+            float4 a[FI][2], b[4][2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < FI; ++i) {
                 const int row = wm + 16 * i + r16;
-                a[i][0] = *reinterpret_cast<const float4 *>(ah + g_cell<C>(row, 4 * kg));
-                a[i][1] = *reinterpret_cast<const float4 *>(ah + g_cell<C>(row, 4 * kg + 16));
+                a[i][0] = *reinterpret_cast<const float4 *>(at + g_cell<C>(row, 4 * kg));
+                a[i][1] = *reinterpret_cast<const float4 *>(at + g_cell<C>(row, 4 * kg + 16));
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -192,7 +219,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(const TA *__restrict__ 
                 b[j][1] = *reinterpret_cast<const float4 *>(bt + g_cell<C>(row, 4 * kg + 16));
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < FI; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -203,52 +230,284 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(const TA *__restrict__ 
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][h].w, b[j][h].w, acc[i][j], 0, 0, 0);
                     }
         } else {
-            uint4 a[4][PA], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = wm + 16 * i + r16;
-                a[i][0] = *reinterpret_cast<const uint4 *>(ah + g_cell<C>(row, 8 * kg));
-                if constexpr (PA == 2)
-                    a[i][PA - 1] = *reinterpret_cast<const uint4 *>(al + g_cell<C>(row, 8 * kg));
-            }
+            // B fragments stay in registers; A fragments are read one row of
+            // MFMA tiles at a time
+            uint4 b[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 b[j] = *reinterpret_cast<const uint4 *>(bt + g_cell<C>(wn + 16 * j + r16, 8 * kg));
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < FI; ++i) {
+                const int row = wm + 16 * i + r16;
+                uint4 a[PA];
+#pragma unroll
+                for (int pa = 0; pa < PA; ++pa)
+                    a[pa] = *reinterpret_cast<const uint4 *>(at + pa * TILE_A + g_cell<C>(row, 8 * kg));
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
                     for (int pa = 0; pa < PA; ++pa)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, a[i][pa]), __builtin_bit_cast(bf16x8, b[j]),
+                            __builtin_bit_cast(bf16x8, a[pa]), __builtin_bit_cast(bf16x8, b[j]),
                             acc[i][j], 0, 0, 0);
-        }
-        if (c + 1 < nk) {
-            E *dst = lds[(c + 1) & 1];
-            sa.store(dst, dst + TILE, tid);
-            sb.store(dst + PA * TILE, nullptr, tid);
-        }
-        __syncthreads();
-    }
-    // lane holds D rows 4 (l / 16) + e, column l % 16 of each 16 x 16 tile
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = n0 + wn + 16 * j + r16;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = m0 + wm + 16 * i + 4 * kg + e;
-                if (row < M && col < N)
-                    Cm[(int64_t)row * N + col] = acc[i][j][e];
             }
         }
+        if (c + 1 < nk)
+            store(lds[(c + 1) & 1]);
+        __syncthreads();
+    }
+    gemm_store<FI>(acc, Cm, M, N, m0 + wm, n0 + wn, lane);
 }
 
-// C = A B^T with both operands K-contiguous unless A_KM / B_KN.  With
-// splits > 1 the K range is cut into `splits` slices whose partial products
-// go to `parts` ([splits][M][N]) and are then summed into C.
+// ---- direct-to-LDS kernel (bf16 operands, K a multiple of 32) --------------
+// The operand tiles go from global memory straight into LDS (one
+// global_load_lds_dwordx4 per 16 rows: lane l writes bytes 16 l .. 16 l + 15 of
+// a 1 KB block, i.e. row l / 4, chunk position l % 4, and fetches the chunk
+// the swizzle puts there), through a ring of NS stages: NS - 1 stages are
+// in flight while one is read.  A stage is complete once this wave's own loads
+// of it have retired (s_waitcnt vmcnt) and every wave has passed the barrier
+// that follows.  The MFMA operands are then read from LDS by one asm block
+// that waits for its own reads, so the compiler adds no wait on the loads of
+// later stages before it.  Its outputs are early-clobber: the first read's
+// destination must not share registers with the addresses of the later ones.
+template <int FI, int PA> struct GFrag {
+    uint4 a[PA][FI], b[4];
+    __device__ void read(uint32_t a_addr, uint32_t b_addr);
+};
+
+template <>
+__device__ __forceinline__ void GFrag<4, 1>::read(uint32_t a_addr, uint32_t b_addr)
+{
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:0\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\t"
+        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b128 %4, %9 offset:0\n\t"
+        "ds_read_b128 %5, %9 offset:1024\n\t"
+        "ds_read_b128 %6, %9 offset:2048\n\t"
+        "ds_read_b128 %7, %9 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[0][3]),
+          "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
+        : "v"(a_addr), "v"(b_addr)
+        : "memory");
+}
+
+template <>
+__device__ __forceinline__ void GFrag<4, 2>::read(uint32_t a_addr, uint32_t b_addr)
+{
+    asm volatile(
+        "ds_read_b128 %0, %12 offset:0\n\t"
+        "ds_read_b128 %1, %12 offset:1024\n\t"
+        "ds_read_b128 %2, %12 offset:2048\n\t"
+        "ds_read_b128 %3, %12 offset:3072\n\t"
+        "ds_read_b128 %4, %12 offset:8192\n\t"
+        "ds_read_b128 %5, %12 offset:9216\n\t"
+        "ds_read_b128 %6, %12 offset:10240\n\t"
+        "ds_read_b128 %7, %12 offset:11264\n\t"
+        "ds_read_b128 %8, %13 offset:0\n\t"
+        "ds_read_b128 %9, %13 offset:1024\n\t"
+        "ds_read_b128 %10, %13 offset:2048\n\t"
+        "ds_read_b128 %11, %13 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[0][3]),
+          "=&v"(a[1][0]), "=&v"(a[1][1]), "=&v"(a[1][2]), "=&v"(a[1][3]),
+          "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
+        : "v"(a_addr), "v"(b_addr)
+        : "memory");
+}
+
+template <>
+__device__ __forceinline__ void GFrag<8, 1>::read(uint32_t a_addr, uint32_t b_addr)
+{
+    asm volatile(
+        "ds_read_b128 %0, %12 offset:0\n\t"
+        "ds_read_b128 %1, %12 offset:1024\n\t"
+        "ds_read_b128 %2, %12 offset:2048\n\t"
+        "ds_read_b128 %3, %12 offset:3072\n\t"
+        "ds_read_b128 %4, %12 offset:4096\n\t"
+        "ds_read_b128 %5, %12 offset:5120\n\t"
+        "ds_read_b128 %6, %12 offset:6144\n\t"
+        "ds_read_b128 %7, %12 offset:7168\n\t"
+        "ds_read_b128 %8, %13 offset:0\n\t"
+        "ds_read_b128 %9, %13 offset:1024\n\t"
+        "ds_read_b128 %10, %13 offset:2048\n\t"
+        "ds_read_b128 %11, %13 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[0][3]),
+          "=&v"(a[0][4]), "=&v"(a[0][5]), "=&v"(a[0][6]), "=&v"(a[0][7]),
+          "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
+        : "v"(a_addr), "v"(b_addr)
+        : "memory");
+}
+
+template <>
+__device__ __forceinline__ void GFrag<8, 2>::read(uint32_t a_addr, uint32_t b_addr)
+{
+    asm volatile(
+        "ds_read_b128 %0, %20 offset:0\n\t"
+        "ds_read_b128 %1, %20 offset:1024\n\t"
+        "ds_read_b128 %2, %20 offset:2048\n\t"
+        "ds_read_b128 %3, %20 offset:3072\n\t"
+        "ds_read_b128 %4, %20 offset:4096\n\t"
+        "ds_read_b128 %5, %20 offset:5120\n\t"
+        "ds_read_b128 %6, %20 offset:6144\n\t"
+        "ds_read_b128 %7, %20 offset:7168\n\t"
+        "ds_read_b128 %8, %20 offset:16384\n\t"
+        "ds_read_b128 %9, %20 offset:17408\n\t"
+        "ds_read_b128 %10, %20 offset:18432\n\t"
+        "ds_read_b128 %11, %20 offset:19456\n\t"
+        "ds_read_b128 %12, %20 offset:20480\n\t"
+        "ds_read_b128 %13, %20 offset:21504\n\t"
+        "ds_read_b128 %14, %20 offset:22528\n\t"
+        "ds_read_b128 %15, %20 offset:23552\n\t"
+        "ds_read_b128 %16, %21 offset:0\n\t"
+        "ds_read_b128 %17, %21 offset:1024\n\t"
+        "ds_read_b128 %18, %21 offset:2048\n\t"
+        "ds_read_b128 %19, %21 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[0][3]),
+          "=&v"(a[0][4]), "=&v"(a[0][5]), "=&v"(a[0][6]), "=&v"(a[0][7]),
+          "=&v"(a[1][0]), "=&v"(a[1][1]), "=&v"(a[1][2]), "=&v"(a[1][3]),
+          "=&v"(a[1][4]), "=&v"(a[1][5]), "=&v"(a[1][6]), "=&v"(a[1][7]),
+          "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
+        : "v"(a_addr), "v"(b_addr)
+        : "memory");
+}
+
+// 16 bytes per lane from global memory into LDS: lane l's bytes land at
+// dst + 16 l (dst is the same for the whole wave)
+__device__ __forceinline__ void lds_dma16(const void *src, void *dst)
+{
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+// s_waitcnt on the vector memory counter alone (vmcnt bits 3:0 and 15:14;
+// expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// A workgroup is 2 x NWN waves, each owning WM x 64 of C: 2 WM rows by 64 NWN
+// columns.
+template <int MODE, int WM, int NWN, int NS>
+__global__ __launch_bounds__(2 * NWN * kWave) void gemm_lds_kernel(const bf16_t *__restrict__ A,
+                                                             const bf16_t *__restrict__ A2,
+                                                             const bf16_t *__restrict__ B,
+                                                             float *__restrict__ Cm, int M, int N,
+                                                             int K, int64_t lda, int64_t ldb,
+                                                             int k_slice)
+{
+    constexpr int PA = GTile<MODE>::parts;
+    constexpr int WAVES = 2 * NWN;
+    constexpr int BM = 2 * WM, BN = 64 * NWN, FI = WM / 16;
+    constexpr int ROW_BYTES = kGBK * 2;                         // 64
+    constexpr int TILE_A = BM * ROW_BYTES, TILE_B = BN * ROW_BYTES;
+    constexpr int STAGE = PA * TILE_A + TILE_B;
+    constexpr int LA = BM / 16 / WAVES, LB = BN / 16 / WAVES;   // 1 KB blocks per wave
+    static_assert(LA * 16 * WAVES == BM && LB * 16 * WAVES == BN, "whole blocks per wave");
+    constexpr int LPS = PA * LA + LB;                           // loads per wave per stage
+    static_assert(NS >= 2 && NS <= 4 && (NS - 2) * LPS < 64, "ring depth");
+    __shared__ __align__(1024) unsigned char lds[NS * STAGE];
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    int tx, ty, tz;
+    gemm_tile(tx, ty, tz);
+    const int m0 = ty * BM, n0 = tx * BN;
+    const int wm = (wave & 1) * WM, wn = (wave >> 1) * 64;
+    const int r16 = lane & 15, kg = lane >> 4;
+
+    // this lane's source rows (clamped into the matrix: rows past M or N are
+    // computed from repeated data and never stored) and chunk
+    const int lrow = lane >> 2, lchunk = (lane & 3) ^ swz4(lrow);
+    const bf16_t *pa[PA][LA];
+    const bf16_t *pb[LB];
+#pragma unroll
+    for (int l = 0; l < LA; ++l) {
+        int gr = m0 + (wave * LA + l) * 16 + lrow;
+        gr = gr < M ? gr : M - 1;
+        pa[0][l] = A + (int64_t)gr * lda + 8 * lchunk;
+        if constexpr (PA == 2)
+            pa[1][l] = A2 + (int64_t)gr * lda + 8 * lchunk;
+    }
+#pragma unroll
+    for (int l = 0; l < LB; ++l) {
+        int gr = n0 + (wave * LB + l) * 16 + lrow;
+        gr = gr < N ? gr : N - 1;
+        pb[l] = B + (int64_t)gr * ldb + 8 * lchunk;
+    }
+    const int kb = tz * k_slice;
+    const int ke = kb + k_slice < K ? kb + k_slice : K;
+    Cm += (int64_t)tz * M * N;
+    const int nk = (ke - kb) / kGBK;
+
+    auto issue = [&](int c) {
+        unsigned char *st = lds + (c % NS) * STAGE;
+        const int k0 = kb + c * kGBK;
+#pragma unroll
+        for (int p = 0; p < PA; ++p)
+#pragma unroll
+            for (int l = 0; l < LA; ++l)
+                lds_dma16(pa[p][l] + k0, st + p * TILE_A + (wave * LA + l) * 1024);
+#pragma unroll
+        for (int l = 0; l < LB; ++l)
+            lds_dma16(pb[l] + k0, st + PA * TILE_A + (wave * LB + l) * 1024);
+    };
+
+    floatx4 acc[FI][4];
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // byte addresses of this lane's fragments in stage 0 (the swizzle of rows
+    // wm + 16 i + r16 does not depend on i)
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+    const uint32_t swz = (uint32_t)((kg ^ swz4(r16)) * 16);
+    const uint32_t a_off = lds0 + (uint32_t)((wm + r16) * ROW_BYTES) + swz;
+    const uint32_t b_off = lds0 + (uint32_t)(PA * TILE_A + (wn + r16) * ROW_BYTES) + swz;
+
+#pragma unroll
+    for (int c = 0; c < NS - 1; ++c)
+        if (c < nk)
+            issue(c);
+    for (int c = 0; c < nk; ++c) {
+        // stage c is this wave's oldest outstanding one: wait until at most
+        // the loads of the stages issued after it are in flight
+        const int after = nk - 1 - c < NS - 2 ? nk - 1 - c : NS - 2;
+        if (after >= 2)
+            wait_vmcnt<2 * LPS>();
+        else if (after == 1)
+            wait_vmcnt<LPS>();
+        else
+            wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        // every wave is done with stage c - 1: refill its buffer
+        if (c + NS - 1 < nk)
+            issue(c + NS - 1);
+        GFrag<FI, PA> f;
+        const uint32_t st = (uint32_t)((c % NS) * STAGE);
+        f.read(a_off + st, b_off + st);
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int p = 0; p < PA; ++p)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, f.a[p][i]), __builtin_bit_cast(bf16x8, f.b[j]),
+                        acc[i][j], 0, 0, 0);
+    }
+    gemm_store<FI>(acc, Cm, M, N, m0 + wm, n0 + wn, lane);
+}
+
+// C = A B^T with both operands K-contiguous.  With splits > 1 the K range is
+// cut into `splits` slices whose partial products go to `parts`
+// ([splits][M][N]) and are then summed into C.
 __global__ void sum_slices_kernel(const float *__restrict__ parts, int splits, int64_t count,
                                   float *__restrict__ C)
 {
@@ -261,9 +520,26 @@ __global__ void sum_slices_kernel(const float *__restrict__ parts, int splits, i
     }
 }
 
-template <typename TA, typename TB, bool A_KM, bool B_KN, int MODE>
-static hipError_t gemm(const TA *A, const TB *B, float *Cm, int M, int N, int K, int64_t lda,
-                       int64_t ldb, hipStream_t stream, int splits = 1, float *parts = nullptr)
+template <int MODE>
+static int gemm_rows_per_tile()
+{
+    return 2 * GTile<MODE>::WM;
+}
+
+// tile shape (2 WM x 64 NWN) and ring depth of the direct-to-LDS kernel per mode
+template <int MODE> struct GLds;
+template <> struct GLds<kBf16> { static constexpr int WM = 128, NWN = 2, NS = 3; };
+template <> struct GLds<kBf16SplitA> { static constexpr int WM = 128, NWN = 2, NS = 2; };
+
+static bool aligned16(const void *p)
+{
+    return ((uintptr_t)p & 15) == 0;
+}
+
+template <typename TA, typename TB, int MODE>
+static hipError_t gemm(const TA *A, const TA *A2, const TB *B, float *Cm, int M, int N, int K,
+                       int64_t lda, int64_t ldb, hipStream_t stream, int splits = 1,
+                       float *parts = nullptr)
 {
     int k_slice = K;
     if (splits > 1) {
@@ -271,10 +547,29 @@ static hipError_t gemm(const TA *A, const TB *B, float *Cm, int M, int N, int K,
         k_slice = (k_slice + kGBK - 1) / kGBK * kGBK;
         splits = (K + k_slice - 1) / k_slice;
     }
-    const dim3 grid((unsigned)((N + kGBN - 1) / kGBN), (unsigned)((M + kGBM - 1) / kGBM),
-                    (unsigned)splits);
-    hipLaunchKernelGGL((gemm_kernel<TA, TB, A_KM, B_KN, MODE>), grid, dim3(kGThreads), 0, stream,
-                       A, B, splits > 1 ? parts : Cm, M, N, K, lda, ldb, k_slice);
+    float *out = splits > 1 ? parts : Cm;
+    bool direct = false;
+    if constexpr (MODE != kF32)
+        direct = K % kGBK == 0 && lda % 8 == 0 && ldb % 8 == 0 && aligned16(A) && aligned16(B) &&
+                 (A2 == nullptr || aligned16(A2));
+    if constexpr (MODE != kF32) {
+        if (direct) {
+            typedef GLds<MODE> G;
+            const int BM = 2 * G::WM, BN = 64 * G::NWN;
+            const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM),
+                            (unsigned)splits);
+            hipLaunchKernelGGL((gemm_lds_kernel<MODE, G::WM, G::NWN, G::NS>), grid,
+                               dim3(2 * G::NWN * kWave), 0, stream, A, A2, B, out, M, N, K, lda, ldb,
+                               k_slice);
+        }
+    }
+    if (!direct) {
+        const int BM = gemm_rows_per_tile<MODE>();
+        const dim3 grid((unsigned)((N + kGBN - 1) / kGBN), (unsigned)((M + BM - 1) / BM),
+                        (unsigned)splits);
+        hipLaunchKernelGGL((gemm_kernel<TA, TB, MODE>), grid, dim3(kGThreads), 0, stream, A, A2, B,
+                           out, M, N, K, lda, ldb, k_slice);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || splits <= 1)
         return err;
@@ -285,7 +580,7 @@ static hipError_t gemm(const TA *A, const TB *B, float *Cm, int M, int N, int K,
     return hipGetLastError();
 }
 
-// out[c][r] = in[r][c] for an R x C matrix of 2- or 4-byte elements, through
+// out[c][r] = in[r][c] for an R x C matrix of 4-byte elements, through
 // 64 x 64 LDS tiles (both sides coalesced); out rows have pitch ldo >= R and
 // their tail r in [R, ldo) is written with zeros.
 template <typename E>
@@ -308,12 +603,64 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E *__restrict__ in
 }
 
 // K of the GEMM that runs over the tokens (dW = dz^T x): the token count
-// rounded up to 8, so that every 16-byte piece of a transposed row (8 bf16 or
-// 4 float32 elements) lies inside the row and is 16-byte aligned; the padding
-// holds zeros.
+// rounded up to 32, a whole number of 32-wide K steps of 16-byte aligned
+// pieces (8 bf16 or 4 float32 elements), plus 32 more when that is a multiple
+// of 512 (rows a power-of-two number of kilobytes apart put the 16 rows one
+// load touches into the same memory channels); the padding holds zeros.
 static int64_t token_pitch(int64_t T)
 {
-    return (T + 7) & ~(int64_t)7;
+    const int64_t p = (T + 31) & ~(int64_t)31;
+    return p % 512 == 0 ? p + 32 : p;
+}
+
+// 16-bit elements: 64 x 64 tiles moved in 16-byte pieces on both sides.  The
+// tile sits in LDS with a row pitch of 65 elements, so that the 8 rows 8
+// apart that one read instruction touches (per column) fall in distinct banks.
+constexpr int kTrPitch = 65;
+
+// out[(c0 + c) ldo + r0 + r] = t[r][c] for the 64 x 64 tile t, 8 consecutive
+// r per lane (one 16-byte store; ldo and r0 are multiples of 8): columns past
+// C and rows past ldo are skipped.
+__device__ __forceinline__ void tile16_store_t(const uint16_t (*t)[kTrPitch], uint16_t *__restrict__ out,
+                                               int64_t r0, int64_t c0, int64_t C, int64_t ldo, int tid)
+{
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int c = pass * 32 + tid / 8, rs = (tid % 8) * 8;
+        if (c0 + c >= C || r0 + rs >= ldo)
+            continue;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w[e] = (uint32_t)t[rs + 2 * e][c] | ((uint32_t)t[rs + 2 * e + 1][c] << 16);
+        *reinterpret_cast<uint4 *>(out + (c0 + c) * ldo + r0 + rs) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+// out[c][r] = in[r][c] for an R x C matrix of 16-bit elements (C a multiple
+// of 8), out pitch ldo >= R (a multiple of 8), the tail r in [R, ldo) zeros
+__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t *__restrict__ in,
+                                                          uint16_t *__restrict__ out, int64_t R,
+                                                          int64_t C, int64_t ldo)
+{
+    __shared__ uint16_t tile[64][kTrPitch];
+    const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int r = pass * 32 + tid / 8, cs = (tid % 8) * 8;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (r0 + r < R && c0 + cs < C)
+            v = *reinterpret_cast<const uint4 *>(in + (r0 + r) * C + c0 + cs);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            tile[r][cs + 2 * e] = (uint16_t)w[e];
+            tile[r][cs + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+        }
+    }
+    __syncthreads();
+    tile16_store_t(tile, out, r0, c0, C, ldo, tid);
 }
 
 template <typename E>
@@ -323,7 +670,12 @@ static hipError_t transpose(const E *in, E *out, int64_t R, int64_t C, hipStream
     if (ldo < 0)
         ldo = R;
     const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((ldo + 63) / 64));
-    hipLaunchKernelGGL((transpose_kernel<E>), grid, dim3(256), 0, stream, in, out, R, C, ldo);
+    if constexpr (sizeof(E) == 2)
+        hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, stream,
+                           reinterpret_cast<const uint16_t *>(in), reinterpret_cast<uint16_t *>(out), R,
+                           C, ldo);
+    else
+        hipLaunchKernelGGL((transpose_kernel<E>), grid, dim3(256), 0, stream, in, out, R, C, ldo);
     return hipGetLastError();
 }
 
@@ -557,6 +909,61 @@ __global__ void bn_bwd_apply_kernel(const float *__restrict__ z, const float *__
     }
 }
 
+// The same step for bf16 storage, fused with the transposes the dW product
+// needs: over a 64 x 64 tile of (token, feature), dz is split into two bf16
+// planes, hi = bf16(dz) and lo = bf16(dz - hi) (the operand form of the bf16
+// products that follow), written row-major ([T][D], for dx) and transposed
+// ([D][Tp], for dW; tokens past T are zeros).  D is a multiple of 8.
+__global__ __launch_bounds__(256) void bn_bwd_apply_split_kernel(
+    const float *__restrict__ z, const float *__restrict__ dq, int64_t T, int D,
+    const float *__restrict__ mean, const float *__restrict__ rstd, const float *__restrict__ gamma,
+    const float *__restrict__ coef, uint16_t *__restrict__ dz_hi, uint16_t *__restrict__ dz_lo,
+    uint16_t *__restrict__ dzt_hi, uint16_t *__restrict__ dzt_lo, int64_t Tp)
+{
+    __shared__ uint16_t th[64][kTrPitch], tl[64][kTrPitch];
+    const int64_t r0 = (int64_t)blockIdx.y * 64;
+    const int c0 = blockIdx.x * 64, tid = threadIdx.x;
+    const int cl = 4 * (tid % 16), c = c0 + cl;           // this thread's 4 features
+    const bool cok = c < D;
+    float mu[4], rs[4], gr[4], k0[4], k1[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        mu[e] = cok ? mean[c + e] : 0.f;
+        rs[e] = cok ? rstd[c + e] : 0.f;
+        gr[e] = (gamma && cok ? gamma[c + e] : 1.f) * rs[e];
+        k0[e] = cok ? coef[2 * (c + e)] : 0.f;
+        k1[e] = cok ? coef[2 * (c + e) + 1] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = tid / 16 + 16 * j;
+        const int64_t t = r0 + r;
+        uint32_t h[4] = {0u, 0u, 0u, 0u}, l[4] = {0u, 0u, 0u, 0u};
+        if (t < T && cok) {
+            const float4 zv = *reinterpret_cast<const float4 *>(z + t * D + c);
+            const float4 gv = *reinterpret_cast<const float4 *>(dq + t * D + c);
+            const float zz[4] = {zv.x, zv.y, zv.z, zv.w}, gg[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float zh = (zz[e] - mu[e]) * rs[e];
+                const float o = gr[e] * (gg[e] - k0[e] - zh * k1[e]);
+                h[e] = f32_to_bf16_bits(o);
+                l[e] = f32_to_bf16_bits(o - bf16_to_f32(h[e]));
+            }
+            *reinterpret_cast<uint2 *>(dz_hi + t * D + c) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            *reinterpret_cast<uint2 *>(dz_lo + t * D + c) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            th[r][cl + e] = (uint16_t)h[e];
+            tl[r][cl + e] = (uint16_t)l[e];
+        }
+    }
+    __syncthreads();
+    tile16_store_t(th, dzt_hi, r0, c0, D, Tp, tid);
+    tile16_store_t(tl, dzt_lo, r0, c0, D, Tp, tid);
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -579,17 +986,22 @@ QueryScratch query_scratch(int64_t T, int d_model, int D, int backward, int elt)
     S.off_wt = a256(S.off_dzt + (size_t)Tp * D * 4);
     S.off_xt = a256(S.off_wt + (size_t)D * d_model * elt);
     S.off_dwp = a256(S.off_xt + (size_t)Tp * d_model * elt);
-    S.dw_splits = dw_splits(T, d_model, D);
+    S.dw_splits = dw_splits(T, d_model, D, elt);
     S.total = backward ? a256(S.off_dwp + (size_t)S.dw_splits * D * d_model * 4) : S.off_coef;
     return S;
 }
 
-// dW = dz^T x has only (D / 128) (d_model / 128) output tiles and a long K
-// (the tokens): cut K so that about 1024 workgroups run.
-int dw_splits(int64_t T, int d_model, int D)
+// dW = dz^T x has only (D / BM) (d_model / BN) output tiles and a long K (the
+// tokens): cut K so that about kDwWorkgroups workgroups run.  (bf16 tiles are
+// those of the direct-to-LDS kernel; when a product falls back to the
+// register-staged one, the split count is only less well matched.)
+constexpr int kDwWorkgroups = 1024;
+int dw_splits(int64_t T, int d_model, int D, int elt)
 {
-    const int64_t tiles = (int64_t)((D + kGBM - 1) / kGBM) * ((d_model + kGBN - 1) / kGBN);
-    int64_t s = (1024 + tiles - 1) / tiles;
+    const int bm = elt == 2 ? 2 * GLds<kBf16SplitA>::WM : gemm_rows_per_tile<kF32>();
+    const int bn = elt == 2 ? 64 * GLds<kBf16SplitA>::NWN : kGBN;
+    const int64_t tiles = (int64_t)((D + bm - 1) / bm) * ((d_model + bn - 1) / bn);
+    int64_t s = (kDwWorkgroups + tiles - 1) / tiles;
     const int64_t max_s = (T + 8 * kGBK - 1) / (8 * kGBK);     // >= 8 K steps a slice
     if (s > max_s)
         s = max_s;
@@ -612,8 +1024,8 @@ static hipError_t query_forward_t(const DT *x, const DT *W, const float *gamma, 
     const QueryScratch S = query_scratch(T, d_model, D, 0, (int)sizeof(DT));
     float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + S.off_part);
     constexpr int MODE = sizeof(DT) == 2 ? kBf16 : kF32;
-    hipError_t err = gemm<DT, DT, false, false, MODE>(x, W, z, (int)T, D, d_model, d_model,
-                                                      d_model, stream);
+    hipError_t err = gemm<DT, DT, MODE>(x, nullptr, W, z, (int)T, D, d_model, d_model, d_model,
+                                        stream);
     if (err != hipSuccess)
         return err;
     hipLaunchKernelGGL(bn_partial_kernel, dim3((unsigned)((D + kBnCols - 1) / kBnCols), (unsigned)S.chunks),
@@ -647,28 +1059,49 @@ static hipError_t query_backward_t(const DT *x, const DT *W, const float *gamma,
                        S.rows_per_chunk, part);
     hipLaunchKernelGGL(bn_bwd_finalize_kernel, dim3((unsigned)((D + 3) / 4)), dim3(4 * kWave), 0,
                        stream, part, S.chunks, D, T, coef, dgamma, dbeta);
-    hipLaunchKernelGGL(bn_bwd_apply_kernel, bn_rows_grid(T, D), dim3(256), 0, stream, z, dq, T, D,
-                       mean, rstd, gamma, coef, dz);
+    constexpr bool SPLIT = sizeof(DT) == 2;
+    uint16_t *dzh = reinterpret_cast<uint16_t *>(dz), *dzl = dzh + T * D;
+    uint16_t *dzth = reinterpret_cast<uint16_t *>(dzt), *dztl = dzth + Tp * D;
+    if constexpr (SPLIT)
+        hipLaunchKernelGGL(bn_bwd_apply_split_kernel,
+                           dim3((unsigned)((D + 63) / 64), (unsigned)((Tp + 63) / 64)), dim3(256), 0,
+                           stream, z, dq, T, D, mean, rstd, gamma, coef, dzh, dzl, dzth, dztl, Tp);
+    else
+        hipLaunchKernelGGL(bn_bwd_apply_kernel, bn_rows_grid(T, D), dim3(256), 0, stream, z, dq, T,
+                           D, mean, rstd, gamma, coef, dz);
     hipError_t err = hipGetLastError();
-    // every GEMM operand K-contiguous: W^T [d_model][D], x^T [d_model][T], dz^T [D][T]
+    // every GEMM operand K-contiguous: W^T [d_model][D], x^T [d_model][Tp], dz^T [D][Tp]
     if (err == hipSuccess)
         err = transpose<E>(reinterpret_cast<const E *>(W), reinterpret_cast<E *>(Wt), D, d_model, stream);
     if (err == hipSuccess)
         err = transpose<E>(reinterpret_cast<const E *>(x), reinterpret_cast<E *>(xt), T, d_model, stream,
                            Tp);
-    if (err == hipSuccess)
-        err = transpose<float>(dz, dzt, T, D, stream, Tp);
-    if (err != hipSuccess)
-        return err;
-    constexpr int MODE = sizeof(DT) == 2 ? kBf16SplitA : kF32;
-    // dx [T][d_model] = dz [T][D] . (W^T)^T
-    err = gemm<float, DT, false, false, MODE>(dz, Wt, dx, (int)T, d_model, D, D, D, stream);
-    if (err != hipSuccess)
-        return err;
-    // dW [D][d_model] = dz^T [D][Tp] . (x^T)^T, K = Tp (zero-padded tokens) cut
-    // into slices
-    return gemm<float, DT, false, false, MODE>(dzt, xt, dW, D, d_model, (int)Tp, Tp, Tp, stream,
-                                               S.dw_splits, dwp);
+    if constexpr (SPLIT) {
+        if (err != hipSuccess)
+            return err;
+        const bf16_t *h = reinterpret_cast<const bf16_t *>(dzh), *l = reinterpret_cast<const bf16_t *>(dzl);
+        const bf16_t *th = reinterpret_cast<const bf16_t *>(dzth), *tl = reinterpret_cast<const bf16_t *>(dztl);
+        // dx [T][d_model] = dz [T][D] . (W^T)^T
+        err = gemm<bf16_t, bf16_t, kBf16SplitA>(h, l, reinterpret_cast<const bf16_t *>(Wt), dx, (int)T,
+                                                d_model, D, D, D, stream);
+        if (err != hipSuccess)
+            return err;
+        // dW [D][d_model] = dz^T [D][Tp] . (x^T)^T, K = Tp (zero-padded tokens)
+        // cut into slices
+        return gemm<bf16_t, bf16_t, kBf16SplitA>(th, tl, reinterpret_cast<const bf16_t *>(xt), dW, D,
+                                                 d_model, (int)Tp, Tp, Tp, stream, S.dw_splits, dwp);
+    } else {
+        if (err == hipSuccess)
+            err = transpose<float>(dz, dzt, T, D, stream, Tp);
+        if (err != hipSuccess)
+            return err;
+        const float *wt = reinterpret_cast<const float *>(Wt), *xtf = reinterpret_cast<const float *>(xt);
+        err = gemm<float, float, kF32>(dz, nullptr, wt, dx, (int)T, d_model, D, D, D, stream);
+        if (err != hipSuccess)
+            return err;
+        return gemm<float, float, kF32>(dzt, nullptr, xtf, dW, D, d_model, (int)Tp, Tp, Tp, stream,
+                                        S.dw_splits, dwp);
+    }
 }
 
 hipError_t launch_query_forward(int dtype, const void *x, const void *W, const float *gamma,

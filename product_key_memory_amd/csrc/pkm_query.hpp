@@ -10,9 +10,10 @@
 namespace pkm {
 
 // Workspace: per-(row chunk, column) batch-norm partials, then (backward)
-// two per-column coefficients, dz [T][D] and dz^T [D][T] float32, W^T
-// [d_model][D] and x^T [d_model][T] (storage type), and the split-K partial
-// sums of dW [dw_splits][D][d_model].
+// two per-column coefficients, dz [T][D] and dz^T [D][Tp] (float32, or for
+// bf16 storage two bf16 planes hi and lo of the same total size), W^T
+// [d_model][D] and x^T [d_model][Tp] (storage type; Tp = T rounded up to 32,
+// zero-padded), and the split-K partial sums of dW [dw_splits][D][d_model].
 struct QueryScratch {
     int chunks;
     int64_t rows_per_chunk;
@@ -20,7 +21,7 @@ struct QueryScratch {
     size_t off_part, off_coef, off_dz, off_dzt, off_wt, off_xt, off_dwp, total;
 };
 QueryScratch query_scratch(int64_t T, int d_model, int D, int backward, int elt);
-int dw_splits(int64_t T, int d_model, int D);
+int dw_splits(int64_t T, int d_model, int D, int elt);
 
 // z = x W^T [T][D] (float32), mean/rstd per column, q = gamma (z - mean) rstd + beta.
 hipError_t launch_query_forward(int dtype, const void *x, const void *W, const float *gamma,

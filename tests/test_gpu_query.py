@@ -80,6 +80,22 @@ def test_query_small_ragged(dtype, affine, T):
     assert np.allclose(db, gref["dbeta"], rtol=1e-4, atol=1e-3)
 
 
+@pytest.mark.parametrize("T,dm,D", [(300, 96, 64), (33, 32, 160)])
+def test_query_direct_lds_path(T, dm, D):
+    """bf16 with every K a multiple of 32 (d_model, d_out and the padded token
+    count): all three products take the direct-to-LDS kernel, here with ragged
+    row and column tiles (rows past M or N are fed from the last row and not
+    stored) and, for T = 33, a single K step in the dW slices."""
+    (q, z, mean, rstd, dx, dW, dg, db), ref, gref = _run(T, dm, D, "bf16", 94, True)
+    assert _rows_rel(z, ref["z"])[0] <= 1e-5
+    assert _bf16_q_ok(q, ref["q"])
+    for got, want in ((dx, gref["dx"]), (dW, gref["dW"])):
+        gate, tight = _rows_rel(got, want)
+        assert gate <= 1e-4 and tight <= 2e-5, (gate, tight)
+    assert np.allclose(dg, gref["dgamma"], rtol=1e-4, atol=1e-3)
+    assert np.allclose(db, gref["dbeta"], rtol=1e-4, atol=1e-3)
+
+
 @pytest.mark.slow
 def test_query_model_width():
     """The workload's widths: d_model = 1600 (the pages' model), d_out = H d_k = 2048."""

@@ -7,20 +7,26 @@
 // statistics, biased variance, optional affine gamma, beta), and its backward.
 //
 // Kernels:
-//   gemm_kernel        C[M][N] (fp32) = sum_k A(m, k) B(n, k) on MFMA, 128 x 128
-//                      tiles, 32-wide K steps staged in double-buffered LDS
-//                      tiles with XOR-swizzled 16-byte chunks; A and B may be
-//                      stored K-contiguous or M/N-contiguous (transposed while
-//                      staging).  bf16 operands use v_mfma_f32_16x16x32_bf16
-//                      (a float32 A is split into bf16 hi + lo, two MFMAs);
-//                      float32 storage uses v_mfma_f32_16x16x4_f32.
+//   gemm_lds_kernel    C[M][N] (fp32) = sum_k A[m][k] B[n][k] for bf16 operands
+//                      (A optionally as two bf16 planes hi + lo, two MFMAs a
+//                      product) on v_mfma_f32_16x16x32_bf16: 256 x 256 tiles of
+//                      8 waves, operands copied from global memory straight
+//                      into LDS (global_load_lds) through a ring of 64-wide K
+//                      stages, one stage in flight while the other is used
+//   gemm_kernel        the same product with register-staged 128-row tiles,
+//                      for float32 operands (v_mfma_f32_16x16x4_f32) and for
+//                      bf16 shapes the direct kernel does not take (K not a
+//                      multiple of 64, unaligned rows)
+//   sum_slices_kernel  the split-K partial products summed
 //   bn_partial_kernel  per (row chunk, column): count, mean, M2 (Welford over
 //                      the chunk's rows, merged across waves by Chan's rule)
 //   bn_finalize_kernel per column: merge the chunks -> mean, rstd
 //   bn_apply_kernel    q = gamma (z - mean) rstd + beta, rounded once
 //   bn_bwd_*           the batch-norm backward (column sums of dq and
-//                      dq * zhat, then dz), followed by two GEMMs:
-//                      dx = dz W and dW = dz^T x.
+//                      dq * zhat, then dz; for bf16 dz leaves as hi + lo
+//                      planes, row-major and transposed), followed by two
+//                      products: dx = dz W and dW = dz^T x
+//   transpose*_kernel  W^T and x^T (K-contiguous operands for the products)
 #include "pkm_device.hpp"
 #include "pkm_query.hpp"
 
@@ -270,13 +276,16 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(const TA *__restrict__ 
 // that waits for its own reads, so the compiler adds no wait on the loads of
 // later stages before it.  Its outputs are early-clobber: the first read's
 // destination must not share registers with the addresses of the later ones.
-template <int FI, int PA> struct GFrag {
+template <int FI, int PA, int RB> struct GFrag {
     uint4 a[PA][FI], b[4];
     __device__ void read(uint32_t a_addr, uint32_t b_addr);
 };
 
+// The reads of one 32-wide K step: A fragment i of plane p at a_addr +
+// p TILE_A + 16 i RB, B fragment j at b_addr + 16 j RB (RB = bytes per tile
+// row: 64 for 32-wide stages, 128 for 64-wide ones).
 template <>
-__device__ __forceinline__ void GFrag<4, 1>::read(uint32_t a_addr, uint32_t b_addr)
+__device__ __forceinline__ void GFrag<4, 1, 64>::read(uint32_t a_addr, uint32_t b_addr)
 {
     asm volatile(
         "ds_read_b128 %0, %8 offset:0\n\t"
@@ -295,7 +304,7 @@ __device__ __forceinline__ void GFrag<4, 1>::read(uint32_t a_addr, uint32_t b_ad
 }
 
 template <>
-__device__ __forceinline__ void GFrag<4, 2>::read(uint32_t a_addr, uint32_t b_addr)
+__device__ __forceinline__ void GFrag<4, 2, 64>::read(uint32_t a_addr, uint32_t b_addr)
 {
     asm volatile(
         "ds_read_b128 %0, %12 offset:0\n\t"
@@ -319,7 +328,7 @@ __device__ __forceinline__ void GFrag<4, 2>::read(uint32_t a_addr, uint32_t b_ad
 }
 
 template <>
-__device__ __forceinline__ void GFrag<8, 1>::read(uint32_t a_addr, uint32_t b_addr)
+__device__ __forceinline__ void GFrag<8, 1, 64>::read(uint32_t a_addr, uint32_t b_addr)
 {
     asm volatile(
         "ds_read_b128 %0, %12 offset:0\n\t"
@@ -343,7 +352,7 @@ __device__ __forceinline__ void GFrag<8, 1>::read(uint32_t a_addr, uint32_t b_ad
 }
 
 template <>
-__device__ __forceinline__ void GFrag<8, 2>::read(uint32_t a_addr, uint32_t b_addr)
+__device__ __forceinline__ void GFrag<8, 2, 64>::read(uint32_t a_addr, uint32_t b_addr)
 {
     asm volatile(
         "ds_read_b128 %0, %20 offset:0\n\t"
@@ -376,6 +385,107 @@ __device__ __forceinline__ void GFrag<8, 2>::read(uint32_t a_addr, uint32_t b_ad
         : "memory");
 }
 
+template <>
+__device__ __forceinline__ void GFrag<4, 1, 128>::read(uint32_t a_addr, uint32_t b_addr)
+{
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:0\n\t"
+        "ds_read_b128 %1, %8 offset:2048\n\t"
+        "ds_read_b128 %2, %8 offset:4096\n\t"
+        "ds_read_b128 %3, %8 offset:6144\n\t"
+        "ds_read_b128 %4, %9 offset:0\n\t"
+        "ds_read_b128 %5, %9 offset:2048\n\t"
+        "ds_read_b128 %6, %9 offset:4096\n\t"
+        "ds_read_b128 %7, %9 offset:6144\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[0][3]),
+          "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
+        : "v"(a_addr), "v"(b_addr)
+        : "memory");
+}
+
+template <>
+__device__ __forceinline__ void GFrag<4, 2, 128>::read(uint32_t a_addr, uint32_t b_addr)
+{
+    asm volatile(
+        "ds_read_b128 %0, %12 offset:0\n\t"
+        "ds_read_b128 %1, %12 offset:2048\n\t"
+        "ds_read_b128 %2, %12 offset:4096\n\t"
+        "ds_read_b128 %3, %12 offset:6144\n\t"
+        "ds_read_b128 %4, %12 offset:16384\n\t"
+        "ds_read_b128 %5, %12 offset:18432\n\t"
+        "ds_read_b128 %6, %12 offset:20480\n\t"
+        "ds_read_b128 %7, %12 offset:22528\n\t"
+        "ds_read_b128 %8, %13 offset:0\n\t"
+        "ds_read_b128 %9, %13 offset:2048\n\t"
+        "ds_read_b128 %10, %13 offset:4096\n\t"
+        "ds_read_b128 %11, %13 offset:6144\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[0][3]),
+          "=&v"(a[1][0]), "=&v"(a[1][1]), "=&v"(a[1][2]), "=&v"(a[1][3]),
+          "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
+        : "v"(a_addr), "v"(b_addr)
+        : "memory");
+}
+
+template <>
+__device__ __forceinline__ void GFrag<8, 1, 128>::read(uint32_t a_addr, uint32_t b_addr)
+{
+    asm volatile(
+        "ds_read_b128 %0, %12 offset:0\n\t"
+        "ds_read_b128 %1, %12 offset:2048\n\t"
+        "ds_read_b128 %2, %12 offset:4096\n\t"
+        "ds_read_b128 %3, %12 offset:6144\n\t"
+        "ds_read_b128 %4, %12 offset:8192\n\t"
+        "ds_read_b128 %5, %12 offset:10240\n\t"
+        "ds_read_b128 %6, %12 offset:12288\n\t"
+        "ds_read_b128 %7, %12 offset:14336\n\t"
+        "ds_read_b128 %8, %13 offset:0\n\t"
+        "ds_read_b128 %9, %13 offset:2048\n\t"
+        "ds_read_b128 %10, %13 offset:4096\n\t"
+        "ds_read_b128 %11, %13 offset:6144\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[0][3]),
+          "=&v"(a[0][4]), "=&v"(a[0][5]), "=&v"(a[0][6]), "=&v"(a[0][7]),
+          "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
+        : "v"(a_addr), "v"(b_addr)
+        : "memory");
+}
+
+template <>
+__device__ __forceinline__ void GFrag<8, 2, 128>::read(uint32_t a_addr, uint32_t b_addr)
+{
+    asm volatile(
+        "ds_read_b128 %0, %20 offset:0\n\t"
+        "ds_read_b128 %1, %20 offset:2048\n\t"
+        "ds_read_b128 %2, %20 offset:4096\n\t"
+        "ds_read_b128 %3, %20 offset:6144\n\t"
+        "ds_read_b128 %4, %20 offset:8192\n\t"
+        "ds_read_b128 %5, %20 offset:10240\n\t"
+        "ds_read_b128 %6, %20 offset:12288\n\t"
+        "ds_read_b128 %7, %20 offset:14336\n\t"
+        "ds_read_b128 %8, %20 offset:32768\n\t"
+        "ds_read_b128 %9, %20 offset:34816\n\t"
+        "ds_read_b128 %10, %20 offset:36864\n\t"
+        "ds_read_b128 %11, %20 offset:38912\n\t"
+        "ds_read_b128 %12, %20 offset:40960\n\t"
+        "ds_read_b128 %13, %20 offset:43008\n\t"
+        "ds_read_b128 %14, %20 offset:45056\n\t"
+        "ds_read_b128 %15, %20 offset:47104\n\t"
+        "ds_read_b128 %16, %21 offset:0\n\t"
+        "ds_read_b128 %17, %21 offset:2048\n\t"
+        "ds_read_b128 %18, %21 offset:4096\n\t"
+        "ds_read_b128 %19, %21 offset:6144\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[0][3]),
+          "=&v"(a[0][4]), "=&v"(a[0][5]), "=&v"(a[0][6]), "=&v"(a[0][7]),
+          "=&v"(a[1][0]), "=&v"(a[1][1]), "=&v"(a[1][2]), "=&v"(a[1][3]),
+          "=&v"(a[1][4]), "=&v"(a[1][5]), "=&v"(a[1][6]), "=&v"(a[1][7]),
+          "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
+        : "v"(a_addr), "v"(b_addr)
+        : "memory");
+}
+
 // 16 bytes per lane from global memory into LDS: lane l's bytes land at
 // dst + 16 l (dst is the same for the whole wave)
 __device__ __forceinline__ void lds_dma16(const void *src, void *dst)
@@ -393,25 +503,37 @@ __device__ __forceinline__ void wait_vmcnt()
 }
 
 // A workgroup is 2 x NWN waves, each owning WM x 64 of C: 2 WM rows by 64 NWN
-// columns.
-template <int MODE, int WM, int NWN, int NS>
+// columns.  A ring stage holds BK (32 or 64) columns of K: tile rows of RB =
+// 2 BK bytes, 1 KB blocks of 1024 / RB rows; with BK = 64 a row is a whole
+// 128-byte cache line.  Chunk kc of row r sits at position kc ^ swz(r mod 16):
+// swz4 for 4 chunks a row, swz8(r) = (r ^ (r >> 3)) mod 8 for 8, which keeps
+// the fragment reads free of bank conflicts for 8 or 16 lanes a cycle alike.
+__device__ __forceinline__ int swz8(int r)
+{
+    return (r ^ (r >> 3)) & 7;
+}
+
+template <int MODE, int WM, int NWN, int NS, int BK>
 __global__ __launch_bounds__(2 * NWN * kWave) void gemm_lds_kernel(const bf16_t *__restrict__ A,
-                                                             const bf16_t *__restrict__ A2,
-                                                             const bf16_t *__restrict__ B,
-                                                             float *__restrict__ Cm, int M, int N,
-                                                             int K, int64_t lda, int64_t ldb,
-                                                             int k_slice)
+                                                                  const bf16_t *__restrict__ A2,
+                                                                  const bf16_t *__restrict__ B,
+                                                                  float *__restrict__ Cm, int M,
+                                                                  int N, int K, int64_t lda,
+                                                                  int64_t ldb, int k_slice)
 {
     constexpr int PA = GTile<MODE>::parts;
     constexpr int WAVES = 2 * NWN;
     constexpr int BM = 2 * WM, BN = 64 * NWN, FI = WM / 16;
-    constexpr int ROW_BYTES = kGBK * 2;                         // 64
-    constexpr int TILE_A = BM * ROW_BYTES, TILE_B = BN * ROW_BYTES;
+    constexpr int RB = 2 * BK;                                  // bytes per tile row
+    constexpr int CPR = RB / 16;                                // 16-byte chunks per row
+    constexpr int RPB = 1024 / RB;                              // rows per 1 KB block
+    constexpr int TILE_A = BM * RB, TILE_B = BN * RB;
     constexpr int STAGE = PA * TILE_A + TILE_B;
-    constexpr int LA = BM / 16 / WAVES, LB = BN / 16 / WAVES;   // 1 KB blocks per wave
-    static_assert(LA * 16 * WAVES == BM && LB * 16 * WAVES == BN, "whole blocks per wave");
+    constexpr int LA = BM / RPB / WAVES, LB = BN / RPB / WAVES; // blocks per wave
+    static_assert(LA * RPB * WAVES == BM && LB * RPB * WAVES == BN, "whole blocks per wave");
     constexpr int LPS = PA * LA + LB;                           // loads per wave per stage
     static_assert(NS >= 2 && NS <= 4 && (NS - 2) * LPS < 64, "ring depth");
+    static_assert(BK == 32 || BK == 64, "stage width");
     __shared__ __align__(1024) unsigned char lds[NS * STAGE];
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     int tx, ty, tz;
@@ -419,34 +541,38 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_lds_kernel(const bf16_t 
     const int m0 = ty * BM, n0 = tx * BN;
     const int wm = (wave & 1) * WM, wn = (wave >> 1) * 64;
     const int r16 = lane & 15, kg = lane >> 4;
+    auto swz = [](int r) { return CPR == 4 ? swz4(r & 15) : swz8(r & 15); };
 
     // this lane's source rows (clamped into the matrix: rows past M or N are
-    // computed from repeated data and never stored) and chunk
-    const int lrow = lane >> 2, lchunk = (lane & 3) ^ swz4(lrow);
+    // computed from repeated data and never stored) and the chunk the swizzle
+    // puts at its position (lane l writes row l / CPR, position l % CPR of
+    // its block)
+    const int lrow = lane / CPR, lpos = lane % CPR;
     const bf16_t *pa[PA][LA];
     const bf16_t *pb[LB];
 #pragma unroll
     for (int l = 0; l < LA; ++l) {
-        int gr = m0 + (wave * LA + l) * 16 + lrow;
-        gr = gr < M ? gr : M - 1;
-        pa[0][l] = A + (int64_t)gr * lda + 8 * lchunk;
+        const int row = (wave * LA + l) * RPB + lrow;
+        const int gr = m0 + row < M ? m0 + row : M - 1;
+        const int kc = lpos ^ swz(row);
+        pa[0][l] = A + (int64_t)gr * lda + 8 * kc;
         if constexpr (PA == 2)
-            pa[1][l] = A2 + (int64_t)gr * lda + 8 * lchunk;
+            pa[1][l] = A2 + (int64_t)gr * lda + 8 * kc;
     }
 #pragma unroll
     for (int l = 0; l < LB; ++l) {
-        int gr = n0 + (wave * LB + l) * 16 + lrow;
-        gr = gr < N ? gr : N - 1;
-        pb[l] = B + (int64_t)gr * ldb + 8 * lchunk;
+        const int row = (wave * LB + l) * RPB + lrow;
+        const int gr = n0 + row < N ? n0 + row : N - 1;
+        pb[l] = B + (int64_t)gr * ldb + 8 * (lpos ^ swz(row));
     }
     const int kb = tz * k_slice;
     const int ke = kb + k_slice < K ? kb + k_slice : K;
     Cm += (int64_t)tz * M * N;
-    const int nk = (ke - kb) / kGBK;
+    const int nk = (ke - kb) / BK;
 
     auto issue = [&](int c) {
         unsigned char *st = lds + (c % NS) * STAGE;
-        const int k0 = kb + c * kGBK;
+        const int k0 = kb + c * BK;
 #pragma unroll
         for (int p = 0; p < PA; ++p)
 #pragma unroll
@@ -464,12 +590,16 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_lds_kernel(const bf16_t 
         for (int j = 0; j < 4; ++j)
             acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // byte addresses of this lane's fragments in stage 0 (the swizzle of rows
-    // wm + 16 i + r16 does not depend on i)
+    // byte addresses of this lane's fragments in stage 0, per 32-wide K half
+    // (the swizzle of rows wm + 16 i + r16 does not depend on i)
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-    const uint32_t swz = (uint32_t)((kg ^ swz4(r16)) * 16);
-    const uint32_t a_off = lds0 + (uint32_t)((wm + r16) * ROW_BYTES) + swz;
-    const uint32_t b_off = lds0 + (uint32_t)(PA * TILE_A + (wn + r16) * ROW_BYTES) + swz;
+    uint32_t a_off[BK / 32], b_off[BK / 32];
+#pragma unroll
+    for (int h = 0; h < BK / 32; ++h) {
+        const uint32_t sw = (uint32_t)(((kg + 4 * h) ^ swz(r16)) * 16);
+        a_off[h] = lds0 + (uint32_t)((wm + r16) * RB) + sw;
+        b_off[h] = lds0 + (uint32_t)(PA * TILE_A + (wn + r16) * RB) + sw;
+    }
 
 #pragma unroll
     for (int c = 0; c < NS - 1; ++c)
@@ -489,18 +619,21 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_lds_kernel(const bf16_t 
         // every wave is done with stage c - 1: refill its buffer
         if (c + NS - 1 < nk)
             issue(c + NS - 1);
-        GFrag<FI, PA> f;
         const uint32_t st = (uint32_t)((c % NS) * STAGE);
-        f.read(a_off + st, b_off + st);
 #pragma unroll
-        for (int i = 0; i < FI; ++i)
+        for (int h = 0; h < BK / 32; ++h) {
+            GFrag<FI, PA, RB> f;
+            f.read(a_off[h] + st, b_off[h] + st);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int i = 0; i < FI; ++i)
 #pragma unroll
-                for (int p = 0; p < PA; ++p)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, f.a[p][i]), __builtin_bit_cast(bf16x8, f.b[j]),
-                        acc[i][j], 0, 0, 0);
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int p = 0; p < PA; ++p)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, f.a[p][i]), __builtin_bit_cast(bf16x8, f.b[j]),
+                            acc[i][j], 0, 0, 0);
+        }
     }
     gemm_store<FI>(acc, Cm, M, N, m0 + wm, n0 + wn, lane);
 }
@@ -528,8 +661,8 @@ static int gemm_rows_per_tile()
 
 // tile shape (2 WM x 64 NWN) and ring depth of the direct-to-LDS kernel per mode
 template <int MODE> struct GLds;
-template <> struct GLds<kBf16> { static constexpr int WM = 128, NWN = 2, NS = 3; };
-template <> struct GLds<kBf16SplitA> { static constexpr int WM = 128, NWN = 2, NS = 2; };
+template <> struct GLds<kBf16> { static constexpr int WM = 128, NWN = 4, NS = 2, BK = 64; };
+template <> struct GLds<kBf16SplitA> { static constexpr int WM = 64, NWN = 4, NS = 2, BK = 64; };
 
 static bool aligned16(const void *p)
 {
@@ -541,24 +674,28 @@ static hipError_t gemm(const TA *A, const TA *A2, const TB *B, float *Cm, int M,
                        int64_t lda, int64_t ldb, hipStream_t stream, int splits = 1,
                        float *parts = nullptr)
 {
+    bool direct = false;
+    int gran = kGBK;                    // K slices are whole stages
+    if constexpr (MODE != kF32) {
+        direct = K % GLds<MODE>::BK == 0 && lda % 8 == 0 && ldb % 8 == 0 && aligned16(A) &&
+                 aligned16(B) && (A2 == nullptr || aligned16(A2));
+        if (direct)
+            gran = GLds<MODE>::BK;
+    }
     int k_slice = K;
     if (splits > 1) {
         k_slice = (K + splits - 1) / splits;
-        k_slice = (k_slice + kGBK - 1) / kGBK * kGBK;
+        k_slice = (k_slice + gran - 1) / gran * gran;
         splits = (K + k_slice - 1) / k_slice;
     }
     float *out = splits > 1 ? parts : Cm;
-    bool direct = false;
-    if constexpr (MODE != kF32)
-        direct = K % kGBK == 0 && lda % 8 == 0 && ldb % 8 == 0 && aligned16(A) && aligned16(B) &&
-                 (A2 == nullptr || aligned16(A2));
     if constexpr (MODE != kF32) {
         if (direct) {
             typedef GLds<MODE> G;
             const int BM = 2 * G::WM, BN = 64 * G::NWN;
             const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM),
                             (unsigned)splits);
-            hipLaunchKernelGGL((gemm_lds_kernel<MODE, G::WM, G::NWN, G::NS>), grid,
+            hipLaunchKernelGGL((gemm_lds_kernel<MODE, G::WM, G::NWN, G::NS, G::BK>), grid,
                                dim3(2 * G::NWN * kWave), 0, stream, A, A2, B, out, M, N, K, lda, ldb,
                                k_slice);
         }
@@ -603,14 +740,14 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E *__restrict__ in
 }
 
 // K of the GEMM that runs over the tokens (dW = dz^T x): the token count
-// rounded up to 32, a whole number of 32-wide K steps of 16-byte aligned
-// pieces (8 bf16 or 4 float32 elements), plus 32 more when that is a multiple
-// of 512 (rows a power-of-two number of kilobytes apart put the 16 rows one
-// load touches into the same memory channels); the padding holds zeros.
+// rounded up to 64, a whole number of 64-wide K steps of 16-byte aligned
+// pieces (8 bf16 or 4 float32 elements), plus 64 more when that is a multiple
+// of 512 (rows a power-of-two number of kilobytes apart put the rows one load
+// touches into the same memory channels); the padding holds zeros.
 static int64_t token_pitch(int64_t T)
 {
-    const int64_t p = (T + 31) & ~(int64_t)31;
-    return p % 512 == 0 ? p + 32 : p;
+    const int64_t p = (T + 63) & ~(int64_t)63;
+    return p % 512 == 0 ? p + 64 : p;
 }
 
 // 16-bit elements: 64 x 64 tiles moved in 16-byte pieces on both sides.  The

@@ -80,12 +80,12 @@ def test_query_small_ragged(dtype, affine, T):
     assert np.allclose(db, gref["dbeta"], rtol=1e-4, atol=1e-3)
 
 
-@pytest.mark.parametrize("T,dm,D", [(300, 96, 64), (33, 32, 160)])
+@pytest.mark.parametrize("T,dm,D", [(300, 128, 64), (33, 64, 192)])
 def test_query_direct_lds_path(T, dm, D):
-    """bf16 with every K a multiple of 32 (d_model, d_out and the padded token
+    """bf16 with every K a multiple of 64 (d_model, d_out and the padded token
     count): all three products take the direct-to-LDS kernel, here with ragged
     row and column tiles (rows past M or N are fed from the last row and not
-    stored) and, for T = 33, a single K step in the dW slices."""
+    stored) and, for T = 33, a single 64-wide K stage in the dW product."""
     (q, z, mean, rstd, dx, dW, dg, db), ref, gref = _run(T, dm, D, "bf16", 94, True)
     assert _rows_rel(z, ref["z"])[0] <= 1e-5
     assert _bf16_q_ok(q, ref["q"])

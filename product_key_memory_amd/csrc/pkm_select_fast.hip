@@ -52,6 +52,10 @@ constexpr int kSurvStride = kFastSurv + 4;           // + one spare slot per lan
 constexpr int kMergeWaves = 4;
 constexpr int kMergeRows = 16;                       // (token, head) rows per wave
 constexpr int kMaxPairs = 128;                       // merge_candidates(32) = 119
+// LDS row pitch of the merge, in 8-byte entries: a row's two lists (2 k <= 64)
+// or its survivors (<= 64), plus one: an odd pitch puts the 16 rows a read
+// instruction touches (same entry, rows tok = 0..15) in distinct banks
+constexpr int kMergePitch = 2 * 32 + 1;
 
 // Scores of the wave's 16 tokens against the sub-keys 0..n_loc-1 of one block
 // (kb = its first row), as order-preserving integers: so[j][i] = ord(score of
@@ -416,7 +420,7 @@ __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
     const uint2 *__restrict__ lists, int64_t rows, int n, int k, int n_pairs, int m,
     int32_t *__restrict__ idx, float *__restrict__ weights, float *__restrict__ scores)
 {
-    __shared__ uint2 s_list[kMergeWaves][kMergeRows * 2 * 32];
+    __shared__ uint2 s_list[kMergeWaves][kMergeRows * kMergePitch];
     __shared__ uint16_t s_pairs[kMaxPairs];
     __shared__ uint16_t s_corner[kMaxCorners];
     const int lane = lane_id();
@@ -431,8 +435,9 @@ __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
         if (lane < m)
             s_corner[lane] = (uint16_t)(lane | ((m / (lane + 1) - 1) << 8));
     }
-    // the wave's rows are contiguous in the lists: stage them in LDS, all
-    // 16-byte loads in flight before the first store
+    // the wave's rows are contiguous in the lists: stage them in LDS (row
+    // pitch kMergePitch entries), all 16-byte loads in flight before the
+    // first store
     const int64_t row0 = ((int64_t)blockIdx.x * kMergeWaves + wave) * kMergeRows;
     const int64_t nrows = rows - row0 < kMergeRows ? rows - row0 : kMergeRows;
     uint2 *sl = s_list[wave];
@@ -449,15 +454,19 @@ __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
 #pragma unroll
         for (int u = 0; u < kPerLane; ++u) {
             const int e = lane + u * kWave;
-            if (e < units)
-                reinterpret_cast<uint4 *>(sl)[e] = buf[u];
+            if (e < units) {
+                // entries 2 e, 2 e + 1 lie in one row (a row has 2 k entries)
+                uint2 *d = sl + (e / k) * kMergePitch + 2 * (e % k);
+                d[0] = make_uint2(buf[u].x, buf[u].y);
+                d[1] = make_uint2(buf[u].z, buf[u].w);
+            }
         }
     }
     __syncthreads();
     if (nrows <= 0)
         return;
     const bool live = tok < nrows;
-    const uint2 *l = sl + tok * 2 * k;
+    const uint2 *l = sl + tok * kMergePitch;
     const uint2 *r = l + k;
 
     // the bound: least corner score of the row (lane group g takes corners
@@ -553,7 +562,7 @@ __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
     // position g + (the counts of the groups before it), every candidate at
     // the next free slot, which only a kept one claims.
     wave_lds_sync();
-    uint64_t *surv = reinterpret_cast<uint64_t *>(sl) + tok * 64;
+    uint64_t *surv = reinterpret_cast<uint64_t *>(sl) + tok * kMergePitch;
     const int c0 = __shfl(cnt, tok), c1 = __shfl(cnt, tok + 16), c2 = __shfl(cnt, tok + 32);
     int off = g + (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
 #pragma unroll

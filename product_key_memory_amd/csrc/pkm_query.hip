@@ -76,16 +76,16 @@ __device__ __forceinline__ int g_cell(int row, int k)
     return row * kGBK + (((k / EPC) ^ s) * EPC) + k % EPC;
 }
 
-// The output tile (tx, ty) and K slice tz of this workgroup.  Workgroup ids
-// are renumbered so that each XCD gets one contiguous range of tiles, walked
-// kGroupM tile rows at a time: tiles that share A and B panels run on the
-// same XCD at about the same time and meet in its L2.  A bijection for any
-// grid, so correctness does not depend on how workgroups are dealt.
-__device__ __forceinline__ void gemm_tile(int &tx, int &ty, int &tz)
+// The output tile (tx, ty) and K slice tz of this workgroup; the grid is 1-D,
+// gx x gy tiles times the K slices.  Workgroup ids are renumbered so that
+// each XCD gets one contiguous range of tiles, walked kGroupM tile rows at a
+// time: tiles that share A and B panels run on the same XCD at about the same
+// time and meet in its L2.  A bijection for any grid, so correctness does not
+// depend on how workgroups are dealt.
+__device__ __forceinline__ void gemm_tile(int gx, int gy, int &tx, int &ty, int &tz)
 {
-    const int gx = gridDim.x, gy = gridDim.y;
-    const int total = gx * gy * (int)gridDim.z;
-    const int g = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    const int total = (int)gridDim.x;
+    const int g = blockIdx.x;
     const int q = total / kXcds, r = total % kXcds;
     const int xcd = g % kXcds, pos = g / kXcds;
     const int id = xcd < r ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(const TA *__restrict__ 
                                                          const TB *__restrict__ B,
                                                          float *__restrict__ Cm, int M, int N,
                                                          int K, int64_t lda, int64_t ldb,
-                                                         int k_slice)
+                                                         int k_slice, int gx, int gy)
 {
     typedef typename GTile<MODE>::E E;
     constexpr int C = GTile<MODE>::C;
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(const TA *__restrict__ 
     __shared__ __align__(16) E lds[2][PA * TILE_A + TILE_B];
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     int tx, ty, tz;
-    gemm_tile(tx, ty, tz);
+    gemm_tile(gx, gy, tx, ty, tz);
     const int m0 = ty * BM, n0 = tx * kGBN;
     const int wm = (wave & 1) * WM, wn = (wave >> 1) * 64;
     const int r16 = lane & 15, kg = lane >> 4;
@@ -519,7 +519,8 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_lds_kernel(const bf16_t 
                                                                   const bf16_t *__restrict__ B,
                                                                   float *__restrict__ Cm, int M,
                                                                   int N, int K, int64_t lda,
-                                                                  int64_t ldb, int k_slice)
+                                                                  int64_t ldb, int k_slice, int gx,
+                                                                  int gy)
 {
     constexpr int PA = GTile<MODE>::parts;
     constexpr int WAVES = 2 * NWN;
@@ -537,7 +538,7 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_lds_kernel(const bf16_t 
     __shared__ __align__(1024) unsigned char lds[NS * STAGE];
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     int tx, ty, tz;
-    gemm_tile(tx, ty, tz);
+    gemm_tile(gx, gy, tx, ty, tz);
     const int m0 = ty * BM, n0 = tx * BN;
     const int wm = (wave & 1) * WM, wn = (wave >> 1) * 64;
     const int r16 = lane & 15, kg = lane >> 4;
@@ -693,19 +694,18 @@ static hipError_t gemm(const TA *A, const TA *A2, const TB *B, float *Cm, int M,
         if (direct) {
             typedef GLds<MODE> G;
             const int BM = 2 * G::WM, BN = 64 * G::NWN;
-            const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM),
-                            (unsigned)splits);
-            hipLaunchKernelGGL((gemm_lds_kernel<MODE, G::WM, G::NWN, G::NS, G::BK>), grid,
-                               dim3(2 * G::NWN * kWave), 0, stream, A, A2, B, out, M, N, K, lda, ldb,
-                               k_slice);
+            const int gx = (N + BN - 1) / BN, gy = (M + BM - 1) / BM;
+            hipLaunchKernelGGL((gemm_lds_kernel<MODE, G::WM, G::NWN, G::NS, G::BK>),
+                               dim3((unsigned)((int64_t)gx * gy * splits)), dim3(2 * G::NWN * kWave),
+                               0, stream, A, A2, B, out, M, N, K, lda, ldb, k_slice, gx, gy);
         }
     }
     if (!direct) {
         const int BM = gemm_rows_per_tile<MODE>();
-        const dim3 grid((unsigned)((N + kGBN - 1) / kGBN), (unsigned)((M + BM - 1) / BM),
-                        (unsigned)splits);
-        hipLaunchKernelGGL((gemm_kernel<TA, TB, MODE>), grid, dim3(kGThreads), 0, stream, A, A2, B,
-                           out, M, N, K, lda, ldb, k_slice);
+        const int gx = (N + kGBN - 1) / kGBN, gy = (M + BM - 1) / BM;
+        hipLaunchKernelGGL((gemm_kernel<TA, TB, MODE>), dim3((unsigned)((int64_t)gx * gy * splits)),
+                           dim3(kGThreads), 0, stream, A, A2, B, out, M, N, K, lda, ldb, k_slice, gx,
+                           gy);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || splits <= 1)
@@ -725,17 +725,20 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E *__restrict__ in
                                                         int64_t R, int64_t C, int64_t ldo)
 {
     __shared__ E tile[64][65];
-    const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+    const int64_t c0 = (int64_t)blockIdx.x * 64;
     const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
-    for (int i = ty; i < 64; i += 4) {
-        const int64_t r = r0 + i, c = c0 + tx;
-        tile[i][tx] = (r < R && c < C) ? in[r * C + c] : (E)0;
-    }
-    __syncthreads();
-    for (int i = ty; i < 64; i += 4) {
-        const int64_t c = c0 + i, r = r0 + tx;
-        if (r < ldo && c < C)
-            out[c * ldo + r] = tile[tx][i];
+    for (int64_t r0 = (int64_t)blockIdx.y * 64; r0 < ldo; r0 += (int64_t)gridDim.y * 64) {
+        for (int i = ty; i < 64; i += 4) {
+            const int64_t r = r0 + i, c = c0 + tx;
+            tile[i][tx] = (r < R && c < C) ? in[r * C + c] : (E)0;
+        }
+        __syncthreads();
+        for (int i = ty; i < 64; i += 4) {
+            const int64_t c = c0 + i, r = r0 + tx;
+            if (r < ldo && c < C)
+                out[c * ldo + r] = tile[tx][i];
+        }
+        __syncthreads();
     }
 }
 
@@ -781,23 +784,34 @@ __global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t *__rest
                                                           int64_t C, int64_t ldo)
 {
     __shared__ uint16_t tile[64][kTrPitch];
-    const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+    const int64_t c0 = (int64_t)blockIdx.x * 64;
     const int tid = threadIdx.x;
+    for (int64_t r0 = (int64_t)blockIdx.y * 64; r0 < ldo; r0 += (int64_t)gridDim.y * 64) {
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-        const int r = pass * 32 + tid / 8, cs = (tid % 8) * 8;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (r0 + r < R && c0 + cs < C)
-            v = *reinterpret_cast<const uint4 *>(in + (r0 + r) * C + c0 + cs);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        for (int pass = 0; pass < 2; ++pass) {
+            const int r = pass * 32 + tid / 8, cs = (tid % 8) * 8;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (r0 + r < R && c0 + cs < C)
+                v = *reinterpret_cast<const uint4 *>(in + (r0 + r) * C + c0 + cs);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            tile[r][cs + 2 * e] = (uint16_t)w[e];
-            tile[r][cs + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+            for (int e = 0; e < 4; ++e) {
+                tile[r][cs + 2 * e] = (uint16_t)w[e];
+                tile[r][cs + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+            }
         }
+        __syncthreads();
+        tile16_store_t(tile, out, r0, c0, C, ldo, tid);
+        __syncthreads();
     }
-    __syncthreads();
-    tile16_store_t(tile, out, r0, c0, C, ldo, tid);
+}
+
+// transposes and the fused batch-norm step walk 64-row tiles from blockIdx.y
+// by gridDim.y, which stays within the launch limit of the y dimension
+static unsigned row_tiles_grid(int64_t rows)
+{
+    const int64_t t = (rows + 63) / 64;
+    return (unsigned)(t < 65535 ? t : 65535);
 }
 
 template <typename E>
@@ -806,7 +820,7 @@ static hipError_t transpose(const E *in, E *out, int64_t R, int64_t C, hipStream
 {
     if (ldo < 0)
         ldo = R;
-    const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((ldo + 63) / 64));
+    const dim3 grid((unsigned)((C + 63) / 64), row_tiles_grid(ldo));
     if constexpr (sizeof(E) == 2)
         hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, stream,
                            reinterpret_cast<const uint16_t *>(in), reinterpret_cast<uint16_t *>(out), R,
@@ -1058,7 +1072,6 @@ __global__ __launch_bounds__(256) void bn_bwd_apply_split_kernel(
     uint16_t *__restrict__ dzt_hi, uint16_t *__restrict__ dzt_lo, int64_t Tp)
 {
     __shared__ uint16_t th[64][kTrPitch], tl[64][kTrPitch];
-    const int64_t r0 = (int64_t)blockIdx.y * 64;
     const int c0 = blockIdx.x * 64, tid = threadIdx.x;
     const int cl = 4 * (tid % 16), c = c0 + cl;           // this thread's 4 features
     const bool cok = c < D;
@@ -1071,34 +1084,37 @@ __global__ __launch_bounds__(256) void bn_bwd_apply_split_kernel(
         k0[e] = cok ? coef[2 * (c + e)] : 0.f;
         k1[e] = cok ? coef[2 * (c + e) + 1] : 0.f;
     }
+    for (int64_t r0 = (int64_t)blockIdx.y * 64; r0 < Tp; r0 += (int64_t)gridDim.y * 64) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = tid / 16 + 16 * j;
-        const int64_t t = r0 + r;
-        uint32_t h[4] = {0u, 0u, 0u, 0u}, l[4] = {0u, 0u, 0u, 0u};
-        if (t < T && cok) {
-            const float4 zv = *reinterpret_cast<const float4 *>(z + t * D + c);
-            const float4 gv = *reinterpret_cast<const float4 *>(dq + t * D + c);
-            const float zz[4] = {zv.x, zv.y, zv.z, zv.w}, gg[4] = {gv.x, gv.y, gv.z, gv.w};
+        for (int j = 0; j < 4; ++j) {
+            const int r = tid / 16 + 16 * j;
+            const int64_t t = r0 + r;
+            uint32_t h[4] = {0u, 0u, 0u, 0u}, l[4] = {0u, 0u, 0u, 0u};
+            if (t < T && cok) {
+                const float4 zv = *reinterpret_cast<const float4 *>(z + t * D + c);
+                const float4 gv = *reinterpret_cast<const float4 *>(dq + t * D + c);
+                const float zz[4] = {zv.x, zv.y, zv.z, zv.w}, gg[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float zh = (zz[e] - mu[e]) * rs[e];
+                    const float o = gr[e] * (gg[e] - k0[e] - zh * k1[e]);
+                    h[e] = f32_to_bf16_bits(o);
+                    l[e] = f32_to_bf16_bits(o - bf16_to_f32(h[e]));
+                }
+                *reinterpret_cast<uint2 *>(dz_hi + t * D + c) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                *reinterpret_cast<uint2 *>(dz_lo + t * D + c) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float zh = (zz[e] - mu[e]) * rs[e];
-                const float o = gr[e] * (gg[e] - k0[e] - zh * k1[e]);
-                h[e] = f32_to_bf16_bits(o);
-                l[e] = f32_to_bf16_bits(o - bf16_to_f32(h[e]));
+                th[r][cl + e] = (uint16_t)h[e];
+                tl[r][cl + e] = (uint16_t)l[e];
             }
-            *reinterpret_cast<uint2 *>(dz_hi + t * D + c) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-            *reinterpret_cast<uint2 *>(dz_lo + t * D + c) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            th[r][cl + e] = (uint16_t)h[e];
-            tl[r][cl + e] = (uint16_t)l[e];
-        }
+        __syncthreads();
+        tile16_store_t(th, dzt_hi, r0, c0, D, Tp, tid);
+        tile16_store_t(tl, dzt_lo, r0, c0, D, Tp, tid);
+        __syncthreads();
     }
-    __syncthreads();
-    tile16_store_t(th, dzt_hi, r0, c0, D, Tp, tid);
-    tile16_store_t(tl, dzt_lo, r0, c0, D, Tp, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -1201,7 +1217,7 @@ static hipError_t query_backward_t(const DT *x, const DT *W, const float *gamma,
     uint16_t *dzth = reinterpret_cast<uint16_t *>(dzt), *dztl = dzth + Tp * D;
     if constexpr (SPLIT)
         hipLaunchKernelGGL(bn_bwd_apply_split_kernel,
-                           dim3((unsigned)((D + 63) / 64), (unsigned)((Tp + 63) / 64)), dim3(256), 0,
+                           dim3((unsigned)((D + 63) / 64), row_tiles_grid(Tp)), dim3(256), 0,
                            stream, z, dq, T, D, mean, rstd, gamma, coef, dzh, dzl, dzth, dztl, Tp);
     else
         hipLaunchKernelGGL(bn_bwd_apply_kernel, bn_rows_grid(T, D), dim3(256), 0, stream, z, dq, T,

@@ -311,6 +311,11 @@ def measure_query_net(torch, _lib, w, dq, stream, d_model: int = 1600) -> dict:
         tf = fl / (ms * 1e-3) / 1e12
         out[name] = {"ms": round(ms, 5), "flops": fl, "TFLOP/s": round(tf, 1),
                      "mfma_frac": round(tf / peak, 4)}
+        if name == "backward" and w.dtype == "bf16":
+            # dz enters both products as two bf16 planes (hi + lo): the MFMAs
+            # execute twice the nominal flops
+            out[name]["mfma_flops"] = 2 * fl
+            out[name]["mfma_work_frac"] = round(2 * tf / peak, 4)
     return out
 
 

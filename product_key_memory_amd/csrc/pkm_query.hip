@@ -265,227 +265,13 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(const TA *__restrict__ 
     gemm_store<FI>(acc, Cm, M, N, m0 + wm, n0 + wn, lane);
 }
 
-// ---- direct-to-LDS kernel (bf16 operands, K a multiple of 32) --------------
+// ---- direct-to-LDS kernel (bf16 operands, K a multiple of the stage) ------
 // The operand tiles go from global memory straight into LDS (one
-// global_load_lds_dwordx4 per 16 rows: lane l writes bytes 16 l .. 16 l + 15 of
-// a 1 KB block, i.e. row l / 4, chunk position l % 4, and fetches the chunk
-// the swizzle puts there), through a ring of NS stages: NS - 1 stages are
-// in flight while one is read.  A stage is complete once this wave's own loads
-// of it have retired (s_waitcnt vmcnt) and every wave has passed the barrier
-// that follows.  The MFMA operands are then read from LDS by one asm block
-// that waits for its own reads, so the compiler adds no wait on the loads of
-// later stages before it.  Its outputs are early-clobber: the first read's
-// destination must not share registers with the addresses of the later ones.
-template <int FI, int PA, int RB> struct GFrag {
-    uint4 a[PA][FI], b[4];
-    __device__ void read(uint32_t a_addr, uint32_t b_addr);
-};
-
-// The reads of one 32-wide K step: A fragment i of plane p at a_addr +
-// p TILE_A + 16 i RB, B fragment j at b_addr + 16 j RB (RB = bytes per tile
-// row: 64 for 32-wide stages, 128 for 64-wide ones).
-template <>
-__device__ __forceinline__ void GFrag<4, 1, 64>::read(uint32_t a_addr, uint32_t b_addr)
-{
-    asm volatile(
-        "ds_read_b128 %0, %8 offset:0\n\t"
-        "ds_read_b128 %1, %8 offset:1024\n\t"
-        "ds_read_b128 %2, %8 offset:2048\n\t"
-        "ds_read_b128 %3, %8 offset:3072\n\t"
-        "ds_read_b128 %4, %9 offset:0\n\t"
-        "ds_read_b128 %5, %9 offset:1024\n\t"
-        "ds_read_b128 %6, %9 offset:2048\n\t"
-        "ds_read_b128 %7, %9 offset:3072\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[0][3]),
-          "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
-        : "v"(a_addr), "v"(b_addr)
-        : "memory");
-}
-
-template <>
-__device__ __forceinline__ void GFrag<4, 2, 64>::read(uint32_t a_addr, uint32_t b_addr)
-{
-    asm volatile(
-        "ds_read_b128 %0, %12 offset:0\n\t"
-        "ds_read_b128 %1, %12 offset:1024\n\t"
-        "ds_read_b128 %2, %12 offset:2048\n\t"
-        "ds_read_b128 %3, %12 offset:3072\n\t"
-        "ds_read_b128 %4, %12 offset:8192\n\t"
-        "ds_read_b128 %5, %12 offset:9216\n\t"
-        "ds_read_b128 %6, %12 offset:10240\n\t"
-        "ds_read_b128 %7, %12 offset:11264\n\t"
-        "ds_read_b128 %8, %13 offset:0\n\t"
-        "ds_read_b128 %9, %13 offset:1024\n\t"
-        "ds_read_b128 %10, %13 offset:2048\n\t"
-        "ds_read_b128 %11, %13 offset:3072\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[0][3]),
-          "=&v"(a[1][0]), "=&v"(a[1][1]), "=&v"(a[1][2]), "=&v"(a[1][3]),
-          "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
-        : "v"(a_addr), "v"(b_addr)
-        : "memory");
-}
-
-template <>
-__device__ __forceinline__ void GFrag<8, 1, 64>::read(uint32_t a_addr, uint32_t b_addr)
-{
-    asm volatile(
-        "ds_read_b128 %0, %12 offset:0\n\t"
-        "ds_read_b128 %1, %12 offset:1024\n\t"
-        "ds_read_b128 %2, %12 offset:2048\n\t"
-        "ds_read_b128 %3, %12 offset:3072\n\t"
-        "ds_read_b128 %4, %12 offset:4096\n\t"
-        "ds_read_b128 %5, %12 offset:5120\n\t"
-        "ds_read_b128 %6, %12 offset:6144\n\t"
-        "ds_read_b128 %7, %12 offset:7168\n\t"
-        "ds_read_b128 %8, %13 offset:0\n\t"
-        "ds_read_b128 %9, %13 offset:1024\n\t"
-        "ds_read_b128 %10, %13 offset:2048\n\t"
-        "ds_read_b128 %11, %13 offset:3072\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[0][3]),
-          "=&v"(a[0][4]), "=&v"(a[0][5]), "=&v"(a[0][6]), "=&v"(a[0][7]),
-          "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
-        : "v"(a_addr), "v"(b_addr)
-        : "memory");
-}
-
-template <>
-__device__ __forceinline__ void GFrag<8, 2, 64>::read(uint32_t a_addr, uint32_t b_addr)
-{
-    asm volatile(
-        "ds_read_b128 %0, %20 offset:0\n\t"
-        "ds_read_b128 %1, %20 offset:1024\n\t"
-        "ds_read_b128 %2, %20 offset:2048\n\t"
-        "ds_read_b128 %3, %20 offset:3072\n\t"
-        "ds_read_b128 %4, %20 offset:4096\n\t"
-        "ds_read_b128 %5, %20 offset:5120\n\t"
-        "ds_read_b128 %6, %20 offset:6144\n\t"
-        "ds_read_b128 %7, %20 offset:7168\n\t"
-        "ds_read_b128 %8, %20 offset:16384\n\t"
-        "ds_read_b128 %9, %20 offset:17408\n\t"
-        "ds_read_b128 %10, %20 offset:18432\n\t"
-        "ds_read_b128 %11, %20 offset:19456\n\t"
-        "ds_read_b128 %12, %20 offset:20480\n\t"
-        "ds_read_b128 %13, %20 offset:21504\n\t"
-        "ds_read_b128 %14, %20 offset:22528\n\t"
-        "ds_read_b128 %15, %20 offset:23552\n\t"
-        "ds_read_b128 %16, %21 offset:0\n\t"
-        "ds_read_b128 %17, %21 offset:1024\n\t"
-        "ds_read_b128 %18, %21 offset:2048\n\t"
-        "ds_read_b128 %19, %21 offset:3072\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[0][3]),
-          "=&v"(a[0][4]), "=&v"(a[0][5]), "=&v"(a[0][6]), "=&v"(a[0][7]),
-          "=&v"(a[1][0]), "=&v"(a[1][1]), "=&v"(a[1][2]), "=&v"(a[1][3]),
-          "=&v"(a[1][4]), "=&v"(a[1][5]), "=&v"(a[1][6]), "=&v"(a[1][7]),
-          "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
-        : "v"(a_addr), "v"(b_addr)
-        : "memory");
-}
-
-template <>
-__device__ __forceinline__ void GFrag<4, 1, 128>::read(uint32_t a_addr, uint32_t b_addr)
-{
-    asm volatile(
-        "ds_read_b128 %0, %8 offset:0\n\t"
-        "ds_read_b128 %1, %8 offset:2048\n\t"
-        "ds_read_b128 %2, %8 offset:4096\n\t"
-        "ds_read_b128 %3, %8 offset:6144\n\t"
-        "ds_read_b128 %4, %9 offset:0\n\t"
-        "ds_read_b128 %5, %9 offset:2048\n\t"
-        "ds_read_b128 %6, %9 offset:4096\n\t"
-        "ds_read_b128 %7, %9 offset:6144\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[0][3]),
-          "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
-        : "v"(a_addr), "v"(b_addr)
-        : "memory");
-}
-
-template <>
-__device__ __forceinline__ void GFrag<4, 2, 128>::read(uint32_t a_addr, uint32_t b_addr)
-{
-    asm volatile(
-        "ds_read_b128 %0, %12 offset:0\n\t"
-        "ds_read_b128 %1, %12 offset:2048\n\t"
-        "ds_read_b128 %2, %12 offset:4096\n\t"
-        "ds_read_b128 %3, %12 offset:6144\n\t"
-        "ds_read_b128 %4, %12 offset:16384\n\t"
-        "ds_read_b128 %5, %12 offset:18432\n\t"
-        "ds_read_b128 %6, %12 offset:20480\n\t"
-        "ds_read_b128 %7, %12 offset:22528\n\t"
-        "ds_read_b128 %8, %13 offset:0\n\t"
-        "ds_read_b128 %9, %13 offset:2048\n\t"
-        "ds_read_b128 %10, %13 offset:4096\n\t"
-        "ds_read_b128 %11, %13 offset:6144\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[0][3]),
-          "=&v"(a[1][0]), "=&v"(a[1][1]), "=&v"(a[1][2]), "=&v"(a[1][3]),
-          "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
-        : "v"(a_addr), "v"(b_addr)
-        : "memory");
-}
-
-template <>
-__device__ __forceinline__ void GFrag<8, 1, 128>::read(uint32_t a_addr, uint32_t b_addr)
-{
-    asm volatile(
-        "ds_read_b128 %0, %12 offset:0\n\t"
-        "ds_read_b128 %1, %12 offset:2048\n\t"
-        "ds_read_b128 %2, %12 offset:4096\n\t"
-        "ds_read_b128 %3, %12 offset:6144\n\t"
-        "ds_read_b128 %4, %12 offset:8192\n\t"
-        "ds_read_b128 %5, %12 offset:10240\n\t"
-        "ds_read_b128 %6, %12 offset:12288\n\t"
-        "ds_read_b128 %7, %12 offset:14336\n\t"
-        "ds_read_b128 %8, %13 offset:0\n\t"
-        "ds_read_b128 %9, %13 offset:2048\n\t"
-        "ds_read_b128 %10, %13 offset:4096\n\t"
-        "ds_read_b128 %11, %13 offset:6144\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[0][3]),
-          "=&v"(a[0][4]), "=&v"(a[0][5]), "=&v"(a[0][6]), "=&v"(a[0][7]),
-          "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
-        : "v"(a_addr), "v"(b_addr)
-        : "memory");
-}
-
-template <>
-__device__ __forceinline__ void GFrag<8, 2, 128>::read(uint32_t a_addr, uint32_t b_addr)
-{
-    asm volatile(
-        "ds_read_b128 %0, %20 offset:0\n\t"
-        "ds_read_b128 %1, %20 offset:2048\n\t"
-        "ds_read_b128 %2, %20 offset:4096\n\t"
-        "ds_read_b128 %3, %20 offset:6144\n\t"
-        "ds_read_b128 %4, %20 offset:8192\n\t"
-        "ds_read_b128 %5, %20 offset:10240\n\t"
-        "ds_read_b128 %6, %20 offset:12288\n\t"
-        "ds_read_b128 %7, %20 offset:14336\n\t"
-        "ds_read_b128 %8, %20 offset:32768\n\t"
-        "ds_read_b128 %9, %20 offset:34816\n\t"
-        "ds_read_b128 %10, %20 offset:36864\n\t"
-        "ds_read_b128 %11, %20 offset:38912\n\t"
-        "ds_read_b128 %12, %20 offset:40960\n\t"
-        "ds_read_b128 %13, %20 offset:43008\n\t"
-        "ds_read_b128 %14, %20 offset:45056\n\t"
-        "ds_read_b128 %15, %20 offset:47104\n\t"
-        "ds_read_b128 %16, %21 offset:0\n\t"
-        "ds_read_b128 %17, %21 offset:2048\n\t"
-        "ds_read_b128 %18, %21 offset:4096\n\t"
-        "ds_read_b128 %19, %21 offset:6144\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0][0]), "=&v"(a[0][1]), "=&v"(a[0][2]), "=&v"(a[0][3]),
-          "=&v"(a[0][4]), "=&v"(a[0][5]), "=&v"(a[0][6]), "=&v"(a[0][7]),
-          "=&v"(a[1][0]), "=&v"(a[1][1]), "=&v"(a[1][2]), "=&v"(a[1][3]),
-          "=&v"(a[1][4]), "=&v"(a[1][5]), "=&v"(a[1][6]), "=&v"(a[1][7]),
-          "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
-        : "v"(a_addr), "v"(b_addr)
-        : "memory");
-}
-
+// global_load_lds_dwordx4 per 1 KB block of tile rows: lane l writes bytes
+// 16 l .. 16 l + 15 of the block and fetches the chunk the swizzle puts there),
+// through a ring of NS stages: NS - 1 stages are in flight while one is read.
+// A stage is complete once this wave's own loads of it have retired
+// (s_waitcnt vmcnt) and every wave has passed the barrier that follows.
 // 16 bytes per lane from global memory into LDS: lane l's bytes land at
 // dst + 16 l (dst is the same for the whole wave)
 __device__ __forceinline__ void lds_dma16(const void *src, void *dst)
@@ -511,6 +297,54 @@ __device__ __forceinline__ void wait_vmcnt()
 __device__ __forceinline__ int swz8(int r)
 {
     return (r ^ (r >> 3)) & 7;
+}
+
+// One ring step: start the copy of a later stage into `fill` (null when there
+// is none) and multiply the fragments of stage `cur`.  The two buffers reach
+// this function as distinct restrict pointers, so the compiler knows that its
+// LDS reads do not touch what the copy writes and adds no wait on the copy
+// before them; the kernel itself waits for a stage's copy (vmcnt) and for
+// every wave (barrier) before it is read.  The fragment reads are ordinary
+// loads, which the compiler interleaves with the MFMAs.
+template <int FI, int PA, int RB, int BK, int TILE_A, int LA, int LB>
+__device__ __forceinline__ void gemm_ring_step(unsigned char *__restrict__ fill,
+                                               const unsigned char *__restrict__ cur,
+                                               const bf16_t *const (&pa)[PA][LA],
+                                               const bf16_t *const (&pb)[LB], int k0, int wave,
+                                               const int (&a_rel)[BK / 32],
+                                               const int (&b_rel)[BK / 32], floatx4 (&acc)[FI][4])
+{
+    if (fill) {
+#pragma unroll
+        for (int p = 0; p < PA; ++p)
+#pragma unroll
+            for (int l = 0; l < LA; ++l)
+                lds_dma16(pa[p][l] + k0, fill + p * TILE_A + (wave * LA + l) * 1024);
+#pragma unroll
+        for (int l = 0; l < LB; ++l)
+            lds_dma16(pb[l] + k0, fill + PA * TILE_A + (wave * LB + l) * 1024);
+    }
+#pragma unroll
+    for (int h = 0; h < BK / 32; ++h) {
+        uint4 b[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            b[j] = *reinterpret_cast<const uint4 *>(cur + b_rel[h] + j * 16 * RB);
+#pragma unroll
+        for (int i = 0; i < FI; ++i) {
+            uint4 a[PA];
+#pragma unroll
+            for (int p = 0; p < PA; ++p)
+                a[p] = *reinterpret_cast<const uint4 *>(cur + a_rel[h] + p * TILE_A + i * 16 * RB);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int p = 0; p < PA; ++p)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, a[p]), __builtin_bit_cast(bf16x8, b[j]), acc[i][j],
+                        0, 0, 0);
+        }
+    }
 }
 
 template <int MODE, int WM, int NWN, int NS, int BK>
@@ -591,15 +425,14 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_lds_kernel(const bf16_t 
         for (int j = 0; j < 4; ++j)
             acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // byte addresses of this lane's fragments in stage 0, per 32-wide K half
+    // byte offsets of this lane's fragments in a stage, per 32-wide K half
     // (the swizzle of rows wm + 16 i + r16 does not depend on i)
-    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-    uint32_t a_off[BK / 32], b_off[BK / 32];
+    int a_rel[BK / 32], b_rel[BK / 32];
 #pragma unroll
     for (int h = 0; h < BK / 32; ++h) {
-        const uint32_t sw = (uint32_t)(((kg + 4 * h) ^ swz(r16)) * 16);
-        a_off[h] = lds0 + (uint32_t)((wm + r16) * RB) + sw;
-        b_off[h] = lds0 + (uint32_t)(PA * TILE_A + (wn + r16) * RB) + sw;
+        const int sw = ((kg + 4 * h) ^ swz(r16)) * 16;
+        a_rel[h] = (wm + r16) * RB + sw;
+        b_rel[h] = PA * TILE_A + (wn + r16) * RB + sw;
     }
 
 #pragma unroll
@@ -617,24 +450,12 @@ __global__ __launch_bounds__(2 * NWN * kWave) void gemm_lds_kernel(const bf16_t 
         else
             wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        // every wave is done with stage c - 1: refill its buffer
-        if (c + NS - 1 < nk)
-            issue(c + NS - 1);
-        const uint32_t st = (uint32_t)((c % NS) * STAGE);
-#pragma unroll
-        for (int h = 0; h < BK / 32; ++h) {
-            GFrag<FI, PA, RB> f;
-            f.read(a_off[h] + st, b_off[h] + st);
-#pragma unroll
-            for (int i = 0; i < FI; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int p = 0; p < PA; ++p)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, f.a[p][i]), __builtin_bit_cast(bf16x8, f.b[j]),
-                            acc[i][j], 0, 0, 0);
-        }
+        asm volatile("" ::: "memory");      // no LDS access moves above the barrier
+        // every wave is done with stage c - 1: its buffer takes stage c + NS - 1
+        const int nxt = c + NS - 1;
+        gemm_ring_step<FI, PA, RB, BK, TILE_A, LA, LB>(
+            nxt < nk ? lds + (nxt % NS) * STAGE : nullptr, lds + (c % NS) * STAGE, pa, pb,
+            kb + nxt * BK, wave, a_rel, b_rel, acc);
     }
     gemm_store<FI>(acc, Cm, M, N, m0 + wm, n0 + wn, lane);
 }

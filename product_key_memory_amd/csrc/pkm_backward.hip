@@ -56,7 +56,8 @@ __device__ __forceinline__ float load_elem<bf16_t>(const bf16_t *p, int64_t i)
 constexpr int kL1Threads = 512;
 constexpr int kColWaves = 16;
 constexpr int kColRows = 16;          // block rows per wave in the column scan (blocks <= 256)
-constexpr int kL2Threads = 1024;
+constexpr int kL2Threads = 512;
+constexpr int kL2Unroll = 4;          // pairs in flight per thread in the level-2 passes
 
 __device__ __forceinline__ int64_t l1_begin(int64_t chunk, int64_t picks)
 {
@@ -188,30 +189,62 @@ __global__ __launch_bounds__(kL2Threads) void bucket_sort_kernel(
     for (int j = threadIdx.x; j < B; j += kL2Threads)
         h[j] = 0;
     __syncthreads();
-    for (int64_t p = beg + (int)threadIdx.x; p < end; p += kL2Threads)
-        atomicAdd(&h[pairs[p].y], 1);
+    // kL2Unroll pairs per thread in flight before their counters are bumped:
+    // a large bucket (a Zipf-hot slot's) is this kernel's critical path
+    for (int64_t q = beg + (int)threadIdx.x; q < end; q += kL2Threads * kL2Unroll) {
+        int key[kL2Unroll];
+#pragma unroll
+        for (int u = 0; u < kL2Unroll; ++u) {
+            const int64_t p = q + (int64_t)u * kL2Threads;
+            key[u] = p < end ? pairs[p].y : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kL2Unroll; ++u)
+            if (key[u] >= 0)
+                atomicAdd(&h[key[u]], 1);
+    }
     __syncthreads();
-    // exclusive scan of h[0 .. B), B <= kL2Threads: one bin per thread
+    // exclusive scan of h[0 .. B): thread t owns bins [BPT t, BPT t + BPT)
+    constexpr int BPT = kMaxBucketSlots / kL2Threads;
     const int lane = lane_id(), w = threadIdx.x / kWave;
-    const int v = (int)threadIdx.x < B ? h[threadIdx.x] : 0;
+    int v[BPT], local = 0;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+        const int bin = BPT * (int)threadIdx.x + e;
+        v[e] = bin < B ? h[bin] : 0;
+        local += v[e];
+    }
     int tw;
-    const int excl = wave_exclusive_scan(v, &tw);
+    const int excl = wave_exclusive_scan(local, &tw);
     if (lane == 0)
         wsum[w] = tw;
     __syncthreads();
     int run = beg + excl;
     for (int u = 0; u < w; ++u)
         run += wsum[u];
-    if ((int)threadIdx.x < nbins) {
-        h[threadIdx.x] = run;
-        slot_start[f0 + threadIdx.x] = run;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+        const int bin = BPT * (int)threadIdx.x + e;
+        if (bin < nbins) {
+            h[bin] = run;
+            slot_start[f0 + bin] = run;
+        }
+        run += v[e];
     }
     if (f0 + B >= slots && threadIdx.x == 0)
         slot_start[slots] = end;
     __syncthreads();
-    for (int64_t p = beg + (int)threadIdx.x; p < end; p += kL2Threads) {
-        const int2 pr = pairs[p];
-        order[atomicAdd(&h[pr.y], 1)] = pr.x;
+    for (int64_t q = beg + (int)threadIdx.x; q < end; q += kL2Threads * kL2Unroll) {
+        int2 pr[kL2Unroll];
+#pragma unroll
+        for (int u = 0; u < kL2Unroll; ++u) {
+            const int64_t p = q + (int64_t)u * kL2Threads;
+            pr[u] = p < end ? pairs[p] : make_int2(0, -1);
+        }
+#pragma unroll
+        for (int u = 0; u < kL2Unroll; ++u)
+            if (pr[u].y >= 0)
+                order[atomicAdd(&h[pr[u].y], 1)] = pr[u].x;
     }
 }
 

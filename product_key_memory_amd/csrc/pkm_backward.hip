@@ -57,7 +57,7 @@ constexpr int kL1Threads = 512;
 constexpr int kColWaves = 16;
 constexpr int kColRows = 16;          // block rows per wave in the column scan (blocks <= 256)
 constexpr int kL2Threads = 512;
-constexpr int kL2Unroll = 4;          // pairs in flight per thread in the level-2 passes
+constexpr int kL2Unroll = 4;          // picks in flight per thread in the counting passes
 
 __device__ __forceinline__ int64_t l1_begin(int64_t chunk, int64_t picks)
 {
@@ -76,8 +76,18 @@ __global__ __launch_bounds__(kL1Threads) void bucket_hist_kernel(
     __syncthreads();
     const int64_t p0 = l1_begin(chunk, picks);
     const int64_t p1 = p0 + chunk < picks ? p0 + chunk : picks;
-    for (int64_t p = p0 + threadIdx.x; p < p1; p += kL1Threads)
-        atomicAdd(&h[idx[p] >> shift], 1);
+    for (int64_t q = p0 + threadIdx.x; q < p1; q += kL1Threads * kL2Unroll) {
+        int32_t f[kL2Unroll];
+#pragma unroll
+        for (int u = 0; u < kL2Unroll; ++u) {
+            const int64_t p = q + (int64_t)u * kL1Threads;
+            f[u] = p < p1 ? idx[p] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kL2Unroll; ++u)
+            if (f[u] >= 0)
+                atomicAdd(&h[f[u] >> shift], 1);
+    }
     __syncthreads();
     int32_t *row = bhist + (int64_t)blockIdx.x * nb;
     for (int b = threadIdx.x; b < nb; b += kL1Threads)
@@ -166,10 +176,19 @@ __global__ __launch_bounds__(kL1Threads) void bucket_scatter_kernel(
     const int32_t lowmask = (1 << shift) - 1;
     const int64_t p0 = l1_begin(chunk, picks);
     const int64_t p1 = p0 + chunk < picks ? p0 + chunk : picks;
-    for (int64_t p = p0 + threadIdx.x; p < p1; p += kL1Threads) {
-        const int32_t f = idx[p];
-        const int pos = atomicAdd(&cur[f >> shift], 1);
-        pairs[pos] = make_int2((int32_t)p, f & lowmask);
+    for (int64_t q = p0 + threadIdx.x; q < p1; q += kL1Threads * kL2Unroll) {
+        int32_t f[kL2Unroll];
+#pragma unroll
+        for (int u = 0; u < kL2Unroll; ++u) {
+            const int64_t p = q + (int64_t)u * kL1Threads;
+            f[u] = p < p1 ? idx[p] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kL2Unroll; ++u)
+            if (f[u] >= 0) {
+                const int pos = atomicAdd(&cur[f[u] >> shift], 1);
+                pairs[pos] = make_int2((int32_t)(q + (int64_t)u * kL1Threads), f[u] & lowmask);
+            }
     }
 }
 

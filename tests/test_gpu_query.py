@@ -97,6 +97,21 @@ def test_query_direct_lds_path(T, dm, D):
 
 
 @pytest.mark.slow
+def test_query_many_tokens():
+    """More 64-token tiles than a launch's y extent allows (T = 2^22 + 37:
+    65,537 tiles of the padded token pitch): the transposes and the fused
+    batch-norm step walk their token tiles by the grid's y extent, and the
+    products run on 1-D grids of tiles."""
+    T = (1 << 22) + 37
+    (q, z, mean, rstd, dx, dW, dg, db), ref, gref = _run(T, 8, 8, "bf16", 95, False)
+    assert _rows_rel(z, ref["z"])[0] <= 1e-5
+    assert _bf16_q_ok(q, ref["q"])
+    for got, want in ((dx, gref["dx"]), (dW, gref["dW"])):
+        gate, tight = _rows_rel(got, want)
+        assert gate <= 1e-4 and tight <= 2e-5, (gate, tight)
+
+
+@pytest.mark.slow
 def test_query_model_width():
     """The workload's widths: d_model = 1600 (the pages' model), d_out = H d_k = 2048."""
     (q, z, mean, rstd, dx, dW, dg, db), ref, gref = _run(2048, 1600, 2048, "bf16", 92, True)

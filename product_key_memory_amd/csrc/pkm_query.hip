@@ -13,10 +13,11 @@
 //                      8 waves, operands copied from global memory straight
 //                      into LDS (global_load_lds) through a ring of 64-wide K
 //                      stages, one stage in flight while the other is used
-//   gemm_kernel        the same product with register-staged 128-row tiles,
-//                      for float32 operands (v_mfma_f32_16x16x4_f32) and for
-//                      bf16 shapes the direct kernel does not take (K not a
-//                      multiple of 64, unaligned rows)
+//   gemm_kernel        the same product with register-staged tiles (256 x 128
+//                      for bf16, 128 x 128 for float32), for float32 operands
+//                      (v_mfma_f32_16x16x4_f32) and for bf16 shapes the direct
+//                      kernel does not take (K not a multiple of 64, unaligned
+//                      rows)
 //   sum_slices_kernel  the split-K partial products summed
 //   bn_partial_kernel  per (row chunk, column): count, mean, M2 (Welford over
 //                      the chunk's rows, merged across waves by Chan's rule)

@@ -44,7 +44,9 @@ __global__ __launch_bounds__(kUpdWaves *kWave) void sparse_update_kernel(
     // 8 elements per step: one 16-byte chunk of a bf16 row, two of a float32
     // row; a lane's steps are all loaded before the first is updated
     const int64_t row = f * d_v;
-    constexpr int kMaxSteps = 4;            // d_v <= 4 * 8 * 64 = 2048 in one pass
+    // d_v <= 2 * 8 * 64 = 1024 in one pass (wider rows take more passes);
+    // four steps a pass held registers for d_v = 2048 and cut the occupancy
+    constexpr int kMaxSteps = 2;
     for (int base = 0; base < d_v; base += kMaxSteps * 8 * kWave) {
         float w[kMaxSteps][8], g[kMaxSteps][8];
 #pragma unroll

@@ -92,6 +92,15 @@ def test_fused_sgd_widest_rows(dtype):
     _fused_vs_chain(inp, 3, 0.02)
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_fused_sgd_ragged_rows(dtype):
+    """d_v = 1600 (the 1024^2-slot workload's rows): 200 16-byte chunks of bf16,
+    a ragged last round of lanes, with runs long enough to take the split path."""
+    inp = pkm_inputs.custom(400, 2, 12, 6, 32, 1600, dtype=dtype, seed=605)
+    print(f"[backward_sgd] d_v 1600 {dtype}", flush=True)
+    _fused_vs_chain(inp, 6, 0.02)
+
+
 def test_fused_sgd_bench_workload():
     """The full bench workload (Zipf-hot slots: some runs are long)."""
     inp = pkm_inputs.make("base-bf16-zipf-bwd")

@@ -245,8 +245,8 @@ def measure_fused_sgd(torch, _lib, p, bufs, ws, ws_bytes, stream) -> dict:
     starts = P(ws) + ((p.T * p.H * p.k * 4 + 255) // 256) * 256
 
     def chain():
-        rc = _lib.backward(p, P(q), P(keys), P(values), P(idx), P(wts), P(dy), P(dq), P(dkeys),
-                           P(dvalues), 0, P(ws), ws_bytes, sp)
+        rc = _lib.backward_overwrite(p, P(q), P(keys), P(values), P(idx), P(wts), P(dy), P(dq),
+                                     P(dkeys), P(dvalues), P(ws), ws_bytes, sp)
         return rc | _lib.sparse_sgd(p, P(values), P(dvalues), starts, 1e-3, sp)
 
     def fused():
@@ -394,8 +394,8 @@ def run_sweep(args) -> None:
             def step():
                 rc = _lib.forward(p, P(q), P(keys), P(values), P(y), P(idx), P(wts), None,
                                   P(fws), fb, sp)
-                rc |= _lib.backward(p, P(q), P(keys), P(values), P(idx), P(wts), P(dy), P(dq),
-                                    P(dkeys), P(dvalues), 0, P(bws), bb, sp)
+                rc |= _lib.backward_overwrite(p, P(q), P(keys), P(values), P(idx), P(wts), P(dy),
+                                              P(dq), P(dkeys), P(dvalues), P(bws), bb, sp)
                 if rc:
                     raise RuntimeError(f"libpkm returned {rc}")
 

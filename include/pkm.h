@@ -125,20 +125,28 @@ pkm_status_t pkm_forward(const pkm_problem_t *p, const void *q, const void *keys
  *   dy       [T][d_v]           dtype
  *   dq       [T][H][d_k]        float32 OUT, overwritten
  *   dkeys    [H][2][n][d_k/2]   float32 OUT, overwritten
- *   dvalues  [n*n][d_v]         float32; dvalues_accumulate != 0: IN/OUT,
- *                               ACCUMULATED (+=), rows no pick selects are left
- *                               untouched; dvalues_accumulate == 0: OUT,
- *                               overwritten (rows no pick selects become 0),
- *                               which also spares reading the old rows.
- * The order in which float32 partial sums meet (slot sort, atomics on rows
- * shared by several waves) varies from run to run, so results vary at the
- * rounding level.
+ *   dvalues  [n*n][d_v]         float32 IN/OUT, ACCUMULATED (+=): the caller
+ *                               zeroes it (or keeps an earlier gradient to add
+ *                               to); rows no pick selects are left untouched.
+ *   workspace  pkm_workspace_bytes(p, 1) bytes (NULL allowed when that is 0)
+ * The order in which float32 partial sums of one slot meet (slot sort,
+ * atomics on rows shared by several waves) varies from run to run, so
+ * dvalues varies at the rounding level.
  */
 pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *keys,
                           const void *values, const int32_t *idx, const float *weights,
-                          const void *dy, float *dq, float *dkeys, float *dvalues,
-                          int dvalues_accumulate, void *workspace, size_t workspace_bytes,
-                          void *stream);
+                          const void *dy, float *dq, float *dkeys, float *dvalues, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* pkm_backward with dvalues OVERWRITTEN instead of accumulated: every row of
+ * dvalues is written, rows no pick selects become 0, and the old contents are
+ * never read (the mode of an optimizer that consumes a fresh gradient; it
+ * spares reading the n*n x d_v float32 array).  Same arguments, same
+ * workspace as pkm_backward. */
+pkm_status_t pkm_backward_overwrite(const pkm_problem_t *p, const void *q, const void *keys,
+                                    const void *values, const int32_t *idx, const float *weights,
+                                    const void *dy, float *dq, float *dkeys, float *dvalues,
+                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * The backward with the sparse SGD step fused in (gptget.net summary,

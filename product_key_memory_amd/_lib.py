@@ -27,7 +27,8 @@ STATUS = {
 }
 
 # every symbol include/pkm.h declares
-EXPORTS = ("pkm_workspace_bytes", "pkm_forward", "pkm_backward", "pkm_backward_sgd",
+EXPORTS = ("pkm_workspace_bytes", "pkm_forward", "pkm_backward", "pkm_backward_overwrite",
+           "pkm_backward_sgd",
            "pkm_forward_select",
            "pkm_forward_gather", "pkm_slot_sort", "pkm_backward_values", "pkm_backward_queries",
            "pkm_sparse_sgd", "pkm_sparse_adam", "pkm_slot_usage", "pkm_query_workspace_bytes",
@@ -69,9 +70,10 @@ def lib() -> ctypes.CDLL:
         L.pkm_workspace_bytes.restype = c_size
         L.pkm_forward.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, c_size, P]
         L.pkm_forward.restype = ctypes.c_int
-        L.pkm_backward.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P,
-                                   ctypes.c_int, P, c_size, P]
-        L.pkm_backward.restype = ctypes.c_int
+        for name in ("pkm_backward", "pkm_backward_overwrite"):
+            getattr(L, name).argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P, P,
+                                         c_size, P]
+            getattr(L, name).restype = ctypes.c_int
         L.pkm_backward_sgd.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P,
                                        ctypes.c_float, P, c_size, P]
         L.pkm_backward_sgd.restype = ctypes.c_int
@@ -115,10 +117,18 @@ def forward(p: Problem, q, keys, values, y, idx, weights, scores, ws, ws_bytes, 
                              ws_bytes, stream)
 
 
-def backward(p: Problem, q, keys, values, idx, weights, dy, dq, dkeys, dvalues, accumulate,
-             ws, ws_bytes, stream) -> int:
+def backward(p: Problem, q, keys, values, idx, weights, dy, dq, dkeys, dvalues, ws, ws_bytes,
+             stream) -> int:
+    """pkm_backward: dvalues accumulated (+=)."""
     return lib().pkm_backward(ctypes.byref(p), q, keys, values, idx, weights, dy, dq, dkeys,
-                              dvalues, int(accumulate), ws, ws_bytes, stream)
+                              dvalues, ws, ws_bytes, stream)
+
+
+def backward_overwrite(p: Problem, q, keys, values, idx, weights, dy, dq, dkeys, dvalues, ws,
+                       ws_bytes, stream) -> int:
+    """pkm_backward_overwrite: dvalues overwritten (unselected rows become 0)."""
+    return lib().pkm_backward_overwrite(ctypes.byref(p), q, keys, values, idx, weights, dy, dq,
+                                        dkeys, dvalues, ws, ws_bytes, stream)
 
 
 def backward_sgd(p: Problem, q, keys, values, idx, weights, dy, dq, dkeys, lr, ws, ws_bytes,

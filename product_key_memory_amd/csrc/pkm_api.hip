@@ -246,11 +246,15 @@ pkm_status_t pkm_backward_queries(const pkm_problem_t *p, const void *q, const v
                : PKM_ERR_HIP;
 }
 
-pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *keys,
-                          const void *values, const int32_t *idx, const float *weights,
-                          const void *dy, float *dq, float *dkeys, float *dvalues,
-                          int dvalues_accumulate, void *workspace, size_t workspace_bytes,
-                          void *stream)
+}  // extern "C"
+
+namespace {
+
+// pkm_backward (accumulate != 0) and pkm_backward_overwrite (accumulate == 0)
+pkm_status_t backward_impl(const pkm_problem_t *p, const void *q, const void *keys,
+                           const void *values, const int32_t *idx, const float *weights,
+                           const void *dy, float *dq, float *dkeys, float *dvalues,
+                           int accumulate, void *workspace, size_t workspace_bytes, void *stream)
 {
     pkm_status_t st = check_problem(p, true);
     if (st != PKM_OK)
@@ -278,12 +282,34 @@ pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *key
         if (st != PKM_OK)
             return st;
     }
-    st = pkm_backward_values(p, values, idx, weights, dy, slot_start, order, dvalues,
-                             dvalues_accumulate, dw, stream);
+    st = pkm_backward_values(p, values, idx, weights, dy, slot_start, order, dvalues, accumulate,
+                             dw, stream);
     if (st != PKM_OK)
         return st;
     return pkm_backward_queries(p, q, keys, idx, weights, dw, dq, dkeys, scratch, scratch_bytes,
                                 stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *keys,
+                          const void *values, const int32_t *idx, const float *weights,
+                          const void *dy, float *dq, float *dkeys, float *dvalues, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    return backward_impl(p, q, keys, values, idx, weights, dy, dq, dkeys, dvalues, 1, workspace,
+                         workspace_bytes, stream);
+}
+
+pkm_status_t pkm_backward_overwrite(const pkm_problem_t *p, const void *q, const void *keys,
+                                    const void *values, const int32_t *idx, const float *weights,
+                                    const void *dy, float *dq, float *dkeys, float *dvalues,
+                                    void *workspace, size_t workspace_bytes, void *stream)
+{
+    return backward_impl(p, q, keys, values, idx, weights, dy, dq, dkeys, dvalues, 0, workspace,
+                         workspace_bytes, stream);
 }
 
 pkm_status_t pkm_backward_sgd(const pkm_problem_t *p, const void *q, const void *keys,

@@ -227,13 +227,17 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
         if constexpr (!kFirst)
             tau = max(tau, (uint32_t)(prev[k - 1] >> 32));
 
-        // survivors: ord >= tau
+        // survivors: ord >= tau.  A token past T (it scored token 0's query)
+        // keeps nothing: no count, no bisection, no compaction store that
+        // claims a position -- its 4 lanes share `live`, so total = 0
         int cnt = 0;
 #pragma unroll
         for (int j = 0; j < kFastTiles; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 cnt += so[j][i] >= tau ? 1 : 0;
+        if (!live)
+            cnt = 0;
         int total = group4_sum(cnt);
         bool fits = total <= kFastSurv;
 
@@ -242,7 +246,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
         // tied scores (more than 64 survivors are real scores, so is the
         // k-th largest)
         uint32_t kth = tau, tie_idx = 0xFFFFFFFFu;
-        if (__ballot(!fits && live) != 0) {
+        if (__ballot(!fits) != 0) {
             uint32_t K = 0;
             for (int bit = 31; bit >= 0; --bit) {
                 const uint32_t cand = K | (1u << bit);
@@ -317,7 +321,8 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t o = so[j][i];
-                const bool keep = exact ? (o > kth || (o == kth && 16 * j + i <= lim_t)) : o >= kth;
+                const bool keep =
+                    live && (exact ? (o > kth || (o == kth && 16 * j + i <= lim_t)) : o >= kth);
                 surv_s[off] = o;
                 surv_i[off] = (uint32_t)(16 * j + i);
                 off += keep ? 1 : 0;

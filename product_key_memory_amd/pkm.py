@@ -95,8 +95,9 @@ def pkm_backward(q: torch.Tensor, keys: torch.Tensor, values: torch.Tensor, idx:
                  weights: torch.Tensor, dy: torch.Tensor, dvalues: torch.Tensor | None = None,
                  out=None):
     """Backward pass.  Returns (dq [T,H,d_k], dkeys [H,2,n,d_k/2], dvalues [n*n,d_v]),
-    all float32.  A given dvalues is ACCUMULATED into; otherwise a new one is
-    returned (overwritten by the library: rows no pick selected are 0)."""
+    all float32.  A given dvalues is ACCUMULATED into (pkm_backward); otherwise
+    a new one is returned, written whole by pkm_backward_overwrite (rows no pick
+    selected are 0)."""
     T, H, n, d_k, d_v = _shapes(q, keys, values)
     dev, dt = q.device, q.dtype
     k = idx.shape[2]
@@ -121,11 +122,11 @@ def pkm_backward(q: torch.Tensor, keys: torch.Tensor, values: torch.Tensor, idx:
     else:
         dq, dkeys = out
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
-    rc = _lib.backward(p, _ptr(q), _ptr(keys), _ptr(values), _ptr(idx), _ptr(weights), _ptr(dy),
-                       _ptr(dq), _ptr(dkeys), _ptr(dvalues), accumulate, _ptr(ws), ws_bytes,
-                       _stream(dev))
+    call = _lib.backward if accumulate else _lib.backward_overwrite
+    rc = call(p, _ptr(q), _ptr(keys), _ptr(values), _ptr(idx), _ptr(weights), _ptr(dy), _ptr(dq),
+              _ptr(dkeys), _ptr(dvalues), _ptr(ws), ws_bytes, _stream(dev))
     if rc != 0:
-        raise PKMError(rc, "pkm_backward")
+        raise PKMError(rc, "pkm_backward" if accumulate else "pkm_backward_overwrite")
     return dq, dkeys, dvalues
 
 

@@ -30,6 +30,26 @@ def bits_to_f64(a: np.ndarray) -> np.ndarray:
     return a.astype(np.float64)
 
 
+def y_sum_bound(values: np.ndarray, idx: np.ndarray, w_gpu: np.ndarray, w_ref: np.ndarray,
+                chunk: int = 64) -> np.ndarray:
+    """Per element of y [T][d_v]: how far float32 sums of the GPU's weights
+    times the value rows may lie from the exact sum with the exact weights,
+        sum over picks of (|w_gpu - w_ref| + gamma |w_gpu|) * |values[f][c]|,
+    gamma = (H k + 2) 2^-24 (with 1% slack): the classic bound on n rounded
+    multiply-adds, any order."""
+    T, H, k = idx.shape
+    d_v = values.shape[1]
+    wg = w_gpu.astype(np.float64)
+    gamma = 1.01 * (H * k + 2) * 2.0 ** -24
+    a = (np.abs(wg - w_ref) + gamma * np.abs(wg)).reshape(T, H * k)
+    out = np.empty((T, d_v))
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        rows = np.abs(bits_to_f64(values[idx[t0:t1].reshape(-1)])).reshape(t1 - t0, H * k, d_v)
+        out[t0:t1] = np.einsum("tp,tpc->tc", a[t0:t1], rows)
+    return out
+
+
 def run_parity(orc, inp: dict, k: int, subset=None, backward: bool = False, tol=None,
                tight=None, nthreads: int = 0) -> dict:
     """Run the GPU path on all of inp's tokens; check `subset` (all if None)
@@ -60,6 +80,9 @@ def run_parity(orc, inp: dict, k: int, subset=None, backward: bool = False, tol=
     assert serr <= 1e-4, f"scores differ by {serr:.3e}"
     rep["w_err"], rep["score_err"] = werr, serr
     rep["y_err"] = parity.assert_rows_close("y", g_y, given["y"], tol)
+    rep["y_elem_err"] = parity.assert_elems_close("y", g_y, given["y"], tol)
+    bound = y_sum_bound(inp["values"], g_idx, g_w, given["weights"])
+    rep["y_bound_ratio"] = parity.assert_y_bound("y", g_y, given["y"], bound, w.dtype)
     if tight is not None:
         assert rep["y_err"] <= tight["y"], f"y error {rep['y_err']:.3e} above the expected {tight['y']}"
     if backward:
@@ -83,9 +106,14 @@ def run_parity(orc, inp: dict, k: int, subset=None, backward: bool = False, tol=
         g_dq = to_host(dq)[sub]
         rep["dq_err"] = parity.assert_rows_close("dq", g_dq, ob["dq"], tol,
                                                  abs_floor=1e-3 * term["dq"])
+        rep["dq_elem_err"] = parity.assert_elems_close("dq", g_dq, ob["dq"], tol,
+                                                       abs_floor=1e-3 * term["dq"])
         g_dk = to_host(dkeys).reshape(-1, half)
         rep["dkeys_err"] = parity.assert_rows_close("dkeys", g_dk, ob["dkeys"].reshape(-1, half), tol,
                                                     abs_floor=1e-3 * term["dkeys"])
+        rep["dkeys_elem_err"] = parity.assert_elems_close("dkeys", g_dk,
+                                                          ob["dkeys"].reshape(-1, half), tol,
+                                                          abs_floor=1e-3 * term["dkeys"])
         g_dv = to_host(dvalues)
         touched = np.zeros(n * n, bool)
         touched[g_idx.ravel()] = True
@@ -93,6 +121,9 @@ def run_parity(orc, inp: dict, k: int, subset=None, backward: bool = False, tol=
         rows = np.nonzero(touched)[0]
         rep["dvalues_err"] = parity.assert_rows_close("dvalues", g_dv[rows], ob["dvalues"][rows], tol,
                                                       abs_floor=1e-3 * term["dvalues"])
+        rep["dvalues_elem_err"] = parity.assert_elems_close("dvalues", g_dv[rows],
+                                                            ob["dvalues"][rows], tol,
+                                                            abs_floor=1e-3 * term["dvalues"])
         if tight is not None:
             # against the typical row size: rows whose own sum nearly cancels
             # (a hot sub-key shared by most picks of a head) amplify float32

@@ -23,6 +23,8 @@ What pins what:
                     unselected rows exactly 0
   finite_diff       central differences of L = sum <dy, y> in float64
   linearity         y linear in values; dvalues independent of values
+  given_idx         forward on a given selection: forward()'s own result on
+                    its own selection, explicit-key recomputation on others
 """
 from __future__ import annotations
 
@@ -298,6 +300,39 @@ def pin_linearity(o):
     b1 = o.backward(q, keys, v1, r1["idx"], r1["weights"], dy)
     b2 = o.backward(q, keys, v2, r1["idx"], r1["weights"], dy)
     assert np.array_equal(b1["dvalues"], b2["dvalues"]), "dvalues must not depend on values"
+
+
+def pin_given_idx(o):
+    """forward_given_idx: on forward()'s own selection it must reproduce
+    forward()'s scores, weights and y; on any other selection (reversed order,
+    random non-top-k slots, repeated across heads) it must equal the plain
+    recomputation from explicit keys (section "Implied keys vs stored
+    sub-keys"): scores = C_i ++ C'_j against q, a scipy softmax over the given
+    k, y = sum over heads of w @ values[idx]."""
+    rng = np.random.default_rng(22)
+    for (T, H, n, d_k, d_v, k) in [(5, 2, 6, 8, 3, 4), (4, 3, 7, 6, 2, 5), (3, 1, 4, 4, 5, 16)]:
+        q, keys, values = rand_problem(rng, T, H, n, d_k, d_v)
+        r = o.forward(q, keys, values, k)
+        g = o.forward_given_idx(q, keys, values, r["idx"])
+        assert np.allclose(g["scores"], r["scores"], rtol=1e-14, atol=1e-14), "given own idx: scores"
+        assert np.allclose(g["weights"], r["weights"], rtol=1e-14, atol=1e-15), "given own idx: weights"
+        assert np.allclose(g["y"], r["y"], rtol=1e-13, atol=1e-14), "given own idx: y"
+        for kind in ("reversed", "random"):
+            if kind == "reversed":
+                sel = r["idx"][:, :, ::-1].copy()
+            else:
+                sel = np.stack([np.stack([rng.choice(n * n, size=k, replace=False)
+                                          for _ in range(H)]) for _ in range(T)]).astype(np.int32)
+            got = o.forward_given_idx(q, keys, values, sel)
+            y = np.zeros((T, d_v))
+            for t in range(T):
+                for h in range(H):
+                    s = explicit_keys(keys, h)[sel[t, h]] @ q[t, h]
+                    w = scipy.special.softmax(s)
+                    assert np.allclose(got["scores"][t, h], s, rtol=1e-12, atol=1e-12), f"{kind}: scores"
+                    assert np.allclose(got["weights"][t, h], w, rtol=1e-12, atol=1e-15), f"{kind}: weights"
+                    y[t] += w @ values[sel[t, h]]
+            assert np.allclose(got["y"], y, rtol=1e-12, atol=1e-13), f"{kind}: y"
 
 
 ALL_PINS = {name[4:]: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

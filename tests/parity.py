@@ -10,8 +10,11 @@ Rules (tolerances are relative, per row, L2):
     >= s_k - 1e-4 * max(|s_k|, |s_k1|).
   * everything else is compared with the oracle recomputed on the GPU's own
     selection, so a legitimate near-tie choice is judged on its own terms:
-    weights element-wise (absolute), y / dq / dkeys / dvalues per row,
-    ||gpu - oracle|| / max(||oracle||, 1e-3 * rms row norm) <= tol.
+    weights element-wise (absolute); y / dq / dkeys / dvalues per row,
+    ||gpu - oracle|| / max(||oracle||, 1e-3 * rms row norm) <= tol, AND
+    element by element, |gpu - oracle| <= tol * (|oracle| + rms of the row);
+    y also element by element within the float32 summation bound plus (bf16)
+    half a bfloat16 spacing -- what the arithmetic itself allows.
   * value-gradient rows no pick selected must be exactly zero.
 """
 from __future__ import annotations
@@ -63,6 +66,61 @@ def row_rel_err(got: np.ndarray, want: np.ndarray, floor: float = 1e-3,
     rms = np.sqrt(np.mean(norms ** 2)) if norms.size else 0.0
     den = np.maximum(np.maximum(norms, floor * rms), abs_floor) + 1e-300
     return np.linalg.norm(got - want, axis=1) / den
+
+
+def elem_rel_err(got: np.ndarray, want: np.ndarray, floor: float = 1e-3,
+                 abs_floor: float = 0.0) -> np.ndarray:
+    """Per element |got - want| / (|want| + rms of want's row), rows = first
+    axis.  The row term is floored like row_rel_err's denominator, scaled to
+    one element: at floor * (rms row norm of the tensor) / sqrt(row length)
+    and at abs_floor / sqrt(row length)."""
+    got = got.reshape(got.shape[0], -1).astype(np.float64)
+    want = want.reshape(want.shape[0], -1).astype(np.float64)
+    if want.size == 0:
+        return np.zeros(want.shape)
+    ncol = want.shape[1]
+    norms = np.linalg.norm(want, axis=1, keepdims=True)
+    tensor_rms = np.sqrt(np.mean(norms ** 2))
+    row = np.maximum(np.maximum(norms, floor * tensor_rms), abs_floor) / np.sqrt(ncol)
+    return np.abs(got - want) / (np.abs(want) + row + 1e-300)
+
+
+def assert_elems_close(name: str, got, want, tol: float, floor: float = 1e-3,
+                       abs_floor: float = 0.0) -> float:
+    """Element by element: |g - o| <= tol * (|o| + rms of the row)."""
+    err = elem_rel_err(np.asarray(got), np.asarray(want), floor, abs_floor)
+    worst = float(err.max()) if err.size else 0.0
+    if err.size and worst > tol:
+        at = np.unravel_index(int(err.argmax()), err.shape)
+        raise AssertionError(f"{name}: worst element error {worst:.3e} > {tol:.1e} at (row, col) "
+                             f"{tuple(int(x) for x in at)}")
+    return worst
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bfloat16 numbers (8 significant bits) at |x|: 2^(e - 8) for
+    |x| in [2^(e-1), 2^e); the subnormal spacing below the normal range."""
+    m, e = np.frexp(np.abs(x))
+    return np.ldexp(1.0, np.maximum(e, -125) - 8)
+
+
+def assert_y_bound(name: str, got, want, bound, storage: str) -> float:
+    """y element by element against what the arithmetic allows: the float32
+    sums may differ from the exact value by at most `bound` (the summation
+    bound, see gpu_util.y_sum_bound), and bfloat16 storage adds one rounding
+    to nearest, at most half a spacing at the stored magnitude.  Returns the
+    worst ratio of the error to the allowance."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    allow = bound + (0.5 * bf16_ulp(np.abs(want) + bound) if storage == "bf16" else 0.0)
+    ratio = np.abs(got - want) / (allow + 1e-300)
+    worst = float(ratio.max()) if ratio.size else 0.0
+    if ratio.size and worst > 1.0:
+        at = np.unravel_index(int(ratio.argmax()), ratio.shape)
+        raise AssertionError(f"{name}: element {tuple(int(x) for x in at)} off by "
+                             f"{abs(got[at] - want[at]):.3e}, allowed {allow[at]:.3e} "
+                             f"(float32 sums + {storage} rounding)")
+    return worst
 
 
 def assert_rows_close(name: str, got, want, tol: float, floor: float = 1e-3,

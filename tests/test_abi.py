@@ -66,9 +66,32 @@ def test_backward_workspace_checks():
     assert _lib.slot_sort(p, FAKE, FAKE, FAKE, FAKE, 16, None) == 4
     assert _lib.backward_queries(p, *[FAKE] * 7, FAKE, 16, None) == 4
     args = [FAKE] * 9
-    assert _lib.backward(p, *args, 0, FAKE, need - 1, None) == 4
-    assert _lib.backward(p, *args, 1, None, 0, None) == 1
-    assert _lib.backward(P(d_v=4104), *args, 0, FAKE, 1 << 30, None) == 2   # backward row limit
+    for call in (_lib.backward, _lib.backward_overwrite):
+        assert call(p, *args, FAKE, need - 1, None) == 4
+        assert call(p, *args, None, 0, None) == 1
+        assert call(P(d_v=4104), *args, FAKE, 1 << 30, None) == 2   # backward row limit
+        assert call(p, *args[:8], None, FAKE, need, None) == 1        # dvalues is required
+
+
+def test_backward_prototype_is_the_contract():
+    """pkm_backward has the contract's 13 parameters -- (p, q, keys, values, idx,
+    weights, dy, dq, dkeys, dvalues, workspace, workspace_bytes, stream) with
+    dvalues accumulated -- and the overwrite mode is an entry point of its own
+    with the same parameters."""
+    with open(os.path.join(ROOT, "include", "pkm.h")) as f:
+        text = f.read()
+
+    def params(name):
+        m = re.search(r"pkm_status_t\s+" + name + r"\s*\(([^)]*)\)", text)
+        assert m, name
+        return [re.split(r"[\s*]+", a.strip())[-1] for a in m.group(1).split(",")]
+
+    want = ["p", "q", "keys", "values", "idx", "weights", "dy", "dq", "dkeys", "dvalues",
+            "workspace", "workspace_bytes", "stream"]
+    assert params("pkm_backward") == want
+    assert params("pkm_backward_overwrite") == want
+    assert "ACCUMULATED" in text.split("pkm_status_t pkm_backward(")[0].rsplit("/*", 1)[1]
+    assert len(_lib.lib().pkm_backward.argtypes) == 13
 
 
 def test_backward_sgd_checks():

@@ -30,13 +30,13 @@ def test_proj_fp32_full(orc):
 
 def test_base_bf16_sampled(orc):
     inp = pkm_inputs.make("base-bf16")
-    sub = pkm_inputs.token_subset(inp["w"].T, 192, seed=7)
+    sub = pkm_inputs.token_subset(inp["w"].T, 1024, seed=7)
     gpu_util.run_parity(orc, inp, inp["w"].k, subset=sub, tight=TIGHT["bf16"])
 
 
 def test_base_bf16_zipf_bwd_sampled(orc):
     inp = pkm_inputs.make("base-bf16-zipf-bwd")
-    sub = pkm_inputs.token_subset(inp["w"].T, 192, seed=8)
+    sub = pkm_inputs.token_subset(inp["w"].T, 1024, seed=8)
     gpu_util.run_parity(orc, inp, inp["w"].k, subset=sub, backward=True, tight=TIGHT["bf16"])
 
 
@@ -69,7 +69,7 @@ def test_base_bf16_zipf_bwd_invariants():
 @pytest.mark.slow
 def test_large_bf16_zipf_bwd_sampled(orc):
     inp = pkm_inputs.make("large-bf16-zipf-bwd")
-    sub = pkm_inputs.token_subset(inp["w"].T, 48, seed=9)
+    sub = pkm_inputs.token_subset(inp["w"].T, 256, seed=9)
     gpu_util.run_parity(orc, inp, inp["w"].k, subset=sub, backward=True, tight=TIGHT["bf16"])
 
 
@@ -146,6 +146,24 @@ def test_edge_two_kernel_selection(orc, case):
         _, idx, _, _ = pk.pkm_forward(q, keys, values, k)
         ref = orc.forward(inp["q"], inp["keys"], inp["values"], k)
         assert np.array_equal(gpu_util.to_host(idx), ref["idx"]), "exact-arithmetic order differs"
+
+
+# T not a multiple of 64 leaves tokens past T in the last workgroup; those
+# lanes score token 0's query.  With token 0's query zero, every sub-key ties
+# (more than 64 survivors in both halves): the lanes past T must keep nothing,
+# also in waves whose live tokens need no bisection and in waves with no live
+# token at all, and must not disturb the live tokens' survivors.
+TAIL_CASES = [(65, 512), (100, 512), (112, 512), (100, 1024)]
+
+
+@pytest.mark.parametrize("T,n", TAIL_CASES, ids=[f"T{c[0]}n{c[1]}" for c in TAIL_CASES])
+def test_two_kernel_selection_tail_tokens_with_tied_token0(orc, T, n):
+    from product_key_memory_amd import _lib
+    assert _lib.workspace_bytes(_lib.Problem(T, 2, n, 32, 512, 16, _lib.PKM_BF16), False) > 0
+    inp = pkm_inputs.custom(T, 2, n, 32, 512, 16, dtype="bf16", seed=T + n)
+    inp["q"][0] = 0          # bfloat16 +0: every score of token 0 is exactly 0
+    rep = gpu_util.run_parity(orc, inp, 32, tight=TIGHT["bf16"])
+    assert rep["rows"] == T * 2
 
 
 def test_k1_is_the_row_itself(orc):

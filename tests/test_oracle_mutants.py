@@ -60,6 +60,19 @@ MUTANTS = [
     ("dq from the other codebook",
      "acc += g[i] * elem(keys, k_dt, (((int64_t)h * 2 + s) * n + i) * half + c);",
      "acc += g[i] * elem(keys, k_dt, (((int64_t)h * 2 + (1 - s)) * n + i) * half + c);"),
+    ("given selection: slot decoded with the halves swapped",
+     "scores[base + r] = half_score(t, h, 0, f / n, H, n, d_k, q, q_dt, keys, k_dt) +\n"
+     "                                   half_score(t, h, 1, f % n, H, n, d_k, q, q_dt, keys, k_dt);",
+     "scores[base + r] = half_score(t, h, 0, f % n, H, n, d_k, q, q_dt, keys, k_dt) +\n"
+     "                                   half_score(t, h, 1, f / n, H, n, d_k, q, q_dt, keys, k_dt);"),
+    ("given selection: right half dropped",
+     "scores[base + r] = half_score(t, h, 0, f / n, H, n, d_k, q, q_dt, keys, k_dt) +\n"
+     "                                   half_score(t, h, 1, f % n, H, n, d_k, q, q_dt, keys, k_dt);",
+     "scores[base + r] = half_score(t, h, 0, f / n, H, n, d_k, q, q_dt, keys, k_dt) +\n"
+     "                                   0.0 * half_score(t, h, 1, f % n, H, n, d_k, q, q_dt, keys, k_dt);"),
+    ("given selection: right half scored on the left codebook",
+     "                                   half_score(t, h, 1, f % n, H, n, d_k, q, q_dt, keys, k_dt);",
+     "                                   half_score(t, h, 0, f % n, H, n, d_k, q, q_dt, keys, k_dt);"),
     ("dkeys from the other query half",
      "const int64_t q_off = (t * H + h) * (int64_t)d_k + (int64_t)s * half;\n                for",
      "const int64_t q_off = (t * H + h) * (int64_t)d_k + (int64_t)(1 - s) * half;\n                for"),

@@ -57,18 +57,19 @@ STAGE_KERNELS = {
     "gather": ("fwd_gather_kernel",),
     "slot_sort": ("bucket_hist_kernel", "bucket_colscan_kernel", "bucket_scatter_kernel",
                   "bucket_sort_kernel"),
-    "bwd_values": ("dv_prepare_kernel", "seg_value_kernel"),
+    "bwd_values": ("seg_value_kernel", "slot_finish_kernel"),
     "bwd_queries": ("bwd_query_kernel", "dkeys_mfma_kernel", "dkeys_reduce_kernel"),
 }
 # the value side of pkm_backward_sgd (timed after the step; in the traffic
-# record only): its seg_value instance is the one whose SGD flag is true
-SGD_VALUE_KERNELS = ("split_prepare_kernel", "seg_value_kernel", "split_apply_kernel")
+# record only): the seg_value instance whose SGD flag is true and the
+# slot_finish instance of mode 2
+SGD_VALUE_KERNELS = {"seg_value_kernel": "true>", "slot_finish_kernel": "2>"}
 
 
 def stage_of(short: str):
     """The stage a kernel (name without namespace and arguments) belongs to."""
     base = short.split("<")[0]
-    if base in SGD_VALUE_KERNELS and (base != "seg_value_kernel" or short.endswith("true>")):
+    if base in SGD_VALUE_KERNELS and short.replace(" ", "").endswith(SGD_VALUE_KERNELS[base]):
         return "bwd_values_sgd"
     for stage, prefixes in STAGE_KERNELS.items():
         if base in prefixes:
@@ -486,7 +487,7 @@ def main():
         rc |= _lib.slot_sort(p, P(idx), P(slot_start), P(order), P(ws), ws_bytes, sp)
         mark(3)
         rc |= _lib.backward_values(p, P(values), P(idx), P(wts), P(dy), P(slot_start), P(order),
-                                   P(dvalues), 0, P(dw), sp)      # dvalues overwritten
+                                   P(dvalues), 0, P(dw), P(ws), ws_bytes, sp)   # overwritten
         mark(4)
         rc |= _lib.backward_queries(p, P(q), P(keys), P(idx), P(wts), P(dw), P(dq), P(dkeys),
                                     P(ws), ws_bytes, sp)

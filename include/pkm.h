@@ -129,9 +129,10 @@ pkm_status_t pkm_forward(const pkm_problem_t *p, const void *q, const void *keys
  *                               zeroes it (or keeps an earlier gradient to add
  *                               to); rows no pick selects are left untouched.
  *   workspace  pkm_workspace_bytes(p, 1) bytes (NULL allowed when that is 0)
- * The order in which float32 partial sums of one slot meet (slot sort,
- * atomics on rows shared by several waves) varies from run to run, so
- * dvalues varies at the rounding level.
+ * Results are the same bits on every run: the picks of one slot meet in
+ * ascending pick id (t*H*k + h*k + r), the pieces of a slot picked more
+ * often than one wave's share are added in a fixed order, and no float
+ * atomics are used anywhere in the backward.
  */
 pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *keys,
                           const void *values, const int32_t *idx, const float *weights,
@@ -142,7 +143,7 @@ pkm_status_t pkm_backward(const pkm_problem_t *p, const void *q, const void *key
  * dvalues is written, rows no pick selects become 0, and the old contents are
  * never read (the mode of an optimizer that consumes a fresh gradient; it
  * spares reading the n*n x d_v float32 array).  Same arguments, same
- * workspace as pkm_backward. */
+ * workspace and the same run-to-run identical results as pkm_backward. */
 pkm_status_t pkm_backward_overwrite(const pkm_problem_t *p, const void *q, const void *keys,
                                     const void *values, const int32_t *idx, const float *weights,
                                     const void *dy, float *dq, float *dkeys, float *dvalues,
@@ -175,10 +176,11 @@ pkm_status_t pkm_backward_sgd(const pkm_problem_t *p, const void *q, const void 
  * The two passes above, stage by stage, for callers that keep the
  * intermediate results or time the stages: pkm_forward is
  * pkm_forward_select followed by pkm_forward_gather; pkm_backward is
- * pkm_slot_sort, pkm_backward_values and pkm_backward_queries.  Same
+ * pkm_slot_sort, pkm_backward_values and pkm_backward_queries (dvalues
+ * accumulated, or overwritten for pkm_backward_overwrite).  Same
  * conventions, same array layouts as above.  A workspace of
- * pkm_workspace_bytes(p, 1) bytes serves pkm_slot_sort and
- * pkm_backward_queries.
+ * pkm_workspace_bytes(p, 1) bytes serves pkm_slot_sort, pkm_backward_values
+ * and pkm_backward_queries.
  */
 
 /* Steps 1-5 of pkm_forward: the selection and its softmax weights
@@ -199,20 +201,25 @@ pkm_status_t pkm_forward_gather(const pkm_problem_t *p, const void *values, cons
  * update (gptget.net summary, "Methodology": only a few memory slots are
  * updated).
  *   slot_start  [n*n + 1]  int32 OUT;  order  [T*H*k]  int32 OUT
- * The order of picks inside one slot is unspecified. */
+ * The picks of one slot are in ascending pick id: the result is unique. */
 pkm_status_t pkm_slot_sort(const pkm_problem_t *p, const int32_t *idx, int32_t *slot_start,
                            int32_t *order, void *workspace, size_t workspace_bytes, void *stream);
 
 /* The value side of pkm_backward over the slot-sorted picks: dw [T][H][k]
  * float32 (OUT, overwritten), dw = <dy[t], values[f]>, and the sparse update
- * dvalues[f] += w * dy[t] (accumulated or overwritten, as in pkm_backward).
- * Each value row is read once per run of picks and most rows of dvalues are
- * written without atomics.  slot_start and order come from pkm_slot_sort on
- * the same idx. */
+ * dvalues[f] += w * dy[t] (dvalues_accumulate != 0: accumulated, as in
+ * pkm_backward; 0: overwritten, as in pkm_backward_overwrite).  Each value
+ * row is read once per run of picks; the picks of a slot are summed in the
+ * order of `order`, a slot picked more often than one wave's share in
+ * pieces whose sums meet in a fixed order (through the workspace), so the
+ * result is the same on every run.  slot_start and order come from
+ * pkm_slot_sort on the same idx.  workspace: pkm_workspace_bytes(p, 1)
+ * bytes. */
 pkm_status_t pkm_backward_values(const pkm_problem_t *p, const void *values, const int32_t *idx,
                                  const float *weights, const void *dy, const int32_t *slot_start,
                                  const int32_t *order, float *dvalues, int dvalues_accumulate,
-                                 float *dw, void *stream);
+                                 float *dw, void *workspace, size_t workspace_bytes,
+                                 void *stream);
 
 /* The query side of pkm_backward, from weights and dw: the softmax backward,
  * then dq and dkeys (both OUT, overwritten).  Each pick's ds reaches its left

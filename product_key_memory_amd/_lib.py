@@ -81,7 +81,7 @@ def lib() -> ctypes.CDLL:
         L.pkm_forward_select.argtypes = [PP, P, P, P, P, P, P, c_size, P]
         L.pkm_forward_gather.argtypes = [PP, P, P, P, P, P]
         L.pkm_slot_sort.argtypes = [PP, P, P, P, P, c_size, P]
-        L.pkm_backward_values.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_int, P, P]
+        L.pkm_backward_values.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_int, P, P, c_size, P]
         L.pkm_backward_queries.argtypes = [PP, P, P, P, P, P, P, P, P, c_size, P]
         F, I64 = ctypes.c_float, ctypes.c_int64
         L.pkm_sparse_sgd.argtypes = [PP, P, P, P, F, P]
@@ -151,9 +151,9 @@ def slot_sort(p: Problem, idx, slot_start, order, ws, ws_bytes, stream) -> int:
 
 
 def backward_values(p: Problem, values, idx, weights, dy, slot_start, order, dvalues,
-                    accumulate, dw, stream) -> int:
+                    accumulate, dw, ws, ws_bytes, stream) -> int:
     return lib().pkm_backward_values(ctypes.byref(p), values, idx, weights, dy, slot_start, order,
-                                     dvalues, int(accumulate), dw, stream)
+                                     dvalues, int(accumulate), dw, ws, ws_bytes, stream)
 
 
 def backward_queries(p: Problem, q, keys, idx, weights, dw, dq, dkeys, ws, ws_bytes,

@@ -46,28 +46,29 @@ pkm_status_t check_problem(const pkm_problem_t *p, bool backward)
 size_t picks_bytes(const pkm_problem_t *p) { return pkm::align256((size_t)(p->T * p->H * p->k) * 4); }
 size_t starts_bytes(const pkm_problem_t *p) { return pkm::align256(((size_t)p->n * p->n + 1) * 4); }
 
+// What one stage of the backward needs beside its arrays: the slot sort's
+// scratch, the value side's piece rows (the sums of the runs longer than one
+// wave's share), the query side's scratch.  The stages run one after the
+// other, so in pkm_backward they share one region.
+size_t split_bytes(const pkm_problem_t *p)
+{
+    return pkm::split_rows_bytes(p->T * p->H * p->k, p->d_v);
+}
 size_t stage_scratch_bytes(const pkm_problem_t *p)
 {
     const size_t v = pkm::slot_sort_scratch(p->T * p->H * p->k, p->n).total;
     const size_t q = pkm::bwd_query_scratch(p->T, p->H, p->n, p->k, p->d_k).total;
-    return v > q ? v : q;
+    const size_t s = split_bytes(p);
+    return v > q ? (v > s ? v : s) : (q > s ? q : s);
 }
 
-// pkm_backward: dw, slot_start, order, then the stages' scratch.
+// pkm_backward, pkm_backward_overwrite and pkm_backward_sgd: dw, slot_start,
+// order, then the stages' scratch.
 size_t backward_bytes(const pkm_problem_t *p)
 {
     return picks_bytes(p) + starts_bytes(p) + picks_bytes(p) + stage_scratch_bytes(p);
 }
-
-// pkm_backward_sgd: the same head; the stages' scratch also holds the sums
-// of the long runs while the value side runs (slot sort before, query side
-// after: the three never overlap).
-size_t backward_sgd_bytes(const pkm_problem_t *p)
-{
-    const size_t split = pkm::split_rows_bytes(p->T * p->H * p->k, p->d_v);
-    const size_t stage = stage_scratch_bytes(p);
-    return picks_bytes(p) + starts_bytes(p) + picks_bytes(p) + (stage > split ? stage : split);
-}
+size_t backward_sgd_bytes(const pkm_problem_t *p) { return backward_bytes(p); }
 
 size_t forward_bytes(const pkm_problem_t *p)
 {
@@ -191,7 +192,7 @@ pkm_status_t pkm_slot_sort(const pkm_problem_t *p, const int32_t *idx, int32_t *
 pkm_status_t pkm_backward_values(const pkm_problem_t *p, const void *values, const int32_t *idx,
                                  const float *weights, const void *dy, const int32_t *slot_start,
                                  const int32_t *order, float *dvalues, int dvalues_accumulate,
-                                 float *dw, void *stream)
+                                 float *dw, void *workspace, size_t workspace_bytes, void *stream)
 {
     pkm_status_t st = check_problem(p, true);
     if (st != PKM_OK)
@@ -203,6 +204,9 @@ pkm_status_t pkm_backward_values(const pkm_problem_t *p, const void *values, con
     if (!aligned16(values) || !aligned16(idx) || !aligned16(weights) || !aligned16(dy) ||
         !aligned16(slot_start) || !aligned16(order) || !aligned16(dvalues) || !aligned16(dw))
         return PKM_ERR_ALIGN;
+    st = check_workspace(p, workspace, workspace_bytes, split_bytes(p));
+    if (st != PKM_OK)
+        return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (T == 0)      // no picks: overwrite leaves an all-zero gradient
         return dvalues_accumulate || pkm::launch_zero_f32(dvalues, (int64_t)p->n * p->n * p->d_v,
@@ -210,8 +214,8 @@ pkm_status_t pkm_backward_values(const pkm_problem_t *p, const void *values, con
                    ? PKM_OK
                    : PKM_ERR_HIP;
     return pkm::launch_bwd_value(p->dtype, values, idx, weights, dy, slot_start, order, dvalues,
-                                 dvalues_accumulate, dw, p->T, p->H, p->n, p->k, p->d_v,
-                                 s) == hipSuccess
+                                 dvalues_accumulate, static_cast<float *>(workspace), dw, p->T,
+                                 p->H, p->n, p->k, p->d_v, s) == hipSuccess
                ? PKM_OK
                : PKM_ERR_HIP;
 }
@@ -283,7 +287,7 @@ pkm_status_t backward_impl(const pkm_problem_t *p, const void *q, const void *ke
             return st;
     }
     st = pkm_backward_values(p, values, idx, weights, dy, slot_start, order, dvalues, accumulate,
-                             dw, stream);
+                             dw, scratch, scratch_bytes, stream);
     if (st != PKM_OK)
         return st;
     return pkm_backward_queries(p, q, keys, idx, weights, dw, dq, dkeys, scratch, scratch_bytes,

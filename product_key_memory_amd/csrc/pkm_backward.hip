@@ -128,18 +128,57 @@ __global__ __launch_bounds__(kColWaves *kWave) void bucket_colscan_kernel(
     }
 }
 
+// The stable placement both levels share.  A workgroup takes its picks in
+// rounds of kL1Threads consecutive ones (thread t: the t-th of the round); a
+// pick's place is cur[key] + (picks of the round before it with the same
+// key) -- those in earlier waves, counted through tab, plus those in lower
+// lanes of its own wave, found by wave_match -- so picks with equal keys keep
+// their order.  tab[w][key] = (round << 8) | (the picks of wave w with that
+// key in this round), valid only while its round tag is the current one.
+// The lowest wave holding a key advances cur[key] after everyone has read it.
+constexpr int kSortWaves = kL1Threads / kWave;
+static_assert(kL2Threads == kL1Threads, "one placement routine for both levels");
+
+template <int KEYS>
+__device__ __forceinline__ void stable_round(uint32_t key, bool valid, int bits, int round,
+                                             int32_t *cur, uint32_t (*tab)[KEYS], int &pos)
+{
+    const int w = threadIdx.x / kWave;
+    const uint64_t peers = wave_match(key, valid, bits);
+    const int rank = __popcll(peers & lanes_below());
+    const uint32_t tag = (uint32_t)round << 8;
+    if (valid && rank == 0)
+        tab[w][key] = tag | (uint32_t)__popcll(peers);
+    __syncthreads();
+    int before = 0, all = 0;
+    if (valid) {
+#pragma unroll
+        for (int u = 0; u < kSortWaves; ++u) {
+            const uint32_t e = tab[u][key];
+            const int c = (e & ~0xFFu) == tag ? (int)(e & 0xFFu) : 0;
+            before += u < w ? c : 0;
+            all += c;
+        }
+        pos = cur[key] + before + rank;
+    }
+    __syncthreads();
+    if (valid && rank == 0 && before == 0)
+        cur[key] += all;
+}
+
 // Level-1 scatter: bucket_base = exclusive scan of total (block 0 stores it,
 // nb + 1 entries), then every pick of the chunk goes to
 // pairs[base[bucket] + bhist[block][bucket] + rank in block] as
-// (pick id, slot & (2^shift - 1)).
+// (pick id, slot & (2^shift - 1)), in pick order within each bucket.
 __global__ __launch_bounds__(kL1Threads) void bucket_scatter_kernel(
-    const int32_t *__restrict__ idx, int64_t picks, int64_t chunk, int shift, int nb,
+    const int32_t *__restrict__ idx, int64_t picks, int64_t chunk, int shift, int nb, int nb_bits,
     const int32_t *__restrict__ bhist, const int32_t *__restrict__ total,
     int32_t *__restrict__ bucket_base, int2 *__restrict__ pairs)
 {
     constexpr int PER = kMaxBuckets / kL1Threads;
     constexpr int W = kL1Threads / kWave;
     __shared__ int32_t cur[kMaxBuckets];
+    __shared__ uint32_t tab[kSortWaves][kMaxBuckets];
     __shared__ int32_t wsum[W];
     const int lane = lane_id(), w = threadIdx.x / kWave;
     // thread t owns buckets [PER t, PER t + PER)
@@ -155,6 +194,8 @@ __global__ __launch_bounds__(kL1Threads) void bucket_scatter_kernel(
     const int excl = wave_exclusive_scan(local, &tw);
     if (lane == 0)
         wsum[w] = tw;
+    for (int e = threadIdx.x; e < kSortWaves * kMaxBuckets; e += kL1Threads)
+        (&tab[0][0])[e] = 0xFFFFFFFFu;              // a round tag no round has
     __syncthreads();
     int run = excl;
     for (int u = 0; u < w; ++u)
@@ -176,19 +217,15 @@ __global__ __launch_bounds__(kL1Threads) void bucket_scatter_kernel(
     const int32_t lowmask = (1 << shift) - 1;
     const int64_t p0 = l1_begin(chunk, picks);
     const int64_t p1 = p0 + chunk < picks ? p0 + chunk : picks;
-    for (int64_t q = p0 + threadIdx.x; q < p1; q += kL1Threads * kL2Unroll) {
-        int32_t f[kL2Unroll];
-#pragma unroll
-        for (int u = 0; u < kL2Unroll; ++u) {
-            const int64_t p = q + (int64_t)u * kL1Threads;
-            f[u] = p < p1 ? idx[p] : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < kL2Unroll; ++u)
-            if (f[u] >= 0) {
-                const int pos = atomicAdd(&cur[f[u] >> shift], 1);
-                pairs[pos] = make_int2((int32_t)(q + (int64_t)u * kL1Threads), f[u] & lowmask);
-            }
+    int round = 0;
+    for (int64_t q = p0; q < p1; q += kL1Threads, ++round) {
+        const int64_t p = q + threadIdx.x;
+        const bool valid = p < p1;
+        const int32_t f = valid ? idx[p] : 0;
+        int pos = 0;
+        stable_round((uint32_t)(f >> shift), valid, nb_bits, round, cur, tab, pos);
+        if (valid)
+            pairs[pos] = make_int2((int32_t)p, f & lowmask);
     }
 }
 
@@ -199,7 +236,8 @@ __global__ __launch_bounds__(kL2Threads) void bucket_sort_kernel(
     int64_t slots, int32_t *__restrict__ slot_start, int32_t *__restrict__ order)
 {
     constexpr int W = kL2Threads / kWave;
-    __shared__ int32_t h[kMaxBucketSlots];
+    __shared__ int32_t h[kMaxBucketSlots];      // counts, then the cursors of the bins
+    __shared__ uint32_t tab[kSortWaves][kMaxBucketSlots];
     __shared__ int32_t wsum[W];
     const int B = 1 << shift;
     const int64_t f0 = (int64_t)blockIdx.x << shift;
@@ -252,104 +290,121 @@ __global__ __launch_bounds__(kL2Threads) void bucket_sort_kernel(
     }
     if (f0 + B >= slots && threadIdx.x == 0)
         slot_start[slots] = end;
+    for (int e = threadIdx.x; e < kSortWaves * kMaxBucketSlots; e += kL2Threads)
+        (&tab[0][0])[e] = 0xFFFFFFFFu;
     __syncthreads();
-    for (int64_t q = beg + (int)threadIdx.x; q < end; q += kL2Threads * kL2Unroll) {
-        int2 pr[kL2Unroll];
-#pragma unroll
-        for (int u = 0; u < kL2Unroll; ++u) {
-            const int64_t p = q + (int64_t)u * kL2Threads;
-            pr[u] = p < end ? pairs[p] : make_int2(0, -1);
-        }
-#pragma unroll
-        for (int u = 0; u < kL2Unroll; ++u)
-            if (pr[u].y >= 0)
-                order[atomicAdd(&h[pr[u].y], 1)] = pr[u].x;
+    // the bucket's pairs arrive in pick order (level 1 is stable); placing
+    // them stably leaves each slot's picks in ascending pick order
+    int round = 0;
+    for (int64_t q = beg; q < end; q += kL2Threads, ++round) {
+        const int64_t p = q + threadIdx.x;
+        const bool valid = p < end;
+        const int2 pr = valid ? pairs[p] : make_int2(0, 0);
+        int pos = 0;
+        stable_round((uint32_t)pr.y, valid, shift, round, h, tab, pos);
+        if (valid)
+            order[pos] = pr.x;
     }
 }
 
-// Overwrite mode: zero the dvalues rows no wave will write whole -- rows no
-// pick selected, and rows with a run of more than `chunk` sorted picks
-// (several waves add into those with atomics).  Each wave checks 64 slots,
-// one per lane, then zeroes the rows found, all lanes on one row at a time.
-__global__ void dv_prepare_kernel(const int32_t *__restrict__ start, int64_t slots, int d_v,
-                                  int chunk, float *__restrict__ dvalues)
+// Pieces of the long runs.  A run of more than `chunk` sorted picks is cut at
+// the nominal chunk bounds; the wave holding a piece stores the piece's sum
+// (no atomics) in row 2 (a >> shift) + (a is not a chunk bound) of `split`,
+// a = the piece's first position in the sorted order.  A run's first piece
+// starts at its own start, every later one at a chunk bound, so no two
+// pieces of one batch share a row (a chunk holds at most the last piece of
+// one long run and the first piece of the next, told apart by the + 1).
+__device__ __forceinline__ int64_t piece_row(int64_t a, int shift)
 {
-    const int lane = lane_id();
-    const int64_t f0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * kWave;
-    if (f0 >= slots)
-        return;
-    const int64_t f = f0 + lane;
-    bool zero = false;
-    if (f < slots) {
-        const int64_t b = start[f], e = start[f + 1];
-        zero = b == e || e - b > chunk;
-    }
-    uint64_t todo = __ballot(zero);
-    while (todo) {
-        const int i = __builtin_ctzll(todo);
-        todo &= todo - 1;
-        float4 *row = reinterpret_cast<float4 *>(dvalues + (f0 + i) * d_v);
-        for (int c = lane; c < d_v / 4; c += kWave)
-            row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    return 2 * (a >> shift) + ((a & (((int64_t)1 << shift) - 1)) != 0 ? 1 : 0);
 }
 
-// The fused SGD: zero the split_acc rows of the runs longer than the chunk
-// of 2^shift picks (row start[f] >> shift), before the segmented reduction
-// adds into them.
-__global__ void split_prepare_kernel(const int32_t *__restrict__ start, int64_t slots, int d_v,
-                                     int shift, float *__restrict__ split_acc)
-{
-    const int lane = lane_id();
-    const int64_t f0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * kWave;
-    if (f0 >= slots)
-        return;
-    const int64_t f = f0 + lane;
-    const bool split = f < slots && start[f + 1] - start[f] > (1 << shift);
-    uint64_t todo = __ballot(split);
-    while (todo) {
-        const int i = __builtin_ctzll(todo);
-        todo &= todo - 1;
-        float4 *row = reinterpret_cast<float4 *>(split_acc + (int64_t)(start[f0 + i] >> shift) * d_v);
-        for (int c = lane; c < d_v / 4; c += kWave)
-            row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-}
-
-// ... and afterwards apply those sums: w = fmaf(-lr, g, w), rounded once.
-template <typename DT>
-__global__ void split_apply_kernel(const int32_t *__restrict__ start, int64_t slots, int d_v,
-                                   int shift, const float *__restrict__ split_acc,
-                                   DT *__restrict__ values, float lr)
+// After the segmented reduction, one pass over the slots (each wave checks
+// 64 slots, one per lane, then serves the rows found, all lanes on one row):
+//   - MODE 0 (overwrite): rows no pick selected become 0;
+//   - every long run's pieces are summed in the order of their positions --
+//     a fixed order, so the result does not depend on which wave ran first
+//     -- and the sum g is stored (MODE 0), added to dvalues (MODE 1), or
+//     applied to the value row, w = fmaf(-lr, g, w) rounded once to the
+//     storage type (MODE 2, the fused SGD; the rows were only read until now).
+template <typename DT, int MODE>
+__global__ void slot_finish_kernel(const int32_t *__restrict__ start, int64_t slots, int d_v,
+                                   int shift, const float *__restrict__ split,
+                                   float *__restrict__ dvalues, DT *__restrict__ values, float lr)
 {
     constexpr int EPC = Elt<DT>::per16;
     const int lane = lane_id();
+    const int64_t chunk = (int64_t)1 << shift;
     const int64_t f0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * kWave;
     if (f0 >= slots)
         return;
     const int64_t f = f0 + lane;
-    const bool split = f < slots && start[f + 1] - start[f] > (1 << shift);
-    uint64_t todo = __ballot(split);
+    bool todo_lane = false;
+    if (f < slots) {
+        const int64_t b = start[f], e = start[f + 1];
+        todo_lane = e - b > chunk || (MODE == 0 && b == e);
+    }
+    uint64_t todo = __ballot(todo_lane);
     while (todo) {
         const int i = __builtin_ctzll(todo);
         todo &= todo - 1;
-        const float *g = split_acc + (int64_t)(start[f0 + i] >> shift) * d_v;
-        DT *row = values + (f0 + i) * d_v;
+        const int64_t fr = f0 + i;
+        const int64_t b = start[fr], e = start[fr + 1];
+        if (b == e) {                                   // overwrite mode, untouched row
+            float4 *row = reinterpret_cast<float4 *>(dvalues + fr * d_v);
+            for (int c = lane; c < d_v / 4; c += kWave)
+                row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+            continue;
+        }
+        const int64_t cb = b >> shift, ce = (e - 1) >> shift;
+        const int64_t r0 = piece_row(b, shift);
         for (int c = lane; c < d_v / EPC; c += kWave) {
-            float w[EPC];
-            unpack16(*reinterpret_cast<const uint4 *>(row + (int64_t)c * EPC), w);
+            float g[EPC];
 #pragma unroll
-            for (int e = 0; e < EPC; ++e)
-                w[e] = fmaf(-lr, g[c * EPC + e], w[e]);
-            if constexpr (sizeof(DT) == 2) {
-                uint4 r;
-                r.x = f32_to_bf16_bits(w[0]) | (f32_to_bf16_bits(w[1]) << 16);
-                r.y = f32_to_bf16_bits(w[2]) | (f32_to_bf16_bits(w[3]) << 16);
-                r.z = f32_to_bf16_bits(w[4]) | (f32_to_bf16_bits(w[5]) << 16);
-                r.w = f32_to_bf16_bits(w[6]) | (f32_to_bf16_bits(w[7]) << 16);
-                *reinterpret_cast<uint4 *>(row + (int64_t)c * EPC) = r;
+            for (int x = 0; x < EPC; ++x)
+                g[x] = 0.f;
+            for (int64_t cc = cb; cc <= ce; ++cc) {
+                const float *src = split + (cc == cb ? r0 : 2 * cc) * d_v + (int64_t)c * EPC;
+#pragma unroll
+                for (int x = 0; x < EPC; x += 4) {
+                    const float4 v = *reinterpret_cast<const float4 *>(src + x);
+                    g[x] += v.x;
+                    g[x + 1] += v.y;
+                    g[x + 2] += v.z;
+                    g[x + 3] += v.w;
+                }
+            }
+            if constexpr (MODE == 2) {
+                DT *dst = values + fr * d_v + (int64_t)c * EPC;
+                float w[EPC];
+                unpack16(*reinterpret_cast<const uint4 *>(dst), w);
+#pragma unroll
+                for (int x = 0; x < EPC; ++x)
+                    w[x] = fmaf(-lr, g[x], w[x]);
+                if constexpr (sizeof(DT) == 2) {
+                    uint4 r;
+                    r.x = f32_to_bf16_bits(w[0]) | (f32_to_bf16_bits(w[1]) << 16);
+                    r.y = f32_to_bf16_bits(w[2]) | (f32_to_bf16_bits(w[3]) << 16);
+                    r.z = f32_to_bf16_bits(w[4]) | (f32_to_bf16_bits(w[5]) << 16);
+                    r.w = f32_to_bf16_bits(w[6]) | (f32_to_bf16_bits(w[7]) << 16);
+                    *reinterpret_cast<uint4 *>(dst) = r;
+                } else {
+                    *reinterpret_cast<float4 *>(dst) = make_float4(w[0], w[1], w[2], w[3]);
+                }
             } else {
-                *reinterpret_cast<float4 *>(row + (int64_t)c * EPC) = make_float4(w[0], w[1], w[2], w[3]);
+                float *dst = dvalues + fr * d_v + (int64_t)c * EPC;
+#pragma unroll
+                for (int x = 0; x < EPC; x += 4) {
+                    float4 o = make_float4(g[x], g[x + 1], g[x + 2], g[x + 3]);
+                    if (MODE == 1) {
+                        const float4 old = *reinterpret_cast<const float4 *>(dst + x);
+                        o.x += old.x;
+                        o.y += old.y;
+                        o.z += old.z;
+                        o.w += old.w;
+                    }
+                    *reinterpret_cast<float4 *>(dst + x) = o;
+                }
             }
         }
     }
@@ -409,34 +464,30 @@ __device__ __forceinline__ void seg_load_row(uint4 (&v)[MCH], const DT *__restri
 
 template <int MCH, int EPC>
 __device__ __forceinline__ void seg_flush(float (&acc)[MCH][EPC], float *__restrict__ dvalues,
-                                          int64_t f, int d_v, int nchunks, int lane,
-                                          bool exclusive, int accumulate)
+                                          float *__restrict__ piece, int64_t f, int d_v,
+                                          int nchunks, int lane, bool exclusive, int accumulate)
 {
-    float *drow = dvalues + f * d_v;
+    // a run this wave holds whole goes to its dvalues row; a piece of a long
+    // run to its piece row (summed later, in order, by slot_finish_kernel)
+    float *drow = exclusive ? dvalues + f * d_v : piece;
+    const bool add = exclusive && accumulate;
 #pragma unroll
     for (int m = 0; m < MCH; ++m) {
         const int c = lane + m * kWave;
         if (c < nchunks) {
             float *dst = drow + (int64_t)c * EPC;
-            if (exclusive) {
 #pragma unroll
-                for (int e = 0; e < EPC / 4; ++e) {
-                    float4 o = make_float4(acc[m][4 * e], acc[m][4 * e + 1], acc[m][4 * e + 2],
-                                           acc[m][4 * e + 3]);
-                    if (accumulate) {
-                        const float4 old = *reinterpret_cast<const float4 *>(dst + 4 * e);
-                        o.x += old.x;
-                        o.y += old.y;
-                        o.z += old.z;
-                        o.w += old.w;
-                    }
-                    *reinterpret_cast<float4 *>(dst + 4 * e) = o;
+            for (int e = 0; e < EPC / 4; ++e) {
+                float4 o = make_float4(acc[m][4 * e], acc[m][4 * e + 1], acc[m][4 * e + 2],
+                                       acc[m][4 * e + 3]);
+                if (add) {
+                    const float4 old = *reinterpret_cast<const float4 *>(dst + 4 * e);
+                    o.x += old.x;
+                    o.y += old.y;
+                    o.z += old.z;
+                    o.w += old.w;
                 }
-            } else {
-#pragma unroll
-                for (int e = 0; e < EPC; ++e)
-                    __hip_atomic_fetch_add(dst + e, acc[m][e], __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+                *reinterpret_cast<float4 *>(dst + 4 * e) = o;
             }
         }
 #pragma unroll
@@ -447,44 +498,36 @@ __device__ __forceinline__ void seg_flush(float (&acc)[MCH][EPC], float *__restr
 
 // The fused update: the run's sum g updates its value row in place,
 // w = fmaf(-lr, g, w) rounded once to the storage type (vrow holds the row's
-// old values), when the row is this wave's alone; a long run's pieces add
-// into its row of split_acc (row start[f] >> shift: long runs hold more than
-// 2^shift sorted picks, so their first positions differ in that quotient),
-// applied after the kernel.
+// old values), when the row is this wave's alone; a long run's piece goes to
+// its piece row, applied after the kernel by slot_finish_kernel.
 template <typename DT, int MCH, int EPC>
 __device__ __forceinline__ void seg_flush_sgd(float (&acc)[MCH][EPC], const float (&vrow)[MCH][EPC],
-                                              DT *values, float *__restrict__ split_acc,
-                                              const int32_t *__restrict__ start, int64_t f,
+                                              DT *values, float *__restrict__ piece, int64_t f,
                                               int d_v, int nchunks, int lane, bool exclusive,
-                                              float lr, int shift)
+                                              float lr)
 {
-    const int64_t srow = exclusive ? 0 : (int64_t)(start[f] >> shift);
+    if (!exclusive) {
+        seg_flush<MCH, EPC>(acc, nullptr, piece, f, d_v, nchunks, lane, false, 0);
+        return;
+    }
 #pragma unroll
     for (int m = 0; m < MCH; ++m) {
         const int c = lane + m * kWave;
         if (c < nchunks) {
-            if (exclusive) {
-                float w[EPC];
+            float w[EPC];
 #pragma unroll
-                for (int e = 0; e < EPC; ++e)
-                    w[e] = fmaf(-lr, acc[m][e], vrow[m][e]);
-                DT *dst = values + f * d_v + (int64_t)c * EPC;
-                if constexpr (sizeof(DT) == 2) {
-                    uint4 r;
-                    r.x = f32_to_bf16_bits(w[0]) | (f32_to_bf16_bits(w[1]) << 16);
-                    r.y = f32_to_bf16_bits(w[2]) | (f32_to_bf16_bits(w[3]) << 16);
-                    r.z = f32_to_bf16_bits(w[4]) | (f32_to_bf16_bits(w[5]) << 16);
-                    r.w = f32_to_bf16_bits(w[6]) | (f32_to_bf16_bits(w[7]) << 16);
-                    *reinterpret_cast<uint4 *>(dst) = r;
-                } else {
-                    *reinterpret_cast<float4 *>(dst) = make_float4(w[0], w[1], w[2], w[3]);
-                }
+            for (int e = 0; e < EPC; ++e)
+                w[e] = fmaf(-lr, acc[m][e], vrow[m][e]);
+            DT *dst = values + f * d_v + (int64_t)c * EPC;
+            if constexpr (sizeof(DT) == 2) {
+                uint4 r;
+                r.x = f32_to_bf16_bits(w[0]) | (f32_to_bf16_bits(w[1]) << 16);
+                r.y = f32_to_bf16_bits(w[2]) | (f32_to_bf16_bits(w[3]) << 16);
+                r.z = f32_to_bf16_bits(w[4]) | (f32_to_bf16_bits(w[5]) << 16);
+                r.w = f32_to_bf16_bits(w[6]) | (f32_to_bf16_bits(w[7]) << 16);
+                *reinterpret_cast<uint4 *>(dst) = r;
             } else {
-                float *dst = split_acc + srow * d_v + (int64_t)c * EPC;
-#pragma unroll
-                for (int e = 0; e < EPC; ++e)
-                    __hip_atomic_fetch_add(dst + e, acc[m][e], __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+                *reinterpret_cast<float4 *>(dst) = make_float4(w[0], w[1], w[2], w[3]);
             }
         }
 #pragma unroll
@@ -494,7 +537,7 @@ __device__ __forceinline__ void seg_flush_sgd(float (&acc)[MCH][EPC], const floa
 }
 
 // SGD: the value rows are updated in place (values is then written, and
-// dvalues is split_acc, see seg_flush_sgd); dw is the same in every mode.
+// dvalues is unused, see seg_flush_sgd); dw is the same in every mode.
 template <typename DT, bool SGD>
 using ValuesPtr = typename std::conditional<SGD, DT *, const DT *>::type;
 
@@ -502,8 +545,8 @@ template <typename DT, int MCH, int U, bool SGD>
 __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
     ValuesPtr<DT, SGD> values, const DT *__restrict__ dy, const int32_t *__restrict__ idx,
     const float *__restrict__ weights, const int32_t *__restrict__ order,
-    const int32_t *__restrict__ start, float *__restrict__ dvalues, float *__restrict__ dw,
-    int64_t picks, int HK, int d_v, int accumulate, float lr, int shift)
+    const int32_t *__restrict__ start, float *__restrict__ dvalues, float *__restrict__ split,
+    float *__restrict__ dw, int64_t picks, int HK, int d_v, int accumulate, float lr, int shift)
 {
     const int chunk = 1 << shift;
     constexpr int EPC = Elt<DT>::per16;
@@ -585,13 +628,19 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
     int seg = 0;
     int seg_end = __builtin_amdgcn_readfirstlane(segs[1]);
     int f_cur = f_first;
-    // the current run's sum leaves: stored, added, or (SGD) applied to its row
+    // the current run's sum leaves: stored, added, or (SGD) applied to its
+    // row; a piece of a long run goes to its piece row
     auto flush = [&](bool exclusive) {
+        float *piece = nullptr;
+        if (!exclusive)
+            piece = split + piece_row(p_begin + __builtin_amdgcn_readfirstlane(segs[seg]), shift) *
+                                (int64_t)d_v;
         if constexpr (SGD)
-            seg_flush_sgd<DT, MCH, EPC>(acc, vrow, values, dvalues, start, f_cur,
-                                        d_v, nchunks, lane, exclusive, lr, shift);
+            seg_flush_sgd<DT, MCH, EPC>(acc, vrow, values, piece, f_cur, d_v, nchunks, lane,
+                                        exclusive, lr);
         else
-            seg_flush<MCH, EPC>(acc, dvalues, f_cur, d_v, nchunks, lane, exclusive, accumulate);
+            seg_flush<MCH, EPC>(acc, dvalues, piece, f_cur, d_v, nchunks, lane, exclusive,
+                                accumulate);
     };
 
     auto work = [&](DyGroup<MCH, U> &g, int j) {
@@ -1234,8 +1283,8 @@ static unsigned grid1d(int64_t n, int per)
 template <typename DT, int MCH, int U, bool SGD>
 static hipError_t launch_seg_t(const void *values, const void *dy, const int32_t *idx,
                                const float *weights, const int32_t *order, const int32_t *start,
-                               float *dvalues, float *dw, int64_t picks, int HK, int d_v,
-                               int accumulate, float lr, hipStream_t stream)
+                               float *dvalues, float *split, float *dw, int64_t picks, int HK,
+                               int d_v, int accumulate, float lr, hipStream_t stream)
 {
     const int shift = seg_shift(picks);
     const int64_t waves = (picks + (1 << shift) - 1) >> shift;
@@ -1244,21 +1293,21 @@ static hipError_t launch_seg_t(const void *values, const void *dy, const int32_t
     const auto vptr = static_cast<ValuesPtr<DT, SGD>>(const_cast<void *>(values));
     hipLaunchKernelGGL((seg_value_kernel<DT, MCH, U, SGD>), dim3(grid1d(waves, kSegWaves)),
                        dim3(kSegWaves * kWave), 0, stream, vptr,
-                       static_cast<const DT *>(dy), idx, weights, order, start, dvalues, dw, picks,
-                       HK, d_v, accumulate, lr, shift);
+                       static_cast<const DT *>(dy), idx, weights, order, start, dvalues, split,
+                       dw, picks, HK, d_v, accumulate, lr, shift);
     return hipGetLastError();
 }
 
 template <typename DT, bool SGD>
 static hipError_t launch_seg_dt(const void *values, const void *dy, const int32_t *idx,
                                 const float *weights, const int32_t *order, const int32_t *start,
-                                float *dvalues, float *dw, int64_t picks, int HK, int d_v,
-                                int accumulate, float lr, hipStream_t stream)
+                                float *dvalues, float *split, float *dw, int64_t picks, int HK,
+                                int d_v, int accumulate, float lr, hipStream_t stream)
 {
     const int per_lane = (d_v / Elt<DT>::per16 + kWave - 1) / kWave;
 #define PKM_SEG(MCH, U)                                                                        \
-    launch_seg_t<DT, MCH, U, SGD>(values, dy, idx, weights, order, start, dvalues, dw, picks, HK, \
-                                  d_v, accumulate, lr, stream)
+    launch_seg_t<DT, MCH, U, SGD>(values, dy, idx, weights, order, start, dvalues, split, dw,   \
+                                  picks, HK, d_v, accumulate, lr, stream)
     if (per_lane <= 1)
         return PKM_SEG(1, 8);
     if (per_lane <= 2)
@@ -1287,61 +1336,73 @@ hipError_t launch_slot_sort(const int32_t *idx, int64_t picks, int n, int32_t *s
                        picks, S.chunk, S.shift, S.buckets, bhist);
     hipLaunchKernelGGL(bucket_colscan_kernel, dim3(grid1d(S.buckets, kWave)),
                        dim3(kColWaves * kWave), 0, stream, bhist, S.blocks, S.buckets, total);
+    int nb_bits = 0;
+    while ((1 << nb_bits) < S.buckets)
+        ++nb_bits;
     hipLaunchKernelGGL(bucket_scatter_kernel, dim3(S.blocks), dim3(kL1Threads), 0, stream, idx,
-                       picks, S.chunk, S.shift, S.buckets, bhist, total, bucket_base, pairs);
+                       picks, S.chunk, S.shift, S.buckets, nb_bits, bhist, total, bucket_base,
+                       pairs);
     hipLaunchKernelGGL(bucket_sort_kernel, dim3(S.buckets), dim3(kL2Threads), 0, stream, pairs,
                        bucket_base, S.shift, slots, slot_start, order);
     return hipGetLastError();
 }
 
+template <typename DT, int MODE>
+static hipError_t launch_finish(const int32_t *slot_start, int64_t slots, int d_v, int shift,
+                                const float *split, float *dvalues, void *values, float lr,
+                                hipStream_t stream)
+{
+    hipLaunchKernelGGL((slot_finish_kernel<DT, MODE>), dim3(grid1d(slots, 4 * kWave)),
+                       dim3(4 * kWave), 0, stream, slot_start, slots, d_v, shift, split, dvalues,
+                       static_cast<DT *>(values), lr);
+    return hipGetLastError();
+}
+
 hipError_t launch_bwd_value(int dtype, const void *values, const int32_t *idx,
                             const float *weights, const void *dy, const int32_t *slot_start,
-                            const int32_t *order, float *dvalues, int accumulate, float *dw,
-                            int64_t T, int H, int n, int k, int d_v, hipStream_t stream)
+                            const int32_t *order, float *dvalues, int accumulate, float *split,
+                            float *dw, int64_t T, int H, int n, int k, int d_v, hipStream_t stream)
 {
     const int64_t picks = T * H * (int64_t)k;
-    if (!accumulate) {
-        const int64_t slots = (int64_t)n * n;
-        hipLaunchKernelGGL(dv_prepare_kernel, dim3(grid1d(slots, 4 * kWave)), dim3(4 * kWave), 0,
-                           stream, slot_start, slots, d_v, 1 << seg_shift(picks), dvalues);
-        const hipError_t err = hipGetLastError();
-        if (err != hipSuccess)
-            return err;
-    }
-    if (dtype == 1)
-        return launch_seg_dt<bf16_t, false>(values, dy, idx, weights, order, slot_start, dvalues,
-                                            dw, picks, H * k, d_v, accumulate, 0.f, stream);
-    return launch_seg_dt<float, false>(values, dy, idx, weights, order, slot_start, dvalues, dw,
-                                       picks, H * k, d_v, accumulate, 0.f, stream);
+    const int64_t slots = (int64_t)n * n;
+    const int shift = seg_shift(picks);
+    hipError_t err =
+        dtype == 1 ? launch_seg_dt<bf16_t, false>(values, dy, idx, weights, order, slot_start,
+                                                  dvalues, split, dw, picks, H * k, d_v,
+                                                  accumulate, 0.f, stream)
+                   : launch_seg_dt<float, false>(values, dy, idx, weights, order, slot_start,
+                                                 dvalues, split, dw, picks, H * k, d_v,
+                                                 accumulate, 0.f, stream);
+    if (err != hipSuccess)
+        return err;
+    // the storage type does not enter modes 0 and 1 (dvalues is float32)
+    return accumulate ? launch_finish<float, 1>(slot_start, slots, d_v, shift, split, dvalues,
+                                                nullptr, 0.f, stream)
+                      : launch_finish<float, 0>(slot_start, slots, d_v, shift, split, dvalues,
+                                                nullptr, 0.f, stream);
 }
 
 hipError_t launch_bwd_value_sgd(int dtype, void *values, const int32_t *idx, const float *weights,
                                 const void *dy, const int32_t *slot_start, const int32_t *order,
-                                float lr, float *split_acc, float *dw, int64_t T, int H, int n,
-                                int k, int d_v, hipStream_t stream)
+                                float lr, float *split, float *dw, int64_t T, int H, int n, int k,
+                                int d_v, hipStream_t stream)
 {
     const int64_t picks = T * H * (int64_t)k;
     const int64_t slots = (int64_t)n * n;
-    const dim3 grid(grid1d(slots, 4 * kWave)), block(4 * kWave);
     const int shift = seg_shift(picks);
-    hipLaunchKernelGGL(split_prepare_kernel, grid, block, 0, stream, slot_start, slots, d_v, shift,
-                       split_acc);
-    hipError_t err = hipGetLastError();
+    hipError_t err =
+        dtype == 1 ? launch_seg_dt<bf16_t, true>(values, dy, idx, weights, order, slot_start,
+                                                 nullptr, split, dw, picks, H * k, d_v, 0, lr,
+                                                 stream)
+                   : launch_seg_dt<float, true>(values, dy, idx, weights, order, slot_start,
+                                                nullptr, split, dw, picks, H * k, d_v, 0, lr,
+                                                stream);
     if (err != hipSuccess)
         return err;
-    err = dtype == 1 ? launch_seg_dt<bf16_t, true>(values, dy, idx, weights, order, slot_start,
-                                                   split_acc, dw, picks, H * k, d_v, 0, lr, stream)
-                     : launch_seg_dt<float, true>(values, dy, idx, weights, order, slot_start,
-                                                  split_acc, dw, picks, H * k, d_v, 0, lr, stream);
-    if (err != hipSuccess)
-        return err;
-    if (dtype == 1)
-        hipLaunchKernelGGL(split_apply_kernel<bf16_t>, grid, block, 0, stream, slot_start, slots,
-                           d_v, shift, split_acc, static_cast<bf16_t *>(values), lr);
-    else
-        hipLaunchKernelGGL(split_apply_kernel<float>, grid, block, 0, stream, slot_start, slots,
-                           d_v, shift, split_acc, static_cast<float *>(values), lr);
-    return hipGetLastError();
+    return dtype == 1 ? launch_finish<bf16_t, 2>(slot_start, slots, d_v, shift, split, nullptr,
+                                                 values, lr, stream)
+                      : launch_finish<float, 2>(slot_start, slots, d_v, shift, split, nullptr,
+                                                values, lr, stream);
 }
 
 template <typename DT>

@@ -159,6 +159,23 @@ __device__ __forceinline__ int wave_exclusive_scan(int v, int *total)
     return inc - v;
 }
 
+// The lanes of this wave whose `key` equals this lane's (keys < 2^bits; lanes
+// with valid == false match nothing and get 0): one ballot per key bit.
+// `bits` must be the same in every lane.
+__device__ __forceinline__ uint64_t wave_match(uint32_t key, bool valid, int bits)
+{
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < bits; ++b) {
+        const bool on = (key >> b) & 1u;
+        const uint64_t set = __ballot(on);
+        m &= on ? set : ~set;
+    }
+    return valid ? m : 0ull;
+}
+
+// Lanes below this one: bit l set for every lane l < lane_id().
+__device__ __forceinline__ uint64_t lanes_below() { return (1ull << lane_id()) - 1ull; }
+
 // Make this wave's LDS stores visible to its own later LDS loads.
 __device__ __forceinline__ void wave_lds_sync()
 {

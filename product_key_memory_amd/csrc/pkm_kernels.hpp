@@ -64,30 +64,33 @@ hipError_t launch_fwd_gather(int dtype, const void *values, const int32_t *idx,
 
 // Counting sort of the T*H*k picks by slot: slot_start [n*n + 1] (the picks
 // of slot f are order[slot_start[f] .. slot_start[f+1])), order [picks] (pick
-// ids t*H*k + h*k + r).  `scratch` holds
-// slot_sort_scratch(picks, n).total bytes.
+// ids t*H*k + h*k + r, ascending within each slot: both levels place their
+// picks stably).  `scratch` holds slot_sort_scratch(picks, n).total bytes.
 hipError_t launch_slot_sort(const int32_t *idx, int64_t picks, int n, int32_t *slot_start,
                             int32_t *order, void *scratch, hipStream_t stream);
 
 // Value side of the backward over the slot-sorted picks: dw = <dy, values[slot]>
 // per pick and dvalues[slot] (+)= sum w * dy -- accumulated into dvalues when
-// `accumulate`, else dvalues is overwritten (untouched rows become 0).
+// `accumulate`, else dvalues is overwritten (untouched rows become 0).  The
+// runs longer than the reduction's chunk are summed through `split`
+// (split_rows_bytes(...) bytes) in a fixed order: no float atomics, the same
+// bits on every run.
 hipError_t launch_bwd_value(int dtype, const void *values, const int32_t *idx,
                             const float *weights, const void *dy, const int32_t *slot_start,
-                            const int32_t *order, float *dvalues, int accumulate, float *dw,
-                            int64_t T, int H, int n, int k, int d_v, hipStream_t stream);
+                            const int32_t *order, float *dvalues, int accumulate, float *split,
+                            float *dw, int64_t T, int H, int n, int k, int d_v, hipStream_t stream);
 
 // The value side with the SGD step fused in: dw as launch_bwd_value, and every
 // selected value row updated in place, w = fmaf(-lr, g, w) rounded once, with
-// g the row's gradient; no dvalues.  split_acc holds split_rows_bytes(...)
-// bytes (the sums of the runs longer than the reduction's chunk).
+// g the row's gradient; no dvalues.  `split` as for launch_bwd_value.
 hipError_t launch_bwd_value_sgd(int dtype, void *values, const int32_t *idx, const float *weights,
                                 const void *dy, const int32_t *slot_start, const int32_t *order,
-                                float lr, float *split_acc, float *dw, int64_t T, int H, int n,
+                                float lr, float *split, float *dw, int64_t T, int H, int n,
                                 int k, int d_v, hipStream_t stream);
+// Two piece rows of d_v floats per nominal chunk of 2^seg_shift sorted picks.
 inline size_t split_rows_bytes(int64_t picks, int d_v)
 {
-    return (size_t)((picks >> seg_shift(picks)) + 1) * (size_t)d_v * 4;
+    return (size_t)(2 * ((picks >> seg_shift(picks)) + 1)) * (size_t)d_v * 4;
 }
 
 // Query side: softmax backward per distinct sub-key, dq (overwritten) and

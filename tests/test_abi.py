@@ -52,7 +52,10 @@ def test_null_and_alignment():
     assert _lib.forward(P(), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 1
     assert _lib.forward(P(), FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 6
     assert _lib.forward_select(P(), FAKE, FAKE, None, FAKE, None, None, 0, None) == 1
-    assert _lib.backward_values(P(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE + 8, None) == 6
+    assert _lib.backward_values(P(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE + 8, FAKE,
+                                1 << 30, None) == 6
+    assert _lib.backward_values(P(), *[FAKE] * 7, 0, FAKE, None, 1 << 30, None) == 1
+    assert _lib.backward_values(P(), *[FAKE] * 7, 0, FAKE, FAKE, 16, None) == 4
     assert _lib.slot_sort(P(), FAKE, None, FAKE, FAKE, 1 << 30, None) == 1
 
 

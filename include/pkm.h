@@ -21,7 +21,8 @@
  *    is enqueued on it; no call synchronises with the host.
  *  - The library allocates no memory and keeps no state between calls; it is
  *    re-entrant.  Scratch memory comes from the caller's `workspace`, sized by
- *    pkm_workspace_bytes().
+ *    pkm_workspace_bytes() -- except for pkm_backward_noalloc, whose scratch is
+ *    a static device array of the library (see there).
  *  - Arguments are validated completely before anything is enqueued.  On any
  *    error a non-zero status is returned and NOTHING has been enqueued.  A
  *    launch failure reported by the HIP runtime returns PKM_ERR_HIP (work
@@ -56,8 +57,10 @@ typedef enum {
     PKM_ERR_WORKSPACE = 4, /* workspace smaller than pkm_workspace_bytes()       */
     PKM_ERR_HIP = 5,       /* the HIP runtime rejected a launch                  */
     PKM_ERR_ALIGN = 6,     /* an array pointer is not 16-byte aligned            */
-    PKM_ERR_ARG = 7        /* a scalar argument outside its domain (learning
+    PKM_ERR_ARG = 7,       /* a scalar argument outside its domain (learning
                               rate, Adam constants, step)                        */
+    PKM_ERR_TOO_LARGE = 8  /* pkm_backward_noalloc: the problem needs more than
+                              its static scratch holds                           */
 } pkm_status_t;
 
 /* Problem sizes.  32 bytes, no padding: T, then six int32 fields. */
@@ -148,6 +151,25 @@ pkm_status_t pkm_backward_overwrite(const pkm_problem_t *p, const void *q, const
                                     const void *values, const int32_t *idx, const float *weights,
                                     const void *dy, float *dq, float *dkeys, float *dvalues,
                                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pkm_backward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace, the same results bit for bit
+ * (dvalues accumulated).  The scratch memory is a static array of 128 MiB
+ * that the library holds on each GPU it runs on until the process ends (the
+ * benchmark workload, T = 16384, H = 4, n = 512, k = 32, d_v = 1024, needs
+ * 113 MiB); a problem whose pkm_workspace_bytes(p, 1) exceeds it returns
+ * PKM_ERR_TOO_LARGE and enqueues nothing.  The call allocates nothing.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in
+ * time on one GPU (other streams, other threads) race and must not be made;
+ * calls in one stream's order are safe.  Nothing in the array needs to start
+ * at zero, and it keeps whatever the last call left.
+ */
+pkm_status_t pkm_backward_noalloc(const pkm_problem_t *p, const void *q, const void *keys,
+                                  const void *values, const int32_t *idx, const float *weights,
+                                  const void *dy, float *dq, float *dkeys, float *dvalues,
+                                  void *stream);
 
 /*
  * The backward with the sparse SGD step fused in (gptget.net summary,

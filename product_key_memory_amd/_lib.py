@@ -24,11 +24,12 @@ STATUS = {
     5: "PKM_ERR_HIP",
     6: "PKM_ERR_ALIGN",
     7: "PKM_ERR_ARG",
+    8: "PKM_ERR_TOO_LARGE",
 }
 
 # every symbol include/pkm.h declares
 EXPORTS = ("pkm_workspace_bytes", "pkm_forward", "pkm_backward", "pkm_backward_overwrite",
-           "pkm_backward_sgd",
+           "pkm_backward_noalloc", "pkm_backward_sgd",
            "pkm_forward_select",
            "pkm_forward_gather", "pkm_slot_sort", "pkm_backward_values", "pkm_backward_queries",
            "pkm_sparse_sgd", "pkm_sparse_adam", "pkm_slot_usage", "pkm_query_workspace_bytes",
@@ -74,6 +75,8 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P, P,
                                          c_size, P]
             getattr(L, name).restype = ctypes.c_int
+        L.pkm_backward_noalloc.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P, P]
+        L.pkm_backward_noalloc.restype = ctypes.c_int
         L.pkm_backward_sgd.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P,
                                        ctypes.c_float, P, c_size, P]
         L.pkm_backward_sgd.restype = ctypes.c_int
@@ -129,6 +132,13 @@ def backward_overwrite(p: Problem, q, keys, values, idx, weights, dy, dq, dkeys,
     """pkm_backward_overwrite: dvalues overwritten (unselected rows become 0)."""
     return lib().pkm_backward_overwrite(ctypes.byref(p), q, keys, values, idx, weights, dy, dq,
                                         dkeys, dvalues, ws, ws_bytes, stream)
+
+
+def backward_noalloc(p: Problem, q, keys, values, idx, weights, dy, dq, dkeys, dvalues,
+                     stream) -> int:
+    """pkm_backward_noalloc: pkm_backward with the library's static scratch."""
+    return lib().pkm_backward_noalloc(ctypes.byref(p), q, keys, values, idx, weights, dy, dq,
+                                      dkeys, dvalues, stream)
 
 
 def backward_sgd(p: Problem, q, keys, values, idx, weights, dy, dq, dkeys, lr, ws, ws_bytes,

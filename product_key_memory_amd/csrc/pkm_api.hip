@@ -9,7 +9,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 namespace {
 
@@ -279,18 +281,18 @@ pkm_status_t backward_impl(const pkm_problem_t *p, const void *q, const void *ke
     int32_t *slot_start = reinterpret_cast<int32_t *>(base + picks_bytes(p));
     int32_t *order = reinterpret_cast<int32_t *>(base + picks_bytes(p) + starts_bytes(p));
     const size_t head = 2 * picks_bytes(p) + starts_bytes(p);
-    void *scratch = T > 0 ? base + head : nullptr;
-    const size_t scratch_bytes = T > 0 ? workspace_bytes - head : 0;
+    void *stage_ws = T > 0 ? base + head : nullptr;
+    const size_t stage_ws_bytes = T > 0 ? workspace_bytes - head : 0;
     if (T > 0) {
-        st = pkm_slot_sort(p, idx, slot_start, order, scratch, scratch_bytes, stream);
+        st = pkm_slot_sort(p, idx, slot_start, order, stage_ws, stage_ws_bytes, stream);
         if (st != PKM_OK)
             return st;
     }
     st = pkm_backward_values(p, values, idx, weights, dy, slot_start, order, dvalues, accumulate,
-                             dw, scratch, scratch_bytes, stream);
+                             dw, stage_ws, stage_ws_bytes, stream);
     if (st != PKM_OK)
         return st;
-    return pkm_backward_queries(p, q, keys, idx, weights, dw, dq, dkeys, scratch, scratch_bytes,
+    return pkm_backward_queries(p, q, keys, idx, weights, dw, dq, dkeys, stage_ws, stage_ws_bytes,
                                 stream);
 }
 
@@ -341,18 +343,18 @@ pkm_status_t pkm_backward_sgd(const pkm_problem_t *p, const void *q, const void 
     int32_t *slot_start = reinterpret_cast<int32_t *>(base + picks_bytes(p));
     int32_t *order = reinterpret_cast<int32_t *>(base + picks_bytes(p) + starts_bytes(p));
     const size_t head = 2 * picks_bytes(p) + starts_bytes(p);
-    void *scratch = T > 0 ? base + head : nullptr;
-    const size_t scratch_bytes = T > 0 ? workspace_bytes - head : 0;
+    void *stage_ws = T > 0 ? base + head : nullptr;
+    const size_t stage_ws_bytes = T > 0 ? workspace_bytes - head : 0;
     if (T > 0) {
-        st = pkm_slot_sort(p, idx, slot_start, order, scratch, scratch_bytes, stream);
+        st = pkm_slot_sort(p, idx, slot_start, order, stage_ws, stage_ws_bytes, stream);
         if (st != PKM_OK)
             return st;
         if (pkm::launch_bwd_value_sgd(p->dtype, values, idx, weights, dy, slot_start, order, lr,
-                                      static_cast<float *>(scratch), dw, T, p->H, p->n, p->k,
+                                      static_cast<float *>(stage_ws), dw, T, p->H, p->n, p->k,
                                       p->d_v, static_cast<hipStream_t>(stream)) != hipSuccess)
             return PKM_ERR_HIP;
     }
-    return pkm_backward_queries(p, q, keys, idx, weights, dw, dq, dkeys, scratch, scratch_bytes,
+    return pkm_backward_queries(p, q, keys, idx, weights, dw, dq, dkeys, stage_ws, stage_ws_bytes,
                                 stream);
 }
 
@@ -538,8 +540,75 @@ const char *pkm_status_string(pkm_status_t s)
     case PKM_ERR_HIP: return "PKM_ERR_HIP: the HIP runtime rejected a launch";
     case PKM_ERR_ALIGN: return "PKM_ERR_ALIGN: an array pointer is not 16-byte aligned";
     case PKM_ERR_ARG: return "PKM_ERR_ARG: a scalar argument is outside its domain";
+    case PKM_ERR_TOO_LARGE:
+        return "PKM_ERR_TOO_LARGE: the problem needs more scratch than pkm_backward_noalloc's "
+               "static buffer (128 MiB per GPU) holds; call pkm_backward with a workspace";
     }
     return "PKM: unknown status";
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// pkm_backward_noalloc: pkm_backward with its workspace in a static device
+// array instead of the caller's memory, for callers that cannot allocate.
+// Each GPU the library runs on holds its own copy of the array (module global
+// memory, kept until the process ends).  In host code `scratch` names a host
+// stand-in, not the device copy: the device address is looked up with
+// hipGetSymbolAddress once per device, with that device current, and only
+// that address is ever handed to kernels.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_lookup;
+
+// The device address of `scratch` on the current device.
+pkm_status_t scratch_address(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return PKM_ERR_HIP;
+    void *ptr = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_lookup);
+        ptr = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!ptr) {
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+                return PKM_ERR_HIP;
+            g_scratch_addr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return PKM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkm_status_t pkm_backward_noalloc(const pkm_problem_t *p, const void *q, const void *keys,
+                                  const void *values, const int32_t *idx, const float *weights,
+                                  const void *dy, float *dq, float *dkeys, float *dvalues,
+                                  void *stream)
+{
+    const pkm_status_t st = check_problem(p, true);
+    if (st != PKM_OK)
+        return st;
+    if (backward_bytes(p) > kNoAllocScratchBytes)
+        return PKM_ERR_TOO_LARGE;
+    void *ws = nullptr;
+    if (p->T > 0) {
+        const pkm_status_t sa = scratch_address(&ws);
+        if (sa != PKM_OK)
+            return sa;
+    }
+    return backward_impl(p, q, keys, values, idx, weights, dy, dq, dkeys, dvalues, 1, ws,
+                         ws ? kNoAllocScratchBytes : 0, stream);
 }
 
 }  // extern "C"

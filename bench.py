@@ -57,13 +57,15 @@ STAGE_KERNELS = {
     "gather": ("fwd_gather_kernel",),
     "slot_sort": ("bucket_hist_kernel", "bucket_colscan_kernel", "bucket_scatter_kernel",
                   "bucket_sort_kernel"),
-    "bwd_values": ("seg_value_kernel", "slot_finish_kernel"),
+    "bwd_values": ("seg_value_kernel", "slot_scan_kernel", "long_run_kernel"),
     "bwd_queries": ("bwd_query_kernel", "dkeys_mfma_kernel", "dkeys_reduce_kernel"),
 }
 # the value side of pkm_backward_sgd (timed after the step; in the traffic
-# record only): the seg_value instance whose SGD flag is true and the
-# slot_finish instance of mode 2
-SGD_VALUE_KERNELS = {"seg_value_kernel": "true>", "slot_finish_kernel": "2>"}
+# record only): the seg_value instance whose SGD flag is true, the slot scan
+# without the zeroing of untouched rows (mode 1; the step overwrites, mode 0)
+# and the long-run sums of mode 2
+SGD_VALUE_KERNELS = {"seg_value_kernel": "true>", "slot_scan_kernel": "1>",
+                     "long_run_kernel": "2>"}
 
 
 def stage_of(short: str):

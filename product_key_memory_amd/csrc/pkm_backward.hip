@@ -128,42 +128,41 @@ __global__ __launch_bounds__(kColWaves *kWave) void bucket_colscan_kernel(
     }
 }
 
-// The stable placement both levels share.  A workgroup takes its picks in
-// rounds of kL1Threads consecutive ones (thread t: the t-th of the round); a
-// pick's place is cur[key] + (picks of the round before it with the same
-// key) -- those in earlier waves, counted through tab, plus those in lower
-// lanes of its own wave, found by wave_match -- so picks with equal keys keep
-// their order.  tab[w][key] = (round << 8) | (the picks of wave w with that
-// key in this round), valid only while its round tag is the current one.
-// The lowest wave holding a key advances cur[key] after everyone has read it.
+// Both levels place their items stably: a workgroup's range is cut into one
+// contiguous sub-range per wave; each wave counts its items per key in LDS,
+// the counts become per-(wave, key) cursors (keys outer, waves inner), and
+// each wave then walks its sub-range in order, 64 items at a time: an item's
+// place is its wave's cursor for the key plus the lanes below it with the
+// same key (wave_match).  Equal keys thus keep their order, and no barrier
+// is needed while placing -- each wave owns its cursors.
 constexpr int kSortWaves = kL1Threads / kWave;
-static_assert(kL2Threads == kL1Threads, "one placement routine for both levels");
+static_assert(kL2Threads == kL1Threads, "the same wave count at both levels");
+// items per lane in flight in the counting and placement loops of a wave's
+// sub-range: a Zipf-hot bucket holds ~24k pairs, 3k per wave, and each trip
+// waits for its loads
+constexpr int kSortUnroll = 16;
 
-template <int KEYS>
-__device__ __forceinline__ void stable_round(uint32_t key, bool valid, int bits, int round,
-                                             int32_t *cur, uint32_t (*tab)[KEYS], int &pos)
+__device__ __forceinline__ void sub_range(int64_t beg, int64_t end, int w, int64_t &sb,
+                                          int64_t &se)
 {
-    const int w = threadIdx.x / kWave;
+    const int64_t len = end - beg;
+    sb = beg + len * w / kSortWaves;
+    se = beg + len * (w + 1) / kSortWaves;
+}
+
+// One 64-item step of a wave's placement: the place of this lane's item
+// (valid lanes only); the highest-ranked lane of each key advances the cursor.
+__device__ __forceinline__ int place_step(uint32_t key, bool valid, int bits, int32_t *cursor)
+{
     const uint64_t peers = wave_match(key, valid, bits);
     const int rank = __popcll(peers & lanes_below());
-    const uint32_t tag = (uint32_t)round << 8;
-    if (valid && rank == 0)
-        tab[w][key] = tag | (uint32_t)__popcll(peers);
-    __syncthreads();
-    int before = 0, all = 0;
+    int pos = 0;
     if (valid) {
-#pragma unroll
-        for (int u = 0; u < kSortWaves; ++u) {
-            const uint32_t e = tab[u][key];
-            const int c = (e & ~0xFFu) == tag ? (int)(e & 0xFFu) : 0;
-            before += u < w ? c : 0;
-            all += c;
-        }
-        pos = cur[key] + before + rank;
+        pos = cursor[key] + rank;
+        if (rank == __popcll(peers) - 1)
+            cursor[key] = pos + 1;
     }
-    __syncthreads();
-    if (valid && rank == 0 && before == 0)
-        cur[key] += all;
+    return pos;
 }
 
 // Level-1 scatter: bucket_base = exclusive scan of total (block 0 stores it,
@@ -177,11 +176,31 @@ __global__ __launch_bounds__(kL1Threads) void bucket_scatter_kernel(
 {
     constexpr int PER = kMaxBuckets / kL1Threads;
     constexpr int W = kL1Threads / kWave;
-    __shared__ int32_t cur[kMaxBuckets];
-    __shared__ uint32_t tab[kSortWaves][kMaxBuckets];
+    __shared__ int32_t hw[kSortWaves][kMaxBuckets];   // per-wave counts, then cursors
     __shared__ int32_t wsum[W];
     const int lane = lane_id(), w = threadIdx.x / kWave;
-    // thread t owns buckets [PER t, PER t + PER)
+    for (int e = threadIdx.x; e < kSortWaves * kMaxBuckets; e += kL1Threads)
+        (&hw[0][0])[e] = 0;
+    const int64_t p0 = l1_begin(chunk, picks);
+    const int64_t p1 = p0 + chunk < picks ? p0 + chunk : picks;
+    int64_t sb, se;
+    sub_range(p0, p1, w, sb, se);
+    __syncthreads();
+    for (int64_t q = sb + lane; q < se; q += kWave * kSortUnroll) {
+        int32_t f[kSortUnroll];
+#pragma unroll
+        for (int u = 0; u < kSortUnroll; ++u) {
+            const int64_t p = q + (int64_t)u * kWave;
+            f[u] = p < se ? idx[p] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kSortUnroll; ++u)
+            if (f[u] >= 0)
+                atomicAdd(&hw[w][f[u] >> shift], 1);
+    }
+    // thread t owns buckets [PER t, PER t + PER): their global starts (an
+    // exclusive scan of total), this block's offset in each, then one cursor
+    // per wave
     int c[PER];
     int local = 0;
 #pragma unroll
@@ -194,8 +213,6 @@ __global__ __launch_bounds__(kL1Threads) void bucket_scatter_kernel(
     const int excl = wave_exclusive_scan(local, &tw);
     if (lane == 0)
         wsum[w] = tw;
-    for (int e = threadIdx.x; e < kSortWaves * kMaxBuckets; e += kL1Threads)
-        (&tab[0][0])[e] = 0xFFFFFFFFu;              // a round tag no round has
     __syncthreads();
     int run = excl;
     for (int u = 0; u < w; ++u)
@@ -205,9 +222,15 @@ __global__ __launch_bounds__(kL1Threads) void bucket_scatter_kernel(
     for (int j = 0; j < PER; ++j) {
         const int b = PER * threadIdx.x + j;
         if (b < nb) {
-            cur[b] = run + row[b];
             if (blockIdx.x == 0)
                 bucket_base[b] = run;
+            int cur = run + row[b];
+#pragma unroll
+            for (int u = 0; u < kSortWaves; ++u) {
+                const int cnt = hw[u][b];
+                hw[u][b] = cur;
+                cur += cnt;
+            }
         }
         run += c[j];
     }
@@ -215,61 +238,77 @@ __global__ __launch_bounds__(kL1Threads) void bucket_scatter_kernel(
         bucket_base[nb] = run;
     __syncthreads();
     const int32_t lowmask = (1 << shift) - 1;
-    const int64_t p0 = l1_begin(chunk, picks);
-    const int64_t p1 = p0 + chunk < picks ? p0 + chunk : picks;
-    int round = 0;
-    for (int64_t q = p0; q < p1; q += kL1Threads, ++round) {
-        const int64_t p = q + threadIdx.x;
-        const bool valid = p < p1;
-        const int32_t f = valid ? idx[p] : 0;
-        int pos = 0;
-        stable_round((uint32_t)(f >> shift), valid, nb_bits, round, cur, tab, pos);
-        if (valid)
-            pairs[pos] = make_int2((int32_t)p, f & lowmask);
+    // kSortUnroll steps of 64 picks per trip: their loads are all in flight
+    // before the first step is placed
+    for (int64_t q = sb; q < se; q += kWave * kSortUnroll) {
+        int32_t f[kSortUnroll];
+#pragma unroll
+        for (int u = 0; u < kSortUnroll; ++u) {
+            const int64_t p = q + u * kWave + lane;
+            f[u] = p < se ? idx[p] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kSortUnroll; ++u) {
+            const int64_t p = q + u * kWave + lane;
+            const bool valid = p < se;
+            const int pos = place_step((uint32_t)(f[u] >> shift), valid, nb_bits, hw[w]);
+            if (valid)
+                pairs[pos] = make_int2((int32_t)p, f[u] & lowmask);
+        }
     }
 }
 
-// Level 2, one workgroup per bucket: histogram of the low slot bits in LDS,
-// scan, slot_start of the bucket's 2^shift slots, then every pick's place.
+// Level 2, one workgroup per bucket: per-wave histograms of the low slot bits
+// in LDS, scan, slot_start of the bucket's 2^shift slots, then every pick's
+// place (the bucket's pairs arrive in pick order, level 1 being stable, so
+// each slot's picks end in ascending pick id).
 __global__ __launch_bounds__(kL2Threads) void bucket_sort_kernel(
     const int2 *__restrict__ pairs, const int32_t *__restrict__ bucket_base, int shift,
     int64_t slots, int32_t *__restrict__ slot_start, int32_t *__restrict__ order)
 {
     constexpr int W = kL2Threads / kWave;
-    __shared__ int32_t h[kMaxBucketSlots];      // counts, then the cursors of the bins
-    __shared__ uint32_t tab[kSortWaves][kMaxBucketSlots];
+    __shared__ int32_t hw[kSortWaves][kMaxBucketSlots];  // per-wave counts, then cursors
     __shared__ int32_t wsum[W];
     const int B = 1 << shift;
     const int64_t f0 = (int64_t)blockIdx.x << shift;
     const int nbins = (int)(slots - f0 < B ? slots - f0 : B);
     const int beg = bucket_base[blockIdx.x], end = bucket_base[blockIdx.x + 1];
-    for (int j = threadIdx.x; j < B; j += kL2Threads)
-        h[j] = 0;
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    for (int e = threadIdx.x; e < kSortWaves * kMaxBucketSlots; e += kL2Threads)
+        (&hw[0][0])[e] = 0;
+    int64_t sb, se;
+    sub_range(beg, end, w, sb, se);
     __syncthreads();
-    // kL2Unroll pairs per thread in flight before their counters are bumped:
+    // kSortUnroll pairs per lane in flight before their counters are bumped:
     // a large bucket (a Zipf-hot slot's) is this kernel's critical path
-    for (int64_t q = beg + (int)threadIdx.x; q < end; q += kL2Threads * kL2Unroll) {
-        int key[kL2Unroll];
+    for (int64_t q = sb + lane; q < se; q += kWave * kSortUnroll) {
+        int key[kSortUnroll];
 #pragma unroll
-        for (int u = 0; u < kL2Unroll; ++u) {
-            const int64_t p = q + (int64_t)u * kL2Threads;
-            key[u] = p < end ? pairs[p].y : -1;
+        for (int u = 0; u < kSortUnroll; ++u) {
+            const int64_t p = q + (int64_t)u * kWave;
+            key[u] = p < se ? pairs[p].y : -1;
         }
 #pragma unroll
-        for (int u = 0; u < kL2Unroll; ++u)
+        for (int u = 0; u < kSortUnroll; ++u)
             if (key[u] >= 0)
-                atomicAdd(&h[key[u]], 1);
+                atomicAdd(&hw[w][key[u]], 1);
     }
     __syncthreads();
-    // exclusive scan of h[0 .. B): thread t owns bins [BPT t, BPT t + BPT)
+    // bin totals, their exclusive scan (thread t owns bins [BPT t, BPT t + BPT)),
+    // then one cursor per (wave, bin)
     constexpr int BPT = kMaxBucketSlots / kL2Threads;
-    const int lane = lane_id(), w = threadIdx.x / kWave;
     int v[BPT], local = 0;
 #pragma unroll
     for (int e = 0; e < BPT; ++e) {
         const int bin = BPT * (int)threadIdx.x + e;
-        v[e] = bin < B ? h[bin] : 0;
-        local += v[e];
+        int t = 0;
+        if (bin < B) {
+#pragma unroll
+            for (int u = 0; u < kSortWaves; ++u)
+                t += hw[u][bin];
+        }
+        v[e] = t;
+        local += t;
     }
     int tw;
     const int excl = wave_exclusive_scan(local, &tw);
@@ -283,27 +322,34 @@ __global__ __launch_bounds__(kL2Threads) void bucket_sort_kernel(
     for (int e = 0; e < BPT; ++e) {
         const int bin = BPT * (int)threadIdx.x + e;
         if (bin < nbins) {
-            h[bin] = run;
             slot_start[f0 + bin] = run;
+            int cur = run;
+#pragma unroll
+            for (int u = 0; u < kSortWaves; ++u) {
+                const int cnt = hw[u][bin];
+                hw[u][bin] = cur;
+                cur += cnt;
+            }
         }
         run += v[e];
     }
     if (f0 + B >= slots && threadIdx.x == 0)
         slot_start[slots] = end;
-    for (int e = threadIdx.x; e < kSortWaves * kMaxBucketSlots; e += kL2Threads)
-        (&tab[0][0])[e] = 0xFFFFFFFFu;
     __syncthreads();
-    // the bucket's pairs arrive in pick order (level 1 is stable); placing
-    // them stably leaves each slot's picks in ascending pick order
-    int round = 0;
-    for (int64_t q = beg; q < end; q += kL2Threads, ++round) {
-        const int64_t p = q + threadIdx.x;
-        const bool valid = p < end;
-        const int2 pr = valid ? pairs[p] : make_int2(0, 0);
-        int pos = 0;
-        stable_round((uint32_t)pr.y, valid, shift, round, h, tab, pos);
-        if (valid)
-            order[pos] = pr.x;
+    for (int64_t q = sb; q < se; q += kWave * kSortUnroll) {
+        int2 pr[kSortUnroll];
+#pragma unroll
+        for (int u = 0; u < kSortUnroll; ++u) {
+            const int64_t p = q + u * kWave + lane;
+            pr[u] = p < se ? pairs[p] : make_int2(0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kSortUnroll; ++u) {
+            const bool valid = q + u * kWave + lane < se;
+            const int pos = place_step((uint32_t)pr[u].y, valid, shift, hw[w]);
+            if (valid)
+                order[pos] = pr[u].x;
+        }
     }
 }
 
@@ -320,90 +366,152 @@ __device__ __forceinline__ int64_t piece_row(int64_t a, int shift)
 }
 
 // After the segmented reduction, one pass over the slots (each wave checks
-// 64 slots, one per lane, then serves the rows found, all lanes on one row):
-//   - MODE 0 (overwrite): rows no pick selected become 0;
-//   - every long run's pieces are summed in the order of their positions --
-//     a fixed order, so the result does not depend on which wave ran first
-//     -- and the sum g is stored (MODE 0), added to dvalues (MODE 1), or
-//     applied to the value row, w = fmaf(-lr, g, w) rounded once to the
-//     storage type (MODE 2, the fused SGD; the rows were only read until now).
-template <typename DT, int MODE>
-__global__ void slot_finish_kernel(const int32_t *__restrict__ start, int64_t slots, int d_v,
-                                   int shift, const float *__restrict__ split,
-                                   float *__restrict__ dvalues, DT *__restrict__ values, float lr)
+// 64 slots, one per lane): in overwrite mode (MODE 0) the rows no pick
+// selected become 0, all lanes on one row at a time; every run longer than
+// the chunk is appended to `longs` (its slot), counted in longs[-1], which
+// seg_value_kernel reset.  The runs of the Zipf-hot queries' slots sit next
+// to each other (slots i n + j of one hot left sub-key i), so they are summed
+// by long_run_kernel, one wave each, rather than in turn by the wave that
+// found them.
+constexpr int kFinishWaves = 4;
+template <int MODE>
+__global__ __launch_bounds__(kFinishWaves *kWave) void slot_scan_kernel(
+    const int32_t *__restrict__ start, int64_t slots, int d_v, int shift,
+    float *__restrict__ dvalues, int32_t *__restrict__ longs)
 {
-    constexpr int EPC = Elt<DT>::per16;
     const int lane = lane_id();
     const int64_t chunk = (int64_t)1 << shift;
     const int64_t f0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * kWave;
     if (f0 >= slots)
         return;
     const int64_t f = f0 + lane;
-    bool todo_lane = false;
+    bool is_long = false, empty = false;
     if (f < slots) {
         const int64_t b = start[f], e = start[f + 1];
-        todo_lane = e - b > chunk || (MODE == 0 && b == e);
+        is_long = e - b > chunk;
+        empty = b == e;
     }
-    uint64_t todo = __ballot(todo_lane);
-    while (todo) {
-        const int i = __builtin_ctzll(todo);
-        todo &= todo - 1;
-        const int64_t fr = f0 + i;
-        const int64_t b = start[fr], e = start[fr + 1];
-        if (b == e) {                                   // overwrite mode, untouched row
-            float4 *row = reinterpret_cast<float4 *>(dvalues + fr * d_v);
+    const uint64_t lm = __ballot(is_long);
+    if (lm) {
+        int at = 0;
+        if (lane == 0)
+            at = atomicAdd(longs - 1, __popcll(lm));
+        at = __shfl(at, 0);
+        if (is_long)
+            longs[at + __popcll(lm & lanes_below())] = (int32_t)f;
+    }
+    if constexpr (MODE == 0) {
+        uint64_t todo = __ballot(empty);
+        while (todo) {
+            const int i = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            float4 *row = reinterpret_cast<float4 *>(dvalues + (f0 + i) * d_v);
             for (int c = lane; c < d_v / 4; c += kWave)
                 row[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-            continue;
         }
+    }
+}
+
+// One wave per listed long run: its pieces summed in the order of their
+// positions -- a fixed order, so the result does not depend on which wave
+// ran first -- and the sum g stored (MODE 0), added to dvalues (MODE 1), or
+// applied to the value row, w = fmaf(-lr, g, w) rounded once to the storage
+// type (MODE 2, the fused SGD; the rows were only read until now).
+template <typename DT, int MODE>
+__global__ __launch_bounds__(kFinishWaves *kWave) void long_run_kernel(
+    const int32_t *__restrict__ start, int d_v, int shift, const float *__restrict__ split,
+    const int32_t *__restrict__ longs, float *__restrict__ dvalues, DT *__restrict__ values,
+    float lr)
+{
+    constexpr int EPC = Elt<DT>::per16;
+    const int lane = lane_id();
+    const int wv = (int)blockIdx.x * kFinishWaves + (int)(threadIdx.x / kWave);
+    if (wv >= longs[-1])
+        return;
+    {
+        const int64_t fr = longs[wv];
+        const int64_t b = start[fr], e = start[fr + 1];
         const int64_t cb = b >> shift, ce = (e - 1) >> shift;
         const int64_t r0 = piece_row(b, shift);
-        for (int c = lane; c < d_v / EPC; c += kWave) {
-            float g[EPC];
+        auto row_of = [&](int64_t cc) { return cc == cb ? r0 : 2 * cc; };
+        // UPL units of EPC floats (16 floats) per lane per pass; the loads of
+        // PIECES pieces are issued before any is added, then the pieces are added
+        // one after the other in position order (the same order in every
+        // mode, so overwrite + sparse SGD and the fused SGD agree bit for bit)
+        constexpr int UPL = 16 / EPC, PIECES = 8;
+        const int nunits = d_v / EPC;
+        for (int u0 = 0; u0 < nunits; u0 += UPL * kWave) {
+            float g[UPL][EPC];
 #pragma unroll
-            for (int x = 0; x < EPC; ++x)
-                g[x] = 0.f;
-            for (int64_t cc = cb; cc <= ce; ++cc) {
-                const float *src = split + (cc == cb ? r0 : 2 * cc) * d_v + (int64_t)c * EPC;
-#pragma unroll
-                for (int x = 0; x < EPC; x += 4) {
-                    const float4 v = *reinterpret_cast<const float4 *>(src + x);
-                    g[x] += v.x;
-                    g[x + 1] += v.y;
-                    g[x + 2] += v.z;
-                    g[x + 3] += v.w;
-                }
-            }
-            if constexpr (MODE == 2) {
-                DT *dst = values + fr * d_v + (int64_t)c * EPC;
-                float w[EPC];
-                unpack16(*reinterpret_cast<const uint4 *>(dst), w);
+            for (int m = 0; m < UPL; ++m)
 #pragma unroll
                 for (int x = 0; x < EPC; ++x)
-                    w[x] = fmaf(-lr, g[x], w[x]);
-                if constexpr (sizeof(DT) == 2) {
-                    uint4 r;
-                    r.x = f32_to_bf16_bits(w[0]) | (f32_to_bf16_bits(w[1]) << 16);
-                    r.y = f32_to_bf16_bits(w[2]) | (f32_to_bf16_bits(w[3]) << 16);
-                    r.z = f32_to_bf16_bits(w[4]) | (f32_to_bf16_bits(w[5]) << 16);
-                    r.w = f32_to_bf16_bits(w[6]) | (f32_to_bf16_bits(w[7]) << 16);
-                    *reinterpret_cast<uint4 *>(dst) = r;
-                } else {
-                    *reinterpret_cast<float4 *>(dst) = make_float4(w[0], w[1], w[2], w[3]);
-                }
-            } else {
-                float *dst = dvalues + fr * d_v + (int64_t)c * EPC;
+                    g[m][x] = 0.f;
+            for (int64_t cc = cb; cc <= ce; cc += PIECES) {
+                float4 ld[PIECES][UPL][EPC / 4];
 #pragma unroll
-                for (int x = 0; x < EPC; x += 4) {
-                    float4 o = make_float4(g[x], g[x + 1], g[x + 2], g[x + 3]);
-                    if (MODE == 1) {
-                        const float4 old = *reinterpret_cast<const float4 *>(dst + x);
-                        o.x += old.x;
-                        o.y += old.y;
-                        o.z += old.z;
-                        o.w += old.w;
+                for (int pc = 0; pc < PIECES; ++pc) {
+                    const int64_t rr = row_of(cc + pc <= ce ? cc + pc : cc);
+#pragma unroll
+                    for (int m = 0; m < UPL; ++m) {
+                        const int u = u0 + lane + m * kWave;
+                        const float *src = split + rr * d_v + (int64_t)(u < nunits ? u : 0) * EPC;
+#pragma unroll
+                        for (int x = 0; x < EPC / 4; ++x)
+                            ld[pc][m][x] = *reinterpret_cast<const float4 *>(src + 4 * x);
                     }
-                    *reinterpret_cast<float4 *>(dst + x) = o;
+                }
+#pragma unroll
+                for (int pc = 0; pc < PIECES; ++pc) {
+                    if (cc + pc <= ce) {
+#pragma unroll
+                        for (int m = 0; m < UPL; ++m)
+#pragma unroll
+                            for (int x = 0; x < EPC / 4; ++x) {
+                                g[m][4 * x] += ld[pc][m][x].x;
+                                g[m][4 * x + 1] += ld[pc][m][x].y;
+                                g[m][4 * x + 2] += ld[pc][m][x].z;
+                                g[m][4 * x + 3] += ld[pc][m][x].w;
+                            }
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < UPL; ++m) {
+                const int u = u0 + lane + m * kWave;
+                if (u >= nunits)
+                    continue;
+                if constexpr (MODE == 2) {
+                    DT *dst = values + fr * d_v + (int64_t)u * EPC;
+                    float w[EPC];
+                    unpack16(*reinterpret_cast<const uint4 *>(dst), w);
+#pragma unroll
+                    for (int x = 0; x < EPC; ++x)
+                        w[x] = fmaf(-lr, g[m][x], w[x]);
+                    if constexpr (sizeof(DT) == 2) {
+                        uint4 r;
+                        r.x = f32_to_bf16_bits(w[0]) | (f32_to_bf16_bits(w[1]) << 16);
+                        r.y = f32_to_bf16_bits(w[2]) | (f32_to_bf16_bits(w[3]) << 16);
+                        r.z = f32_to_bf16_bits(w[4]) | (f32_to_bf16_bits(w[5]) << 16);
+                        r.w = f32_to_bf16_bits(w[6]) | (f32_to_bf16_bits(w[7]) << 16);
+                        *reinterpret_cast<uint4 *>(dst) = r;
+                    } else {
+                        *reinterpret_cast<float4 *>(dst) = make_float4(w[0], w[1], w[2], w[3]);
+                    }
+                } else {
+                    float *dst = dvalues + fr * d_v + (int64_t)u * EPC;
+#pragma unroll
+                    for (int x = 0; x < EPC; x += 4) {
+                        float4 o = make_float4(g[m][x], g[m][x + 1], g[m][x + 2], g[m][x + 3]);
+                        if (MODE == 1) {
+                            const float4 old = *reinterpret_cast<const float4 *>(dst + x);
+                            o.x += old.x;
+                            o.y += old.y;
+                            o.z += old.z;
+                            o.w += old.w;
+                        }
+                        *reinterpret_cast<float4 *>(dst + x) = o;
+                    }
                 }
             }
         }
@@ -468,7 +576,7 @@ __device__ __forceinline__ void seg_flush(float (&acc)[MCH][EPC], float *__restr
                                           int nchunks, int lane, bool exclusive, int accumulate)
 {
     // a run this wave holds whole goes to its dvalues row; a piece of a long
-    // run to its piece row (summed later, in order, by slot_finish_kernel)
+    // run to its piece row (summed later, in order, by long_run_kernel)
     float *drow = exclusive ? dvalues + f * d_v : piece;
     const bool add = exclusive && accumulate;
 #pragma unroll
@@ -499,7 +607,7 @@ __device__ __forceinline__ void seg_flush(float (&acc)[MCH][EPC], float *__restr
 // The fused update: the run's sum g updates its value row in place,
 // w = fmaf(-lr, g, w) rounded once to the storage type (vrow holds the row's
 // old values), when the row is this wave's alone; a long run's piece goes to
-// its piece row, applied after the kernel by slot_finish_kernel.
+// its piece row, applied after the kernel by long_run_kernel.
 template <typename DT, int MCH, int EPC>
 __device__ __forceinline__ void seg_flush_sgd(float (&acc)[MCH][EPC], const float (&vrow)[MCH][EPC],
                                               DT *values, float *__restrict__ piece, int64_t f,
@@ -559,6 +667,8 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
     __shared__ int32_t s_seg[kSegWaves][kMaxLen + 1];
     const int lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        long_list(split, picks, d_v)[-1] = 0;   // the count of the long-run list (slot_scan_kernel)
     const int64_t nom = ((int64_t)blockIdx.x * kSegWaves + wv) * chunk;
     if (nom >= picks)
         return;
@@ -1347,14 +1457,26 @@ hipError_t launch_slot_sort(const int32_t *idx, int64_t picks, int n, int32_t *s
     return hipGetLastError();
 }
 
+// slot_scan_kernel (untouched rows, the list of long runs) then
+// long_run_kernel, one wave per possible long run (at most picks / chunk + 1;
+// the waves past the listed count return at once).  `longs` follows the
+// piece rows in the split buffer (split_rows_bytes lays it out).
 template <typename DT, int MODE>
-static hipError_t launch_finish(const int32_t *slot_start, int64_t slots, int d_v, int shift,
-                                const float *split, float *dvalues, void *values, float lr,
+static hipError_t launch_finish(const int32_t *slot_start, int64_t slots, int64_t picks, int d_v,
+                                int shift, float *split, float *dvalues, void *values, float lr,
                                 hipStream_t stream)
 {
-    hipLaunchKernelGGL((slot_finish_kernel<DT, MODE>), dim3(grid1d(slots, 4 * kWave)),
-                       dim3(4 * kWave), 0, stream, slot_start, slots, d_v, shift, split, dvalues,
-                       static_cast<DT *>(values), lr);
+    int32_t *longs = long_list(split, picks, d_v);
+    hipLaunchKernelGGL((slot_scan_kernel<MODE == 0 ? 0 : 1>),
+                       dim3(grid1d(slots, kFinishWaves * kWave)), dim3(kFinishWaves * kWave), 0,
+                       stream, slot_start, slots, d_v, shift, dvalues, longs);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    const int64_t max_long = (picks >> shift) + 1;
+    hipLaunchKernelGGL((long_run_kernel<DT, MODE>), dim3(grid1d(max_long, kFinishWaves)),
+                       dim3(kFinishWaves * kWave), 0, stream, slot_start, d_v, shift, split, longs,
+                       dvalues, static_cast<DT *>(values), lr);
     return hipGetLastError();
 }
 
@@ -1376,10 +1498,10 @@ hipError_t launch_bwd_value(int dtype, const void *values, const int32_t *idx,
     if (err != hipSuccess)
         return err;
     // the storage type does not enter modes 0 and 1 (dvalues is float32)
-    return accumulate ? launch_finish<float, 1>(slot_start, slots, d_v, shift, split, dvalues,
-                                                nullptr, 0.f, stream)
-                      : launch_finish<float, 0>(slot_start, slots, d_v, shift, split, dvalues,
-                                                nullptr, 0.f, stream);
+    return accumulate ? launch_finish<float, 1>(slot_start, slots, picks, d_v, shift, split,
+                                                dvalues, nullptr, 0.f, stream)
+                      : launch_finish<float, 0>(slot_start, slots, picks, d_v, shift, split,
+                                                dvalues, nullptr, 0.f, stream);
 }
 
 hipError_t launch_bwd_value_sgd(int dtype, void *values, const int32_t *idx, const float *weights,
@@ -1399,10 +1521,10 @@ hipError_t launch_bwd_value_sgd(int dtype, void *values, const int32_t *idx, con
                                                 stream);
     if (err != hipSuccess)
         return err;
-    return dtype == 1 ? launch_finish<bf16_t, 2>(slot_start, slots, d_v, shift, split, nullptr,
-                                                 values, lr, stream)
-                      : launch_finish<float, 2>(slot_start, slots, d_v, shift, split, nullptr,
-                                                values, lr, stream);
+    return dtype == 1 ? launch_finish<bf16_t, 2>(slot_start, slots, picks, d_v, shift, split,
+                                                 nullptr, values, lr, stream)
+                      : launch_finish<float, 2>(slot_start, slots, picks, d_v, shift, split,
+                                                nullptr, values, lr, stream);
 }
 
 template <typename DT>

@@ -16,7 +16,7 @@ static_assert((1 << kSegShift) == kSegChunk, "kSegShift = log2(kSegChunk)");
 // log2 of the picks per wave of the value side: 256, or fewer (down to 32) on
 // small batches, so that about 2048 waves share the work.  Runs of more than
 // that many sorted picks are "long" (cut between waves).
-inline int seg_shift(int64_t picks)
+__host__ __device__ inline int seg_shift(int64_t picks)
 {
     int s = kSegShift;
     while (s > 5 && (picks >> s) < 2048)
@@ -87,10 +87,22 @@ hipError_t launch_bwd_value_sgd(int dtype, void *values, const int32_t *idx, con
                                 const void *dy, const int32_t *slot_start, const int32_t *order,
                                 float lr, float *split, float *dw, int64_t T, int H, int n,
                                 int k, int d_v, hipStream_t stream);
-// Two piece rows of d_v floats per nominal chunk of 2^seg_shift sorted picks.
-inline size_t split_rows_bytes(int64_t picks, int d_v)
+// The value side's scratch: two piece rows of d_v floats per nominal chunk
+// of 2^seg_shift sorted picks, then the list of long runs: a count, followed
+// by at most picks / chunk + 1 slots (long_list points at the first slot,
+// the count sits just before it).
+__host__ __device__ inline size_t split_piece_bytes(int64_t picks, int d_v)
 {
     return (size_t)(2 * ((picks >> seg_shift(picks)) + 1)) * (size_t)d_v * 4;
+}
+__host__ __device__ inline size_t split_rows_bytes(int64_t picks, int d_v)
+{
+    return split_piece_bytes(picks, d_v) + 256 + (size_t)((picks >> seg_shift(picks)) + 1) * 4;
+}
+__host__ __device__ inline int32_t *long_list(float *split, int64_t picks, int d_v)
+{
+    return reinterpret_cast<int32_t *>(reinterpret_cast<char *>(split) +
+                                       split_piece_bytes(picks, d_v) + 256);
 }
 
 // Query side: softmax backward per distinct sub-key, dq (overwritten) and

@@ -43,6 +43,12 @@ def parse():
                     help="instead of the bench line: the step (forward + backward) over heads "
                          "H in 1, 2, 4, 8 and picks k in 8, 16, 32 on the workload's other shapes, "
                          "one JSON line each with tokens/s and the fraction of slots in use")
+    ap.add_argument("--flat", action="store_true",
+                    help="instead of the bench line: the selection by product keys against the "
+                         "flat search over all n^2 keys (pkm_flat_forward_select) for n in 128, "
+                         "256, 512 at the workload's other shapes, --flat-tokens tokens; one JSON "
+                         "line per n")
+    ap.add_argument("--flat-tokens", type=int, default=4096)
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="no GPU work: read the rocprofv3 databases of a FETCH_SIZE run and a "
                          "WRITE_SIZE run of `bench.py --calibrate-copy`, and write the "
@@ -354,7 +360,8 @@ def cpu_baseline(inp, k: int, count: int) -> dict:
 
 def run_sweep(args) -> None:
     """The speed / memory-use knobs: heads H and picks k on the workload's
-    remaining shapes (synthetic inputs of the same recipe, one draw per H).
+    remaining shapes (synthetic inputs of the same recipe, one draw per H),
+    and at k = 32 one codebook pair shared by the heads (the first head's).
     Per point: W warm-up and K timed steps of pkm_forward + pkm_backward
     (dvalues overwritten) bracketed by events, and the share of the n*n slots
     some pick selected in the batch."""
@@ -386,8 +393,10 @@ def run_sweep(args) -> None:
         dvalues = torch.empty((n * n, d_v), dtype=torch.float32, device=dev)
         dq = torch.empty((T, H, d_k), dtype=torch.float32, device=dev)
         dkeys = torch.empty((H, 2, n, d_k // 2), dtype=torch.float32, device=dev)
-        for k in (8, 16, 32):
-            p = problem(T, H, n, k, d_k, d_v, tdt)
+        keys_one = keys[0].contiguous()          # one codebook pair for every head
+        for k, shared in ((8, False), (16, False), (32, False), (32, True)):
+            p = problem(T, H, n, k, d_k, d_v, tdt, keys_shared=shared)
+            kp = P(keys_one) if shared else P(keys)
             fb, bb = _lib.workspace_bytes(p, False), _lib.workspace_bytes(p, True)
             fws = torch.empty(max(fb, 1), dtype=torch.uint8, device=dev)
             bws = torch.empty(max(bb, 1), dtype=torch.uint8, device=dev)
@@ -395,9 +404,9 @@ def run_sweep(args) -> None:
             wts = torch.empty((T, H, k), dtype=torch.float32, device=dev)
 
             def step():
-                rc = _lib.forward(p, P(q), P(keys), P(values), P(y), P(idx), P(wts), None,
+                rc = _lib.forward(p, P(q), kp, P(values), P(y), P(idx), P(wts), None,
                                   P(fws), fb, sp)
-                rc |= _lib.backward_overwrite(p, P(q), P(keys), P(values), P(idx), P(wts), P(dy),
+                rc |= _lib.backward_overwrite(p, P(q), kp, P(values), P(idx), P(wts), P(dy),
                                               P(dq), P(dkeys), P(dvalues), P(bws), bb, sp)
                 if rc:
                     raise RuntimeError(f"libpkm returned {rc}")
@@ -413,11 +422,80 @@ def run_sweep(args) -> None:
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / args.steps
             used = torch.unique(idx).numel() / (n * n)
-            print(json.dumps({"sweep": {"workload": base.name, "H": H, "k": k},
+            print(json.dumps({"sweep": {"workload": base.name, "H": H, "k": k,
+                                        "codebooks": "shared" if shared else "per head"},
                               "tokens_per_s": round(T / (ms * 1e-3), 1),
                               "ms_per_step": round(ms, 4), "used_fraction": round(used, 4)}),
                   flush=True)
         del q, keys, values, dy, y, dvalues, dq, dkeys
+        torch.cuda.empty_cache()
+
+
+def run_flat(args) -> None:
+    """Search cost, flat against product keys (companion page, "Search cost:
+    flat vs product keys"): the workload's recipe at --flat-tokens tokens and
+    n = 128, 256, 512; per n, W warm-up and K timed calls of each selection
+    (scores, top-k, softmax; the gather that follows is the same for both)
+    bracketed by events.  Flops: product keys 2 T H 2 n (d_k / 2), flat
+    2 T H n^2 d_k.  The sets of the two searches are compared (equal wherever
+    the k-th / (k+1)-th gap is clear; the parity tests check that)."""
+    import dataclasses
+
+    import torch
+    import pkm_inputs
+    from product_key_memory_amd import _lib
+    from product_key_memory_amd.pkm import problem
+
+    dev = torch.device("cuda", 0)
+    base = pkm_inputs.WORKLOADS[args.workload]
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    P = lambda t: t.data_ptr()  # noqa: E731
+    for n in (128, 256, 512):
+        w0 = dataclasses.replace(base, n=n, T=args.flat_tokens, zipf=0.0, backward=False,
+                                 name=f"{base.name}-n{n}-T{args.flat_tokens}")
+        inp = pkm_inputs.make(w0, with_dy=False)
+        q = torch.from_numpy(inp["q"].view(np.int16)).to(dev).view(torch.bfloat16)
+        keys = torch.from_numpy(inp["keys"].view(np.int16)).to(dev).view(torch.bfloat16)
+        T, H, k, d_k = w0.T, w0.H, w0.k, w0.d_k
+        p = problem(T, H, n, k, d_k, w0.d_v, torch.bfloat16)
+        fb = _lib.workspace_bytes(p, False)
+        fws = torch.empty(max(fb, 1), dtype=torch.uint8, device=dev)
+        out = {name: (torch.empty((T, H, k), dtype=torch.int32, device=dev),
+                      torch.empty((T, H, k), dtype=torch.float32, device=dev))
+               for name in ("product", "flat")}
+        calls = {
+            "product": lambda: _lib.forward_select(p, P(q), P(keys), P(out["product"][0]),
+                                                   P(out["product"][1]), None, P(fws), fb, sp),
+            "flat": lambda: _lib.flat_forward_select(p, P(q), P(keys), P(out["flat"][0]),
+                                                     P(out["flat"][1]), None, sp),
+        }
+        flops = {"product": 2 * T * H * 2 * n * (d_k // 2), "flat": 2 * T * H * n * n * d_k}
+        res = {}
+        for name, fn in calls.items():
+            steps = args.steps if name == "product" else max(2, args.steps // 4)
+            for _ in range(args.warmup if name == "product" else 1):
+                assert fn() == 0, name
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            tf = flops[name] / (ms * 1e-3) / 1e12
+            res[name] = {"ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                         "flops": flops[name], "TFLOP/s": round(tf, 1),
+                         "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+        same = (out["product"][0].sort(dim=2).values == out["flat"][0].sort(dim=2).values)
+        same_rows = float(same.all(dim=2).float().mean().item())
+        print(json.dumps({"flat_vs_product": {"workload": w0.name, "T": T, "H": H, "n": n,
+                                              "keys": n * n, "k": k, "d_k": d_k},
+                          "product": res["product"], "flat": res["flat"],
+                          "flat_over_product_time": round(res["flat"]["ms"] / res["product"]["ms"], 1),
+                          "identical_sets": round(same_rows, 5)}), flush=True)
+        del q, keys, fws, out
         torch.cuda.empty_cache()
 
 
@@ -428,6 +506,9 @@ def main():
         return
     if args.sweep:
         run_sweep(args)
+        return
+    if args.flat:
+        run_flat(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -63,6 +63,13 @@ typedef enum {
                               its static scratch holds                           */
 } pkm_status_t;
 
+/* Or-ed into pkm_problem_t.dtype: ONE pair of codebooks serves every head
+ * (gptget.net summary, "Technical Contribution": the heads differ in their
+ * query mappings).  keys is then [2][n][d_k/2] instead of [H][2][n][d_k/2],
+ * and dkeys [2][n][d_k/2] holds the sub-key gradient summed over the heads.
+ * Every entry point that takes keys or dkeys accepts it; the others ignore it. */
+#define PKM_KEYS_SHARED 0x100
+
 /* Problem sizes.  32 bytes, no padding: T, then six int32 fields. */
 typedef struct {
     int64_t T;      /* tokens (>= 0)                                          */
@@ -71,7 +78,7 @@ typedef struct {
     int32_t k;      /* slots selected per head (also the per-half top-k)      */
     int32_t d_k;    /* query width per head; halves of d_k/2                  */
     int32_t d_v;    /* value row width                                        */
-    int32_t dtype;  /* pkm_dtype_t                                            */
+    int32_t dtype;  /* pkm_dtype_t, optionally | PKM_KEYS_SHARED              */
 } pkm_problem_t;
 
 /* Bytes of device workspace pkm_forward and pkm_forward_select (backward = 0),
@@ -97,7 +104,8 @@ size_t pkm_workspace_bytes(const pkm_problem_t *p, int backward);
  * and y[t] = sum over heads and picks of weight * values[slot].
  *
  *   q        [T][H][d_k]        dtype   (q1 = first d_k/2 of each head)
- *   keys     [H][2][n][d_k/2]   dtype   ([h][0] left codebook, [h][1] right)
+ *   keys     [H][2][n][d_k/2]   dtype   ([h][0] left codebook, [h][1] right;
+ *                                       [2][n][d_k/2] with PKM_KEYS_SHARED)
  *   values   [n*n][d_v]         dtype   (row f = i*n + j)
  *   y        [T][d_v]           dtype   OUT, overwritten (float32 sums,
  *                                       rounded to nearest-even for bf16)
@@ -127,7 +135,8 @@ pkm_status_t pkm_forward(const pkm_problem_t *p, const void *q, const void *keys
  *   idx, weights      [T][H][k] as produced by pkm_forward for these inputs
  *   dy       [T][d_v]           dtype
  *   dq       [T][H][d_k]        float32 OUT, overwritten
- *   dkeys    [H][2][n][d_k/2]   float32 OUT, overwritten
+ *   dkeys    [H][2][n][d_k/2]   float32 OUT, overwritten ([2][n][d_k/2], the
+ *                               sum over heads, with PKM_KEYS_SHARED)
  *   dvalues  [n*n][d_v]         float32 IN/OUT, ACCUMULATED (+=): the caller
  *                               zeroes it (or keeps an earlier gradient to add
  *                               to); rows no pick selects are left untouched.
@@ -211,6 +220,19 @@ pkm_status_t pkm_backward_sgd(const pkm_problem_t *p, const void *q, const void 
 pkm_status_t pkm_forward_select(const pkm_problem_t *p, const void *q, const void *keys,
                                 int32_t *idx, float *weights, float *scores, void *workspace,
                                 size_t workspace_bytes, void *stream);
+
+/* The flat-key search that product keys replace, as a workload of its own
+ * (companion page, "Search cost: flat vs product keys": a flat memory
+ * compares the query with every key): for every (t, h) all n*n implied keys
+ * -- key f = i*n + j is left sub-key i followed by right sub-key j --
+ * scored with one d_k-wide dot product each (float32 accumulation), the
+ * exact top-k by (score desc, slot asc), and the softmax of the k scores.
+ * Same outputs, layouts and PKM_KEYS_SHARED as pkm_forward_select; y follows
+ * from pkm_forward_gather.  About n*n*d_k*2 flops per (token, head) against
+ * the product keys' 2*n*d_k.  Supported: bf16 storage (else PKM_ERR_DTYPE),
+ * d_k = 512, 32 <= n <= 1024, k <= 32 (else PKM_ERR_SHAPE).  No workspace. */
+pkm_status_t pkm_flat_forward_select(const pkm_problem_t *p, const void *q, const void *keys,
+                                     int32_t *idx, float *weights, float *scores, void *stream);
 
 /* y[t] = sum over heads h and picks r of weights[t][h][r] * values[idx[t][h][r]]
  * (gptget.net summary, "Methodology": weighted sum of the selected values). */

@@ -14,6 +14,7 @@ LIB_PATH = os.environ.get("PKM_LIB") or os.path.join(os.path.dirname(os.path.abs
 
 PKM_FP32 = 0
 PKM_BF16 = 1
+PKM_KEYS_SHARED = 0x100      # or-ed into Problem.dtype: one codebook pair for every head
 
 STATUS = {
     0: "PKM_OK",
@@ -30,7 +31,7 @@ STATUS = {
 # every symbol include/pkm.h declares
 EXPORTS = ("pkm_workspace_bytes", "pkm_forward", "pkm_backward", "pkm_backward_overwrite",
            "pkm_backward_noalloc", "pkm_backward_sgd",
-           "pkm_forward_select",
+           "pkm_forward_select", "pkm_flat_forward_select",
            "pkm_forward_gather", "pkm_slot_sort", "pkm_backward_values", "pkm_backward_queries",
            "pkm_sparse_sgd", "pkm_sparse_adam", "pkm_slot_usage", "pkm_query_workspace_bytes",
            "pkm_query_forward", "pkm_query_backward", "pkm_status_string")
@@ -83,6 +84,7 @@ def lib() -> ctypes.CDLL:
         PP = ctypes.POINTER(Problem)
         L.pkm_forward_select.argtypes = [PP, P, P, P, P, P, P, c_size, P]
         L.pkm_forward_gather.argtypes = [PP, P, P, P, P, P]
+        L.pkm_flat_forward_select.argtypes = [PP, P, P, P, P, P, P]
         L.pkm_slot_sort.argtypes = [PP, P, P, P, P, c_size, P]
         L.pkm_backward_values.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_int, P, P, c_size, P]
         L.pkm_backward_queries.argtypes = [PP, P, P, P, P, P, P, P, P, c_size, P]
@@ -95,7 +97,8 @@ def lib() -> ctypes.CDLL:
         L.pkm_query_workspace_bytes.restype = c_size
         L.pkm_query_forward.argtypes = [QP, P, P, P, P, F, P, P, P, P, P, c_size, P]
         L.pkm_query_backward.argtypes = [QP, P, P, P, P, P, P, P, P, P, P, P, P, c_size, P]
-        for name in ("pkm_forward_select", "pkm_forward_gather", "pkm_slot_sort",
+        for name in ("pkm_forward_select", "pkm_flat_forward_select", "pkm_forward_gather",
+                     "pkm_slot_sort",
                      "pkm_backward_values", "pkm_backward_queries", "pkm_sparse_sgd",
                      "pkm_sparse_adam", "pkm_slot_usage", "pkm_query_forward",
                      "pkm_query_backward"):
@@ -150,6 +153,11 @@ def backward_sgd(p: Problem, q, keys, values, idx, weights, dy, dq, dkeys, lr, w
 def forward_select(p: Problem, q, keys, idx, weights, scores, ws, ws_bytes, stream) -> int:
     return lib().pkm_forward_select(ctypes.byref(p), q, keys, idx, weights, scores, ws, ws_bytes,
                                     stream)
+
+
+def flat_forward_select(p: Problem, q, keys, idx, weights, scores, stream) -> int:
+    """pkm_flat_forward_select: the flat search over all n*n implied keys."""
+    return lib().pkm_flat_forward_select(ctypes.byref(p), q, keys, idx, weights, scores, stream)
 
 
 def forward_gather(p: Problem, values, idx, weights, y, stream) -> int:

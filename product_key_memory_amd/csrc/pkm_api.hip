@@ -26,11 +26,21 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // A pointer to an array with no elements (T == 0) may be NULL.
 bool missing(const void *p, int64_t count) { return count > 0 && p == nullptr; }
 
+// The storage type and the layout flag carried by pkm_problem_t.dtype.
+int storage(const pkm_problem_t *p) { return p->dtype & 0xFF; }
+bool keys_shared(const pkm_problem_t *p) { return (p->dtype & PKM_KEYS_SHARED) != 0; }
+// elements from one head's codebooks to the next (0: every head reads the same pair)
+int64_t key_hstride(const pkm_problem_t *p)
+{
+    return keys_shared(p) ? 0 : (int64_t)2 * p->n * (p->d_k / 2);
+}
+
 pkm_status_t check_problem(const pkm_problem_t *p, bool backward)
 {
     if (!p)
         return PKM_ERR_NULL;
-    if (p->dtype != PKM_FP32 && p->dtype != PKM_BF16)
+    if ((storage(p) != PKM_FP32 && storage(p) != PKM_BF16) ||
+        (p->dtype & ~(0xFF | PKM_KEYS_SHARED)) != 0)
         return PKM_ERR_DTYPE;
     if (p->T < 0 || p->H < 1 || p->H > kMaxH || p->n < 1 || p->n > kMaxN || p->k < 1 ||
         p->k > p->n || p->k > kMaxK || p->d_k < 16 || p->d_k > kMaxDk || p->d_k % 16 != 0 ||
@@ -74,7 +84,7 @@ size_t backward_sgd_bytes(const pkm_problem_t *p) { return backward_bytes(p); }
 
 size_t forward_bytes(const pkm_problem_t *p)
 {
-    return pkm::select_workspace_bytes(p->T, p->H, p->n, p->k, p->dtype, p->d_k);
+    return pkm::select_workspace_bytes(p->T, p->H, p->n, p->k, storage(p), p->d_k);
 }
 
 pkm_status_t check_workspace(const pkm_problem_t *p, const void *ws, size_t have, size_t need)
@@ -117,8 +127,33 @@ pkm_status_t pkm_forward_select(const pkm_problem_t *p, const void *q, const voi
         return st;
     if (T == 0)
         return PKM_OK;
-    return pkm::launch_fwd_select(p->dtype, q, keys, p->T, p->H, p->n, p->k, p->d_k, idx, weights,
+    return pkm::launch_fwd_select(storage(p), q, keys, key_hstride(p), p->T, p->H, p->n, p->k,
+                                  p->d_k, idx, weights,
                                   scores, workspace, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? PKM_OK
+               : PKM_ERR_HIP;
+}
+
+pkm_status_t pkm_flat_forward_select(const pkm_problem_t *p, const void *q, const void *keys,
+                                     int32_t *idx, float *weights, float *scores, void *stream)
+{
+    pkm_status_t st = check_problem(p, false);
+    if (st != PKM_OK)
+        return st;
+    if (storage(p) != PKM_BF16)
+        return PKM_ERR_DTYPE;
+    if (p->d_k != 512 || p->n < 32 || p->k > 32)
+        return PKM_ERR_SHAPE;
+    const int64_t T = p->T;
+    if (missing(q, T) || !keys || missing(idx, T) || missing(weights, T))
+        return PKM_ERR_NULL;
+    if (!aligned16(q) || !aligned16(keys) || !aligned16(idx) || !aligned16(weights) ||
+        (scores && !aligned16(scores)))
+        return PKM_ERR_ALIGN;
+    if (T == 0)
+        return PKM_OK;
+    return pkm::launch_flat_select(q, keys, key_hstride(p), T, p->H, p->n, p->k, idx, weights,
+                                   scores, static_cast<hipStream_t>(stream)) == hipSuccess
                ? PKM_OK
                : PKM_ERR_HIP;
 }
@@ -136,7 +171,7 @@ pkm_status_t pkm_forward_gather(const pkm_problem_t *p, const void *values, cons
         return PKM_ERR_ALIGN;
     if (T == 0)
         return PKM_OK;
-    return pkm::launch_fwd_gather(p->dtype, values, idx, weights, y, p->T, p->H * p->k, p->d_v,
+    return pkm::launch_fwd_gather(storage(p), values, idx, weights, y, p->T, p->H * p->k, p->d_v,
                                   static_cast<hipStream_t>(stream)) == hipSuccess
                ? PKM_OK
                : PKM_ERR_HIP;
@@ -215,7 +250,7 @@ pkm_status_t pkm_backward_values(const pkm_problem_t *p, const void *values, con
                                                           s) == hipSuccess
                    ? PKM_OK
                    : PKM_ERR_HIP;
-    return pkm::launch_bwd_value(p->dtype, values, idx, weights, dy, slot_start, order, dvalues,
+    return pkm::launch_bwd_value(storage(p), values, idx, weights, dy, slot_start, order, dvalues,
                                  dvalues_accumulate, static_cast<float *>(workspace), dw, p->T,
                                  p->H, p->n, p->k, p->d_v, s) == hipSuccess
                ? PKM_OK
@@ -242,12 +277,15 @@ pkm_status_t pkm_backward_queries(const pkm_problem_t *p, const void *q, const v
     if (st != PKM_OK)
         return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const int heads_of_dkeys = keys_shared(p) ? 1 : p->H;
     if (T == 0)
-        return pkm::launch_zero_f32(dkeys, (int64_t)p->H * 2 * p->n * (p->d_k / 2), s) == hipSuccess
+        return pkm::launch_zero_f32(dkeys, (int64_t)heads_of_dkeys * 2 * p->n * (p->d_k / 2),
+                                    s) == hipSuccess
                    ? PKM_OK
                    : PKM_ERR_HIP;
-    return pkm::launch_bwd_query(p->dtype, q, keys, idx, weights, dw, dq, dkeys, p->T, p->H, p->n,
-                                 p->k, p->d_k, workspace, s) == hipSuccess
+    return pkm::launch_bwd_query(storage(p), q, keys, key_hstride(p), keys_shared(p), idx, weights,
+                                 dw, dq, dkeys, p->T, p->H, p->n, p->k, p->d_k, workspace,
+                                 s) == hipSuccess
                ? PKM_OK
                : PKM_ERR_HIP;
 }
@@ -349,7 +387,7 @@ pkm_status_t pkm_backward_sgd(const pkm_problem_t *p, const void *q, const void 
         st = pkm_slot_sort(p, idx, slot_start, order, stage_ws, stage_ws_bytes, stream);
         if (st != PKM_OK)
             return st;
-        if (pkm::launch_bwd_value_sgd(p->dtype, values, idx, weights, dy, slot_start, order, lr,
+        if (pkm::launch_bwd_value_sgd(storage(p), values, idx, weights, dy, slot_start, order, lr,
                                       static_cast<float *>(stage_ws), dw, T, p->H, p->n, p->k,
                                       p->d_v, static_cast<hipStream_t>(stream)) != hipSuccess)
             return PKM_ERR_HIP;
@@ -371,7 +409,7 @@ pkm_status_t pkm_sparse_sgd(const pkm_problem_t *p, void *values, const float *d
     if (!std::isfinite(lr))
         return PKM_ERR_ARG;
     pkm::UpdateParams prm{lr, 0.f, 0.f, 0.f, 1.f, 1.f};
-    return pkm::launch_sparse_update(p->dtype, values, dvalues, slot_start, nullptr, nullptr,
+    return pkm::launch_sparse_update(storage(p), values, dvalues, slot_start, nullptr, nullptr,
                                      (int64_t)p->n * p->n, p->d_v, false, prm,
                                      static_cast<hipStream_t>(stream)) == hipSuccess
                ? PKM_OK
@@ -399,7 +437,7 @@ pkm_status_t pkm_sparse_adam(const pkm_problem_t *p, void *values, const float *
     if (!(c1 > 0.0) || !(c2 > 0.0))
         return PKM_ERR_ARG;
     pkm::UpdateParams prm{lr, beta1, beta2, eps, (float)c1, (float)c2};
-    return pkm::launch_sparse_update(p->dtype, values, dvalues, slot_start, adam_m, adam_v,
+    return pkm::launch_sparse_update(storage(p), values, dvalues, slot_start, adam_m, adam_v,
                                      (int64_t)p->n * p->n, p->d_v, true, prm,
                                      static_cast<hipStream_t>(stream)) == hipSuccess
                ? PKM_OK

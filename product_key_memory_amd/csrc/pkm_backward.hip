@@ -852,7 +852,7 @@ struct Row4<bf16_t> {
 // (half <= 256 JPL).
 template <typename DT, int JPL>
 __global__ __launch_bounds__(kQryWaves *kWave) void bwd_query_kernel(
-    const DT *__restrict__ keys, const int32_t *__restrict__ idx,
+    const DT *__restrict__ keys, int64_t key_hstride, const int32_t *__restrict__ idx,
     const float *__restrict__ weights, const float *__restrict__ dw, float *__restrict__ dq,
     int32_t *__restrict__ gl_i, float *__restrict__ gl_g, int64_t T, int H, int n, int k, int d_k)
 {
@@ -882,7 +882,7 @@ __global__ __launch_bounds__(kQryWaves *kWave) void bwd_query_kernel(
     wave_lds_sync();
 
     const int passes = k <= kWave / 2 ? 1 : 2;
-    const DT *kh = keys + (int64_t)h * 2 * n * half;
+    const DT *kh = keys + h * key_hstride;
     const __amdgpu_buffer_rsrc_t rsrc = buffer_over(kh, 2 * n * half * (int)sizeof(DT));
     constexpr int kOut = 0x40000000;      // an offset past any codebook: reads zeros
     // byte offset of this lane's 4 elements in a sub-key row (kOut past the
@@ -1370,14 +1370,20 @@ __global__ __launch_bounds__(kDkWaves *kWave) void dkeys_mfma_kernel(
     }
 }
 
+// dkeys = the token blocks' partials summed in block order; with shared
+// codebooks (fold = H) also over the heads, head by head within each block:
+// dkeys[s][i][c] = sum_b sum_h partial[b][h][s][i][c] (count = one block's
+// partial, H * 2 * n * half).
 __global__ void dkeys_reduce_kernel(const float *__restrict__ partial, int blocks, int64_t count,
-                                    float *__restrict__ dkeys)
+                                    int fold, float *__restrict__ dkeys)
 {
+    const int64_t out = count / fold;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < count; e += stride) {
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < out; e += stride) {
         float acc = 0.f;
         for (int b = 0; b < blocks; ++b)
-            acc += partial[(int64_t)b * count + e];
+            for (int h = 0; h < fold; ++h)
+                acc += partial[(int64_t)b * count + h * out + e];
         dkeys[e] = acc;
     }
 }
@@ -1528,10 +1534,10 @@ hipError_t launch_bwd_value_sgd(int dtype, void *values, const int32_t *idx, con
 }
 
 template <typename DT>
-static hipError_t launch_query_t(const void *q, const void *keys, const int32_t *idx,
-                                 const float *weights, const float *dw, float *dq, float *dkeys,
-                                 int64_t T, int H, int n, int k, int d_k, void *scratch,
-                                 hipStream_t stream)
+static hipError_t launch_query_t(const void *q, const void *keys, int64_t key_hstride,
+                                 bool keys_shared, const int32_t *idx, const float *weights,
+                                 const float *dw, float *dq, float *dkeys, int64_t T, int H, int n,
+                                 int k, int d_k, void *scratch, hipStream_t stream)
 {
     const BwdQueryScratch S = bwd_query_scratch(T, H, n, k, d_k);
     char *base = static_cast<char *>(scratch);
@@ -1541,11 +1547,11 @@ static hipError_t launch_query_t(const void *q, const void *keys, const int32_t 
     const int64_t rows = T * H;
     if (d_k / 2 <= 4 * kWave)
         hipLaunchKernelGGL((bwd_query_kernel<DT, 1>), dim3(grid1d(rows, kQryWaves)),
-                           dim3(kQryWaves * kWave), 0, stream, static_cast<const DT *>(keys), idx,
+                           dim3(kQryWaves * kWave), 0, stream, static_cast<const DT *>(keys), key_hstride, idx,
                            weights, dw, dq, gl_i, gl_g, T, H, n, k, d_k);
     else
         hipLaunchKernelGGL((bwd_query_kernel<DT, 2>), dim3(grid1d(rows, kQryWaves)),
-                           dim3(kQryWaves * kWave), 0, stream, static_cast<const DT *>(keys), idx,
+                           dim3(kQryWaves * kWave), 0, stream, static_cast<const DT *>(keys), key_hstride, idx,
                            weights, dw, dq, gl_i, gl_g, T, H, n, k, d_k);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
@@ -1581,22 +1587,23 @@ static hipError_t launch_query_t(const void *q, const void *keys, const int32_t 
     if (err != hipSuccess)
         return err;
     const int64_t count = (int64_t)H * 2 * n * half;
-    const int64_t rblocks = grid1d(count, 256);
+    const int fold = keys_shared ? H : 1;
+    const int64_t rblocks = grid1d(count / fold, 256);
     hipLaunchKernelGGL(dkeys_reduce_kernel, dim3((unsigned)(rblocks < 8192 ? rblocks : 8192)),
-                       dim3(256), 0, stream, partial, S.blocks, count, dkeys);
+                       dim3(256), 0, stream, partial, S.blocks, count, fold, dkeys);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_query(int dtype, const void *q, const void *keys, const int32_t *idx,
-                            const float *weights, const float *dw, float *dq, float *dkeys,
-                            int64_t T, int H, int n, int k, int d_k, void *scratch,
-                            hipStream_t stream)
+hipError_t launch_bwd_query(int dtype, const void *q, const void *keys, int64_t key_hstride,
+                            bool keys_shared, const int32_t *idx, const float *weights,
+                            const float *dw, float *dq, float *dkeys, int64_t T, int H, int n,
+                            int k, int d_k, void *scratch, hipStream_t stream)
 {
     if (dtype == 1)
-        return launch_query_t<bf16_t>(q, keys, idx, weights, dw, dq, dkeys, T, H, n, k, d_k,
-                                      scratch, stream);
-    return launch_query_t<float>(q, keys, idx, weights, dw, dq, dkeys, T, H, n, k, d_k, scratch,
-                                 stream);
+        return launch_query_t<bf16_t>(q, keys, key_hstride, keys_shared, idx, weights, dw, dq,
+                                      dkeys, T, H, n, k, d_k, scratch, stream);
+    return launch_query_t<float>(q, keys, key_hstride, keys_shared, idx, weights, dw, dq, dkeys,
+                                 T, H, n, k, d_k, scratch, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -50,12 +50,21 @@ inline size_t select_workspace_bytes(int64_t T, int H, int n, int k, int dtype, 
 // Forward selection: sub-key scoring (MFMA), exact per-half top-k, pruned
 // k x k combine, softmax.  Writes idx / weights / scores [T][H][k].
 // `workspace` holds select_workspace_bytes(...) bytes.
-hipError_t launch_fwd_select(int dtype, const void *q, const void *keys, int64_t T, int H,
-                             int n, int k, int d_k, int32_t *idx, float *weights,
-                             float *scores, void *workspace, hipStream_t stream);
-hipError_t launch_select_fast(const void *q, const void *keys, int64_t T, int H, int n, int k,
-                              int d_k, int32_t *idx, float *weights, float *scores,
-                              void *workspace, hipStream_t stream);
+// keys of head h start key_hstride elements after those of head h - 1 (0:
+// one codebook pair shared by every head).
+hipError_t launch_fwd_select(int dtype, const void *q, const void *keys, int64_t key_hstride,
+                             int64_t T, int H, int n, int k, int d_k, int32_t *idx,
+                             float *weights, float *scores, void *workspace, hipStream_t stream);
+hipError_t launch_select_fast(const void *q, const void *keys, int64_t key_hstride, int64_t T,
+                              int H, int n, int k, int d_k, int32_t *idx, float *weights,
+                              float *scores, void *workspace, hipStream_t stream);
+
+// The flat-key search: all n*n implied keys of each (token, head) scored
+// with one d_k-wide dot product, exact top-k, softmax (bf16, d_k = 512,
+// 32 <= n <= 1024, k <= 32).
+hipError_t launch_flat_select(const void *q, const void *keys, int64_t key_hstride, int64_t T,
+                              int H, int n, int k, int32_t *idx, float *weights, float *scores,
+                              hipStream_t stream);
 
 // y[t] = sum over the H*k picks of token t of weight * values[slot].
 hipError_t launch_fwd_gather(int dtype, const void *values, const int32_t *idx,
@@ -107,11 +116,13 @@ __host__ __device__ inline int32_t *long_list(float *split, int64_t picks, int d
 
 // Query side: softmax backward per distinct sub-key, dq (overwritten) and
 // dkeys (overwritten) from weights and dw.  `scratch` holds
-// bwd_query_scratch(T, H, n, k, d_k).total bytes.
-hipError_t launch_bwd_query(int dtype, const void *q, const void *keys, const int32_t *idx,
-                            const float *weights, const float *dw, float *dq, float *dkeys,
-                            int64_t T, int H, int n, int k, int d_k, void *scratch,
-                            hipStream_t stream);
+// bwd_query_scratch(T, H, n, k, d_k).total bytes.  keys_shared: every head
+// reads one codebook pair (key_hstride 0) and dkeys [2][n][d_k/2] sums the
+// heads' gradients.
+hipError_t launch_bwd_query(int dtype, const void *q, const void *keys, int64_t key_hstride,
+                            bool keys_shared, const int32_t *idx, const float *weights,
+                            const float *dw, float *dq, float *dkeys, int64_t T, int H, int n,
+                            int k, int d_k, void *scratch, hipStream_t stream);
 
 // Fill `count` floats with zero (a kernel, so it can sit inside a captured graph).
 hipError_t launch_zero_f32(float *p, int64_t count, hipStream_t stream);

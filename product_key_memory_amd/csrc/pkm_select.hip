@@ -211,8 +211,8 @@ __device__ __forceinline__ void merge_row(const float *ls, const int *li, const 
 
 template <typename DT>
 __global__ __launch_bounds__(kSelThreads) void fwd_select_kernel(
-    const DT *__restrict__ q, const DT *__restrict__ keys, int64_t T, int H, int n, int k,
-    int d_k, SelLayout L, int32_t *__restrict__ idx, float *__restrict__ weights,
+    const DT *__restrict__ q, const DT *__restrict__ keys, int64_t key_hstride, int64_t T, int H,
+    int n, int k, int d_k, SelLayout L, int32_t *__restrict__ idx, float *__restrict__ weights,
     float *__restrict__ scores)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kSelThreads) void fwd_select_kernel(
         }
         __syncthreads();
 
-        const DT *kbase = keys + ((int64_t)h * 2 + s) * (int64_t)n * half;
+        const DT *kbase = keys + h * key_hstride + (int64_t)s * n * half;
         const int ntiles = (n + 15) / 16;
         for (int tile = wave; tile < ntiles; tile += kSelWaves) {
             const floatx4 acc = score_tile(kbase, n, half, qt, L.q_stride, tile);
@@ -300,9 +300,9 @@ __global__ __launch_bounds__(kSelThreads) void fwd_select_kernel(
 }
 
 template <typename DT>
-static hipError_t launch_select_t(const void *q, const void *keys, int64_t T, int H, int n,
-                                  int k, int d_k, int32_t *idx, float *weights, float *scores,
-                                  hipStream_t stream)
+static hipError_t launch_select_t(const void *q, const void *keys, int64_t key_hstride, int64_t T,
+                                  int H, int n, int k, int d_k, int32_t *idx, float *weights,
+                                  float *scores, hipStream_t stream)
 {
     const SelLayout L = sel_layout(n, k, d_k / 2, (int)sizeof(DT));
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_select_kernel<DT>),
@@ -311,21 +311,23 @@ static hipError_t launch_select_t(const void *q, const void *keys, int64_t T, in
         return err;
     const dim3 grid((unsigned)((T + kSelTokens - 1) / kSelTokens), (unsigned)H);
     hipLaunchKernelGGL(fwd_select_kernel<DT>, grid, dim3(kSelThreads), L.total, stream,
-                       static_cast<const DT *>(q), static_cast<const DT *>(keys), T, H, n, k,
-                       d_k, L, idx, weights, scores);
+                       static_cast<const DT *>(q), static_cast<const DT *>(keys), key_hstride, T,
+                       H, n, k, d_k, L, idx, weights, scores);
     return hipGetLastError();
 }
 
-hipError_t launch_fwd_select(int dtype, const void *q, const void *keys, int64_t T, int H,
-                             int n, int k, int d_k, int32_t *idx, float *weights,
-                             float *scores, void *workspace, hipStream_t stream)
+hipError_t launch_fwd_select(int dtype, const void *q, const void *keys, int64_t key_hstride,
+                             int64_t T, int H, int n, int k, int d_k, int32_t *idx,
+                             float *weights, float *scores, void *workspace, hipStream_t stream)
 {
     if (select_fast_ok(dtype, n, k, d_k))
-        return launch_select_fast(q, keys, T, H, n, k, d_k, idx, weights, scores, workspace,
-                                  stream);
+        return launch_select_fast(q, keys, key_hstride, T, H, n, k, d_k, idx, weights, scores,
+                                  workspace, stream);
     if (dtype == 1)
-        return launch_select_t<bf16_t>(q, keys, T, H, n, k, d_k, idx, weights, scores, stream);
-    return launch_select_t<float>(q, keys, T, H, n, k, d_k, idx, weights, scores, stream);
+        return launch_select_t<bf16_t>(q, keys, key_hstride, T, H, n, k, d_k, idx, weights,
+                                       scores, stream);
+    return launch_select_t<float>(q, keys, key_hstride, T, H, n, k, d_k, idx, weights, scores,
+                                  stream);
 }
 
 }  // namespace pkm

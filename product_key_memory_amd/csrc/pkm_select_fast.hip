@@ -137,8 +137,8 @@ template <int BLOCKS>
 // wave hides (measured: 0.186 -> 0.177 ms for the selection at n = 512, and
 // 0.61 -> 0.58 ms at n = 1024).
 __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_eu(3, 3))) void fwd_topk_half_kernel(
-    const bf16_t *__restrict__ q, const bf16_t *__restrict__ keys, int64_t T, int H, int n,
-    int k, uint2 *__restrict__ lists)
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ keys, int64_t key_hstride, int64_t T,
+    int H, int n, int k, uint2 *__restrict__ lists)
 {
     // the codebook steps during the scoring, the survivors afterwards
     constexpr int kSurvUnits = 2 * kFastWaves * kFastTok * kSurvStride * 4 / 16;
@@ -165,7 +165,8 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
     const uint16_t *qrow = reinterpret_cast<const uint16_t *>(q) +
                            ((live ? t : 0) * H + h) * (int64_t)d_k + (int64_t)s * half;
     const int tid0 = threadIdx.x;
-    const uint16_t *kb = reinterpret_cast<const uint16_t *>(keys) + ((int64_t)h * 2 + s) * (int64_t)n * half;
+    const uint16_t *kb =
+        reinterpret_cast<const uint16_t *>(keys) + h * key_hstride + (int64_t)s * n * half;
 
     // one block of sub-keys; straight-line code for each block (a loop over
     // the blocks kept values alive across its back edge and cost a wave per
@@ -622,21 +623,21 @@ static int merge_bound_size(int k)
             return m;
 }
 
-hipError_t launch_select_fast(const void *q, const void *keys, int64_t T, int H, int n, int k,
-                              int d_k, int32_t *idx, float *weights, float *scores,
-                              void *workspace, hipStream_t stream)
+hipError_t launch_select_fast(const void *q, const void *keys, int64_t key_hstride, int64_t T,
+                              int H, int n, int k, int d_k, int32_t *idx, float *weights,
+                              float *scores, void *workspace, hipStream_t stream)
 {
     (void)d_k;      // 512 on this path
     uint2 *lists = static_cast<uint2 *>(workspace);
     const dim3 grid((unsigned)((T + kFastTokWG - 1) / kFastTokWG), (unsigned)H, 2);
     if (n <= kFastBlock)
         hipLaunchKernelGGL(fwd_topk_half_kernel<1>, grid, dim3(kFastWaves * kWave), 0, stream,
-                           static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(keys), T, H,
-                           n, k, lists);
+                           static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(keys),
+                           key_hstride, T, H, n, k, lists);
     else
         hipLaunchKernelGGL(fwd_topk_half_kernel<2>, grid, dim3(kFastWaves * kWave), 0, stream,
-                           static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(keys), T, H,
-                           n, k, lists);
+                           static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(keys),
+                           key_hstride, T, H, n, k, lists);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;

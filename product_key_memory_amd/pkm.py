@@ -18,10 +18,12 @@ def pkm_status_string(code: int) -> str:
     return _lib.status_string(code)
 
 
-def problem(T, H, n, k, d_k, d_v, dtype) -> Problem:
+def problem(T, H, n, k, d_k, d_v, dtype, keys_shared: bool = False) -> Problem:
     code = _DTYPES.get(dtype, dtype) if isinstance(dtype, torch.dtype) else dtype
     if isinstance(code, torch.dtype):
         raise TypeError(f"unsupported dtype {dtype}")
+    if keys_shared:
+        code = int(code) | _lib.PKM_KEYS_SHARED
     return Problem(int(T), int(H), int(n), int(k), int(d_k), int(d_v), int(code))
 
 
@@ -51,28 +53,36 @@ def _stream(device) -> int:
 
 
 def _shapes(q, keys, values):
-    if q.dim() != 3 or keys.dim() != 4 or values.dim() != 2:
-        raise ValueError("expected q [T,H,d_k], keys [H,2,n,d_k/2], values [n*n,d_v]")
+    """Sizes, and whether the codebooks are shared by the heads: keys
+    [H, 2, n, d_k/2] (one pair per head) or [2, n, d_k/2] (one pair for all)."""
+    if q.dim() != 3 or keys.dim() not in (3, 4) or values.dim() != 2:
+        raise ValueError("expected q [T,H,d_k], keys [H,2,n,d_k/2] or [2,n,d_k/2], "
+                         "values [n*n,d_v]")
     T, H, d_k = q.shape
-    n = keys.shape[2]
+    shared = keys.dim() == 3
+    n = keys.shape[-2]
     d_v = values.shape[1]
     if q.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {q.dtype}")
     if q.device.type != "cuda":
         raise ValueError("tensors must be on a GPU")
-    return T, H, n, d_k, d_v
+    return T, H, n, d_k, d_v, shared
+
+
+def _keys_shape(H, n, d_k, shared):
+    return (2, n, d_k // 2) if shared else (H, 2, n, d_k // 2)
 
 
 def pkm_forward(q: torch.Tensor, keys: torch.Tensor, values: torch.Tensor, k: int,
                 want_scores: bool = True, out=None):
     """Forward pass.  Returns (y [T,d_v] in q.dtype, idx [T,H,k] int32,
     weights [T,H,k] float32, scores [T,H,k] float32 or None)."""
-    T, H, n, d_k, d_v = _shapes(q, keys, values)
+    T, H, n, d_k, d_v, shared = _shapes(q, keys, values)
     dev, dt = q.device, q.dtype
     _check(q, "q", (T, H, d_k), dt, dev)
-    _check(keys, "keys", (H, 2, n, d_k // 2), dt, dev)
+    _check(keys, "keys", _keys_shape(H, n, d_k, shared), dt, dev)
     _check(values, "values", (n * n, d_v), dt, dev)
-    p = problem(T, H, n, k, d_k, d_v, dt)
+    p = problem(T, H, n, k, d_k, d_v, dt, shared)
     ws_bytes = pkm_workspace_bytes(p, False)
     if ws_bytes == (1 << 64) - 1:
         raise PKMError(2, "pkm_forward")
@@ -91,6 +101,30 @@ def pkm_forward(q: torch.Tensor, keys: torch.Tensor, values: torch.Tensor, k: in
     return y, idx, weights, scores
 
 
+def pkm_flat_forward(q: torch.Tensor, keys: torch.Tensor, values: torch.Tensor, k: int):
+    """The flat-key search over all n*n implied keys (pkm_flat_forward_select),
+    then the same gather as pkm_forward.  Returns (y, idx, weights, scores)
+    like pkm_forward.  bf16, d_k = 512, 32 <= n <= 1024, k <= 32."""
+    T, H, n, d_k, d_v, shared = _shapes(q, keys, values)
+    dev, dt = q.device, q.dtype
+    _check(q, "q", (T, H, d_k), dt, dev)
+    _check(keys, "keys", _keys_shape(H, n, d_k, shared), dt, dev)
+    _check(values, "values", (n * n, d_v), dt, dev)
+    p = problem(T, H, n, k, d_k, d_v, dt, shared)
+    y = torch.empty((T, d_v), dtype=dt, device=dev)
+    idx = torch.empty((T, H, k), dtype=torch.int32, device=dev)
+    weights = torch.empty((T, H, k), dtype=torch.float32, device=dev)
+    scores = torch.empty((T, H, k), dtype=torch.float32, device=dev)
+    rc = _lib.flat_forward_select(p, _ptr(q), _ptr(keys), _ptr(idx), _ptr(weights), _ptr(scores),
+                                  _stream(dev))
+    if rc != 0:
+        raise PKMError(rc, "pkm_flat_forward_select")
+    rc = _lib.forward_gather(p, _ptr(values), _ptr(idx), _ptr(weights), _ptr(y), _stream(dev))
+    if rc != 0:
+        raise PKMError(rc, "pkm_forward_gather")
+    return y, idx, weights, scores
+
+
 def pkm_backward(q: torch.Tensor, keys: torch.Tensor, values: torch.Tensor, idx: torch.Tensor,
                  weights: torch.Tensor, dy: torch.Tensor, dvalues: torch.Tensor | None = None,
                  out=None):
@@ -98,16 +132,16 @@ def pkm_backward(q: torch.Tensor, keys: torch.Tensor, values: torch.Tensor, idx:
     all float32.  A given dvalues is ACCUMULATED into (pkm_backward); otherwise
     a new one is returned, written whole by pkm_backward_overwrite (rows no pick
     selected are 0)."""
-    T, H, n, d_k, d_v = _shapes(q, keys, values)
+    T, H, n, d_k, d_v, shared = _shapes(q, keys, values)
     dev, dt = q.device, q.dtype
     k = idx.shape[2]
     _check(q, "q", (T, H, d_k), dt, dev)
-    _check(keys, "keys", (H, 2, n, d_k // 2), dt, dev)
+    _check(keys, "keys", _keys_shape(H, n, d_k, shared), dt, dev)
     _check(values, "values", (n * n, d_v), dt, dev)
     _check(idx, "idx", (T, H, k), torch.int32, dev)
     _check(weights, "weights", (T, H, k), torch.float32, dev)
     _check(dy, "dy", (T, d_v), dt, dev)
-    p = problem(T, H, n, k, d_k, d_v, dt)
+    p = problem(T, H, n, k, d_k, d_v, dt, shared)
     ws_bytes = pkm_workspace_bytes(p, True)
     if ws_bytes == (1 << 64) - 1:
         raise PKMError(2, "pkm_backward")
@@ -118,7 +152,7 @@ def pkm_backward(q: torch.Tensor, keys: torch.Tensor, values: torch.Tensor, idx:
         _check(dvalues, "dvalues", (n * n, d_v), torch.float32, dev)
     if out is None:
         dq = torch.empty((T, H, d_k), dtype=torch.float32, device=dev)
-        dkeys = torch.empty((H, 2, n, d_k // 2), dtype=torch.float32, device=dev)
+        dkeys = torch.empty(_keys_shape(H, n, d_k, shared), dtype=torch.float32, device=dev)
     else:
         dq, dkeys = out
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
@@ -138,22 +172,22 @@ def pkm_backward_sgd(q: torch.Tensor, keys: torch.Tensor, values: torch.Tensor,
     selected becomes fmaf(-lr, g, w) rounded once to the storage type, g being
     the row's float32 gradient (pkm_backward's dvalues row).  No dvalues array
     is formed."""
-    T, H, n, d_k, d_v = _shapes(q, keys, values)
+    T, H, n, d_k, d_v, shared = _shapes(q, keys, values)
     dev, dt = q.device, q.dtype
     k = idx.shape[2]
     _check(q, "q", (T, H, d_k), dt, dev)
-    _check(keys, "keys", (H, 2, n, d_k // 2), dt, dev)
+    _check(keys, "keys", _keys_shape(H, n, d_k, shared), dt, dev)
     _check(values, "values", (n * n, d_v), dt, dev)
     _check(idx, "idx", (T, H, k), torch.int32, dev)
     _check(weights, "weights", (T, H, k), torch.float32, dev)
     _check(dy, "dy", (T, d_v), dt, dev)
-    p = problem(T, H, n, k, d_k, d_v, dt)
+    p = problem(T, H, n, k, d_k, d_v, dt, shared)
     ws_bytes = pkm_workspace_bytes(p, 2)
     if ws_bytes == (1 << 64) - 1:
         raise PKMError(2, "pkm_backward_sgd")
     if out is None:
         dq = torch.empty((T, H, d_k), dtype=torch.float32, device=dev)
-        dkeys = torch.empty((H, 2, n, d_k // 2), dtype=torch.float32, device=dev)
+        dkeys = torch.empty(_keys_shape(H, n, d_k, shared), dtype=torch.float32, device=dev)
     else:
         dq, dkeys = out
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None

@@ -48,6 +48,27 @@ def test_forward_rejects_bad_shapes(kw, code):
     assert rc == code, _lib.STATUS.get(rc)
 
 
+def test_dtype_flags():
+    """dtype carries the storage type and the shared-codebook flag only."""
+    shared = _lib.PKM_KEYS_SHARED
+    assert _lib.workspace_bytes(P(dtype=1 | shared), True) == _lib.workspace_bytes(P(dtype=1), True)
+    assert _lib.workspace_bytes(P(dtype=1 | 0x200), True) == (1 << 64) - 1
+    assert _lib.forward(P(dtype=0x200), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 3
+    assert _lib.forward(P(dtype=2 | shared), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 3
+
+
+def test_flat_select_checks():
+    """The flat search: bf16 storage only, d_k = 512, n >= 32, k <= 32."""
+    ok = dict(d_k=512, n=64, k=8, dtype=1)
+    args = [FAKE, FAKE, FAKE, FAKE, None, None]
+    assert _lib.flat_forward_select(P(**{**ok, "dtype": 0}), *args) == 3
+    assert _lib.flat_forward_select(P(**{**ok, "d_k": 256}), *args) == 2
+    assert _lib.flat_forward_select(P(**{**ok, "n": 16}), *args) == 2
+    assert _lib.flat_forward_select(P(**{**ok, "k": 33}), *args) == 2
+    assert _lib.flat_forward_select(P(**ok), None, FAKE, FAKE, FAKE, None, None) == 1
+    assert _lib.flat_forward_select(P(**{**ok, "T": 0}), None, FAKE, None, None, None, None) == 0
+
+
 def test_null_and_alignment():
     assert _lib.forward(P(), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 1
     assert _lib.forward(P(), FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 6

@@ -58,8 +58,8 @@ constexpr int kMaxPairs = 128;                       // merge_candidates(32) = 1
 constexpr int kMergePitch = 2 * 32 + 1;
 
 // Scores of the wave's 16 tokens against the sub-keys 0..n_loc-1 of one block
-// (kb = its first row), as order-preserving integers: so[j][i] = ord(score of
-// sub-key 16 j + 4 g + i) for token `tok` (rows past n_loc score 0; the caller
+// (kb = its first row), as float32 bit patterns: so[j][i] = the score of
+// sub-key 16 j + 4 g + i for token `tok` (rows past n_loc score 0; the caller
 // masks them).  The workgroup's 4 waves (64 tokens)
 // share the codebook through LDS: per step p it holds rows 32 p .. 32 p + 31
 // (16 KB, double-buffered), each thread loading 4 of its 16-byte chunks, so
@@ -116,7 +116,7 @@ __device__ __forceinline__ void fast_scores(uint32_t (&so)[kFastTiles][4], const
         for (int w = 0; w < 2; ++w)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                so[2 * p + w][i] = ord_f32(acc[w][i]);
+                so[2 * p + w][i] = __float_as_uint(acc[w][i]);
         // step p + 1 goes to the other buffer (its readers finished at the
         // last barrier); step p + 2 is fetched while step p + 1 is worked on
         if (p + 1 < steps)
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
         if (n_loc < kFastBlock) {
             // sub-key 16 j + 4 g + i of the block exists iff 16 j + i < lim
             const int lim = n_loc - 4 * g;
-            const uint32_t neg = ord_f32(-INFINITY);
+            const uint32_t neg = __float_as_uint(-INFINITY);
 #pragma unroll
             for (int j = 0; j < kFastTiles; ++j)
 #pragma unroll
@@ -200,33 +200,36 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
                     so[j][i] = 16 * j + i < lim ? so[j][i] : neg;
         }
 
+        // The filter works on the float scores (compares, maxima); only the
+        // survivors become order-preserving keys, when they are read back.
+        auto sf = [&](int j, int i) { return __uint_as_float(so[j][i]); };
         // tau: k-th largest of the token's 64 group maxima (groups of 8 scores)
-        uint32_t gm[16];
+        float gm[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
-            uint32_t x = so[2 * m][0];
+            float x = sf(2 * m, 0);
 #pragma unroll
             for (int i = 1; i < 4; ++i)
-                x = max(x, so[2 * m][i]);
+                x = fmaxf(x, sf(2 * m, i));
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                x = max(x, so[2 * m + 1][i]);
+                x = fmaxf(x, sf(2 * m + 1, i));
             gm[m] = x;
         }
         group4_sort_desc<16>(gm);
-        uint32_t tau_src = gm[0];
+        float tau_src = gm[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r)
             if (r == ((k - 1) & 15))
                 tau_src = gm[r];
-        uint32_t tau = (uint32_t)__shfl((int)tau_src, tok + 16 * ((k - 1) >> 4));
+        float tau = __shfl(tau_src, tok + 16 * ((k - 1) >> 4));
         // A single block has n > 256 valid sub-keys, >= 33 groups of real
         // scores, so tau is a real score and the sub-keys past n never
         // survive.  A second block may hold fewer than k sub-keys: there the
         // first block's k-th key (a real score) raises the bar, and keys
         // below it cannot reach the top k anyway.
         if constexpr (!kFirst)
-            tau = max(tau, (uint32_t)(prev[k - 1] >> 32));
+            tau = fmaxf(tau, unord_f32((uint32_t)(prev[k - 1] >> 32)));
 
         // survivors: ord >= tau.  A token past T (it scored token 0's query)
         // keeps nothing: no count, no bisection, no compaction store that
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
         for (int j = 0; j < kFastTiles; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                cnt += so[j][i] >= tau ? 1 : 0;
+                cnt += sf(j, i) >= tau ? 1 : 0;
         if (!live)
             cnt = 0;
         int total = group4_sum(cnt);
@@ -246,8 +249,16 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
         // by bisection on the score bits and then on the index among exactly
         // tied scores (more than 64 survivors are real scores, so is the
         // k-th largest)
-        uint32_t kth = tau, tie_idx = 0xFFFFFFFFu;
-        if (__ballot(!fits) != 0) {
+        // (the whole wave then works on order-preserving keys: `ordm`)
+        const bool ordm = __ballot(!fits) != 0;
+        uint32_t kth = 0, tie_idx = 0xFFFFFFFFu;
+        if (ordm) {
+#pragma unroll
+            for (int j = 0; j < kFastTiles; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    so[j][i] = ord_f32(sf(j, i));
+            kth = ord_f32(tau);
             uint32_t K = 0;
             for (int bit = 31; bit >= 0; --bit) {
                 const uint32_t cand = K | (1u << bit);
@@ -298,7 +309,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
         const bool exact = tie_idx != 0xFFFFFFFFu;
         const int lim_t = exact ? (int)tie_idx - 4 * g : 0;   // 16 j + i <= lim_t among ties
         int mine = cnt;
-        if (exact) {
+        if (ordm && exact) {
             // recount this lane's share under the exact bound
             int c = 0;
 #pragma unroll
@@ -317,18 +328,32 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
         // ends the group's range.
         const int c0 = __shfl(mine, tok), c1 = __shfl(mine, tok + 16), c2 = __shfl(mine, tok + 32);
         int off = g + (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
+        if (ordm) {
 #pragma unroll
-        for (int j = 0; j < kFastTiles; ++j) {
+            for (int j = 0; j < kFastTiles; ++j) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t o = so[j][i];
-                const bool keep =
-                    live && (exact ? (o > kth || (o == kth && 16 * j + i <= lim_t)) : o >= kth);
-                surv_s[off] = o;
-                surv_i[off] = (uint32_t)(16 * j + i);
-                off += keep ? 1 : 0;
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t o = so[j][i];
+                    const bool keep =
+                        live && (exact ? (o > kth || (o == kth && 16 * j + i <= lim_t)) : o >= kth);
+                    surv_s[off] = o;
+                    surv_i[off] = (uint32_t)(16 * j + i);
+                    off += keep ? 1 : 0;
+                }
+                __builtin_amdgcn_sched_barrier(0);     // one tile's keys at a time
             }
-            __builtin_amdgcn_sched_barrier(0);     // one tile's keys at a time
+        } else {
+#pragma unroll
+            for (int j = 0; j < kFastTiles; ++j) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool keep = live && sf(j, i) >= tau;
+                    surv_s[off] = so[j][i];
+                    surv_i[off] = (uint32_t)(16 * j + i);
+                    off += keep ? 1 : 0;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         wave_lds_sync();
         const int b1 = c0, b2 = c0 + c1, b3 = c0 + c1 + c2;
@@ -338,7 +363,9 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
             // survivor e was written by lane group src_g, at position e + src_g
             const int e = 16 * g + r;
             const int src_g = (e >= b1 ? 1 : 0) + (e >= b2 ? 1 : 0) + (e >= b3 ? 1 : 0);
-            v[r] = e < total ? ((uint64_t)surv_s[e + src_g] << 32) |
+            const uint32_t sv = surv_s[e + src_g];
+            const uint32_t hi = ordm ? sv : ord_f32(__uint_as_float(sv));
+            v[r] = e < total ? ((uint64_t)hi << 32) |
                                    (uint64_t)~(surv_i[e + src_g] + 4u * (uint32_t)src_g + (uint32_t)base)
                              : 0ull;
         }

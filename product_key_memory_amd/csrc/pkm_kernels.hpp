@@ -34,11 +34,11 @@ inline int merge_candidates(int k)
 }
 
 // The two-kernel selection path: bf16 storage, query halves of exactly 256,
-// 256 < n <= 1024, k <= 32.  Its per-half top-k lists pass through the
+// 128 <= n <= 1024, k <= 32.  Its per-half top-k lists pass through the
 // workspace: [T][H][2][k] entries of (score bits, sub-key), 8 bytes each.
 inline bool select_fast_ok(int dtype, int n, int k, int d_k)
 {
-    return dtype == 1 && n > 256 && n <= 1024 && k <= 32 && d_k == 512;
+    return dtype == 1 && n >= 128 && n <= 1024 && k <= 32 && d_k == 512;
 }
 inline size_t select_workspace_bytes(int64_t T, int H, int n, int k, int dtype, int d_k)
 {

@@ -1,12 +1,12 @@
 // pkm_select_fast.hip -- forward selection for bf16 storage, query halves of
-// 256, 256 < n <= 1024, k <= 32, as two kernels (gptget.net summary of "Large
+// 256, 128 <= n <= 1024, k <= 32, as two kernels (gptget.net summary of "Large
 // Memory Layers with Product Keys", "Methodology": split q into q1, q2, search
 // each against its own sub-key set, combine the best sub-keys; companion page
 // "Why top-k of each half is enough").
 //
 // 1. fwd_topk_half_kernel: one wave per (16 tokens, head, half).  The
 //    codebook is scored in blocks of 512 sub-keys (one block for n <= 512,
-//    two for n <= 1024).  The wave computes its tokens' scores of a block
+//    two for n <= 1024; one of 256 for n <= 256).  The wave computes its tokens' scores of a block
 //    straight into registers with v_mfma_f32_16x16x32_bf16 (sub-keys as M,
 //    tokens as N): lane l holds, for token l % 16, the scores of sub-keys
 //    16 j + 4 (l / 16) + i of the block (tile j < 32, i < 4).  All selection
@@ -44,8 +44,8 @@ namespace pkm {
 constexpr int kFastWaves = 4;
 constexpr int kFastTok = 16;                         // tokens per wave
 constexpr int kFastTokWG = kFastWaves * kFastTok;    // tokens per workgroup
-constexpr int kFastTiles = 32;                       // 16-sub-key tiles per block
-constexpr int kFastBlock = 16 * kFastTiles;          // 512 sub-keys per block
+constexpr int kFastTiles = 32;                       // 16-sub-key tiles per block (at most)
+constexpr int kFastBlock = 16 * kFastTiles;          // 512 sub-keys per block (at most)
 constexpr int kFastKSteps = 8;                       // 32-wide K steps: half = 256
 constexpr int kFastSurv = 64;                        // survivors per token at most
 constexpr int kSurvStride = kFastSurv + 4;           // + one spare slot per lane group
@@ -68,7 +68,8 @@ constexpr int kMergePitch = 2 * 32 + 1;
 // rows an MFMA operand read touches (same chunk, rows r16 = 0..15) then fall
 // in distinct banks.  Within a step the two tiles' accumulation chains
 // alternate, so consecutive MFMAs do not wait on each other.
-__device__ __forceinline__ void fast_scores(uint32_t (&so)[kFastTiles][4], const uint16_t *kb,
+template <int TILES>
+__device__ __forceinline__ void fast_scores(uint32_t (&so)[TILES][4], const uint16_t *kb,
                                             const uint4 (&qf)[kFastKSteps], int n_loc, int r16,
                                             int g, uint4 *kbuf, int tid)
 {
@@ -76,7 +77,7 @@ __device__ __forceinline__ void fast_scores(uint32_t (&so)[kFastTiles][4], const
     constexpr int chunks = half * 2 / 16;            // 32 chunks of 16 bytes per row
     constexpr int step_units = 32 * chunks;          // 1024 chunks per 32-row step
     constexpr int per_thread = step_units / (kFastWaves * kWave);
-    constexpr int steps = kFastTiles / 2;
+    constexpr int steps = TILES / 2;
     // rows past n_loc read as zeros
     const __amdgpu_buffer_rsrc_t rsrc = buffer_over(kb, n_loc * half * 2);
     uint4 pre[per_thread];
@@ -128,10 +129,14 @@ __device__ __forceinline__ void fast_scores(uint32_t (&so)[kFastTiles][4], const
 }
 
 // lists[((t H + h) 2 + s) k + e] = (ord score, sub-key) of the e-th best
-// sub-key of half s, e < k.  BLOCKS = number of 512-sub-key blocks (1: n <= 512,
-// 2: n <= 1024), a template argument so that each case gets its own register
-// allocation.
-template <int BLOCKS>
+// sub-key of half s, e < k.  BLOCKS (1 or 2) blocks of TILES x 16 sub-keys
+// (TILES = 8, 16, 32: 128, 256, 512 sub-keys); the group maxima are over
+// groups of TILES / 4 scores, 64 groups per token.  The launcher picks the
+// shape so that the first block is more than 3/4 full (at least 48 real
+// groups, so tau is a real score and about k + 10 survive), the second
+// block, if any, holding the rest: template arguments so that each case
+// gets its own register allocation.
+template <int BLOCKS, int TILES>
 // Three waves per SIMD: the register budget (168) makes the compiler spill a
 // few dozen registers to scratch, which costs less than the latency a third
 // wave hides (measured: 0.186 -> 0.177 ms for the selection at n = 512, and
@@ -179,22 +184,22 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
         // block to the next
         int g = g_lane, tid = tid0;
         asm volatile("" : "+v"(g), "+v"(tid));
-        const int base = kFirst ? 0 : kFastBlock;
-        const int n_loc = n - base < kFastBlock ? n - base : kFastBlock;
+        const int base = kFirst ? 0 : (16 * TILES);
+        const int n_loc = n - base < (16 * TILES) ? n - base : (16 * TILES);
         // B fragments: token `tok`, K slice 32 kk + 8 g .. + 7 (loaded per
         // block, so they are not held through the selection)
         uint4 qf[kFastKSteps];
 #pragma unroll
         for (int kk = 0; kk < kFastKSteps; ++kk)
             qf[kk] = *reinterpret_cast<const uint4 *>(qrow + 32 * kk + 8 * g);
-        uint32_t so[kFastTiles][4];
+        uint32_t so[TILES][4];
         fast_scores(so, kb + (int64_t)base * half, qf, n_loc, tok, g, lds, tid);
-        if (n_loc < kFastBlock) {
+        if (n_loc < (16 * TILES)) {
             // sub-key 16 j + 4 g + i of the block exists iff 16 j + i < lim
             const int lim = n_loc - 4 * g;
             const uint32_t neg = __float_as_uint(-INFINITY);
 #pragma unroll
-            for (int j = 0; j < kFastTiles; ++j)
+            for (int j = 0; j < TILES; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     so[j][i] = 16 * j + i < lim ? so[j][i] : neg;
@@ -203,17 +208,16 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
         // The filter works on the float scores (compares, maxima); only the
         // survivors become order-preserving keys, when they are read back.
         auto sf = [&](int j, int i) { return __uint_as_float(so[j][i]); };
-        // tau: k-th largest of the token's 64 group maxima (groups of 8 scores)
+        // tau: k-th largest of the token's 64 group maxima (a lane's scores
+        // 4 j + i in groups of SPG = TILES / 4 consecutive ones)
+        constexpr int SPG = TILES / 4;
         float gm[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
-            float x = sf(2 * m, 0);
+            float x = sf((SPG * m) / 4, (SPG * m) % 4);
 #pragma unroll
-            for (int i = 1; i < 4; ++i)
-                x = fmaxf(x, sf(2 * m, i));
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                x = fmaxf(x, sf(2 * m + 1, i));
+            for (int e = SPG * m + 1; e < SPG * (m + 1); ++e)
+                x = fmaxf(x, sf(e / 4, e % 4));
             gm[m] = x;
         }
         group4_sort_desc<16>(gm);
@@ -223,9 +227,8 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
             if (r == ((k - 1) & 15))
                 tau_src = gm[r];
         float tau = __shfl(tau_src, tok + 16 * ((k - 1) >> 4));
-        // A single block has n > 256 valid sub-keys, >= 33 groups of real
-        // scores, so tau is a real score and the sub-keys past n never
-        // survive.  A second block may hold fewer than k sub-keys: there the
+        // A first block is more than 3/4 full, >= 48 groups of real scores,
+        // so tau is a real score and the sub-keys past n never survive.  A second block may hold fewer than k sub-keys: there the
         // first block's k-th key (a real score) raises the bar, and keys
         // below it cannot reach the top k anyway.
         if constexpr (!kFirst)
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
         // claims a position -- its 4 lanes share `live`, so total = 0
         int cnt = 0;
 #pragma unroll
-        for (int j = 0; j < kFastTiles; ++j)
+        for (int j = 0; j < TILES; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 cnt += sf(j, i) >= tau ? 1 : 0;
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
         uint32_t kth = 0, tie_idx = 0xFFFFFFFFu;
         if (ordm) {
 #pragma unroll
-            for (int j = 0; j < kFastTiles; ++j)
+            for (int j = 0; j < TILES; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     so[j][i] = ord_f32(sf(j, i));
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
                 const uint32_t cand = K | (1u << bit);
                 int c = 0;
 #pragma unroll
-                for (int j = 0; j < kFastTiles; ++j)
+                for (int j = 0; j < TILES; ++j)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         c += so[j][i] >= cand ? 1 : 0;
@@ -273,7 +276,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
             }
             int above = 0;
 #pragma unroll
-            for (int j = 0; j < kFastTiles; ++j)
+            for (int j = 0; j < TILES; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     above += so[j][i] > K ? 1 : 0;
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
                 const int lim_c = (int)cand - 4 * g;
                 int c = 0;
 #pragma unroll
-                for (int j = 0; j < kFastTiles; ++j)
+                for (int j = 0; j < TILES; ++j)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         c += (so[j][i] == K && 16 * j + i < lim_c) ? 1 : 0;
@@ -313,7 +316,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
             // recount this lane's share under the exact bound
             int c = 0;
 #pragma unroll
-            for (int j = 0; j < kFastTiles; ++j)
+            for (int j = 0; j < TILES; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t o = so[j][i];
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
         int off = g + (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
         if (ordm) {
 #pragma unroll
-            for (int j = 0; j < kFastTiles; ++j) {
+            for (int j = 0; j < TILES; ++j) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t o = so[j][i];
@@ -344,7 +347,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < kFastTiles; ++j) {
+            for (int j = 0; j < TILES; ++j) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const bool keep = live && sf(j, i) >= tau;
@@ -657,14 +660,24 @@ hipError_t launch_select_fast(const void *q, const void *keys, int64_t key_hstri
     (void)d_k;      // 512 on this path
     uint2 *lists = static_cast<uint2 *>(workspace);
     const dim3 grid((unsigned)((T + kFastTokWG - 1) / kFastTokWG), (unsigned)H, 2);
-    if (n <= kFastBlock)
-        hipLaunchKernelGGL(fwd_topk_half_kernel<1>, grid, dim3(kFastWaves * kWave), 0, stream,
+    // block shapes: the first block more than 3/4 full
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(kFastWaves * kWave), 0, stream,
                            static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(keys),
                            key_hstride, T, H, n, k, lists);
+    };
+    if (n <= 128)
+        go(fwd_topk_half_kernel<1, 8>);
+    else if (n <= 192)
+        go(fwd_topk_half_kernel<2, 8>);
+    else if (n <= 256)
+        go(fwd_topk_half_kernel<1, 16>);
+    else if (n <= 384)
+        go(fwd_topk_half_kernel<2, 16>);
+    else if (n <= 512)
+        go(fwd_topk_half_kernel<1, 32>);
     else
-        hipLaunchKernelGGL(fwd_topk_half_kernel<2>, grid, dim3(kFastWaves * kWave), 0, stream,
-                           static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(keys),
-                           key_hstride, T, H, n, k, lists);
+        go(fwd_topk_half_kernel<2, 32>);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;

@@ -110,9 +110,13 @@ def test_edge(orc, case, dtype):
     assert rep["rows"] == T * H
 
 
-# the two-kernel selection (bf16, d_k = 512, 256 < n <= 1024, k <= 32): per-half
-# top-k over blocks of 512 sub-keys, then the pruned combine
+# the two-kernel selection (bf16, d_k = 512, 128 <= n <= 1024, k <= 32): per-half
+# top-k over blocks of 512 sub-keys (256 for n <= 256), then the pruned combine
 FAST_EDGE = [
+    (50, 2, 128, 16, 512, 16, "normal"),      # smallest n on the path: 256-sub-key blocks, groups of 4
+    (37, 3, 200, 32, 512, 24, "dup"),         # ragged n in a 256-block, duplicated sub-keys
+    (20, 1, 256, 32, 512, 16, "right_zero"),  # all right scores tie in a 256-block: exact bisection
+    (33, 2, 130, 7, 512, 16, "integer"),      # exact arithmetic in a 256-block
     # T,  H, n,    k,  d_k, d_v, kind
     (100, 3, 300, 20, 512, 24, "normal"),      # ragged T and n, k < 32
     (70, 2, 257, 32, 512, 16, "normal"),       # smallest n on the path: one sub-key in the last tile
@@ -153,7 +157,7 @@ def test_edge_two_kernel_selection(orc, case):
 # (more than 64 survivors in both halves): the lanes past T must keep nothing,
 # also in waves whose live tokens need no bisection and in waves with no live
 # token at all, and must not disturb the live tokens' survivors.
-TAIL_CASES = [(65, 512), (100, 512), (112, 512), (100, 1024)]
+TAIL_CASES = [(65, 512), (100, 512), (112, 512), (100, 1024), (100, 200)]
 
 
 @pytest.mark.parametrize("T,n", TAIL_CASES, ids=[f"T{c[0]}n{c[1]}" for c in TAIL_CASES])

@@ -49,6 +49,15 @@ def parse():
                          "256, 512 at the workload's other shapes, --flat-tokens tokens; one JSON "
                          "line per n")
     ap.add_argument("--flat-tokens", type=int, default=4096)
+    ap.add_argument("--record-counters", nargs=4, metavar=("PMC_A", "PMC_B", "PMC_DRAM", "TRACE"),
+                    help="no GPU work: read the csv output directories of the three rocprofv3 "
+                         "--pmc passes (COUNTER_PASSES) and of a --kernel-trace pass of this "
+                         "bench, and write the per-kernel counter table to "
+                         "profiles/pkm_counters_<workload>.md")
+    ap.add_argument("--record-layer", nargs=2, metavar=("TRACE", "BENCH_LOG"),
+                    help="no GPU work: from the csv output directory of a rocprofv3 "
+                         "--kernel-trace --stats pass of this bench, the recorded traffic and "
+                         "the log of a plain run, write profiles/pkm_layer_<workload>.md")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="no GPU work: read the rocprofv3 databases of a FETCH_SIZE run and a "
                          "WRITE_SIZE run of `bench.py --calibrate-copy`, and write the "
@@ -196,6 +205,205 @@ def record_traffic(fetch_db: str, write_db: str, workload: str) -> str:
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     return path
+
+
+# The two counter passes --record-counters reads (each within one pass's
+# limits: at most 8 SQ and 4 TCC counters).  Work counters (instructions,
+# busy cycles, hits) do not depend on the pass's timing; the durations come
+# from a kernel-trace pass of its own, and every rate is taken against the
+# nominal peak clock, 2.4 GHz: no clock is derived from the counters.
+COUNTER_PASSES = {
+    "A": ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS",
+          "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR"],
+    "B": ["SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+          "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "TCC_HIT_sum", "TCC_MISS_sum"],
+    # L2 requests to the DRAM address space, in 32-byte units
+    "DRAM": ["TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"],
+}
+PEAK_CLOCK_HZ = 2.4e9
+SIMDS = 1024
+
+
+def _short_name(name: str) -> str:
+    return name.split("(")[0].replace("void ", "").replace("pkm::", "").strip()
+
+
+def _csv_rows(directory: str, suffix: str) -> list:
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True)):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def record_counters(pmc_a: str, pmc_b: str, pmc_dram: str, trace: str, workload: str) -> str:
+    """Per kernel: mean duration of its dispatches in the trace pass; means of
+    the counters per dispatch in the two counter passes; rates against
+    1024 SIMDs x duration x 2.4 GHz."""
+    dur, calls = {}, {}
+    for r in _csv_rows(trace, "kernel_trace.csv"):
+        k = _short_name(r["Kernel_Name"])
+        dur.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    cnt = {}
+    for d in (pmc_a, pmc_b, pmc_dram):
+        per = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            key = (_short_name(r["Kernel_Name"]), r["Dispatch_Id"])
+            per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+            per[key]["_grid"] = int(r["Grid_Size"])
+        for (k, _), vals in per.items():
+            acc = cnt.setdefault(k, {})
+            for name, v in vals.items():
+                acc.setdefault(name, []).append(v)
+    lines = []
+    for k in sorted(dur, key=lambda k: -sum(dur[k]) / len(dur[k])):
+        t = sum(dur[k]) / len(dur[k])
+        c = {name: sum(v) / len(v) for name, v in cnt.get(k, {}).items()}
+        if "SQ_WAVES" not in c or t < 5e-6:
+            continue
+        cap = SIMDS * t * PEAK_CLOCK_HZ
+        waves = max(c["SQ_WAVES"], 1.0)
+        lds = c.get("SQ_ACTIVE_INST_LDS", 0.0)
+        hits, miss = c.get("TCC_HIT_sum", 0.0), c.get("TCC_MISS_sum", 0.0)
+        rd = 32 * c.get("TCC_EA0_RDREQ_DRAM_32B_sum", 0.0)
+        wr = 32 * c.get("TCC_EA0_WRREQ_WRITE_DRAM_32B_sum", 0.0)
+        lines.append("| `%s` | %d | %.1f | %.1f | %.1f | %d | %d | %d | %d | %s | %s | %.3f | %.3f | %.2f |" % (
+            k, c.get("_grid", 0), t * 1e6,
+            100 * c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / cap,
+            100 * 4 * c.get("SQ_INSTS_VALU", 0.0) / cap,
+            round(c.get("SQ_INSTS_VALU", 0.0) / waves), round(c.get("SQ_INSTS_MFMA", 0.0) / waves),
+            round(c.get("SQ_INSTS_LDS", 0.0) / waves), round(c.get("SQ_INSTS_SALU", 0.0) / waves),
+            "%.2f" % (c.get("SQ_LDS_BANK_CONFLICT", 0.0) / lds) if lds else "-",
+            "%.1f" % (100 * hits / (hits + miss)) if hits + miss else "-",
+            rd / 1e9, wr / 1e9, (rd + wr) / t / 1e12))
+    out = os.path.join(PROFILES, f"pkm_counters_{workload}.md")
+    with open(out, "w") as f:
+        f.write(COUNTERS_HEADER.format(workload=workload,
+                                       a=" ".join(COUNTER_PASSES["A"]), b=" ".join(COUNTER_PASSES["B"]),
+                                       dram=" ".join(COUNTER_PASSES["DRAM"])))
+        f.write("\n".join(lines) + "\n")
+    return out
+
+
+def record_layer(trace: str, bench_log: str, workload: str, steps: int, warmup: int) -> str:
+    """Kernel table of the trace pass (kernel_stats.csv), the traffic per
+    stage from the recorded FETCH_SIZE / WRITE_SIZE runs, and the JSON line
+    of a plain run."""
+    stats = _csv_rows(trace, "kernel_stats.csv")
+    total = sum(float(r["TotalDurationNs"]) for r in stats) or 1.0
+    rows = []
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        share = 100 * float(r["TotalDurationNs"]) / total
+        if share < 0.05:
+            continue
+        rows.append("| `%s` | %s | %.1f | %.1f |" % (_short_name(r["Name"]), r["Calls"],
+                                                     float(r["AverageNs"]) / 1e3, share))
+    try:
+        with open(traffic_file(workload)) as f:
+            traffic = json.load(f)
+    except (OSError, ValueError):
+        traffic = None
+    tlines = []
+    if traffic:
+        cal = traffic["calibration"]
+        tlines.append("Calibration: a plain elementwise kernel (bitwise not over 64 Mi int32: 256 MiB "
+                      "read, 256 MiB written) in the same runs, the median of its dispatches; factors "
+                      "FETCH_SIZE x%.4f, WRITE_SIZE x%.4f.  FETCH_SIZE and WRITE_SIZE count what "
+                      "the L2 moves to and from the fabric, that is the MALL (Infinity Cache) or "
+                      "HBM: gfx950 has no counter past the MALL, so these are L2<->fabric bytes, "
+                      "an upper bound on HBM traffic.\n" % (cal["fetch_factor"], cal["write_factor"]))
+        tlines.append("| stage | read GB | written GB | kernels (read / written GB) |")
+        tlines.append("|---|---|---|---|")
+        for stage, v in traffic["stages"].items():
+            ks = ", ".join("`%s` %.3f / %.3f" % (k, kv.get("read_bytes", 0) / 1e9,
+                                                 kv.get("write_bytes", 0) / 1e9)
+                           for k, kv in sorted(v["kernels"].items()))
+            tlines.append("| %s | %.3f | %.3f | %s |" % (stage, v["read_bytes"] / 1e9,
+                                                      v["write_bytes"] / 1e9, ks))
+        tlines.append("\nSource hash of the kernels these counters belong to: `%s` (bench.py "
+                      "reports `traffic` only while the sources still hash to it)." %
+                      traffic["source_sha256"])
+    line = ""
+    with open(bench_log) as f:
+        for ln in f:
+            if ln.startswith("{") and '"metric"' in ln:
+                line = ln.strip()
+    out = os.path.join(PROFILES, f"pkm_layer_{workload}.md")
+    with open(out, "w") as f:
+        f.write(LAYER_HEADER.format(workload=workload, steps=steps, warmup=warmup,
+                                    runs=steps + warmup))
+        f.write("\n".join(rows) + "\n\n## Traffic per stage launch (FETCH_SIZE, WRITE_SIZE; "
+                "KiB per dispatch x calibration)\n\n")
+        f.write("\n".join(tlines) if tlines else "not recorded for these sources")
+        f.write("\n\n## bench.py line (default 20 timed steps, 5 warm-up)\n\n```json\n%s\n```\n" % line)
+    return out
+
+
+LAYER_HEADER = """# PKM layer, fwd+bwd, `{workload}` (T=16384, H=4, n=512, k=32, d_k=512, d_v=1024, bf16): kernel trace and traffic
+
+One MI355X (gfx950), one process.  Inputs seeded and synthetic
+(`pkm_inputs.py`), resident in HBM.  Step = forward (selection, gather) +
+backward (slot sort, value side with dvalues overwritten, query side).
+
+## Commands (from the repository root on the GPU box; `cd /tmp` first for rocprofv3's own files)
+
+```
+python3 bench.py > gpurun_out/bench.log
+rocprofv3 --kernel-trace --stats -d gpurun_out/lay_t -o t --output-format csv -- python3 bench.py --steps {steps} --warmup {warmup} --no-cpu-baseline
+rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof_fetch -o fetch -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy
+rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof_write -o write -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy
+python3 bench.py --record-traffic gpurun_out/prof_fetch/fetch_results.db gpurun_out/prof_write/write_results.db
+python3 bench.py --record-layer gpurun_out/lay_t gpurun_out/bench.log
+```
+
+## Kernel trace (kernel_stats of the trace pass; the step's kernels run {runs} times = {warmup} warm-up + {steps} timed steps; after the step the bench times the update, usage, fused-SGD, sweep-free extras and the query network, {runs} runs each)
+
+| kernel | calls | avg µs | share % |
+|---|---|---|---|
+"""
+
+
+COUNTERS_HEADER = """# Per-kernel counters, `{workload}`
+
+One MI355X (gfx950), one process.  Durations: the mean over a kernel's
+dispatches in a kernel-trace pass.  Counters: means per dispatch over two
+counter passes (each runs the benchmark for 1 warm-up and 1 timed step; the
+kernels and their work are those of the timed runs).  Rates are against the
+machine's capacity over the kernel's duration at the nominal 2.4 GHz peak
+clock -- no clock is derived from the counters:
+
+* MFMA busy % = `SQ_VALU_MFMA_BUSY_CYCLES` / (1024 SIMDs x duration x 2.4 GHz)
+  (16 busy cycles per `v_mfma_f32_16x16x32_bf16`);
+* VALU issue % = 4 x `SQ_INSTS_VALU` / (1024 x duration x 2.4 GHz) (a wave64
+  VALU instruction holds a 16-lane SIMD for 4 cycles);
+* per-wave instruction counts = counter / `SQ_WAVES`; LDS conflict cycles per
+  LDS instruction = `SQ_LDS_BANK_CONFLICT` / `SQ_ACTIVE_INST_LDS`; L2 hit =
+  `TCC_HIT` / (`TCC_HIT` + `TCC_MISS`);
+* DRAM-destined GB = 32 x `TCC_EA0_RDREQ_DRAM_32B` (reads) and 32 x
+  `TCC_EA0_WRREQ_WRITE_DRAM_32B` (writes): the L2's requests sorted by
+  destination (DRAM, as against GMI or IO).  The MALL (Infinity Cache) sits on
+  the memory side of the fabric, so its hits count here as well: gfx950 shows
+  no counter past it, and these bytes and their rate (the last column, over
+  the kernel's duration) are L2<->fabric figures, an upper bound on what HBM
+  itself moved.
+
+Kernels under 5 µs are left out.
+
+## Commands (from the repository root on the GPU box; `cd /tmp` first)
+
+```
+rocprofv3 --kernel-trace --stats -d gpurun_out/cnt_t -o t --output-format csv -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline
+rocprofv3 --pmc {a} -d gpurun_out/cnt_a -o p --output-format csv -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline
+rocprofv3 --pmc {b} -d gpurun_out/cnt_b -o p --output-format csv -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline
+rocprofv3 --pmc {dram} -d gpurun_out/cnt_d -o p --output-format csv -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline
+python3 bench.py --record-counters gpurun_out/cnt_a gpurun_out/cnt_b gpurun_out/cnt_d gpurun_out/cnt_t
+```
+
+| kernel | grid | µs | MFMA busy % | VALU issue % | VALU / wave | MFMA / wave | LDS / wave | SALU / wave | LDS conflict cycles / LDS instr | L2 hit % | DRAM-destined read GB | DRAM-destined write GB | L2<->fabric TB/s |
+|---|---|---|---|---|---|---|---|---|---|---|---|---|---|
+"""
 
 
 def measure_extras(torch, _lib, p, values, dvalues, slot_start, w, elt, touched, stream) -> dict:
@@ -503,6 +711,12 @@ def main():
     args = parse()
     if args.record_traffic:
         print(record_traffic(*args.record_traffic, args.workload))
+        return
+    if args.record_layer:
+        print(record_layer(*args.record_layer, args.workload, args.steps, args.warmup))
+        return
+    if args.record_counters:
+        print(record_counters(*args.record_counters, args.workload))
         return
     if args.sweep:
         run_sweep(args)

@@ -144,6 +144,24 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int vof
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// dst + 16 l (dst is the same for the whole wave); a lane reaching past the
+// buffer's end reads zeros.  The copy counts on the vector memory counter.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void *dst, int voffset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16,
+                                             voffset, 0, 0, 0);
+}
+
+// s_waitcnt on the vector memory counter alone (vmcnt bits 3:0 and 15:14;
+// expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Exclusive prefix sum over the 64 lanes; *total receives the wave total.
 __device__ __forceinline__ int wave_exclusive_scan(int v, int *total)
 {
@@ -244,6 +262,8 @@ __device__ __forceinline__ void wave_sort_desc(uint64_t (&v)[R])
 __device__ __forceinline__ float g4_shfl(float v, int m) { return __shfl_xor(v, m); }
 __device__ __forceinline__ uint32_t g4_shfl(uint32_t v, int m) { return (uint32_t)__shfl_xor((int)v, m); }
 __device__ __forceinline__ uint64_t g4_shfl(uint64_t v, int m) { return shfl_xor_u64(v, m); }
+__device__ __forceinline__ float g4_bcast(float v, int src) { return __shfl(v, src); }
+__device__ __forceinline__ uint32_t g4_bcast(uint32_t v, int src) { return (uint32_t)__shfl((int)v, src); }
 
 // Sum over the 4 lanes that share lane % 16.
 __device__ __forceinline__ int group4_sum(int v)
@@ -251,6 +271,83 @@ __device__ __forceinline__ int group4_sum(int v)
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
     return v;
+}
+
+__device__ __forceinline__ float vmax(float a, float b) { return fmaxf(a, b); }
+__device__ __forceinline__ float vmin(float a, float b) { return fminf(a, b); }
+__device__ __forceinline__ uint32_t vmax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t vmin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+
+// The k-th largest (1 <= k <= 64) of the 64 values a 4-lane group holds (16
+// a lane, element e = 16 (lane / 16) + r), returned in all 4 lanes; v is
+// left permuted.  A bitonic network whose every merge of size `size` starts
+// by exchanging element e with its mirror e ^ (size - 1): every exchange then
+// keeps the larger value at the lower position, so in-lane exchanges are one
+// max and one min with no compare.  For k = 32 the last merge stops after its
+// mirror exchange: positions 0..31 then hold the 32 largest values, and the
+// 32nd is their least.
+template <typename T>
+__device__ __forceinline__ T group4_kth(T (&v)[16], int k)
+{
+    const int g = lane_id() >> 4;
+    auto inlane = [&](int r, int r2) {
+        const T a = v[r], b = v[r2];
+        v[r] = vmax(a, b);
+        v[r2] = vmin(a, b);
+    };
+    // the stride exchanges 8 .. 1 of 16-runs inside the lane
+    auto runs16 = [&](int from) {
+#pragma unroll
+        for (int stride = 8; stride > 0; stride >>= 1)
+            if (stride <= from)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if ((r & stride) == 0)
+                        inlane(r, r | stride);
+    };
+    // with lane group g ^ (lanes / 16): the mirror register 15 - r or the
+    // same register; the lower lane group keeps the larger value
+    auto cross = [&](int lanes, bool mirror, bool lower) {
+        T o[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            o[r] = g4_shfl(v[mirror ? 15 - r : r], lanes);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const T hi = vmax(v[r], o[r]), lo = vmin(v[r], o[r]);
+            v[r] = lower ? hi : lo;
+        }
+    };
+#pragma unroll
+    for (int size = 2; size <= 16; size <<= 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if ((r & (size >> 1)) == 0)
+                inlane(r, r ^ (size - 1));
+        runs16(size >> 2);
+    }
+    cross(16, true, (g & 1) == 0);      // size 32: e ^ 31 = lane group g ^ 1, register 15 - r
+    runs16(8);
+    cross(48, true, g < 2);             // size 64: e ^ 63 = lane group g ^ 3, register 15 - r
+    T x;
+    if (k == 32) {
+        x = v[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r)
+            x = vmin(x, v[r]);
+        x = vmin(x, g4_shfl(x, 16));
+        // lane groups 0 and 1 hold the 32 largest: every lane reads group 0's
+        return g4_bcast(x, lane_id() & 15);
+    }
+    cross(16, false, (g & 1) == 0);     // stride 16
+    runs16(8);
+    x = v[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r)
+        if (r == ((k - 1) & 15))
+            x = v[r];
+    return g4_bcast(x, (lane_id() & 15) + 16 * ((k - 1) >> 4));
 }
 
 template <int R, typename T>

@@ -260,13 +260,7 @@ __global__ __launch_bounds__(kFlatWaves *kWave) __attribute__((amdgpu_waves_per_
 #pragma unroll
             for (int m = 0; m < 16; ++m)
                 gm[m] = max(max(so[m][0], so[m][1]), max(so[m][2], so[m][3]));
-            group4_sort_desc<16>(gm);
-            uint32_t tau_src = gm[0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r)
-                if (r == ((k - 1) & 15))
-                    tau_src = gm[r];
-            tau = (uint32_t)__shfl((int)tau_src, tok + 16 * ((k - 1) >> 4));
+            tau = group4_kth(gm, k);
         } else {
             // the running k-th best score: keys below it cannot enter
             tau = (uint32_t)(best[k - 1] >> 32);

@@ -280,14 +280,6 @@ __device__ __forceinline__ void lds_dma16(const void *src, void *dst)
     __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
 
-// s_waitcnt on the vector memory counter alone (vmcnt bits 3:0 and 15:14;
-// expcnt and lgkmcnt left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // A workgroup is 2 x NWN waves, each owning WM x 64 of C: 2 WM rows by 64 NWN
 // columns.  A ring stage holds BK (32 or 64) columns of K: tile rows of RB =

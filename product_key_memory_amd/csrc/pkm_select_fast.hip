@@ -57,75 +57,98 @@ constexpr int kMaxPairs = 128;                       // merge_candidates(32) = 1
 // instruction touches (same entry, rows tok = 0..15) in distinct banks
 constexpr int kMergePitch = 2 * 32 + 1;
 
+// One 32-row step of the scoring: this wave's share of the next step's rows
+// goes from the codebook straight into `fill` (buffer loads into LDS) while
+// the MFMAs read the current step from `cur`.  The two are restrict
+// pointers, so the compiler does not wait on the copy before the reads; each
+// A fragment is read one MFMA pair ahead of its use.  Chunk c of local row r
+// sits at position c ^ (r % 16) of the row: the 16 rows an MFMA operand read
+// touches (same chunk, rows r16 = 0..15) then fall in distinct banks; thread
+// u of the workgroup fills position u + 256 m (1 KB per wave and m, the
+// layout a wave's LDS load writes).  The two tiles' accumulation chains
+// alternate, so consecutive MFMAs do not wait on each other.
+__device__ __forceinline__ void fast_step(uint4 *__restrict__ fill, const uint4 *__restrict__ cur,
+                                          __amdgpu_buffer_rsrc_t rsrc, int p_next, int tid,
+                                          const uint4 (&qf)[kFastKSteps], int r16, int g,
+                                          floatx4 (&acc)[2])
+{
+    constexpr int chunks = kFastKSteps * 32 * 2 / 16;       // 32 chunks of 16 bytes per row
+    constexpr int per_thread = 32 * chunks / (kFastWaves * kWave);
+    if (fill) {
+        const int wave = tid / kWave;
+#pragma unroll
+        for (int m = 0; m < per_thread; ++m) {
+            const int u = tid + m * kFastWaves * kWave;
+            const int rl = u / chunks, c = (u % chunks) ^ (rl & 15);
+            buffer_load_lds16(rsrc, fill + m * kFastWaves * kWave + wave * kWave,
+                              ((32 * p_next + rl) * chunks + c) * 16);
+        }
+    }
+    uint4 a[2], b[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w)
+        a[w] = cur[(16 * w + r16) * chunks + (g ^ r16)];
+#pragma unroll
+    for (int kk = 0; kk < kFastKSteps; ++kk) {
+        if (kk + 1 < kFastKSteps) {
+#pragma unroll
+            for (int w = 0; w < 2; ++w)
+                b[w] = cur[(16 * w + r16) * chunks + ((4 * (kk + 1) + g) ^ r16)];
+        }
+#pragma unroll
+        for (int w = 0; w < 2; ++w)
+            acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, a[w]), __builtin_bit_cast(bf16x8, qf[kk]), acc[w], 0, 0, 0);
+#pragma unroll
+        for (int w = 0; w < 2; ++w)
+            a[w] = b[w];
+    }
+}
+
 // Scores of the wave's 16 tokens against the sub-keys 0..n_loc-1 of one block
 // (kb = its first row), as float32 bit patterns: so[j][i] = the score of
-// sub-key 16 j + 4 g + i for token `tok` (rows past n_loc score 0; the caller
-// masks them).  The workgroup's 4 waves (64 tokens)
+// sub-key 16 j + 4 g + i for token `tok` (rows past n_loc read as zeros or
+// stale data; the caller masks them).  The workgroup's 4 waves (64 tokens)
 // share the codebook through LDS: per step p it holds rows 32 p .. 32 p + 31
-// (16 KB, double-buffered), each thread loading 4 of its 16-byte chunks, so
-// the L2 serves each codebook once per 64 tokens instead of once per 16.
-// Chunk c of local row r sits at position c ^ (r % 16) of the row: the 16
-// rows an MFMA operand read touches (same chunk, rows r16 = 0..15) then fall
-// in distinct banks.  Within a step the two tiles' accumulation chains
-// alternate, so consecutive MFMAs do not wait on each other.
+// (16 KB, double-buffered), so the L2 serves each codebook once per 64
+// tokens instead of once per 16.  A step's rows are complete once this
+// wave's own copies have retired and every wave has passed the barrier that
+// follows, which also frees the other buffer for the next step's copy.
 template <int TILES>
 __device__ __forceinline__ void fast_scores(uint32_t (&so)[TILES][4], const uint16_t *kb,
                                             const uint4 (&qf)[kFastKSteps], int n_loc, int r16,
                                             int g, uint4 *kbuf, int tid)
 {
     constexpr int half = kFastKSteps * 32;
-    constexpr int chunks = half * 2 / 16;            // 32 chunks of 16 bytes per row
+    constexpr int chunks = half * 2 / 16;
     constexpr int step_units = 32 * chunks;          // 1024 chunks per 32-row step
-    constexpr int per_thread = step_units / (kFastWaves * kWave);
     constexpr int steps = TILES / 2;
-    // rows past n_loc read as zeros
     const __amdgpu_buffer_rsrc_t rsrc = buffer_over(kb, n_loc * half * 2);
-    uint4 pre[per_thread];
-    auto gload = [&](int p) {
+    {
+        const int wave = tid / kWave;
 #pragma unroll
-        for (int m = 0; m < per_thread; ++m) {
+        for (int m = 0; m < step_units / (kFastWaves * kWave); ++m) {
             const int u = tid + m * kFastWaves * kWave;
             const int rl = u / chunks, c = (u % chunks) ^ (rl & 15);
-            pre[m] = buffer_load16(rsrc, ((32 * p + rl) * chunks + c) * 16, 0);
+            buffer_load_lds16(rsrc, kbuf + m * kFastWaves * kWave + wave * kWave,
+                              (rl * chunks + c) * 16);
         }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int m = 0; m < per_thread; ++m)
-            kbuf[buf * step_units + tid + m * kFastWaves * kWave] = pre[m];
-    };
-    gload(0);
-    lstore(0);
-    gload(1);
-    __syncthreads();
+    }
 #pragma unroll
     for (int p = 0; p < steps; ++p) {
-        const uint4 *cur = kbuf + (p & 1) * step_units;
+        wait_vmcnt<0>();
+        __syncthreads();
         floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int kk = 0; kk < kFastKSteps; ++kk) {
-#pragma unroll
-            for (int w = 0; w < 2; ++w) {
-                const int rl = 16 * w + r16;
-                const uint4 a = cur[rl * chunks + ((4 * kk + g) ^ r16)];
-                acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[kk]), acc[w],
-                    0, 0, 0);
-            }
-        }
+        fast_step(p + 1 < steps ? kbuf + ((p + 1) & 1) * step_units : nullptr,
+                  kbuf + (p & 1) * step_units, rsrc, p + 1, tid, qf, r16, g, acc);
 #pragma unroll
         for (int w = 0; w < 2; ++w)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 so[2 * p + w][i] = __float_as_uint(acc[w][i]);
-        // step p + 1 goes to the other buffer (its readers finished at the
-        // last barrier); step p + 2 is fetched while step p + 1 is worked on
-        if (p + 1 < steps)
-            lstore((p + 1) & 1);
-        if (p + 2 < steps)
-            gload(p + 2);
-        __syncthreads();
     }
+    // every wave is done with the last step's buffer before LDS is reused
+    __syncthreads();
 }
 
 // lists[((t H + h) 2 + s) k + e] = (ord score, sub-key) of the e-th best
@@ -195,6 +218,9 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
         uint32_t so[TILES][4];
         fast_scores(so, kb + (int64_t)base * half, qf, n_loc, tok, g, lds, tid);
         if (n_loc < (16 * TILES)) {
+            // (an asm statement keeps this a branch: a whole block skips the
+            // selects)
+            asm volatile("" ::: "memory");
             // sub-key 16 j + 4 g + i of the block exists iff 16 j + i < lim
             const int lim = n_loc - 4 * g;
             const uint32_t neg = __float_as_uint(-INFINITY);
@@ -220,31 +246,26 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
                 x = fmaxf(x, sf(e / 4, e % 4));
             gm[m] = x;
         }
-        group4_sort_desc<16>(gm);
-        float tau_src = gm[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r)
-            if (r == ((k - 1) & 15))
-                tau_src = gm[r];
-        float tau = __shfl(tau_src, tok + 16 * ((k - 1) >> 4));
+        float tau = group4_kth(gm, k);
         // A first block is more than 3/4 full, >= 48 groups of real scores,
         // so tau is a real score and the sub-keys past n never survive.  A second block may hold fewer than k sub-keys: there the
         // first block's k-th key (a real score) raises the bar, and keys
         // below it cannot reach the top k anyway.
         if constexpr (!kFirst)
             tau = fmaxf(tau, unord_f32((uint32_t)(prev[k - 1] >> 32)));
+        // a token past T (it scored token 0's query) keeps nothing: no score
+        // compares >= NaN, so it counts no survivor, takes no bisection and
+        // claims no position in the compaction (its 4 lanes share `live`)
+        if (!live)
+            tau = __uint_as_float(0x7fc00000u);
 
-        // survivors: ord >= tau.  A token past T (it scored token 0's query)
-        // keeps nothing: no count, no bisection, no compaction store that
-        // claims a position -- its 4 lanes share `live`, so total = 0
+        // survivors: score >= tau
         int cnt = 0;
 #pragma unroll
         for (int j = 0; j < TILES; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 cnt += sf(j, i) >= tau ? 1 : 0;
-        if (!live)
-            cnt = 0;
         int total = group4_sum(cnt);
         bool fits = total <= kFastSurv;
 
@@ -350,7 +371,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
             for (int j = 0; j < TILES; ++j) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const bool keep = live && sf(j, i) >= tau;
+                    const bool keep = sf(j, i) >= tau;
                     surv_s[off] = so[j][i];
                     surv_i[off] = (uint32_t)(16 * j + i);
                     off += keep ? 1 : 0;

@@ -1374,17 +1374,25 @@ __global__ __launch_bounds__(kDkWaves *kWave) void dkeys_mfma_kernel(
 // codebooks (fold = H) also over the heads, head by head within each block:
 // dkeys[s][i][c] = sum_b sum_h partial[b][h][s][i][c] (count = one block's
 // partial, H * 2 * n * half).
+// Four consecutive outputs per thread (16-byte loads; out is a multiple of 4,
+// as half is), each summed in the same order as one at a time.
 __global__ void dkeys_reduce_kernel(const float *__restrict__ partial, int blocks, int64_t count,
                                     int fold, float *__restrict__ dkeys)
 {
     const int64_t out = count / fold;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < out; e += stride) {
-        float acc = 0.f;
+    for (int64_t e4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; 4 * e4 < out; e4 += stride) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int b = 0; b < blocks; ++b)
-            for (int h = 0; h < fold; ++h)
-                acc += partial[(int64_t)b * count + h * out + e];
-        dkeys[e] = acc;
+            for (int h = 0; h < fold; ++h) {
+                const float4 v =
+                    *reinterpret_cast<const float4 *>(partial + (int64_t)b * count + h * out + 4 * e4);
+                acc.x += v.x;
+                acc.y += v.y;
+                acc.z += v.z;
+                acc.w += v.w;
+            }
+        *reinterpret_cast<float4 *>(dkeys + 4 * e4) = acc;
     }
 }
 
@@ -1588,7 +1596,7 @@ static hipError_t launch_query_t(const void *q, const void *keys, int64_t key_hs
         return err;
     const int64_t count = (int64_t)H * 2 * n * half;
     const int fold = keys_shared ? H : 1;
-    const int64_t rblocks = grid1d(count / fold, 256);
+    const int64_t rblocks = grid1d(count / fold / 4, 256);
     hipLaunchKernelGGL(dkeys_reduce_kernel, dim3((unsigned)(rblocks < 8192 ? rblocks : 8192)),
                        dim3(256), 0, stream, partial, S.blocks, count, fold, dkeys);
     return hipGetLastError();

@@ -570,7 +570,7 @@ def run_sweep(args) -> None:
     """The speed / memory-use knobs: heads H and picks k on the workload's
     remaining shapes (synthetic inputs of the same recipe, one draw per H),
     and at k = 32 one codebook pair shared by the heads (the first head's).
-    Per point: W warm-up and K timed steps of pkm_forward + pkm_backward
+    Per point: W warm-up and K timed steps of pkm_forward + pkm_backward_overwrite
     (dvalues overwritten) bracketed by events, and the share of the n*n slots
     some pick selected in the batch."""
     import dataclasses

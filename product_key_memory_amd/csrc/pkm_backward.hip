@@ -5,16 +5,17 @@
 // backward pass; gradient reaches the k selected scores of each head, and from
 // each score its left and right sub-key scores.
 //
-// Value side (no float atomics on the value gradient in the common case):
+// Value side (no float atomics: the result is the same on every run):
 //   1. the T*H*k picks are counting-sorted by slot into slot_start [n*n + 1]
-//      and order [T*H*k], in two levels whose counters all sit in LDS;
-//   2. one wave per fixed chunk of the sorted picks walks its slot segments:
-//      the value row of a segment is read once, every pick p of it gives
-//      dw_p = <dy[t_p], values[f]>, and sum_p w_p dy[t_p] is added to
-//      dvalues[f] with a plain read-modify-write when the whole segment lies
-//      in the chunk (no other wave touches that row), with float atomics only
-//      for segments cut by a chunk boundary (this also spreads a hot slot
-//      over many waves).
+//      and order [T*H*k], in two levels whose counters all sit in LDS, stably
+//      (the picks of a slot in ascending pick id);
+//   2. one wave per chunk of the sorted picks walks its slot segments: the
+//      value row of a segment is read once, every pick p of it gives
+//      dw_p = <dy[t_p], values[f]>, and sum_p w_p dy[t_p] goes to dvalues[f]
+//      with a plain store (or read-modify-write) when the whole segment lies
+//      in the chunk (no other wave touches that row); a segment longer than
+//      the chunk (a Zipf-hot slot) is cut into pieces, each stored to a row
+//      of its own, and the pieces are summed afterwards in position order.
 // Query side:
 //   3. one wave per (token, head), one lane per pick: the softmax backward
 //      ds_r = w_r (dw_r - sum_r' w_r' dw_r') matters only summed over the
@@ -26,9 +27,10 @@
 //      dq = sum_i g_i * sub-key row i (the rows of the distinct sub-keys are
 //      fetched in batches), and (i, g_i) goes to a compact list;
 //   4. dkeys[h][s][i] = sum_t g * q_half[t]: each workgroup owns one token
-//      block and 64 columns of one codebook and accumulates the product of
-//      the sparse g matrix (densified per 32-token step in LDS) with q in
-//      MFMA registers; a last kernel sums the token blocks' partials.
+//      block and 128 columns (64 for n > 512) of one codebook and accumulates
+//      the product of the sparse g matrix (densified per 64- or 32-token step
+//      in LDS) with q in MFMA registers; a last kernel sums the token blocks'
+//      partials in block order.
 #include <type_traits>
 
 #include "pkm_device.hpp"
@@ -533,8 +535,9 @@ constexpr int kSegWaves = 4;
 // then streams the picks in groups of U with two groups of dy rows in flight;
 // the value row of the next run is fetched while the current one is worked
 // on.  A run's sum is stored (the row is this wave's alone) unless the run is
-// longer than chunk: those rows, zeroed beforehand in overwrite mode, take
-// float atomics from each wave that holds a piece.
+// longer than chunk: each wave holding a piece of such a run stores the
+// piece's sum to the piece's own row of `split` (piece_row), and
+// long_run_kernel adds the pieces in position order.
 template <int MCH, int U>
 struct DyGroup {
     uint4 r[U][MCH];

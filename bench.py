@@ -25,6 +25,7 @@ METRIC = "PKM layer tokens/sec fwd+bwd (n=512,H=4,k=32,d=1024); gather HBM GB/s 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 MFMA_FP32_PEAK_TFLOPS = 157.3
+MFMA_FP64_PEAK_TFLOPS = 78.6    # the selection of float32 storage scores on the fp64 MFMA
 
 
 def parse():
@@ -207,7 +208,7 @@ def record_traffic(fetch_db: str, write_db: str, workload: str) -> str:
     return path
 
 
-# The two counter passes --record-counters reads (each within one pass's
+# The three counter passes --record-counters reads (each within one pass's
 # limits: at most 8 SQ and 4 TCC counters).  Work counters (instructions,
 # busy cycles, hits) do not depend on the pass's timing; the durations come
 # from a kernel-trace pass of its own, and every rate is taken against the
@@ -240,7 +241,7 @@ def _csv_rows(directory: str, suffix: str) -> list:
 
 def record_counters(pmc_a: str, pmc_b: str, pmc_dram: str, trace: str, workload: str) -> str:
     """Per kernel: mean duration of its dispatches in the trace pass; means of
-    the counters per dispatch in the two counter passes; rates against
+    the counters per dispatch in the three counter passes; rates against
     1024 SIMDs x duration x 2.4 GHz."""
     dur, calls = {}, {}
     for r in _csv_rows(trace, "kernel_trace.csv"):
@@ -280,7 +281,8 @@ def record_counters(pmc_a: str, pmc_b: str, pmc_dram: str, trace: str, workload:
             rd / 1e9, wr / 1e9, (rd + wr) / t / 1e12))
     out = os.path.join(PROFILES, f"pkm_counters_{workload}.md")
     with open(out, "w") as f:
-        f.write(COUNTERS_HEADER.format(workload=workload,
+        f.write(COUNTERS_HEADER.format(workload=workload, title=workload_title(workload),
+                                       wl_arg=workload_arg(workload),
                                        a=" ".join(COUNTER_PASSES["A"]), b=" ".join(COUNTER_PASSES["B"]),
                                        dram=" ".join(COUNTER_PASSES["DRAM"])))
         f.write("\n".join(lines) + "\n")
@@ -332,8 +334,8 @@ def record_layer(trace: str, bench_log: str, workload: str, steps: int, warmup: 
                 line = ln.strip()
     out = os.path.join(PROFILES, f"pkm_layer_{workload}.md")
     with open(out, "w") as f:
-        f.write(LAYER_HEADER.format(workload=workload, steps=steps, warmup=warmup,
-                                    runs=steps + warmup))
+        f.write(LAYER_HEADER.format(workload=workload, title=workload_title(workload), steps=steps,
+                                    warmup=warmup, runs=steps + warmup, wl_arg=workload_arg(workload)))
         f.write("\n".join(rows) + "\n\n## Traffic per stage launch (FETCH_SIZE, WRITE_SIZE; "
                 "KiB per dispatch x calibration)\n\n")
         f.write("\n".join(tlines) if tlines else "not recorded for these sources")
@@ -341,7 +343,13 @@ def record_layer(trace: str, bench_log: str, workload: str, steps: int, warmup: 
     return out
 
 
-LAYER_HEADER = """# PKM layer, fwd+bwd, `{workload}` (T=16384, H=4, n=512, k=32, d_k=512, d_v=1024, bf16): kernel trace and traffic
+def workload_title(workload: str) -> str:
+    import pkm_inputs
+    w = pkm_inputs.WORKLOADS[workload]
+    return f"T={w.T}, H={w.H}, n={w.n}, k={w.k}, d_k={w.d_k}, d_v={w.d_v}, {w.dtype}"
+
+
+LAYER_HEADER = """# PKM layer, fwd+bwd, `{workload}` ({title}): kernel trace and traffic
 
 One MI355X (gfx950), one process.  Inputs seeded and synthetic
 (`pkm_inputs.py`), resident in HBM.  Step = forward (selection, gather) +
@@ -350,12 +358,12 @@ backward (slot sort, value side with dvalues overwritten, query side).
 ## Commands (from the repository root on the GPU machine; `cd /tmp` first for rocprofv3's own files)
 
 ```
-python3 bench.py > gpurun_out/bench.log
-rocprofv3 --kernel-trace --stats -d gpurun_out/lay_t -o t --output-format csv -- python3 bench.py --steps {steps} --warmup {warmup} --no-cpu-baseline
-rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof_fetch -o fetch -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy
-rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof_write -o write -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy
-python3 bench.py --record-traffic gpurun_out/prof_fetch/fetch_results.db gpurun_out/prof_write/write_results.db
-python3 bench.py --record-layer gpurun_out/lay_t gpurun_out/bench.log
+python3 bench.py{wl_arg} > gpurun_out/bench.log
+rocprofv3 --kernel-trace --stats -d gpurun_out/lay_t -o t --output-format csv -- python3 bench.py{wl_arg} --steps {steps} --warmup {warmup} --no-cpu-baseline
+rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof_fetch -o fetch -- python3 bench.py{wl_arg} --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy
+rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof_write -o write -- python3 bench.py{wl_arg} --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy
+python3 bench.py{wl_arg} --record-traffic gpurun_out/prof_fetch/fetch_results.db gpurun_out/prof_write/write_results.db
+python3 bench.py{wl_arg} --record-layer gpurun_out/lay_t gpurun_out/bench.log
 ```
 
 ## Kernel trace (kernel_stats of the trace pass; the step's kernels run {runs} times = {warmup} warm-up + {steps} timed steps; after the step the bench times the update, usage, fused-SGD, sweep-free extras and the query network, {runs} runs each)
@@ -365,10 +373,14 @@ python3 bench.py --record-layer gpurun_out/lay_t gpurun_out/bench.log
 """
 
 
-COUNTERS_HEADER = """# Per-kernel counters, `{workload}`
+def workload_arg(workload: str) -> str:
+    return "" if workload == "base-bf16-zipf-bwd" else f" --workload {workload}"
+
+
+COUNTERS_HEADER = """# Per-kernel counters, `{workload}` ({title})
 
 One MI355X (gfx950), one process.  Durations: the mean over a kernel's
-dispatches in a kernel-trace pass.  Counters: means per dispatch over two
+dispatches in a kernel-trace pass.  Counters: means per dispatch over three
 counter passes (each runs the benchmark for 1 warm-up and 1 timed step; the
 kernels and their work are those of the timed runs).  Rates are against the
 machine's capacity over the kernel's duration at the nominal 2.4 GHz peak
@@ -394,11 +406,11 @@ Kernels under 5 µs are left out.
 ## Commands (from the repository root on the GPU machine; `cd /tmp` first)
 
 ```
-rocprofv3 --kernel-trace --stats -d gpurun_out/cnt_t -o t --output-format csv -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline
-rocprofv3 --pmc {a} -d gpurun_out/cnt_a -o p --output-format csv -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline
-rocprofv3 --pmc {b} -d gpurun_out/cnt_b -o p --output-format csv -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline
-rocprofv3 --pmc {dram} -d gpurun_out/cnt_d -o p --output-format csv -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline
-python3 bench.py --record-counters gpurun_out/cnt_a gpurun_out/cnt_b gpurun_out/cnt_d gpurun_out/cnt_t
+rocprofv3 --kernel-trace --stats -d gpurun_out/cnt_t -o t --output-format csv -- python3 bench.py{wl_arg} --steps 1 --warmup 1 --no-cpu-baseline
+rocprofv3 --pmc {a} -d gpurun_out/cnt_a -o p --output-format csv -- python3 bench.py{wl_arg} --steps 1 --warmup 1 --no-cpu-baseline
+rocprofv3 --pmc {b} -d gpurun_out/cnt_b -o p --output-format csv -- python3 bench.py{wl_arg} --steps 1 --warmup 1 --no-cpu-baseline
+rocprofv3 --pmc {dram} -d gpurun_out/cnt_d -o p --output-format csv -- python3 bench.py{wl_arg} --steps 1 --warmup 1 --no-cpu-baseline
+python3 bench.py{wl_arg} --record-counters gpurun_out/cnt_a gpurun_out/cnt_b gpurun_out/cnt_d gpurun_out/cnt_t
 ```
 
 | kernel | grid | µs | MFMA busy % | VALU issue % | VALU / wave | MFMA / wave | LDS / wave | SALU / wave | LDS conflict cycles / LDS instr | L2 hit % | DRAM-destined read GB | DRAM-destined write GB | L2<->fabric TB/s |
@@ -834,10 +846,12 @@ def main():
                  "GB/s": round(work[name]["bytes"] / (ms * 1e-3) / 1e9, 1)}
         entry["hbm_frac"] = round(entry["GB/s"] / HBM_PEAK_GBS, 4)
         if "flops" in work[name]:
+            # the contraction's own peak: bf16 MFMA, or (float32 storage) the
+            # fp64 MFMA the selection scores with
             tf = work[name]["flops"] / (ms * 1e-3) / 1e12
-            peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+            peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP64_PEAK_TFLOPS
             entry.update({"flops": work[name]["flops"], "TFLOP/s": round(tf, 2),
-                          "mfma_frac": round(tf / peak, 4)})
+                          "mfma_peak": peak, "mfma_frac": round(tf / peak, 4)})
         if name in traffic:
             entry["traffic"] = traffic[name]["read_bytes"] + traffic[name]["write_bytes"]
         kernels[name] = entry
@@ -849,9 +863,15 @@ def main():
 
     dominant = max(STAGES, key=lambda s: per_stage[s])
     dk = kernels[dominant]
-    roofline = {"kernel": dominant, "bound": "hbm", "achieved": dk["GB/s"], "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(dk["GB/s"] / HBM_PEAK_GBS, 4),
-                "traffic": dk.get("traffic")}
+    if "flops" in dk:
+        # a contraction (the selection's scoring) is priced against its MFMA peak
+        roofline = {"kernel": dominant, "bound": "mfma", "achieved": dk["TFLOP/s"],
+                    "peak": dk["mfma_peak"], "unit": "TFLOP/s", "frac": dk["mfma_frac"],
+                    "traffic": dk.get("traffic")}
+    else:
+        roofline = {"kernel": dominant, "bound": "hbm", "achieved": dk["GB/s"],
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(dk["GB/s"] / HBM_PEAK_GBS, 4), "traffic": dk.get("traffic")}
 
     out = {
         "metric": METRIC,

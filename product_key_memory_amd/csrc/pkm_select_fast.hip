@@ -5,16 +5,18 @@
 // "Why top-k of each half is enough").
 //
 // 1. fwd_topk_half_kernel: one wave per (16 tokens, head, half).  The
-//    codebook is scored in blocks of 512 sub-keys (one block for n <= 512,
-//    two for n <= 1024; one of 256 for n <= 256).  The wave computes its tokens' scores of a block
-//    straight into registers with v_mfma_f32_16x16x32_bf16 (sub-keys as M,
-//    tokens as N): lane l holds, for token l % 16, the scores of sub-keys
-//    16 j + 4 (l / 16) + i of the block (tile j < 32, i < 4).  All selection
-//    work then runs on the 4 lanes that share a token, so every instruction
-//    serves the wave's 16 tokens at once:
-//      - tau = k-th largest of the token's 64 group maxima (groups of 8
-//        scores), by a bitonic sort inside the 4-lane group: the k groups
-//        above it each hold a score >= tau, so at least k scores survive;
+//    codebook is scored in one or two blocks of 128, 256 or 512 sub-keys
+//    (the launcher picks the shape so that the first block is more than 3/4
+//    full).  The wave computes its tokens' scores of a block straight into
+//    registers with v_mfma_f32_16x16x32_bf16 (sub-keys as M, tokens as N):
+//    lane l holds, for token l % 16, the scores of sub-keys
+//    16 j + 4 (l / 16) + i of the block (tile j, i < 4).  All selection work
+//    then runs on the 4 lanes that share a token, so every instruction serves
+//    the wave's 16 tokens at once:
+//      - tau = k-th largest of the token's 64 group maxima (groups of
+//        TILES / 4 scores), by a bitonic network inside the 4-lane group:
+//        the k groups above it each hold a score >= tau, so at least k
+//        scores survive;
 //      - survivors (score >= tau) are compacted into LDS and sorted as 64-bit
 //        keys (score, then lower index first) inside the 4-lane group; when a
 //        token has more than 64 survivors (heavy ties) its exact k-th largest

@@ -654,7 +654,8 @@ def run_sweep(args) -> None:
 def run_flat(args) -> None:
     """Search cost, flat against product keys (companion page, "Search cost:
     flat vs product keys"): the workload's recipe at --flat-tokens tokens and
-    n = 128, 256, 512; per n, W warm-up and K timed calls of each selection
+    n = 128, 256, 512; per n, W warm-up and K timed calls of the product-key selection and 1 warm-up
+    and max(2, K / 4) timed calls of the flat search
     (scores, top-k, softmax; the gather that follows is the same for both)
     bracketed by events.  Flops: product keys 2 T H 2 n (d_k / 2), flat
     2 T H n^2 d_k.  The sets of the two searches are compared (equal wherever

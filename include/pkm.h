@@ -95,7 +95,8 @@ size_t pkm_workspace_bytes(const pkm_problem_t *p, int backward);
  * of each half is enough").  For every token t and head h:
  *   1. split q[t][h] into q1 = first half, q2 = second half;
  *   2. score q1 against the n left sub-keys and q2 against the n right
- *      sub-keys (inner products, float32 accumulation);
+ *      sub-keys (inner products: float32 sums for bf16 storage; for float32
+ *      storage float64 sums, each score rounded once to float32);
  *   3. keep the exact top-k of each half, ordered (score desc, index asc);
  *   4. combine: the score of slot (i, j) is left_i + right_j; keep the k best
  *      slots by (score desc, slot asc) -- the same set as a flat search over

@@ -348,10 +348,9 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
             mine = c;
         }
         // Lane group g writes its survivors from position g + (the counts of
-        // the groups before it): every candidate is stored at the next free
-        // position, which only a kept one claims, so the writes need no
-        // branches; the last unclaimed store lands in the spare slot that
-        // ends the group's range.
+        // the groups before it), each at the next free position; the stores
+        // are predicated (exec-masked), so only the lanes keeping a candidate
+        // touch LDS (the position after each group's range stays a spare).
         const int c0 = __shfl(mine, tok), c1 = __shfl(mine, tok + 16), c2 = __shfl(mine, tok + 32);
         int off = g + (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
         if (ordm) {
@@ -362,8 +361,10 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
                     const uint32_t o = so[j][i];
                     const bool keep =
                         live && (exact ? (o > kth || (o == kth && 16 * j + i <= lim_t)) : o >= kth);
-                    surv_s[off] = o;
-                    surv_i[off] = (uint32_t)(16 * j + i);
+                    if (keep) {
+                        surv_s[off] = o;
+                        surv_i[off] = (uint32_t)(16 * j + i);
+                    }
                     off += keep ? 1 : 0;
                 }
                 __builtin_amdgcn_sched_barrier(0);     // one tile's keys at a time
@@ -374,8 +375,10 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const bool keep = sf(j, i) >= tau;
-                    surv_s[off] = so[j][i];
-                    surv_i[off] = (uint32_t)(16 * j + i);
+                    if (keep) {
+                        surv_s[off] = so[j][i];
+                        surv_i[off] = (uint32_t)(16 * j + i);
+                    }
                     off += keep ? 1 : 0;
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -622,16 +625,19 @@ __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
 
     // The survivors (key >= kth) go to this wave's list area, free once every
     // lane has its candidates: 64 slots per row.  Lane group g writes from
-    // position g + (the counts of the groups before it), every candidate at
-    // the next free slot, which only a kept one claims.
+    // position g + (the counts of the groups before it), each survivor at the
+    // next free slot, by predicated stores (only lanes keeping a candidate
+    // touch LDS).
     wave_lds_sync();
     uint64_t *surv = reinterpret_cast<uint64_t *>(sl) + tok * kMergePitch;
     const int c0 = __shfl(cnt, tok), c1 = __shfl(cnt, tok + 16), c2 = __shfl(cnt, tok + 32);
     int off = g + (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
 #pragma unroll
     for (int c = 0; c < 32; ++c) {
-        surv[off] = v[c];
-        off += live && v[c] >= kth ? 1 : 0;
+        const bool keep = live && v[c] >= kth;
+        if (keep)
+            surv[off] = v[c];
+        off += keep ? 1 : 0;
     }
     wave_lds_sync();
     const int b1 = c0, b2 = c0 + c1, b3 = c0 + c1 + c2;

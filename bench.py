@@ -355,15 +355,15 @@ One MI355X (gfx950), one process.  Inputs seeded and synthetic
 (`pkm_inputs.py`), resident in HBM.  Step = forward (selection, gather) +
 backward (slot sort, value side with dvalues overwritten, query side).
 
-## Commands (from the repository root on the GPU machine; `cd /tmp` first for rocprofv3's own files)
+## Commands (from the repository root; `<out>` is any output directory)
 
 ```
-python3 bench.py{wl_arg} > gpurun_out/bench.log
-rocprofv3 --kernel-trace --stats -d gpurun_out/lay_t -o t --output-format csv -- python3 bench.py{wl_arg} --steps {steps} --warmup {warmup} --no-cpu-baseline
-rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof_fetch -o fetch -- python3 bench.py{wl_arg} --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy
-rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof_write -o write -- python3 bench.py{wl_arg} --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy
-python3 bench.py{wl_arg} --record-traffic gpurun_out/prof_fetch/fetch_results.db gpurun_out/prof_write/write_results.db
-python3 bench.py{wl_arg} --record-layer gpurun_out/lay_t gpurun_out/bench.log
+python3 bench.py{wl_arg} > <out>/bench.log
+rocprofv3 --kernel-trace --stats -d <out>/lay_t -o t --output-format csv -- python3 bench.py{wl_arg} --steps {steps} --warmup {warmup} --no-cpu-baseline
+rocprofv3 --pmc FETCH_SIZE -d <out>/prof_fetch -o fetch -- python3 bench.py{wl_arg} --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy
+rocprofv3 --pmc WRITE_SIZE -d <out>/prof_write -o write -- python3 bench.py{wl_arg} --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy
+python3 bench.py{wl_arg} --record-traffic <out>/prof_fetch/fetch_results.db <out>/prof_write/write_results.db
+python3 bench.py{wl_arg} --record-layer <out>/lay_t <out>/bench.log
 ```
 
 ## Kernel trace (kernel_stats of the trace pass; the step's kernels run {runs} times = {warmup} warm-up + {steps} timed steps; after the step the bench times the update, usage, fused-SGD, sweep-free extras and the query network, {runs} runs each)
@@ -403,14 +403,14 @@ clock -- no clock is derived from the counters:
 
 Kernels under 5 µs are left out.
 
-## Commands (from the repository root on the GPU machine; `cd /tmp` first)
+## Commands (from the repository root; `<out>` is any output directory)
 
 ```
-rocprofv3 --kernel-trace --stats -d gpurun_out/cnt_t -o t --output-format csv -- python3 bench.py{wl_arg} --steps 1 --warmup 1 --no-cpu-baseline
-rocprofv3 --pmc {a} -d gpurun_out/cnt_a -o p --output-format csv -- python3 bench.py{wl_arg} --steps 1 --warmup 1 --no-cpu-baseline
-rocprofv3 --pmc {b} -d gpurun_out/cnt_b -o p --output-format csv -- python3 bench.py{wl_arg} --steps 1 --warmup 1 --no-cpu-baseline
-rocprofv3 --pmc {dram} -d gpurun_out/cnt_d -o p --output-format csv -- python3 bench.py{wl_arg} --steps 1 --warmup 1 --no-cpu-baseline
-python3 bench.py{wl_arg} --record-counters gpurun_out/cnt_a gpurun_out/cnt_b gpurun_out/cnt_d gpurun_out/cnt_t
+rocprofv3 --kernel-trace --stats -d <out>/cnt_t -o t --output-format csv -- python3 bench.py{wl_arg} --steps 1 --warmup 1 --no-cpu-baseline
+rocprofv3 --pmc {a} -d <out>/cnt_a -o p --output-format csv -- python3 bench.py{wl_arg} --steps 1 --warmup 1 --no-cpu-baseline
+rocprofv3 --pmc {b} -d <out>/cnt_b -o p --output-format csv -- python3 bench.py{wl_arg} --steps 1 --warmup 1 --no-cpu-baseline
+rocprofv3 --pmc {dram} -d <out>/cnt_d -o p --output-format csv -- python3 bench.py{wl_arg} --steps 1 --warmup 1 --no-cpu-baseline
+python3 bench.py{wl_arg} --record-counters <out>/cnt_a <out>/cnt_b <out>/cnt_d <out>/cnt_t
 ```
 
 | kernel | grid | µs | MFMA busy % | VALU issue % | VALU / wave | MFMA / wave | LDS / wave | SALU / wave | LDS conflict cycles / LDS instr | L2 hit % | DRAM-destined read GB | DRAM-destined write GB | L2<->fabric TB/s |
@@ -739,7 +739,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the sharding design is described in the design notes); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)

@@ -180,7 +180,7 @@ __global__ __launch_bounds__(kL1Threads) void bucket_scatter_kernel(
     constexpr int W = kL1Threads / kWave;
     __shared__ int32_t hw[kSortWaves][kMaxBuckets];   // per-wave counts, then cursors
     __shared__ int32_t wsum[W];
-    const int lane = lane_id(), w = threadIdx.x / kWave;
+    const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     for (int e = threadIdx.x; e < kSortWaves * kMaxBuckets; e += kL1Threads)
         (&hw[0][0])[e] = 0;
     const int64_t p0 = l1_begin(chunk, picks);
@@ -196,9 +196,12 @@ __global__ __launch_bounds__(kL1Threads) void bucket_scatter_kernel(
             f[u] = p < se ? idx[p] : -1;
         }
 #pragma unroll
-        for (int u = 0; u < kSortUnroll; ++u)
+        for (int u = 0; u < kSortUnroll; ++u) {
+            if (q - lane + (int64_t)u * kWave >= se)
+                break;              // (wave-uniform) the steps past the sub-range
             if (f[u] >= 0)
                 atomicAdd(&hw[w][f[u] >> shift], 1);
+        }
     }
     // thread t owns buckets [PER t, PER t + PER): their global starts (an
     // exclusive scan of total), this block's offset in each, then one cursor
@@ -251,6 +254,8 @@ __global__ __launch_bounds__(kL1Threads) void bucket_scatter_kernel(
         }
 #pragma unroll
         for (int u = 0; u < kSortUnroll; ++u) {
+            if (q + (int64_t)u * kWave >= se)
+                break;              // (wave-uniform) no item of this step or later ones
             const int64_t p = q + u * kWave + lane;
             const bool valid = p < se;
             const int pos = place_step((uint32_t)(f[u] >> shift), valid, nb_bits, hw[w]);
@@ -275,7 +280,7 @@ __global__ __launch_bounds__(kL2Threads) void bucket_sort_kernel(
     const int64_t f0 = (int64_t)blockIdx.x << shift;
     const int nbins = (int)(slots - f0 < B ? slots - f0 : B);
     const int beg = bucket_base[blockIdx.x], end = bucket_base[blockIdx.x + 1];
-    const int lane = lane_id(), w = threadIdx.x / kWave;
+    const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     for (int e = threadIdx.x; e < kSortWaves * kMaxBucketSlots; e += kL2Threads)
         (&hw[0][0])[e] = 0;
     int64_t sb, se;
@@ -291,9 +296,12 @@ __global__ __launch_bounds__(kL2Threads) void bucket_sort_kernel(
             key[u] = p < se ? pairs[p].y : -1;
         }
 #pragma unroll
-        for (int u = 0; u < kSortUnroll; ++u)
+        for (int u = 0; u < kSortUnroll; ++u) {
+            if (q - lane + (int64_t)u * kWave >= se)
+                break;              // (wave-uniform) the steps past the sub-range
             if (key[u] >= 0)
                 atomicAdd(&hw[w][key[u]], 1);
+        }
     }
     __syncthreads();
     // bin totals, their exclusive scan (thread t owns bins [BPT t, BPT t + BPT)),
@@ -347,6 +355,8 @@ __global__ __launch_bounds__(kL2Threads) void bucket_sort_kernel(
         }
 #pragma unroll
         for (int u = 0; u < kSortUnroll; ++u) {
+            if (q + (int64_t)u * kWave >= se)
+                break;              // (wave-uniform) no item of this step or later ones
             const bool valid = q + u * kWave + lane < se;
             const int pos = place_step((uint32_t)pr[u].y, valid, shift, hw[w]);
             if (valid)

@@ -85,6 +85,26 @@ def test_flat_edge(orc, case):
         assert np.array_equal(gpu_util.to_host(idx), ref["idx"]), "exact-arithmetic order differs"
 
 
+def test_flat_shared_codebooks_equal_replicated():
+    """PKM_KEYS_SHARED: one codebook pair [2][n][d_k/2] for all heads gives the
+    same bits as that pair replicated into every head's slot (the same
+    arithmetic on the same numbers; the kernel reads the pair with a head
+    stride of 0)."""
+    import product_key_memory_amd as pk
+    dev = gpu_util.device()
+    inp = pkm_inputs.custom(37, 3, 48, 8, 512, 16, dtype="bf16", seed=4711, kind="normal")
+    H = inp["w"].H
+    shared = np.ascontiguousarray(inp["keys"][0])
+    rep = np.ascontiguousarray(np.broadcast_to(shared, (H,) + shared.shape))
+    print(f"[flat shared] T=37 H={H} n=48 k=8", flush=True)
+    q, values = gpu_util.to_dev(inp["q"], dev), gpu_util.to_dev(inp["values"], dev)
+    out_s = pk.pkm_flat_forward(q, gpu_util.to_dev(shared, dev), values, 8)
+    out_r = pk.pkm_flat_forward(q, gpu_util.to_dev(rep, dev), values, 8)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("y", "idx", "weights", "scores"), out_s, out_r):
+        assert torch.equal(a, b), f"{name}: shared codebooks differ from the replicated ones"
+
+
 def test_flat_rejects_unsupported():
     import product_key_memory_amd as pk
     from product_key_memory_amd import PKMError

@@ -51,9 +51,10 @@ __device__ __forceinline__ float load_elem<bf16_t>(const bf16_t *p, int64_t i)
 
 // ---------------------------------------------------------------------------
 // 1. counting sort of the picks by slot, in two levels so that every counter
-//    lives in LDS: level 1 groups the picks by bucket = slot >> shift (at most
-//    2048 buckets) with per-block histograms; level 2 sorts each bucket by the
-//    low bits of the slot inside one workgroup.
+//    lives in LDS: level 1 groups the picks by bucket = slot >> shift (at
+//    most 4096 buckets of at least 128 slots) with per-block histograms;
+//    level 2 sorts each bucket by the low bits of the slot inside one
+//    workgroup.
 // ---------------------------------------------------------------------------
 constexpr int kL1Threads = 512;
 constexpr int kColWaves = 16;
@@ -181,8 +182,10 @@ __global__ __launch_bounds__(kL1Threads) void bucket_scatter_kernel(
     __shared__ int32_t hw[kSortWaves][kMaxBuckets];   // per-wave counts, then cursors
     __shared__ int32_t wsum[W];
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    for (int e = threadIdx.x; e < kSortWaves * kMaxBuckets; e += kL1Threads)
-        (&hw[0][0])[e] = 0;
+    // only the nb buckets in use (the rows are kMaxBuckets long)
+    for (int u = 0; u < kSortWaves; ++u)
+        for (int b = threadIdx.x; b < nb; b += kL1Threads)
+            hw[u][b] = 0;
     const int64_t p0 = l1_begin(chunk, picks);
     const int64_t p1 = p0 + chunk < picks ? p0 + chunk : picks;
     int64_t sb, se;
@@ -281,8 +284,10 @@ __global__ __launch_bounds__(kL2Threads) void bucket_sort_kernel(
     const int nbins = (int)(slots - f0 < B ? slots - f0 : B);
     const int beg = bucket_base[blockIdx.x], end = bucket_base[blockIdx.x + 1];
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    for (int e = threadIdx.x; e < kSortWaves * kMaxBucketSlots; e += kL2Threads)
-        (&hw[0][0])[e] = 0;
+    // only the B slots of a bucket (the rows are kMaxBucketSlots long)
+    for (int u = 0; u < kSortWaves; ++u)
+        for (int b = threadIdx.x; b < B; b += kL2Threads)
+            hw[u][b] = 0;
     int64_t sb, se;
     sub_range(beg, end, w, sb, se);
     __syncthreads();

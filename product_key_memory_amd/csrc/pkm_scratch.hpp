@@ -12,8 +12,11 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Scratch of the two-level slot sort: level-1 block histograms [blocks][buckets],
 // bucket totals and starts, and the (pick, low slot bits) pairs grouped by bucket.
-constexpr int kMaxBuckets = 2048;
+constexpr int kMaxBuckets = 4096;
 constexpr int kMaxBucketSlots = 1024;
+constexpr int kMinBucketShift = 7;    // buckets of at least 128 slots (measured: 2048
+                                      // buckets of 128 at 512^2 slots, 4096 of 256 at
+                                      // 1024^2 beat both finer and coarser ones)
 constexpr int kMaxL1Blocks = 256;
 
 struct SlotSortScratch {
@@ -28,7 +31,7 @@ inline SlotSortScratch slot_sort_scratch(int64_t picks, int n)
 {
     const int64_t slots = (int64_t)n * n;
     SlotSortScratch S;
-    S.shift = 0;
+    S.shift = kMinBucketShift;
     while ((slots + ((int64_t)1 << S.shift) - 1) >> S.shift > kMaxBuckets)
         ++S.shift;
     S.buckets = (int)((slots + ((int64_t)1 << S.shift) - 1) >> S.shift);

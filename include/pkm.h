@@ -86,8 +86,9 @@ typedef struct {
  * (backward = 2) need for this problem; 0 if none (the workspace may then be
  * NULL).  Returns (size_t)-1 for an invalid descriptor or another value of
  * `backward`.  The forward needs workspace only on its two-kernel selection
- * path (bf16, d_k = 512, 128 <= n <= 1024, k <= 32): T*H*2*k*8 bytes rounded up
- * to 256, for the per-half top-k lists. */
+ * path (d_k = 512, k <= 32, and 128 <= n <= 1024 for bf16 storage,
+ * 128 <= n <= 256 for float32): T*H*2*k*8 bytes rounded up to 256, for the
+ * per-half top-k lists. */
 size_t pkm_workspace_bytes(const pkm_problem_t *p, int backward);
 
 /*

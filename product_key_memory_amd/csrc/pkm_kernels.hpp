@@ -33,12 +33,16 @@ inline int merge_candidates(int k)
     return c;
 }
 
-// The two-kernel selection path: bf16 storage, query halves of exactly 256,
-// 128 <= n <= 1024, k <= 32.  Its per-half top-k lists pass through the
-// workspace: [T][H][2][k] entries of (score bits, sub-key), 8 bytes each.
+// The two-kernel selection path: query halves of exactly 256, k <= 32, and
+// 128 <= n <= 1024 for bf16 storage, 128 <= n <= 256 for float32.  Its
+// per-half top-k lists pass through the workspace: [T][H][2][k] entries of
+// (score bits, sub-key), 8 bytes each.
 inline bool select_fast_ok(int dtype, int n, int k, int d_k)
 {
-    return dtype == 1 && n >= 128 && n <= 1024 && k <= 32 && d_k == 512;
+    // bf16: 128 <= n <= 1024; float32 (scored on the fp64 MFMA, whose
+    // 64 query registers leave room for blocks of 256 sub-keys): n <= 256
+    const int n_max = dtype == 1 ? 1024 : dtype == 0 ? 256 : 0;
+    return n >= 128 && n <= n_max && k <= 32 && d_k == 512;
 }
 inline size_t select_workspace_bytes(int64_t T, int H, int n, int k, int dtype, int d_k)
 {
@@ -55,9 +59,9 @@ inline size_t select_workspace_bytes(int64_t T, int H, int n, int k, int dtype, 
 hipError_t launch_fwd_select(int dtype, const void *q, const void *keys, int64_t key_hstride,
                              int64_t T, int H, int n, int k, int d_k, int32_t *idx,
                              float *weights, float *scores, void *workspace, hipStream_t stream);
-hipError_t launch_select_fast(const void *q, const void *keys, int64_t key_hstride, int64_t T,
-                              int H, int n, int k, int d_k, int32_t *idx, float *weights,
-                              float *scores, void *workspace, hipStream_t stream);
+hipError_t launch_select_fast(int dtype, const void *q, const void *keys, int64_t key_hstride,
+                              int64_t T, int H, int n, int k, int d_k, int32_t *idx,
+                              float *weights, float *scores, void *workspace, hipStream_t stream);
 
 // The flat-key search: all n*n implied keys of each (token, head) scored
 // with one d_k-wide dot product, exact top-k, softmax (bf16, d_k = 512,

@@ -321,8 +321,8 @@ hipError_t launch_fwd_select(int dtype, const void *q, const void *keys, int64_t
                              float *weights, float *scores, void *workspace, hipStream_t stream)
 {
     if (select_fast_ok(dtype, n, k, d_k))
-        return launch_select_fast(q, keys, key_hstride, T, H, n, k, d_k, idx, weights, scores,
-                                  workspace, stream);
+        return launch_select_fast(dtype, q, keys, key_hstride, T, H, n, k, d_k, idx, weights,
+                                  scores, workspace, stream);
     if (dtype == 1)
         return launch_select_t<bf16_t>(q, keys, key_hstride, T, H, n, k, d_k, idx, weights,
                                        scores, stream);

@@ -1,5 +1,6 @@
-// pkm_select_fast.hip -- forward selection for bf16 storage, query halves of
-// 256, 128 <= n <= 1024, k <= 32, as two kernels (gptget.net summary of "Large
+// pkm_select_fast.hip -- forward selection for query halves of 256, k <= 32,
+// 128 <= n <= 1024 for bf16 storage and 128 <= n <= 256 for float32, as two
+// kernels (gptget.net summary of "Large
 // Memory Layers with Product Keys", "Methodology": split q into q1, q2, search
 // each against its own sub-key set, combine the best sub-keys; companion page
 // "Why top-k of each half is enough").
@@ -153,6 +154,91 @@ __device__ __forceinline__ void fast_scores(uint32_t (&so)[TILES][4], const uint
     __syncthreads();
 }
 
+// float32 storage: a codebook row is 256 floats (1 KB, 64 chunks of 16
+// bytes) and a step one tile of 16 rows (16 KB, double-buffered like the
+// bf16 steps, chunk c of row r at position c ^ (r % 16)).  The operands widen
+// exactly to float64 and v_mfma_f64_16x16x4_f64 accumulates in float64, so
+// each score is the exact dot product rounded once to float32.  A lane's K
+// slice of an MFMA is the same for A and B (element e of its float4 of K step
+// ks), so the 64 MFMAs of a tile sum every product once.  The f64 MFMA leaves
+// row 4 i + l / 16 of the tile in register i of lane l (the bf16 one: row
+// 4 (l / 16) + i); A row m is therefore read from local row 4 (m % 4) + m / 4,
+// which puts sub-key 4 g + i of the tile in register i of lane group g, the
+// layout the selection reads.
+constexpr int kF32Chunks = 64;                       // chunks of a 256-float row
+constexpr int kF32KSteps = 16;                       // float4 K steps: half = 256
+__device__ __forceinline__ void fast_step_f32(uint4 *__restrict__ fill, const uint4 *__restrict__ cur,
+                                              __amdgpu_buffer_rsrc_t rsrc, int p_next, int tid,
+                                              const float4 (&qf)[kF32KSteps], int r16, int g,
+                                              doublex4 &acc)
+{
+    constexpr int per_thread = 16 * kF32Chunks / (kFastWaves * kWave);
+    if (fill) {
+        const int wave = tid / kWave;
+#pragma unroll
+        for (int m = 0; m < per_thread; ++m) {
+            const int u = tid + m * kFastWaves * kWave;
+            const int rl = u / kF32Chunks, c = (u % kF32Chunks) ^ (rl & 15);
+            buffer_load_lds16(rsrc, fill + m * kFastWaves * kWave + wave * kWave,
+                              ((16 * p_next + rl) * kF32Chunks + c) * 16);
+        }
+    }
+    const int rr = (r16 & 3) << 2 | r16 >> 2;      // a permutation of 0..15
+    float4 a = __builtin_bit_cast(float4, cur[rr * kF32Chunks + (g ^ rr)]), b;
+#pragma unroll
+    for (int ks = 0; ks < kF32KSteps; ++ks) {
+        if (ks + 1 < kF32KSteps)
+            b = __builtin_bit_cast(float4, cur[rr * kF32Chunks + ((4 * (ks + 1) + g) ^ rr)]);
+        // an opaque copy of the query fragment: its widening to float64 stays
+        // here (hoisted out of the step loop, all 64 would need 128 registers)
+        float4 qv = qf[ks];
+        asm volatile("" : "+v"(qv.x), "+v"(qv.y), "+v"(qv.z), "+v"(qv.w));
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a.x, (double)qv.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a.y, (double)qv.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a.z, (double)qv.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a.w, (double)qv.w, acc, 0, 0, 0);
+        a = b;
+    }
+}
+
+template <int TILES>
+__device__ __forceinline__ void fast_scores_f32(uint32_t (&so)[TILES][4], const float *kb,
+                                                const float *qrow, int n_loc, int r16, int g,
+                                                uint4 *kbuf, int tid)
+{
+    constexpr int half = 16 * kF32KSteps;            // 256 floats per row
+    constexpr int step_units = 16 * kF32Chunks;      // 1024 chunks per 16-row step
+    const __amdgpu_buffer_rsrc_t rsrc = buffer_over(kb, n_loc * half * 4);
+    // B fragments: token `tok` (= r16), floats 16 ks + 4 g .. + 3
+    float4 qf[kF32KSteps];
+#pragma unroll
+    for (int ks = 0; ks < kF32KSteps; ++ks)
+        qf[ks] = *reinterpret_cast<const float4 *>(qrow + 16 * ks + 4 * g);
+    {
+        const int wave = tid / kWave;
+#pragma unroll
+        for (int m = 0; m < step_units / (kFastWaves * kWave); ++m) {
+            const int u = tid + m * kFastWaves * kWave;
+            const int rl = u / kF32Chunks, c = (u % kF32Chunks) ^ (rl & 15);
+            buffer_load_lds16(rsrc, kbuf + m * kFastWaves * kWave + wave * kWave,
+                              (rl * kF32Chunks + c) * 16);
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < TILES; ++p) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        doublex4 acc = {0.0, 0.0, 0.0, 0.0};
+        fast_step_f32(p + 1 < TILES ? kbuf + ((p + 1) & 1) * step_units : nullptr,
+                      kbuf + (p & 1) * step_units, rsrc, p + 1, tid, qf, r16, g, acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            so[p][i] = __float_as_uint((float)acc[i]);
+    }
+    // every wave is done with the last step's buffer before LDS is reused
+    __syncthreads();
+}
+
 // lists[((t H + h) 2 + s) k + e] = (ord score, sub-key) of the e-th best
 // sub-key of half s, e < k.  BLOCKS (1 or 2) blocks of TILES x 16 sub-keys
 // (TILES = 8, 16, 32: 128, 256, 512 sub-keys); the group maxima are over
@@ -161,13 +247,13 @@ __device__ __forceinline__ void fast_scores(uint32_t (&so)[TILES][4], const uint
 // groups, so tau is a real score and about k + 10 survive), the second
 // block, if any, holding the rest: template arguments so that each case
 // gets its own register allocation.
-template <int BLOCKS, int TILES>
+template <typename DT, int BLOCKS, int TILES>
 // Three waves per SIMD: the register budget (168) makes the compiler spill a
 // few dozen registers to scratch, which costs less than the latency a third
 // wave hides (measured: 0.186 -> 0.177 ms for the selection at n = 512, and
 // 0.61 -> 0.58 ms at n = 1024).
 __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_eu(3, 3))) void fwd_topk_half_kernel(
-    const bf16_t *__restrict__ q, const bf16_t *__restrict__ keys, int64_t key_hstride, int64_t T,
+    const DT *__restrict__ q, const DT *__restrict__ keys, int64_t key_hstride, int64_t T,
     int H, int n, int k, uint2 *__restrict__ lists)
 {
     // the codebook steps during the scoring, the survivors afterwards
@@ -192,11 +278,9 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
     uint32_t *surv_i = surv_i_all[wave] + tok * kSurvStride;
     uint64_t *prev = s_prev[wave][tok];
 
-    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(q) +
-                           ((live ? t : 0) * H + h) * (int64_t)d_k + (int64_t)s * half;
+    const DT *qrow = q + ((live ? t : 0) * H + h) * (int64_t)d_k + (int64_t)s * half;
     const int tid0 = threadIdx.x;
-    const uint16_t *kb =
-        reinterpret_cast<const uint16_t *>(keys) + h * key_hstride + (int64_t)s * n * half;
+    const DT *kb = keys + h * key_hstride + (int64_t)s * n * half;
 
     // one block of sub-keys; straight-line code for each block (a loop over
     // the blocks kept values alive across its back edge and cost a wave per
@@ -211,14 +295,20 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
         asm volatile("" : "+v"(g), "+v"(tid));
         const int base = kFirst ? 0 : (16 * TILES);
         const int n_loc = n - base < (16 * TILES) ? n - base : (16 * TILES);
-        // B fragments: token `tok`, K slice 32 kk + 8 g .. + 7 (loaded per
-        // block, so they are not held through the selection)
-        uint4 qf[kFastKSteps];
-#pragma unroll
-        for (int kk = 0; kk < kFastKSteps; ++kk)
-            qf[kk] = *reinterpret_cast<const uint4 *>(qrow + 32 * kk + 8 * g);
         uint32_t so[TILES][4];
-        fast_scores(so, kb + (int64_t)base * half, qf, n_loc, tok, g, lds, tid);
+        if constexpr (std::is_same<DT, float>::value) {
+            fast_scores_f32(so, kb + (int64_t)base * half, qrow, n_loc, tok, g, lds, tid);
+        } else {
+            // B fragments: token `tok`, K slice 32 kk + 8 g .. + 7 (loaded per
+            // block, so they are not held through the selection)
+            const uint16_t *qr = reinterpret_cast<const uint16_t *>(qrow);
+            uint4 qf[kFastKSteps];
+#pragma unroll
+            for (int kk = 0; kk < kFastKSteps; ++kk)
+                qf[kk] = *reinterpret_cast<const uint4 *>(qr + 32 * kk + 8 * g);
+            fast_scores(so, reinterpret_cast<const uint16_t *>(kb + (int64_t)base * half), qf, n_loc,
+                        tok, g, lds, tid);
+        }
         if (n_loc < (16 * TILES)) {
             // (an asm statement keeps this a branch: a whole block skips the
             // selects)
@@ -682,31 +772,39 @@ static int merge_bound_size(int k)
             return m;
 }
 
-hipError_t launch_select_fast(const void *q, const void *keys, int64_t key_hstride, int64_t T,
-                              int H, int n, int k, int d_k, int32_t *idx, float *weights,
-                              float *scores, void *workspace, hipStream_t stream)
+hipError_t launch_select_fast(int dtype, const void *q, const void *keys, int64_t key_hstride,
+                              int64_t T, int H, int n, int k, int d_k, int32_t *idx,
+                              float *weights, float *scores, void *workspace, hipStream_t stream)
 {
     (void)d_k;      // 512 on this path
     uint2 *lists = static_cast<uint2 *>(workspace);
     const dim3 grid((unsigned)((T + kFastTokWG - 1) / kFastTokWG), (unsigned)H, 2);
     // block shapes: the first block more than 3/4 full
-    auto go = [&](auto kern) {
+    auto go = [&](auto kern, auto dt) {
+        typedef decltype(dt) DT;
         hipLaunchKernelGGL(kern, grid, dim3(kFastWaves * kWave), 0, stream,
-                           static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(keys),
-                           key_hstride, T, H, n, k, lists);
+                           static_cast<const DT *>(q), static_cast<const DT *>(keys), key_hstride,
+                           T, H, n, k, lists);
     };
-    if (n <= 128)
-        go(fwd_topk_half_kernel<1, 8>);
+    if (dtype == 0) {
+        // float32 storage, n <= 256 (select_fast_ok): blocks of 128 sub-keys
+        // (a block of 256 with the float32 query fragments spills)
+        if (n <= 128)
+            go(fwd_topk_half_kernel<float, 1, 8>, float{});
+        else
+            go(fwd_topk_half_kernel<float, 2, 8>, float{});
+    } else if (n <= 128)
+        go(fwd_topk_half_kernel<bf16_t, 1, 8>, bf16_t{});
     else if (n <= 192)
-        go(fwd_topk_half_kernel<2, 8>);
+        go(fwd_topk_half_kernel<bf16_t, 2, 8>, bf16_t{});
     else if (n <= 256)
-        go(fwd_topk_half_kernel<1, 16>);
+        go(fwd_topk_half_kernel<bf16_t, 1, 16>, bf16_t{});
     else if (n <= 384)
-        go(fwd_topk_half_kernel<2, 16>);
+        go(fwd_topk_half_kernel<bf16_t, 2, 16>, bf16_t{});
     else if (n <= 512)
-        go(fwd_topk_half_kernel<1, 32>);
+        go(fwd_topk_half_kernel<bf16_t, 1, 32>, bf16_t{});
     else
-        go(fwd_topk_half_kernel<2, 32>);
+        go(fwd_topk_half_kernel<bf16_t, 2, 32>, bf16_t{});
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;

@@ -15,6 +15,10 @@ Rules (tolerances are relative, per row, L2):
     element by element, |gpu - oracle| <= tol * (|oracle| + rms of the row);
     y also element by element within the float32 summation bound plus (bf16)
     half a bfloat16 spacing -- what the arithmetic itself allows.
+  * dq and dkeys are compared with the oracle's backward at the weights the
+    GPU backward was handed; a row (or element) whose sum cancels far below
+    the size of its terms may instead lie within the float32 error bound of
+    that sum (grad_sum_bound): any rounding of a term then outweighs it.
   * value-gradient rows no pick selected must be exactly zero.
 """
 from __future__ import annotations
@@ -54,26 +58,30 @@ def check_selection(gpu_idx: np.ndarray, ref: dict, given: dict, n: int) -> dict
 
 
 def row_rel_err(got: np.ndarray, want: np.ndarray, floor: float = 1e-3,
-                abs_floor: float = 0.0) -> np.ndarray:
+                abs_floor: float = 0.0, den_floor=None) -> np.ndarray:
     """Per-row ||got - want|| / max(||want||, floor * rms row norm of want, abs_floor).
 
     abs_floor is for tensors whose exact value is (nearly) all zero, where the
     rms of the reference is itself rounding noise: the caller passes 1e-3 of
-    the size of one term of the sums that make a row."""
+    the size of one term of the sums that make a row.  den_floor, if given, is
+    a further per-row floor of the denominator."""
     got = got.reshape(got.shape[0], -1).astype(np.float64)
     want = want.reshape(want.shape[0], -1).astype(np.float64)
     norms = np.linalg.norm(want, axis=1)
     rms = np.sqrt(np.mean(norms ** 2)) if norms.size else 0.0
-    den = np.maximum(np.maximum(norms, floor * rms), abs_floor) + 1e-300
-    return np.linalg.norm(got - want, axis=1) / den
+    den = np.maximum(np.maximum(norms, floor * rms), abs_floor)
+    if den_floor is not None:
+        den = np.maximum(den, np.asarray(den_floor, np.float64).reshape(-1))
+    return np.linalg.norm(got - want, axis=1) / (den + 1e-300)
 
 
 def elem_rel_err(got: np.ndarray, want: np.ndarray, floor: float = 1e-3,
-                 abs_floor: float = 0.0) -> np.ndarray:
+                 abs_floor: float = 0.0, elem_floor=None) -> np.ndarray:
     """Per element |got - want| / (|want| + rms of want's row), rows = first
     axis.  The row term is floored like row_rel_err's denominator, scaled to
     one element: at floor * (rms row norm of the tensor) / sqrt(row length)
-    and at abs_floor / sqrt(row length)."""
+    and at abs_floor / sqrt(row length).  elem_floor, if given (the shape of
+    want), is added to each element's denominator."""
     got = got.reshape(got.shape[0], -1).astype(np.float64)
     want = want.reshape(want.shape[0], -1).astype(np.float64)
     if want.size == 0:
@@ -82,19 +90,85 @@ def elem_rel_err(got: np.ndarray, want: np.ndarray, floor: float = 1e-3,
     norms = np.linalg.norm(want, axis=1, keepdims=True)
     tensor_rms = np.sqrt(np.mean(norms ** 2))
     row = np.maximum(np.maximum(norms, floor * tensor_rms), abs_floor) / np.sqrt(ncol)
-    return np.abs(got - want) / (np.abs(want) + row + 1e-300)
+    den = np.abs(want) + row
+    if elem_floor is not None:
+        den = den + np.asarray(elem_floor, np.float64).reshape(want.shape)
+    return np.abs(got - want) / (den + 1e-300)
 
 
 def assert_elems_close(name: str, got, want, tol: float, floor: float = 1e-3,
-                       abs_floor: float = 0.0) -> float:
-    """Element by element: |g - o| <= tol * (|o| + rms of the row)."""
-    err = elem_rel_err(np.asarray(got), np.asarray(want), floor, abs_floor)
+                       abs_floor: float = 0.0, allow=None) -> float:
+    """Element by element: |g - o| <= tol * (|o| + rms of the row) + allow,
+    allow (the shape of want, or None) being an absolute rounding allowance
+    such as gpu_util.grad_sum_bound's."""
+    err = elem_rel_err(np.asarray(got), np.asarray(want), floor, abs_floor,
+                       None if allow is None else np.asarray(allow) / tol)
     worst = float(err.max()) if err.size else 0.0
     if err.size and worst > tol:
         at = np.unravel_index(int(err.argmax()), err.shape)
         raise AssertionError(f"{name}: worst element error {worst:.3e} > {tol:.1e} at (row, col) "
                              f"{tuple(int(x) for x in at)}")
     return worst
+
+
+def _widen(a: np.ndarray) -> np.ndarray:
+    """float64 copy of float32 data or of bfloat16 bit patterns (uint16)."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def grad_sum_bound(q, keys, values, idx, w, dy, shared: bool = False, chunk: int = 64) -> dict:
+    """Per element of dq [T][H][d_k] and dkeys ([H][2][n][d_k/2], or
+    [2][n][d_k/2] summed over the heads when `shared`): how far a float32
+    evaluation may lie from the exact gradients at the same weights w, in any
+    order of the sums.
+
+    Pick e of (t, h) (slot f = i n + j) has dw_e = <dy_t, values[f]> (d_v
+    multiply-adds), s = sum_e' w_e' dw_e' (k more) and ds_e = w_e (dw_e - s);
+    with a_e = sum_c |dy_t[c]| |values[f][c]|, every rounding up to ds_e is
+    covered by m_e = |w_e| (a_e + sum_e' |w_e'| a_e').  An element of dq or
+    dkeys sums r products ds_e x (x a sub-key or query element: one more
+    rounding each), so the classic bound on chains of rounded operations gives
+        |error| <= gamma(d_v + k + 3 + r) * sum_e m_e |x|,
+    gamma(m) = m u / (1 - m u), u = 2^-24, r = k for dq and the number of
+    picks of the sub-key for dkeys.  Exact-arithmetic cancellation (a token
+    whose k picks share a sub-key contributes sum_e ds_e = s (1 - sum w) ~ 0)
+    leaves results far below sum_e m_e |x|: only this bound holds there."""
+    T, H, k = idx.shape
+    n, half = keys.shape[-2], keys.shape[-1]
+    d_v = values.shape[1]
+    qa = np.abs(_widen(q)).reshape(T, H, 2, half)
+    ka = np.abs(_widen(keys)).reshape(-1, 2, n, half)
+    va, dya = np.abs(_widen(values)), np.abs(_widen(dy))
+    a = np.empty((T, H, k))
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        rows = va[idx[t0:t1].reshape(-1)].reshape(t1 - t0, H * k, d_v)
+        a[t0:t1] = np.einsum("tpc,tc->tp", rows, dya[t0:t1]).reshape(t1 - t0, H, k)
+    aw = np.abs(np.asarray(w, np.float64))
+    m = aw * (a + np.sum(aw * a, axis=2, keepdims=True))
+    u = 2.0 ** -24
+
+    def gamma(r):
+        r = np.asarray(r, np.float64)
+        return r * u / (1.0 - r * u)
+
+    dq = np.empty((T, H, 2, half))
+    dk = np.zeros((1 if shared else H, 2, n, half))
+    picks = np.zeros((1 if shared else H, 2, n))
+    mag = np.zeros_like(dk)
+    tt = np.repeat(np.arange(T), k)
+    for h in range(H):
+        hk = 0 if shared else h
+        for s, sub in ((0, idx[:, h] // n), (1, idx[:, h] % n)):
+            M = np.zeros((T, n))             # M[t][i] = sum of m_e over t's picks of sub-key i
+            np.add.at(M, (tt, sub.reshape(-1)), m[:, h].reshape(-1))
+            dq[:, h, s] = gamma(d_v + 2 * k + 3) * (M @ ka[0 if shared else h, s])
+            mag[hk, s] += M.T @ qa[:, h, s]
+            picks[hk, s] += np.bincount(sub.reshape(-1), minlength=n)
+    dk = gamma(d_v + k + 3 + picks)[..., None] * mag
+    return {"dq": dq.reshape(T, H, 2 * half), "dkeys": dk[0] if shared else dk}
 
 
 def bf16_ulp(x: np.ndarray) -> np.ndarray:
@@ -124,8 +198,15 @@ def assert_y_bound(name: str, got, want, bound, storage: str) -> float:
 
 
 def assert_rows_close(name: str, got, want, tol: float, floor: float = 1e-3,
-                      abs_floor: float = 0.0) -> float:
-    err = row_rel_err(np.asarray(got), np.asarray(want), floor, abs_floor)
+                      abs_floor: float = 0.0, allow=None) -> float:
+    """Row by row: ||g - o|| <= tol * max(||o||, floors), or within the norm
+    of the row of `allow` (an absolute per-element rounding allowance such as
+    gpu_util.grad_sum_bound's, the shape of want; None for none)."""
+    den_floor = None
+    if allow is not None:
+        a = np.asarray(allow, np.float64)
+        den_floor = np.linalg.norm(a.reshape(a.shape[0], -1), axis=1) / tol
+    err = row_rel_err(np.asarray(got), np.asarray(want), floor, abs_floor, den_floor)
     worst = float(err.max()) if err.size else 0.0
     assert worst <= tol, f"{name}: worst row relative error {worst:.3e} > {tol:.1e} (row {int(err.argmax())})"
     return worst

@@ -143,8 +143,9 @@ def test_status_strings():
 
 
 def test_forward_workspace_checks():
-    """The two-kernel selection (bf16, d_k = 512, 128 <= n <= 1024, k <= 32)
-    keeps its per-half top-k lists in the caller's workspace."""
+    """The two-kernel selection (d_k = 512, k <= 32, 128 <= n <= 1024 for bf16
+    and 128 <= n <= 256 for float32) keeps its per-half top-k lists in the
+    caller's workspace."""
     p = P(T=100, H=3, n=300, k=20, d_k=512, d_v=64, dtype=_lib.PKM_BF16)
     need = _lib.workspace_bytes(p, False)
     assert need == (100 * 3 * 2 * 20 * 8 + 255) // 256 * 256
@@ -161,6 +162,12 @@ def test_forward_workspace_checks():
     for n, k in ((127, 20), (1024, 33)):
         assert _lib.workspace_bytes(P(T=100, H=3, n=n, k=k, d_k=512, d_v=64,
                                       dtype=_lib.PKM_BF16), False) == 0
+    # float32 storage: the two-kernel path for 128 <= n <= 256 only
+    for n, k, on in ((128, 16, True), (256, 32, True), (127, 16, False), (257, 16, False),
+                     (200, 33, False)):
+        got = _lib.workspace_bytes(P(T=100, H=3, n=n, k=k, d_k=512, d_v=64, dtype=_lib.PKM_FP32),
+                                   False)
+        assert got == ((100 * 3 * 2 * k * 8 + 255) // 256 * 256 if on else 0), (n, k)
 
 
 def QP(**kw):

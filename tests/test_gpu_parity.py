@@ -110,8 +110,9 @@ def test_edge(orc, case, dtype):
     assert rep["rows"] == T * H
 
 
-# the two-kernel selection (bf16, d_k = 512, 128 <= n <= 1024, k <= 32): per-half
-# top-k over blocks of 512 sub-keys (256 for n <= 256), then the pruned combine
+# the two-kernel selection (d_k = 512, k <= 32; bf16 with 128 <= n <= 1024,
+# float32 with 128 <= n <= 256): per-half top-k over blocks of 128, 256 or 512
+# sub-keys, then the pruned combine
 FAST_EDGE = [
     (50, 2, 128, 16, 512, 16, "normal"),      # smallest n on the path: 256-sub-key blocks, groups of 4
     (37, 3, 200, 32, 512, 24, "dup"),         # ragged n in a 256-block, duplicated sub-keys
@@ -131,19 +132,29 @@ FAST_EDGE = [
     (12, 1, 1024, 32, 512, 16, "right_zero"),  # the exact branch in both blocks
     (30, 2, 700, 5, 512, 16, "integer"),       # exact arithmetic across the blocks
 ]
+FAST_EDGE = [c + ("bf16",) for c in FAST_EDGE] + [
+    # float32 storage, scored on the fp64 MFMA in blocks of 128 sub-keys
+    (50, 2, 128, 16, 512, 16, "normal", "fp32"),      # one block
+    (37, 3, 200, 32, 512, 24, "dup", "fp32"),         # two blocks, duplicated sub-keys
+    (40, 2, 129, 32, 512, 16, "normal", "fp32"),      # a second block of one sub-key (< k)
+    (20, 1, 256, 32, 512, 16, "right_zero", "fp32"),  # the exact bisection in both blocks
+    (33, 2, 130, 7, 512, 16, "integer", "fp32"),      # exact arithmetic: the oracle's order
+]
 
 
-@pytest.mark.parametrize("case", FAST_EDGE, ids=[f"T{c[0]}H{c[1]}n{c[2]}k{c[3]}-{c[6]}" for c in FAST_EDGE])
+@pytest.mark.parametrize("case", FAST_EDGE,
+                         ids=[f"T{c[0]}H{c[1]}n{c[2]}k{c[3]}-{c[6]}-{c[7]}" for c in FAST_EDGE])
 def test_edge_two_kernel_selection(orc, case):
     import product_key_memory_amd as pk
     from product_key_memory_amd import _lib
-    T, H, n, k, d_k, d_v, kind = case
+    T, H, n, k, d_k, d_v, kind, dtype = case
+    code = _lib.PKM_BF16 if dtype == "bf16" else _lib.PKM_FP32
     # this shape takes the two-kernel path: it is the one that needs a forward workspace
-    assert _lib.workspace_bytes(_lib.Problem(T, H, n, k, d_k, d_v, _lib.PKM_BF16), False) > 0
-    inp = pkm_inputs.custom(T, H, n, k, d_k, d_v, dtype="bf16", seed=T * 131 + n + 7, kind=kind)
-    rep = gpu_util.run_parity(orc, inp, k, backward=True, tight=TIGHT["bf16"])
+    assert _lib.workspace_bytes(_lib.Problem(T, H, n, k, d_k, d_v, code), False) > 0
+    inp = pkm_inputs.custom(T, H, n, k, d_k, d_v, dtype=dtype, seed=T * 131 + n + 7, kind=kind)
+    rep = gpu_util.run_parity(orc, inp, k, backward=True, tight=TIGHT[dtype])
     assert rep["rows"] == T * H
-    if kind == "integer":
+    if kind == "integer" or (kind == "right_zero" and dtype == "fp32"):
         # exact arithmetic: the order itself, ties included, is the oracle's
         dev = gpu_util.device()
         q, keys, values = (gpu_util.to_dev(inp[x], dev) for x in ("q", "keys", "values"))
@@ -157,16 +168,18 @@ def test_edge_two_kernel_selection(orc, case):
 # (more than 64 survivors in both halves): the lanes past T must keep nothing,
 # also in waves whose live tokens need no bisection and in waves with no live
 # token at all, and must not disturb the live tokens' survivors.
-TAIL_CASES = [(65, 512), (100, 512), (112, 512), (100, 1024), (100, 200)]
+TAIL_CASES = [(65, 512, "bf16"), (100, 512, "bf16"), (112, 512, "bf16"), (100, 1024, "bf16"),
+              (100, 200, "bf16"), (100, 200, "fp32")]
 
 
-@pytest.mark.parametrize("T,n", TAIL_CASES, ids=[f"T{c[0]}n{c[1]}" for c in TAIL_CASES])
-def test_two_kernel_selection_tail_tokens_with_tied_token0(orc, T, n):
+@pytest.mark.parametrize("T,n,dtype", TAIL_CASES, ids=[f"T{c[0]}n{c[1]}-{c[2]}" for c in TAIL_CASES])
+def test_two_kernel_selection_tail_tokens_with_tied_token0(orc, T, n, dtype):
     from product_key_memory_amd import _lib
-    assert _lib.workspace_bytes(_lib.Problem(T, 2, n, 32, 512, 16, _lib.PKM_BF16), False) > 0
-    inp = pkm_inputs.custom(T, 2, n, 32, 512, 16, dtype="bf16", seed=T + n)
-    inp["q"][0] = 0          # bfloat16 +0: every score of token 0 is exactly 0
-    rep = gpu_util.run_parity(orc, inp, 32, tight=TIGHT["bf16"])
+    code = _lib.PKM_BF16 if dtype == "bf16" else _lib.PKM_FP32
+    assert _lib.workspace_bytes(_lib.Problem(T, 2, n, 32, 512, 16, code), False) > 0
+    inp = pkm_inputs.custom(T, 2, n, 32, 512, 16, dtype=dtype, seed=T + n)
+    inp["q"][0] = 0          # +0: every score of token 0 is exactly 0
+    rep = gpu_util.run_parity(orc, inp, 32, tight=TIGHT[dtype])
     assert rep["rows"] == T * 2
 
 

@@ -54,14 +54,17 @@ def test_shared_codebooks(orc, case):
     g_y = gpu_util.bits_to_f64(gpu_util.to_host(y))
     parity.assert_rows_close("y", g_y, given["y"], tol)
     parity.assert_elems_close("y", g_y, given["y"], tol)
-    ob = orc.backward(inp["q"], rep, inp["values"], g_idx, given["weights"], inp["dy"])
+    w_in = g_w.astype(np.float64)            # the weights the backward was handed
+    ob = orc.backward(inp["q"], rep, inp["values"], g_idx, w_in, inp["dy"])
+    allow = parity.grad_sum_bound(inp["q"], shared, inp["values"], g_idx, w_in, inp["dy"], shared=True)
     half = d_k // 2
-    parity.assert_rows_close("dq", gpu_util.to_host(dq), ob["dq"], tol)
-    parity.assert_elems_close("dq", gpu_util.to_host(dq), ob["dq"], tol)
+    parity.assert_rows_close("dq", gpu_util.to_host(dq), ob["dq"], tol, allow=allow["dq"])
+    parity.assert_elems_close("dq", gpu_util.to_host(dq), ob["dq"], tol, allow=allow["dq"])
     want = ob["dkeys"].sum(axis=0).reshape(-1, half)
     got = gpu_util.to_host(dkeys).reshape(-1, half)
-    parity.assert_rows_close("dkeys (summed over heads)", got, want, tol)
-    parity.assert_elems_close("dkeys (summed over heads)", got, want, tol)
+    a_dk = allow["dkeys"].reshape(-1, half)
+    parity.assert_rows_close("dkeys (summed over heads)", got, want, tol, allow=a_dk)
+    parity.assert_elems_close("dkeys (summed over heads)", got, want, tol, allow=a_dk)
     # the fold over heads against the per-head sub-key gradient of the replicated run
     summed = dkeys_r.double().sum(dim=0).cpu().numpy().reshape(-1, half)
     parity.assert_rows_close("dkeys vs replicated", got, summed, 1e-5)

@@ -18,6 +18,7 @@ pytestmark = pytest.mark.gpu
 CASES = [
     # dtype, T, H, n, k, d_k, d_v
     ("fp32", 40, 3, 37, 5, 48, 24),        # the one-kernel selection, fp32 storage
+    ("fp32", 100, 3, 200, 20, 512, 24),    # the two-kernel selection, fp32 storage
     ("bf16", 40, 3, 37, 5, 48, 24),
     ("bf16", 100, 3, 300, 20, 512, 24),    # the two-kernel selection
     ("bf16", 2048, 4, 512, 32, 512, 64),   # the benchmark's memory shape

@@ -45,8 +45,9 @@
 extern "C" {
 #endif
 
-/* Storage type of q, keys, values, y and dy.  Arithmetic is always float32
- * (products of bfloat16 operands are exact in float32). */
+/* Storage type of q, keys, values, y and dy.  Arithmetic is float32
+ * (products of bfloat16 operands are exact in float32), except the sub-key
+ * scores of float32 storage: float64 sums, each rounded once to float32. */
 typedef enum { PKM_FP32 = 0, PKM_BF16 = 1 } pkm_dtype_t;
 
 typedef enum {

@@ -89,6 +89,13 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask)
     return ((uint64_t)hi << 32) | lo;
 }
 
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src)
+{
+    const uint32_t lo = __shfl((int)(uint32_t)v, src);
+    const uint32_t hi = __shfl((int)(uint32_t)(v >> 32), src);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ float wave_sum(float v)
 {
 #pragma unroll

@@ -567,9 +567,10 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
 constexpr int kMaxCorners = 16;
 constexpr int kMergeSurv = 60;      // + a spare slot per lane group: < 64 per row
 
+// list entries as staged in LDS: (score as float bits, sub-key)
 __device__ __forceinline__ float merge_score(uint2 l, uint2 r)
 {
-    return unord_f32(l.x) + unord_f32(r.x);
+    return __uint_as_float(l.x) + __uint_as_float(r.x);
 }
 
 __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
@@ -611,10 +612,11 @@ __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
         for (int u = 0; u < kPerLane; ++u) {
             const int e = lane + u * kWave;
             if (e < units) {
-                // entries 2 e, 2 e + 1 lie in one row (a row has 2 k entries)
+                // entries 2 e, 2 e + 1 lie in one row (a row has 2 k entries);
+                // the scores go back to floats once here, not per candidate
                 uint2 *d = sl + (e / k) * kMergePitch + 2 * (e % k);
-                d[0] = make_uint2(buf[u].x, buf[u].y);
-                d[1] = make_uint2(buf[u].z, buf[u].w);
+                d[0] = make_uint2(__float_as_uint(unord_f32(buf[u].x)), buf[u].y);
+                d[1] = make_uint2(__float_as_uint(unord_f32(buf[u].z)), buf[u].w);
             }
         }
     }
@@ -740,25 +742,60 @@ __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
     }
     group4_sort_desc<16>(w);
 
-    // ranks 16 g + q sit in lane groups 0 and 1; the softmax sums both
+    // ranks 16 g + q sit in lane groups 0 and 1 (k <= 32); lane group g'
+    // takes ranks 8 g' .. 8 g' + 7, registers 8 (g' % 2) + r of lane group
+    // g' / 2, so the softmax and the stores are spread over all four lanes
+    const int src = tok + 16 * (g >> 1);
+    uint64_t x[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const uint64_t a = shfl_u64(w[r], src), b = shfl_u64(w[8 + r], src);
+        x[r] = (g & 1) ? b : a;
+    }
     const int64_t out = (row0 + tok) * (int64_t)k;
     const float top = __shfl(key_score(w[0]), tok);
-    float ex[16], z = 0.f;
+    const int e0 = 8 * g;
+    float ex[8], z = 0.f;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        ex[q] = 16 * g + q < k ? expf(key_score(w[q]) - top) : 0.f;
-        z += ex[q];
+    for (int r = 0; r < 8; ++r) {
+        ex[r] = e0 + r < k ? expf(key_score(x[r]) - top) : 0.f;
+        z += ex[r];
     }
     z += __shfl_xor(z, 16);
-    if (live && g < 2) {
+    z += __shfl_xor(z, 32);
+    if (live && e0 < k) {
+        int32_t oi[8];
+        float ow[8], os[8];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int e = 16 * g + q;
-            if (e < k) {
-                idx[out + e] = (int32_t)key_index(w[q]);
-                weights[out + e] = ex[q] / z;
-                if (scores)
-                    scores[out + e] = key_score(w[q]);
+        for (int r = 0; r < 8; ++r) {
+            oi[r] = (int32_t)key_index(x[r]);
+            ow[r] = ex[r] / z;
+            os[r] = key_score(x[r]);
+        }
+        if ((k & 3) == 0) {
+            // 16-byte stores: out + e0 is a multiple of 4 and so is k - e0
+#pragma unroll
+            for (int h4 = 0; h4 < 2; ++h4) {
+                if (e0 + 4 * h4 < k) {
+                    const int at = e0 + 4 * h4;
+                    *reinterpret_cast<int4 *>(idx + out + at) =
+                        make_int4(oi[4 * h4], oi[4 * h4 + 1], oi[4 * h4 + 2], oi[4 * h4 + 3]);
+                    *reinterpret_cast<float4 *>(weights + out + at) =
+                        make_float4(ow[4 * h4], ow[4 * h4 + 1], ow[4 * h4 + 2], ow[4 * h4 + 3]);
+                    if (scores)
+                        *reinterpret_cast<float4 *>(scores + out + at) =
+                            make_float4(os[4 * h4], os[4 * h4 + 1], os[4 * h4 + 2], os[4 * h4 + 3]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                if (e0 + r < k) {
+                    idx[out + e0 + r] = oi[r];
+                    weights[out + e0 + r] = ow[r];
+                    if (scores)
+                        scores[out + e0 + r] = os[r];
+                }
             }
         }
     }

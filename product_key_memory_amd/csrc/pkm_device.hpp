@@ -77,6 +77,42 @@ __device__ __forceinline__ uint64_t make_key(float s, uint32_t index)
 __device__ __forceinline__ float key_score(uint64_t key) { return unord_f32((uint32_t)(key >> 32)); }
 __device__ __forceinline__ uint32_t key_index(uint64_t key) { return ~(uint32_t)key; }
 
+// Keys that sort as float64 values.  For an index below 2^IB (IB <= 20) the
+// key 2^52 + ord * 2^IB + (2^IB - 1 - index) has bit 52 set and nothing above
+// it, so its bit pattern is a positive normal float64 (biased exponent 1),
+// and float64 order, integer order and (score descending, index ascending)
+// all agree.  A sort then exchanges two keys with one v_max_f64 and one
+// v_min_f64 instead of a 64-bit compare and four selects.  0 (+0.0) is below
+// every key and pads a sort.
+template <int IB>
+__device__ __forceinline__ uint64_t dkey(uint32_t ord, uint32_t index)
+{
+    static_assert(IB >= 1 && IB <= 20, "the key must stay below 2^53");
+    return (1ull << 52) | ((uint64_t)ord << IB) | (uint64_t)((1u << IB) - 1u - index);
+}
+template <int IB>
+__device__ __forceinline__ uint32_t dkey_ord(uint64_t key) { return (uint32_t)(key >> IB); }
+template <int IB>
+__device__ __forceinline__ uint32_t dkey_index(uint64_t key)
+{
+    return (1u << IB) - 1u - ((uint32_t)key & ((1u << IB) - 1u));
+}
+// max / min of two such keys.  Written as instructions so that the compiler
+// adds no canonicalisation of the operands (they are bit patterns of normal
+// numbers, never NaN, so the IEEE max / min is the plain order).
+__device__ __forceinline__ uint64_t dkey_max(uint64_t a, uint64_t b)
+{
+    uint64_t r;
+    asm("v_max_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ uint64_t dkey_min(uint64_t a, uint64_t b)
+{
+    uint64_t r;
+    asm("v_min_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // ---------------------------------------------------------------------------
 // wave64 primitives
 // ---------------------------------------------------------------------------
@@ -355,6 +391,56 @@ __device__ __forceinline__ T group4_kth(T (&v)[16], int k)
         if (r == ((k - 1) & 15))
             x = v[r];
     return g4_bcast(x, (lane_id() & 15) + 16 * ((k - 1) >> 4));
+}
+
+// Descending sort of the 64 keys (dkey format, or 0) a 4-lane group holds,
+// 16 a lane (element e = 16 (lane / 16) + r in register r).  The network is
+// group4_kth's: every merge of size s starts by exchanging element e with its
+// mirror e ^ (s - 1), so every exchange keeps the larger key at the lower
+// position -- in-lane exchanges are one max and one min, with no compare and
+// no direction.
+__device__ __forceinline__ void group4_sort_desc_dkey(uint64_t (&v)[16])
+{
+    const int g = lane_id() >> 4;
+    auto inlane = [&](int r, int r2) {
+        const uint64_t a = v[r], b = v[r2];
+        v[r] = dkey_max(a, b);
+        v[r2] = dkey_min(a, b);
+    };
+    auto runs16 = [&](int from) {
+#pragma unroll
+        for (int stride = 8; stride > 0; stride >>= 1)
+            if (stride <= from)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if ((r & stride) == 0)
+                        inlane(r, r | stride);
+    };
+    // with lane group g ^ (lanes / 16), register 15 - r (mirror) or r; the
+    // lower lane group keeps the larger key
+    auto cross = [&](int lanes, bool mirror, bool lower) {
+        uint64_t o[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            o[r] = shfl_xor_u64(v[mirror ? 15 - r : r], lanes);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            v[r] = lower ? dkey_max(v[r], o[r]) : dkey_min(v[r], o[r]);
+    };
+#pragma unroll
+    for (int size = 2; size <= 16; size <<= 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if ((r & (size >> 1)) == 0)
+                inlane(r, r ^ (size - 1));
+        runs16(size >> 2);
+    }
+    cross(16, true, (g & 1) == 0);      // size 32: e ^ 31 = lane group g ^ 1, register 15 - r
+    runs16(8);
+    cross(48, true, g < 2);             // size 64: e ^ 63 = lane group g ^ 3, register 15 - r
+    cross(16, false, (g & 1) == 0);     // stride 16
+    runs16(8);
 }
 
 template <int R, typename T>

@@ -19,7 +19,9 @@
 //        the k groups above it each hold a score >= tau, so at least k
 //        scores survive;
 //      - survivors (score >= tau) are compacted into LDS and sorted as 64-bit
-//        keys (score, then lower index first) inside the 4-lane group; when a
+//        keys (score, then lower index first) inside the 4-lane group -- keys
+//        whose bit patterns are normal float64 numbers of the same order, so
+//        each exchange is one float64 max and one min; when a
 //        token has more than 64 survivors (heavy ties) its exact k-th largest
 //        key is found by bisection on the score bits, then on the index among
 //        exact ties, and exactly k survive;
@@ -52,6 +54,8 @@ constexpr int kFastBlock = 16 * kFastTiles;          // 512 sub-keys per block (
 constexpr int kFastKSteps = 8;                       // 32-wide K steps: half = 256
 constexpr int kFastSurv = 64;                        // survivors per token at most
 constexpr int kSurvStride = kFastSurv + 4;           // + one spare slot per lane group
+constexpr int kSubBits = 10;                         // sub-key index < n <= 1024
+constexpr int kSlotBits = 20;                        // slot i n + j < n^2 <= 2^20
 constexpr int kMergeWaves = 4;
 constexpr int kMergeRows = 16;                       // (token, head) rows per wave
 constexpr int kMaxPairs = 128;                       // merge_candidates(32) = 119
@@ -344,7 +348,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
         // first block's k-th key (a real score) raises the bar, and keys
         // below it cannot reach the top k anyway.
         if constexpr (!kFirst)
-            tau = fmaxf(tau, unord_f32((uint32_t)(prev[k - 1] >> 32)));
+            tau = fmaxf(tau, unord_f32(dkey_ord<kSubBits>(prev[k - 1])));
         // a token past T (it scored token 0's query) keeps nothing: no score
         // compares >= NaN, so it counts no survivor, takes no bisection and
         // claims no position in the compaction (its 4 lanes share `live`)
@@ -484,11 +488,10 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
             const int src_g = (e >= b1 ? 1 : 0) + (e >= b2 ? 1 : 0) + (e >= b3 ? 1 : 0);
             const uint32_t sv = surv_s[e + src_g];
             const uint32_t hi = ordm ? sv : ord_f32(__uint_as_float(sv));
-            v[r] = e < total ? ((uint64_t)hi << 32) |
-                                   (uint64_t)~(surv_i[e + src_g] + 4u * (uint32_t)src_g + (uint32_t)base)
+            v[r] = e < total ? dkey<kSubBits>(hi, surv_i[e + src_g] + 4u * (uint32_t)src_g + (uint32_t)base)
                              : 0ull;
         }
-        group4_sort_desc<16>(v);
+        group4_sort_desc_dkey(v);
         // lane group g holds ranks 16 g .. 16 g + 15 of the block
         if constexpr (!kFirst) {
             // top k of the two sorted lists A (first block) and B (this one):
@@ -542,7 +545,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
             for (int r = 0; r < 16; ++r) {
                 const int e = 16 * g + r;
                 if (e < k)
-                    out[e] = make_uint2((uint32_t)(v[r] >> 32), ~(uint32_t)v[r]);
+                    out[e] = make_uint2(dkey_ord<kSubBits>(v[r]), dkey_index<kSubBits>(v[r]));
             }
         }
     };
@@ -650,11 +653,11 @@ __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
         if (live && pc < n_pairs) {
             const int a = s_pairs[pc] & 0xFF, b = s_pairs[pc] >> 8;
             const uint2 la = l[a], rb = r[b];
-            v[c] = make_key(merge_score(la, rb), la.y * (uint32_t)n + rb.y);
+            v[c] = dkey<kSlotBits>(ord_f32(merge_score(la, rb)), la.y * (uint32_t)n + rb.y);
         } else {
             v[c] = 0ull;
         }
-        cnt += (uint32_t)(v[c] >> 32) >= otau ? 1 : 0;
+        cnt += dkey_ord<kSlotBits>(v[c]) >= otau ? 1 : 0;
     }
     if (!live)
         cnt = 0;        // rows past the end keep nothing
@@ -663,7 +666,7 @@ __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
         int c = 0;
 #pragma unroll
         for (int e = 0; e < 32; ++e)
-            c += (uint32_t)(v[e] >> 32) >= o ? 1 : 0;
+            c += dkey_ord<kSlotBits>(v[e]) >= o ? 1 : 0;
         return c;
     };
     // Raise the bound while more than kMergeSurv survive: bisection on the
@@ -691,11 +694,11 @@ __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
     // Rows still above (heavy ties): the exact k-th largest key by bisection
     // on the 64-bit keys, which are distinct (the slot is part of the key);
     // exactly k keys are >= it.
-    uint64_t kth = live ? (uint64_t)otau << 32 : ~0ull;
+    uint64_t kth = live ? dkey<kSlotBits>(otau, (1u << kSlotBits) - 1u) : ~0ull;
     if (__ballot(live && total > kMergeSurv) != 0) {
         const bool more = live && total > kMergeSurv;
         uint64_t K = 0;
-        for (int bit = 63; bit >= 0; --bit) {
+        for (int bit = 52; bit >= 0; --bit) {     // every key is below 2^53
             const uint64_t cand = K | (1ull << bit);
             int c = 0;
 #pragma unroll
@@ -740,7 +743,7 @@ __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
         const int src_g = (e >= b1 ? 1 : 0) + (e >= b2 ? 1 : 0) + (e >= b3 ? 1 : 0);
         w[q] = live && e < total ? surv[e + src_g] : 0ull;
     }
-    group4_sort_desc<16>(w);
+    group4_sort_desc_dkey(w);
 
     // ranks 16 g + q sit in lane groups 0 and 1 (k <= 32); lane group g'
     // takes ranks 8 g' .. 8 g' + 7, registers 8 (g' % 2) + r of lane group
@@ -753,12 +756,12 @@ __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
         x[r] = (g & 1) ? b : a;
     }
     const int64_t out = (row0 + tok) * (int64_t)k;
-    const float top = __shfl(key_score(w[0]), tok);
+    const float top = __shfl(unord_f32(dkey_ord<kSlotBits>(w[0])), tok);
     const int e0 = 8 * g;
     float ex[8], z = 0.f;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-        ex[r] = e0 + r < k ? expf(key_score(x[r]) - top) : 0.f;
+        ex[r] = e0 + r < k ? expf(unord_f32(dkey_ord<kSlotBits>(x[r])) - top) : 0.f;
         z += ex[r];
     }
     z += __shfl_xor(z, 16);
@@ -768,9 +771,9 @@ __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
         float ow[8], os[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            oi[r] = (int32_t)key_index(x[r]);
+            oi[r] = (int32_t)dkey_index<kSlotBits>(x[r]);
             ow[r] = ex[r] / z;
-            os[r] = key_score(x[r]);
+            os[r] = unord_f32(dkey_ord<kSlotBits>(x[r]));
         }
         if ((k & 3) == 0) {
             // 16-byte stores: out + e0 is a multiple of 4 and so is k - e0

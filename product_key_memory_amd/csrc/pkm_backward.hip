@@ -1007,7 +1007,7 @@ __global__ __launch_bounds__(kQryWaves *kWave) void bwd_query_kernel(
         const float l_g = in_list ? s_g[wv][lane] : 0.f;
 
         // dq half += g * sub-key row, kBatch rows in flight, each entry 4 JPL
-        // FMAs; a segment's unused tail is skipped 8 entries at a time
+        // FMAs; a segment's unused tail is skipped 4 entries at a time
 #pragma unroll
         for (int sg = 0; sg < 2; ++sg) {
 #pragma unroll
@@ -1026,7 +1026,7 @@ __global__ __launch_bounds__(kQryWaves *kWave) void bwd_query_kernel(
                 }
 #pragma unroll
                 for (int u = 0; u < kBatch; ++u) {
-                    if (u % 8 == 0 && first_e + u >= seg_cnt[sg])
+                    if (u % 4 == 0 && first_e + u >= seg_cnt[sg])
                         break;
                     const float gv = __int_as_float(
                         __builtin_amdgcn_readlane(__float_as_int(l_g), 32 * sg + first_e + u));

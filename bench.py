@@ -240,9 +240,11 @@ def _csv_rows(directory: str, suffix: str) -> list:
 
 
 def record_counters(pmc_a: str, pmc_b: str, pmc_dram: str, trace: str, workload: str) -> str:
-    """Per kernel: mean duration of its dispatches in the trace pass; means of
-    the counters per dispatch in the three counter passes; rates against
-    1024 SIMDs x duration x 2.4 GHz."""
+    """Per kernel: median duration of its dispatches in the trace pass (a
+    cold first dispatch does not move it); means of the counters per
+    dispatch in the three counter passes; rates against 1024 SIMDs x
+    duration x 2.4 GHz."""
+    import statistics
     dur, calls = {}, {}
     for r in _csv_rows(trace, "kernel_trace.csv"):
         k = _short_name(r["Kernel_Name"])
@@ -259,8 +261,8 @@ def record_counters(pmc_a: str, pmc_b: str, pmc_dram: str, trace: str, workload:
             for name, v in vals.items():
                 acc.setdefault(name, []).append(v)
     lines = []
-    for k in sorted(dur, key=lambda k: -sum(dur[k]) / len(dur[k])):
-        t = sum(dur[k]) / len(dur[k])
+    for k in sorted(dur, key=lambda k: -statistics.median(dur[k])):
+        t = statistics.median(dur[k])
         c = {name: sum(v) / len(v) for name, v in cnt.get(k, {}).items()}
         if "SQ_WAVES" not in c or t < 5e-6:
             continue
@@ -379,8 +381,8 @@ def workload_arg(workload: str) -> str:
 
 COUNTERS_HEADER = """# Per-kernel counters, `{workload}` ({title})
 
-One MI355X (gfx950), one process.  Durations: the mean over a kernel's
-dispatches in a kernel-trace pass.  Counters: means per dispatch over three
+One MI355X (gfx950), one process.  Durations: the median over a kernel's
+dispatches in a kernel-trace pass of 2 warm-up and 5 timed steps.  Counters: means per dispatch over three
 counter passes (each runs the benchmark for 1 warm-up and 1 timed step; the
 kernels and their work are those of the timed runs).  Rates are against the
 machine's capacity over the kernel's duration at the nominal 2.4 GHz peak
@@ -406,7 +408,7 @@ Kernels under 5 µs are left out.
 ## Commands (from the repository root; `<out>` is any output directory)
 
 ```
-rocprofv3 --kernel-trace --stats -d <out>/cnt_t -o t --output-format csv -- python3 bench.py{wl_arg} --steps 1 --warmup 1 --no-cpu-baseline
+rocprofv3 --kernel-trace --stats -d <out>/cnt_t -o t --output-format csv -- python3 bench.py{wl_arg} --steps 5 --warmup 2 --no-cpu-baseline
 rocprofv3 --pmc {a} -d <out>/cnt_a -o p --output-format csv -- python3 bench.py{wl_arg} --steps 1 --warmup 1 --no-cpu-baseline
 rocprofv3 --pmc {b} -d <out>/cnt_b -o p --output-format csv -- python3 bench.py{wl_arg} --steps 1 --warmup 1 --no-cpu-baseline
 rocprofv3 --pmc {dram} -d <out>/cnt_d -o p --output-format csv -- python3 bench.py{wl_arg} --steps 1 --warmup 1 --no-cpu-baseline

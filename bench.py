@@ -96,6 +96,11 @@ def stage_of(short: str):
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 
 
+def sig(x: float, digits: int = 4) -> float:
+    """x rounded to `digits` significant digits (small rates stay visible)."""
+    return float(f"{x:.{digits}g}")
+
+
 def traffic_file(workload: str) -> str:
     return os.path.join(PROFILES, f"hbm_traffic_{workload}.json")
 
@@ -845,16 +850,16 @@ def main():
     kernels = {}
     for name in STAGES:
         ms = per_stage[name]
-        entry = {"ms": round(ms, 5), "bytes": work[name]["bytes"],
-                 "GB/s": round(work[name]["bytes"] / (ms * 1e-3) / 1e9, 1)}
-        entry["hbm_frac"] = round(entry["GB/s"] / HBM_PEAK_GBS, 4)
+        gbs = work[name]["bytes"] / (ms * 1e-3) / 1e9
+        entry = {"ms": round(ms, 5), "bytes": work[name]["bytes"], "GB/s": sig(gbs),
+                 "hbm_frac": sig(gbs / HBM_PEAK_GBS)}
         if "flops" in work[name]:
             # the contraction's own peak: bf16 MFMA, or (float32 storage) the
             # fp64 MFMA the selection scores with
             tf = work[name]["flops"] / (ms * 1e-3) / 1e12
             peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_FP64_PEAK_TFLOPS
-            entry.update({"flops": work[name]["flops"], "TFLOP/s": round(tf, 2),
-                          "mfma_peak": peak, "mfma_frac": round(tf / peak, 4)})
+            entry.update({"flops": work[name]["flops"], "TFLOP/s": sig(tf),
+                          "mfma_peak": peak, "mfma_frac": sig(tf / peak)})
         if name in traffic:
             entry["traffic"] = traffic[name]["read_bytes"] + traffic[name]["write_bytes"]
         kernels[name] = entry
@@ -874,7 +879,7 @@ def main():
     else:
         roofline = {"kernel": dominant, "bound": "hbm", "achieved": dk["GB/s"],
                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(dk["GB/s"] / HBM_PEAK_GBS, 4), "traffic": dk.get("traffic")}
+                    "frac": dk["hbm_frac"], "traffic": dk.get("traffic")}
 
     out = {
         "metric": METRIC,

@@ -687,7 +687,10 @@ __global__ __launch_bounds__(kSegWaves *kWave) void seg_value_kernel(
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (blockIdx.x == 0 && threadIdx.x == 0)
         long_list(split, picks, d_v)[-1] = 0;   // the count of the long-run list (slot_scan_kernel)
-    const int64_t nom = ((int64_t)blockIdx.x * kSegWaves + wv) * chunk;
+    // neighbouring chunks on one XCD: the slots i n + j of one left sub-key i
+    // are picked by largely the same tokens, whose dy rows are then read
+    // again from the same L2
+    const int64_t nom = ((int64_t)xcd_contiguous_id() * kSegWaves + wv) * chunk;
     if (nom >= picks)
         return;
     // a bound inside a run of at most chunk picks moves to the run's end

@@ -118,6 +118,21 @@ __device__ __forceinline__ uint64_t dkey_min(uint64_t a, uint64_t b)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Workgroups are dealt to the 8 XCDs (each with its own L2) in turn.  The id
+// below renumbers a 1-D grid so that each XCD gets one contiguous range of
+// ids, walked in order: work items next to each other in id run on the same
+// XCD at about the same time and share its L2.  A bijection for any grid, so
+// correctness does not depend on how workgroups are actually dealt.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_contiguous_id()
+{
+    const int total = (int)gridDim.x;
+    const int g = (int)blockIdx.x;
+    const int q = total / kXcds, r = total % kXcds;
+    const int xcd = g % kXcds, pos = g / kXcds;
+    return xcd < r ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
+}
+
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask)
 {
     const uint32_t lo = __shfl_xor((int)(uint32_t)v, mask);

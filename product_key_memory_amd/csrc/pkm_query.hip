@@ -40,7 +40,6 @@ namespace pkm {
 // ---------------------------------------------------------------------------
 constexpr int kGBN = 128, kGBK = 32;
 constexpr int kGThreads = 256;
-constexpr int kXcds = 8;          // workgroups are dealt to the XCDs in turn
 constexpr int kGroupM = 8;        // tile rows walked together on one XCD
 
 // kBf16: bf16 A and B.  kBf16SplitA: A given as two bf16 planes, hi + lo (a
@@ -81,15 +80,10 @@ __device__ __forceinline__ int g_cell(int row, int k)
 // gx x gy tiles times the K slices.  Workgroup ids are renumbered so that
 // each XCD gets one contiguous range of tiles, walked kGroupM tile rows at a
 // time: tiles that share A and B panels run on the same XCD at about the same
-// time and meet in its L2.  A bijection for any grid, so correctness does not
-// depend on how workgroups are dealt.
+// time and meet in its L2.
 __device__ __forceinline__ void gemm_tile(int gx, int gy, int &tx, int &ty, int &tz)
 {
-    const int total = (int)gridDim.x;
-    const int g = blockIdx.x;
-    const int q = total / kXcds, r = total % kXcds;
-    const int xcd = g % kXcds, pos = g / kXcds;
-    const int id = xcd < r ? xcd * (q + 1) + pos : r * (q + 1) + (xcd - r) * q + pos;
+    const int id = xcd_contiguous_id();
     const int per_z = gx * gy;
     tz = id / per_z;
     const int l = id % per_z;

@@ -172,15 +172,20 @@ __device__ __forceinline__ int place_step(uint32_t key, bool valid, int bits, in
 // nb + 1 entries), then every pick of the chunk goes to
 // pairs[base[bucket] + bhist[block][bucket] + rank in block] as
 // (pick id, slot & (2^shift - 1)), in pick order within each bucket.
+// Block 0 also writes bucket_order, the order in which level 2's workgroups
+// take the buckets: the large ones (more than four times the mean, a
+// Zipf-hot slot's) first, then the rest, each in bucket order, so that the
+// longest workgroups start in the first round instead of finishing last.
 __global__ __launch_bounds__(kL1Threads) void bucket_scatter_kernel(
     const int32_t *__restrict__ idx, int64_t picks, int64_t chunk, int shift, int nb, int nb_bits,
     const int32_t *__restrict__ bhist, const int32_t *__restrict__ total,
-    int32_t *__restrict__ bucket_base, int2 *__restrict__ pairs)
+    int32_t *__restrict__ bucket_base, int32_t *__restrict__ bucket_order, int2 *__restrict__ pairs)
 {
     constexpr int PER = kMaxBuckets / kL1Threads;
     constexpr int W = kL1Threads / kWave;
     __shared__ int32_t hw[kSortWaves][kMaxBuckets];   // per-wave counts, then cursors
     __shared__ int32_t wsum[W];
+    __shared__ int32_t wbig[W];
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     // only the nb buckets in use (the rows are kMaxBuckets long)
     for (int u = 0; u < kSortWaves; ++u)
@@ -216,6 +221,35 @@ __global__ __launch_bounds__(kL1Threads) void bucket_scatter_kernel(
         const int b = PER * threadIdx.x + j;
         c[j] = b < nb ? total[b] : 0;
         local += c[j];
+    }
+    if (blockIdx.x == 0) {
+        const int64_t big = 4 * ((picks + nb - 1) / nb);
+        int nbig = 0;
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            nbig += (PER * (int)threadIdx.x + j < nb && c[j] > big) ? 1 : 0;
+        int tb;
+        const int bexcl = wave_exclusive_scan(nbig, &tb);
+        if (lane == 0)
+            wbig[w] = tb;
+        __syncthreads();
+        int pos_big = bexcl, all_big = 0;
+        for (int u = 0; u < W; ++u) {
+            pos_big += u < w ? wbig[u] : 0;
+            all_big += wbig[u];
+        }
+        // the buckets before this thread's first are all in use when it has one
+        int pos_small = all_big + PER * (int)threadIdx.x - pos_big;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int b = PER * threadIdx.x + j;
+            if (b < nb) {
+                if (c[j] > big)
+                    bucket_order[pos_big++] = b;
+                else
+                    bucket_order[pos_small++] = b;
+            }
+        }
     }
     int tw;
     const int excl = wave_exclusive_scan(local, &tw);
@@ -273,16 +307,18 @@ __global__ __launch_bounds__(kL1Threads) void bucket_scatter_kernel(
 // place (the bucket's pairs arrive in pick order, level 1 being stable, so
 // each slot's picks end in ascending pick id).
 __global__ __launch_bounds__(kL2Threads) void bucket_sort_kernel(
-    const int2 *__restrict__ pairs, const int32_t *__restrict__ bucket_base, int shift,
-    int64_t slots, int32_t *__restrict__ slot_start, int32_t *__restrict__ order)
+    const int2 *__restrict__ pairs, const int32_t *__restrict__ bucket_base,
+    const int32_t *__restrict__ bucket_order, int shift, int64_t slots,
+    int32_t *__restrict__ slot_start, int32_t *__restrict__ order)
 {
     constexpr int W = kL2Threads / kWave;
     __shared__ int32_t hw[kSortWaves][kMaxBucketSlots];  // per-wave counts, then cursors
     __shared__ int32_t wsum[W];
     const int B = 1 << shift;
-    const int64_t f0 = (int64_t)blockIdx.x << shift;
+    const int bucket = bucket_order[blockIdx.x];
+    const int64_t f0 = (int64_t)bucket << shift;
     const int nbins = (int)(slots - f0 < B ? slots - f0 : B);
-    const int beg = bucket_base[blockIdx.x], end = bucket_base[blockIdx.x + 1];
+    const int beg = bucket_base[bucket], end = bucket_base[bucket + 1];
     const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     // only the B slots of a bucket (the rows are kMaxBucketSlots long)
     for (int u = 0; u < kSortWaves; ++u)
@@ -1475,6 +1511,7 @@ hipError_t launch_slot_sort(const int32_t *idx, int64_t picks, int n, int32_t *s
     int32_t *bhist = reinterpret_cast<int32_t *>(base + S.off_bhist);
     int32_t *total = reinterpret_cast<int32_t *>(base + S.off_total);
     int32_t *bucket_base = reinterpret_cast<int32_t *>(base + S.off_base);
+    int32_t *bucket_order = reinterpret_cast<int32_t *>(base + S.off_order);
     int2 *pairs = reinterpret_cast<int2 *>(base + S.off_pairs);
     const int64_t slots = (int64_t)n * n;
     hipLaunchKernelGGL(bucket_hist_kernel, dim3(S.blocks), dim3(kL1Threads), 0, stream, idx,
@@ -1486,9 +1523,9 @@ hipError_t launch_slot_sort(const int32_t *idx, int64_t picks, int n, int32_t *s
         ++nb_bits;
     hipLaunchKernelGGL(bucket_scatter_kernel, dim3(S.blocks), dim3(kL1Threads), 0, stream, idx,
                        picks, S.chunk, S.shift, S.buckets, nb_bits, bhist, total, bucket_base,
-                       pairs);
+                       bucket_order, pairs);
     hipLaunchKernelGGL(bucket_sort_kernel, dim3(S.buckets), dim3(kL2Threads), 0, stream, pairs,
-                       bucket_base, S.shift, slots, slot_start, order);
+                       bucket_base, bucket_order, S.shift, slots, slot_start, order);
     return hipGetLastError();
 }
 

@@ -11,7 +11,8 @@ namespace pkm {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Scratch of the two-level slot sort: level-1 block histograms [blocks][buckets],
-// bucket totals and starts, and the (pick, low slot bits) pairs grouped by bucket.
+// bucket totals and starts, the order in which level 2 takes the buckets, and
+// the (pick, low slot bits) pairs grouped by bucket.
 constexpr int kMaxBuckets = 4096;
 constexpr int kMaxBucketSlots = 1024;
 constexpr int kMinBucketShift = 7;    // buckets of at least 128 slots (measured: 2048
@@ -24,7 +25,7 @@ struct SlotSortScratch {
     int buckets;            // ceil(slots / 2^shift) <= kMaxBuckets
     int blocks;             // level-1 workgroups, each over `chunk` consecutive picks
     int64_t chunk;
-    size_t off_bhist, off_total, off_base, off_pairs, total;
+    size_t off_bhist, off_total, off_base, off_order, off_pairs, total;
 };
 
 inline SlotSortScratch slot_sort_scratch(int64_t picks, int n)
@@ -51,7 +52,8 @@ inline SlotSortScratch slot_sort_scratch(int64_t picks, int n)
     S.off_bhist = 0;
     S.off_total = align256((size_t)S.blocks * S.buckets * 4);
     S.off_base = align256(S.off_total + (size_t)S.buckets * 4);
-    S.off_pairs = align256(S.off_base + ((size_t)S.buckets + 1) * 4);
+    S.off_order = align256(S.off_base + ((size_t)S.buckets + 1) * 4);
+    S.off_pairs = align256(S.off_order + (size_t)S.buckets * 4);
     S.total = align256(S.off_pairs + (size_t)(picks > 0 ? picks : 0) * 8);
     return S;
 }

@@ -53,7 +53,7 @@ constexpr int kFastTiles = 32;                       // 16-sub-key tiles per blo
 constexpr int kFastBlock = 16 * kFastTiles;          // 512 sub-keys per block (at most)
 constexpr int kFastKSteps = 8;                       // 32-wide K steps: half = 256
 constexpr int kFastSurv = 64;                        // survivors per token at most
-constexpr int kSurvStride = kFastSurv + 4;           // + one spare slot per lane group
+constexpr int kSurvStride = kFastSurv + 4;           // row pitch of a token's survivors (words)
 constexpr int kSubBits = 10;                         // sub-key index < n <= 1024
 constexpr int kSlotBits = 20;                        // slot i n + j < n^2 <= 2^20
 constexpr int kMergeWaves = 4;
@@ -420,12 +420,9 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
             }
         }
 
-        // compact the survivors per token as two 32-bit arrays (scores, and
-        // the part 16 j + i of the sub-key known at compile time: 64-bit keys
-        // built here would pin register pairs for all 128 candidates), then
-        // sort them as keys in the 4-lane group.  The reader adds 4 x (the
-        // writing lane group), which it knows from the survivor's position,
-        // and the block's first sub-key.
+        // compact the survivors per token as two 32-bit arrays (scores and
+        // sub-keys: 64-bit keys built here would pin register pairs for all
+        // 128 candidates), then sort them as keys in the 4-lane group.
         const bool exact = tie_idx != 0xFFFFFFFFu;
         const int lim_t = exact ? (int)tie_idx - 4 * g : 0;   // 16 j + i <= lim_t among ties
         int mine = cnt;
@@ -441,12 +438,14 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
                 }
             mine = c;
         }
-        // Lane group g writes its survivors from position g + (the counts of
-        // the groups before it), each at the next free position; the stores
-        // are predicated (exec-masked), so only the lanes keeping a candidate
-        // touch LDS (the position after each group's range stays a spare).
+        // Lane group g writes its survivors from position (the counts of the
+        // groups before it), each at the next free position; the stores are
+        // predicated (exec-masked), so only the lanes keeping a candidate
+        // touch LDS, and survivor e ends at position e.  Sub-key 16 j + i +
+        // gb: the constant part and the lane's own part, one add per store.
         const int c0 = __shfl(mine, tok), c1 = __shfl(mine, tok + 16), c2 = __shfl(mine, tok + 32);
-        int off = g + (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
+        int off = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
+        const uint32_t gb = 4u * (uint32_t)g + (uint32_t)base;
         if (ordm) {
 #pragma unroll
             for (int j = 0; j < TILES; ++j) {
@@ -457,7 +456,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
                         live && (exact ? (o > kth || (o == kth && 16 * j + i <= lim_t)) : o >= kth);
                     if (keep) {
                         surv_s[off] = o;
-                        surv_i[off] = (uint32_t)(16 * j + i);
+                        surv_i[off] = (uint32_t)(16 * j + i) + gb;
                     }
                     off += keep ? 1 : 0;
                 }
@@ -471,7 +470,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
                     const bool keep = sf(j, i) >= tau;
                     if (keep) {
                         surv_s[off] = so[j][i];
-                        surv_i[off] = (uint32_t)(16 * j + i);
+                        surv_i[off] = (uint32_t)(16 * j + i) + gb;
                     }
                     off += keep ? 1 : 0;
                 }
@@ -479,17 +478,13 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
             }
         }
         wave_lds_sync();
-        const int b1 = c0, b2 = c0 + c1, b3 = c0 + c1 + c2;
         uint64_t v[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            // survivor e was written by lane group src_g, at position e + src_g
             const int e = 16 * g + r;
-            const int src_g = (e >= b1 ? 1 : 0) + (e >= b2 ? 1 : 0) + (e >= b3 ? 1 : 0);
-            const uint32_t sv = surv_s[e + src_g];
+            const uint32_t sv = surv_s[e];
             const uint32_t hi = ordm ? sv : ord_f32(__uint_as_float(sv));
-            v[r] = e < total ? dkey<kSubBits>(hi, surv_i[e + src_g] + 4u * (uint32_t)src_g + (uint32_t)base)
-                             : 0ull;
+            v[r] = e < total ? dkey<kSubBits>(hi, surv_i[e]) : 0ull;
         }
         group4_sort_desc_dkey(v);
         // lane group g holds ranks 16 g .. 16 g + 15 of the block
@@ -568,7 +563,7 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
 // more than kMergeSurv candidates, the survivors are compacted into LDS and
 // sorted 64 per row; otherwise every candidate is sorted, 128 per row.
 constexpr int kMaxCorners = 16;
-constexpr int kMergeSurv = 60;      // + a spare slot per lane group: < 64 per row
+constexpr int kMergeSurv = 64;      // survivors per row at most: the sort's width
 
 // list entries as staged in LDS: (score as float bits, sub-key)
 __device__ __forceinline__ float merge_score(uint2 l, uint2 r)
@@ -720,13 +715,13 @@ __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
 
     // The survivors (key >= kth) go to this wave's list area, free once every
     // lane has its candidates: 64 slots per row.  Lane group g writes from
-    // position g + (the counts of the groups before it), each survivor at the
+    // position (the counts of the groups before it), each survivor at the
     // next free slot, by predicated stores (only lanes keeping a candidate
-    // touch LDS).
+    // touch LDS): survivor e ends at position e.
     wave_lds_sync();
     uint64_t *surv = reinterpret_cast<uint64_t *>(sl) + tok * kMergePitch;
     const int c0 = __shfl(cnt, tok), c1 = __shfl(cnt, tok + 16), c2 = __shfl(cnt, tok + 32);
-    int off = g + (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
+    int off = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
 #pragma unroll
     for (int c = 0; c < 32; ++c) {
         const bool keep = live && v[c] >= kth;
@@ -735,13 +730,11 @@ __global__ __launch_bounds__(kMergeWaves *kWave) void fwd_merge_kernel(
         off += keep ? 1 : 0;
     }
     wave_lds_sync();
-    const int b1 = c0, b2 = c0 + c1, b3 = c0 + c1 + c2;
     uint64_t w[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         const int e = 16 * g + q;
-        const int src_g = (e >= b1 ? 1 : 0) + (e >= b2 ? 1 : 0) + (e >= b3 ? 1 : 0);
-        w[q] = live && e < total ? surv[e + src_g] : 0ull;
+        w[q] = live && e < total ? surv[e] : 0ull;
     }
     group4_sort_desc_dkey(w);
 

@@ -424,8 +424,8 @@ __device__ __forceinline__ int64_t piece_row(int64_t a, int shift)
 // the chunk is appended to `longs` (its slot), counted in longs[-1], which
 // seg_value_kernel reset.  The runs of the Zipf-hot queries' slots sit next
 // to each other (slots i n + j of one hot left sub-key i), so they are summed
-// by long_run_kernel, one wave each, rather than in turn by the wave that
-// found them.
+// by long_run_kernel, one workgroup each, rather than in turn by the wave
+// that found them.
 constexpr int kFinishWaves = 4;
 template <int MODE>
 __global__ __launch_bounds__(kFinishWaves *kWave) void slot_scan_kernel(
@@ -478,22 +478,24 @@ __global__ __launch_bounds__(kFinishWaves *kWave) void long_run_kernel(
 {
     constexpr int EPC = Elt<DT>::per16;
     const int lane = lane_id();
-    const int wv = (int)blockIdx.x * kFinishWaves + (int)(threadIdx.x / kWave);
-    if (wv >= longs[-1])
-        return;
-    {
-        const int64_t fr = longs[wv];
+    // workgroup b takes the listed runs b, b + gridDim.x, ...; its waves
+    // split a run's row into column parts, so each wave keeps more pieces
+    // in flight (a Zipf-hot run has a few dozen)
+    const int part = (int)(threadIdx.x / kWave);
+    const int runs = longs[-1];
+    for (int run = (int)blockIdx.x; run < runs; run += (int)gridDim.x) {
+        const int64_t fr = longs[run];
         const int64_t b = start[fr], e = start[fr + 1];
         const int64_t cb = b >> shift, ce = (e - 1) >> shift;
         const int64_t r0 = piece_row(b, shift);
         auto row_of = [&](int64_t cc) { return cc == cb ? r0 : 2 * cc; };
-        // UPL units of EPC floats (16 floats) per lane per pass; the loads of
-        // PIECES pieces are issued before any is added, then the pieces are added
-        // one after the other in position order (the same order in every
-        // mode, so overwrite + sparse SGD and the fused SGD agree bit for bit)
-        constexpr int UPL = 16 / EPC, PIECES = 8;
+        // one unit of EPC floats per lane per pass; the loads of PIECES pieces
+        // are issued before any is added, then the pieces are added one after
+        // the other in position order (the same order in every mode, so
+        // overwrite + sparse SGD and the fused SGD agree bit for bit)
+        constexpr int UPL = 1, PIECES = 128 / EPC;
         const int nunits = d_v / EPC;
-        for (int u0 = 0; u0 < nunits; u0 += UPL * kWave) {
+        for (int u0 = part * UPL * kWave; u0 < nunits; u0 += kFinishWaves * UPL * kWave) {
             float g[UPL][EPC];
 #pragma unroll
             for (int m = 0; m < UPL; ++m)
@@ -1530,9 +1532,9 @@ hipError_t launch_slot_sort(const int32_t *idx, int64_t picks, int n, int32_t *s
 }
 
 // slot_scan_kernel (untouched rows, the list of long runs) then
-// long_run_kernel, one wave per possible long run (at most picks / chunk + 1;
-// the waves past the listed count return at once).  `longs` follows the
-// piece rows in the split buffer (split_rows_bytes lays it out).
+// long_run_kernel, up to 256 workgroups walking the listed runs (at most
+// picks / chunk + 1), four waves to a run.  `longs` follows the piece rows in
+// the split buffer (split_rows_bytes lays it out).
 template <typename DT, int MODE>
 static hipError_t launch_finish(const int32_t *slot_start, int64_t slots, int64_t picks, int d_v,
                                 int shift, float *split, float *dvalues, void *values, float lr,
@@ -1545,8 +1547,9 @@ static hipError_t launch_finish(const int32_t *slot_start, int64_t slots, int64_
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
+    // at most picks / chunk + 1 long runs, walked by at most 256 workgroups
     const int64_t max_long = (picks >> shift) + 1;
-    hipLaunchKernelGGL((long_run_kernel<DT, MODE>), dim3(grid1d(max_long, kFinishWaves)),
+    hipLaunchKernelGGL((long_run_kernel<DT, MODE>), dim3((unsigned)(max_long < 256 ? max_long : 256)),
                        dim3(kFinishWaves * kWave), 0, stream, slot_start, d_v, shift, split, longs,
                        dvalues, static_cast<DT *>(values), lr);
     return hipGetLastError();

@@ -559,9 +559,10 @@ __global__ __launch_bounds__(kFastWaves *kWave) __attribute__((amdgpu_waves_per_
 // the set S = {(a, b) : (a + 1)(b + 1) <= m}, m the least value with |S| >= k,
 // holds at least k candidates, so the k-th best score is at least the least
 // score in S -- the least of its corner scores s(a, m / (a + 1) - 1), as the
-// lists are sorted and rounding is monotone.  When no row of the wave keeps
-// more than kMergeSurv candidates, the survivors are compacted into LDS and
-// sorted 64 per row; otherwise every candidate is sorted, 128 per row.
+// lists are sorted and rounding is monotone.  A row keeping more than
+// kMergeSurv candidates raises the bound by bisection on the score (under
+// heavy ties: the exact k-th key, by bisection on the 64-bit keys); the at
+// most kMergeSurv survivors are then compacted into LDS and sorted per row.
 constexpr int kMaxCorners = 16;
 constexpr int kMergeSurv = 64;      // survivors per row at most: the sort's width
 

@@ -138,12 +138,14 @@ __device__ __forceinline__ void flat_scores(uint32_t (&so)[kFlatTiles][4], const
 }
 
 // A token's buffered candidates (fill <= 48 entries of score and slot) merged
-// into its running top k: they become 64-bit keys (order-preserving score,
-// then the complemented slot: ties go to the lower slot), are sorted inside
-// the token's 4 lanes, and the top k of the sorted list A (the running one)
-// and B (the candidates) are max(A[e], B[31 - e]) for e < 32 -- a bitonic
-// sequence -- put in order by a bitonic merge.  Wave-wide: every lane takes
-// part (tokens with an empty buffer merge zero keys, which changes nothing).
+// into its running top k: they become 64-bit keys that order as float64
+// values (order-preserving score, then the lower slot first; slots < 2^20),
+// are sorted inside the token's 4 lanes, and the top k of the sorted list A
+// (the running one) and B (the candidates) are max(A[e], B[31 - e]) for
+// e < 32 -- a bitonic sequence -- put in order by a bitonic merge, every
+// exchange one float64 max and one min.  Wave-wide: every lane takes part
+// (tokens with an empty buffer merge zero keys, which changes nothing).
+constexpr int kFlatSlotBits = 20;
 __device__ __forceinline__ void merge_buffer(int g, int tok, int fill, const uint32_t *buf_s,
                                              const uint32_t *buf_f, uint64_t *best)
 {
@@ -151,9 +153,9 @@ __device__ __forceinline__ void merge_buffer(int g, int tok, int fill, const uin
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int e = 16 * g + r;
-        v[r] = e < fill ? ((uint64_t)buf_s[e] << 32) | (uint64_t)~buf_f[e] : 0ull;
+        v[r] = e < fill ? dkey<kFlatSlotBits>(buf_s[e], buf_f[e]) : 0ull;
     }
-    group4_sort_desc<16>(v);
+    group4_sort_desc_dkey(v);
     // lane groups 0 and 1 hold C; B[31 - e] is register 15 - r of the other group
     const int ga = g & 1;
     uint64_t c[16];
@@ -161,12 +163,12 @@ __device__ __forceinline__ void merge_buffer(int g, int tok, int fill, const uin
     for (int r = 0; r < 16; ++r) {
         const uint64_t a = best[16 * ga + r];
         const uint64_t b = shfl_xor_u64(v[15 - r], 16);
-        c[r] = a > b ? a : b;
+        c[r] = dkey_max(a, b);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const uint64_t o = shfl_xor_u64(c[r], 16);
-        c[r] = ((c[r] > o) == (ga == 0)) ? c[r] : o;
+        c[r] = ga == 0 ? dkey_max(c[r], o) : dkey_min(c[r], o);
     }
 #pragma unroll
     for (int stride = 8; stride > 0; stride >>= 1)
@@ -174,8 +176,8 @@ __device__ __forceinline__ void merge_buffer(int g, int tok, int fill, const uin
         for (int r = 0; r < 16; ++r)
             if ((r & stride) == 0) {
                 const uint64_t x = c[r], y = c[r | stride];
-                c[r] = x > y ? x : y;
-                c[r | stride] = x > y ? y : x;
+                c[r] = dkey_max(x, y);
+                c[r | stride] = dkey_min(x, y);
             }
     wave_lds_sync();
     if (g < 2) {
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(kFlatWaves *kWave) __attribute__((amdgpu_waves_per_
             tau = group4_kth(gm, k);
         } else {
             // the running k-th best score: keys below it cannot enter
-            tau = (uint32_t)(best[k - 1] >> 32);
+            tau = dkey_ord<kFlatSlotBits>(best[k - 1]);
         }
 
         // survivors: ord >= tau (a token past T keeps nothing)
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(kFlatWaves *kWave) __attribute__((amdgpu_waves_per_
             merge_buffer(g, tok, fill, buf_s, buf_f, best);
             fill = 0;
             if (!first) {
-                tau = (uint32_t)(best[k - 1] >> 32);
+                tau = dkey_ord<kFlatSlotBits>(best[k - 1]);
                 cnt = count_ge(tau);
                 total = group4_sum(cnt);
             }
@@ -386,11 +388,11 @@ __global__ __launch_bounds__(kFlatWaves *kWave) __attribute__((amdgpu_waves_per_
 #pragma unroll
     for (int r = 0; r < 16; ++r)
         v[r] = g < 2 && 16 * g + r < k ? best[16 * g + r] : 0ull;
-    const float top = key_score(best[0]);
+    const float top = unord_f32(dkey_ord<kFlatSlotBits>(best[0]));
     float ex[16], z = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        ex[r] = g < 2 && 16 * g + r < k ? expf(key_score(v[r]) - top) : 0.f;
+        ex[r] = g < 2 && 16 * g + r < k ? expf(unord_f32(dkey_ord<kFlatSlotBits>(v[r])) - top) : 0.f;
         z += ex[r];
     }
     z += __shfl_xor(z, 16);
@@ -400,10 +402,10 @@ __global__ __launch_bounds__(kFlatWaves *kWave) __attribute__((amdgpu_waves_per_
         for (int r = 0; r < 16; ++r) {
             const int e = 16 * g + r;
             if (e < k) {
-                idx[out + e] = (int32_t)key_index(v[r]);
+                idx[out + e] = (int32_t)dkey_index<kFlatSlotBits>(v[r]);
                 weights[out + e] = ex[r] / z;
                 if (scores)
-                    scores[out + e] = key_score(v[r]);
+                    scores[out + e] = unord_f32(dkey_ord<kFlatSlotBits>(v[r]));
             }
         }
     }
